@@ -1,0 +1,191 @@
+"""Python binding of libquantwm (the QuantWM 2-bit KV-cache hot path on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libquantwm.so.  PyTorch provides device memory and the current stream.  The
+library must be built first (python -m bit_kv_cache_head_amd.build); importing
+this package raises if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+from ._abi import (lib, LIB_PATH, QWM_OK, QWM_F32, QWM_BF16, QWM_QSAC, QWM_PSAC, QWM_OP_STATS,
+                   QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION, Tokens, QStats,
+                   Packed, Diag, Segment, check)
+
+D, NC, R, GROUP = 128, 256, 8, 64
+
+__all__ = ["QueryStats", "PackedChunk", "Workspace", "update_query_stats", "build_centroids",
+           "quantize_keys", "quantize_values", "attention", "segments_tensor", "zeros_stride",
+           "QWM_QSAC", "QWM_PSAC", "LIB_PATH", "new_diag"]
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _tokens(x: torch.Tensor) -> Tokens:
+    """Descriptor of a [T, H, d] tensor (bf16 or fp32, channel stride 1)."""
+    if x.dim() != 3:
+        raise ValueError("token tensor must be [T, H, d]")
+    if not x.is_cuda:
+        raise ValueError("token tensor must be on the GPU")
+    if x.stride(2) != 1:
+        raise ValueError("channel stride must be 1")
+    dt = {torch.bfloat16: QWM_BF16, torch.float32: QWM_F32}.get(x.dtype)
+    if dt is None:
+        raise ValueError("token dtype must be bfloat16 or float32")
+    T, H, d = x.shape
+    return Tokens(C.c_void_p(x.data_ptr()), dt, H, d, 0, T, x.stride(0), x.stride(1))
+
+
+def zeros_stride(T: int) -> int:
+    return int(lib.qwm_zeros_stride(T))
+
+
+class Workspace:
+    """Grow-only device scratch buffer (256-byte aligned by the caching allocator)."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes: int, device) -> tuple:
+        if nbytes == 0:
+            return C.c_void_p(0), 0
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return C.c_void_p(self.buf.data_ptr()), self.buf.numel()
+
+
+_WS = Workspace()
+
+
+def new_diag(device="cuda") -> torch.Tensor:
+    """Device counters: [nonfinite_rows, exact_fallbacks, scale_saturations, reserved] int64."""
+    return torch.zeros(4, dtype=torch.int64, device=device)
+
+
+class QueryStats:
+    """Per-head running Query statistics and principal basis (device tensors)."""
+
+    def __init__(self, H: int, device="cuda"):
+        self.H = H
+        self.S = torch.zeros(H, D, D, dtype=torch.float64, device=device)
+        self.n = torch.zeros(H, dtype=torch.int64, device=device)
+        self.w = torch.ones(H, D, dtype=torch.float32, device=device)
+        self.U = torch.zeros(H, D, R, dtype=torch.bfloat16, device=device)
+        self.lam = torch.zeros(H, R, dtype=torch.float32, device=device)
+        self.energy = torch.zeros(H, dtype=torch.float32, device=device)
+        self.iters = torch.zeros(H, dtype=torch.int32, device=device)
+
+    def desc(self) -> QStats:
+        return QStats(_ptr(self.S), _ptr(self.n), _ptr(self.w), _ptr(self.U), _ptr(self.lam),
+                      _ptr(self.energy), _ptr(self.iters), self.H, D, R, 0)
+
+
+class PackedChunk:
+    """One packed chunk: codes [H,T,32] u8, idx [H,T] u8, scale [H,T,2] fp16 bits,
+    zeros [H, zstride] u8, c [H,T,8] i8 and c_scale [H,T] fp16 bits (keys)."""
+
+    def __init__(self, T: int, H: int, keys: bool, device="cuda"):
+        self.T, self.H, self.keys = T, H, keys
+        self.codes = torch.empty(H, T, D // 4, dtype=torch.uint8, device=device)
+        self.idx = torch.empty(H, T, dtype=torch.uint8, device=device)
+        self.scale = torch.empty(H, T, 2, dtype=torch.int16, device=device)
+        self.zeros = torch.zeros(H, zeros_stride(T), dtype=torch.uint8, device=device)
+        self.c = torch.empty(H, T, R, dtype=torch.int8, device=device) if keys else None
+        self.c_scale = torch.empty(H, T, dtype=torch.int16, device=device) if keys else None
+
+    def desc(self) -> Packed:
+        return Packed(_ptr(self.codes), _ptr(self.idx), _ptr(self.scale), _ptr(self.zeros),
+                      _ptr(self.c), _ptr(self.c_scale), self.T, self.H, R)
+
+    def nbytes(self) -> int:
+        tot = self.codes.numel() + self.idx.numel() + 2 * self.scale.numel() + self.zeros.numel()
+        if self.keys:
+            tot += self.c.numel() + 2 * self.c_scale.numel()
+        return tot
+
+
+def update_query_stats(q: torch.Tensor, st: QueryStats, compute_basis: bool = True):
+    td = _tokens(q)
+    check(lib.qwm_update_query_stats(C.byref(td), C.byref(st.desc()), int(compute_basis),
+                                     C.c_void_p(0), 0, _stream()))
+
+
+def build_centroids(x: torch.Tensor, iters: int, seed: int = 0, init: torch.Tensor | None = None,
+                    out: torch.Tensor | None = None, diag: torch.Tensor | None = None) -> torch.Tensor:
+    """[H, 256, 128] bf16 centroid table by `iters` Lloyd iterations."""
+    td = _tokens(x)
+    if out is None:
+        out = torch.empty(td.H, NC, D, dtype=torch.bfloat16, device=x.device)
+    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_CENTROIDS, td.T, td.H, 0), x.device)
+    check(lib.qwm_build_centroids(C.byref(td), NC, iters, C.c_uint64(seed), _ptr(init), _ptr(out),
+                                  _ptr(diag), ws, nb, _stream()))
+    return out
+
+
+def quantize_keys(k: torch.Tensor, centroids: torch.Tensor, w: torch.Tensor | None, U: torch.Tensor | None,
+                  M: int = 8, flags: int = QWM_QSAC | QWM_PSAC, out: PackedChunk | None = None,
+                  diag: torch.Tensor | None = None) -> PackedChunk:
+    td = _tokens(k)
+    if out is None:
+        out = PackedChunk(td.T, td.H, True, k.device)
+    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_KEYS, td.T, td.H, 0), k.device)
+    check(lib.qwm_quantize_keys(C.byref(td), _ptr(centroids), _ptr(w), _ptr(U), M, flags,
+                                C.byref(out.desc()), _ptr(diag), ws, nb, _stream()))
+    return out
+
+
+def quantize_values(v: torch.Tensor, centroids: torch.Tensor, out: PackedChunk | None = None,
+                    diag: torch.Tensor | None = None) -> PackedChunk:
+    td = _tokens(v)
+    if out is None:
+        out = PackedChunk(td.T, td.H, False, v.device)
+    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_VALUES, td.T, td.H, 0), v.device)
+    check(lib.qwm_quantize_values(C.byref(td), _ptr(centroids), C.byref(out.desc()), _ptr(diag),
+                                  ws, nb, _stream()))
+    return out
+
+
+def segments_tensor(segments, device="cuda") -> tuple:
+    """Device array of segment descriptors.  `segments`: list of
+    (k: PackedChunk, v: PackedChunk, k_centroids, v_centroids, U or None).
+    Returns (device uint8 tensor, total keys).  Keep the tensor alive while in use."""
+    arr = (Segment * len(segments))()
+    total = 0
+    for i, (kp, vp, kc, vc, U) in enumerate(segments):
+        s = arr[i]
+        s.k_codes, s.k_idx, s.k_scale, s.k_zeros = (kp.codes.data_ptr(), kp.idx.data_ptr(),
+                                                    kp.scale.data_ptr(), kp.zeros.data_ptr())
+        s.k_c, s.k_c_scale = kp.c.data_ptr(), kp.c_scale.data_ptr()
+        s.v_codes, s.v_idx, s.v_scale, s.v_zeros = (vp.codes.data_ptr(), vp.idx.data_ptr(),
+                                                    vp.scale.data_ptr(), vp.zeros.data_ptr())
+        s.k_centroids, s.v_centroids = kc.data_ptr(), vc.data_ptr()
+        s.U = 0 if U is None else U.data_ptr()
+        s.T = kp.T
+        total += kp.T
+    host = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
+    return host.to(device), total
+
+
+def attention(q: torch.Tensor, segs: torch.Tensor, n_segs: int, total_keys: int, scale: float | None = None,
+              want_lse: bool = False, want_top1: bool = False):
+    """out [Tq, H, 128] fp32 (+ lse [H, Tq], top1 [H, Tq] int32)."""
+    td = _tokens(q)
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    out = torch.empty(td.T, td.H, D, dtype=torch.float32, device=q.device)
+    lse = torch.empty(td.H, td.T, dtype=torch.float32, device=q.device) if want_lse else None
+    top1 = torch.empty(td.H, td.T, dtype=torch.int32, device=q.device) if want_top1 else None
+    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_ATTENTION, total_keys, td.H, td.T), q.device)
+    check(lib.qwm_attention(C.byref(td), C.c_void_p(segs.data_ptr()), n_segs, total_keys, C.c_float(scale),
+                            _ptr(out), _ptr(lse), _ptr(top1), ws, nb, _stream()))
+    return out, lse, top1

@@ -1,0 +1,185 @@
+// C ABI of libquantwm: argument validation, workspace sizing, dispatch.
+#include <cstdio>
+#include <string>
+
+#include "common.hpp"
+
+namespace qwm_host {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+qwm_status fail(qwm_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+qwm_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QWM_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return QWM_OK;
+}
+
+// defined in the kernel translation units
+qwm_status launch_stats(const qwm_tokens* q, const qwm_qstats* st, int32_t compute_basis, hipStream_t stream);
+qwm_status launch_keys(const qwm_tokens* k, const uint16_t* centroids, const float* w, const uint16_t* U,
+                       int32_t M, uint32_t flags, const qwm_packed* out, qwm_diag* diag, void* ws,
+                       hipStream_t stream);
+qwm_status launch_values(const qwm_tokens* v, const uint16_t* centroids, const qwm_packed* out, qwm_diag* diag,
+                         void* ws, hipStream_t stream);
+qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const uint16_t* init, uint16_t* centroids,
+                        qwm_diag* diag, void* ws, hipStream_t stream);
+qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
+                            float scale, float* out, float* lse, int32_t* top1, void* ws, hipStream_t stream);
+size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd);
+size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq);
+
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static qwm_status check_tokens(const qwm_tokens* t, const char* name, bool allow_empty) {
+  if (!t) return fail(QWM_ERR_ARG, std::string(name) + ": null descriptor");
+  if (t->d != qwm::D) return fail(QWM_ERR_UNSUPPORTED, std::string(name) + ": head dim must be 128");
+  if (t->dtype != QWM_BF16 && t->dtype != QWM_F32) return fail(QWM_ERR_UNSUPPORTED, std::string(name) + ": dtype");
+  if (t->H < 1) return fail(QWM_ERR_ARG, std::string(name) + ": H < 1");
+  if (t->T < 0 || (!allow_empty && t->T < 1)) return fail(QWM_ERR_ARG, std::string(name) + ": bad token count");
+  if (t->T > ((int64_t)1 << 31) / t->H) return fail(QWM_ERR_UNSUPPORTED, std::string(name) + ": H*T >= 2^31");
+  if (t->T > 0 && !t->ptr) return fail(QWM_ERR_ARG, std::string(name) + ": null data");
+  if (t->T > 0 && !aligned(t->ptr, 16)) return fail(QWM_ERR_ARG, std::string(name) + ": data not 16-byte aligned");
+  if (t->stride_t < 0 || t->stride_h < 0 || t->stride_t % 8 || t->stride_h % 8)
+    return fail(QWM_ERR_ARG, std::string(name) + ": strides must be non-negative multiples of 8 elements");
+  if (t->T > 1 && t->stride_t < qwm::D && t->stride_t != 0)
+    return fail(QWM_ERR_ARG, std::string(name) + ": token stride smaller than a row");
+  return QWM_OK;
+}
+
+static qwm_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return QWM_OK;
+  if (!ws) return fail(QWM_ERR_WORKSPACE, "workspace is null");
+  if (!aligned(ws, 256)) return fail(QWM_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (have < need)
+    return fail(QWM_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes, got " +
+                                       std::to_string(have));
+  return QWM_OK;
+}
+
+static qwm_status check_packed(const qwm_packed* p, const qwm_tokens* x, bool keys, bool psac) {
+  if (!p) return fail(QWM_ERR_ARG, "packed: null descriptor");
+  if (p->T != x->T || p->H != x->H) return fail(QWM_ERR_ARG, "packed: shape differs from the tokens");
+  if (!p->codes || !p->idx || !p->scale || !p->zeros) return fail(QWM_ERR_ARG, "packed: null array");
+  if (!aligned(p->codes, 16) || !aligned(p->scale, 4) || !aligned(p->zeros, 4))
+    return fail(QWM_ERR_ARG, "packed: codes must be 16-byte, scale and zeros 4-byte aligned");
+  if (keys) {
+    if (!p->c || !p->c_scale) return fail(QWM_ERR_ARG, "packed keys: null c / c_scale");
+    if (p->r != qwm::R) return fail(QWM_ERR_UNSUPPORTED, "packed keys: rank must be 8");
+    if (!aligned(p->c, 8) || !aligned(p->c_scale, 2)) return fail(QWM_ERR_ARG, "packed keys: c misaligned");
+  }
+  (void)psac;
+  return QWM_OK;
+}
+
+}  // namespace qwm_host
+
+using namespace qwm_host;
+
+extern "C" {
+
+int32_t qwm_abi_version(void) { return QWM_ABI_VERSION; }
+
+const char* qwm_last_error(void) { return g_last_error.c_str(); }
+
+int64_t qwm_zeros_stride(int64_t T) { return qwm::zeros_stride(T); }
+
+size_t qwm_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t n) {
+  if (T < 0 || H < 1) return 0;
+  switch (op) {
+    case QWM_OP_STATS: return 0;
+    case QWM_OP_CENTROIDS: return select_ws_bytes(T, H, true);
+    case QWM_OP_KEYS:
+    case QWM_OP_VALUES: return select_ws_bytes(T, H, false);
+    case QWM_OP_ATTENTION: return attention_ws_bytes(T, H, n);
+    default: return 0;
+  }
+}
+
+qwm_status qwm_update_query_stats(const qwm_tokens* q, const qwm_qstats* st, int32_t compute_basis, void* ws,
+                                  size_t ws_bytes, qwm_stream stream) {
+  (void)ws; (void)ws_bytes;
+  qwm_status s = check_tokens(q, "queries", true);
+  if (s != QWM_OK) return s;
+  if (!st) return fail(QWM_ERR_ARG, "stats: null descriptor");
+  if (st->H != q->H || st->d != qwm::D) return fail(QWM_ERR_ARG, "stats: H / d differ from the queries");
+  if (st->r != qwm::R) return fail(QWM_ERR_UNSUPPORTED, "stats: rank must be 8");
+  if (!st->S || !st->n || !st->w) return fail(QWM_ERR_ARG, "stats: null S / n / w");
+  if (!aligned(st->S, 8) || !aligned(st->n, 8) || !aligned(st->w, 4)) return fail(QWM_ERR_ARG, "stats: misaligned");
+  if (compute_basis && (!st->U || !st->lambda || !st->energy))
+    return fail(QWM_ERR_ARG, "stats: null U / lambda / energy");
+  return launch_stats(q, st, compute_basis, static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_build_centroids(const qwm_tokens* x, int32_t n_centroids, int32_t iters, uint64_t seed,
+                               const uint16_t* init, uint16_t* centroids, qwm_diag* diag, void* ws,
+                               size_t ws_bytes, qwm_stream stream) {
+  qwm_status s = check_tokens(x, "tokens", false);
+  if (s != QWM_OK) return s;
+  if (n_centroids != qwm::NC) return fail(QWM_ERR_UNSUPPORTED, "n_centroids must be 256");
+  if (iters < 0 || iters > 1000) return fail(QWM_ERR_ARG, "iters out of range [0, 1000]");
+  if (!centroids || !aligned(centroids, 16)) return fail(QWM_ERR_ARG, "centroids: null or not 16-byte aligned");
+  if (init && !aligned(init, 16)) return fail(QWM_ERR_ARG, "init: not 16-byte aligned");
+  if (!init && x->T < qwm::NC) return fail(QWM_ERR_ARG, "seeded start needs at least 256 tokens");
+  if (diag && !aligned(diag, 8)) return fail(QWM_ERR_ARG, "diag misaligned");
+  s = check_ws(ws, ws_bytes, select_ws_bytes(x->T, x->H, true));
+  if (s != QWM_OK) return s;
+  return launch_lloyd(x, iters, seed, init, centroids, diag, ws, static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_quantize_keys(const qwm_tokens* k, const uint16_t* centroids, const float* w, const uint16_t* U,
+                             int32_t M, uint32_t flags, const qwm_packed* out, qwm_diag* diag, void* ws,
+                             size_t ws_bytes, qwm_stream stream) {
+  qwm_status s = check_tokens(k, "keys", false);
+  if (s != QWM_OK) return s;
+  if (!centroids || !aligned(centroids, 16)) return fail(QWM_ERR_ARG, "centroids: null or not 16-byte aligned");
+  if (flags & ~(uint32_t)(QWM_QSAC | QWM_PSAC)) return fail(QWM_ERR_ARG, "unknown flag bits");
+  if ((flags & QWM_QSAC) && (M < 1 || M > qwm::NC)) return fail(QWM_ERR_ARG, "M must be in [1, 256]");
+  if (w && !aligned(w, 4)) return fail(QWM_ERR_ARG, "w misaligned");
+  if (U && !aligned(U, 16)) return fail(QWM_ERR_ARG, "U not 16-byte aligned");
+  if (diag && !aligned(diag, 8)) return fail(QWM_ERR_ARG, "diag misaligned");
+  s = check_packed(out, k, true, (flags & QWM_PSAC) && U);
+  if (s != QWM_OK) return s;
+  s = check_ws(ws, ws_bytes, select_ws_bytes(k->T, k->H, false));
+  if (s != QWM_OK) return s;
+  return launch_keys(k, centroids, w, U, (flags & QWM_QSAC) ? M : 1, flags, out, diag, ws,
+                     static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_quantize_values(const qwm_tokens* v, const uint16_t* centroids, const qwm_packed* out,
+                               qwm_diag* diag, void* ws, size_t ws_bytes, qwm_stream stream) {
+  qwm_status s = check_tokens(v, "values", false);
+  if (s != QWM_OK) return s;
+  if (!centroids || !aligned(centroids, 16)) return fail(QWM_ERR_ARG, "centroids: null or not 16-byte aligned");
+  if (diag && !aligned(diag, 8)) return fail(QWM_ERR_ARG, "diag misaligned");
+  s = check_packed(out, v, false, false);
+  if (s != QWM_OK) return s;
+  s = check_ws(ws, ws_bytes, select_ws_bytes(v->T, v->H, false));
+  if (s != QWM_OK) return s;
+  return launch_values(v, centroids, out, diag, ws, static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
+                         float scale, float* out, float* lse, int32_t* top1, void* ws, size_t ws_bytes,
+                         qwm_stream stream) {
+  qwm_status s = check_tokens(q, "queries", false);
+  if (s != QWM_OK) return s;
+  if (!segs || !aligned(segs, 8)) return fail(QWM_ERR_ARG, "segments: null or misaligned device array");
+  if (n_segs < 1 || n_segs > 4096) return fail(QWM_ERR_ARG, "n_segs must be in [1, 4096]");
+  if (total_keys < 1) return fail(QWM_ERR_ARG, "total_keys must be positive");
+  if (!(scale > 0.0f) || !__builtin_isfinite(scale)) return fail(QWM_ERR_ARG, "scale must be finite and positive");
+  if (!out || !aligned(out, 16)) return fail(QWM_ERR_ARG, "out: null or not 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(QWM_ERR_ARG, "lse misaligned");
+  if (top1 && !aligned(top1, 4)) return fail(QWM_ERR_ARG, "top1 misaligned");
+  s = check_ws(ws, ws_bytes, attention_ws_bytes(total_keys, q->H, q->T));
+  if (s != QWM_OK) return s;
+  return launch_attention(q, segs, n_segs, total_keys, scale, out, lse, top1, ws, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

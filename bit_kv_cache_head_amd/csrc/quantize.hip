@@ -1,0 +1,956 @@
+// Centroid choice, INT2 residual codec, PSAC coefficients and the Lloyd
+// iteration (QuantWM Sec. 2 centroid-residual code, Sec. 4.1 QSAC, Sec. 4.2
+// PSAC; method steps (2)-(4); App. D.1 packed storage).
+//
+// Every token's centroid choice is computed from one MFMA GEMM of the token
+// against the per-head table m_j = bf16(-2 w (.) mu_j), augmented with
+// B_j = ||mu_j||_w^2 split over three bf16 columns, so that
+//     f_j ~ e_j = ||k - mu_j||_w^2 - ||k||_w^2
+// with a certified error |f_j - e_j| <= c (||k||_w^2 + B_j).  A token whose
+// choice the bound cannot certify (close runners-up, non-finite values) is
+// sent to an exact fp64 path; no result depends on the approximation.
+#include "common.hpp"
+
+namespace qwm {
+
+enum { MODE_ASSIGN = 0, MODE_VALUES = 1, MODE_KEYS = 2 };
+
+constexpr int SEL_TOK = 128;     // tokens per block pass (4 waves x 32)
+
+struct TablePrepArgs {
+  const uint16_t* mu;   // [H][256][128] bf16
+  const float* w;       // [H][128] or null (w = 1)
+  uint16_t* tbl;        // [H][256][128] bf16  (-2 w mu)
+  uint16_t* aug;        // [H][256][4]   bf16  (B hi, mid, lo, 0)
+  float* Bj;            // [H][256]
+  float* Bmax;          // [H]
+  double* Wg;           // [H][2]
+  int32_t* counter;     // fallback work counter (zeroed here)
+};
+
+// One block per head, thread j = centroid j.
+__global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
+  const int h = blockIdx.x, j = threadIdx.x;
+  __shared__ float ws[D];
+  __shared__ float bm[256];
+  if (j < D) ws[j] = a.w ? a.w[h * D + j] : 1.0f;
+  if (h == 0 && j == 0) *a.counter = 0;
+  __syncthreads();
+  const uint16_t* mj = a.mu + ((int64_t)h * NC + j) * D;
+  uint16_t* tj = a.tbl + ((int64_t)h * NC + j) * D;
+  double B = 0.0;
+  for (int c0 = 0; c0 < D; c0 += 8) {
+    u32x4 v = *reinterpret_cast<const u32x4*>(mj + c0);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t lo16 = v[e] & 0xFFFFu, hi16 = v[e] >> 16;
+      const float m0 = bf16_bits_to_f32(lo16), m1 = bf16_bits_to_f32(hi16);
+      const float w0 = ws[c0 + 2 * e], w1 = ws[c0 + 2 * e + 1];
+      B = fma((double)w0 * (double)m0, (double)m0, B);
+      B = fma((double)w1 * (double)m1, (double)m1, B);
+      const uint32_t t0 = f32_to_bf16_bits(-2.0f * w0 * m0);
+      const uint32_t t1 = f32_to_bf16_bits(-2.0f * w1 * m1);
+      o[e] = t0 | (t1 << 16);
+    }
+    *reinterpret_cast<u32x4*>(tj + c0) = o;
+  }
+  const uint32_t bh = f64_to_bf16_bits(B);
+  const double r1 = B - (double)bf16_bits_to_f32(bh);
+  const uint32_t bmid = f64_to_bf16_bits(r1);
+  const double r2 = r1 - (double)bf16_bits_to_f32(bmid);
+  const uint32_t blo = f64_to_bf16_bits(r2);
+  uint16_t* ag = a.aug + ((int64_t)h * NC + j) * 4;
+  ag[0] = (uint16_t)bh; ag[1] = (uint16_t)bmid; ag[2] = (uint16_t)blo; ag[3] = 0;
+  a.Bj[h * NC + j] = (float)B;
+  bm[j] = (float)B;
+  __syncthreads();
+  if (j == 0) {
+    float mx = 0.f;
+    for (int i = 0; i < NC; ++i) mx = fmaxf(mx, bm[i]);
+    a.Bmax[h] = mx * (1.0f + 1.0f / 65536.0f);
+    double s0 = 0.0, s1 = 0.0;
+    for (int c = 0; c < 64; ++c) s0 += (double)ws[c];
+    for (int c = 64; c < D; ++c) s1 += (double)ws[c];
+    a.Wg[2 * h] = s0;
+    a.Wg[2 * h + 1] = s1;
+  }
+}
+
+struct SelectArgs {
+  const void* x; int64_t T; int64_t st; int64_t sh;
+  const uint16_t* tbl; const uint16_t* aug; const float* Bj; const float* Bmax; const double* Wg;
+  const uint16_t* mu;   // [H][256][128]
+  const float* w;       // [H][128] or null
+  const uint16_t* U;    // [H][128][8] or null
+  int32_t M; uint32_t flags; float cb;  // cb: certified relative error coefficient
+  int32_t blocks_per_head;
+  // outputs
+  uint8_t* idx;         // [H][T] (assignment for MODE_ASSIGN)
+  uint8_t* codes; uint16_t* scale; uint8_t* zeros; int64_t zstride; int8_t* cq; uint16_t* cscale;
+  int32_t* counter; int32_t* worklist;
+  qwm_diag* diag;
+};
+
+struct SelShared {
+  uint16_t tbl[NC * D];        // swizzled: row j, 16-byte chunk c at (c ^ (j & 15))
+  uint16_t aug[NC][4];
+  float w[D];
+  uint16_t ut[R][D];           // U^T (bf16)
+  uint8_t codes[4][32][32];
+  uint8_t idx[4][32];
+  uint16_t scale[4][32][2];
+  uint8_t nib[4][32];
+  int8_t cq[4][32][R];
+  uint16_t cs[4][32];
+};
+
+__device__ __forceinline__ float pack_idx(float f, uint32_t j) {
+  return __uint_as_float((__float_as_uint(f) & 0xFFFFFF00u) | j);
+}
+
+// Thresholds of the INT2 code: q = #{k : r > tau'_k}, k = 1..3.
+struct GroupCodec {
+  float s;       // step (fp16 value)
+  int z;         // zero-point
+  float t1, t2, t3;
+  uint32_t sbits;
+};
+
+__device__ __forceinline__ GroupCodec make_codec(float lo, float hi, bool* sat) {
+  GroupCodec g;
+  const double Rg = (double)hi - (double)lo;
+  g.sbits = fp16_up_div(Rg, 3.0f, sat);
+  g.s = f16_bits_to_f32(g.sbits);
+  if (g.s == 0.0f) {
+    g.z = 0;
+    g.t1 = g.t2 = g.t3 = __uint_as_float(0x7F800000u);   // +inf: every code 0
+    return g;
+  }
+  int z = rne_quot(-lo, g.s);
+  z = z < 0 ? 0 : (z > 3 ? 3 : z);
+  g.z = z;
+  float t[3];
+#pragma unroll
+  for (int k = 1; k <= 3; ++k) {
+    const float tau = ((float)(k - z) - 0.5f) * g.s;        // exact
+    // rne rounds the tie r == tau up to k - z iff k - z is even
+    t[k - 1] = (((k - z) & 1) == 0) ? prev_float(tau) : tau;
+  }
+  g.t1 = t[0]; g.t2 = t[1]; g.t3 = t[2];
+  return g;
+}
+
+__device__ __forceinline__ uint32_t code_of(float r, const GroupCodec& g) {
+  return (uint32_t)(r > g.t1) + (uint32_t)(r > g.t2) + (uint32_t)(r > g.t3);
+}
+
+template <int MODE, bool F32>
+__global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
+  __shared__ SelShared sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hh = lane >> 5, ln = lane & 31;
+  const int h = blockIdx.y;
+  const bool use_qsac = (MODE == MODE_KEYS) && (a.flags & QWM_QSAC);
+  const bool use_psac = (MODE == MODE_KEYS) && (a.flags & QWM_PSAC) && a.U != nullptr;
+
+  // ---- stage the per-head table, weights and U^T ----
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.tbl + (int64_t)h * NC * D);
+    for (int e = tid; e < NC * 16; e += 256) {
+      const int j = e >> 4, c = e & 15;
+      reinterpret_cast<u32x4*>(sm.tbl)[j * 16 + (c ^ (j & 15))] = src[e];
+    }
+    const uint2* asrc = reinterpret_cast<const uint2*>(a.aug + (int64_t)h * NC * 4);
+    reinterpret_cast<uint2*>(sm.aug)[tid] = asrc[tid];
+    if (tid < D) sm.w[tid] = a.w ? a.w[h * D + tid] : 1.0f;
+    if (use_psac) {
+      for (int e = tid; e < D * R; e += 256) sm.ut[e % R][e / R] = a.U[(int64_t)h * D * R + e];
+    }
+  }
+  __syncthreads();
+  const float Bmax = a.Bmax[h];
+  const double W0 = a.Wg[2 * h], W1 = a.Wg[2 * h + 1];
+  const float cb = a.cb;
+
+  const int64_t ntile = (a.T + SEL_TOK - 1) / SEL_TOK;
+  for (int64_t tile = blockIdx.x; tile < ntile; tile += a.blocks_per_head) {
+    const int64_t tok0 = tile * SEL_TOK + wv * 32;
+    const int64_t tok = tok0 + ln;
+    const bool valid = tok < a.T;
+    const int64_t rowoff = (int64_t)h * a.sh + (valid ? tok : 0) * a.st;
+
+    // ---- token fragments (B operand): channels 16 s + 8 hh + j ----
+    bf16x8 kb[8];
+    bf16x8 kl[8];
+    (void)kl;
+    if (!F32) {
+      const uint16_t* xr = static_cast<const uint16_t*>(a.x) + rowoff;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        u32x4 v = valid ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+        kb[s] = __builtin_bit_cast(bf16x8, v);
+      }
+    } else {
+      const float* xr = static_cast<const float*>(a.x) + rowoff;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        f32x4 v0 = valid ? *reinterpret_cast<const f32x4*>(xr + 16 * s + 8 * hh) : f32x4{0, 0, 0, 0};
+        f32x4 v1 = valid ? *reinterpret_cast<const f32x4*>(xr + 16 * s + 8 * hh + 4) : f32x4{0, 0, 0, 0};
+        u32x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float x0 = e ? v0[2] : v0[0], x1 = e ? v0[3] : v0[1];
+          const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
+          hi[e] = h0 | (h1 << 16);
+          lo[e] = f32_to_bf16_bits(x0 - bf16_bits_to_f32(h0)) | (f32_to_bf16_bits(x1 - bf16_bits_to_f32(h1)) << 16);
+          const float y0 = e ? v1[2] : v1[0], y1 = e ? v1[3] : v1[1];
+          const uint32_t g0 = f32_to_bf16_bits(y0), g1 = f32_to_bf16_bits(y1);
+          hi[2 + e] = g0 | (g1 << 16);
+          lo[2 + e] = f32_to_bf16_bits(y0 - bf16_bits_to_f32(g0)) | (f32_to_bf16_bits(y1 - bf16_bits_to_f32(g1)) << 16);
+        }
+        kb[s] = __builtin_bit_cast(bf16x8, hi);
+        kl[s] = __builtin_bit_cast(bf16x8, lo);
+      }
+    }
+    bf16x8 kaug;
+    {
+      u32x4 v = {0, 0, 0, 0};
+      if (hh == 0) { v[0] = 0x3F803F80u; v[1] = 0x3F80u; }   // (1, 1, 1, 0, ...)
+      kaug = __builtin_bit_cast(bf16x8, v);
+    }
+
+    // ---- distance GEMM, folded into (smallest, second smallest) per lane ----
+    float min1 = __builtin_inff(), min2 = __builtin_inff();
+#pragma unroll 1
+    for (int ct = 0; ct < 8; ++ct) {
+      f32x16 acc = {};
+      const int j = 32 * ct + ln;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int c = 2 * s + hh;
+        const bf16x8 af = reinterpret_cast<const bf16x8*>(sm.tbl)[j * 16 + (c ^ (j & 15))];
+        acc = mfma_bf16(af, kb[s], acc);
+        if (F32) acc = mfma_bf16(af, kl[s], acc);
+      }
+      {
+        u32x4 v = {0, 0, 0, 0};
+        if (hh == 0) { const uint2 g = reinterpret_cast<const uint2*>(sm.aug)[j]; v[0] = g.x; v[1] = g.y; }
+        acc = mfma_bf16(__builtin_bit_cast(bf16x8, v), kaug, acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t jj = 32 * ct + c_row(i, hh);
+        const float pf = pack_idx(acc[i], jj);
+        min2 = __builtin_amdgcn_fmed3f(min1, min2, pf);
+        min1 = fminf(min1, pf);
+      }
+    }
+    {
+      const float o1 = swap32_f(min1), o2 = swap32_f(min2);
+      const float n2 = fminf(fmaxf(min1, o1), fminf(min2, o2));
+      min1 = fminf(min1, o1);
+      min2 = n2;
+    }
+    const uint32_t j1 = __float_as_uint(min1) & 0xFFu;
+
+    // ---- token norm A = sum_c w_c k_c^2 (fp32) ----
+    float A = 0.f;
+    if (!F32) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 v = __builtin_bit_cast(u32x4, kb[s]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = __uint_as_float(v[e] << 16), x1 = __uint_as_float(v[e] & 0xFFFF0000u);
+          const int c = 16 * s + 8 * hh + 2 * e;
+          A = fmaf(sm.w[c] * x0, x0, A);
+          A = fmaf(sm.w[c + 1] * x1, x1, A);
+        }
+      }
+    } else {
+      const float* xr = static_cast<const float*>(a.x) + rowoff;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = 16 * s + 8 * hh + e;
+          const float x = valid ? xr[c] : 0.f;
+          A = fmaf(sm.w[c] * x, x, A);
+        }
+    }
+    A += swap32_f(A);
+    const float A_hi = A * (1.0f + 1.0f / 32768.0f), A_lo = A * (1.0f - 1.0f / 32768.0f);
+    // certified bounds on d_Q(j) = A + e_j
+    const float f1 = __uint_as_float(__float_as_uint(min1) & 0xFFFFFF00u);
+    const float f2 = __uint_as_float(__float_as_uint(min2) & 0xFFFFFF00u);
+    const float upper1 = A_hi * (1.0f + cb) + f1 + cb * Bmax;
+    const float lower2 = A_lo * (1.0f - cb) + f2 - cb * Bmax;
+
+    bool fast = valid && __builtin_isfinite(min1) && __builtin_isfinite(A) && __builtin_isfinite(upper1);
+
+    if (MODE == MODE_ASSIGN) {
+      fast = fast && (lower2 > upper1);
+      if (valid && hh == 0) {
+        if (fast) {
+          sm.idx[wv][ln] = (uint8_t)j1;
+        } else {
+          const int slot = atomicAdd(a.counter, 1);
+          a.worklist[slot] = (int32_t)((int64_t)h * a.T + tok);
+          sm.idx[wv][ln] = 0;
+        }
+      }
+    } else {
+      // ---- residual against the first candidate ----
+      float r[64];
+      const uint16_t* mj = a.mu + ((int64_t)h * NC + j1) * D;
+      float lo0 = 0.f, hi0 = 0.f, lo1 = 0.f, hi1 = 0.f;
+      const float* xf = F32 ? static_cast<const float*>(a.x) + rowoff : nullptr;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 mv = *reinterpret_cast<const u32x4*>(mj + 16 * s + 8 * hh);
+        const u32x4 kv = __builtin_bit_cast(u32x4, kb[s]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t mw = mv[e >> 1], kw = kv[e >> 1];
+          const float m = (e & 1) ? __uint_as_float(mw & 0xFFFF0000u) : __uint_as_float(mw << 16);
+          float x;
+          if (F32) x = valid ? xf[16 * s + 8 * hh + e] : 0.f;
+          else x = (e & 1) ? __uint_as_float(kw & 0xFFFF0000u) : __uint_as_float(kw << 16);
+          const float rv = x - m;
+          r[8 * s + e] = rv;
+          if (s < 4) { lo0 = fminf(lo0, rv); hi0 = fmaxf(hi0, rv); }
+          else { lo1 = fminf(lo1, rv); hi1 = fmaxf(hi1, rv); }
+        }
+      }
+      lo0 = fminf(lo0, swap32_f(lo0)); hi0 = fmaxf(hi0, swap32_f(hi0));
+      lo1 = fminf(lo1, swap32_f(lo1)); hi1 = fmaxf(hi1, swap32_f(hi1));
+      const double R0 = (double)hi0 - (double)lo0, R1 = (double)hi1 - (double)lo1;
+      if (use_qsac) {
+        const double S1 = W0 * R0 * R0 + W1 * R1 * R1;
+        const double thr = fmax((double)upper1, S1 * (1.0 + 1.0 / 1048576.0));
+        fast = fast && __builtin_isfinite(S1) && ((double)lower2 > thr);
+      } else {
+        fast = fast && (lower2 > upper1);
+      }
+      bool sat0 = false, sat1 = false;
+      const GroupCodec g0 = make_codec(lo0, hi0, &sat0);
+      const GroupCodec g1 = make_codec(lo1, hi1, &sat1);
+      // codes: lane holds channels 16 s + 8 hh + e -> bytes 4 s + 2 hh (+1)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const GroupCodec& g = s < 4 ? g0 : g1;
+        uint32_t bits = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bits |= code_of(r[8 * s + e], g) << (2 * e);
+        if (valid) *reinterpret_cast<uint16_t*>(&sm.codes[wv][ln][4 * s + 2 * hh]) = (uint16_t)bits;
+        if (use_psac) {
+          // E = r - r_hat (exact in fp32), reuse r[] storage
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float q = (float)((bits >> (2 * e)) & 3u);
+            r[8 * s + e] = r[8 * s + e] - g.s * (q - (float)g.z);
+          }
+        }
+      }
+      if (use_psac && F32) {
+        // add the rounding error of r = fl32(k - mu) (TwoSum) so that E = k - mu - r_hat
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const u32x4 mv = *reinterpret_cast<const u32x4*>(mj + 16 * s + 8 * hh);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t mw = mv[e >> 1];
+            const float m = (e & 1) ? __uint_as_float(mw & 0xFFFF0000u) : __uint_as_float(mw << 16);
+            const float x = valid ? xf[16 * s + 8 * hh + e] : 0.f;
+            const float rr = x - m;
+            const float bv = rr - x;
+            const float err = (x - (rr - bv)) + (-m - bv);
+            r[8 * s + e] += err;
+          }
+        }
+      }
+      if (valid && hh == 0) {
+        if (fast) {
+          sm.idx[wv][ln] = (uint8_t)j1;
+          sm.scale[wv][ln][0] = (uint16_t)g0.sbits;
+          sm.scale[wv][ln][1] = (uint16_t)g1.sbits;
+          sm.nib[wv][ln] = (uint8_t)(g0.z | (g1.z << 2));
+          if ((sat0 || sat1) && a.diag) atomicAdd((unsigned long long*)&a.diag->scale_saturations,
+                                                  (unsigned long long)((int)sat0 + (int)sat1));
+        } else {
+          const int slot = atomicAdd(a.counter, 1);
+          a.worklist[slot] = (int32_t)((int64_t)h * a.T + tok);
+          sm.idx[wv][ln] = 0;
+          sm.nib[wv][ln] = 0;
+          sm.scale[wv][ln][0] = 0;
+          sm.scale[wv][ln][1] = 0;
+        }
+      }
+      if (MODE == MODE_KEYS) {
+        if (use_psac) {
+          // C = E U on MFMA: A = U^T (rows 0..7 valid), B = E split into 3 bf16 parts
+          f32x16 acc = {};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            bf16x8 uf;
+            if (ln < R) uf = *reinterpret_cast<const bf16x8*>(&sm.ut[ln][16 * s + 8 * hh]);
+            else uf = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+            u32x4 p0, p1, p2;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              uint32_t wlo[3], whi[3];
+#pragma unroll
+              for (int half = 0; half < 2; ++half) {
+                const float ev = r[8 * s + 2 * e2 + half];
+                const uint32_t b0 = f32_to_bf16_bits(ev);
+                const float rem1 = ev - bf16_bits_to_f32(b0);
+                const uint32_t b1 = f32_to_bf16_bits(rem1);
+                const float rem2 = rem1 - bf16_bits_to_f32(b1);
+                const uint32_t b2 = f32_to_bf16_bits(rem2);
+                if (half == 0) { wlo[0] = b0; wlo[1] = b1; wlo[2] = b2; }
+                else { whi[0] = b0; whi[1] = b1; whi[2] = b2; }
+              }
+              p0[e2] = wlo[0] | (whi[0] << 16);
+              p1[e2] = wlo[1] | (whi[1] << 16);
+              p2[e2] = wlo[2] | (whi[2] << 16);
+            }
+            acc = mfma_bf16(uf, __builtin_bit_cast(bf16x8, p0), acc);
+            acc = mfma_bf16(uf, __builtin_bit_cast(bf16x8, p1), acc);
+            acc = mfma_bf16(uf, __builtin_bit_cast(bf16x8, p2), acc);
+          }
+          // lane (token, hh) holds C[4 hh + 0..3] in acc[0..3]
+          float m = fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])), fmaxf(fabsf(acc[2]), fabsf(acc[3])));
+          m = fmaxf(m, swap32_f(m));
+          bool sat = false;
+          const uint32_t csb = fp16_up_div((double)m, 127.0f, &sat);
+          const float cs = f16_bits_to_f32(csb);
+          int8_t qv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            int qi = 0;
+            if (cs > 0.f) {
+              qi = rne_quot(acc[i], cs);
+              qi = qi < -127 ? -127 : (qi > 127 ? 127 : qi);
+            }
+            qv[i] = (int8_t)qi;
+          }
+          if (valid) {
+            *reinterpret_cast<uint32_t*>(&sm.cq[wv][ln][4 * hh]) =
+                (uint32_t)(uint8_t)qv[0] | ((uint32_t)(uint8_t)qv[1] << 8) |
+                ((uint32_t)(uint8_t)qv[2] << 16) | ((uint32_t)(uint8_t)qv[3] << 24);
+            if (hh == 0) sm.cs[wv][ln] = (uint16_t)csb;
+          }
+        } else if (valid) {
+          *reinterpret_cast<uint32_t*>(&sm.cq[wv][ln][4 * hh]) = 0u;
+          if (hh == 0) sm.cs[wv][ln] = 0;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- coalesced write-out of the wave's 32 tokens ----
+    {
+      const int64_t base = (int64_t)h * a.T + tok0;
+      const int nv = (int)((a.T - tok0) < 32 ? (a.T - tok0) : 32);   // tokens of this wave
+      if (nv > 0) {
+        if (lane < nv) a.idx[base + lane] = sm.idx[wv][lane];
+        if (MODE != MODE_ASSIGN) {
+          // codes: 32 bytes per token, 16 bytes per lane
+          {
+            const int t = lane >> 1, part = lane & 1;
+            if (t < nv)
+              *reinterpret_cast<u32x4*>(a.codes + (base + t) * 32 + 16 * part) =
+                  *reinterpret_cast<const u32x4*>(&sm.codes[wv][t][16 * part]);
+          }
+          if (lane < nv)
+            *reinterpret_cast<uint32_t*>(a.scale + (base + lane) * 2) =
+                *reinterpret_cast<const uint32_t*>(&sm.scale[wv][lane][0]);
+          // zeros: token pairs (tok0 is even)
+          if (2 * lane < nv) {
+            const uint8_t lo = sm.nib[wv][2 * lane];
+            const uint8_t hi = (2 * lane + 1 < nv) ? sm.nib[wv][2 * lane + 1] : 0;
+            a.zeros[(int64_t)h * a.zstride + (tok0 >> 1) + lane] = (uint8_t)(lo | (hi << 4));
+          }
+          if (MODE == MODE_KEYS) {
+            if (lane < nv) {
+              *reinterpret_cast<uint2*>(a.cq + (base + lane) * R) = *reinterpret_cast<const uint2*>(&sm.cq[wv][lane][0]);
+              a.cscale[base + lane] = sm.cs[wv][lane];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact path for the tokens the fast path did not certify: plain fp64 scoring
+// of all centroids, one wave per token.
+// ---------------------------------------------------------------------------
+template <int MODE, bool F32>
+__global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ double kx[4][D];
+  __shared__ double dq[4][NC];
+  const int count = *a.counter;
+  if (blockIdx.x == 0 && tid == 0 && a.diag && count > 0)
+    atomicAdd((unsigned long long*)&a.diag->exact_fallbacks, (unsigned long long)count);
+  const bool use_qsac = (MODE == MODE_KEYS) && (a.flags & QWM_QSAC);
+  const bool use_psac = (MODE == MODE_KEYS) && (a.flags & QWM_PSAC) && a.U != nullptr;
+  for (int item = blockIdx.x * 4 + wv; item < count; item += gridDim.x * 4) {
+    const int64_t id = a.worklist[item];
+    const int h = (int)(id / a.T);
+    const int64_t tok = id % a.T;
+    const int64_t rowoff = (int64_t)h * a.sh + tok * a.st;
+    // token row, 2 channels per lane
+    double x0, x1;
+    if (F32) {
+      const float* xr = static_cast<const float*>(a.x) + rowoff;
+      x0 = xr[2 * lane]; x1 = xr[2 * lane + 1];
+    } else {
+      const uint16_t* xr = static_cast<const uint16_t*>(a.x) + rowoff;
+      x0 = bf16_bits_to_f32(xr[2 * lane]); x1 = bf16_bits_to_f32(xr[2 * lane + 1]);
+    }
+    const int bad = __any(!(__builtin_isfinite(x0) && __builtin_isfinite(x1)));
+    const int64_t base = (int64_t)h * a.T + tok;
+    if (bad) {
+      if (MODE != MODE_ASSIGN) {
+        if (lane < 8) *reinterpret_cast<uint32_t*>(a.codes + base * 32 + 4 * lane) = 0u;
+        if (lane == 0) {
+          a.idx[base] = 0;
+          a.scale[base * 2] = 0; a.scale[base * 2 + 1] = 0;
+          if (MODE == MODE_KEYS) {
+            *reinterpret_cast<uint2*>(a.cq + base * R) = make_uint2(0u, 0u);
+            a.cscale[base] = 0;
+          }
+          if (a.diag) atomicAdd((unsigned long long*)&a.diag->nonfinite_rows, 1ull);
+        }
+      } else if (lane == 0) {
+        a.idx[base] = 0;
+        if (a.diag) atomicAdd((unsigned long long*)&a.diag->nonfinite_rows, 1ull);
+      }
+      continue;
+    }
+    kx[wv][2 * lane] = x0;
+    kx[wv][2 * lane + 1] = x1;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const bool wts = use_qsac && a.w != nullptr;
+    // d_Q for centroids lane + 64 q
+    for (int q = 0; q < 4; ++q) {
+      const int j = lane + 64 * q;
+      const uint16_t* mj = a.mu + ((int64_t)h * NC + j) * D;
+      double s = 0.0;
+      for (int c = 0; c < D; ++c) {
+        const double df = kx[wv][c] - (double)bf16_bits_to_f32(mj[c]);
+        const double wc = wts ? (double)a.w[h * D + c] : 1.0;
+        s = fma(wc * df, df, s);
+      }
+      dq[wv][j] = s;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    int win = 0;
+    if (!use_qsac) {
+      double bv = dq[wv][lane];
+      int bj = lane;
+      for (int q = 1; q < 4; ++q) {
+        const double v = dq[wv][lane + 64 * q];
+        if (v < bv) { bv = v; bj = lane + 64 * q; }
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        const double ov = __shfl_xor(bv, o, 64);
+        const int oj = __shfl_xor(bj, o, 64);
+        if (ov < bv || (ov == bv && oj < bj)) { bv = ov; bj = oj; }
+      }
+      win = bj;
+    } else {
+      const double Wa = a.Wg[2 * h], Wb = a.Wg[2 * h + 1];
+      double bestS = __builtin_inf();
+      int bestj = 0;
+      // M rounds of (d_Q, j) selection
+      for (int m = 0; m < a.M; ++m) {
+        double bv = __builtin_inf();
+        int bj = NC;
+        for (int q = 0; q < 4; ++q) {
+          const int j = lane + 64 * q;
+          const double v = dq[wv][j];
+          if (v < bv || (v == bv && j < bj)) { bv = v; bj = j; }
+        }
+        for (int o = 32; o > 0; o >>= 1) {
+          const double ov = __shfl_xor(bv, o, 64);
+          const int oj = __shfl_xor(bj, o, 64);
+          if (ov < bv || (ov == bv && oj < bj)) { bv = ov; bj = oj; }
+        }
+        if (bj >= NC) break;
+        // remove it from the pool
+        if (lane == (bj & 63)) dq[wv][bj] = __builtin_inf();
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        // S for candidate bj: lanes 0..31 group 0, 32..63 group 1
+        const uint16_t* mj = a.mu + ((int64_t)h * NC + bj) * D;
+        float rlo = 0.f, rhi = 0.f;
+        {
+          const float m0 = bf16_bits_to_f32(mj[2 * lane]), m1 = bf16_bits_to_f32(mj[2 * lane + 1]);
+          const float r0 = (float)x0 - m0, r1 = (float)x1 - m1;
+          rlo = fminf(fminf(r0, r1), 0.f);
+          rhi = fmaxf(fmaxf(r0, r1), 0.f);
+        }
+        for (int o = 16; o > 0; o >>= 1) {
+          rlo = fminf(rlo, __shfl_xor(rlo, o, 64));
+          rhi = fmaxf(rhi, __shfl_xor(rhi, o, 64));
+        }
+        const double Rg = (double)rhi - (double)rlo;
+        const double Ra = __shfl(Rg, 0, 64), Rb = __shfl(Rg, 32, 64);
+        const double S = Wa * Ra * Ra + Wb * Rb * Rb;
+        if (S < bestS || (S == bestS && bj < bestj)) { bestS = S; bestj = bj; }
+      }
+      win = bestj;
+    }
+    if (MODE == MODE_ASSIGN) {
+      if (lane == 0) a.idx[base] = (uint8_t)win;
+      continue;
+    }
+    // codec for the winner
+    const uint16_t* mw = a.mu + ((int64_t)h * NC + win) * D;
+    const float m0 = bf16_bits_to_f32(mw[2 * lane]), m1 = bf16_bits_to_f32(mw[2 * lane + 1]);
+    const float r0 = (float)x0 - m0, r1 = (float)x1 - m1;
+    float rlo = fminf(fminf(r0, r1), 0.f), rhi = fmaxf(fmaxf(r0, r1), 0.f);
+    for (int o = 16; o > 0; o >>= 1) {
+      rlo = fminf(rlo, __shfl_xor(rlo, o, 64));
+      rhi = fmaxf(rhi, __shfl_xor(rhi, o, 64));
+    }
+    bool sat = false;
+    const GroupCodec g = make_codec(rlo, rhi, &sat);   // lanes 0..31: group 0, 32..63: group 1
+    const uint32_t q0 = code_of(r0, g), q1 = code_of(r1, g);
+    // byte b = channels 4b..4b+3 = lanes 2b, 2b+1
+    const uint32_t pair = q0 | (q1 << 2);
+    const uint32_t other = __shfl_xor(pair, 1, 64);
+    if ((lane & 1) == 0) a.codes[base * 32 + (lane >> 1)] = (uint8_t)(pair | (other << 4));
+    const uint32_t sb0 = __shfl(g.sbits, 0, 64), sb1 = __shfl(g.sbits, 32, 64);
+    const int z0 = __shfl(g.z, 0, 64), z1 = __shfl(g.z, 32, 64);
+    const int nsat = __popcll(__ballot(sat && ((lane & 31) == 0)));
+    if (lane == 0) {
+      a.idx[base] = (uint8_t)win;
+      a.scale[base * 2] = (uint16_t)sb0;
+      a.scale[base * 2 + 1] = (uint16_t)sb1;
+      const uint32_t nib = (uint32_t)(z0 | (z1 << 2));
+      uint8_t* zb = a.zeros + (int64_t)h * a.zstride + (tok >> 1);
+      uint32_t* word = reinterpret_cast<uint32_t*>(reinterpret_cast<uintptr_t>(zb) & ~(uintptr_t)3);
+      const int sh = 8 * (int)(reinterpret_cast<uintptr_t>(zb) & 3) + 4 * (int)(tok & 1);
+      atomicOr(word, nib << sh);
+      if (nsat && a.diag) atomicAdd((unsigned long long*)&a.diag->scale_saturations, (unsigned long long)nsat);
+    }
+    if (MODE == MODE_KEYS) {
+      int8_t* cq = a.cq + base * R;
+      if (use_psac) {
+        // E = k - mu - r_hat in fp64 (exact), C = E U in fp64
+        const double e0 = x0 - (double)m0 - (double)g.s * (double)((int)q0 - g.z);
+        const double e1 = x1 - (double)m1 - (double)g.s * (double)((int)q1 - g.z);
+        const uint16_t* Uh = a.U + (int64_t)h * D * R;
+        double C[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          double v = e0 * (double)bf16_bits_to_f32(Uh[(2 * lane) * R + i]) +
+                     e1 * (double)bf16_bits_to_f32(Uh[(2 * lane + 1) * R + i]);
+          C[i] = wave_sum_d(v);
+        }
+        double m = 0.0;
+#pragma unroll
+        for (int i = 0; i < R; ++i) m = fmax(m, fabs(C[i]));
+        bool s2 = false;
+        const uint32_t csb = fp16_up_div(m, 127.0f, &s2);
+        const double cs = (double)f16_bits_to_f32(csb);
+        if (lane < R) {
+          int qi = 0;
+          if (cs > 0.0) {
+            // round half to even of C / cs, decided with exact products (n +- 1/2) cs
+            double Ci = C[0];
+#pragma unroll
+            for (int i = 1; i < R; ++i) if (lane == i) Ci = C[i];
+            double n = rint(Ci / cs);
+            if (Ci > (n + 0.5) * cs) n += 1.0;
+            if (Ci < (n - 0.5) * cs) n -= 1.0;
+            int ni = (int)n;
+            if (Ci == (n + 0.5) * cs && (ni & 1)) ni += 1;
+            else if (Ci == (n - 0.5) * cs && (ni & 1)) ni -= 1;
+            qi = ni < -127 ? -127 : (ni > 127 ? 127 : ni);
+          }
+          cq[lane] = (int8_t)qi;
+        }
+        if (lane == 0) a.cscale[base] = (uint16_t)csb;
+      } else {
+        if (lane < R) cq[lane] = 0;
+        if (lane == 0) a.cscale[base] = 0;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Lloyd: Forgy seeding and the deterministic mean update.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t splitmix_next(uint64_t& state) {
+  state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// perm [H][T] int32 workspace.  Grid H, 256 threads.
+__global__ __launch_bounds__(256) void forgy_kernel(const void* x, int32_t dtype, int64_t T, int64_t st, int64_t sh,
+                                                    uint64_t seed, int32_t* perm, uint16_t* out) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  int32_t* p = perm + (int64_t)h * T;
+  for (int64_t i = tid; i < T; i += 256) p[i] = (int32_t)i;
+  __syncthreads();
+  __shared__ int32_t pick[NC];
+  if (tid == 0) {
+    uint64_t state = seed + ((uint64_t)h << 32);
+    for (int i = 0; i < NC; ++i) {
+      const uint64_t r = splitmix_next(state);
+      const int64_t j = i + (int64_t)(r % (uint64_t)(T - i));
+      const int32_t t = p[i]; p[i] = p[j]; p[j] = t;
+      pick[i] = p[i];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < NC * D; e += 256) {
+    const int i = e / D, c = e % D;
+    const int64_t off = (int64_t)h * sh + (int64_t)pick[i] * st + c;
+    uint32_t b;
+    if (dtype == QWM_BF16) b = static_cast<const uint16_t*>(x)[off];
+    else b = f32_to_bf16_bits(static_cast<const float*>(x)[off]);
+    out[((int64_t)h * NC + i) * D + c] = (uint16_t)b;
+  }
+}
+
+// Block (g, h) owns clusters 8g .. 8g+7 of head h.  Members are visited in
+// token order, so the fp64 sums are deterministic.
+__global__ __launch_bounds__(256) void lloyd_update_kernel(const void* x, int32_t dtype, int64_t T, int64_t st,
+                                                           int64_t sh, const uint8_t* assign, const uint16_t* cin,
+                                                           uint16_t* cout) {
+  const int g = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ int32_t list[256];
+  __shared__ int32_t wcount[4][8];
+  __shared__ int32_t start[9];
+  const int k = tid >> 5, q = tid & 31;    // accumulator role: cluster k, channels 4q..4q+3
+  double sum[4] = {0.0, 0.0, 0.0, 0.0};
+  int64_t cnt = 0;
+  const uint8_t* ah = assign + (int64_t)h * T;
+  for (int64_t t0 = 0; t0 < T; t0 += 256) {
+    const int64_t t = t0 + tid;
+    const int rel = (t < T) ? (int)ah[t] - 8 * g : -1;
+    const bool mine = rel >= 0 && rel < 8;
+    int pos = 0;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint64_t m = __ballot(mine && rel == kk);
+      if (lane == 0) wcount[wv][kk] = __popcll(m);
+      if (mine && rel == kk) pos = __popcll(m & ((1ull << lane) - 1ull));
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int kk = 0; kk < 8; ++kk) {
+        start[kk] = acc;
+        for (int w2 = 0; w2 < 4; ++w2) acc += wcount[w2][kk];
+      }
+      start[8] = acc;
+    }
+    __syncthreads();
+    if (mine) {
+      int off = start[rel];
+      for (int w2 = 0; w2 < wv; ++w2) off += wcount[w2][rel];
+      list[off + pos] = (int32_t)t;
+    }
+    __syncthreads();
+    for (int e = start[k]; e < start[k + 1]; ++e) {
+      const int64_t tt = list[e];
+      const int64_t off = (int64_t)h * sh + tt * st + 4 * q;
+      if (dtype == QWM_BF16) {
+        const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + off);
+        sum[0] += (double)__uint_as_float(v.x << 16);
+        sum[1] += (double)__uint_as_float(v.x & 0xFFFF0000u);
+        sum[2] += (double)__uint_as_float(v.y << 16);
+        sum[3] += (double)__uint_as_float(v.y & 0xFFFF0000u);
+      } else {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + off);
+        sum[0] += (double)v[0]; sum[1] += (double)v[1]; sum[2] += (double)v[2]; sum[3] += (double)v[3];
+      }
+    }
+    cnt += start[k + 1] - start[k];
+    __syncthreads();
+  }
+  const int64_t j = 8 * g + k;
+  const uint16_t* src = cin + ((int64_t)h * NC + j) * D + 4 * q;
+  uint16_t* dst = cout + ((int64_t)h * NC + j) * D + 4 * q;
+  if (cnt > 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = (uint16_t)f64_to_bf16_bits(sum[e] / (double)cnt);
+  } else if (src != dst) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = src[e];
+  }
+}
+
+}  // namespace qwm
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+namespace qwm_host {
+using namespace qwm;
+
+struct SelWork {
+  uint16_t* tbl; uint16_t* aug; float* Bj; float* Bmax; double* Wg; int32_t* counter; int32_t* worklist;
+  uint8_t* assign; int32_t* perm;
+};
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd) {
+  size_t b = 0;
+  b += align256((size_t)H * NC * D * 2);
+  b += align256((size_t)H * NC * 4 * 2);
+  b += align256((size_t)H * NC * 4);
+  b += align256((size_t)H * 4);
+  b += align256((size_t)H * 2 * 8);
+  b += align256(16);
+  b += align256((size_t)H * T * 4);
+  if (lloyd) {
+    b += align256((size_t)H * T);
+    b += align256((size_t)H * T * 4);
+  }
+  return b;
+}
+
+static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd) {
+  char* p = static_cast<char*>(ws);
+  SelWork w{};
+  auto take = [&](size_t n) { char* r = p; p += align256(n); return r; };
+  w.tbl = reinterpret_cast<uint16_t*>(take((size_t)H * NC * D * 2));
+  w.aug = reinterpret_cast<uint16_t*>(take((size_t)H * NC * 4 * 2));
+  w.Bj = reinterpret_cast<float*>(take((size_t)H * NC * 4));
+  w.Bmax = reinterpret_cast<float*>(take((size_t)H * 4));
+  w.Wg = reinterpret_cast<double*>(take((size_t)H * 2 * 8));
+  w.counter = reinterpret_cast<int32_t*>(take(16));
+  w.worklist = reinterpret_cast<int32_t*>(take((size_t)H * T * 4));
+  if (lloyd) {
+    w.assign = reinterpret_cast<uint8_t*>(take((size_t)H * T));
+    w.perm = reinterpret_cast<int32_t*>(take((size_t)H * T * 4));
+  }
+  return w;
+}
+
+static int blocks_per_head(int64_t T, int32_t H) {
+  const int64_t ntile = (T + SEL_TOK - 1) / SEL_TOK;
+  int64_t want = (2 * 256 * 2 + H - 1) / H;   // about four blocks per CU overall
+  if (want < 1) want = 1;
+  return (int)(ntile < want ? ntile : want);
+}
+
+template <int MODE>
+static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t stream, const char* what) {
+  const int bph = blocks_per_head(x->T, x->H);
+  a.blocks_per_head = bph;
+  if (x->dtype == QWM_BF16)
+    hipLaunchKernelGGL((select_kernel<MODE, false>), dim3(bph, x->H), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((select_kernel<MODE, true>), dim3(bph, x->H), dim3(256), 0, stream, a);
+  qwm_status s = check_launch(what);
+  if (s != QWM_OK) return s;
+  const int fb = 64;
+  if (x->dtype == QWM_BF16)
+    hipLaunchKernelGGL((fallback_kernel<MODE, false>), dim3(fb), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fallback_kernel<MODE, true>), dim3(fb), dim3(256), 0, stream, a);
+  return check_launch(what);
+}
+
+static void fill_common(SelectArgs& a, const qwm_tokens* x, const SelWork& w, const uint16_t* mu) {
+  a.x = x->ptr; a.T = x->T; a.st = x->stride_t; a.sh = x->stride_h;
+  a.tbl = w.tbl; a.aug = w.aug; a.Bj = w.Bj; a.Bmax = w.Bmax; a.Wg = w.Wg;
+  a.mu = mu; a.counter = w.counter; a.worklist = w.worklist;
+}
+
+static qwm_status prep(const SelWork& w, const uint16_t* mu, const float* wts, int32_t H, hipStream_t stream) {
+  TablePrepArgs p{mu, wts, w.tbl, w.aug, w.Bj, w.Bmax, w.Wg, w.counter};
+  hipLaunchKernelGGL(prep_table_kernel, dim3(H), dim3(256), 0, stream, p);
+  return check_launch("centroid table preparation");
+}
+
+// Certified relative error coefficient of the GEMM distances: bf16 rounding of
+// w * mu (2^-9 per term, counted twice), fp32 accumulation, the 8 index bits
+// packed into each value (2^-15), the bf16 split of B_j; plus slack.
+static float error_coeff(bool weighted) {
+  return weighted ? (1.0f / 256.0f + 1.0f / 4096.0f) : (1.0f / 4096.0f);
+}
+
+qwm_status launch_keys(const qwm_tokens* k, const uint16_t* centroids, const float* w, const uint16_t* U,
+                       int32_t M, uint32_t flags, const qwm_packed* out, qwm_diag* diag, void* ws,
+                       hipStream_t stream) {
+  SelWork wk = carve(ws, k->T, k->H, false);
+  const bool qsac = flags & QWM_QSAC;
+  const float* wts = qsac ? w : nullptr;
+  qwm_status s = prep(wk, centroids, wts, k->H, stream);
+  if (s != QWM_OK) return s;
+  SelectArgs a{};
+  fill_common(a, k, wk, centroids);
+  a.w = wts; a.U = (flags & QWM_PSAC) ? U : nullptr; a.M = M; a.flags = flags;
+  a.cb = error_coeff(wts != nullptr);
+  a.idx = out->idx; a.codes = out->codes; a.scale = out->scale; a.zeros = out->zeros;
+  a.zstride = zeros_stride(k->T); a.cq = out->c; a.cscale = out->c_scale; a.diag = diag;
+  return run_select<MODE_KEYS>(k, a, stream, "key quantization");
+}
+
+qwm_status launch_values(const qwm_tokens* v, const uint16_t* centroids, const qwm_packed* out, qwm_diag* diag,
+                         void* ws, hipStream_t stream) {
+  SelWork wk = carve(ws, v->T, v->H, false);
+  qwm_status s = prep(wk, centroids, nullptr, v->H, stream);
+  if (s != QWM_OK) return s;
+  SelectArgs a{};
+  fill_common(a, v, wk, centroids);
+  a.w = nullptr; a.U = nullptr; a.M = 1; a.flags = 0; a.cb = error_coeff(false);
+  a.idx = out->idx; a.codes = out->codes; a.scale = out->scale; a.zeros = out->zeros;
+  a.zstride = zeros_stride(v->T); a.cq = nullptr; a.cscale = nullptr; a.diag = diag;
+  return run_select<MODE_VALUES>(v, a, stream, "value quantization");
+}
+
+qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const uint16_t* init, uint16_t* centroids,
+                        qwm_diag* diag, void* ws, hipStream_t stream) {
+  SelWork wk = carve(ws, x->T, x->H, true);
+  const uint16_t* cur = init;
+  if (init == nullptr) {
+    hipLaunchKernelGGL(forgy_kernel, dim3(x->H), dim3(256), 0, stream, x->ptr, x->dtype, x->T, x->stride_t,
+                       x->stride_h, seed, wk.perm, centroids);
+    qwm_status s = check_launch("centroid seeding");
+    if (s != QWM_OK) return s;
+    cur = centroids;
+  }
+  if (iters == 0 && init != nullptr && init != centroids) {
+    if (hipMemcpyAsync(centroids, init, (size_t)x->H * NC * D * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return check_launch("centroid copy");
+    return QWM_OK;
+  }
+  for (int it = 0; it < iters; ++it) {
+    qwm_status s = prep(wk, cur, nullptr, x->H, stream);
+    if (s != QWM_OK) return s;
+    SelectArgs a{};
+    fill_common(a, x, wk, cur);
+    a.M = 1; a.flags = 0; a.cb = error_coeff(false);
+    a.idx = wk.assign; a.diag = diag;
+    s = run_select<MODE_ASSIGN>(x, a, stream, "Lloyd assignment");
+    if (s != QWM_OK) return s;
+    hipLaunchKernelGGL(lloyd_update_kernel, dim3(NC / 8, x->H), dim3(256), 0, stream, x->ptr, x->dtype, x->T,
+                       x->stride_t, x->stride_h, wk.assign, cur, centroids);
+    s = check_launch("Lloyd update");
+    if (s != QWM_OK) return s;
+    cur = centroids;
+  }
+  return QWM_OK;
+}
+
+}  // namespace qwm_host

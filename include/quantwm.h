@@ -1,0 +1,198 @@
+/*
+ * quantwm.h — C ABI of libquantwm: the data-parallel hot path of QuantWM's
+ * training-free, strictly causal 2-bit KV cache (Zhao et al., "QuantWM:
+ * Temporally Consistent 2-Bit KV Cache Quantization for World Models and
+ * Video Generation", arXiv 2609.26425 v2), for AMD MI355X (gfx950).
+ *
+ * Conventions shared by every call
+ *  - Every buffer argument is DEVICE memory owned by the caller.  The library
+ *    never allocates, frees or keeps a pointer after a call returns.
+ *  - Every call validates its arguments on the host first (no HIP call is made
+ *    when validation fails), then only enqueues kernels on `stream` (a
+ *    hipStream_t; NULL = the default stream) and returns.  Results are ready
+ *    when the stream reaches that point.
+ *  - Return value: QWM_OK, or an error code; qwm_last_error() returns a
+ *    thread-local description of the last failure.  No exception crosses the
+ *    ABI.  Calls are reentrant; calls that share output or state buffers must
+ *    be ordered by the caller (same stream).
+ *  - Shapes: head dim d = 128, residual groups of 64 channels (G = 2),
+ *    n_c = 256 centroids, PSAC rank r = 8 (the configuration of the paper's
+ *    implementation details, Sec. 5.1 / App. D.1).
+ *  - bf16 and fp16 values travel as uint16_t bit patterns.
+ *  - Token tensors are [T][H][d] with element strides (channel stride 1).
+ *
+ * Packed chunk layout (one chunk of T tokens, H heads; qwm_packed):
+ *    codes   [H][T][d/4]  u8   INT2 residual codes, channel 4b+i in bits 2i..2i+1 of byte b
+ *    idx     [H][T]       u8   centroid index
+ *    scale   [H][T][G]    fp16 group step size s_g
+ *    zeros   [H][zstride] u8   zero-points: token t owns the 4-bit field z_0 | z_1 << 2
+ *                              in byte t/2 (low nibble for even t); zstride =
+ *                              qwm_zeros_stride(T) = ceil(T/2) rounded up to 4
+ *    c       [H][T][r]    i8   PSAC coefficients (keys only)
+ *    c_scale [H][T]       fp16 PSAC coefficient scale (keys only)
+ *  Dequantization: k0_hat_c = mu[idx]_c + s_g (q_c - z_g) (g = c / 64),
+ *                  k_hat = k0_hat + (c_scale * c) U^T,  v_hat = mu_v[idx] + s (q - z).
+ */
+#ifndef QUANTWM_H
+#define QUANTWM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QWM_ABI_VERSION 1
+#define QWM_HEAD_DIM 128
+#define QWM_GROUP 64
+#define QWM_CENTROIDS 256
+#define QWM_RANK 8
+
+typedef enum {
+  QWM_OK = 0,
+  QWM_ERR_ARG = 1,          /* null / misaligned pointer, bad shape or stride, bad value */
+  QWM_ERR_UNSUPPORTED = 2,  /* a shape this build does not implement (d, n_c, r, dtype) */
+  QWM_ERR_WORKSPACE = 3,    /* workspace missing or smaller than qwm_workspace_bytes() */
+  QWM_ERR_HIP = 4           /* a HIP launch failed; qwm_last_error() has the HIP text */
+} qwm_status;
+
+typedef enum { QWM_F32 = 0, QWM_BF16 = 1 } qwm_dtype;
+
+/* Key-quantization flags.  0 = nearest centroid only (the QVG-style baseline). */
+enum { QWM_QSAC = 1u, QWM_PSAC = 2u };
+
+/* Workspace-sizing operation ids for qwm_workspace_bytes(). */
+enum { QWM_OP_STATS = 0, QWM_OP_CENTROIDS = 1, QWM_OP_KEYS = 2, QWM_OP_VALUES = 3,
+       QWM_OP_ATTENTION = 4 };
+
+typedef void* qwm_stream; /* hipStream_t */
+
+/* A token tensor: element (t, h, c) at ptr + t*stride_t + h*stride_h + c. */
+typedef struct {
+  const void* ptr;   /* device; 16-byte aligned; rows of d elements contiguous */
+  int32_t dtype;     /* qwm_dtype */
+  int32_t H;         /* heads */
+  int32_t d;         /* channels per head, must be 128 */
+  int32_t reserved;
+  int64_t T;         /* tokens */
+  int64_t stride_t;  /* elements between consecutive tokens (multiple of 8) */
+  int64_t stride_h;  /* elements between consecutive heads (multiple of 8) */
+} qwm_tokens;
+
+/* Per-head Query statistics (QuantWM Sec. 4.1-4.2, App. C.3, App. D.1). */
+typedef struct {
+  double* S;        /* [H][d][d] running sum of q q^T (in/out) */
+  int64_t* n;       /* [H] Queries seen so far (in/out) */
+  float* w;         /* [H][d] channel sensitivity diag(S)/n, 1 while n == 0 (out) */
+  uint16_t* U;      /* [H][d][r] bf16 top-r eigenvectors of S/n (out; zero while n == 0) */
+  float* lambda;    /* [H][r] their eigenvalues, descending (out) */
+  float* energy;    /* [H] sum of the top-r eigenvalues / trace (out) */
+  int32_t* iters;   /* [H] eigen-iterations used, negative if not converged; may be NULL */
+  int32_t H, d, r, reserved;
+} qwm_qstats;
+
+/* One packed chunk (layout above).  c and c_scale are NULL for Values. */
+typedef struct {
+  uint8_t* codes;
+  uint8_t* idx;
+  uint16_t* scale;
+  uint8_t* zeros;
+  int8_t* c;
+  uint16_t* c_scale;
+  int64_t T;
+  int32_t H, r;
+} qwm_packed;
+
+/* Optional device-side counters (int64, accumulated with atomics). */
+typedef struct {
+  int64_t nonfinite_rows;     /* tokens with a NaN/Inf channel: stored as idx 0, codes 0 */
+  int64_t exact_fallbacks;    /* tokens whose centroid choice needed the exact (slow) path */
+  int64_t scale_saturations;  /* group ranges beyond 3 * 65504 (scale saturates) */
+  int64_t reserved;
+} qwm_diag;
+
+/* One cached chunk as read by qwm_attention.  Pointers address the whole
+ * chunk ([H][...] arrays); centroid tables are [H][256][d] bf16; U is
+ * [H][d][r] bf16 or NULL (no PSAC term: cold-start chunk or PSAC off). */
+typedef struct {
+  const uint8_t* k_codes; const uint8_t* k_idx; const uint16_t* k_scale; const uint8_t* k_zeros;
+  const int8_t* k_c; const uint16_t* k_c_scale;
+  const uint8_t* v_codes; const uint8_t* v_idx; const uint16_t* v_scale; const uint8_t* v_zeros;
+  const uint16_t* k_centroids; const uint16_t* v_centroids; const uint16_t* U;
+  int64_t T;
+} qwm_segment;
+
+/* Update the per-head Query statistics with the Queries q (T may be 0) and
+ * refresh w; with compute_basis != 0 also the principal basis U, lambda,
+ * energy (QuantWM method step (1) and (4); Sec. 4.2: M_h = (1/N) sum q q^T,
+ * w = diag(M_h), U_r = top-8 eigenvectors of M_h stored in BF16).
+ * S accumulates in fp64; q may be QWM_BF16 or QWM_F32.
+ * Eigenvector order: eigenvalue descending; sign: largest-|entry| positive.
+ * Workspace: qwm_workspace_bytes(QWM_OP_STATS, ...) bytes (0 today). */
+qwm_status qwm_update_query_stats(const qwm_tokens* q, const qwm_qstats* st, int32_t compute_basis,
+                                  void* ws, size_t ws_bytes, qwm_stream stream);
+
+/* Build a table of n_centroids BF16 centroids per head for the tokens x by
+ * `iters` Lloyd iterations (QVG's K-means, which QuantWM builds on: QuantWM
+ * Sec. 2; QVG Sec. 2A/2C).  init == NULL: Forgy start with 256 distinct
+ * tokens drawn by a SplitMix64-driven partial Fisher-Yates shuffle seeded with
+ * seed + (head << 32); otherwise warm start from init ([H][256][d] bf16, may
+ * equal centroids).  Assignment: nearest centroid (ties -> lowest index),
+ * exact; update: bf16(mean) computed in fp64; empty clusters keep their value.
+ * Output centroids [H][256][d] bf16.  Requires T >= 256 when init == NULL.
+ * Workspace: qwm_workspace_bytes(QWM_OP_CENTROIDS, T, H, ...). */
+qwm_status qwm_build_centroids(const qwm_tokens* x, int32_t n_centroids, int32_t iters, uint64_t seed,
+                               const uint16_t* init, uint16_t* centroids, qwm_diag* diag,
+                               void* ws, size_t ws_bytes, qwm_stream stream);
+
+/* Quantize one chunk of Keys (QuantWM Sec. 4.1 QSAC, Sec. 4.2 PSAC; method
+ * steps (2)-(4)).  flags & QWM_QSAC: Query-aware distance d_Q with weights w
+ * (NULL -> w = 1, the cold start), the M (1..256) nearest candidates by
+ * (d_Q, index), final choice by (S, index) with S = sum_g (sum_{c in g} w_c) R_g^2,
+ * R_g = max(0, max r) - min(0, min r) over the residual r = fl32(k - mu) in group g.
+ * Without QWM_QSAC: nearest centroid.  Codec: s_g = smallest fp16 with 3 s_g >= R_g,
+ * z_g = clamp(rne(-lo_g / s_g), 0, 3), q_c = clamp(rne(r_c / s_g) + z_g, 0, 3)
+ * (rne = round half to even of the exact quotient; s_g = 0 -> z = q = 0).
+ * flags & QWM_PSAC with U != NULL: E = k - k0_hat, C = E U ([d][r] bf16),
+ * c_scale = smallest fp16 with 127 c_scale >= max|C|, c = clamp(rne(C / c_scale),
+ * -127, 127); otherwise c = 0 and c_scale = 0.
+ * out->T must equal k->T and out->H k->H.  Workspace: QWM_OP_KEYS. */
+qwm_status qwm_quantize_keys(const qwm_tokens* k, const uint16_t* centroids, const float* w,
+                             const uint16_t* U, int32_t M, uint32_t flags, const qwm_packed* out,
+                             qwm_diag* diag, void* ws, size_t ws_bytes, qwm_stream stream);
+
+/* Quantize one chunk of Values: nearest centroid plus the INT2 codec above,
+ * no compensation (QuantWM Sec. 2 centroid-residual code; PSAC is Key-only).
+ * Workspace: QWM_OP_VALUES. */
+qwm_status qwm_quantize_values(const qwm_tokens* v, const uint16_t* centroids, const qwm_packed* out,
+                               qwm_diag* diag, void* ws, size_t ws_bytes, qwm_stream stream);
+
+/* Attention of the Queries q over every key of every segment (no mask):
+ * out = softmax(scale * (Q K0_hat^T + (Q U) (c_scale c)^T)) V_hat
+ * (the logit-side PSAC compensation of QuantWM's method section; the logits
+ * of Sec. 3.3 with scale = 1/sqrt(d)).
+ * segs: DEVICE array of n_segs descriptors (1 <= n_segs <= 4096), each with
+ * T >= 1 tokens; keys are numbered in segment order.
+ * out [Tq][H][d] fp32; lse [H][Tq] fp32 (natural log of the softmax
+ * denominator, may be NULL); top1 [H][Tq] int32 = argmax of the logits over
+ * all keys (may be NULL).  Workspace: QWM_OP_ATTENTION with T = total keys
+ * and n_segs = Tq (query count). */
+qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs,
+                         int64_t total_keys, float scale, float* out, float* lse, int32_t* top1,
+                         void* ws, size_t ws_bytes, qwm_stream stream);
+
+/* Bytes of workspace an operation needs (256-byte aligned pointer required).
+ * QWM_OP_ATTENTION: T = total cached keys, n = number of queries. */
+size_t qwm_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t n);
+
+/* Row stride of the zeros array for a chunk of T tokens. */
+int64_t qwm_zeros_stride(int64_t T);
+
+const char* qwm_last_error(void);
+int32_t qwm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QUANTWM_H */

@@ -1,0 +1,104 @@
+"""The C ABI: the library loads without a GPU, exports every declared symbol,
+and rejects bad arguments on the host before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "quantwm.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qwm_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    from bit_kv_cache_head_amd import _abi
+    declared = _declared()
+    assert declared, "no declarations found"
+    assert sorted(_abi.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(_abi.lib, name), name
+    assert _abi.lib.qwm_abi_version() == 1
+
+
+def test_struct_layouts_match_header_sizes():
+    from bit_kv_cache_head_amd import _abi
+    assert C.sizeof(_abi.Tokens) == 48
+    assert C.sizeof(_abi.QStats) == 72
+    assert C.sizeof(_abi.Packed) == 64
+    assert C.sizeof(_abi.Segment) == 112
+    assert C.sizeof(_abi.Diag) == 32
+
+
+def test_sizes_and_strides():
+    from bit_kv_cache_head_amd._abi import lib
+    assert lib.qwm_zeros_stride(1) == 4
+    assert lib.qwm_zeros_stride(8) == 4
+    assert lib.qwm_zeros_stride(9) == 8
+    assert lib.qwm_zeros_stride(1560) == 780
+    assert lib.qwm_workspace_bytes(0, 1560, 12, 0) == 0
+    k = lib.qwm_workspace_bytes(2, 1560, 12, 0)
+    assert k >= 12 * 256 * 128 * 2 + 12 * 1560 * 4
+    assert lib.qwm_workspace_bytes(1, 1560, 12, 0) > k          # Lloyd adds assignment + shuffle
+    assert lib.qwm_workspace_bytes(4, 64, 1, 16) == 0           # one split needs no workspace
+
+
+def _tok(ptr=0x1000, T=16, H=2, d=128, dtype=1, st=256, sh=128):
+    from bit_kv_cache_head_amd._abi import Tokens
+    return Tokens(C.c_void_p(ptr), dtype, H, d, 0, T, st, sh)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(d=64), 2), (dict(dtype=7), 2), (dict(H=0), 1), (dict(ptr=0), 1), (dict(ptr=0x1004), 1),
+    (dict(st=100), 1), (dict(T=-1), 1),
+])
+def test_key_argument_validation(case, code):
+    """Errors come back before any device access (pointers here are never dereferenced)."""
+    from bit_kv_cache_head_amd._abi import lib, Packed
+    t = _tok(**case)
+    out = Packed(C.c_void_p(0x2000), C.c_void_p(0x3000), C.c_void_p(0x4000), C.c_void_p(0x5000),
+                 C.c_void_p(0x6000), C.c_void_p(0x7000), t.T, t.H, 8)
+    st = lib.qwm_quantize_keys(C.byref(t), C.c_void_p(0x8000), None, None, 8, 3, C.byref(out), None,
+                               None, 0, None)
+    assert st == code
+    assert lib.qwm_last_error()
+
+
+def test_other_validation_paths():
+    from bit_kv_cache_head_amd._abi import lib, Packed, QStats
+    t = _tok()
+    out = Packed(C.c_void_p(0x2000), C.c_void_p(0x3000), C.c_void_p(0x4000), C.c_void_p(0x5000),
+                 C.c_void_p(0x6000), C.c_void_p(0x7000), t.T, t.H, 8)
+    # M out of range, unknown flags, workspace missing
+    assert lib.qwm_quantize_keys(C.byref(t), C.c_void_p(0x8000), None, None, 0, 1, C.byref(out), None,
+                                 None, 0, None) == 1
+    assert lib.qwm_quantize_keys(C.byref(t), C.c_void_p(0x8000), None, None, 8, 8, C.byref(out), None,
+                                 None, 0, None) == 1
+    assert lib.qwm_quantize_keys(C.byref(t), C.c_void_p(0x8000), None, None, 8, 3, C.byref(out), None,
+                                 None, 0, None) == 3
+    assert b"workspace" in lib.qwm_last_error()
+    # shape mismatch between tokens and packed chunk
+    bad = Packed(C.c_void_p(0x2000), C.c_void_p(0x3000), C.c_void_p(0x4000), C.c_void_p(0x5000),
+                 C.c_void_p(0x6000), C.c_void_p(0x7000), t.T + 1, t.H, 8)
+    assert lib.qwm_quantize_values(C.byref(t), C.c_void_p(0x8000), C.byref(bad), None, None, 0, None) == 1
+    # Lloyd: seeded start needs >= 256 tokens; centroid count must be 256
+    assert lib.qwm_build_centroids(C.byref(t), 256, 3, 0, None, C.c_void_p(0x9000), None, None, 0, None) == 1
+    assert lib.qwm_build_centroids(C.byref(t), 128, 3, 0, None, C.c_void_p(0x9000), None, None, 0, None) == 2
+    # stats: rank must be 8, H must match
+    qs = QStats(C.c_void_p(0x1000), C.c_void_p(0x2000), C.c_void_p(0x3000), C.c_void_p(0x4000),
+                C.c_void_p(0x5000), C.c_void_p(0x6000), None, t.H, 128, 4, 0)
+    assert lib.qwm_update_query_stats(C.byref(t), C.byref(qs), 1, None, 0, None) == 2
+    qs.r, qs.H = 8, 3
+    assert lib.qwm_update_query_stats(C.byref(t), C.byref(qs), 1, None, 0, None) == 1
+    # attention: segments, scale
+    assert lib.qwm_attention(C.byref(t), None, 1, 10, C.c_float(0.1), C.c_void_p(0x1000), None, None,
+                             None, 0, None) == 1
+    assert lib.qwm_attention(C.byref(t), C.c_void_p(0x1000), 0, 10, C.c_float(0.1), C.c_void_p(0x1000),
+                             None, None, None, 0, None) == 1
+    assert lib.qwm_attention(C.byref(t), C.c_void_p(0x1000), 1, 10, C.c_float(-1.0), C.c_void_p(0x1000),
+                             None, None, None, 0, None) == 1

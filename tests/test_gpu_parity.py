@@ -1,0 +1,442 @@
+"""GPU parity of every hot-path stage against the CPU oracle, on the same seeded
+inputs, through the C ABI.  Bars: bit-exact centroid indices, INT2 codes,
+scales and zero-points (mismatches allowed only at counted near-ties of
+relative gap < 1e-6); PSAC INT8 coefficients within +-1 LSB and their scale
+within one fp16 ulp; w within 1e-6 relative; U within one bf16 ulp; attention
+relative L2 <= 2e-3 against the oracle run on the same packed cache."""
+import sys
+
+import numpy as np
+import pytest
+
+import datagen
+from oracle import attention as OA
+from oracle import formats as F
+from oracle import lloyd as OL
+from oracle import quantize as Qz
+from oracle import stats as OS
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def qwm():
+    import torch
+    assert torch.cuda.is_available()
+    import bit_kv_cache_head_amd as q     # raises when the HIP library is missing
+    return q
+
+
+# ---------------------------------------------------------------------------
+# Query statistics and principal basis
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,dtype", [("480p", "bf16"), ("tiny", "f32")])
+def test_query_stats_and_basis(qwm, name, dtype):
+    import torch
+    from gpu_helpers import dev_tokens, host
+    _log(f"stats {name}")
+    w = datagen.make_workload(name, heads=[0, 1, 2] if name == "480p" else None, n_chunks=2, chunk=300,
+                              n_queries=None if name == "480p" else 333)
+    H = w.H
+    st = qwm.QueryStats(H)
+    # cold start: no Queries yet -> w = 1, no basis
+    qwm.update_query_stats(dev_tokens(w.Q[:0], dtype), st, compute_basis=True)
+    torch.cuda.synchronize()
+    assert torch.all(st.w == 1) and torch.all(st.n == 0) and torch.all(st.U.float() == 0)
+    Qs = [w.Q[:150], w.Q[150:]] if name == "480p" else [w.Q]
+    S = [np.zeros((128, 128)) for _ in range(H)]
+    n = [0] * H
+    for Qc in Qs:
+        qwm.update_query_stats(dev_tokens(Qc, dtype), st, compute_basis=True)
+        for h in range(H):
+            S[h], n[h] = OS.update(S[h], n[h], Qc[:, h])
+    torch.cuda.synchronize()
+    for h in range(H):
+        # Each 16-token MFMA partial is a sum of exact products rounded in fp32 before
+        # it is added in fp64: |dS_ij| <= gamma_16 sum_t |q_ti q_tj| <= gamma_16 sqrt(S_ii S_jj)
+        # (Cauchy-Schwarz), gamma_16 = 16u / (1 - 16u) < 1e-6 with u = 2^-24; fp32 Queries
+        # take the fp64 path (error ~1e-16).
+        gamma = 1e-6 if dtype == "bf16" else 1e-13
+        dS = np.abs(st.S[h].cpu().numpy() - S[h])
+        bound = gamma * np.sqrt(np.outer(np.diag(S[h]), np.diag(S[h])))
+        assert np.all(dS <= bound), float(np.max(dS / bound))
+        assert int(st.n[h]) == n[h]
+        np.testing.assert_allclose(st.w[h].cpu().numpy(), OS.channel_weights(S[h], n[h]), rtol=1e-6)
+        b = OS.principal_basis(S[h], n[h])
+        assert int(st.iters[h]) > 0, "eigen-iteration did not converge"
+        Ug = host(st.U[h])
+        ulp = np.ldexp(1.0, np.frexp(np.abs(b["U_bf16"]))[1] - 8)
+        assert np.all(np.abs(Ug - b["U_bf16"]) <= ulp), np.max(np.abs(Ug - b["U_bf16"]) / ulp)
+        np.testing.assert_allclose(st.lam[h].cpu().numpy(), b["lam"], rtol=1e-6)
+        assert abs(float(st.energy[h]) - b["energy"]) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Lloyd centroid tables
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,dtype,T", [("480p", "bf16", 777), ("tiny", "f32", 600)])
+def test_lloyd_tables(qwm, name, dtype, T):
+    import torch
+    from gpu_helpers import dev_tokens, dev_table, host
+    _log(f"lloyd {name} T={T}")
+    w = datagen.make_workload(name, heads=[0, 1] if name == "480p" else None, n_chunks=1, chunk=T)
+    X = w.K
+    H = w.H
+    seed = 1234
+    diag = qwm.new_diag()
+    Cg = qwm.build_centroids(dev_tokens(X, dtype), iters=4, seed=seed, diag=diag)
+    torch.cuda.synchronize()
+    for h in range(H):
+        Co = OL.lloyd(X[:, h].astype(np.float64), 256, 4, seed=seed, head=h)
+        np.testing.assert_array_equal(host(Cg[h]), Co)
+    # warm start from a given table, two more iterations
+    init = np.stack([OL.lloyd(X[:, h].astype(np.float64), 256, 1, seed=7, head=h) for h in range(H)])
+    Cw = qwm.build_centroids(dev_tokens(X, dtype), iters=2, init=dev_table(init), diag=diag)
+    torch.cuda.synchronize()
+    for h in range(H):
+        Co = OL.lloyd(X[:, h].astype(np.float64), 256, 2, init=init[h])
+        np.testing.assert_array_equal(host(Cw[h]), Co)
+    _log(f"  diag {diag.tolist()}")
+    assert int(diag[0]) == 0
+
+
+# ---------------------------------------------------------------------------
+# Key and value quantization
+# ---------------------------------------------------------------------------
+def _key_inputs(name, T, heads, seed=5):
+    w = datagen.make_workload(name, heads=heads, n_chunks=2, chunk=T,
+                              n_queries=None if name != "tiny" else 400)
+    K = w.K[T:2 * T] if name != "tiny" else w.K[:T]
+    H = w.H
+    tables, ws, Us = [], [], []
+    for h in range(H):
+        prev = w.K[:T, h].astype(np.float64)
+        tables.append(OL.lloyd(prev, 256, 3, seed=seed, head=h))
+        S, n = OS.update(np.zeros((128, 128)), 0, w.Q[: min(T, w.Q.shape[0]), h])
+        ws.append(OS.channel_weights(S, n))
+        Us.append(OS.principal_basis(S, n)["U_bf16"])
+    return w, K, np.stack(tables), np.stack(ws), np.stack(Us)
+
+
+@pytest.mark.parametrize("flags,M", [(3, 8), (1, 8), (2, 8), (0, 8), (3, 1), (3, 256)])
+def test_quantize_keys(qwm, flags, M):
+    import torch
+    from gpu_helpers import dev_tokens, dev_table, dev_basis, packed_host, idx_mismatches_allowed, compare_codec
+    _log(f"keys flags={flags} M={M}")
+    T = 777
+    w, K, Ct, wt, Ut = _key_inputs("480p", T, [0, 1])
+    H = w.H
+    diag = qwm.new_diag()
+    wdev = torch.from_numpy(wt).cuda()
+    out = qwm.quantize_keys(dev_tokens(K, "bf16"), dev_table(Ct), wdev, dev_basis(Ut), M=M, flags=flags,
+                            diag=diag)
+    torch.cuda.synchronize()
+    g = packed_host(out)
+    total_mis = 0
+    for h in range(H):
+        o = Qz.quantize_keys(K[:, h].astype(np.float64), Ct[h], wt[h], Ut[h], M=M, flags=flags)
+        kind = "qsac" if flags & 1 else "nearest"
+        nmis, nbad = idx_mismatches_allowed(kind, o, g["idx"][h], K[:, h], Ct[h], w=wt[h], M=M)
+        assert nbad == 0, f"head {h}: {nbad} centroid choices differ beyond near-ties"
+        total_mis += nmis
+        same = o["idx"] == g["idx"][h]
+        compare_codec(o, {k: v[h] for k, v in g.items()}, T, same)
+        if flags & 2:
+            dc = np.abs(g["c"][h].astype(np.int64) - o["Cq"].astype(np.int64))
+            assert dc[same].max() <= 1
+            gs = F.bits_to_fp16(g["c_scale_bits"][h])
+            os_ = o["c_scale"]
+            ulp = np.ldexp(1.0, np.frexp(np.maximum(os_, 6.1e-5))[1] - 11)
+            assert np.all(np.abs(gs - os_)[same] <= ulp[same])
+            _log(f"  head {h}: C exact {np.mean(dc[same] == 0):.5f}, c_scale exact {np.mean(gs[same] == os_[same]):.5f}")
+        else:
+            assert np.all(g["c"][h] == 0) and np.all(g["c_scale_bits"][h] == 0)
+    _log(f"  idx near-tie mismatches {total_mis}, diag {diag.tolist()}")
+
+
+def test_quantize_keys_cold_start_and_fp32(qwm):
+    """Chunk 0: w = 1 and no basis (PSAC inactive); fp32 tokens."""
+    import torch
+    from gpu_helpers import dev_tokens, dev_table, packed_host, idx_mismatches_allowed, compare_codec
+    T = 600
+    w, K, Ct, wt, Ut = _key_inputs("tiny", T, None)
+    out = qwm.quantize_keys(dev_tokens(K, "f32"), dev_table(Ct), None, None, M=8, flags=3)
+    torch.cuda.synchronize()
+    g = packed_host(out)
+    o = Qz.quantize_keys(K[:, 0].astype(np.float64), Ct[0], None, None, M=8, flags=3)
+    nmis, nbad = idx_mismatches_allowed("qsac", o, g["idx"][0], K[:, 0], Ct[0], None, 8)
+    assert nbad == 0
+    compare_codec(o, {k: v[0] for k, v in g.items()}, T, o["idx"] == g["idx"][0])
+    assert np.all(g["c"] == 0)
+    # fp32 with weights and PSAC
+    wdev = torch.from_numpy(wt).cuda()
+    from gpu_helpers import dev_basis
+    out = qwm.quantize_keys(dev_tokens(K, "f32"), dev_table(Ct), wdev, dev_basis(Ut), M=8, flags=3)
+    torch.cuda.synchronize()
+    g = packed_host(out)
+    o = Qz.quantize_keys(K[:, 0].astype(np.float64), Ct[0], wt[0], Ut[0], M=8, flags=3)
+    nmis, nbad = idx_mismatches_allowed("qsac", o, g["idx"][0], K[:, 0], Ct[0], wt[0], 8)
+    assert nbad == 0
+    same = o["idx"] == g["idx"][0]
+    compare_codec(o, {k: v[0] for k, v in g.items()}, T, same)
+    assert np.abs(g["c"][0].astype(int) - o["Cq"].astype(int))[same].max() <= 1
+
+
+@pytest.mark.parametrize("T", [777, 1, 64, 129])
+def test_quantize_values(qwm, T):
+    import torch
+    from gpu_helpers import dev_tokens, dev_table, packed_host, idx_mismatches_allowed, compare_codec
+    _log(f"values T={T}")
+    w = datagen.make_workload("480p", heads=[3, 4], n_chunks=2, chunk=max(T, 300))
+    V = w.V[-T:]
+    Ct = np.stack([OL.lloyd(w.V[:300, h].astype(np.float64), 256, 2, seed=9, head=h) for h in range(2)])
+    out = qwm.quantize_values(dev_tokens(V, "bf16"), dev_table(Ct))
+    torch.cuda.synchronize()
+    g = packed_host(out)
+    for h in range(2):
+        o = Qz.quantize_values(V[:, h].astype(np.float64), Ct[h])
+        nmis, nbad = idx_mismatches_allowed("nearest", o, g["idx"][h], V[:, h], Ct[h])
+        assert nbad == 0
+        compare_codec(o, {k: v[h] for k, v in g.items()}, T, o["idx"] == g["idx"][h])
+
+
+def test_nonfinite_and_degenerate_tokens(qwm):
+    import torch
+    from gpu_helpers import dev_tokens, dev_table, packed_host
+    w = datagen.make_workload("480p", heads=[0], n_chunks=1, chunk=300)
+    K = w.K.copy()
+    Ct = OL.lloyd(K[:, 0].astype(np.float64), 256, 2, seed=3, head=0)[None]
+    K[5, 0, 7] = np.nan
+    K[9, 0, 100] = np.inf
+    K[11, 0] = Ct[0, 17]            # exactly a centroid: zero residual, zero scales
+    diag = qwm.new_diag()
+    out = qwm.quantize_keys(dev_tokens(K, "bf16"), dev_table(Ct), None, None, M=8, flags=1, diag=diag)
+    torch.cuda.synchronize()
+    g = packed_host(out)
+    for t in (5, 9):
+        assert g["idx"][0, t] == 0 and np.all(g["codes"][0, t] == 0) and np.all(g["scale_bits"][0, t] == 0)
+    assert int(diag[0]) == 2
+    assert g["idx"][0, 11] == 17 and np.all(g["scale_bits"][0, 11] == 0) and np.all(g["codes"][0, 11] == 0)
+    z = F.unpack_zeros(g["zeros"][0, :150], 300)
+    assert np.all(z[11] == 0) and np.all(z[5] == 0)
+    o = Qz.quantize_keys(np.delete(K[:, 0], [5, 9], axis=0).astype(np.float64), Ct[0], None, None, M=8, flags=1)
+    keep = np.delete(np.arange(300), [5, 9])
+    np.testing.assert_array_equal(g["idx"][0, keep], o["idx"])
+
+
+# ---------------------------------------------------------------------------
+# Attention over the compressed cache
+# ---------------------------------------------------------------------------
+def _oracle_segments(w, chunk_sizes, heads):
+    """Quantize consecutive chunks with the oracle (its own tables, stats and
+    basis), returning per-segment per-head dicts and packed arrays."""
+    H = len(heads)
+    segs = []
+    S = [np.zeros((128, 128)) for _ in range(H)]
+    n = [0] * H
+    prevk = [None] * H
+    prevv = [None] * H
+    pos = 0
+    for ci, T in enumerate(chunk_sizes):
+        sl = slice(pos, pos + T)
+        per = []
+        for h in range(H):
+            Kc = w.K[sl, h].astype(np.float64)
+            Vc = w.V[sl, h].astype(np.float64)
+            iters = 2 if prevk[h] is not None else 3
+            if T >= 256 or prevk[h] is not None:
+                Ck = OL.lloyd(Kc, 256, iters, seed=21, head=h, init=prevk[h])
+                Cv = OL.lloyd(Vc, 256, iters, seed=22, head=h, init=prevv[h])
+            else:   # a first chunk shorter than the table: seed it from 256 later tokens
+                Ck = OL.lloyd(w.K[-256:, h].astype(np.float64), 256, 1, seed=21, head=h)
+                Cv = OL.lloyd(w.V[-256:, h].astype(np.float64), 256, 1, seed=22, head=h)
+            U = OS.principal_basis(S[h], n[h])["U_bf16"] if n[h] else None
+            kq = Qz.quantize_keys(Kc, Ck, OS.channel_weights(S[h], n[h]), U, M=8)
+            vq = Qz.quantize_values(Vc, Cv)
+            per.append(dict(k=kq, v=vq, Ck=Ck, Cv=Cv, U=U,
+                            oracle=dict(k_idx=kq["idx"], k_q=kq["q"], k_scale=kq["scale"], k_zero=kq["zero"],
+                                        k_Cq=kq["Cq"], k_cs=kq["c_scale"], k_centroids=Ck, U=U,
+                                        v_idx=vq["idx"], v_q=vq["q"], v_scale=vq["scale"], v_zero=vq["zero"],
+                                        v_centroids=Cv)))
+            S[h], n[h] = OS.update(S[h], n[h], w.Q[sl, h])
+            prevk[h], prevv[h] = Ck, Cv
+        segs.append(per)
+        pos += T
+    return segs
+
+
+def _upload_segments(qwm, segs, H):
+    import torch
+    from gpu_helpers import upload_packed, dev_table, dev_basis
+    keep = []
+    lst = []
+    for per in segs:
+        T = len(per[0]["k"]["idx"])
+        kp = upload_packed(qwm.PackedChunk, H, T, True, [p["k"] for p in per])
+        vp = upload_packed(qwm.PackedChunk, H, T, False, [p["v"] for p in per])
+        kc = dev_table(np.stack([p["Ck"] for p in per]))
+        vc = dev_table(np.stack([p["Cv"] for p in per]))
+        U = None if per[0]["U"] is None else dev_basis(np.stack([p["U"] for p in per]))
+        keep.append((kp, vp, kc, vc, U))
+        lst.append((kp, vp, kc, vc, U))
+    dseg, total = qwm.segments_tensor(lst)
+    return dseg, total, keep
+
+
+@pytest.mark.parametrize("want_top1,sizes", [(True, [300, 257, 64, 1, 130]), (False, [300, 257, 64, 1, 130]),
+                                              (True, [64, 1, 130])])
+def test_attention_on_oracle_cache(qwm, want_top1, sizes):
+    import torch
+    from gpu_helpers import dev_tokens
+    _log(f"attention oracle cache {sizes}")
+    w = datagen.make_workload("480p", heads=[0, 1], n_chunks=1, chunk=sum(sizes) + 256)
+    segs = _oracle_segments(w, sizes, [0, 1])
+    dseg, total, keep = _upload_segments(qwm, segs, 2)
+    Qv = w.Q[-200:]
+    out, lse, top1 = qwm.attention(dev_tokens(Qv, "bf16"), dseg, len(sizes), total, want_lse=True,
+                                   want_top1=want_top1)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for h in range(2):
+        O, L, top = OA.cache_attention(Qv[:, h].astype(np.float64), [s[h]["oracle"] for s in segs],
+                                       1 / np.sqrt(128))
+        err = np.linalg.norm(out[:, h] - O) / np.linalg.norm(O)
+        _log(f"  head {h}: rel L2 {err:.2e}")
+        assert err <= 2e-3
+        np.testing.assert_allclose(lse.cpu().numpy()[h], L, rtol=1e-4, atol=1e-4)
+        if want_top1:
+            _check_top1(top1.cpu().numpy()[h], top, Qv[:, h], segs, h)
+
+
+def _check_top1(gt, ot, Qh, segs, h):
+    """Top-1 agrees except where the oracle's top-2 logit gap is < 1e-3 relative."""
+    Ks = [OA.segment_kv(s[h]["oracle"])[0] for s in segs]
+    Kall = np.concatenate(Ks)
+    L = Qh.astype(np.float64) @ Kall.T
+    for i in np.nonzero(gt != ot)[0]:
+        a, b = L[i, ot[i]], L[i, gt[i]]
+        assert abs(a - b) <= 1e-3 * abs(a), (i, a, b)
+
+
+def test_attention_full_shape_random_cache(qwm):
+    """480p step shape: 25 segments x 1,560 keys, 1,560 queries, 12 heads, the
+    bench's launch configuration; seeded random packed cache; sampled queries."""
+    import torch
+    from gpu_helpers import dev_tokens, upload_packed, dev_table, dev_basis
+    _log("attention full shape")
+    rng = np.random.default_rng(77)
+    H, T, nseg, Tq = 12, 1560, 25, 1560
+    lst, oracle_segs = [], []
+    for s in range(nseg):
+        kh, vh, ors = [], [], []
+        Ck = F.bf16_rne(rng.standard_normal((H, 256, 128)) * 2)
+        Cv = F.bf16_rne(rng.standard_normal((H, 256, 128)) * 2)
+        U = None
+        if s > 0:
+            U = np.stack([F.bf16_rne(datagen.haar_orthogonal(rng, 128)[:, :8]) for _ in range(H)])
+        for h in range(H):
+            def one(keys):
+                q = rng.integers(0, 4, (T, 128)).astype(np.uint8)
+                z = rng.integers(0, 4, (T, 2)).astype(np.uint8)
+                sc = (rng.uniform(0.01, 0.2, (T, 2))).astype(np.float16).astype(np.float64)
+                d = dict(q=q, zero=z, scale=sc, idx=rng.integers(0, 256, T).astype(np.uint8),
+                         codes=F.pack_codes(q), zeros=F.pack_zeros(z), scale_bits=F.fp16_bits(sc))
+                if keys:
+                    d["Cq"] = rng.integers(-127, 128, (T, 8)).astype(np.int8)
+                    d["c_scale"] = rng.uniform(1e-4, 1e-3, T).astype(np.float16).astype(np.float64)
+                    d["c_scale_bits"] = F.fp16_bits(d["c_scale"])
+                return d
+            kq, vq = one(True), one(False)
+            kh.append(kq)
+            vh.append(vq)
+            ors.append(dict(k_idx=kq["idx"], k_q=kq["q"], k_scale=kq["scale"], k_zero=kq["zero"], k_Cq=kq["Cq"],
+                            k_cs=kq["c_scale"], k_centroids=Ck[h], U=None if U is None else U[h],
+                            v_idx=vq["idx"], v_q=vq["q"], v_scale=vq["scale"], v_zero=vq["zero"],
+                            v_centroids=Cv[h]))
+        kp = upload_packed(qwm.PackedChunk, H, T, True, kh)
+        vp = upload_packed(qwm.PackedChunk, H, T, False, vh)
+        lst.append((kp, vp, dev_table(Ck), dev_table(Cv), None if U is None else dev_basis(U)))
+        oracle_segs.append(ors)
+    dseg, total = qwm.segments_tensor(lst)
+    Qv = datagen.make_workload("480p", heads=list(range(H)), n_chunks=1, chunk=Tq).Q
+    out, lse, top1 = qwm.attention(dev_tokens(Qv, "bf16"), dseg, nseg, total, want_lse=True, want_top1=True)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    sample = np.array([0, 1, 127, 128, 777, 1535, 1536, 1559])
+    for h in (0, 5, 11):
+        O, L, top = OA.cache_attention(Qv[sample, h].astype(np.float64), [s[h] for s in oracle_segs],
+                                       1 / np.sqrt(128))
+        err = np.linalg.norm(out[sample, h] - O) / np.linalg.norm(O)
+        _log(f"  head {h}: rel L2 {err:.2e}")
+        assert err <= 2e-3
+        np.testing.assert_allclose(lse.cpu().numpy()[h, sample], L, rtol=1e-4, atol=1e-4)
+
+
+# ---------------------------------------------------------------------------
+# Streaming pipeline, end to end, and determinism
+# ---------------------------------------------------------------------------
+def test_streaming_pipeline_end_to_end(qwm):
+    """Three 300-token chunks, 2 heads: GPU pipeline (stats -> basis -> Lloyd ->
+    keys -> values -> attention) against the oracle pipeline from the same inputs."""
+    import torch
+    from gpu_helpers import dev_tokens, packed_host, host
+    _log("pipeline")
+    H, T, nch = 2, 300, 3
+    w = datagen.make_workload("480p", heads=[0, 1], n_chunks=nch, chunk=T)
+    st = qwm.QueryStats(H)
+    ref = _oracle_segments(w, [T] * nch, [0, 1])
+    gsegs = []
+    prev = (None, None)
+    for c in range(nch):
+        sl = w.chunk_slice(c)
+        K, V = dev_tokens(w.K[sl], "bf16"), dev_tokens(w.V[sl], "bf16")
+        if c == 0:
+            Ck = qwm.build_centroids(K, 3, seed=21)
+            Cv = qwm.build_centroids(V, 3, seed=22)
+            kp = qwm.quantize_keys(K, Ck, None, None, M=8, flags=3)
+            U = None
+        else:
+            Ck = qwm.build_centroids(K, 2, init=prev[0])
+            Cv = qwm.build_centroids(V, 2, init=prev[1])
+            U = st.U.clone()
+            kp = qwm.quantize_keys(K, Ck, st.w.clone(), U, M=8, flags=3)
+        vp = qwm.quantize_values(V, Cv)
+        qwm.update_query_stats(dev_tokens(w.Q[sl], "bf16"), st, compute_basis=True)
+        torch.cuda.synchronize()
+        for h in range(H):
+            np.testing.assert_array_equal(host(Ck[h]), ref[c][h]["Ck"])
+            np.testing.assert_array_equal(host(Cv[h]), ref[c][h]["Cv"])
+            gk = packed_host(kp)
+            assert np.mean(gk["idx"][h] == ref[c][h]["k"]["idx"]) == 1.0
+        gsegs.append((kp, vp, Ck, Cv, U))
+        prev = (Ck, Cv)
+    dseg, total = qwm.segments_tensor(gsegs)
+    Qv = w.Q[w.chunk_slice(nch - 1)]
+    out, _, _ = qwm.attention(dev_tokens(Qv, "bf16"), dseg, nch, total)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for h in range(H):
+        O, _, _ = OA.cache_attention(Qv[:, h].astype(np.float64), [s[h]["oracle"] for s in ref], 1 / np.sqrt(128))
+        assert np.linalg.norm(out[:, h] - O) / np.linalg.norm(O) <= 2e-3
+
+
+def test_determinism(qwm):
+    import torch
+    from gpu_helpers import dev_tokens, packed_host
+    w = datagen.make_workload("480p", heads=[0, 1, 2], n_chunks=1, chunk=1000)
+    K = dev_tokens(w.K, "bf16")
+    C1 = qwm.build_centroids(K, 3, seed=5)
+    C2 = qwm.build_centroids(K, 3, seed=5)
+    st = qwm.QueryStats(3)
+    qwm.update_query_stats(dev_tokens(w.Q, "bf16"), st)
+    a = packed_host(qwm.quantize_keys(K, C1, st.w, st.U, M=8, flags=3))
+    b = packed_host(qwm.quantize_keys(K, C2, st.w, st.U, M=8, flags=3))
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
