@@ -20,7 +20,8 @@ constexpr int SEL_TOK = 128;     // tokens per block pass (4 waves x 32)
 struct TablePrepArgs {
   const uint16_t* mu;   // [H][256][128] bf16
   const float* w;       // [H][128] or null (w = 1)
-  uint16_t* tbl;        // [H][256][128] bf16  (-2 w mu)
+  uint16_t* tbl;        // [H][256][128] bf16  (-2 w mu), rounded
+  uint16_t* tbl_lo;     // [H][256][128] bf16  remainder of -2 w mu (weighted tables only)
   uint16_t* aug;        // [H][256][4]   bf16  (B hi, mid, lo, 0)
   float* Bj;            // [H][256]
   float* Bmax;          // [H]
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
   double B = 0.0;
   for (int c0 = 0; c0 < D; c0 += 8) {
     u32x4 v = *reinterpret_cast<const u32x4*>(mj + c0);
-    u32x4 o;
+    u32x4 o, ol;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       uint32_t lo16 = v[e] & 0xFFFFu, hi16 = v[e] >> 16;
@@ -49,11 +50,14 @@ __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
       const float w0 = ws[c0 + 2 * e], w1 = ws[c0 + 2 * e + 1];
       B = fma((double)w0 * (double)m0, (double)m0, B);
       B = fma((double)w1 * (double)m1, (double)m1, B);
-      const uint32_t t0 = f32_to_bf16_bits(-2.0f * w0 * m0);
-      const uint32_t t1 = f32_to_bf16_bits(-2.0f * w1 * m1);
+      const float p0 = -2.0f * w0 * m0, p1 = -2.0f * w1 * m1;
+      const uint32_t t0 = f32_to_bf16_bits(p0);
+      const uint32_t t1 = f32_to_bf16_bits(p1);
       o[e] = t0 | (t1 << 16);
+      ol[e] = f32_to_bf16_bits(p0 - bf16_bits_to_f32(t0)) | (f32_to_bf16_bits(p1 - bf16_bits_to_f32(t1)) << 16);
     }
     *reinterpret_cast<u32x4*>(tj + c0) = o;
+    if (a.w) *reinterpret_cast<u32x4*>(a.tbl_lo + ((int64_t)h * NC + j) * D + c0) = ol;
   }
   const uint32_t bh = f64_to_bf16_bits(B);
   const double r1 = B - (double)bf16_bits_to_f32(bh);
@@ -79,7 +83,8 @@ __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
 
 struct SelectArgs {
   const void* x; int64_t T; int64_t st; int64_t sh;
-  const uint16_t* tbl; const uint16_t* aug; const float* Bj; const float* Bmax; const double* Wg;
+  const uint16_t* tbl; const uint16_t* tbl_lo; const uint16_t* aug; const float* Bj; const float* Bmax;
+  const double* Wg;
   const uint16_t* mu;   // [H][256][128]
   const float* w;       // [H][128] or null
   const uint16_t* U;    // [H][128][8] or null
@@ -92,9 +97,11 @@ struct SelectArgs {
   qwm_diag* diag;
 };
 
+template <bool WT>
 struct SelShared {
-  uint16_t tbl[NC * D];        // swizzled: row j, 16-byte chunk c at (c ^ (j & 15))
+  uint16_t tbl[WT ? 2 : 1][NC * D];   // swizzled: row j, 16-byte chunk c at (c ^ (j & 15)); [1] = remainder
   uint16_t aug[NC][4];
+  float bj[NC];
   float w[D];
   uint16_t ut[R][D];           // U^T (bf16)
   uint8_t codes[4][32][32];
@@ -145,23 +152,97 @@ __device__ __forceinline__ uint32_t code_of(float r, const GroupCodec& g) {
   return (uint32_t)(r > g.t1) + (uint32_t)(r > g.t2) + (uint32_t)(r > g.t3);
 }
 
-template <int MODE, bool F32>
-__global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
-  __shared__ SelShared sm;
+// Per-lane running list of the K smallest packed values (t[0] <= ... <= t[K-1]).
+template <int K>
+__device__ __forceinline__ void topk_insert(float (&t)[K], float x) {
+#pragma unroll
+  for (int k = K - 1; k >= 1; --k) t[k] = __builtin_amdgcn_fmed3f(t[k - 1], t[k], x);
+  t[0] = fminf(t[0], x);
+}
+
+__device__ __forceinline__ void cswap(float& x, float& y) {
+  const float lo = fminf(x, y), hi = fmaxf(x, y);
+  x = lo;
+  y = hi;
+}
+
+__device__ __forceinline__ float unpacked(float p) { return __uint_as_float(__float_as_uint(p) & 0xFFFFFF00u); }
+
+// Residual statistics of the token against centroid j over the lane's 64
+// channels (16 s + 8 hh + e): weighted squared distance and group ranges.
+struct ResidStats {
+  float d, lo0, hi0, lo1, hi1;
+};
+
+// token value of channel 16 s + 8 hh + e: from the packed bf16 fragment, or the fp32 copy
+template <bool F32>
+__device__ __forceinline__ float kval(const bf16x8 (&kb)[8], const float* kf, int s, int e) {
+  if (F32) return kf[8 * s + e];
+  const uint32_t w = __builtin_bit_cast(u32x4, kb[s])[e >> 1];
+  return (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+}
+
+template <bool F32, bool WEIGHTED>
+__device__ __forceinline__ ResidStats resid_stats(const bf16x8 (&kb)[8], const float* kf, const uint16_t* mj,
+                                                  int hh, const float* wsm) {
+  // Keep the unpacked token and the weights out of registers across calls:
+  // they are re-derived per candidate (cheap) instead of pinning 128 VGPRs.
+  asm volatile("" ::: "memory");
+  ResidStats o{0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    u32x4 kw = __builtin_bit_cast(u32x4, kb[s]);
+    asm volatile("" : "+v"(kw));
+    const u32x4 mv = *reinterpret_cast<const u32x4*>(mj + 16 * s + 8 * hh);
+    f32x4 w0 = {1.f, 1.f, 1.f, 1.f}, w1 = {1.f, 1.f, 1.f, 1.f};
+    if (WEIGHTED) {
+      w0 = *reinterpret_cast<const f32x4*>(wsm + 16 * s + 8 * hh);
+      w1 = *reinterpret_cast<const f32x4*>(wsm + 16 * s + 8 * hh + 4);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t mw = mv[e >> 1];
+      const float m = (e & 1) ? __uint_as_float(mw & 0xFFFF0000u) : __uint_as_float(mw << 16);
+      float x;
+      if (F32) x = kf[8 * s + e];
+      else x = (e & 1) ? __uint_as_float(kw[e >> 1] & 0xFFFF0000u) : __uint_as_float(kw[e >> 1] << 16);
+      const float r = x - m;
+      if (WEIGHTED) o.d = fmaf((e < 4 ? w0[e] : w1[e - 4]) * r, r, o.d);
+      else o.d = fmaf(r, r, o.d);
+      if (s < 4) { o.lo0 = fminf(o.lo0, r); o.hi0 = fmaxf(o.hi0, r); }
+      else { o.lo1 = fminf(o.lo1, r); o.hi1 = fmaxf(o.hi1, r); }
+    }
+  }
+  o.d += swap32_f(o.d);
+  o.lo0 = fminf(o.lo0, swap32_f(o.lo0)); o.hi0 = fmaxf(o.hi0, swap32_f(o.hi0));
+  o.lo1 = fminf(o.lo1, swap32_f(o.lo1)); o.hi1 = fmaxf(o.hi1, swap32_f(o.hi1));
+  return o;
+}
+
+constexpr float DREL = 1.0f / 65536.0f;   // relative error bound of the fp32 rescored distance
+
+// QS: QSAC selection (keys with the QSAC flag and M > 1); otherwise nearest.
+// WT: the table carries a bf16 remainder (weighted distances).
+template <int MODE, bool F32, bool QS, bool WT>
+__global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(SelectArgs a) {
+  constexpr int KT = QS ? 8 : 3;   // values tracked per lane (each lane holds half the centroids)
+  __shared__ SelShared<WT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hh = lane >> 5, ln = lane & 31;
   const int h = blockIdx.y;
-  const bool use_qsac = (MODE == MODE_KEYS) && (a.flags & QWM_QSAC);
   const bool use_psac = (MODE == MODE_KEYS) && (a.flags & QWM_PSAC) && a.U != nullptr;
 
   // ---- stage the per-head table, weights and U^T ----
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(a.tbl + (int64_t)h * NC * D);
+    const u32x4* srcl = reinterpret_cast<const u32x4*>(a.tbl_lo + (int64_t)h * NC * D);
     for (int e = tid; e < NC * 16; e += 256) {
       const int j = e >> 4, c = e & 15;
-      reinterpret_cast<u32x4*>(sm.tbl)[j * 16 + (c ^ (j & 15))] = src[e];
+      reinterpret_cast<u32x4*>(sm.tbl[0])[j * 16 + (c ^ (j & 15))] = src[e];
+      if (WT) reinterpret_cast<u32x4*>(sm.tbl[WT ? 1 : 0])[j * 16 + (c ^ (j & 15))] = srcl[e];
     }
     const uint2* asrc = reinterpret_cast<const uint2*>(a.aug + (int64_t)h * NC * 4);
     reinterpret_cast<uint2*>(sm.aug)[tid] = asrc[tid];
+    sm.bj[tid] = a.Bj[h * NC + tid] * (1.0f + 1.0f / 1048576.0f);   // upper bound of B_j
     if (tid < D) sm.w[tid] = a.w ? a.w[h * D + tid] : 1.0f;
     if (use_psac) {
       for (int e = tid; e < D * R; e += 256) sm.ut[e % R][e / R] = a.U[(int64_t)h * D * R + e];
@@ -171,6 +252,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
   const float Bmax = a.Bmax[h];
   const double W0 = a.Wg[2 * h], W1 = a.Wg[2 * h + 1];
   const float cb = a.cb;
+  const uint16_t* muh = a.mu + (int64_t)h * NC * D;
 
   const int64_t ntile = (a.T + SEL_TOK - 1) / SEL_TOK;
   for (int64_t tile = blockIdx.x; tile < ntile; tile += a.blocks_per_head) {
@@ -179,34 +261,32 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
     const bool valid = tok < a.T;
     const int64_t rowoff = (int64_t)h * a.sh + (valid ? tok : 0) * a.st;
 
-    // ---- token fragments (B operand): channels 16 s + 8 hh + j ----
+    // ---- token fragments (B operand) and fp32 copy: channels 16 s + 8 hh + e ----
     bf16x8 kb[8];
     bf16x8 kl[8];
-    (void)kl;
+    float kf[F32 ? 64 : 1];
     if (!F32) {
       const uint16_t* xr = static_cast<const uint16_t*>(a.x) + rowoff;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        u32x4 v = valid ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+        const u32x4 v = valid ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
         kb[s] = __builtin_bit_cast(bf16x8, v);
       }
     } else {
       const float* xr = static_cast<const float*>(a.x) + rowoff;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        f32x4 v0 = valid ? *reinterpret_cast<const f32x4*>(xr + 16 * s + 8 * hh) : f32x4{0, 0, 0, 0};
-        f32x4 v1 = valid ? *reinterpret_cast<const f32x4*>(xr + 16 * s + 8 * hh + 4) : f32x4{0, 0, 0, 0};
+        const f32x4 v0 = valid ? *reinterpret_cast<const f32x4*>(xr + 16 * s + 8 * hh) : f32x4{0, 0, 0, 0};
+        const f32x4 v1 = valid ? *reinterpret_cast<const f32x4*>(xr + 16 * s + 8 * hh + 4) : f32x4{0, 0, 0, 0};
         u32x4 hi, lo;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float x0 = e ? v0[2] : v0[0], x1 = e ? v0[3] : v0[1];
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = e < 2 ? v0[2 * e] : v1[2 * e - 4];
+          const float x1 = e < 2 ? v0[2 * e + 1] : v1[2 * e - 3];
+          if (F32) { kf[8 * s + 2 * e] = x0; kf[8 * s + 2 * e + 1] = x1; }
           const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
           hi[e] = h0 | (h1 << 16);
           lo[e] = f32_to_bf16_bits(x0 - bf16_bits_to_f32(h0)) | (f32_to_bf16_bits(x1 - bf16_bits_to_f32(h1)) << 16);
-          const float y0 = e ? v1[2] : v1[0], y1 = e ? v1[3] : v1[1];
-          const uint32_t g0 = f32_to_bf16_bits(y0), g1 = f32_to_bf16_bits(y1);
-          hi[2 + e] = g0 | (g1 << 16);
-          lo[2 + e] = f32_to_bf16_bits(y0 - bf16_bits_to_f32(g0)) | (f32_to_bf16_bits(y1 - bf16_bits_to_f32(g1)) << 16);
         }
         kb[s] = __builtin_bit_cast(bf16x8, hi);
         kl[s] = __builtin_bit_cast(bf16x8, lo);
@@ -219,8 +299,10 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
       kaug = __builtin_bit_cast(bf16x8, v);
     }
 
-    // ---- distance GEMM, folded into (smallest, second smallest) per lane ----
-    float min1 = __builtin_inff(), min2 = __builtin_inff();
+    // ---- distance GEMM; each lane keeps its KT smallest (value | index) ----
+    float t[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) t[k] = __builtin_inff();
 #pragma unroll 1
     for (int ct = 0; ct < 8; ++ct) {
       f32x16 acc = {};
@@ -228,9 +310,14 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int c = 2 * s + hh;
-        const bf16x8 af = reinterpret_cast<const bf16x8*>(sm.tbl)[j * 16 + (c ^ (j & 15))];
+        const bf16x8 af = reinterpret_cast<const bf16x8*>(sm.tbl[0])[j * 16 + (c ^ (j & 15))];
         acc = mfma_bf16(af, kb[s], acc);
         if (F32) acc = mfma_bf16(af, kl[s], acc);
+        if (WT) {
+          const bf16x8 al = reinterpret_cast<const bf16x8*>(sm.tbl[WT ? 1 : 0])[j * 16 + (c ^ (j & 15))];
+          acc = mfma_bf16(al, kb[s], acc);
+          if (F32) acc = mfma_bf16(al, kl[s], acc);
+        }
       }
       {
         u32x4 v = {0, 0, 0, 0};
@@ -238,61 +325,152 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
         acc = mfma_bf16(__builtin_bit_cast(bf16x8, v), kaug, acc);
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t jj = 32 * ct + c_row(i, hh);
-        const float pf = pack_idx(acc[i], jj);
-        min2 = __builtin_amdgcn_fmed3f(min1, min2, pf);
-        min1 = fminf(min1, pf);
-      }
+      for (int i = 0; i < 16; ++i) topk_insert<KT>(t, pack_idx(acc[i], 32 * ct + c_row(i, hh)));
     }
-    {
-      const float o1 = swap32_f(min1), o2 = swap32_f(min2);
-      const float n2 = fminf(fmaxf(min1, o1), fminf(min2, o2));
-      min1 = fminf(min1, o1);
-      min2 = n2;
+    // canonical per-token list: g[0..KT) = half 0, g[KT..2KT) = half 1 (identical on both lanes)
+    float g[2 * KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      const float o = swap32_f(t[k]);
+      g[k] = hh ? o : t[k];
+      g[KT + k] = hh ? t[k] : o;
     }
-    const uint32_t j1 = __float_as_uint(min1) & 0xFFu;
+    const float floor_unt = fminf(unpacked(g[KT - 1]), unpacked(g[2 * KT - 1]));   // every untracked value is >= this
+    float gmin = g[0];
+    int kmin = 0;
+    if (g[KT] < gmin) { gmin = g[KT]; kmin = KT; }
 
-    // ---- token norm A = sum_c w_c k_c^2 (fp32) ----
+    // ---- token norm A = sum_c w_c k_c^2 ----
     float A = 0.f;
-    if (!F32) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const u32x4 v = __builtin_bit_cast(u32x4, kb[s]);
+    for (int s = 0; s < 8; ++s)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = __uint_as_float(v[e] << 16), x1 = __uint_as_float(v[e] & 0xFFFF0000u);
-          const int c = 16 * s + 8 * hh + 2 * e;
-          A = fmaf(sm.w[c] * x0, x0, A);
-          A = fmaf(sm.w[c + 1] * x1, x1, A);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float x = kval<F32>(kb, kf, s, e);
+        A = fmaf(sm.w[16 * s + 8 * hh + e] * x, x, A);
       }
-    } else {
-      const float* xr = static_cast<const float*>(a.x) + rowoff;
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int c = 16 * s + 8 * hh + e;
-          const float x = valid ? xr[c] : 0.f;
-          A = fmaf(sm.w[c] * x, x, A);
-        }
-    }
     A += swap32_f(A);
     const float A_hi = A * (1.0f + 1.0f / 32768.0f), A_lo = A * (1.0f - 1.0f / 32768.0f);
-    // certified bounds on d_Q(j) = A + e_j
-    const float f1 = __uint_as_float(__float_as_uint(min1) & 0xFFFFFF00u);
-    const float f2 = __uint_as_float(__float_as_uint(min2) & 0xFFFFFF00u);
-    const float upper1 = A_hi * (1.0f + cb) + f1 + cb * Bmax;
-    const float lower2 = A_lo * (1.0f - cb) + f2 - cb * Bmax;
+    // certified bounds on d_Q(j) = A + e_j from the GEMM value f_j:
+    //   [lbA + f_j - cb B_j, ubA + f_j + cb B_j]
+    const float lbA = A_lo * (1.0f - cb), ubA = A_hi * (1.0f + cb);
+    const float L_unt = lbA + floor_unt - cb * Bmax;
+#define QWM_LB(pv) (lbA + unpacked(pv) - cb * sm.bj[__float_as_uint(pv) & 0xFFu])
+#define QWM_UB(pv) (ubA + unpacked(pv) + cb * sm.bj[__float_as_uint(pv) & 0xFFu])
 
-    bool fast = valid && __builtin_isfinite(min1) && __builtin_isfinite(A) && __builtin_isfinite(upper1);
+    bool fast = valid && __builtin_isfinite(gmin) && __builtin_isfinite(A) && __builtin_isfinite(ubA + cb * Bmax);
+    int win = (int)(__float_as_uint(gmin) & 0xFFu);
+    float wlo0 = 0.f, whi0 = 0.f, wlo1 = 0.f, whi1 = 0.f;   // group ranges of the winner
+    bool have_w = false;                                   // ranges known for the winner
+
+    if (!QS) {
+      // nearest centroid (weighted when QSAC runs with M == 1)
+      float c0 = g[0], c1 = g[1], c2 = g[2], c3 = g[KT], c4 = g[KT + 1], c5 = g[KT + 2];
+      cswap(c0, c3); cswap(c1, c4); cswap(c2, c5);
+      cswap(c1, c3); cswap(c2, c4);
+      cswap(c2, c3);
+      cswap(c3, c4);
+      cswap(c4, c5);
+      cswap(c3, c4);
+      const float ub0 = QWM_UB(c0);
+      const bool by_bounds = (QWM_LB(c1) > ub0) && (QWM_LB(c2) > ub0) && (QWM_LB(c3) > ub0) &&
+                             (QWM_LB(c4) > ub0) && (QWM_LB(c5) > ub0) && (L_unt > ub0);
+      float d1 = __builtin_inff();   // smallest rescored distance
+      const float cn[6] = {c0, c1, c2, c3, c4, c5};
+      float dn[6];
+      uint32_t evm = 0;
+#pragma unroll
+      for (int e = 0; e < 6; ++e) {
+        dn[e] = 0.f;
+        const bool need = fast && !by_bounds && (QWM_LB(cn[e]) <= d1 * (1.0f + DREL));
+        if (!__any(need)) continue;
+        const int j = (int)(__float_as_uint(cn[e]) & 0xFFu);
+        const ResidStats rs = resid_stats<F32, WT>(kb, kf, muh + (int64_t)j * D, hh, sm.w);
+        if (need) {
+          evm |= 1u << e;
+          dn[e] = rs.d;
+          if (!have_w || rs.d < d1 || (rs.d == d1 && j < win)) {
+            d1 = rs.d; win = j;
+            wlo0 = rs.lo0; whi0 = rs.hi0; wlo1 = rs.lo1; whi1 = rs.hi1; have_w = true;
+          }
+        }
+      }
+      if (fast && !by_bounds) {
+        // every other tracked centroid (rescored or not) and every untracked one
+        // must stay strictly above the winner
+        const float hi1 = d1 * (1.0f + DREL);
+        bool ok = have_w && (L_unt > hi1);
+#pragma unroll
+        for (int e = 0; e < 6; ++e) {
+          const int j = (int)(__float_as_uint(cn[e]) & 0xFFu);
+          const float lo = ((evm >> e) & 1u) ? dn[e] * (1.0f - DREL) : QWM_LB(cn[e]);
+          ok = ok && (j == win || lo > hi1);
+        }
+        fast = ok;
+      }
+    } else {
+      // QSAC.  Tracked candidate k is certainly outside the M nearest when M other
+      // values are certainly smaller; the untracked ones must all be outside too.
+      float Lb[2 * KT], Ub[2 * KT];
+#pragma unroll
+      for (int k = 0; k < 2 * KT; ++k) { Lb[k] = QWM_LB(g[k]); Ub[k] = QWM_UB(g[k]); }
+      int below_floor = 0;
+      uint32_t outmask = 0;
+#pragma unroll
+      for (int k = 0; k < 2 * KT; ++k) {
+        below_floor += (Ub[k] < L_unt) ? 1 : 0;
+        int n_before = 0;
+#pragma unroll
+        for (int m = 0; m < 2 * KT; ++m) n_before += (Ub[m] < Lb[k]) ? 1 : 0;
+        outmask |= (n_before >= a.M ? 1u : 0u) << k;
+      }
+      const bool unt_out = below_floor >= a.M;   // untracked centroids are all outside the M nearest
+      // score S for every possible member, smallest values of both halves first,
+      // skipping candidates whose distance bound already exceeds the best S (S >= d_Q)
+      double Sbest = __builtin_inf();
+      float dwin = 0.f;
+      float dv[2 * KT];
+      uint32_t evmask = 0;
+#pragma unroll
+      for (int step = 0; step < 2 * KT; ++step) {
+        const int k = (step & 1) ? KT + (step >> 1) : (step >> 1);
+        dv[k] = 0.f;
+        const bool need = fast && !((outmask >> k) & 1u) &&
+                          ((double)Lb[k] <= Sbest * (1.0 + 1.0 / 1048576.0));
+        if (!__any(need)) continue;
+        const int j = (int)(__float_as_uint(g[k]) & 0xFFu);
+        const ResidStats rs = resid_stats<F32, WT>(kb, kf, muh + (int64_t)j * D, hh, sm.w);
+        if (need) {
+          evmask |= 1u << k;
+          dv[k] = rs.d;
+          const double R0 = (double)rs.hi0 - (double)rs.lo0, R1 = (double)rs.hi1 - (double)rs.lo1;
+          const double S = W0 * R0 * R0 + W1 * R1 * R1;
+          if (!have_w || S < Sbest || (S == Sbest && j < win)) {
+            Sbest = S; win = j; dwin = rs.d;
+            wlo0 = rs.lo0; whi0 = rs.hi0; wlo1 = rs.lo1; whi1 = rs.hi1; have_w = true;
+          }
+        }
+      }
+      if (fast) {
+        // the winner must be among the M nearest: count every centroid that may precede it
+        const float dwin_hi = dwin * (1.0f + DREL);
+        int before = 0;
+#pragma unroll
+        for (int k = 0; k < 2 * KT; ++k) {
+          const int j = (int)(__float_as_uint(g[k]) & 0xFFu);
+          const float lo = ((evmask >> k) & 1u) ? dv[k] * (1.0f - DREL) : Lb[k];
+          before += (j != win && lo <= dwin_hi) ? 1 : 0;
+        }
+        // untracked centroids either lie outside the M nearest or cannot beat the best S (S >= d_Q)
+        const bool unt_ok = unt_out || ((double)L_unt > Sbest * (1.0 + 1.0 / 1048576.0));
+        fast = have_w && __builtin_isfinite(Sbest) && unt_ok && (L_unt > dwin_hi) && (before <= a.M - 1);
+      }
+    }
 
     if (MODE == MODE_ASSIGN) {
-      fast = fast && (lower2 > upper1);
       if (valid && hh == 0) {
         if (fast) {
-          sm.idx[wv][ln] = (uint8_t)j1;
+          sm.idx[wv][ln] = (uint8_t)win;
         } else {
           const int slot = atomicAdd(a.counter, 1);
           a.worklist[slot] = (int32_t)((int64_t)h * a.T + tok);
@@ -300,78 +478,69 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
         }
       }
     } else {
-      // ---- residual against the first candidate ----
-      float r[64];
-      const uint16_t* mj = a.mu + ((int64_t)h * NC + j1) * D;
-      float lo0 = 0.f, hi0 = 0.f, lo1 = 0.f, hi1 = 0.f;
-      const float* xf = F32 ? static_cast<const float*>(a.x) + rowoff : nullptr;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const u32x4 mv = *reinterpret_cast<const u32x4*>(mj + 16 * s + 8 * hh);
-        const u32x4 kv = __builtin_bit_cast(u32x4, kb[s]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t mw = mv[e >> 1], kw = kv[e >> 1];
-          const float m = (e & 1) ? __uint_as_float(mw & 0xFFFF0000u) : __uint_as_float(mw << 16);
-          float x;
-          if (F32) x = valid ? xf[16 * s + 8 * hh + e] : 0.f;
-          else x = (e & 1) ? __uint_as_float(kw & 0xFFFF0000u) : __uint_as_float(kw << 16);
-          const float rv = x - m;
-          r[8 * s + e] = rv;
-          if (s < 4) { lo0 = fminf(lo0, rv); hi0 = fmaxf(hi0, rv); }
-          else { lo1 = fminf(lo1, rv); hi1 = fmaxf(hi1, rv); }
-        }
-      }
-      lo0 = fminf(lo0, swap32_f(lo0)); hi0 = fmaxf(hi0, swap32_f(hi0));
-      lo1 = fminf(lo1, swap32_f(lo1)); hi1 = fmaxf(hi1, swap32_f(hi1));
-      const double R0 = (double)hi0 - (double)lo0, R1 = (double)hi1 - (double)lo1;
-      if (use_qsac) {
-        const double S1 = W0 * R0 * R0 + W1 * R1 * R1;
-        const double thr = fmax((double)upper1, S1 * (1.0 + 1.0 / 1048576.0));
-        fast = fast && __builtin_isfinite(S1) && ((double)lower2 > thr);
-      } else {
-        fast = fast && (lower2 > upper1);
+      // ---- ranges of the winner (when the choice came from bounds alone) ----
+      const uint16_t* mw = muh + (int64_t)win * D;
+      if (__any(!have_w)) {
+        const ResidStats rs = resid_stats<F32, WT>(kb, kf, mw, hh, sm.w);
+        if (!have_w) { wlo0 = rs.lo0; whi0 = rs.hi0; wlo1 = rs.lo1; whi1 = rs.hi1; }
       }
       bool sat0 = false, sat1 = false;
-      const GroupCodec g0 = make_codec(lo0, hi0, &sat0);
-      const GroupCodec g1 = make_codec(lo1, hi1, &sat1);
-      // codes: lane holds channels 16 s + 8 hh + e -> bytes 4 s + 2 hh (+1)
+      const GroupCodec g0 = make_codec(wlo0, whi0, &sat0);
+      const GroupCodec g1 = make_codec(wlo1, whi1, &sat1);
+      // codes, and PSAC's E = r - r_hat (exact in fp32) fed straight into C = E U on
+      // MFMA (A = U^T, rows 0..7 valid; B = E split into three bf16 parts)
+      f32x16 pacc = {};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const GroupCodec& g = s < 4 ? g0 : g1;
+        const u32x4 mv = *reinterpret_cast<const u32x4*>(mw + 16 * s + 8 * hh);
         uint32_t bits = 0;
+        float Ev[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bits |= code_of(r[8 * s + e], g) << (2 * e);
-        if (valid) *reinterpret_cast<uint16_t*>(&sm.codes[wv][ln][4 * s + 2 * hh]) = (uint16_t)bits;
-        if (use_psac) {
-          // E = r - r_hat (exact in fp32), reuse r[] storage
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float q = (float)((bits >> (2 * e)) & 3u);
-            r[8 * s + e] = r[8 * s + e] - g.s * (q - (float)g.z);
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t mwd = mv[e >> 1];
+          const float m = (e & 1) ? __uint_as_float(mwd & 0xFFFF0000u) : __uint_as_float(mwd << 16);
+          const float r = kval<F32>(kb, kf, s, e) - m;
+          const uint32_t q = code_of(r, g);
+          bits |= q << (2 * e);
+          Ev[e] = r - g.s * ((float)q - (float)g.z);
+          if (F32 && use_psac) {
+            // add the rounding error of r = fl32(k - mu) (TwoSum) so that E = k - mu - r_hat
+            const float x = kval<F32>(kb, kf, s, e);
+            const float bv = r - x;
+            Ev[e] += (x - (r - bv)) + (-m - bv);
           }
         }
-      }
-      if (use_psac && F32) {
-        // add the rounding error of r = fl32(k - mu) (TwoSum) so that E = k - mu - r_hat
+        if (valid) *reinterpret_cast<uint16_t*>(&sm.codes[wv][ln][4 * s + 2 * hh]) = (uint16_t)bits;
+        if (use_psac) {
+          bf16x8 uf;
+          if (ln < R) uf = *reinterpret_cast<const bf16x8*>(&sm.ut[ln][16 * s + 8 * hh]);
+          else uf = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+          u32x4 p0, p1, p2;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const u32x4 mv = *reinterpret_cast<const u32x4*>(mj + 16 * s + 8 * hh);
+          for (int e2 = 0; e2 < 4; ++e2) {
+            uint32_t b[2][3];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t mw = mv[e >> 1];
-            const float m = (e & 1) ? __uint_as_float(mw & 0xFFFF0000u) : __uint_as_float(mw << 16);
-            const float x = valid ? xf[16 * s + 8 * hh + e] : 0.f;
-            const float rr = x - m;
-            const float bv = rr - x;
-            const float err = (x - (rr - bv)) + (-m - bv);
-            r[8 * s + e] += err;
+            for (int half = 0; half < 2; ++half) {
+              const float ev = Ev[2 * e2 + half];
+              const uint32_t b0 = f32_to_bf16_bits(ev);
+              const float rem1 = ev - bf16_bits_to_f32(b0);
+              const uint32_t b1 = f32_to_bf16_bits(rem1);
+              const float rem2 = rem1 - bf16_bits_to_f32(b1);
+              b[half][0] = b0; b[half][1] = b1; b[half][2] = f32_to_bf16_bits(rem2);
+            }
+            p0[e2] = b[0][0] | (b[1][0] << 16);
+            p1[e2] = b[0][1] | (b[1][1] << 16);
+            p2[e2] = b[0][2] | (b[1][2] << 16);
           }
+          pacc = mfma_bf16(uf, __builtin_bit_cast(bf16x8, p0), pacc);
+          pacc = mfma_bf16(uf, __builtin_bit_cast(bf16x8, p1), pacc);
+          pacc = mfma_bf16(uf, __builtin_bit_cast(bf16x8, p2), pacc);
         }
       }
       if (valid && hh == 0) {
         if (fast) {
-          sm.idx[wv][ln] = (uint8_t)j1;
+          sm.idx[wv][ln] = (uint8_t)win;
           sm.scale[wv][ln][0] = (uint16_t)g0.sbits;
           sm.scale[wv][ln][1] = (uint16_t)g1.sbits;
           sm.nib[wv][ln] = (uint8_t)(g0.z | (g1.z << 2));
@@ -388,43 +557,14 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
       }
       if (MODE == MODE_KEYS) {
         if (use_psac) {
-          // C = E U on MFMA: A = U^T (rows 0..7 valid), B = E split into 3 bf16 parts
-          f32x16 acc = {};
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            bf16x8 uf;
-            if (ln < R) uf = *reinterpret_cast<const bf16x8*>(&sm.ut[ln][16 * s + 8 * hh]);
-            else uf = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-            u32x4 p0, p1, p2;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              uint32_t wlo[3], whi[3];
-#pragma unroll
-              for (int half = 0; half < 2; ++half) {
-                const float ev = r[8 * s + 2 * e2 + half];
-                const uint32_t b0 = f32_to_bf16_bits(ev);
-                const float rem1 = ev - bf16_bits_to_f32(b0);
-                const uint32_t b1 = f32_to_bf16_bits(rem1);
-                const float rem2 = rem1 - bf16_bits_to_f32(b1);
-                const uint32_t b2 = f32_to_bf16_bits(rem2);
-                if (half == 0) { wlo[0] = b0; wlo[1] = b1; wlo[2] = b2; }
-                else { whi[0] = b0; whi[1] = b1; whi[2] = b2; }
-              }
-              p0[e2] = wlo[0] | (whi[0] << 16);
-              p1[e2] = wlo[1] | (whi[1] << 16);
-              p2[e2] = wlo[2] | (whi[2] << 16);
-            }
-            acc = mfma_bf16(uf, __builtin_bit_cast(bf16x8, p0), acc);
-            acc = mfma_bf16(uf, __builtin_bit_cast(bf16x8, p1), acc);
-            acc = mfma_bf16(uf, __builtin_bit_cast(bf16x8, p2), acc);
-          }
+          const f32x16 acc = pacc;
           // lane (token, hh) holds C[4 hh + 0..3] in acc[0..3]
           float m = fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])), fmaxf(fabsf(acc[2]), fabsf(acc[3])));
           m = fmaxf(m, swap32_f(m));
           bool sat = false;
           const uint32_t csb = fp16_up_div((double)m, 127.0f, &sat);
           const float cs = f16_bits_to_f32(csb);
-          int8_t qv[4];
+          uint32_t packed = 0;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             int qi = 0;
@@ -432,12 +572,10 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
               qi = rne_quot(acc[i], cs);
               qi = qi < -127 ? -127 : (qi > 127 ? 127 : qi);
             }
-            qv[i] = (int8_t)qi;
+            packed |= ((uint32_t)(uint8_t)(int8_t)qi) << (8 * i);
           }
           if (valid) {
-            *reinterpret_cast<uint32_t*>(&sm.cq[wv][ln][4 * hh]) =
-                (uint32_t)(uint8_t)qv[0] | ((uint32_t)(uint8_t)qv[1] << 8) |
-                ((uint32_t)(uint8_t)qv[2] << 16) | ((uint32_t)(uint8_t)qv[3] << 24);
+            *reinterpret_cast<uint32_t*>(&sm.cq[wv][ln][4 * hh]) = packed;
             if (hh == 0) sm.cs[wv][ln] = (uint16_t)csb;
           }
         } else if (valid) {
@@ -455,7 +593,6 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
       if (nv > 0) {
         if (lane < nv) a.idx[base + lane] = sm.idx[wv][lane];
         if (MODE != MODE_ASSIGN) {
-          // codes: 32 bytes per token, 16 bytes per lane
           {
             const int t = lane >> 1, part = lane & 1;
             if (t < nv)
@@ -465,7 +602,6 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
           if (lane < nv)
             *reinterpret_cast<uint32_t*>(a.scale + (base + lane) * 2) =
                 *reinterpret_cast<const uint32_t*>(&sm.scale[wv][lane][0]);
-          // zeros: token pairs (tok0 is even)
           if (2 * lane < nv) {
             const uint8_t lo = sm.nib[wv][2 * lane];
             const uint8_t hi = (2 * lane + 1 < nv) ? sm.nib[wv][2 * lane + 1] : 0;
@@ -492,6 +628,7 @@ template <int MODE, bool F32>
 __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   __shared__ double kx[4][D];
+  __shared__ double wx[4][D];
   __shared__ double dq[4][NC];
   const int count = *a.counter;
   if (blockIdx.x == 0 && tid == 0 && a.diag && count > 0)
@@ -537,15 +674,24 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     const bool wts = use_qsac && a.w != nullptr;
-    // d_Q for centroids lane + 64 q
+    wx[wv][2 * lane] = wts ? (double)a.w[h * D + 2 * lane] : 1.0;
+    wx[wv][2 * lane + 1] = wts ? (double)a.w[h * D + 2 * lane + 1] : 1.0;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // d_Q for centroids lane + 64 q, direct form in fp64
     for (int q = 0; q < 4; ++q) {
       const int j = lane + 64 * q;
-      const uint16_t* mj = a.mu + ((int64_t)h * NC + j) * D;
+      const u32x4* mrow = reinterpret_cast<const u32x4*>(a.mu + ((int64_t)h * NC + j) * D);
       double s = 0.0;
-      for (int c = 0; c < D; ++c) {
-        const double df = kx[wv][c] - (double)bf16_bits_to_f32(mj[c]);
-        const double wc = wts ? (double)a.w[h * D + c] : 1.0;
-        s = fma(wc * df, df, s);
+      for (int c8 = 0; c8 < D / 8; ++c8) {
+        const u32x4 v = mrow[c8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t wd = v[e >> 1];
+          const double m = (double)((e & 1) ? __uint_as_float(wd & 0xFFFF0000u) : __uint_as_float(wd << 16));
+          const double df = kx[wv][8 * c8 + e] - m;
+          s = fma(wx[wv][8 * c8 + e] * df, df, s);
+        }
       }
       dq[wv][j] = s;
     }
@@ -805,7 +951,7 @@ namespace qwm_host {
 using namespace qwm;
 
 struct SelWork {
-  uint16_t* tbl; uint16_t* aug; float* Bj; float* Bmax; double* Wg; int32_t* counter; int32_t* worklist;
+  uint16_t* tbl; uint16_t* tbl_lo; uint16_t* aug; float* Bj; float* Bmax; double* Wg; int32_t* counter; int32_t* worklist;
   uint8_t* assign; int32_t* perm;
 };
 
@@ -813,6 +959,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd) {
   size_t b = 0;
+  b += align256((size_t)H * NC * D * 2);
   b += align256((size_t)H * NC * D * 2);
   b += align256((size_t)H * NC * 4 * 2);
   b += align256((size_t)H * NC * 4);
@@ -832,6 +979,7 @@ static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd) {
   SelWork w{};
   auto take = [&](size_t n) { char* r = p; p += align256(n); return r; };
   w.tbl = reinterpret_cast<uint16_t*>(take((size_t)H * NC * D * 2));
+  w.tbl_lo = reinterpret_cast<uint16_t*>(take((size_t)H * NC * D * 2));
   w.aug = reinterpret_cast<uint16_t*>(take((size_t)H * NC * 4 * 2));
   w.Bj = reinterpret_cast<float*>(take((size_t)H * NC * 4));
   w.Bmax = reinterpret_cast<float*>(take((size_t)H * 4));
@@ -856,13 +1004,32 @@ template <int MODE>
 static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t stream, const char* what) {
   const int bph = blocks_per_head(x->T, x->H);
   a.blocks_per_head = bph;
-  if (x->dtype == QWM_BF16)
-    hipLaunchKernelGGL((select_kernel<MODE, false>), dim3(bph, x->H), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((select_kernel<MODE, true>), dim3(bph, x->H), dim3(256), 0, stream, a);
+  const bool qs = (MODE == MODE_KEYS) && (a.flags & QWM_QSAC) && a.M > 1;
+  const bool wt = (MODE == MODE_KEYS) && a.w != nullptr;
+  const dim3 grid(bph, x->H), block(256);
+  const bool f32 = x->dtype != QWM_BF16;
+  if constexpr (MODE == MODE_KEYS) {
+    if (f32) {
+      if (qs && wt) hipLaunchKernelGGL((select_kernel<MODE, true, true, true>), grid, block, 0, stream, a);
+      else if (qs) hipLaunchKernelGGL((select_kernel<MODE, true, true, false>), grid, block, 0, stream, a);
+      else if (wt) hipLaunchKernelGGL((select_kernel<MODE, true, false, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((select_kernel<MODE, true, false, false>), grid, block, 0, stream, a);
+    } else {
+      if (qs && wt) hipLaunchKernelGGL((select_kernel<MODE, false, true, true>), grid, block, 0, stream, a);
+      else if (qs) hipLaunchKernelGGL((select_kernel<MODE, false, true, false>), grid, block, 0, stream, a);
+      else if (wt) hipLaunchKernelGGL((select_kernel<MODE, false, false, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((select_kernel<MODE, false, false, false>), grid, block, 0, stream, a);
+    }
+  } else {
+    if (f32) hipLaunchKernelGGL((select_kernel<MODE, true, false, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((select_kernel<MODE, false, false, false>), grid, block, 0, stream, a);
+  }
   qwm_status s = check_launch(what);
   if (s != QWM_OK) return s;
-  const int fb = 64;
+  // one wave per flagged token; the count is known only on the device, so the
+  // grid covers the worst case and idle blocks exit at once
+  const int64_t worst = ((int64_t)x->H * x->T + 3) / 4;
+  const int fb = (int)(worst < 2048 ? worst : 2048);
   if (x->dtype == QWM_BF16)
     hipLaunchKernelGGL((fallback_kernel<MODE, false>), dim3(fb), dim3(256), 0, stream, a);
   else
@@ -872,21 +1039,25 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
 
 static void fill_common(SelectArgs& a, const qwm_tokens* x, const SelWork& w, const uint16_t* mu) {
   a.x = x->ptr; a.T = x->T; a.st = x->stride_t; a.sh = x->stride_h;
-  a.tbl = w.tbl; a.aug = w.aug; a.Bj = w.Bj; a.Bmax = w.Bmax; a.Wg = w.Wg;
+  a.tbl = w.tbl; a.tbl_lo = w.tbl_lo; a.aug = w.aug; a.Bj = w.Bj; a.Bmax = w.Bmax; a.Wg = w.Wg;
   a.mu = mu; a.counter = w.counter; a.worklist = w.worklist;
 }
 
 static qwm_status prep(const SelWork& w, const uint16_t* mu, const float* wts, int32_t H, hipStream_t stream) {
-  TablePrepArgs p{mu, wts, w.tbl, w.aug, w.Bj, w.Bmax, w.Wg, w.counter};
+  TablePrepArgs p{mu, wts, w.tbl, w.tbl_lo, w.aug, w.Bj, w.Bmax, w.Wg, w.counter};
   hipLaunchKernelGGL(prep_table_kernel, dim3(H), dim3(256), 0, stream, p);
   return check_launch("centroid table preparation");
 }
 
-// Certified relative error coefficient of the GEMM distances: bf16 rounding of
-// w * mu (2^-9 per term, counted twice), fp32 accumulation, the 8 index bits
-// packed into each value (2^-15), the bf16 split of B_j; plus slack.
+// Certified bound c on |f_j - e_j| / (||k||_w^2 + B_j) for the GEMM values:
+//   fp32 accumulation of 131 exact products: <= 131 u * 2 (A + B)   ~ 1.6e-5
+//   the 8 index bits packed into each value: <= 2^-15 |f| <= 2^-14 (A + B)
+//   bf16 split of B_j (2^-24 B) and of fp32 tokens (2^-17 (A + B))
+//   weighted tables carry a bf16 remainder (hi + lo, 259 products): the
+//   accumulation term doubles to ~3.1e-5 and the split leaves 2^-18 (A + B)
+// i.e. 8.5e-5 unweighted and 9.6e-5 weighted; the constants below add margin.
 static float error_coeff(bool weighted) {
-  return weighted ? (1.0f / 256.0f + 1.0f / 4096.0f) : (1.0f / 4096.0f);
+  return weighted ? (1.0f / 8192.0f + 1.0f / 32768.0f) : (1.0f / 8192.0f);
 }
 
 qwm_status launch_keys(const qwm_tokens* k, const uint16_t* centroids, const float* w, const uint16_t* U,
