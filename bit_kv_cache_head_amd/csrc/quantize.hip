@@ -33,7 +33,7 @@ struct TablePrepArgs {
 __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
   const int h = blockIdx.x, j = threadIdx.x;
   __shared__ float ws[D];
-  __shared__ float bm[256];
+  __shared__ float bm[4];
   if (j < D) ws[j] = a.w ? a.w[h * D + j] : 1.0f;
   if (h == 0 && j == 0) *a.counter = 0;
   __syncthreads();
@@ -67,18 +67,16 @@ __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
   uint16_t* ag = a.aug + ((int64_t)h * NC + j) * 4;
   ag[0] = (uint16_t)bh; ag[1] = (uint16_t)bmid; ag[2] = (uint16_t)blo; ag[3] = 0;
   a.Bj[h * NC + j] = (float)B;
-  bm[j] = (float)B;
+  // block max of B over the 256 centroids; group weight sums over 64 channels
+  // (fp64 sums of fp32 weights, exact for any sane spread of magnitudes)
+  const float wmax = wave_max_f((float)B);
+  const int lane = j & 63, wv = j >> 6;
+  double gsum = 0.0;
+  if (wv < 2) gsum = wave_sum_d((double)ws[j]);
+  if (lane == 0) bm[wv] = wmax;
   __syncthreads();
-  if (j == 0) {
-    float mx = 0.f;
-    for (int i = 0; i < NC; ++i) mx = fmaxf(mx, bm[i]);
-    a.Bmax[h] = mx * (1.0f + 1.0f / 65536.0f);
-    double s0 = 0.0, s1 = 0.0;
-    for (int c = 0; c < 64; ++c) s0 += (double)ws[c];
-    for (int c = 64; c < D; ++c) s1 += (double)ws[c];
-    a.Wg[2 * h] = s0;
-    a.Wg[2 * h + 1] = s1;
-  }
+  if (j == 0) a.Bmax[h] = fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3])) * (1.0f + 1.0f / 65536.0f);
+  if (wv < 2 && lane == 0) a.Wg[2 * h + wv] = gsum;
 }
 
 struct SelectArgs {
@@ -678,22 +676,31 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
     wx[wv][2 * lane + 1] = wts ? (double)a.w[h * D + 2 * lane + 1] : 1.0;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    // d_Q for centroids lane + 64 q, direct form in fp64
-    for (int q = 0; q < 4; ++q) {
-      const int j = lane + 64 * q;
-      const u32x4* mrow = reinterpret_cast<const u32x4*>(a.mu + ((int64_t)h * NC + j) * D);
-      double s = 0.0;
+    // d_Q for centroids lane + 64 q, direct form in fp64.  Channels outer (one
+    // 8-channel slice of k and w at a time), the four centroids inner, so the
+    // token never has to live in registers as a whole.
+    {
+      const u32x4* mrow = reinterpret_cast<const u32x4*>(a.mu + ((int64_t)h * NC + lane) * D);
+      double s[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma nounroll
       for (int c8 = 0; c8 < D / 8; ++c8) {
-        const u32x4 v = mrow[c8];
+        double kk[8], ww[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t wd = v[e >> 1];
-          const double m = (double)((e & 1) ? __uint_as_float(wd & 0xFFFF0000u) : __uint_as_float(wd << 16));
-          const double df = kx[wv][8 * c8 + e] - m;
-          s = fma(wx[wv][8 * c8 + e] * df, df, s);
+        for (int e = 0; e < 8; ++e) { kk[e] = kx[wv][8 * c8 + e]; ww[e] = wx[wv][8 * c8 + e]; }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 v = mrow[q * 64 * (D / 8) + c8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t wd = v[e >> 1];
+            const double m = (double)((e & 1) ? __uint_as_float(wd & 0xFFFF0000u) : __uint_as_float(wd << 16));
+            const double df = kk[e] - m;
+            s[q] = fma(ww[e] * df, df, s[q]);
+          }
         }
       }
-      dq[wv][j] = s;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dq[wv][lane + 64 * q] = s[q];
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -873,64 +880,99 @@ __global__ __launch_bounds__(256) void forgy_kernel(const void* x, int32_t dtype
   }
 }
 
-// Block (g, h) owns clusters 8g .. 8g+7 of head h.  Members are visited in
-// token order, so the fp64 sums are deterministic.
+// Block (g, h) owns clusters 8g .. 8g+7 of head h; half-wave k (32 lanes,
+// lane q = channels 4q..4q+3) owns cluster 8g+k.  The assignment bytes are
+// staged in LDS 4,096 at a time; each half-wave scans them in token order and
+// appends its members to a private list, which it drains (loads four token
+// rows in flight) whenever the list could overflow and at the end.  Members
+// are summed in token order, so the fp64 sums are deterministic.
+constexpr int LU_TILE = 4096;
+constexpr int LU_LIST = 256;
+
+__device__ __forceinline__ void lu_accumulate(const void* x, int32_t dtype, int64_t rowbase, int64_t st,
+                                              const int32_t* list, int n, double (&sum)[4]) {
+  int e = 0;
+  if (dtype == QWM_BF16) {
+    const uint16_t* xb = static_cast<const uint16_t*>(x) + rowbase;
+    for (; e + 4 <= n; e += 4) {
+      uint2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint2*>(xb + (int64_t)list[e + u] * st);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sum[0] += (double)__uint_as_float(v[u].x << 16);
+        sum[1] += (double)__uint_as_float(v[u].x & 0xFFFF0000u);
+        sum[2] += (double)__uint_as_float(v[u].y << 16);
+        sum[3] += (double)__uint_as_float(v[u].y & 0xFFFF0000u);
+      }
+    }
+    for (; e < n; ++e) {
+      const uint2 v = *reinterpret_cast<const uint2*>(xb + (int64_t)list[e] * st);
+      sum[0] += (double)__uint_as_float(v.x << 16);
+      sum[1] += (double)__uint_as_float(v.x & 0xFFFF0000u);
+      sum[2] += (double)__uint_as_float(v.y << 16);
+      sum[3] += (double)__uint_as_float(v.y & 0xFFFF0000u);
+    }
+  } else {
+    const float* xf = static_cast<const float*>(x) + rowbase;
+    for (; e + 4 <= n; e += 4) {
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(xf + (int64_t)list[e + u] * st);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sum[0] += (double)v[u][0]; sum[1] += (double)v[u][1]; sum[2] += (double)v[u][2]; sum[3] += (double)v[u][3];
+      }
+    }
+    for (; e < n; ++e) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(xf + (int64_t)list[e] * st);
+      sum[0] += (double)v[0]; sum[1] += (double)v[1]; sum[2] += (double)v[2]; sum[3] += (double)v[3];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void lloyd_update_kernel(const void* x, int32_t dtype, int64_t T, int64_t st,
                                                            int64_t sh, const uint8_t* assign, const uint16_t* cin,
                                                            uint16_t* cout) {
-  const int g = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  __shared__ int32_t list[256];
-  __shared__ int32_t wcount[4][8];
-  __shared__ int32_t start[9];
-  const int k = tid >> 5, q = tid & 31;    // accumulator role: cluster k, channels 4q..4q+3
+  const int g = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  __shared__ __align__(16) uint8_t tile[LU_TILE];
+  __shared__ int32_t list[8][LU_LIST];
+  const int k = tid >> 5, q = tid & 31, half = (tid >> 5) & 1;
+  const int j = 8 * g + k;
+  const int64_t rowbase = (int64_t)h * sh + 4 * q;
   double sum[4] = {0.0, 0.0, 0.0, 0.0};
   int64_t cnt = 0;
+  int n = 0;
   const uint8_t* ah = assign + (int64_t)h * T;
-  for (int64_t t0 = 0; t0 < T; t0 += 256) {
-    const int64_t t = t0 + tid;
-    const int rel = (t < T) ? (int)ah[t] - 8 * g : -1;
-    const bool mine = rel >= 0 && rel < 8;
-    int pos = 0;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const uint64_t m = __ballot(mine && rel == kk);
-      if (lane == 0) wcount[wv][kk] = __popcll(m);
-      if (mine && rel == kk) pos = __popcll(m & ((1ull << lane) - 1ull));
-    }
+  for (int64_t t0 = 0; t0 < T; t0 += LU_TILE) {
+    const int64_t len = (T - t0 < LU_TILE) ? (T - t0) : LU_TILE;
     __syncthreads();
-    if (tid == 0) {
-      int acc = 0;
-      for (int kk = 0; kk < 8; ++kk) {
-        start[kk] = acc;
-        for (int w2 = 0; w2 < 4; ++w2) acc += wcount[w2][kk];
-      }
-      start[8] = acc;
-    }
+    // assignment rows carry no alignment promise: byte loads, coalesced
+    for (int e = tid; e < len; e += 256) tile[e] = ah[t0 + e];
     __syncthreads();
-    if (mine) {
-      int off = start[rel];
-      for (int w2 = 0; w2 < wv; ++w2) off += wcount[w2][rel];
-      list[off + pos] = (int32_t)t;
-    }
-    __syncthreads();
-    for (int e = start[k]; e < start[k + 1]; ++e) {
-      const int64_t tt = list[e];
-      const int64_t off = (int64_t)h * sh + tt * st + 4 * q;
-      if (dtype == QWM_BF16) {
-        const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + off);
-        sum[0] += (double)__uint_as_float(v.x << 16);
-        sum[1] += (double)__uint_as_float(v.x & 0xFFFF0000u);
-        sum[2] += (double)__uint_as_float(v.y << 16);
-        sum[3] += (double)__uint_as_float(v.y & 0xFFFF0000u);
-      } else {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + off);
-        sum[0] += (double)v[0]; sum[1] += (double)v[1]; sum[2] += (double)v[2]; sum[3] += (double)v[3];
+    for (int b = 0; b < len; b += 32) {
+      const bool match = (b + q < len) && tile[b + q] == (uint8_t)j;
+      const uint64_t m = __ballot(match);
+      const uint32_t mh = (uint32_t)(m >> (32 * half));
+      if (match) list[k][n + __popc(mh & ((1u << q) - 1u))] = (int32_t)(t0 + b + q);
+      n += __popc(mh);
+      // drain when the next 32 could overflow (decided per wave, both halves alike)
+      const int nmax = max(n, __shfl_xor(n, 32, 64));
+      if (nmax > LU_LIST - 32) {
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        lu_accumulate(x, dtype, rowbase, st, list[k], n, sum);
+        cnt += n;
+        n = 0;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       }
     }
-    cnt += start[k + 1] - start[k];
-    __syncthreads();
   }
-  const int64_t j = 8 * g + k;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  lu_accumulate(x, dtype, rowbase, st, list[k], n, sum);
+  cnt += n;
   const uint16_t* src = cin + ((int64_t)h * NC + j) * D + 4 * q;
   uint16_t* dst = cout + ((int64_t)h * NC + j) * D + 4 * q;
   if (cnt > 0) {
@@ -1029,7 +1071,7 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
   // one wave per flagged token; the count is known only on the device, so the
   // grid covers the worst case and idle blocks exit at once
   const int64_t worst = ((int64_t)x->H * x->T + 3) / 4;
-  const int fb = (int)(worst < 2048 ? worst : 2048);
+  const int fb = (int)(worst < 256 ? worst : 256);
   if (x->dtype == QWM_BF16)
     hipLaunchKernelGGL((fallback_kernel<MODE, false>), dim3(fb), dim3(256), 0, stream, a);
   else

@@ -93,15 +93,32 @@ __global__ void finalize_kernel(const double* __restrict__ S, int64_t* __restric
 
 // ---------------------------------------------------------------------------
 // Principal basis: block subspace iteration (P = 16 columns) in fp64, warm-
-// started from the stored basis; each round is ORTH_PER_ROUND x POWER_STEPS
-// products with A (Cholesky-QR re-orthonormalization in between) followed by a
-// Rayleigh-Ritz step and a residual test on the top-8 Ritz pairs.  One 256-thread block per head; thread t holds row t/2, columns
-// 64*(t%2) .. +64 of A = S/n in registers.
+// started from the stored basis.  Each round is ORTH_PER_ROUND x POWER_STEPS
+// products with A (Cholesky-QR re-orthonormalization in between), then a
+// Rayleigh-Ritz step and a residual test on the top-8 Ritz pairs.
+//
+// One 256-thread block per head.  The products A X and the 16x16 Gram
+// matrices run on the fp64 MFMA (v_mfma_f64_16x16x4, IEEE fp64 FMAs); wave w
+// keeps rows 32w .. 32w+31 of A = S/n in registers as MFMA A-fragments.
+// Lane layout of the 16x16x4 fp64 MFMA: A[i][k] from lane i + 16k, B[k][j]
+// from lane j + 16k, result D[i][j] in lane j + 16 (i % 4), register i / 4.
 // ---------------------------------------------------------------------------
 constexpr int P = 16;
-constexpr int EIG_ROUNDS = 24;      // Rayleigh-Ritz checks
-constexpr int POWER_STEPS = 3;      // products with A between re-orthonormalizations
+constexpr int PP = P + 1;             // padded row
+constexpr int EIG_ROUNDS = 24;        // Rayleigh-Ritz checks
+constexpr int POWER_STEPS = 3;        // products with A between re-orthonormalizations
 constexpr int ORTH_PER_ROUND = 3;
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
 
 __device__ __forceinline__ uint64_t mix64(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -110,84 +127,89 @@ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
 }
 
 struct EigShared {
-  double X[D][P + 1];
-  double Y[D][P + 1];
-  double Hm[P][P + 1];
-  double W[P][P + 1];
-  double G[P][P + 1];
-  double red[8][P];
+  double X[D][PP];        // orthonormal block
+  double Y[D][PP];        // products
+  double Z[D][PP];        // second product buffer
+  double part[4][P][PP];  // per-wave Gram partials
+  double Hm[P][PP];
+  double W[P][PP];
+  double G[P][PP];
   double cs[P / 2][2];
   double theta[P];
+  double red[4][P];
+  int order[P];
   double trace;
-  int conv;
 };
 
-// Y = A X
-__device__ __forceinline__ void matvec(const double (&a)[64], EigShared& sm, int tid) {
-  const int i = tid >> 1, half = tid & 1;
-  double acc[P];
+// dst = A src (128 x 16).
+__device__ __forceinline__ void matvec(const double (&a)[2][32], const double (*src)[PP], double (*dst)[PP],
+                                       int tid) {
+  const int l = tid & 63, wv = tid >> 6;
+  f64x4 c0 = {0.0, 0.0, 0.0, 0.0}, c1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int j = 0; j < P; ++j) acc[j] = 0.0;
-#pragma unroll
-  for (int c = 0; c < 64; ++c) {
-    const double av = a[c];
-    const double* xr = sm.X[64 * half + c];
-#pragma unroll
-    for (int j = 0; j < P; ++j) acc[j] = fma(av, xr[j], acc[j]);
+  for (int s = 0; s < 32; ++s) {
+    const double bv = src[4 * s + (l >> 4)][l & 15];
+    c0 = mfma_f64(a[0][s], bv, c0);
+    c1 = mfma_f64(a[1][s], bv, c1);
   }
 #pragma unroll
-  for (int j = 0; j < P; ++j) acc[j] += __shfl_xor(acc[j], 1, 64);
-  if (half == 0) {
-#pragma unroll
-    for (int j = 0; j < P; ++j) sm.Y[i][j] = acc[j];
+  for (int r = 0; r < 4; ++r) {
+    dst[32 * wv + (l >> 4) + 4 * r][l & 15] = c0[r];
+    dst[32 * wv + 16 + (l >> 4) + 4 * r][l & 15] = c1[r];
   }
   __syncthreads();
 }
 
-// G = Y^T Y, or Hm = X^T Y when xty; one entry per thread, four independent
-// partial sums so the LDS loads and fp64 FMAs overlap.
-__device__ __forceinline__ void gram16(EigShared& sm, int tid, bool xty) {
-  const int a = tid >> 4, b = tid & 15;
-  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-#pragma unroll 4
-  for (int i = 0; i < D; i += 4) {
-    const double* L0 = xty ? sm.X[i] : sm.Y[i];
-    const double* L1 = xty ? sm.X[i + 1] : sm.Y[i + 1];
-    const double* L2 = xty ? sm.X[i + 2] : sm.Y[i + 2];
-    const double* L3 = xty ? sm.X[i + 3] : sm.Y[i + 3];
-    s0 = fma(L0[a], sm.Y[i][b], s0);
-    s1 = fma(L1[a], sm.Y[i + 1][b], s1);
-    s2 = fma(L2[a], sm.Y[i + 2][b], s2);
-    s3 = fma(L3[a], sm.Y[i + 3][b], s3);
+// out = L^T R (16 x 16); wave w sums rows 32w .. 32w+31, partials added in a fixed order.
+__device__ __forceinline__ void gram16(EigShared& sm, const double (*L)[PP], const double (*Rm)[PP],
+                                       double (*out)[PP], int tid) {
+  const int l = tid & 63, wv = tid >> 6;
+  f64x4 c0 = {0.0, 0.0, 0.0, 0.0}, c1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < 8; s += 2) {
+    const int r0 = 32 * wv + 4 * s + (l >> 4);
+    c0 = mfma_f64(L[r0][l & 15], Rm[r0][l & 15], c0);
+    c1 = mfma_f64(L[r0 + 4][l & 15], Rm[r0 + 4][l & 15], c1);
   }
-  const double s = (s0 + s1) + (s2 + s3);
-  if (xty) sm.Hm[a][b] = s; else sm.G[a][b] = s;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sm.part[wv][(l >> 4) + 4 * r][l & 15] = c0[r] + c1[r];
+  __syncthreads();
+  {
+    const int i = tid >> 4, j = tid & 15;
+    out[i][j] = (sm.part[0][i][j] + sm.part[1][i][j]) + (sm.part[2][i][j] + sm.part[3][i][j]);
+  }
   __syncthreads();
 }
 
-// Cholesky of G (upper factor in G's upper triangle) by wave 0, lane = column.
-__device__ void cholesky16(EigShared& sm, int tid) {
+// Upper Cholesky factor of G + shift*I into G's upper triangle, by wave 0
+// (lane j = column j).  shift_rel > 0 adds shift_rel * trace(G) to the
+// diagonal (shifted Cholesky-QR: keeps the factorization finite when the
+// block is numerically rank deficient).
+__device__ void cholesky16(EigShared& sm, int tid, double shift_rel) {
   if (tid < 64) {
     const int j = tid;
-    double col[P];   // column j of the factor
+    double shift = 0.0;
+    if (shift_rel > 0.0) {
+      double dj = (j < P) ? sm.G[j][j] : 0.0;
+      shift = shift_rel * wave_sum_d(dj);
+    }
+    double col[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) col[p] = 0.0;
 #pragma unroll
     for (int k = 0; k < P; ++k) {
-      // r_kk from lane k
       double dkk = 0.0;
       if (j == k) {
-        double s = sm.G[k][k];
+        double s = sm.G[k][k] + shift;
 #pragma unroll
         for (int p = 0; p < P; ++p) if (p < k) s -= col[p] * col[p];
         dkk = sqrt(fmax(s, 1e-300));
         col[k] = dkk;
       }
       dkk = __shfl(dkk, k, 64);
-      // column k of the factor, broadcast entry by entry
       double ck[P];
 #pragma unroll
-      for (int p = 0; p < P; ++p) ck[p] = __shfl(col[p], k, 64);
+      for (int p = 0; p < P; ++p) ck[p] = (p < k) ? __shfl(col[p], k, 64) : 0.0;
       if (j > k && j < P) {
         double s = sm.G[k][j];
 #pragma unroll
@@ -203,113 +225,148 @@ __device__ void cholesky16(EigShared& sm, int tid) {
   __syncthreads();
 }
 
-// X = Y R^{-1} (R upper, in G), rows in parallel.
-__device__ __forceinline__ void solve_rows(EigShared& sm, int tid, bool into_x) {
+// dst = src R^{-1} (R upper, in G), one row per thread; src == dst allowed.
+__device__ __forceinline__ void solve_rows(EigShared& sm, const double (*src)[PP], double (*dst)[PP], int tid) {
   if (tid < D) {
     double x[P];
 #pragma unroll
     for (int j = 0; j < P; ++j) {
-      double s = sm.Y[tid][j];
+      double s = src[tid][j];
 #pragma unroll
       for (int p = 0; p < P; ++p) if (p < j) s -= x[p] * sm.G[p][j];
       x[j] = s / sm.G[j][j];
     }
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      if (into_x) sm.X[tid][j] = x[j]; else sm.Y[tid][j] = x[j];
-    }
+    for (int j = 0; j < P; ++j) dst[tid][j] = x[j];
   }
   __syncthreads();
 }
 
-// X = orth(Y) by two rounds of Cholesky QR.
-__device__ void orthonormalize(EigShared& sm, int tid) {
-  gram16(sm, tid, false);
-  cholesky16(sm, tid);
-  solve_rows(sm, tid, false);   // Y <- Y R^-1
-  gram16(sm, tid, false);
-  cholesky16(sm, tid);
-  solve_rows(sm, tid, true);    // X <- Y R^-1
+// dst = orth(src) by `passes` rounds of Cholesky QR, the first one shifted;
+// the intermediate passes overwrite src.  After the shifted pass (shift s =
+// 3e-12 trace) column j has squared norm ~ r_j^2 / (r_j^2 + s), r_j being its
+// component orthogonal to the earlier columns, so a column well below 1 is a
+// direction the block does not really span (A rank deficient, e.g. fewer
+// Queries than columns, leaves only rounding noise there, and that noise is
+// nearly the same in every column).  Such columns are replaced by fresh hashed
+// vectors so that the next pass sees a full-rank block.  `salt` varies the
+// replacements from call to call.
+__device__ void orthonormalize(EigShared& sm, double (*src)[PP], double (*dst)[PP], int passes, int tid,
+                               int& salt, int h) {
+  for (int ps = 0; ps < passes; ++ps) {
+    gram16(sm, src, src, sm.G, tid);
+    if (ps == 1) {
+      uint32_t weak = 0;
+#pragma unroll
+      for (int j = 0; j < P; ++j) weak |= (sm.G[j][j] < 0.1 ? 1u : 0u) << j;
+      if (weak) {                       // uniform: every thread read the same diagonal
+        ++salt;
+        for (int e = tid; e < D * P; e += 256) {
+          const int i = e / P, j = e % P;
+          if ((weak >> j) & 1u)
+            src[i][j] = (double)(mix64(0xC0FFEEull * (uint64_t)salt + 0x9E37ull * (uint64_t)e +
+                                       ((uint64_t)h << 40)) >> 11) * (1.0 / 9007199254740992.0) - 0.5;
+        }
+        __syncthreads();
+        gram16(sm, src, src, sm.G, tid);
+        cholesky16(sm, tid, 3e-12);     // the new columns are not orthogonal yet: shift once more
+        solve_rows(sm, src, src, tid);
+        gram16(sm, src, src, sm.G, tid);
+      }
+    }
+    cholesky16(sm, tid, ps == 0 ? 3e-12 : 0.0);
+    solve_rows(sm, src, ps + 1 == passes ? dst : src, tid);
+  }
 }
 
-// Cyclic Jacobi on the 16x16 symmetric Hm (parallel round-robin ordering),
-// accumulating W.  All threads call; thread 0..7 own the 8 rotations of a round.
+// Cyclic Jacobi on the symmetric 16x16 Hm (parallel round-robin ordering,
+// eight disjoint rotations per round), accumulating W.  Runs in wave 0; the
+// rotations of one round touch disjoint entries, so each lane updates the
+// entries it read.
+__device__ __forceinline__ int rr_pos(int k, int round) { return k == 0 ? 0 : 1 + (k - 1 + round) % (P - 1); }
+
 __device__ void jacobi16(EigShared& sm, int tid) {
-  if (tid < P * P) {
-    const int a = tid >> 4, b = tid & 15;
-    sm.W[a][b] = (a == b) ? 1.0 : 0.0;
+  if (tid < 64) {
+    const int l = tid;
+    for (int e = l; e < P * P; e += 64) sm.W[e >> 4][e & 15] = ((e >> 4) == (e & 15)) ? 1.0 : 0.0;
+    wave_sync();
+    for (int sweep = 0; sweep < 10; ++sweep) {
+      double off = 0.0, tot = 0.0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = l + 64 * u;
+        const double v = sm.Hm[e >> 4][e & 15];
+        tot += v * v;
+        if ((e >> 4) != (e & 15)) off += v * v;
+      }
+      off = wave_sum_d(off);
+      tot = wave_sum_d(tot);
+      if (off <= 1e-24 * tot) break;
+      for (int round = 0; round < P - 1; ++round) {
+        if (l < P / 2) {
+          int p = rr_pos(l, round), q = rr_pos(P - 1 - l, round);
+          if (p > q) { const int t = p; p = q; q = t; }
+          const double apq = sm.Hm[p][q];
+          double c = 1.0, sn = 0.0;
+          if (apq != 0.0) {
+            const double theta = (sm.Hm[q][q] - sm.Hm[p][p]) / (2.0 * apq);
+            const double t = (theta >= 0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+            c = 1.0 / sqrt(t * t + 1.0);
+            sn = t * c;
+          }
+          sm.cs[l][0] = c;
+          sm.cs[l][1] = sn;
+        }
+        wave_sync();
+        // columns: Hm <- Hm J, W <- W J; task (pair k, row)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = l + 64 * u, k = e >> 4, row = e & 15;
+          int p = rr_pos(k, round), q = rr_pos(P - 1 - k, round);
+          if (p > q) { const int t = p; p = q; q = t; }
+          const double c = sm.cs[k][0], sn = sm.cs[k][1];
+          const double ap = sm.Hm[row][p], aq = sm.Hm[row][q];
+          const double vp = sm.W[row][p], vq = sm.W[row][q];
+          sm.Hm[row][p] = c * ap - sn * aq;
+          sm.Hm[row][q] = sn * ap + c * aq;
+          sm.W[row][p] = c * vp - sn * vq;
+          sm.W[row][q] = sn * vp + c * vq;
+        }
+        wave_sync();
+        // rows: Hm <- J^T Hm; task (pair k, column)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = l + 64 * u, k = e >> 4, col = e & 15;
+          int p = rr_pos(k, round), q = rr_pos(P - 1 - k, round);
+          if (p > q) { const int t = p; p = q; q = t; }
+          const double c = sm.cs[k][0], sn = sm.cs[k][1];
+          const double ap = sm.Hm[p][col], aq = sm.Hm[q][col];
+          sm.Hm[p][col] = c * ap - sn * aq;
+          sm.Hm[q][col] = sn * ap + c * aq;
+        }
+        wave_sync();
+      }
+    }
+    // Ritz values in descending order (rank by counting; ties by index)
+    if (l < P) {
+      const double v = sm.Hm[l][l];
+      int rank = 0;
+#pragma unroll
+      for (int m = 0; m < P; ++m) {
+        const double o = sm.Hm[m][m];
+        rank += (o > v) || (o == v && m < l);
+      }
+      sm.order[rank] = l;
+      sm.theta[rank] = v;
+    }
   }
   __syncthreads();
-  for (int sweep = 0; sweep < 8; ++sweep) {
-    // convergence: off-diagonal mass
-    if (tid == 0) {
-      double off = 0.0, tot = 0.0;
-      for (int a = 0; a < P; ++a)
-        for (int b = 0; b < P; ++b) {
-          const double v = sm.Hm[a][b] * sm.Hm[a][b];
-          tot += v;
-          if (a != b) off += v;
-        }
-      sm.conv = (off <= 1e-24 * tot) ? 1 : 0;
-    }
-    __syncthreads();
-    if (sm.conv) break;
-    for (int round = 0; round < P - 1; ++round) {
-      // round-robin pairing of 16 indices: position 0 fixed, others rotate
-      if (tid < P / 2) {
-        auto pos = [&](int k) { return k == 0 ? 0 : 1 + (k - 1 + round) % (P - 1); };
-        int p = pos(tid), q = pos(P - 1 - tid);
-        if (p > q) { int t = p; p = q; q = t; }
-        const double apq = sm.Hm[p][q];
-        double c = 1.0, s = 0.0;
-        if (apq != 0.0) {
-          const double theta = (sm.Hm[q][q] - sm.Hm[p][p]) / (2.0 * apq);
-          const double t = (theta >= 0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
-          c = 1.0 / sqrt(t * t + 1.0);
-          s = t * c;
-        }
-        sm.cs[tid][0] = c;
-        sm.cs[tid][1] = s;
-      }
-      __syncthreads();
-      // column update (Hm <- Hm J, W <- W J): thread -> (pair, row)
-      double hp = 0, hq = 0, wp = 0, wq = 0;
-      int p = 0, q = 0, row = 0;
-      const bool act = tid < (P / 2) * P;
-      if (act) {
-        const int k = tid >> 4;
-        row = tid & 15;
-        auto pos = [&](int kk) { return kk == 0 ? 0 : 1 + (kk - 1 + round) % (P - 1); };
-        p = pos(k); q = pos(P - 1 - k);
-        if (p > q) { int t = p; p = q; q = t; }
-        const double c = sm.cs[k][0], s = sm.cs[k][1];
-        const double ap = sm.Hm[row][p], aq = sm.Hm[row][q];
-        hp = c * ap - s * aq; hq = s * ap + c * aq;
-        const double vp = sm.W[row][p], vq = sm.W[row][q];
-        wp = c * vp - s * vq; wq = s * vp + c * vq;
-      }
-      __syncthreads();
-      if (act) { sm.Hm[row][p] = hp; sm.Hm[row][q] = hq; sm.W[row][p] = wp; sm.W[row][q] = wq; }
-      __syncthreads();
-      // row update (Hm <- J^T Hm): thread -> (pair, column)
-      if (act) {
-        const int k = tid >> 4, col = tid & 15;
-        const double c = sm.cs[k][0], s = sm.cs[k][1];
-        const double ap = sm.Hm[p][col], aq = sm.Hm[q][col];
-        hp = c * ap - s * aq; hq = s * ap + c * aq;
-        row = col;
-      }
-      __syncthreads();
-      if (act) { sm.Hm[p][row] = hp; sm.Hm[q][row] = hq; }
-      __syncthreads();
-    }
-  }
 }
 
 __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ S, const int64_t* __restrict__ n,
                                                   uint16_t* __restrict__ U, float* __restrict__ lambda,
                                                   float* __restrict__ energy, int32_t* __restrict__ iters) {
-  const int h = blockIdx.x, tid = threadIdx.x;
+  const int h = blockIdx.x, tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
   __shared__ EigShared sm;
   const int64_t nn = n[h];
   uint16_t* Uh = U + (int64_t)h * D * R;
@@ -319,25 +376,25 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ S, 
     if (tid == 0) { energy[h] = 0.f; if (iters) iters[h] = 0; }
     return;
   }
-  const double inv_n = 1.0 / (double)nn;
   const double* Sh = S + (int64_t)h * D * D;
-  double a[64];
-  {
-    const int i = tid >> 1, half = tid & 1;
+  // A = S / n as MFMA A-fragments: a[t][s] = A[32w + 16t + l%16][4s + l/16]
+  // (symmetric by construction: read the upper triangle)
+  double a[2][32];
 #pragma unroll
-    for (int c = 0; c < 64; ++c) {
-      // symmetric by construction: use the upper triangle
-      const int col = 64 * half + c;
-      const double v = (i <= col) ? Sh[i * D + col] : Sh[col * D + i];
-      a[c] = v / (double)nn;
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      const int i = 32 * wv + 16 * t + (l & 15), c = 4 * s + (l >> 4);
+      const double v = (i <= c) ? Sh[i * D + c] : Sh[c * D + i];
+      a[t][s] = v / (double)nn;
     }
   }
-  if (tid == 0) {
+  if (tid < 64) {
     double tr = 0.0;
-    for (int c = 0; c < D; ++c) tr += Sh[c * D + c] / (double)nn;
-    sm.trace = tr;
+    for (int c = l; c < D; c += 64) tr += Sh[c * D + c] / (double)nn;
+    tr = wave_sum_d(tr);
+    if (l == 0) sm.trace = tr;
   }
-  (void)inv_n;
   // start: previous basis (if any) in columns 0..7, hashed vectors elsewhere
   {
     int mine = 0;
@@ -356,95 +413,69 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ S, 
     }
   }
   __syncthreads();
-  orthonormalize(sm, tid);
+  int salt = 0;
+  orthonormalize(sm, sm.Y, sm.X, 3, tid, salt, h);
   int it = 0, converged = 0;
   for (it = 1; it <= EIG_ROUNDS; ++it) {
-    // subspace iteration: POWER_STEPS products with A per orthonormalization
     for (int o = 0; o < ORTH_PER_ROUND; ++o) {
+      // POWER_STEPS products, ping-ponging so that the last lands in Y
+      const double (*src)[PP] = sm.X;
+#pragma unroll
       for (int p = 0; p < POWER_STEPS; ++p) {
-        matvec(a, sm, tid);                 // Y = A X
-        if (p + 1 < POWER_STEPS) {
-          for (int e = tid; e < D * P; e += 256) sm.X[e / P][e % P] = sm.Y[e / P][e % P];
-          __syncthreads();
-        }
+        double (*dst)[PP] = ((POWER_STEPS - 1 - p) % 2 == 0) ? sm.Y : sm.Z;
+        matvec(a, src, dst, tid);
+        src = dst;
       }
-      orthonormalize(sm, tid);              // X = orth(Y)
+      orthonormalize(sm, sm.Y, sm.X, 2, tid, salt, h);
     }
-    matvec(a, sm, tid);                     // Y = A X
+    matvec(a, sm.X, sm.Y, tid);                   // Y = A X
+    // Rayleigh-Ritz: Hm = sym(X^T A X), eigen-decomposed by Jacobi
+    gram16(sm, sm.X, sm.Y, sm.G, tid);
     {
-      gram16(sm, tid, true);            // Hm = X^T A X
-      if (tid < P * P) {
-        const int r = tid >> 4, c = tid & 15;
-        const double v = 0.5 * (sm.Hm[r][c] + sm.Hm[c][r]);
-        sm.G[r][c] = v;
-      }
-      __syncthreads();
-      if (tid < P * P) sm.Hm[tid >> 4][tid & 15] = sm.G[tid >> 4][tid & 15];
-      __syncthreads();
-      jacobi16(sm, tid);
-      // sort Ritz values descending (thread 0), permutation into red[0][*]
-      if (tid == 0) {
-        int order[P];
-        for (int j = 0; j < P; ++j) order[j] = j;
-        for (int x = 1; x < P; ++x)
-          for (int y = x; y > 0 && sm.Hm[order[y]][order[y]] > sm.Hm[order[y - 1]][order[y - 1]]; --y) {
-            int t = order[y]; order[y] = order[y - 1]; order[y - 1] = t;
-          }
-        for (int j = 0; j < P; ++j) { sm.theta[j] = sm.Hm[order[j]][order[j]]; sm.red[0][j] = (double)order[j]; }
-      }
-      __syncthreads();
-      // X <- X W(:, order), Y <- Y W(:, order)
-      {
-        double xr[P], yr[P];
-#pragma unroll
-        for (int j = 0; j < P; ++j) { xr[j] = 0.0; yr[j] = 0.0; }
-        if (tid < D) {
-          for (int k = 0; k < P; ++k) {
-            const double xk = sm.X[tid][k], yk = sm.Y[tid][k];
-#pragma unroll
-            for (int j = 0; j < P; ++j) {
-              const double wkj = sm.W[k][(int)sm.red[0][j]];
-              xr[j] = fma(xk, wkj, xr[j]);
-              yr[j] = fma(yk, wkj, yr[j]);
-            }
-          }
-        }
-        __syncthreads();
-        if (tid < D) {
-#pragma unroll
-          for (int j = 0; j < P; ++j) { sm.X[tid][j] = xr[j]; sm.Y[tid][j] = yr[j]; }
-        }
-      }
-      __syncthreads();
-      // residuals of the top R Ritz pairs
-      if (tid < D) {
-        double rs[R];
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-          const double r = sm.Y[tid][j] - sm.theta[j] * sm.X[tid][j];
-          rs[j] = r * r;
-        }
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-          double v = rs[j];
-          for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-          if ((tid & 63) == 0) sm.red[1 + (tid >> 6)][j] = v;
-        }
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int ok = 1;
-        const double scale = fabs(sm.theta[0]) > 0 ? fabs(sm.theta[0]) : 1.0;
-        for (int j = 0; j < R; ++j) {
-          const double res = sqrt(sm.red[1][j] + sm.red[2][j]);
-          if (!(res <= 1e-9 * scale)) ok = 0;
-        }
-        sm.conv = ok;
-      }
-      __syncthreads();
-      if (sm.conv) { converged = 1; break; }
+      const int r = tid >> 4, c = tid & 15;
+      sm.Hm[r][c] = 0.5 * (sm.G[r][c] + sm.G[c][r]);
     }
-    orthonormalize(sm, tid);            // X = orth(Y), continue from the rotated basis
+    __syncthreads();
+    jacobi16(sm, tid);
+    // X <- X W(:, order), Y <- Y W(:, order)
+    if (tid < D) {
+      double xr[P], yr[P];
+#pragma unroll
+      for (int j = 0; j < P; ++j) { xr[j] = 0.0; yr[j] = 0.0; }
+      for (int k = 0; k < P; ++k) {
+        const double xk = sm.X[tid][k], yk = sm.Y[tid][k];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          const double wkj = sm.W[k][sm.order[j]];
+          xr[j] = fma(xk, wkj, xr[j]);
+          yr[j] = fma(yk, wkj, yr[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < P; ++j) { sm.X[tid][j] = xr[j]; sm.Y[tid][j] = yr[j]; }
+    }
+    __syncthreads();
+    // residuals |A x_j - theta_j x_j| of the top R Ritz pairs (rows split over waves 0, 1)
+    if (tid < D) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const double r = sm.Y[tid][j] - sm.theta[j] * sm.X[tid][j];
+        const double v = wave_sum_d(r * r);
+        if (l == 0) sm.red[wv][j] = v;
+      }
+    }
+    __syncthreads();
+    {
+      const double scale = fabs(sm.theta[0]) > 0 ? fabs(sm.theta[0]) : 1.0;
+      int ok = 1;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const double res = sqrt(sm.red[0][j] + sm.red[1][j]);
+        ok &= (res <= 1e-9 * scale) ? 1 : 0;
+      }
+      if (ok) { converged = 1; break; }   // uniform: every thread reads the same values
+    }
+    orthonormalize(sm, sm.Y, sm.X, 2, tid, salt, h);  // continue from A X_rot
   }
   // outputs: sign rule, bf16, eigenvalues, energy
   if (tid < R) {

@@ -76,6 +76,31 @@ def test_query_stats_and_basis(qwm, name, dtype):
         assert abs(float(st.energy[h]) - b["energy"]) < 1e-6
 
 
+def test_basis_rank_deficient(qwm):
+    """Fewer Queries than basis columns: M_h has rank 5, so only the top five
+    eigenpairs are unique.  They must match the oracle; the rest of the basis
+    must stay finite and orthonormal (to bf16 precision), with zero Ritz
+    values."""
+    import torch
+    from gpu_helpers import dev_tokens, host
+    w = datagen.make_workload("480p", heads=[0, 1], n_chunks=1, chunk=5)
+    Qc = w.Q[:5]
+    st = qwm.QueryStats(2)
+    qwm.update_query_stats(dev_tokens(Qc, "bf16"), st, compute_basis=True)
+    torch.cuda.synchronize()
+    for h in range(2):
+        S, n = OS.update(np.zeros((128, 128)), 0, Qc[:, h])
+        b = OS.principal_basis(S, n)
+        Ug = host(st.U[h])
+        assert np.all(np.isfinite(Ug))
+        ulp = np.ldexp(1.0, np.frexp(np.abs(b["U_bf16"][:, :5]))[1] - 8)
+        assert np.all(np.abs(Ug[:, :5] - b["U_bf16"][:, :5]) <= ulp)
+        np.testing.assert_allclose(Ug.T @ Ug, np.eye(8), atol=2e-2)
+        lam = st.lam[h].cpu().numpy()
+        np.testing.assert_allclose(lam[:5], b["lam"][:5], rtol=1e-6)
+        assert np.all(np.abs(lam[5:]) <= 1e-6 * lam[0])
+
+
 # ---------------------------------------------------------------------------
 # Lloyd centroid tables
 # ---------------------------------------------------------------------------
