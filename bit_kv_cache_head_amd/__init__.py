@@ -126,7 +126,7 @@ def build_centroids(x: torch.Tensor, iters: int, seed: int = 0, init: torch.Tens
     td = _tokens(x)
     if out is None:
         out = torch.empty(td.H, NC, D, dtype=torch.bfloat16, device=x.device)
-    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_CENTROIDS, td.T, td.H, 0), x.device)
+    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_CENTROIDS, td.T, td.H, 0, 0), x.device)
     check(lib.qwm_build_centroids(C.byref(td), NC, iters, C.c_uint64(seed), _ptr(init), _ptr(out),
                                   _ptr(diag), ws, nb, _stream()))
     return out
@@ -138,7 +138,7 @@ def quantize_keys(k: torch.Tensor, centroids: torch.Tensor, w: torch.Tensor | No
     td = _tokens(k)
     if out is None:
         out = PackedChunk(td.T, td.H, True, k.device)
-    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_KEYS, td.T, td.H, 0), k.device)
+    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_KEYS, td.T, td.H, 0, 0), k.device)
     check(lib.qwm_quantize_keys(C.byref(td), _ptr(centroids), _ptr(w), _ptr(U), M, flags,
                                 C.byref(out.desc()), _ptr(diag), ws, nb, _stream()))
     return out
@@ -149,7 +149,7 @@ def quantize_values(v: torch.Tensor, centroids: torch.Tensor, out: PackedChunk |
     td = _tokens(v)
     if out is None:
         out = PackedChunk(td.T, td.H, False, v.device)
-    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_VALUES, td.T, td.H, 0), v.device)
+    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_VALUES, td.T, td.H, 0, 0), v.device)
     check(lib.qwm_quantize_values(C.byref(td), _ptr(centroids), C.byref(out.desc()), _ptr(diag),
                                   ws, nb, _stream()))
     return out
@@ -185,7 +185,7 @@ def attention(q: torch.Tensor, segs: torch.Tensor, n_segs: int, total_keys: int,
     out = torch.empty(td.T, td.H, D, dtype=torch.float32, device=q.device)
     lse = torch.empty(td.H, td.T, dtype=torch.float32, device=q.device) if want_lse else None
     top1 = torch.empty(td.H, td.T, dtype=torch.int32, device=q.device) if want_top1 else None
-    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_ATTENTION, total_keys, td.H, td.T), q.device)
+    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_ATTENTION, total_keys, td.H, td.T, n_segs), q.device)
     check(lib.qwm_attention(C.byref(td), C.c_void_p(segs.data_ptr()), n_segs, total_keys, C.c_float(scale),
                             _ptr(out), _ptr(lse), _ptr(top1), ws, nb, _stream()))
     return out, lse, top1

@@ -57,7 +57,7 @@ def _load():
     L.qwm_quantize_keys.argtypes = [P, P, P, P, C.c_int32, C.c_uint32, P, P, P, C.c_size_t, P]
     L.qwm_quantize_values.argtypes = [P, P, P, P, P, C.c_size_t, P]
     L.qwm_attention.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, C.c_size_t, P]
-    L.qwm_workspace_bytes.argtypes = [C.c_int32, C.c_int64, C.c_int32, C.c_int64]
+    L.qwm_workspace_bytes.argtypes = [C.c_int32, C.c_int64, C.c_int32, C.c_int64, C.c_int32]
     L.qwm_workspace_bytes.restype = C.c_size_t
     L.qwm_zeros_stride.argtypes = [C.c_int64]
     L.qwm_zeros_stride.restype = C.c_int64

@@ -33,7 +33,7 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
 qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
                             float scale, float* out, float* lse, int32_t* top1, void* ws, hipStream_t stream);
 size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd);
-size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq);
+size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs);
 
 static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -90,14 +90,14 @@ const char* qwm_last_error(void) { return g_last_error.c_str(); }
 
 int64_t qwm_zeros_stride(int64_t T) { return qwm::zeros_stride(T); }
 
-size_t qwm_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t n) {
+size_t qwm_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t n, int32_t n_segs) {
   if (T < 0 || H < 1) return 0;
   switch (op) {
     case QWM_OP_STATS: return 0;
     case QWM_OP_CENTROIDS: return select_ws_bytes(T, H, true);
     case QWM_OP_KEYS:
     case QWM_OP_VALUES: return select_ws_bytes(T, H, false);
-    case QWM_OP_ATTENTION: return attention_ws_bytes(T, H, n);
+    case QWM_OP_ATTENTION: return n_segs >= 1 ? attention_ws_bytes(T, H, n, n_segs) : 0;
     default: return 0;
   }
 }
@@ -177,7 +177,7 @@ qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n
   if (!out || !aligned(out, 16)) return fail(QWM_ERR_ARG, "out: null or not 16-byte aligned");
   if (lse && !aligned(lse, 4)) return fail(QWM_ERR_ARG, "lse misaligned");
   if (top1 && !aligned(top1, 4)) return fail(QWM_ERR_ARG, "top1 misaligned");
-  s = check_ws(ws, ws_bytes, attention_ws_bytes(total_keys, q->H, q->T));
+  s = check_ws(ws, ws_bytes, attention_ws_bytes(total_keys, q->H, q->T, n_segs));
   if (s != QWM_OK) return s;
   return launch_attention(q, segs, n_segs, total_keys, scale, out, lse, top1, ws, static_cast<hipStream_t>(stream));
 }

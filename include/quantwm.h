@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define QWM_ABI_VERSION 1
+#define QWM_ABI_VERSION 2
 #define QWM_HEAD_DIM 128
 #define QWM_GROUP 64
 #define QWM_CENTROIDS 256
@@ -176,15 +176,19 @@ qwm_status qwm_quantize_values(const qwm_tokens* v, const uint16_t* centroids, c
  * T >= 1 tokens; keys are numbered in segment order.
  * out [Tq][H][d] fp32; lse [H][Tq] fp32 (natural log of the softmax
  * denominator, may be NULL); top1 [H][Tq] int32 = argmax of the logits over
- * all keys (may be NULL).  Workspace: QWM_OP_ATTENTION with T = total keys
- * and n_segs = Tq (query count). */
+ * all keys (may be NULL).  Workspace: QWM_OP_ATTENTION with T = total keys,
+ * n = Tq (query count) and n_segs.  Centroid values must lie in fp16's range
+ * (|x| <= 65504): the dequantized tiles are fp16 MFMA operands. */
 qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs,
                          int64_t total_keys, float scale, float* out, float* lse, int32_t* top1,
                          void* ws, size_t ws_bytes, qwm_stream stream);
 
 /* Bytes of workspace an operation needs (256-byte aligned pointer required).
- * QWM_OP_ATTENTION: T = total cached keys, n = number of queries. */
-size_t qwm_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t n);
+ * QWM_OP_ATTENTION: T = total cached keys, n = number of queries, n_segs =
+ * number of segments (fp16 copies of every segment's centroid tables live in
+ * the workspace: n_segs * H * 128 KiB, plus the split-key partials); the other
+ * operations ignore n and n_segs. */
+size_t qwm_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t n, int32_t n_segs);
 
 /* Row stride of the zeros array for a chunk of T tokens. */
 int64_t qwm_zeros_stride(int64_t T);

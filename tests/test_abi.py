@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert sorted(_abi.EXPORTS) == declared
     for name in declared:
         assert hasattr(_abi.lib, name), name
-    assert _abi.lib.qwm_abi_version() == 1
+    assert _abi.lib.qwm_abi_version() == 2
 
 
 def test_struct_layouts_match_header_sizes():
@@ -41,11 +41,15 @@ def test_sizes_and_strides():
     assert lib.qwm_zeros_stride(8) == 4
     assert lib.qwm_zeros_stride(9) == 8
     assert lib.qwm_zeros_stride(1560) == 780
-    assert lib.qwm_workspace_bytes(0, 1560, 12, 0) == 0
-    k = lib.qwm_workspace_bytes(2, 1560, 12, 0)
+    assert lib.qwm_workspace_bytes(0, 1560, 12, 0, 0) == 0
+    k = lib.qwm_workspace_bytes(2, 1560, 12, 0, 0)
     assert k >= 12 * 256 * 128 * 2 + 12 * 1560 * 4
-    assert lib.qwm_workspace_bytes(1, 1560, 12, 0) > k          # Lloyd adds assignment + shuffle
-    assert lib.qwm_workspace_bytes(4, 64, 1, 16) == 0           # one split needs no workspace
+    assert lib.qwm_workspace_bytes(1, 1560, 12, 0, 0) > k       # Lloyd adds assignment + shuffle
+    # attention: fp16 centroid tables for every (segment, head), plus split partials
+    assert lib.qwm_workspace_bytes(4, 64, 1, 16, 1) == 2 * 256 * 128 * 2     # one split: tables only
+    big = lib.qwm_workspace_bytes(4, 39000, 12, 1560, 25)
+    assert big >= 25 * 12 * 2 * 256 * 128 * 2
+    assert lib.qwm_workspace_bytes(4, 39000, 12, 1560, 0) == 0
 
 
 def _tok(ptr=0x1000, T=16, H=2, d=128, dtype=1, st=256, sh=128):
