@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the path runs in the HIP kernels of
 libquantwm.so.  PyTorch provides device memory and the current stream.  The
-library must be built first (python -m bit_kv_cache_head_amd.build); importing
+library must be built first (python bit_kv_cache_head_amd/build.py); importing
 this package raises if it is missing.
 """
 from __future__ import annotations
@@ -189,3 +189,11 @@ def attention(q: torch.Tensor, segs: torch.Tensor, n_segs: int, total_keys: int,
     check(lib.qwm_attention(C.byref(td), C.c_void_p(segs.data_ptr()), n_segs, total_keys, C.c_float(scale),
                             _ptr(out), _ptr(lse), _ptr(top1), ws, nb, _stream()))
     return out, lse, top1
+
+
+def reference_top1(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
+    """top1 [H, Tq] int32: argmax over all keys k [Tk, H, 128] (bf16) of q . k."""
+    tq, tk = _tokens(q), _tokens(k)
+    top1 = torch.empty(tq.H, tq.T, dtype=torch.int32, device=q.device)
+    check(lib.qwm_reference_top1(C.byref(tq), C.byref(tk), _ptr(top1), _stream()))
+    return top1

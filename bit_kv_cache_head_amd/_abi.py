@@ -14,7 +14,7 @@ QWM_OP_STATS, QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION = 0
 
 # every symbol include/quantwm.h declares
 EXPORTS = ["qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys", "qwm_quantize_values",
-           "qwm_attention", "qwm_workspace_bytes", "qwm_zeros_stride", "qwm_last_error", "qwm_abi_version"]
+           "qwm_attention", "qwm_reference_top1", "qwm_workspace_bytes", "qwm_zeros_stride", "qwm_last_error", "qwm_abi_version"]
 
 
 class Tokens(C.Structure):
@@ -49,7 +49,7 @@ class Segment(C.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bit_kv_cache_head_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python bit_kv_cache_head_amd/build.py`")
     L = C.CDLL(LIB_PATH)
     P = C.c_void_p
     L.qwm_update_query_stats.argtypes = [P, P, C.c_int32, P, C.c_size_t, P]
@@ -57,6 +57,7 @@ def _load():
     L.qwm_quantize_keys.argtypes = [P, P, P, P, C.c_int32, C.c_uint32, P, P, P, C.c_size_t, P]
     L.qwm_quantize_values.argtypes = [P, P, P, P, P, C.c_size_t, P]
     L.qwm_attention.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, C.c_size_t, P]
+    L.qwm_reference_top1.argtypes = [P, P, P, P]
     L.qwm_workspace_bytes.argtypes = [C.c_int32, C.c_int64, C.c_int32, C.c_int64, C.c_int32]
     L.qwm_workspace_bytes.restype = C.c_size_t
     L.qwm_zeros_stride.argtypes = [C.c_int64]

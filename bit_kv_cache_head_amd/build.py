@@ -1,6 +1,8 @@
 """Build libquantwm.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m bit_kv_cache_head_amd.build        # or bit_kv_cache_head_amd.build.build()
+    python bit_kv_cache_head_amd/build.py        # or __graft_entry__.build()
+
+Run it as a script (not with -m): importing the package loads the library.
 """
 from __future__ import annotations
 
@@ -15,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libquantwm.so")
-SOURCES = ["api.hip", "stats.hip", "quantize.hip", "attention.hip"]
+SOURCES = ["api.hip", "stats.hip", "quantize.hip", "attention.hip", "reference.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -32,6 +32,7 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
                         qwm_diag* diag, void* ws, hipStream_t stream);
 qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
                             float scale, float* out, float* lse, int32_t* top1, void* ws, hipStream_t stream);
+qwm_status launch_reference_top1(const qwm_tokens* q, const qwm_tokens* k, int32_t* top1, hipStream_t stream);
 size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd);
 size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs);
 
@@ -180,6 +181,19 @@ qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n
   s = check_ws(ws, ws_bytes, attention_ws_bytes(total_keys, q->H, q->T, n_segs));
   if (s != QWM_OK) return s;
   return launch_attention(q, segs, n_segs, total_keys, scale, out, lse, top1, ws, static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_reference_top1(const qwm_tokens* q, const qwm_tokens* k, int32_t* top1, qwm_stream stream) {
+  qwm_status s = check_tokens(q, "queries", false);
+  if (s != QWM_OK) return s;
+  s = check_tokens(k, "keys", false);
+  if (s != QWM_OK) return s;
+  if (q->dtype != QWM_BF16 || k->dtype != QWM_BF16)
+    return fail(QWM_ERR_UNSUPPORTED, "reference top-1: queries and keys must be bf16");
+  if (q->H != k->H) return fail(QWM_ERR_ARG, "reference top-1: queries and keys differ in H");
+  if (k->T > ((int64_t)1 << 31) - 64) return fail(QWM_ERR_UNSUPPORTED, "reference top-1: too many keys");
+  if (!top1 || !aligned(top1, 4)) return fail(QWM_ERR_ARG, "top1: null or misaligned");
+  return launch_reference_top1(q, k, top1, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -183,6 +183,15 @@ qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n
                          int64_t total_keys, float scale, float* out, float* lse, int32_t* top1,
                          void* ws, size_t ws_bytes, qwm_stream stream);
 
+/* Top-1 key of every Query over unquantized keys, the reference side of the
+ * token-shift metric (QuantWM v2 Sec. 5.3: how often the key a Query attends
+ * to most differs between the quantized cache and BF16).
+ * top1[h][i] = argmax_j q_i . k_j (lowest j on ties), logits accumulated in
+ * fp32 from exact bf16 products.  q: [Tq][H][d] bf16, k: [Tk][H][d] bf16 (all
+ * keys in cache order); top1: [H][Tq] int32, device.  No workspace.
+ * Returns QWM_ERR_UNSUPPORTED for fp32 inputs. */
+qwm_status qwm_reference_top1(const qwm_tokens* q, const qwm_tokens* k, int32_t* top1, qwm_stream stream);
+
 /* Bytes of workspace an operation needs (256-byte aligned pointer required).
  * QWM_OP_ATTENTION: T = total cached keys, n = number of queries, n_segs =
  * number of segments (fp16 copies of every segment's centroid tables live in

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "quantwm.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qwm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qwm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -106,3 +106,13 @@ def test_other_validation_paths():
                              None, None, None, 0, None) == 1
     assert lib.qwm_attention(C.byref(t), C.c_void_p(0x1000), 1, 10, C.c_float(-1.0), C.c_void_p(0x1000),
                              None, None, None, 0, None) == 1
+
+
+def test_reference_top1_validation():
+    from bit_kv_cache_head_amd._abi import lib
+    q = _tok(dtype=1)
+    k = _tok(ptr=0x2000, dtype=1, T=100)
+    assert lib.qwm_reference_top1(C.byref(q), C.byref(_tok(ptr=0x2000, dtype=0)), C.c_void_p(0x3000), None) == 2
+    assert lib.qwm_reference_top1(C.byref(q), C.byref(_tok(ptr=0x2000, H=3)), C.c_void_p(0x3000), None) == 1
+    assert lib.qwm_reference_top1(C.byref(q), C.byref(k), None, None) == 1
+    assert b"top1" in lib.qwm_last_error()
