@@ -1,19 +1,30 @@
 """Benchmark of the QuantWM 2-bit KV-cache hot path on one MI355X.
 
-One step = one streaming chunk of the 480p-shaped single-layer workload
-(H = 12 heads, d = 128; 24 cached latent frames of 30x52 = 1,560 tokens plus
-the new frame): update the Query statistics with the previous chunk's Queries
-and re-derive the principal basis, refresh the K and V centroid tables with 3
-warm-started Lloyd iterations, quantize the new Keys (QSAC + PSAC) and Values,
-then attend with the new chunk's 1,560 Queries over all 39,000 cached keys in
-25 compressed segments.  Inputs are seeded synthetic caches resident in HBM.
+Default workload (480p): one step = one streaming chunk of the 480p-shaped
+single-layer cache (H = 12 heads, d = 128; 24 cached latent frames of
+30x52 = 1,560 tokens plus the new frame): update the Query statistics with the
+previous chunk's Queries and re-derive the principal basis, refresh the K and V
+centroid tables with 3 warm-started Lloyd iterations, quantize the new Keys
+(QSAC + PSAC, M = 8) and Values, then attend with the new chunk's 1,560 Queries
+over all 39,000 cached keys in 25 compressed segments.  Inputs are seeded
+synthetic caches resident in HBM.
 
-Prints one JSON line.  `value` = new-chunk tokens per second through the whole
-step; the attention kernel's roofline and the CPU oracle baseline ride along.
+Other workloads (--workload):
+  720p    the same streaming step with H = 40 and 3,600-token chunks
+  tiny    one pass: 4,096 fp32 keys/values, 512 Queries, 10 seeded Lloyd iterations
+  depth   one layer of the full-depth cache (H = 40, 28,000 tokens, 1,560 Queries,
+          10 seeded Lloyd iterations); resident bytes of all 40 layers reported
+  rollout causal rollout of 40 chunks (H = 24) for each ablation (nearest
+          centroid, QSAC, PSAC, QSAC + PSAC); per-ablation throughput and the
+          top-1 shift rate against attention over the bf16 keys
+
+Prints one JSON line.  `value` = new tokens per second through the whole step;
+the attention kernel's roofline and (480p) the CPU oracle baseline ride along.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,12 +36,15 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2516.6
-H, CHUNK, NCHUNK, D = 12, 1560, 25, 128
+D = 128
 ATTN_FLOP_PER_QKH = 2 * (128 + 8) + 2 * 128           # 528: logits (with PSAC) + PV
 KEY_BYTES_PER_TOKEN_HEAD = 256 + 47.5                  # read bf16 key, write packed key
 KEY_TABLE_BYTES_PER_HEAD = 256 * 128 * 2 + 128 * 4 + 128 * 8 * 2   # centroids + w + U
 PACKED_BYTES_PER_KEY_HEAD = 85.0                       # K 47.5 + V 37.5 bytes read by attention
-SEG_TABLE_BYTES_PER_HEAD = 2 * 256 * 128 * 2 + 128 * 8 * 2
+SEG_TABLE_BYTES_PER_HEAD = 2 * 256 * 128 * 2 + 128 * 8 * 2        # K, V centroids + U = 133,120
+BITS_PER_TOKEN_HEAD = 680                              # K 380 + V 300 bits resident
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_480p_step_traffic.md")
+ATTN_SOURCE = os.path.join(ROOT, "bit_kv_cache_head_amd", "csrc", "attention.hip")
 
 
 def log(msg):
@@ -42,36 +56,73 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="480p", choices=["480p", "720p", "tiny", "depth", "rollout"])
+    ap.add_argument("--f-energy", type=float, default=None, help="top-8 Query energy (720p: 0.60 or 0.71)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-queries", type=int, default=48)
+    ap.add_argument("--cpu-sample-queries", type=int, default=480)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run device copies of a known size (reference for HBM byte counters)")
     return ap.parse_args()
 
 
-class Step:
-    """Device state of the workload and the streaming step."""
+COPY_BYTES = 256 * 2 ** 20
+
+
+def copy_calibration(torch):
+    """Three device-to-device copies of 256 MiB: a kernel whose HBM traffic is
+    known (reads and writes COPY_BYTES each), profiled beside the hot path to
+    scale the FETCH_SIZE / WRITE_SIZE counters."""
+    x = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+
+
+def attention_traffic():
+    """HBM bytes per attention launch from the committed counter summary, when
+    it was taken on the attention source as it is now; else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()[:16]
+    fields = {}
+    for line in text.splitlines():
+        for key in ("source_sha", "hbm_bytes_per_launch"):
+            if line.startswith(key + ":"):
+                fields[key] = line.split(":", 1)[1].strip()
+    if fields.get("source_sha") != sha or "hbm_bytes_per_launch" not in fields:
+        return None
+    return float(fields["hbm_bytes_per_launch"])
+
+
+class Stream:
+    """Streaming step: a causally prefilled cache of n-1 chunks plus the step
+    that adds chunk n-1 (480p and 720p workloads)."""
 
     def __init__(self, qwm, torch, w):
         self.qwm, self.torch = qwm, torch
+        self.H, self.chunk, self.nch = w.H, w.chunk, w.n_chunks
         dev = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()
         self.K, self.V, self.Q = dev(w.K), dev(w.V), dev(w.Q)
-        self.st = qwm.QueryStats(H)
+        self.st = qwm.QueryStats(self.H)
         self.segs = []
-        self.tables = []
         prev = None
-        for c in range(NCHUNK - 1):                     # prefill the cache causally
-            sl = w.chunk_slice(c)
-            seg, prev = self._chunk(c, sl, prev, keep=True)
+        for c in range(self.nch - 1):                    # prefill the cache causally
+            seg, prev = self._chunk(c, w.chunk_slice(c), prev)
             self.segs.append(seg)
-            self.tables.append(prev)
         self.prev = prev
-        sl = w.chunk_slice(NCHUNK - 1)
-        self.sl_new = sl
-        self.sl_prevq = w.chunk_slice(NCHUNK - 2)
-        # buffers of the new chunk
+        self.sl_new = w.chunk_slice(self.nch - 1)
+        self.sl_prevq = w.chunk_slice(self.nch - 2)
+        H, T = self.H, self.chunk
         self.Ck = torch.empty(H, 256, D, dtype=torch.bfloat16, device="cuda")
         self.Cv = torch.empty_like(self.Ck)
-        self.kp = qwm.PackedChunk(CHUNK, H, True)
-        self.vp = qwm.PackedChunk(CHUNK, H, False)
+        self.kp = qwm.PackedChunk(T, H, True)
+        self.vp = qwm.PackedChunk(T, H, False)
         self.segs.append((self.kp, self.vp, self.Ck, self.Cv, self.st.U))
         self.dsegs, self.total = qwm.segments_tensor(self.segs)
         self.diag = qwm.new_diag()
@@ -79,8 +130,11 @@ class Step:
         # a side stream, overlapped with the Lloyd refresh
         self.side = torch.cuda.Stream()
         self.stats_done = torch.cuda.Event()
+        self.queries = T
+        self.new_tokens = T
+        self.stage_names = ["launch_stats", "lloyd_kv", "keys_incl_stats_wait", "values", "attention"]
 
-    def _chunk(self, c, sl, prev, keep):
+    def _chunk(self, c, sl, prev):
         qwm = self.qwm
         K, V = self.K[sl], self.V[sl]
         if prev is None:
@@ -94,15 +148,14 @@ class Step:
             U = self.st.U.clone()
             kp = qwm.quantize_keys(K, Ck, self.st.w, U, M=8, flags=3)
         vp = qwm.quantize_values(V, Cv)
-        if c < NCHUNK - 2:        # the step itself adds the previous chunk's Queries
+        if c < self.nch - 2:        # the step itself adds the previous chunk's Queries
             qwm.update_query_stats(self.Q[sl], self.st, compute_basis=True)
         return (kp, vp, Ck, Cv, U), (Ck, Cv)
 
     def run(self, events=None):
-        qwm = self.qwm
+        qwm, torch = self.qwm, self.torch
         rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
         K, V = self.K[self.sl_new], self.V[self.sl_new]
-        torch = self.torch
         main = torch.cuda.current_stream()
         rec(0)
         self.side.wait_stream(main)
@@ -118,59 +171,286 @@ class Step:
         rec(3)
         qwm.quantize_values(V, self.Cv, out=self.vp, diag=self.diag)
         rec(4)
-        out, _, _ = qwm.attention(self.Q[self.sl_new], self.dsegs, NCHUNK, self.total)
+        out, _, _ = qwm.attention(self.Q[self.sl_new], self.dsegs, self.nch, self.total)
         rec(5)
         return out
 
 
-def cpu_baseline(w, nq):
-    """The oracle (untuned) on one head of the step; extrapolated to the whole
-    step (12 heads, 1,560 queries).  Attention is timed on `nq` sampled queries
-    over all 25 segments, whose packed contents are seeded random arrays."""
+class OnePass:
+    """One pass over a single chunk (tiny, and one layer of depth): statistics
+    and basis from the Queries, 10 seeded Lloyd iterations for K and V, keys,
+    values, attention of the Queries over the chunk."""
+
+    def __init__(self, qwm, torch, w):
+        self.qwm, self.torch = qwm, torch
+        self.H, self.chunk = w.H, w.chunk
+        dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        dev = lambda a: torch.from_numpy(a).to(dt).cuda()
+        self.K, self.V, self.Q = dev(w.K), dev(w.V), dev(w.Q)
+        H, T = self.H, w.T
+        self.st = qwm.QueryStats(H)
+        self.Ck = torch.empty(H, 256, D, dtype=torch.bfloat16, device="cuda")
+        self.Cv = torch.empty_like(self.Ck)
+        self.kp = qwm.PackedChunk(T, H, True)
+        self.vp = qwm.PackedChunk(T, H, False)
+        self.dsegs, self.total = qwm.segments_tensor([(self.kp, self.vp, self.Ck, self.Cv, self.st.U)])
+        self.diag = qwm.new_diag()
+        self.nch = 1
+        self.queries = int(w.Q.shape[0])
+        self.new_tokens = T
+        self.stage_names = ["stats_and_basis", "lloyd_kv_10", "keys", "values", "attention"]
+
+    def run(self, events=None):
+        qwm = self.qwm
+        rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+        rec(0)
+        self.st.reset()
+        qwm.update_query_stats(self.Q, self.st, compute_basis=True)
+        rec(1)
+        qwm.build_centroids(self.K, 10, seed=1, out=self.Ck, diag=self.diag)
+        qwm.build_centroids(self.V, 10, seed=2, out=self.Cv, diag=self.diag)
+        rec(2)
+        qwm.quantize_keys(self.K, self.Ck, self.st.w, self.st.U, M=8, flags=3, out=self.kp, diag=self.diag)
+        rec(3)
+        qwm.quantize_values(self.V, self.Cv, out=self.vp, diag=self.diag)
+        rec(4)
+        out, _, _ = qwm.attention(self.Q, self.dsegs, 1, self.total)
+        rec(5)
+        return out
+
+
+def cpu_baseline(w, nq, heads=6):
+    """The oracle (untuned) on a bounded sample of the 480p step: the quantize
+    side (statistics + Jacobi basis, 3 + 3 Lloyd iterations, QSAC + PSAC keys,
+    values of the new chunk) for `heads` of the 12 heads, attention of `nq`
+    Queries of head 0 over all 25 segments (seeded random packed contents);
+    extrapolated to the whole step (12 heads, 1,560 Queries)."""
     import numpy as np
-    from oracle import attention as OA, formats as F, lloyd as OL, quantize as Qz, stats as OS
+    from oracle import attention as OA, lloyd as OL, quantize as Qz, stats as OS
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    h = 0
+    H, CHUNK, NCHUNK = w.H, w.chunk, w.n_chunks
     sl = w.chunk_slice(NCHUNK - 1)
     slp = w.chunk_slice(NCHUNK - 2)
-    K = w.K[sl, h].astype(np.float64)
-    Vv = w.V[sl, h].astype(np.float64)
-    S0, n0 = OS.update(np.zeros((D, D)), 0, w.Q[:slp.start, h])
-    prevk = OL.lloyd(w.K[slp, h].astype(np.float64), 256, 1, seed=1, head=h)
-    prevv = OL.lloyd(w.V[slp, h].astype(np.float64), 256, 1, seed=2, head=h)
-    t0 = time.perf_counter()
-    S, n = OS.update(S0, n0, w.Q[slp, h])
-    basis = OS.principal_basis(S, n)
-    wts = OS.channel_weights(S, n)
-    Ck = OL.lloyd(K, 256, 3, init=prevk)
-    Cv = OL.lloyd(Vv, 256, 3, init=prevv)
-    kq = Qz.quantize_keys(K, Ck, wts, basis["U_bf16"], M=8)
-    vq = Qz.quantize_values(Vv, Cv)
-    t_quant = time.perf_counter() - t0
+    t_quant = 0.0
+    tables = None
+    for h in range(heads):
+        K = w.K[sl, h].astype(np.float64)
+        Vv = w.V[sl, h].astype(np.float64)
+        S0, n0 = OS.update(np.zeros((D, D)), 0, w.Q[:slp.start, h])
+        prevk = OL.lloyd(w.K[slp, h].astype(np.float64), 256, 1, seed=1, head=h)
+        prevv = OL.lloyd(w.V[slp, h].astype(np.float64), 256, 1, seed=2, head=h)
+        t0 = time.perf_counter()
+        S, n = OS.update(S0, n0, w.Q[slp, h])
+        basis = OS.principal_basis(S, n)
+        wts = OS.channel_weights(S, n)
+        Ck = OL.lloyd(K, 256, 3, init=prevk)
+        Cv = OL.lloyd(Vv, 256, 3, init=prevv)
+        Qz.quantize_keys(K, Ck, wts, basis["U_bf16"], M=8)
+        Qz.quantize_values(Vv, Cv)
+        t_quant += time.perf_counter() - t0
+        if tables is None:
+            tables = (Ck, Cv, basis["U_bf16"])
     rng = np.random.default_rng(5)
     segs = []
+    Ck, Cv, U = tables
     for s in range(NCHUNK):
         q = rng.integers(0, 4, (CHUNK, 128)).astype(np.uint8)
         z = rng.integers(0, 4, (CHUNK, 2)).astype(np.uint8)
         sc = rng.uniform(0.01, 0.2, (CHUNK, 2)).astype(np.float16).astype(np.float64)
         segs.append(dict(k_idx=rng.integers(0, 256, CHUNK), k_q=q, k_scale=sc, k_zero=z,
                          k_Cq=rng.integers(-127, 128, (CHUNK, 8)), k_cs=np.full(CHUNK, 1e-3),
-                         k_centroids=Ck, U=basis["U_bf16"], v_idx=rng.integers(0, 256, CHUNK), v_q=q,
+                         k_centroids=Ck, U=U, v_idx=rng.integers(0, 256, CHUNK), v_q=q,
                          v_scale=sc, v_zero=z, v_centroids=Cv))
-    Qs = w.Q[sl, h][:nq].astype(np.float64)
+    Qs = w.Q[sl, 0][:nq].astype(np.float64)
     t1 = time.perf_counter()
     OA.cache_attention(Qs, segs, 1 / np.sqrt(D))
     t_attn = time.perf_counter() - t1
-    step_s = H * (t_quant + t_attn * CHUNK / nq)
-    return {"value": CHUNK / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"head 0 of the step: stats+Jacobi basis, 3+3 Lloyd iterations, QSAC+PSAC keys and "
-                      f"values of the 1,560-token chunk ({t_quant:.2f} s), attention of {nq} queries over "
-                      f"39,000 keys ({t_attn:.2f} s); extrapolated x12 heads and x{CHUNK // nq} queries",
+    step_s = t_quant * H / heads + t_attn * H * CHUNK / nq
+    return {"value": round(CHUNK / step_s, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"quantize side of the step for {heads} of {H} heads: stats + Jacobi basis, 3 + 3 Lloyd "
+                      f"iterations, QSAC + PSAC keys and values of the 1,560-token chunk ({t_quant:.2f} s); "
+                      f"attention of {nq} Queries of one head over 39,000 keys ({t_attn:.2f} s); extrapolated "
+                      f"to {H} heads and 1,560 Queries",
             "seconds_sampled": round(t_quant + t_attn, 2)}
+
+
+def keys_bulk(qwm, torch, Kall, table, st):
+    """Key quantization of many tokens in one call (QSAC + PSAC): HBM rate."""
+    H = Kall.shape[1]
+    kb = qwm.PackedChunk(Kall.shape[0], H, True)
+    for _ in range(2):
+        qwm.quantize_keys(Kall, table, st.w, st.U, M=8, flags=3, out=kb)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    nb = 5
+    for _ in range(nb):
+        qwm.quantize_keys(Kall, table, st.w, st.U, M=8, flags=3, out=kb)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / nb
+    byts = KEY_BYTES_PER_TOKEN_HEAD * Kall.shape[0] * H + KEY_TABLE_BYTES_PER_HEAD * H
+    return {"tokens": int(Kall.shape[0]), "token_heads": int(Kall.shape[0]) * H, "ms": round(ms, 4),
+            "tokens_per_s": round(Kall.shape[0] / (ms * 1e-3), 1),
+            "GBps": round(byts / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def timed_steps(step, torch, steps, warmup):
+    import numpy as np
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    step.diag.zero_()
+    step.run()
+    torch.cuda.synchronize()
+    diag_step = step.diag.tolist()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        step.run(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t_start.elapsed_time(t_end) / steps
+    stage = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(step.stage_names)}
+    return ms, stage, wall, diag_step
+
+
+def roofline(step, attn_ms):
+    flops = ATTN_FLOP_PER_QKH * step.queries * step.total * step.H
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    attn_bytes = PACKED_BYTES_PER_KEY_HEAD * step.total * step.H + SEG_TABLE_BYTES_PER_HEAD * step.H * step.nch \
+        + step.queries * step.H * (256 + 512)
+    return {"kernel": "attention (fused dequant + PSAC + online softmax; the call includes the fp16 table "
+                      "conversion and the split merge)",
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+            "flop_per_launch": flops, "avg_launch_ms": round(attn_ms, 4),
+            "algorithmic_bytes_per_launch": int(attn_bytes),
+            "compressed_GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1)}
+
+
+def base_result(args, metric_value, ms, dtype, config):
+    return {
+        "metric": "Key tokens/s quantized (QSAC+PSAC) + compressed-cache attention MFMA %/HBM GB/s",
+        "value": round(metric_value, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic", "config": config,
+    }
+
+
+def run_stream_or_pass(args, qwm, torch, w):
+    if args.workload in ("480p", "720p"):
+        log(f"prefilling {w.n_chunks - 1} chunks")
+        step = Stream(qwm, torch, w)
+        config = {"workload": f"{args.workload}-shaped single layer, streaming step: H={w.H}, d=128, "
+                              f"{w.n_chunks - 1} cached chunks + 1 new chunk of {w.chunk:,} tokens "
+                              f"({w.chunk * w.n_chunks:,} keys in {w.n_chunks} segments), {w.chunk:,} queries; "
+                              f"M=8, r=8, 256 centroids, 3 warm Lloyd iterations",
+                  "heads": w.H, "chunk_tokens": w.chunk, "cached_keys": w.chunk * w.n_chunks, "queries": w.chunk}
+    else:
+        step = OnePass(qwm, torch, w)
+        config = {"workload": f"{args.workload}: one pass over {w.T:,} tokens x {w.H} heads ({w.dtype}), "
+                              f"{w.Q.shape[0]:,} queries; 10 seeded Lloyd iterations, M=8, r=8",
+                  "heads": w.H, "tokens": w.T, "queries": int(w.Q.shape[0])}
+    if args.f_energy is not None:
+        config["f_energy"] = args.f_energy
+    torch.cuda.synchronize()
+    log("timing")
+    ms, stage, wall, diag_step = timed_steps(step, torch, args.steps, args.warmup)
+    res = base_result(args, step.new_tokens / (ms * 1e-3), ms, "f32" if w.dtype == "f32" else "bf16", config)
+    res["roofline"] = roofline(step, stage["attention"])
+    if args.workload == "480p":
+        res["roofline"]["traffic"] = attention_traffic()
+    res["stages_ms"] = {k: round(v, 4) for k, v in stage.items()}
+    if isinstance(step, Stream):
+        res["keys_step"] = {"token_heads": step.chunk * step.H,
+                            "ms_incl_stats_wait": round(stage["keys_incl_stats_wait"], 4)}
+        res["keys_bulk"] = keys_bulk(qwm, torch, step.K[: (step.nch - 1) * step.chunk], step.prev[0], step.st)
+    else:
+        res["keys_bulk"] = keys_bulk(qwm, torch, step.K, step.Ck, step.st)
+    res["wall_s_timed"] = round(wall, 3)
+    res["exact_fallbacks_per_step"] = int(diag_step[1])
+    res["nonfinite_rows_per_step"] = int(diag_step[0])
+    res["eig_iterations"] = step.st.iters.tolist()
+    if args.workload == "depth":
+        layers = 40
+        resident = layers * w.H * (w.T * BITS_PER_TOKEN_HEAD // 8 + SEG_TABLE_BYTES_PER_HEAD)
+        bf16 = layers * w.H * w.T * 2 * D * 2
+        res["resident"] = {"layers": layers, "bytes": int(resident), "GiB": round(resident / 2 ** 30, 3),
+                           "bf16_GiB": round(bf16 / 2 ** 30, 3), "ratio": round(bf16 / resident, 3),
+                           "per_layer_ms": round(ms, 3), "all_layers_s": round(layers * ms * 1e-3, 3),
+                           "note": "one synthetic layer timed; the 40 layers do identical work"}
+    if args.workload == "480p" and not args.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_queries)
+    return res
+
+
+def run_rollout(args, qwm, torch, w):
+    """Causal rollout for every ablation: tokens/s and the token-shift rate
+    (fraction of (head, Query) pairs whose top-1 key under the quantized cache
+    differs from the top-1 over the bf16 keys)."""
+    import numpy as np
+    dev = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()
+    Kd, Vd, Qd = dev(w.K), dev(w.V), dev(w.Q)
+    H, T, nch = w.H, w.chunk, w.n_chunks
+    names = {0: "nearest", 1: "qsac", 2: "psac", 3: "qsac+psac"}
+    refs = []
+    for t in range(nch):
+        sl = w.chunk_slice(t)
+        refs.append(qwm.reference_top1(Qd[sl], Kd[: sl.stop]))
+    torch.cuda.synchronize()
+    out = {}
+    for flags in (0, 1, 2, 3):
+        for _ in range(2):                        # the first pass warms up, the second is timed
+            st = qwm.QueryStats(H)
+            segs, prev, tops = [], None, []
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for t in range(nch):
+                sl = w.chunk_slice(t)
+                K, V = Kd[sl], Vd[sl]
+                if prev is None:
+                    Ck = qwm.build_centroids(K, 10, seed=1)
+                    Cv = qwm.build_centroids(V, 10, seed=2)
+                    U = None
+                    kp = qwm.quantize_keys(K, Ck, None, None, M=8, flags=flags)
+                else:
+                    Ck = qwm.build_centroids(K, 3, init=prev[0])
+                    Cv = qwm.build_centroids(V, 3, init=prev[1])
+                    U = st.U.clone() if flags & 2 else None
+                    kp = qwm.quantize_keys(K, Ck, st.w if flags & 1 else None, U, M=8, flags=flags)
+                vp = qwm.quantize_values(V, Cv)
+                segs.append((kp, vp, Ck, Cv, U))
+                dsegs, total = qwm.segments_tensor(segs)
+                _, _, top1 = qwm.attention(Qd[sl], dsegs, len(segs), total, want_top1=True)
+                tops.append(top1)
+                qwm.update_query_stats(Qd[sl], st, compute_basis=True)   # causal: feeds the next chunks
+                prev = (Ck, Cv)
+            torch.cuda.synchronize()
+            secs = time.perf_counter() - t0
+        rates = [float((tops[t] != refs[t]).float().mean().item()) for t in range(nch)]
+        out[names[flags]] = {"tokens_per_s": round(nch * T / secs, 1), "seconds": round(secs, 4),
+                             "shift_rate": round(float(np.mean(rates[1:])), 5),
+                             "shift_rate_cold_start": round(rates[0], 5)}
+        log(f"  {names[flags]}: {out[names[flags]]}")
+    config = {"workload": f"rollout: H={H}, d=128, {nch} chunks x {T:,} tokens, causal statistics, 10 seeded + "
+                          f"3 warm Lloyd iterations per chunk, attention of each chunk's Queries over the cache so far",
+              "heads": H, "chunk_tokens": T, "chunks": nch}
+    best = out["qsac+psac"]
+    res = base_result(args, best["tokens_per_s"], best["seconds"] * 1e3 / nch, "bf16", config)
+    res["steps"], res["warmup"] = nch, 1
+    res["ablations"] = out
+    return res
 
 
 def main():
@@ -179,93 +459,19 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is not "
               f"part of this build", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     import bit_kv_cache_head_amd as qwm
     import datagen
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    log("generating the 480p workload")
-    w = datagen.make_workload("480p")
-    log("prefilling 24 chunks")
-    step = Step(qwm, torch, w)
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step.run()
-    torch.cuda.synchronize()
-    step.diag.zero_()
-    step.run()
-    torch.cuda.synchronize()
-    diag_step = step.diag.tolist()
-    log("timing")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        step.run(evs[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = t_start.elapsed_time(t_end) / args.steps
-    names = ["launch_stats", "lloyd_kv", "keys_incl_stats_wait", "values", "attention"]
-    stage = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
-    attn_ms = stage["attention"]
-    flops = ATTN_FLOP_PER_QKH * CHUNK * step.total * H
-    achieved = flops / (attn_ms * 1e-3) / 1e12
-    attn_bytes = PACKED_BYTES_PER_KEY_HEAD * step.total * H + SEG_TABLE_BYTES_PER_HEAD * H * NCHUNK \
-        + CHUNK * H * (256 + 512)
-    key_bytes = KEY_BYTES_PER_TOKEN_HEAD * CHUNK * H + KEY_TABLE_BYTES_PER_HEAD * H
-
-    # bulk key throughput: the 24 cached chunks' keys in one call (QSAC + PSAC)
-    Kall = step.K[: (NCHUNK - 1) * CHUNK]
-    kb = qwm.PackedChunk(Kall.shape[0], H, True)
-    for _ in range(2):
-        qwm.quantize_keys(Kall, step.prev[0], step.st.w, step.st.U, M=8, flags=3, out=kb)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    nb = 5
-    for _ in range(nb):
-        qwm.quantize_keys(Kall, step.prev[0], step.st.w, step.st.U, M=8, flags=3, out=kb)
-    e1.record()
-    torch.cuda.synchronize()
-    bulk_ms = e0.elapsed_time(e1) / nb
-    bulk_bytes = KEY_BYTES_PER_TOKEN_HEAD * Kall.shape[0] * H + KEY_TABLE_BYTES_PER_HEAD * H
-
-    res = {
-        "metric": "Key tokens/s quantized (QSAC+PSAC) + compressed-cache attention MFMA %/HBM GB/s",
-        "value": round(CHUNK / (ms * 1e-3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "480p-shaped single layer, streaming step: H=12, d=128, 24 cached chunks "
-                               "+ 1 new chunk of 1,560 tokens (39,000 keys in 25 segments), 1,560 queries; "
-                               "M=8, r=8, 256 centroids, 3 warm Lloyd iterations",
-                   "heads": H, "chunk_tokens": CHUNK, "cached_keys": int(step.total), "queries": CHUNK},
-        "roofline": {"kernel": "attention (fused dequant + PSAC + online softmax; includes the split merge)",
-                     "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                     "flop_per_launch": flops, "avg_launch_ms": round(attn_ms, 4),
-                     "compressed_GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1)},
-        "stages_ms": {k: round(v, 4) for k, v in stage.items()},
-        "keys_step": {"token_heads": CHUNK * H, "ms_incl_stats_wait": round(stage["keys_incl_stats_wait"], 4)},
-        "keys_bulk": {"tokens": int(Kall.shape[0]), "token_heads": int(Kall.shape[0]) * H,
-                      "ms": round(bulk_ms, 4),
-                      "tokens_per_s": round(Kall.shape[0] / (bulk_ms * 1e-3), 1),
-                      "GBps": round(bulk_bytes / (bulk_ms * 1e-3) / 1e9, 1),
-                      "hbm_frac": round(bulk_bytes / (bulk_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
-        "wall_s_timed": round(wall, 3),
-        "exact_fallbacks_per_step": int(diag_step[1]), "nonfinite_rows_per_step": int(diag_step[0]),
-        "eig_iterations": step.st.iters.tolist(),
-    }
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle sample")
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_queries)
+    if args.copy_calibration:
+        copy_calibration(torch)
+    log(f"generating the {args.workload} workload")
+    w = datagen.make_workload(args.workload, f_energy=args.f_energy)
+    if args.workload == "rollout":
+        res = run_rollout(args, qwm, torch, w)
+    else:
+        res = run_stream_or_pass(args, qwm, torch, w)
     print(json.dumps(res), flush=True)
 
 

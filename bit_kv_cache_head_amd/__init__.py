@@ -85,6 +85,13 @@ class QueryStats:
         self.energy = torch.zeros(H, dtype=torch.float32, device=device)
         self.iters = torch.zeros(H, dtype=torch.int32, device=device)
 
+    def reset(self):
+        """Back to the cold start (no Queries seen)."""
+        self.S.zero_()
+        self.n.zero_()
+        self.w.fill_(1.0)
+        self.U.zero_()
+
     def desc(self) -> QStats:
         return QStats(_ptr(self.S), _ptr(self.n), _ptr(self.w), _ptr(self.U), _ptr(self.lam),
                       _ptr(self.energy), _ptr(self.iters), self.H, D, R, 0)
