@@ -126,13 +126,17 @@ class Stream:
         self.segs.append((self.kp, self.vp, self.Ck, self.Cv, self.st.U))
         self.dsegs, self.total = qwm.segments_tensor(self.segs)
         self.diag = qwm.new_diag()
-        # the Query statistics and basis only feed the key quantization: they run on
-        # a side stream, overlapped with the Lloyd refresh
+        self.vdiag = qwm.new_diag()      # the V side counts on its own stream
+        # the Query statistics and basis only feed the key quantization, and the V side
+        # (table refresh, values) is independent of the K side: each runs on its own
+        # stream, overlapped with the K table refresh
         self.side = torch.cuda.Stream()
+        self.vside = torch.cuda.Stream()
         self.stats_done = torch.cuda.Event()
+        self.v_done = torch.cuda.Event()
         self.queries = T
         self.new_tokens = T
-        self.stage_names = ["launch_stats", "lloyd_kv", "keys_incl_stats_wait", "values", "attention"]
+        self.stage_names = ["launch_side_streams", "lloyd_k", "keys_incl_stats_wait", "values_wait", "attention"]
 
     def _chunk(self, c, sl, prev):
         qwm = self.qwm
@@ -159,17 +163,21 @@ class Stream:
         main = torch.cuda.current_stream()
         rec(0)
         self.side.wait_stream(main)
+        self.vside.wait_stream(main)
         with torch.cuda.stream(self.side):
             qwm.update_query_stats(self.Q[self.sl_prevq], self.st, compute_basis=True)
             self.stats_done.record(self.side)
+        with torch.cuda.stream(self.vside):
+            qwm.build_centroids(V, 3, init=self.prev[1], out=self.Cv, diag=self.vdiag)
+            qwm.quantize_values(V, self.Cv, out=self.vp, diag=self.vdiag)
+            self.v_done.record(self.vside)
         rec(1)
         qwm.build_centroids(K, 3, init=self.prev[0], out=self.Ck, diag=self.diag)
-        qwm.build_centroids(V, 3, init=self.prev[1], out=self.Cv, diag=self.diag)
         rec(2)
         main.wait_event(self.stats_done)
         qwm.quantize_keys(K, self.Ck, self.st.w, self.st.U, M=8, flags=3, out=self.kp, diag=self.diag)
         rec(3)
-        qwm.quantize_values(V, self.Cv, out=self.vp, diag=self.diag)
+        main.wait_event(self.v_done)
         rec(4)
         out, _, _ = qwm.attention(self.Q[self.sl_new], self.dsegs, self.nch, self.total)
         rec(5)
@@ -304,10 +312,12 @@ def timed_steps(step, torch, steps, warmup):
     for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
-    step.diag.zero_()
+    diags = [step.diag] + ([step.vdiag] if hasattr(step, "vdiag") else [])
+    for d in diags:
+        d.zero_()
     step.run()
     torch.cuda.synchronize()
-    diag_step = step.diag.tolist()
+    diag_step = sum(d for d in diags).tolist()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

@@ -51,17 +51,22 @@ def zeros_stride(T: int) -> int:
 
 
 class Workspace:
-    """Grow-only device scratch buffer (256-byte aligned by the caching allocator)."""
+    """Grow-only device scratch buffers (256-byte aligned by the caching
+    allocator), one per stream: calls enqueued on different streams may run
+    concurrently and must not share scratch memory."""
 
     def __init__(self):
-        self.buf = None
+        self.bufs = {}
 
     def get(self, nbytes: int, device) -> tuple:
         if nbytes == 0:
             return C.c_void_p(0), 0
-        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        return C.c_void_p(self.buf.data_ptr()), self.buf.numel()
+        key = (device, torch.cuda.current_stream(device).cuda_stream)
+        buf = self.bufs.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            self.bufs[key] = buf
+        return C.c_void_p(buf.data_ptr()), buf.numel()
 
 
 _WS = Workspace()

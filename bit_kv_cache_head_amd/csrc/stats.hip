@@ -107,7 +107,12 @@ constexpr int P = 16;
 constexpr int PP = P + 1;             // padded row
 constexpr int EIG_ROUNDS = 24;        // Rayleigh-Ritz checks
 constexpr int POWER_STEPS = 3;        // products with A between re-orthonormalizations
-constexpr int ORTH_PER_ROUND = 3;
+constexpr int ORTH_PER_ROUND = 4;
+// Residual test |A x - theta x| <= EIG_RESIDUAL * theta_1: the eigenvector error
+// it leaves (~ residual / eigen-gap, ~1e-6 here) is at the level of the
+// statistics' own rounding (fp32 partial sums of bf16 products, 1e-6
+// relative) and far below half a bf16 ulp of the stored basis.
+constexpr double EIG_RESIDUAL = 1e-7;
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
@@ -471,7 +476,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ S, 
 #pragma unroll
       for (int j = 0; j < R; ++j) {
         const double res = sqrt(sm.red[0][j] + sm.red[1][j]);
-        ok &= (res <= 1e-9 * scale) ? 1 : 0;
+        ok &= (res <= EIG_RESIDUAL * scale) ? 1 : 0;
       }
       if (ok) { converged = 1; break; }   // uniform: every thread reads the same values
     }
