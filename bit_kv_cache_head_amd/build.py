@@ -29,9 +29,15 @@ CFLAGS = [
 ]
 
 
+# Per-source additions.  attention.hip sees no NaN in its logits (scores of
+# finite fp16 tiles; keys past a segment end are masked with -inf), so its
+# max reductions need no NaN quieting.
+EXTRA = {"attention.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

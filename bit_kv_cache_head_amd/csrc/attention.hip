@@ -55,11 +55,17 @@ struct AttnArgs {
 // channels sit 16 bits apart in the packed code word, so one shift and one
 // mask put both into the two fp16 halves.  Q uses the same order (the
 // contraction does not care); V_hat keeps the natural order.
+// Rows are padded by 16 bytes: 16 lanes reading the same 16-byte column of 16
+// consecutive rows then cover all 64 banks once, and every LDS address is a
+// per-thread base plus a compile-time offset.
+constexpr int KSTR = 2 * D + 16;      // bytes per K0_hat row
+constexpr int VSTR = 2 * AT_K + 16;   // bytes per V_hat^T row
 struct AttnBuf {
-  _Float16 khat[AT_K * D];     // [key][128 permuted], 16-byte chunk c of row k at (c ^ (k & 15))
-  _Float16 chat[AT_K][16];     // PSAC channels: c_scale * c (8) + zero padding (8)
-  _Float16 vt[D * AT_K];       // [channel][slot], chunk c of row ch at (c ^ ((ch >> 1) & 7))
+  uint8_t khat[AT_K * KSTR];   // [key][128 permuted channels] fp16
+  uint8_t vt[D * VSTR];        // [channel][64 keys in vslot order] fp16
+  uint8_t chat[AT_K * 16];     // [key][8] fp16: c_scale * c
 };
+constexpr int BUF_BYTES = (int)sizeof(AttnBuf);
 
 // slot of a key in the transposed V tile: bits 2 and 3 swapped (matches the
 // register order of the probabilities produced by the S^T MFMA)
@@ -77,6 +83,20 @@ __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uin
 // two INT2 codes 16 bits apart (at bit `sh` and `sh + 16`) -> fp16 pair (1024 + q0, 1024 + q1)
 __device__ __forceinline__ h2 code_pair(uint32_t w, int sh) {
   return as_h2(((w >> sh) & 0x00030003u) | 0x64006400u);
+}
+// The same with both masks in registers (one v_and_or_b32 instead of an AND
+// and an OR: a VOP3 instruction encodes only one literal).
+struct CodeMasks {
+  uint32_t q, e;   // 0x00030003, 0x64006400
+};
+__device__ __forceinline__ CodeMasks code_masks() {
+  CodeMasks m;
+  asm("v_mov_b32 %0, 0x30003" : "=v"(m.q));
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(m.e));
+  return m;
+}
+__device__ __forceinline__ h2 code_pair(uint32_t w, int sh, const CodeMasks& m) {
+  return as_h2(((w >> sh) & m.q) | m.e);
 }
 
 // ---------------------------------------------------------------------------
@@ -119,186 +139,356 @@ __global__ __launch_bounds__(256) void attention_tables_kernel(const qwm_segment
 
 __device__ __forceinline__ cseg& seg_at(const AttnArgs& a, int i) { return ((cseg*)a.segs)[i]; }
 
-// Position in the flattened (segment, tile) sequence of one split.
-struct TileIt {
-  int seg;          // segment index, n_segs when done
-  int64_t tile;     // tile index within the segment
-  int64_t t_hi;     // end of this split's tile range in the segment
+__device__ __forceinline__ int ntiles(int64_t T) { return (int)((T + AT_K - 1) / AT_K); }
+
+// ---------------------------------------------------------------------------
+// Tile positions.  The tiles of all segments, in segment order, form one
+// sequence; split p of nsplit owns a contiguous share of it.  A position is
+// wave-uniform (scalar registers).
+// ---------------------------------------------------------------------------
+struct Pos {
+  int seg;          // segment index
+  int tile;         // tile index within the segment
   int64_t kbase;    // global index of the segment's first key
 };
 
-__device__ __forceinline__ void seg_range(const AttnArgs& a, int seg, int split, int64_t& lo, int64_t& hi) {
-  const int64_t T = seg_at(a, seg).T;
-  const int64_t nt = (T + AT_K - 1) / AT_K;
-  lo = nt * split / a.nsplit;
-  hi = nt * (split + 1) / a.nsplit;
-}
-
-// first tile at or after segment `seg` (kbase = first key of `seg`)
-__device__ __forceinline__ TileIt first_tile(const AttnArgs& a, int seg, int64_t kbase, int split) {
-  TileIt it;
-  while (seg < a.n_segs) {
-    int64_t lo, hi;
-    seg_range(a, seg, split, lo, hi);
-    if (lo < hi) { it.seg = seg; it.tile = lo; it.t_hi = hi; it.kbase = kbase; return it; }
-    kbase += seg_at(a, seg).T;
-    ++seg;
-  }
-  it.seg = a.n_segs; it.tile = 0; it.t_hi = 0; it.kbase = kbase;
-  return it;
-}
-
-// The tile iterator is wave-uniform; saying so keeps it in scalar registers, so
-// descriptor reads stay scalar loads.
 __device__ __forceinline__ int64_t sfl64(int64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
-__device__ __forceinline__ TileIt uni(const TileIt& t) {
-  TileIt u;
-  u.seg = __builtin_amdgcn_readfirstlane(t.seg);
-  u.tile = sfl64(t.tile);
-  u.t_hi = sfl64(t.t_hi);
-  u.kbase = sfl64(t.kbase);
-  return u;
+
+// Number of tiles over all segments (every lane gets the total).
+__device__ int count_tiles(const AttnArgs& a, int lane) {
+  int tot = 0;
+  for (int base = 0; base < a.n_segs; base += 64) {
+    const int s = base + lane;
+    int nt = s < a.n_segs ? ntiles(a.segs[s].T) : 0;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) nt += __shfl_xor(nt, d, 64);
+    tot += nt;
+  }
+  return __builtin_amdgcn_readfirstlane(tot);
 }
 
-__device__ __forceinline__ TileIt next_tile(const AttnArgs& a, const TileIt& it, int split) {
-  if (it.tile + 1 < it.t_hi) { TileIt n = it; n.tile += 1; return n; }
-  return first_tile(a, it.seg + 1, it.kbase + seg_at(a, it.seg).T, split);
+// Position of tile g of the sequence (0 <= g < total): a prefix scan of the
+// per-segment tile counts, 64 segments at a time.
+__device__ Pos locate(const AttnArgs& a, int g, int lane) {
+  int carry = 0;
+  int64_t kcarry = 0;
+  for (int base = 0; base < a.n_segs; base += 64) {
+    const int s = base + lane;
+    const int64_t T = s < a.n_segs ? a.segs[s].T : 0;
+    const int nt = ntiles(T);
+    int inc = nt;
+    int64_t kinc = T;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(inc, d, 64);
+      const int64_t ko = __shfl_up(kinc, d, 64);
+      if (lane >= d) { inc += o; kinc += ko; }
+    }
+    const uint64_t hit = __ballot(carry + inc > g);
+    if (hit != 0) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      Pos p;
+      p.seg = base + l;
+      p.tile = g - carry - __shfl(inc - nt, l, 64);
+      p.kbase = kcarry + __shfl(kinc - T, l, 64);
+      p.seg = __builtin_amdgcn_readfirstlane(p.seg);
+      p.tile = __builtin_amdgcn_readfirstlane(p.tile);
+      p.kbase = sfl64(p.kbase);
+      return p;
+    }
+    carry += __shfl(inc, 63, 64);
+    kcarry += __shfl(kinc, 63, 64);
+  }
+  Pos p;
+  p.seg = a.n_segs - 1; p.tile = 0; p.kbase = 0;   // not reached for g < total
+  return p;
 }
 
-// Per-thread share of one tile, loaded in three stages so that no load waits
-// for another inside the loop:
-//   idx  (issued three tiles ahead): the centroid index bytes;
-//   raw  (two tiles ahead): codes, scales, zero-point bytes, PSAC bytes, plus
-//        the centroid rows (their idx arrived one iteration earlier);
-//   all arithmetic on these bytes happens in dequant_tile.
-// Loads never branch: keys past the segment end read the segment's last key
-// and are zeroed in dequant_tile.
+// The next tile (the caller knows one exists); T = keys of p's segment.
+__device__ __forceinline__ Pos advance(const AttnArgs& a, Pos p, int64_t T) {
+  p.tile += 1;
+  while ((int64_t)p.tile * AT_K >= T && p.seg + 1 < a.n_segs) {
+    p.kbase += T;
+    p.seg += 1;
+    p.tile = 0;
+    T = seg_at(a, p.seg).T;
+  }
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Loads.  Every packed array is read through a buffer descriptor whose base
+// is the tile's first row and whose size covers only the rows that exist, so
+// rows past the segment end read as zeros (no clamping or masking in the
+// loop) and each thread's byte offsets are the same for every tile.
+// Keys past the end thus dequantize to centroid 0 of their table (finite);
+// their logits are masked before the softmax.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_CFG = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ rsrc_t buf(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, RSRC_CFG);
+}
+__device__ __forceinline__ uint32_t ld8(rsrc_t r, int off) { return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0); }
+__device__ __forceinline__ uint32_t ld16(rsrc_t r, int off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
+__device__ __forceinline__ uint32_t ld32(rsrc_t r, int off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+__device__ __forceinline__ u32x4 ld128(rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Per-thread share of one tile (fixed for the whole kernel):
 //  K:    key tid / 8, channels 16 (tid % 8) .. +16 (one code word)
 //  PSAC: key tid / 8, coefficients 2 (tid % 8), +1 for tid % 8 < 4
 //  V:    keys 2 (tid % 32), +1, channels 8 (tid / 32) .. +8
+struct Lane {
+  int key, blk, p, oct;
+  uint32_t zsh_k, zsh_v;   // bit offset of this thread's zero-point in its byte
+  int c_off;               // byte offset of this thread's PSAC pair in a tile buffer
+};
+__device__ __forceinline__ Lane lane_share(int tid) {
+  Lane L;
+  L.key = tid >> 3;
+  L.blk = tid & 7;
+  L.p = tid & 31;
+  L.oct = tid >> 5;
+  L.zsh_k = 4u * (uint32_t)(L.key & 1) + 2u * (uint32_t)(L.blk >> 2);
+  L.zsh_v = 2u * (uint32_t)(L.oct >> 3);
+  // threads blk < 4 own coefficient pairs 2 blk, 2 blk + 1 of their key; the
+  // others compute the same pair and store it into the unused padding of their
+  // K0_hat row, so that the store needs no branch
+  L.c_off = L.blk < 4 ? (int)offsetof(AttnBuf, chat) + L.key * 16 + 4 * L.blk
+                      : L.key * KSTR + 2 * D + 4 * (L.blk & 3);
+  return L;
+}
+
+// Three load stages, so that no load waits for another inside the loop:
+//   idx (issued three tiles ahead): the centroid index bytes;
+//   raw (two tiles ahead): codes, scales, zero-point bytes, PSAC bytes, and
+//        the fp16 centroid rows (their idx arrived one iteration earlier);
+//   all arithmetic on these bytes happens in dequant_tile.
 struct TileIdx {
   uint32_t k, v0, v1;
 };
 struct TileRegs {
-  uint32_t kcode, kscale, kzb, c2, cs;   // raw bytes / halves
-  uint32_t vcode[2], vscale[2], vzb[2];
-  u32x4 kmu[2];                           // 16 permuted fp16 centroid channels
-  u32x4 vmu[2];                           // 8 fp16 centroid channels of each key
+  uint32_t kcode, kscale, kzb, c2, cs;
+  uint32_t vcode0, vcode1, vscale0, vscale1, vzb;
+  u32x4 kmu[2];   // 16 permuted fp16 centroid channels
+  u32x4 vmu[2];   // 8 fp16 centroid channels of each of the two keys
 };
 
-__device__ __forceinline__ int64_t clamp_key(int64_t gk, int64_t T) { return gk < T ? gk : T - 1; }
-
-__device__ __forceinline__ void load_idx(const AttnArgs& a, const TileIt& it, int h, int tid, TileIdx& x) {
-  cseg& sg = seg_at(a, it.seg);
-  const int64_t T = sg.T, k0 = it.tile * AT_K, hb = (int64_t)h * T;
-  x.k = gmem(sg.k_idx)[hb + clamp_key(k0 + (tid >> 3), T)];
-  const int64_t g0 = k0 + 2 * (tid & 31);
-  x.v0 = gmem(sg.v_idx)[hb + clamp_key(g0, T)];
-  x.v1 = gmem(sg.v_idx)[hb + clamp_key(g0 + 1, T)];
+// The fields of a segment that a load stage needs.  They are read (scalar
+// loads) only when the stage moves to another segment, and carried in scalar
+// registers, so the load stages never wait for scalar memory.
+struct RawSeg {
+  const uint8_t* k_codes; const uint16_t* k_scale; const uint8_t* k_zeros;
+  const int8_t* k_c; const uint16_t* k_c_scale;
+  const uint8_t* v_codes; const uint16_t* v_scale; const uint8_t* v_zeros;
+  int64_t T;
+  bool psac;
+};
+struct IdxSeg {
+  const uint8_t* k_idx; const uint8_t* v_idx;
+  int64_t T;
+};
+__device__ __forceinline__ RawSeg raw_seg(const AttnArgs& a, int s) {
+  cseg& g = seg_at(a, s);
+  RawSeg r;
+  r.k_codes = g.k_codes; r.k_scale = g.k_scale; r.k_zeros = g.k_zeros; r.k_c = g.k_c; r.k_c_scale = g.k_c_scale;
+  r.v_codes = g.v_codes; r.v_scale = g.v_scale; r.v_zeros = g.v_zeros; r.T = g.T; r.psac = g.U != nullptr;
+  return r;
+}
+__device__ __forceinline__ IdxSeg idx_seg(const AttnArgs& a, int s) {
+  cseg& g = seg_at(a, s);
+  IdxSeg r;
+  r.k_idx = g.k_idx; r.v_idx = g.v_idx; r.T = g.T;
+  return r;
 }
 
-__device__ __forceinline__ void load_raw(const AttnArgs& a, const TileIt& it, int h, int tid, bool psac,
+__device__ __forceinline__ void load_idx(const IdxSeg& sg, const Pos& P, int h, const Lane& L, TileIdx& x) {
+  const int64_t T = sg.T, k0 = (int64_t)P.tile * AT_K;
+  const int rem = (int)(T - k0 < AT_K ? T - k0 : AT_K);
+  const int64_t row = (int64_t)h * T + k0;
+  const rsrc_t rk = buf(sg.k_idx + row, rem);
+  const rsrc_t rv = buf(sg.v_idx + row, rem);
+  x.k = ld8(rk, L.key);
+  x.v0 = ld8(rv, 2 * L.p);
+  x.v1 = ld8(rv, 2 * L.p + 1);
+}
+
+__device__ __forceinline__ void load_raw(const AttnArgs& a, const RawSeg& sg, const Pos& P, int h, const Lane& L,
                                          const TileIdx& x, TileRegs& r) {
-  cseg& sg = seg_at(a, it.seg);
-  const int64_t T = sg.T, k0 = it.tile * AT_K, hb = (int64_t)h * T;
-  const int64_t zb = (int64_t)h * zeros_stride(T);
-  const uint16_t* ktab = a.tabs + ((int64_t)(it.seg * a.H + h) * 2 + 0) * TAB_ELEMS;
-  const uint16_t* vtab = ktab + TAB_ELEMS;
+  const int64_t T = sg.T, k0 = (int64_t)P.tile * AT_K;
+  const int rem = (int)(T - k0 < AT_K ? T - k0 : AT_K);
+  const int64_t row = (int64_t)h * T + k0;
+  const int64_t zrow = (int64_t)h * zeros_stride(T) + (k0 >> 1);
+  const bool psac = sg.psac;
+  const uint16_t* ktab = a.tabs + ((int64_t)(P.seg * a.H + h) * 2) * TAB_ELEMS;
   {
-    const int blk = tid & 7, g = blk >> 2;
-    const int64_t gk = clamp_key(k0 + (tid >> 3), T);
-    const int64_t row = hb + gk;
-    r.kcode = *gmem(reinterpret_cast<const uint32_t*>(sg.k_codes + row * 32 + 4 * blk));
-    r.kscale = gmem(sg.k_scale)[row * 2 + g];
-    r.kzb = gmem(sg.k_zeros)[zb + (gk >> 1)];
-    const u32x4* mu = reinterpret_cast<const u32x4*>(ktab + (int64_t)x.k * D + 16 * blk);
-    r.kmu[0] = gmem(mu)[0];
-    r.kmu[1] = gmem(mu)[1];
-    // PSAC bytes; without PSAC any in-bounds bytes do (the term is skipped)
-    const uint16_t* c2p = psac ? reinterpret_cast<const uint16_t*>(sg.k_c + row * R + 2 * (blk & 3))
-                               : reinterpret_cast<const uint16_t*>(sg.k_codes + row * 32);
-    const uint16_t* csp = psac ? sg.k_c_scale + row : sg.k_scale + row * 2;
-    r.c2 = *gmem(c2p);
-    r.cs = *gmem(csp);
+    const int g = L.blk >> 2;
+    r.kcode = ld32(buf(sg.k_codes + row * 32, rem * 32), L.key * 32 + 4 * L.blk);
+    r.kscale = ld16(buf(sg.k_scale + row * 2, rem * 4), L.key * 4 + 2 * g);
+    r.kzb = ld8(buf(sg.k_zeros + zrow, (rem + 1) >> 1), L.key >> 1);
+    const rsrc_t kt = buf(ktab, TAB_ELEMS * 2);
+    const int mo = (int)(x.k * (D * 2)) + 32 * L.blk;
+    r.kmu[0] = ld128(kt, mo);
+    r.kmu[1] = ld128(kt, mo + 16);
+    // without PSAC the descriptors are empty: the loads return zeros and touch no memory
+    r.c2 = ld16(buf(psac ? (const void*)(sg.k_c + row * R) : (const void*)sg.k_codes, psac ? rem * R : 0),
+                L.key * R + 2 * (L.blk & 3));
+    r.cs = ld16(buf(psac ? (const void*)(sg.k_c_scale + row) : (const void*)sg.k_codes, psac ? rem * 2 : 0),
+                L.key * 2);
   }
   {
-    const int oct = tid >> 5, g = oct >> 3;
-    const int64_t g0 = k0 + 2 * (tid & 31);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t gk = clamp_key(g0 + u, T);
-      const int64_t row = hb + gk;
-      r.vcode[u] = *gmem(reinterpret_cast<const uint16_t*>(sg.v_codes + row * 32 + 2 * oct));
-      r.vscale[u] = gmem(sg.v_scale)[row * 2 + g];
-      r.vzb[u] = gmem(sg.v_zeros)[zb + (gk >> 1)];
-      r.vmu[u] = *gmem(reinterpret_cast<const u32x4*>(vtab + (int64_t)(u ? x.v1 : x.v0) * D + 8 * oct));
-    }
+    const int g = L.oct >> 3;
+    const rsrc_t vc = buf(sg.v_codes + row * 32, rem * 32);
+    const rsrc_t vs = buf(sg.v_scale + row * 2, rem * 4);
+    r.vcode0 = ld16(vc, (2 * L.p) * 32 + 2 * L.oct);
+    r.vcode1 = ld16(vc, (2 * L.p + 1) * 32 + 2 * L.oct);
+    r.vscale0 = ld16(vs, (2 * L.p) * 4 + 2 * g);
+    r.vscale1 = ld16(vs, (2 * L.p + 1) * 4 + 2 * g);
+    r.vzb = ld8(buf(sg.v_zeros + zrow, (rem + 1) >> 1), L.p);
+    const rsrc_t vt = buf(ktab + TAB_ELEMS, TAB_ELEMS * 2);
+    r.vmu[0] = ld128(vt, (int)(x.v0 * (D * 2)) + 16 * L.oct);
+    r.vmu[1] = ld128(vt, (int)(x.v1 * (D * 2)) + 16 * L.oct);
   }
 }
 
-// fp16 step | fp16 (-1024 - z) << 16 for key gk, group g, from the raw bytes
-__device__ __forceinline__ uint32_t sz_pair(uint32_t sbits, uint32_t zbyte, int64_t gk, int g) {
-  const uint32_t z = (zbyte >> (4 * (uint32_t)(gk & 1) + 2 * g)) & 3u;
-  const uint16_t nz = __builtin_bit_cast(uint16_t, (_Float16)(-1024.0f - (float)z));
-  return sbits | ((uint32_t)nz << 16);
-}
+// fp16 pair (-1024 - z0, -1024 - z1) from two 2-bit zero-points: 0xE400 + z
+__device__ __forceinline__ h2 neg_zero_pair(uint32_t z01) { return as_h2(z01 | 0xE400E400u); }
 
-// nvalid = keys of this tile inside its segment; k0 = first key's index in it
-__device__ __forceinline__ void dequant_tile(const TileRegs& r, int tid, int nvalid, int64_t k0, AttnBuf& b) {
+__device__ __forceinline__ void dequant_tile(const TileRegs& r, const Lane& L, const CodeMasks& cm, AttnBuf& b) {
   {
-    const int key = tid >> 3, blk = tid & 7;
-    const bool ok = key < nvalid;
-    const uint32_t ksz = sz_pair(r.kscale, r.kzb, k0 + key, blk >> 2);
-    const h2 s2 = as_h2((ksz & 0xFFFFu) * 0x10001u);
-    const h2 nz2 = as_h2((ksz >> 16) * 0x10001u);
+    // K0_hat: s (c - z) + mu in packed fp16 (c - z is exact; one rounding in the fma)
+    const uint32_t z = __builtin_amdgcn_ubfe(r.kzb, L.zsh_k, 2);
+    const h2 nz2 = neg_zero_pair(z * 0x10001u);
+    const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)r.kscale);
+    const h2 s2 = {s, s};
     u32x4 o[2];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const h2 d = code_pair(r.kcode, 2 * m) + nz2;
-      const h2 v = __builtin_elementwise_fma(s2, d, as_h2(r.kmu[m >> 2][m & 3]));
-      o[m >> 2][m & 3] = ok ? as_u32(v) : 0u;
+      const h2 d = code_pair(r.kcode, 2 * m, cm) + nz2;
+      o[m >> 2][m & 3] = as_u32(__builtin_elementwise_fma(s2, d, as_h2(r.kmu[m >> 2][m & 3])));
     }
-    u32x4* kr = reinterpret_cast<u32x4*>(b.khat) + key * 16;
-    kr[(2 * blk) ^ (key & 15)] = o[0];
-    kr[(2 * blk + 1) ^ (key & 15)] = o[1];
-    if (blk < 4) {
-      // PSAC coefficients c_scale * c of this key, two of the eight
-      const float cs = f16_bits_to_f32(r.cs);
-      const int8_t c0 = (int8_t)(r.c2 & 0xFFu), c1 = (int8_t)((r.c2 >> 8) & 0xFFu);
-      *reinterpret_cast<uint32_t*>(&b.chat[key][2 * blk]) = ok ? pack_f16x2(cs * (float)c0, cs * (float)c1) : 0u;
+    u32x4* kr = reinterpret_cast<u32x4*>(b.khat + L.key * KSTR + 32 * L.blk);
+    kr[0] = o[0];
+    kr[1] = o[1];
+    {
+      // PSAC coefficients c_scale * c of this key, two of the eight: the int8
+      // pair becomes the exact fp16 pair (1024 + c + 128) - 1152, then one
+      // rounded fp16 product
+      const uint32_t sp = __builtin_amdgcn_perm(0u, r.c2, 0x0C010C00u) ^ 0x64806480u;
+      const h2 c = as_h2(sp) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
+      const _Float16 cs = __builtin_bit_cast(_Float16, (uint16_t)r.cs);
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(&b) + L.c_off) = as_u32(c * h2{cs, cs});
     }
   }
   {
-    // keys 2p (low half) and 2p + 1 (high half) of channel 8 oct + c; a key past
-    // the segment end gets s = 0, mu = 0 and a zero (-1024 - z) word: value 0
-    const int p = tid & 31, oct = tid >> 5, g = oct >> 3;
-    const bool v0 = 2 * p < nvalid, v1 = 2 * p + 1 < nvalid;
-    const uint32_t cw = (v0 ? r.vcode[0] : 0u) | ((v1 ? r.vcode[1] : 0u) << 16);
-    const uint32_t sz0 = v0 ? sz_pair(r.vscale[0], r.vzb[0], k0 + 2 * p, g) : 0u;
-    const uint32_t sz1 = v1 ? sz_pair(r.vscale[1], r.vzb[1], k0 + 2 * p + 1, g) : 0u;
-    const h2 s2 = as_h2((sz0 & 0xFFFFu) | (sz1 << 16));
-    const h2 nz2 = as_h2((sz0 >> 16) | (sz1 & 0xFFFF0000u));
-    const int slot = vslot(2 * p);
+    // V_hat, keys 2p (low half) and 2p + 1 (high half) of channel 8 oct + c
+    const uint32_t cw = r.vcode0 | (r.vcode1 << 16);
+    const h2 s2 = as_h2(r.vscale0 | (r.vscale1 << 16));
+    const uint32_t t = r.vzb >> L.zsh_v;    // bits 0-1: key 2p, bits 4-5: key 2p + 1
+    const h2 nz2 = neg_zero_pair((t | (t << 12)) & 0x00030003u);
+    uint8_t* vrow = b.vt + 8 * L.oct * VSTR + 2 * vslot(2 * L.p);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const uint32_t w0 = v0 ? r.vmu[0][c >> 1] : 0u, w1 = v1 ? r.vmu[1][c >> 1] : 0u;
-      const uint32_t mu2 = __builtin_amdgcn_perm(w1, w0, (c & 1) ? 0x07060302u : 0x05040100u);
-      const h2 d = code_pair(cw, 2 * c) + nz2;
-      const uint32_t v = as_u32(__builtin_elementwise_fma(s2, d, as_h2(mu2)));
-      const int ch = 8 * oct + c;
-      const int ck = (slot >> 3) ^ ((ch >> 1) & 7);
-      *reinterpret_cast<uint32_t*>(&b.vt[ch * AT_K + ck * 8 + (slot & 7)]) = v;
+      const uint32_t mu2 = __builtin_amdgcn_perm(r.vmu[1][c >> 1], r.vmu[0][c >> 1], (c & 1) ? 0x07060302u : 0x05040100u);
+      const h2 d = code_pair(cw, 2 * c, cm) + nz2;
+      *reinterpret_cast<uint32_t*>(vrow + c * VSTR) = as_u32(__builtin_elementwise_fma(s2, d, as_h2(mu2)));
     }
   }
 }
 
-__device__ __forceinline__ int tile_nvalid(const AttnArgs& a, const TileIt& it) {
-  const int64_t rest = seg_at(a, it.seg).T - it.tile * AT_K;
-  return (int)(rest < AT_K ? rest : AT_K);
+// Phase 1 of a tile: S^T for its 64 keys as two 32-key MFMA tiles (A: keys
+// 0..31, B: 32..63), their steps alternating so that consecutive MFMAs are
+// independent, with the dequantization of the next tile into the other buffer
+// woven between them one code word at a time: a wave's VALU work issued
+// between its own MFMAs runs while they execute.  The order is fixed by
+// scheduling barriers; operand reads run two steps ahead.
+__device__ __forceinline__ void tile_phase1(const AttnBuf* __restrict__ B, AttnBuf* __restrict__ W,
+                                            const f16x8 (&qf)[8], const f16x8& qpf, int ln, int hh,
+                                            const TileRegs& r, const Lane& L, const CodeMasks& cm,
+                                            f32x16& sa, f32x16& sb2) {
+  const uint8_t* krow = B->khat + ln * KSTR + 16 * hh;
+  // K0_hat: s (c - z) + mu in packed fp16 (c - z is exact; one rounding in the fma)
+  const uint32_t kz = __builtin_amdgcn_ubfe(r.kzb, L.zsh_k, 2);
+  const h2 knz = neg_zero_pair(kz * 0x10001u);
+  const _Float16 ksc = __builtin_bit_cast(_Float16, (uint16_t)r.kscale);
+  const h2 ks2 = {ksc, ksc};
+  // V_hat, keys 2p (low half) and 2p + 1 (high half) of channel 8 oct + c
+  const uint32_t cw = r.vcode0 | (r.vcode1 << 16);
+  const h2 vs2 = as_h2(r.vscale0 | (r.vscale1 << 16));
+  const uint32_t vzt = r.vzb >> L.zsh_v;    // bits 0-1: key 2p, bits 4-5: key 2p + 1
+  const h2 vnz = neg_zero_pair((vzt | (vzt << 12)) & 0x00030003u);
+  uint8_t* vw = W->vt + 8 * L.oct * VSTR + 2 * vslot(2 * L.p);
+  u32x4* kw = reinterpret_cast<u32x4*>(W->khat + L.key * KSTR + 32 * L.blk);
+
+  f16x8 fa[8], fb[8];
+  fa[0] = *reinterpret_cast<const f16x8*>(krow);
+  fb[0] = *reinterpret_cast<const f16x8*>(krow + 32 * KSTR);
+  fa[1] = *reinterpret_cast<const f16x8*>(krow + 32);
+  fb[1] = *reinterpret_cast<const f16x8*>(krow + 32 * KSTR + 32);
+  f16x8 ca, cb;
+  u32x4 ko[2];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    if (s + 2 < 8) {
+      fa[s + 2] = *reinterpret_cast<const f16x8*>(krow + 32 * (s + 2));
+      fb[s + 2] = *reinterpret_cast<const f16x8*>(krow + 32 * KSTR + 32 * (s + 2));
+    } else if (s == 6) {
+      // PSAC step operands: k = 0..7 (hh = 0) are the coefficients; the hh = 1
+      // half reads the same finite values against zeros in qpf (all of qpf is
+      // zero for a segment without PSAC, whose coefficients are stored as zeros)
+      ca = *reinterpret_cast<const f16x8*>(B->chat + ln * 16);
+      cb = *reinterpret_cast<const f16x8*>(B->chat + (32 + ln) * 16);
+    }
+    sa = mfma_f16(fa[s], qf[s], sa);
+    {
+      const h2 d = code_pair(r.kcode, 2 * s, cm) + knz;
+      ko[s >> 2][s & 3] = as_u32(__builtin_elementwise_fma(ks2, d, as_h2(r.kmu[s >> 2][s & 3])));
+      if ((s & 3) == 3) kw[s >> 2] = ko[s >> 2];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    sb2 = mfma_f16(fb[s], qf[s], sb2);
+    {
+      const uint32_t mu2 = __builtin_amdgcn_perm(r.vmu[1][s >> 1], r.vmu[0][s >> 1], (s & 1) ? 0x07060302u : 0x05040100u);
+      const h2 d = code_pair(cw, 2 * s, cm) + vnz;
+      *reinterpret_cast<uint32_t*>(vw + s * VSTR) = as_u32(__builtin_elementwise_fma(vs2, d, as_h2(mu2)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sa = mfma_f16(ca, qpf, sa);
+  {
+    // PSAC coefficients c_scale * c of this thread's key, two of the eight: the
+    // int8 pair becomes the exact fp16 pair (1024 + c + 128) - 1152, then one
+    // rounded fp16 product
+    const uint32_t sp = __builtin_amdgcn_perm(0u, r.c2, 0x0C010C00u) ^ 0x64806480u;
+    const h2 c = as_h2(sp) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
+    const _Float16 cs = __builtin_bit_cast(_Float16, (uint16_t)r.cs);
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(W) + L.c_off) = as_u32(c * h2{cs, cs});
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  sb2 = mfma_f16(cb, qpf, sb2);
+}
+
+// Lanes l and l ^ 32 hold the two halves of one query column.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+// the value held by lane l ^ 32
+__device__ __forceinline__ uint32_t pair_other(uint32_t v, int hh) {
+  const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return hh ? s[0] : s[1];
 }
 
 template <bool TOP1>
@@ -318,6 +508,7 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   const int64_t qi = qw0 + ln;
   const bool qvalid = qi < a.Tq;
   const int64_t qoff = (int64_t)h * a.qsh + (qvalid ? qi : 0) * a.qst;
+  const Lane L = lane_share(tid);
 
   // Q fragments (B operand of S^T), fp16, in the permuted channel order of the
   // K0_hat rows: k-step s, half hh holds channels 16 s + 4 hh + e and
@@ -352,9 +543,11 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) o_acc[c] = f32x16{};
 
-  TileIt it = first_tile(a, 0, 0, split);
-  if (it.seg >= a.n_segs) {
-    // nothing to do for this split: publish an empty partial
+  // this split's share of the tile sequence
+  const int total = count_tiles(a, lane);
+  const int g0 = (int)((int64_t)total * split / a.nsplit);
+  const int count = (int)((int64_t)total * (split + 1) / a.nsplit) - g0;
+  if (count <= 0) {
     if (qvalid && a.nsplit > 1 && hh == 0) {
       const int64_t pidx = ((int64_t)split * a.H + h) * a.Tq + qi;
       a.pm[pidx] = -__builtin_inff(); a.pl[pidx] = 0.f;
@@ -362,27 +555,28 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
     }
     return;
   }
-  // the zero padding of the PSAC channels never changes
-  if (tid < 2 * AT_K)
-    *reinterpret_cast<u32x4*>(&sb[tid / AT_K].chat[tid % AT_K][8]) = u32x4{0u, 0u, 0u, 0u};
+  // positions of tiles n, n + 1, n + 2, n + 3 of the split (past the end a
+  // position repeats the last tile, so every stage loads memory that exists)
+  Pos P0 = locate(a, g0, lane);
+  Pos P1 = count > 1 ? advance(a, P0, seg_at(a, P0.seg).T) : P0;
+  Pos P2 = count > 2 ? advance(a, P1, seg_at(a, P1.seg).T) : P1;
+  Pos P3 = count > 3 ? advance(a, P2, seg_at(a, P2.seg).T) : P2;
+  // per-stage segment fields: T and the PSAC flag for tiles n and n + 1, the
+  // raw stage's arrays (n + 2), the idx stage's arrays (n + 3)
+  int64_t T0 = seg_at(a, P0.seg).T, T1 = seg_at(a, P1.seg).T;
+  RawSeg rs = raw_seg(a, P2.seg);
+  IdxSeg is = idx_seg(a, P3.seg);
+
   // pipeline fill: tile 0 dequantized, tile 1 in registers, tile 2's indices in flight
+  const CodeMasks cm = code_masks();
   TileRegs regs;
   TileIdx tix;
-  load_idx(a, it, h, tid, tix);
-  load_raw(a, it, h, tid, seg_at(a, it.seg).U != nullptr, tix, regs);
-  dequant_tile(regs, tid, tile_nvalid(a, it), it.tile * AT_K, sb[0]);
-  TileIt nt = next_tile(a, it, split);
-  TileIt nn = (nt.seg < a.n_segs) ? next_tile(a, nt, split) : nt;
-  {
-    // loads never sit behind a branch (a branch would turn the loaded registers
-    // into phi copies that wait for the data): stages past the end of the split
-    // reload a tile that exists, and nobody reads what they produce
-    const TileIt l1 = uni((nt.seg < a.n_segs) ? nt : it);
-    load_idx(a, l1, h, tid, tix);
-    load_raw(a, l1, h, tid, seg_at(a, l1.seg).U != nullptr, tix, regs);
-    const TileIt l2 = uni((nn.seg < a.n_segs) ? nn : l1);
-    load_idx(a, l2, h, tid, tix);
-  }
+  load_idx(idx_seg(a, P0.seg), P0, h, L, tix);
+  load_raw(a, raw_seg(a, P0.seg), P0, h, L, tix, regs);
+  dequant_tile(regs, L, cm, sb[0]);
+  load_idx(idx_seg(a, P1.seg), P1, h, L, tix);
+  load_raw(a, raw_seg(a, P1.seg), P1, h, L, tix, regs);
+  load_idx(idx_seg(a, P2.seg), P2, h, L, tix);
   __syncthreads();
 
   int cur = 0;
@@ -390,11 +584,11 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   f16x8 qpf = __builtin_bit_cast(f16x8, u32x4{0, 0, 0, 0});
   bool psac = false;
   const h2 ones = as_h2(0x3C003C00u);
-  while (true) {
-    cseg& sg = seg_at(a, it.seg);
-    if (it.seg != qp_seg) {
+  for (int n = 0; n < count; ++n) {
+    if (P0.seg != qp_seg) {
       // Q U for this segment: (U^T) (Q^T) on MFMA with bf16 operands
-      qp_seg = it.seg;
+      cseg& sg = seg_at(a, P0.seg);
+      qp_seg = P0.seg;
       psac = sg.U != nullptr;
       qpf = __builtin_bit_cast(f16x8, u32x4{0, 0, 0, 0});
       if (psac && wave_active) {
@@ -434,104 +628,113 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
       }
     }
     const AttnBuf& B = sb[cur];
-    const int64_t k0 = it.tile * AT_K;
-    const int nvalid = (int)((sg.T - k0) < AT_K ? (sg.T - k0) : AT_K);
-    const TileIt n3 = uni((nn.seg < a.n_segs) ? next_tile(a, nn, split) : nn);
+    const int64_t k0 = (int64_t)P0.tile * AT_K;
+    const int nvalid = (int)((T0 - k0) < AT_K ? (T0 - k0) : AT_K);
 
-    // The tile is processed as two 32-key halves; the next tile is dequantized
-    // between them.
+    // ---- phase 1: S^T for the tile's 64 keys as two 32-key MFMA tiles (A: keys
+    //      0..31, B: 32..63), their steps alternating so that consecutive MFMAs
+    //      are independent, and in the same instruction stream the dequantization
+    //      of the next tile into the other buffer and the loads of the two tiles
+    //      after it.  Nothing here branches, so MFMAs and VALU work interleave.
+    //      Past the end of the split the stages repeat the last tile (into a
+    //      buffer nobody reads), so that no load is conditional.
+    f32x16 sa = {}, sb2 = {};
+    tile_phase1(&sb[cur], &sb[cur ^ 1], qf, qpf, ln, hh, regs, L, cm, sa, sb2);
+    load_raw(a, rs, P2, h, L, tix, regs);
+    load_idx(is, P3, h, L, tix);
+
+    if (wave_active) {
+      // ---- keys past the segment end (their rows hold centroid 0) ----
+      if (nvalid < AT_K) {
+        // row c_row(i, hh) = 4 hh + (8 (i / 4) + i % 4) of each 32-key tile
+        // against the limit, taken opaquely so the compares use inline constants
+        int t;
+        asm volatile("v_sub_u32 %0, %1, %2" : "=v"(t) : "s"(nvalid), "v"(4 * hh));
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      if (wave_active && 32 * kt < nvalid) {
-        // ---- S^T = K_ext Q_ext^T for 32 keys x 32 queries ----
-        f32x16 sacc = {};
-        const int key = 32 * kt + ln;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int c = 2 * s + hh;
-          const f16x8 kf = reinterpret_cast<const f16x8*>(B.khat)[key * 16 + (c ^ (key & 15))];
-          sacc = mfma_f16(kf, qf[s], sacc);
+        for (int i = 0; i < 16; ++i) {
+          if (t <= 8 * (i >> 2) + (i & 3)) sa[i] = -__builtin_inff();
+          if (t <= 32 + 8 * (i >> 2) + (i & 3)) sb2[i] = -__builtin_inff();
         }
-        if (psac) {
-          const f16x8 cf = *reinterpret_cast<const f16x8*>(&B.chat[key][8 * hh]);
-          sacc = mfma_f16(cf, qpf, sacc);
+      }
+      // ---- phase 2: the tile's row max; lazy rescale of what was accumulated ----
+      float mt = fmaxf(fmaxf(sa[0], sa[1]), sa[2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, sa[i]), sa[i + 1]);
+      mt = fmaxf(fmaxf(mt, sa[15]), sb2[0]);
+#pragma unroll
+      for (int i = 1; i < 15; i += 2) mt = fmaxf(fmaxf(mt, sb2[i]), sb2[i + 1]);
+      mt = fmaxf(mt, sb2[15]);
+      if (TOP1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (sa[i] > best_v) { best_v = sa[i]; best_i = (int32_t)(P0.kbase + k0 + c_row(i, hh)); }
         }
-        // ---- online softmax (exp2 domain) ----
-        if (32 * kt + 32 > nvalid) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (32 * kt + c_row(i, hh) >= nvalid) sacc[i] = -__builtin_inff();
+        for (int i = 0; i < 16; ++i) {
+          if (sb2[i] > best_v) { best_v = sb2[i]; best_i = (int32_t)(P0.kbase + k0 + 32 + c_row(i, hh)); }
         }
-        float mt = -__builtin_inff();
+      }
+      mt = pair_max(mt) * sc2;
+      if (mt > m_run + RESCALE_SLACK || m_run == -__builtin_inff()) {
+        // raise the running max (to this max) and rescale what was accumulated
+        const float alpha = (m_run == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m_run - mt);
+        m_run = mt;
+        l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(sacc[i], sacc[i + 1]));
-        if (TOP1) {
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (sacc[i] > best_v) { best_v = sacc[i]; best_i = (int32_t)(it.kbase + k0 + 32 * kt + c_row(i, hh)); }
-        }
-        mt = fmaxf(mt, swap32_f(mt)) * sc2;
-        if (mt > m_run + RESCALE_SLACK || m_run == -__builtin_inff()) {
-          // raise the running max (to this max) and rescale what was accumulated
-          const float alpha = (m_run == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m_run - mt);
-          m_run = mt;
-          l_run *= alpha;
+          for (int i = 0; i < 16; ++i) o_acc[c][i] *= alpha;
+      }
+      // ---- phase 3: P = exp2(S sc2 - m) in fp16 and O^T += V^T P; the second
+      //      half's exponentials overlap the first half's MFMAs ----
+      const uint8_t* vrow = B.vt + ln * VSTR + 16 * hh;
+      float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
+      for (int kt = 0; kt < 2; ++kt) {
+        const f32x16& sc = kt ? sb2 : sa;
+        // V_hat operands: keys (slots) 8 (2 (2 kt + s2) + hh) .. +8 of channel 32 c + ln
+        f16x8 vf[4][2];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) o_acc[c][i] *= alpha;
-        }
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+            vf[c][s2] = *reinterpret_cast<const f16x8*>(vrow + 32 * c * VSTR + 64 * kt + 32 * s2);
         u32x4 pw[2];
-        float lsum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[i], sc2, -m_run));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[i + 1], sc2, -m_run));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], sc2, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], sc2, -m_run));
           const h2 pk = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
           // the denominator sums exactly the fp16 probabilities the P V product uses
-          lsum = __builtin_amdgcn_fdot2(pk, ones, lsum, false);
+          if (i & 2) lsum1 = __builtin_amdgcn_fdot2(pk, ones, lsum1, false);
+          else lsum0 = __builtin_amdgcn_fdot2(pk, ones, lsum0, false);
           // PV k-step 2 kt + i / 8, element (i % 8)
           pw[i >> 3][(i & 7) >> 1] = as_u32(pk);
         }
-        l_run += lsum;
-        // ---- O^T += V^T P over these 32 keys ----
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int ch = 32 * c + ln;
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const int chunk = (2 * (2 * kt + s2) + hh) ^ ((ch >> 1) & 7);
-            const f16x8 vf = *reinterpret_cast<const f16x8*>(&B.vt[ch * AT_K + chunk * 8]);
-            o_acc[c] = mfma_f16(vf, __builtin_bit_cast(f16x8, pw[s2]), o_acc[c]);
-          }
-        }
+          for (int s2 = 0; s2 < 2; ++s2) o_acc[c] = mfma_f16(vf[c][s2], __builtin_bit_cast(f16x8, pw[s2]), o_acc[c]);
       }
-      if (kt == 0) {
-        // ---- next tile: dequantize from registers into the other buffer; fetch the
-        //      bytes of the tile after it and the indices of the one after that.
-        //      Past the end of the split these stages repeat a tile that exists
-        //      (into a buffer nobody reads), so that no load is conditional. ----
-        const TileIt d1 = uni((nt.seg < a.n_segs) ? nt : it);
-        dequant_tile(regs, tid, tile_nvalid(a, d1), d1.tile * AT_K, sb[cur ^ 1]);
-        const TileIt l2 = uni((nn.seg < a.n_segs) ? nn : d1);
-        load_raw(a, l2, h, tid, seg_at(a, l2.seg).U != nullptr, tix, regs);
-        const TileIt l3 = uni((n3.seg < a.n_segs) ? n3 : l2);
-        load_idx(a, l3, h, tid, tix);
-      }
+      l_run += lsum0 + lsum1;
     }
     __syncthreads();
-    if (nt.seg >= a.n_segs) break;
-    it = nt;
-    nt = nn;
-    nn = n3;
+    P0 = P1; T0 = T1;
+    P1 = P2; T1 = rs.T;
+    if (P3.seg != P2.seg) rs = raw_seg(a, P3.seg);
+    P2 = P3;
+    if (n + 4 < count) {
+      P3 = advance(a, P3, is.T);
+      if (P3.seg != P2.seg) is = idx_seg(a, P3.seg);
+    }
     cur ^= 1;
   }
 
   // ---- epilogue ----
-  const float l_tot = l_run + swap32_f(l_run);
+  const float l_tot = pair_sum(l_run);
   if (TOP1) {
-    const float ov = swap32_f(best_v);
-    const int32_t oi = (int32_t)swap32_u((uint32_t)best_i);
+    const float ov = __uint_as_float(pair_other(__float_as_uint(best_v), hh));
+    const int32_t oi = (int32_t)pair_other((uint32_t)best_i, hh);
     if (ov > best_v || (ov == best_v && oi < best_i)) { best_v = ov; best_i = oi; }
   }
   if (!qvalid) return;
