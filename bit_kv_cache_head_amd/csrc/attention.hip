@@ -72,6 +72,14 @@ constexpr int BUF_BYTES = (int)sizeof(AttnBuf);
 __device__ __forceinline__ int vslot(int key) {
   return (key & ~0xC) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
+// Byte offset of (channel ch, slot) in the V_hat^T tile: the 16-byte chunks of
+// row ch are XOR-swizzled by (ch / 16) % 8, so the dequantizing threads (16
+// channel groups x 8 keys per wave) spread their 32-bit stores over the banks,
+// while the MFMA operand reads (16 consecutive rows, one chunk) stay
+// conflict-free and keep a per-lane base plus compile-time offsets.
+__device__ __forceinline__ int vt_offset(int ch, int slot) {
+  return ch * VSTR + 16 * ((slot >> 3) ^ ((ch >> 4) & 7)) + 2 * (slot & 7);
+}
 
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   const uint16_t x = __builtin_bit_cast(uint16_t, (_Float16)a);
@@ -234,17 +242,30 @@ constexpr int RSRC_CFG = 0x00020000;   // raw buffer, 32-bit data format (gfx9 f
 __device__ __forceinline__ rsrc_t buf(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, RSRC_CFG);
 }
-__device__ __forceinline__ uint32_t ld8(rsrc_t r, int off) { return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0); }
-__device__ __forceinline__ uint32_t ld16(rsrc_t r, int off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
-__device__ __forceinline__ uint32_t ld32(rsrc_t r, int off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
-__device__ __forceinline__ u32x4 ld128(rsrc_t r, int off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+// off: per-thread byte offset; so: wave-uniform byte offset.  The range check
+// covers off + so, so a descriptor can span a whole segment-head while the
+// tile's offset travels in so.
+__device__ __forceinline__ uint32_t ld8(rsrc_t r, int off, int so = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, so, 0);
+}
+__device__ __forceinline__ uint8_t ld8b(rsrc_t r, int off, int so = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, so, 0);
+}
+__device__ __forceinline__ uint32_t ld16(rsrc_t r, int off, int so = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, so, 0);
+}
+__device__ __forceinline__ uint32_t ld32(rsrc_t r, int off, int so = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, so, 0);
+}
+__device__ __forceinline__ u32x4 ld128(rsrc_t r, int off, int so = 0) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, so, 0));
 }
 
 // Per-thread share of one tile (fixed for the whole kernel):
 //  K:    key tid / 8, channels 16 (tid % 8) .. +16 (one code word)
 //  PSAC: key tid / 8, coefficients 2 (tid % 8), +1 for tid % 8 < 4
-//  V:    keys 2 (tid % 32), +1, channels 8 (tid / 32) .. +8
+//  V:    keys 2 (tid / 16), +1, channels 8 (tid % 16) .. +8 (a wave: 8 keys, all channels,
+//        so its centroid-row loads touch 8 table rows, not 64)
 struct Lane {
   int key, blk, p, oct;
   uint32_t zsh_k, zsh_v;   // bit offset of this thread's zero-point in its byte
@@ -254,8 +275,8 @@ __device__ __forceinline__ Lane lane_share(int tid) {
   Lane L;
   L.key = tid >> 3;
   L.blk = tid & 7;
-  L.p = tid & 31;
-  L.oct = tid >> 5;
+  L.p = tid >> 4;
+  L.oct = tid & 15;
   L.zsh_k = 4u * (uint32_t)(L.key & 1) + 2u * (uint32_t)(L.blk >> 2);
   L.zsh_v = 2u * (uint32_t)(L.oct >> 3);
   // threads blk < 4 own coefficient pairs 2 blk, 2 blk + 1 of their key; the
@@ -271,8 +292,11 @@ __device__ __forceinline__ Lane lane_share(int tid) {
 //   raw (two tiles ahead): codes, scales, zero-point bytes, PSAC bytes, and
 //        the fp16 centroid rows (their idx arrived one iteration earlier);
 //   all arithmetic on these bytes happens in dequant_tile.
+// Kept as bytes: the zero-extension then happens where the table offsets are
+// formed, not on the loop-carried value (which would make the top of every
+// iteration wait for these loads).
 struct TileIdx {
-  uint32_t k, v0, v1;
+  uint8_t k, v0, v1;
 };
 struct TileRegs {
   uint32_t kcode, kscale, kzb, c2, cs;
@@ -281,81 +305,89 @@ struct TileRegs {
   u32x4 vmu[2];   // 8 fp16 centroid channels of each of the two keys
 };
 
-// The fields of a segment that a load stage needs.  They are read (scalar
-// loads) only when the stage moves to another segment, and carried in scalar
-// registers, so the load stages never wait for scalar memory.
-struct RawSeg {
-  const uint8_t* k_codes; const uint16_t* k_scale; const uint8_t* k_zeros;
-  const int8_t* k_c; const uint16_t* k_c_scale;
-  const uint8_t* v_codes; const uint16_t* v_scale; const uint8_t* v_zeros;
-  int64_t T;
-  bool psac;
+// One segment-head's packed arrays as seen by the bytes/index stage: the
+// head's base addresses, carried in scalar registers from the moment the
+// stage enters the segment.  Each load builds a buffer descriptor spanning
+// the head's rows (num_records = their bytes), so rows past the segment end
+// read as zeros, and reaches the tile's rows through the scalar offset
+// (the range check covers it).  Offsets are 32-bit: a segment holds fewer
+// than 2^26 keys.
+struct SegDesc {
+  const uint8_t *kc, *ks, *kz, *c, *cs, *vc, *vs, *vz, *ki, *vi;
+  int T;
+  int cT;     // rows of PSAC coefficients: T, or 0 without PSAC (empty descriptors)
 };
-struct IdxSeg {
-  const uint8_t* k_idx; const uint8_t* v_idx;
-  int64_t T;
-};
-__device__ __forceinline__ RawSeg raw_seg(const AttnArgs& a, int s) {
+__device__ __forceinline__ SegDesc seg_desc(const AttnArgs& a, int s, int h) {
   cseg& g = seg_at(a, s);
-  RawSeg r;
-  r.k_codes = g.k_codes; r.k_scale = g.k_scale; r.k_zeros = g.k_zeros; r.k_c = g.k_c; r.k_c_scale = g.k_c_scale;
-  r.v_codes = g.v_codes; r.v_scale = g.v_scale; r.v_zeros = g.v_zeros; r.T = g.T; r.psac = g.U != nullptr;
-  return r;
-}
-__device__ __forceinline__ IdxSeg idx_seg(const AttnArgs& a, int s) {
-  cseg& g = seg_at(a, s);
-  IdxSeg r;
-  r.k_idx = g.k_idx; r.v_idx = g.v_idx; r.T = g.T;
-  return r;
+  const int64_t T = g.T;
+  const int64_t hb = (int64_t)h * T;
+  const int64_t zb = (int64_t)h * zeros_stride(T);
+  SegDesc d;
+  const bool psac = g.U != nullptr;
+  d.kc = g.k_codes + hb * 32;
+  d.ks = reinterpret_cast<const uint8_t*>(g.k_scale + hb * 2);
+  d.kz = g.k_zeros + zb;
+  // without PSAC the descriptors are empty: the loads return zeros and touch no memory
+  d.c = psac ? reinterpret_cast<const uint8_t*>(g.k_c + hb * R) : g.k_codes;
+  d.cs = psac ? reinterpret_cast<const uint8_t*>(g.k_c_scale + hb) : g.k_codes;
+  d.vc = g.v_codes + hb * 32;
+  d.vs = reinterpret_cast<const uint8_t*>(g.v_scale + hb * 2);
+  d.vz = g.v_zeros + zb;
+  d.ki = g.k_idx + hb;
+  d.vi = g.v_idx + hb;
+  d.T = (int)T;
+  // wave-uniform by construction; saying so keeps the descriptors scalar
+  d.cT = __builtin_amdgcn_readfirstlane(psac ? (int)T : 0);
+  return d;
 }
 
-__device__ __forceinline__ void load_idx(const IdxSeg& sg, const Pos& P, int h, const Lane& L, TileIdx& x) {
-  const int64_t T = sg.T, k0 = (int64_t)P.tile * AT_K;
-  const int rem = (int)(T - k0 < AT_K ? T - k0 : AT_K);
-  const int64_t row = (int64_t)h * T + k0;
-  const rsrc_t rk = buf(sg.k_idx + row, rem);
-  const rsrc_t rv = buf(sg.v_idx + row, rem);
-  x.k = ld8(rk, L.key);
-  x.v0 = ld8(rv, 2 * L.p);
-  x.v1 = ld8(rv, 2 * L.p + 1);
+__device__ __forceinline__ void load_idx(const SegDesc& d, const Pos& P, const Lane& L, TileIdx& x) {
+  const int k0 = P.tile * AT_K;
+  const rsrc_t ki = buf(d.ki, d.T), vi = buf(d.vi, d.T);
+  x.k = ld8b(ki, L.key, k0);
+  x.v0 = ld8b(vi, 2 * L.p, k0);
+  x.v1 = ld8b(vi, 2 * L.p + 1, k0);
 }
 
-__device__ __forceinline__ void load_raw(const AttnArgs& a, const RawSeg& sg, const Pos& P, int h, const Lane& L,
-                                         const TileIdx& x, TileRegs& r) {
-  const int64_t T = sg.T, k0 = (int64_t)P.tile * AT_K;
-  const int rem = (int)(T - k0 < AT_K ? T - k0 : AT_K);
-  const int64_t row = (int64_t)h * T + k0;
-  const int64_t zrow = (int64_t)h * zeros_stride(T) + (k0 >> 1);
-  const bool psac = sg.psac;
-  const uint16_t* ktab = a.tabs + ((int64_t)(P.seg * a.H + h) * 2) * TAB_ELEMS;
+// The packed bytes of a tile (codes, scales, zero-points, PSAC bytes).
+__device__ __forceinline__ void load_bytes(const SegDesc& d, const Pos& P, const Lane& L, TileRegs& r) {
+  const int k0 = P.tile * AT_K, T = d.T;
   {
     const int g = L.blk >> 2;
-    r.kcode = ld32(buf(sg.k_codes + row * 32, rem * 32), L.key * 32 + 4 * L.blk);
-    r.kscale = ld16(buf(sg.k_scale + row * 2, rem * 4), L.key * 4 + 2 * g);
-    r.kzb = ld8(buf(sg.k_zeros + zrow, (rem + 1) >> 1), L.key >> 1);
-    const rsrc_t kt = buf(ktab, TAB_ELEMS * 2);
-    const int mo = (int)(x.k * (D * 2)) + 32 * L.blk;
-    r.kmu[0] = ld128(kt, mo);
-    r.kmu[1] = ld128(kt, mo + 16);
-    // without PSAC the descriptors are empty: the loads return zeros and touch no memory
-    r.c2 = ld16(buf(psac ? (const void*)(sg.k_c + row * R) : (const void*)sg.k_codes, psac ? rem * R : 0),
-                L.key * R + 2 * (L.blk & 3));
-    r.cs = ld16(buf(psac ? (const void*)(sg.k_c_scale + row) : (const void*)sg.k_codes, psac ? rem * 2 : 0),
-                L.key * 2);
+    r.kcode = ld32(buf(d.kc, T * 32), L.key * 32 + 4 * L.blk, k0 * 32);
+    r.kscale = ld16(buf(d.ks, T * 4), L.key * 4 + 2 * g, k0 * 4);
+    r.kzb = ld8(buf(d.kz, (T + 1) >> 1), L.key >> 1, k0 >> 1);
+    r.c2 = ld16(buf(d.c, d.cT * R), L.key * R + 2 * (L.blk & 3), k0 * R);
+    r.cs = ld16(buf(d.cs, d.cT * 2), L.key * 2, k0 * 2);
   }
   {
     const int g = L.oct >> 3;
-    const rsrc_t vc = buf(sg.v_codes + row * 32, rem * 32);
-    const rsrc_t vs = buf(sg.v_scale + row * 2, rem * 4);
-    r.vcode0 = ld16(vc, (2 * L.p) * 32 + 2 * L.oct);
-    r.vcode1 = ld16(vc, (2 * L.p + 1) * 32 + 2 * L.oct);
-    r.vscale0 = ld16(vs, (2 * L.p) * 4 + 2 * g);
-    r.vscale1 = ld16(vs, (2 * L.p + 1) * 4 + 2 * g);
-    r.vzb = ld8(buf(sg.v_zeros + zrow, (rem + 1) >> 1), L.p);
-    const rsrc_t vt = buf(ktab + TAB_ELEMS, TAB_ELEMS * 2);
-    r.vmu[0] = ld128(vt, (int)(x.v0 * (D * 2)) + 16 * L.oct);
-    r.vmu[1] = ld128(vt, (int)(x.v1 * (D * 2)) + 16 * L.oct);
+    const rsrc_t vc = buf(d.vc, T * 32), vs = buf(d.vs, T * 4);
+    r.vcode0 = ld16(vc, (2 * L.p) * 32 + 2 * L.oct, k0 * 32);
+    r.vcode1 = ld16(vc, (2 * L.p + 1) * 32 + 2 * L.oct, k0 * 32);
+    r.vscale0 = ld16(vs, (2 * L.p) * 4 + 2 * g, k0 * 4);
+    r.vscale1 = ld16(vs, (2 * L.p + 1) * 4 + 2 * g, k0 * 4);
+    r.vzb = ld8(buf(d.vz, (T + 1) >> 1), L.p, k0 >> 1);
   }
+}
+
+// The fp16 centroid rows of a tile's keys (segment seg), from its indices.
+__device__ __forceinline__ void load_mu(const AttnArgs& a, int seg, int h, const Lane& L, const TileIdx& x,
+                                        TileRegs& r) {
+  const uint16_t* ktab = a.tabs + ((int64_t)(seg * a.H + h) * 2) * TAB_ELEMS;
+  const rsrc_t kt = buf(ktab, TAB_ELEMS * 2);
+  const int mo = (int)(x.k * (D * 2)) + 32 * L.blk;
+  r.kmu[0] = ld128(kt, mo);
+  r.kmu[1] = ld128(kt, mo + 16);
+  const rsrc_t vt = buf(ktab + TAB_ELEMS, TAB_ELEMS * 2);
+  r.vmu[0] = ld128(vt, (int)(x.v0 * (D * 2)) + 16 * L.oct);
+  r.vmu[1] = ld128(vt, (int)(x.v1 * (D * 2)) + 16 * L.oct);
+}
+
+// Copy the packed-byte fields (the centroid rows are loaded separately).
+__device__ __forceinline__ void take_bytes(TileRegs& d, const TileRegs& s) {
+  d.kcode = s.kcode; d.kscale = s.kscale; d.kzb = s.kzb; d.c2 = s.c2; d.cs = s.cs;
+  d.vcode0 = s.vcode0; d.vcode1 = s.vcode1; d.vscale0 = s.vscale0; d.vscale1 = s.vscale1; d.vzb = s.vzb;
 }
 
 // fp16 pair (-1024 - z0, -1024 - z1) from two 2-bit zero-points: 0xE400 + z
@@ -393,7 +425,7 @@ __device__ __forceinline__ void dequant_tile(const TileRegs& r, const Lane& L, c
     const h2 s2 = as_h2(r.vscale0 | (r.vscale1 << 16));
     const uint32_t t = r.vzb >> L.zsh_v;    // bits 0-1: key 2p, bits 4-5: key 2p + 1
     const h2 nz2 = neg_zero_pair((t | (t << 12)) & 0x00030003u);
-    uint8_t* vrow = b.vt + 8 * L.oct * VSTR + 2 * vslot(2 * L.p);
+    uint8_t* vrow = b.vt + vt_offset(8 * L.oct, vslot(2 * L.p));
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint32_t mu2 = __builtin_amdgcn_perm(r.vmu[1][c >> 1], r.vmu[0][c >> 1], (c & 1) ? 0x07060302u : 0x05040100u);
@@ -424,7 +456,7 @@ __device__ __forceinline__ void tile_phase1(const AttnBuf* __restrict__ B, AttnB
   const h2 vs2 = as_h2(r.vscale0 | (r.vscale1 << 16));
   const uint32_t vzt = r.vzb >> L.zsh_v;    // bits 0-1: key 2p, bits 4-5: key 2p + 1
   const h2 vnz = neg_zero_pair((vzt | (vzt << 12)) & 0x00030003u);
-  uint8_t* vw = W->vt + 8 * L.oct * VSTR + 2 * vslot(2 * L.p);
+  uint8_t* vw = W->vt + vt_offset(8 * L.oct, vslot(2 * L.p));
   u32x4* kw = reinterpret_cast<u32x4*>(W->khat + L.key * KSTR + 32 * L.blk);
 
   f16x8 fa[8], fb[8];
@@ -561,22 +593,32 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   Pos P1 = count > 1 ? advance(a, P0, seg_at(a, P0.seg).T) : P0;
   Pos P2 = count > 2 ? advance(a, P1, seg_at(a, P1.seg).T) : P1;
   Pos P3 = count > 3 ? advance(a, P2, seg_at(a, P2.seg).T) : P2;
-  // per-stage segment fields: T and the PSAC flag for tiles n and n + 1, the
-  // raw stage's arrays (n + 2), the idx stage's arrays (n + 3)
-  int64_t T0 = seg_at(a, P0.seg).T, T1 = seg_at(a, P1.seg).T;
-  RawSeg rs = raw_seg(a, P2.seg);
-  IdxSeg is = idx_seg(a, P3.seg);
+  // Load stages of tile t: packed bytes and indices three tiles ahead (HBM
+  // latency), centroid rows two tiles ahead (from the indices), dequantization
+  // one tile ahead.  Segment fields: T of tiles n .. n + 2, the arrays of
+  // tile n + 3's segment.
+  int64_t T0 = seg_at(a, P0.seg).T, T1 = seg_at(a, P1.seg).T, T2 = seg_at(a, P2.seg).T;
+  SegDesc sd = seg_desc(a, P3.seg, h);
 
-  // pipeline fill: tile 0 dequantized, tile 1 in registers, tile 2's indices in flight
+  // pipeline fill: tile 0 dequantized, tile 1 complete in registers, tile 2's
+  // bytes and indices in flight
   const CodeMasks cm = code_masks();
-  TileRegs regs;
+  TileRegs regs, nbytes;
   TileIdx tix;
-  load_idx(idx_seg(a, P0.seg), P0, h, L, tix);
-  load_raw(a, raw_seg(a, P0.seg), P0, h, L, tix, regs);
-  dequant_tile(regs, L, cm, sb[0]);
-  load_idx(idx_seg(a, P1.seg), P1, h, L, tix);
-  load_raw(a, raw_seg(a, P1.seg), P1, h, L, tix, regs);
-  load_idx(idx_seg(a, P2.seg), P2, h, L, tix);
+  {
+    const SegDesc d0 = seg_desc(a, P0.seg, h);
+    load_idx(d0, P0, L, tix);
+    load_bytes(d0, P0, L, regs);
+    load_mu(a, P0.seg, h, L, tix, regs);
+    dequant_tile(regs, L, cm, sb[0]);
+    const SegDesc d1 = seg_desc(a, P1.seg, h);
+    load_idx(d1, P1, L, tix);
+    load_bytes(d1, P1, L, regs);
+    load_mu(a, P1.seg, h, L, tix, regs);
+    const SegDesc d2 = seg_desc(a, P2.seg, h);
+    load_idx(d2, P2, L, tix);
+    load_bytes(d2, P2, L, nbytes);
+  }
   __syncthreads();
 
   int cur = 0;
@@ -640,8 +682,12 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
     //      buffer nobody reads), so that no load is conditional.
     f32x16 sa = {}, sb2 = {};
     tile_phase1(&sb[cur], &sb[cur ^ 1], qf, qpf, ln, hh, regs, L, cm, sa, sb2);
-    load_raw(a, rs, P2, h, L, tix, regs);
-    load_idx(is, P3, h, L, tix);
+    // tile n + 2: its bytes arrived during the previous iteration; fetch its
+    // centroid rows.  Tile n + 3: bytes and indices.
+    take_bytes(regs, nbytes);
+    load_mu(a, P2.seg, h, L, tix, regs);
+    load_bytes(sd, P3, L, nbytes);
+    load_idx(sd, P3, L, tix);
 
     if (wave_active) {
       // ---- keys past the segment end (their rows hold centroid 0) ----
@@ -687,7 +733,9 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
       }
       // ---- phase 3: P = exp2(S sc2 - m) in fp16 and O^T += V^T P; the second
       //      half's exponentials overlap the first half's MFMAs ----
-      const uint8_t* vrow = B.vt + ln * VSTR + 16 * hh;
+      // physical chunk of logical chunk 2 (2 kt + s2) + hh in row 32 c + ln:
+      // 2 ((2 kt + s2) ^ c) + (hh ^ (ln / 16)), see vt_offset
+      const uint8_t* vrow = B.vt + ln * VSTR + 16 * (hh ^ (ln >> 4));
       float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -698,7 +746,7 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
         for (int c = 0; c < 4; ++c)
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2)
-            vf[c][s2] = *reinterpret_cast<const f16x8*>(vrow + 32 * c * VSTR + 64 * kt + 32 * s2);
+            vf[c][s2] = *reinterpret_cast<const f16x8*>(vrow + 32 * c * VSTR + 32 * ((2 * kt + s2) ^ c));
         u32x4 pw[2];
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
@@ -720,12 +768,11 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
     }
     __syncthreads();
     P0 = P1; T0 = T1;
-    P1 = P2; T1 = rs.T;
-    if (P3.seg != P2.seg) rs = raw_seg(a, P3.seg);
-    P2 = P3;
+    P1 = P2; T1 = T2;
+    P2 = P3; T2 = sd.T;
     if (n + 4 < count) {
-      P3 = advance(a, P3, is.T);
-      if (P3.seg != P2.seg) is = idx_seg(a, P3.seg);
+      P3 = advance(a, P3, sd.T);
+      if (P3.seg != P2.seg) sd = seg_desc(a, P3.seg, h);
     }
     cur ^= 1;
   }
