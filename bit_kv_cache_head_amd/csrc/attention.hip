@@ -44,6 +44,7 @@ struct AttnArgs {
   int32_t nqb; int32_t units;
   float scale;
   const uint16_t* tabs;   // fp16 centroid tables [seg][H][2][256][128]: K (channel-permuted), V
+  const uint16_t* ut;     // fp16 basis fragments [seg][H][R][8][2][8] (zero without PSAC), see attention_tables_kernel
   // final outputs (nsplit == 1)
   float* out; float* lse; int32_t* top1; int32_t H;
   // partial outputs (nsplit > 1): [split][H][Tq][D], [split][H][Tq] x (m, l), top value / index
@@ -109,12 +110,32 @@ __device__ __forceinline__ h2 code_pair(uint32_t w, int sh, const CodeMasks& m) 
 
 // ---------------------------------------------------------------------------
 // fp16 copies of every segment's centroid tables (exact for bf16 values in
-// fp16's normal range).  Grid (n_segs * H), 256 threads, thread = centroid.
+// fp16's normal range), and of its basis as the A operand of (U^T)(Q^T): for
+// basis vector n, k-step s and lane half hh, the 8 values U[c][n] at the
+// channels c = 16 s + 4 hh + j / 2 + 8 (j % 2) (j = 0..7) that the Query
+// fragments hold in that position.  Zeros for a segment without a basis.
+// Grid (n_segs * H), 256 threads, thread = centroid.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attention_tables_kernel(const qwm_segment* __restrict__ segs, int32_t H,
-                                                               uint16_t* __restrict__ tabs) {
+                                                               uint16_t* __restrict__ tabs, uint16_t* __restrict__ ut) {
   const int sh = blockIdx.x, seg = sh / H, h = sh % H, j = threadIdx.x;
   const qwm_segment& sg = segs[seg];
+  {
+    // four consecutive fragment values (same n, s, hh; j' = 4 (j % 2) .. +4)
+    const int i = 4 * j, n = i >> 7, s = (i >> 4) & 7, hf = (i >> 3) & 1;
+    uint32_t w[2] = {0u, 0u};
+    if (sg.U != nullptr) {
+      const uint16_t* Uh = sg.U + (int64_t)h * D * R;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jj = (i & 7) + e;
+        const int c = 16 * s + 4 * hf + (jj >> 1) + 8 * (jj & 1);
+        const uint16_t v = __builtin_bit_cast(uint16_t, (_Float16)__uint_as_float((uint32_t)Uh[c * R + n] << 16));
+        w[e >> 1] |= (uint32_t)v << (16 * (e & 1));
+      }
+    }
+    *reinterpret_cast<uint2*>(ut + (int64_t)sh * R * D + i) = make_uint2(w[0], w[1]);
+  }
   const u32x4* kr = reinterpret_cast<const u32x4*>(sg.k_centroids + ((int64_t)h * NC + j) * D);
   const u32x4* vr = reinterpret_cast<const u32x4*>(sg.v_centroids + ((int64_t)h * NC + j) * D);
   u32x4* kt = reinterpret_cast<u32x4*>(tabs + ((int64_t)sh * 2 + 0) * TAB_ELEMS + (int64_t)j * D);
@@ -624,50 +645,30 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   int cur = 0;
   int qp_seg = -1;
   f16x8 qpf = __builtin_bit_cast(f16x8, u32x4{0, 0, 0, 0});
-  bool psac = false;
   const h2 ones = as_h2(0x3C003C00u);
   for (int n = 0; n < count; ++n) {
     if (P0.seg != qp_seg) {
-      // Q U for this segment: (U^T) (Q^T) on MFMA with bf16 operands
-      cseg& sg = seg_at(a, P0.seg);
+      // Q U for this segment: (U^T) (Q^T) on MFMA with the Query fragments as
+      // B; the basis fragments come from the workspace (zeros without PSAC;
+      // rows n >= R read as zeros, past the end of their buffer)
       qp_seg = P0.seg;
-      psac = sg.U != nullptr;
-      qpf = __builtin_bit_cast(f16x8, u32x4{0, 0, 0, 0});
-      if (psac && wave_active) {
-        const __attribute__((address_space(1))) uint16_t* Uh = gmem(sg.U) + (int64_t)h * D * R;
-        f32x16 acc = {};
+      const rsrc_t ur = buf(a.ut + (int64_t)(P0.seg * a.H + h) * (R * D), R * D * 2);
+      f32x16 acc = {};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          u32x4 uv = {0, 0, 0, 0};
-          if (ln < R) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              uv[e] = (uint32_t)Uh[(16 * s + 8 * hh + 2 * e) * R + ln] |
-                      ((uint32_t)Uh[(16 * s + 8 * hh + 2 * e + 1) * R + ln] << 16);
-          }
-          u32x4 qv;
-          if (a.qdtype == QWM_BF16) {
-            qv = qvalid ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + qoff + 16 * s + 8 * hh)
-                        : u32x4{0, 0, 0, 0};
-          } else {
-            const float* src = static_cast<const float*>(a.q) + qoff + 16 * s + 8 * hh;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              qv[e] = qvalid ? (f32_to_bf16_bits(src[2 * e]) | (f32_to_bf16_bits(src[2 * e + 1]) << 16)) : 0u;
-          }
-          acc = mfma_bf16(__builtin_bit_cast(bf16x8, uv), __builtin_bit_cast(bf16x8, qv), acc);
-        }
-        // lane (query, hh) holds (QU)[4 hh + 0..3]; hh = 0 needs all 8
-        const float o0 = swap32_f(acc[0]), o1 = swap32_f(acc[1]), o2 = swap32_f(acc[2]), o3 = swap32_f(acc[3]);
-        u32x4 pv = {0, 0, 0, 0};
-        if (hh == 0) {
-          pv[0] = pack_f16x2(acc[0], acc[1]);
-          pv[1] = pack_f16x2(acc[2], acc[3]);
-          pv[2] = pack_f16x2(o0, o1);
-          pv[3] = pack_f16x2(o2, o3);
-        }
-        qpf = __builtin_bit_cast(f16x8, pv);
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 v = ld128(ur, ((ln * 8 + s) * 2 + hh) * 16);
+        acc = mfma_f16(__builtin_bit_cast(f16x8, v), qf[s], acc);
       }
+      // lane (query, hh) holds (QU)[4 hh + 0..3]; hh = 0 needs all 8
+      const float o0 = swap32_f(acc[0]), o1 = swap32_f(acc[1]), o2 = swap32_f(acc[2]), o3 = swap32_f(acc[3]);
+      u32x4 pv = {0, 0, 0, 0};
+      if (hh == 0) {
+        pv[0] = pack_f16x2(acc[0], acc[1]);
+        pv[1] = pack_f16x2(acc[2], acc[3]);
+        pv[2] = pack_f16x2(o0, o1);
+        pv[3] = pack_f16x2(o2, o3);
+      }
+      qpf = __builtin_bit_cast(f16x8, pv);
     }
     const AttnBuf& B = sb[cur];
     const int64_t k0 = (int64_t)P0.tile * AT_K;
@@ -873,7 +874,8 @@ static int attention_splits(int64_t Tq, int32_t H, int64_t total_keys) {
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs) {
-  size_t bytes = al256((size_t)n_segs * H * 2 * TAB_ELEMS * sizeof(uint16_t));
+  size_t bytes = al256((size_t)n_segs * H * 2 * TAB_ELEMS * sizeof(uint16_t)) +
+                 al256((size_t)n_segs * H * R * D * sizeof(uint16_t));
   const int ns = attention_splits(Tq, H, total_keys);
   if (ns > 1) {
     const size_t n = (size_t)ns * H * Tq;
@@ -893,6 +895,8 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
   char* p = static_cast<char*>(ws);
   a.tabs = reinterpret_cast<uint16_t*>(p);
   p += al256((size_t)n_segs * q->H * 2 * TAB_ELEMS * sizeof(uint16_t));
+  a.ut = reinterpret_cast<uint16_t*>(p);
+  p += al256((size_t)n_segs * q->H * R * D * sizeof(uint16_t));
   if (a.nsplit > 1) {
     const size_t n = (size_t)a.nsplit * q->H * q->T;
     a.po = reinterpret_cast<float*>(p); p += al256(n * D * 4);
@@ -902,7 +906,7 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
     a.pti = reinterpret_cast<int32_t*>(p);
   }
   hipLaunchKernelGGL(attention_tables_kernel, dim3((unsigned)(n_segs * q->H)), dim3(NC), 0, stream, segs, q->H,
-                     const_cast<uint16_t*>(a.tabs));
+                     const_cast<uint16_t*>(a.tabs), const_cast<uint16_t*>(a.ut));
   qwm_status s = check_launch("attention tables");
   if (s != QWM_OK) return s;
   const int per = (a.units + 7) / 8;

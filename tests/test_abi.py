@@ -46,7 +46,8 @@ def test_sizes_and_strides():
     assert k >= 12 * 256 * 128 * 2 + 12 * 1560 * 4
     assert lib.qwm_workspace_bytes(1, 1560, 12, 0, 0) > k       # Lloyd adds assignment + shuffle
     # attention: fp16 centroid tables for every (segment, head), plus split partials
-    assert lib.qwm_workspace_bytes(4, 64, 1, 16, 1) == 2 * 256 * 128 * 2     # one split: tables only
+    # one split: fp16 centroid tables and basis fragments only
+    assert lib.qwm_workspace_bytes(4, 64, 1, 16, 1) == 2 * 256 * 128 * 2 + 8 * 128 * 2
     big = lib.qwm_workspace_bytes(4, 39000, 12, 1560, 25)
     assert big >= 25 * 12 * 2 * 256 * 128 * 2
     assert lib.qwm_workspace_bytes(4, 39000, 12, 1560, 0) == 0
