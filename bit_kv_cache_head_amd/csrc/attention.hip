@@ -114,15 +114,18 @@ __device__ __forceinline__ h2 code_pair(uint32_t w, int sh, const CodeMasks& m) 
 // basis vector n, k-step s and lane half hh, the 8 values U[c][n] at the
 // channels c = 16 s + 4 hh + j / 2 + 8 (j % 2) (j = 0..7) that the Query
 // fragments hold in that position.  Zeros for a segment without a basis.
-// Grid (n_segs * H), 256 threads, thread = centroid.
+// Grid (n_segs * H, 8): block (sh, y) converts centroids 32 y .. +32, thread
+// (centroid 32 y + tid / 8, channels 16 (tid % 8) .. +16), so a wave reads 8
+// whole rows; blocks y = 0 also write the basis fragments.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attention_tables_kernel(const qwm_segment* __restrict__ segs, int32_t H,
                                                                uint16_t* __restrict__ tabs, uint16_t* __restrict__ ut) {
-  const int sh = blockIdx.x, seg = sh / H, h = sh % H, j = threadIdx.x;
+  const int sh = blockIdx.x, seg = sh / H, h = sh % H, tid = threadIdx.x;
+  const int j = 32 * (int)blockIdx.y + (tid >> 3), blk = tid & 7;
   const qwm_segment& sg = segs[seg];
-  {
-    // four consecutive fragment values (same n, s, hh; j' = 4 (j % 2) .. +4)
-    const int i = 4 * j, n = i >> 7, s = (i >> 4) & 7, hf = (i >> 3) & 1;
+  if (blockIdx.y == 0) {
+    // four consecutive fragment values (same n, s, hh; j' = 4 (tid % 2) .. +4)
+    const int i = 4 * tid, n = i >> 7, s = (i >> 4) & 7, hf = (i >> 3) & 1;
     uint32_t w[2] = {0u, 0u};
     if (sg.U != nullptr) {
       const uint16_t* Uh = sg.U + (int64_t)h * D * R;
@@ -140,14 +143,13 @@ __global__ __launch_bounds__(256) void attention_tables_kernel(const qwm_segment
   const u32x4* vr = reinterpret_cast<const u32x4*>(sg.v_centroids + ((int64_t)h * NC + j) * D);
   u32x4* kt = reinterpret_cast<u32x4*>(tabs + ((int64_t)sh * 2 + 0) * TAB_ELEMS + (int64_t)j * D);
   u32x4* vtb = reinterpret_cast<u32x4*>(tabs + ((int64_t)sh * 2 + 1) * TAB_ELEMS + (int64_t)j * D);
-#pragma unroll
-  for (int blk = 0; blk < D / 16; ++blk) {
+  {
     const u32x4 a = kr[2 * blk], b = kr[2 * blk + 1];   // channels 16 blk + 0..7, + 8..15
     u32x4 o0, o1;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       // word m = (channel m, channel m + 8)
-      const uint32_t lo = (m < 8) ? ((m & 1) ? (a[m >> 1] >> 16) : (a[m >> 1] & 0xFFFFu)) : 0u;
+      const uint32_t lo = (m & 1) ? (a[m >> 1] >> 16) : (a[m >> 1] & 0xFFFFu);
       const uint32_t hi = (m & 1) ? (b[m >> 1] >> 16) : (b[m >> 1] & 0xFFFFu);
       const uint32_t w = pack_f16x2(__uint_as_float(lo << 16), __uint_as_float(hi << 16));
       if (m < 4) o0[m] = w; else o1[m - 4] = w;
@@ -905,7 +907,7 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
     a.ptv = reinterpret_cast<float*>(p); p += al256(n * 4);
     a.pti = reinterpret_cast<int32_t*>(p);
   }
-  hipLaunchKernelGGL(attention_tables_kernel, dim3((unsigned)(n_segs * q->H)), dim3(NC), 0, stream, segs, q->H,
+  hipLaunchKernelGGL(attention_tables_kernel, dim3((unsigned)(n_segs * q->H), D / 16), dim3(NC), 0, stream, segs, q->H,
                      const_cast<uint16_t*>(a.tabs), const_cast<uint16_t*>(a.ut));
   qwm_status s = check_launch("attention tables");
   if (s != QWM_OK) return s;
