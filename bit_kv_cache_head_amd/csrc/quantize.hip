@@ -15,6 +15,8 @@ namespace qwm {
 
 enum { MODE_ASSIGN = 0, MODE_VALUES = 1, MODE_KEYS = 2 };
 
+constexpr int PREP_PARTS = NC / 32;   // table-preparation blocks per head
+
 constexpr int SEL_TOK = 128;     // tokens per block pass (4 waves x 32)
 
 struct TablePrepArgs {
@@ -24,30 +26,38 @@ struct TablePrepArgs {
   uint16_t* tbl_lo;     // [H][256][128] bf16  remainder of -2 w mu (weighted tables only)
   uint16_t* aug;        // [H][256][4]   bf16  (B hi, mid, lo, 0)
   float* Bj;            // [H][256]
-  float* Bmax;          // [H]
+  float* Bmax;          // [H][PREP_PARTS] partial maxima of B (times 1 + 2^-16)
   double* Wg;           // [H][2]
   int32_t* counter;     // fallback work counter (zeroed here)
 };
 
-// One block per head, thread j = centroid j.
+// Block (h, part): centroids 32 part .. +32 of head h; thread (centroid
+// 32 part + tid / 8, channels 16 (tid % 8) .. +16).  B_j is summed over each
+// thread's 16 channels in fp64 and then over the 8 threads of the centroid.
+// Each block writes the maximum of its 32 B_j; block 0 the group weight sums.
 __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
-  const int h = blockIdx.x, j = threadIdx.x;
+  const int h = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
+  const int j = 32 * part + (tid >> 3), c0 = 16 * (tid & 7);
   __shared__ float ws[D];
   __shared__ float bm[4];
-  if (j < D) ws[j] = a.w ? a.w[h * D + j] : 1.0f;
-  if (h == 0 && j == 0) *a.counter = 0;
+  if (tid < D) ws[tid] = a.w ? a.w[h * D + tid] : 1.0f;
+  if (h == 0 && part == 0 && tid == 0) *a.counter = 0;
   __syncthreads();
-  const uint16_t* mj = a.mu + ((int64_t)h * NC + j) * D;
-  uint16_t* tj = a.tbl + ((int64_t)h * NC + j) * D;
+  const uint16_t* mj = a.mu + ((int64_t)h * NC + j) * D + c0;
+  uint16_t* tj = a.tbl + ((int64_t)h * NC + j) * D + c0;
   double B = 0.0;
-  for (int c0 = 0; c0 < D; c0 += 8) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(mj + c0);
+  u32x4 v[2];
+  v[0] = *reinterpret_cast<const u32x4*>(mj);
+  v[1] = *reinterpret_cast<const u32x4*>(mj + 8);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
     u32x4 o, ol;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      uint32_t lo16 = v[e] & 0xFFFFu, hi16 = v[e] >> 16;
+      const int c = c0 + 8 * half + 2 * e;
+      uint32_t lo16 = v[half][e] & 0xFFFFu, hi16 = v[half][e] >> 16;
       const float m0 = bf16_bits_to_f32(lo16), m1 = bf16_bits_to_f32(hi16);
-      const float w0 = ws[c0 + 2 * e], w1 = ws[c0 + 2 * e + 1];
+      const float w0 = ws[c], w1 = ws[c + 1];
       B = fma((double)w0 * (double)m0, (double)m0, B);
       B = fma((double)w1 * (double)m1, (double)m1, B);
       const float p0 = -2.0f * w0 * m0, p1 = -2.0f * w1 * m1;
@@ -56,27 +66,33 @@ __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
       o[e] = t0 | (t1 << 16);
       ol[e] = f32_to_bf16_bits(p0 - bf16_bits_to_f32(t0)) | (f32_to_bf16_bits(p1 - bf16_bits_to_f32(t1)) << 16);
     }
-    *reinterpret_cast<u32x4*>(tj + c0) = o;
-    if (a.w) *reinterpret_cast<u32x4*>(a.tbl_lo + ((int64_t)h * NC + j) * D + c0) = ol;
+    *reinterpret_cast<u32x4*>(tj + 8 * half) = o;
+    if (a.w) *reinterpret_cast<u32x4*>(a.tbl_lo + ((int64_t)h * NC + j) * D + c0 + 8 * half) = ol;
   }
-  const uint32_t bh = f64_to_bf16_bits(B);
-  const double r1 = B - (double)bf16_bits_to_f32(bh);
-  const uint32_t bmid = f64_to_bf16_bits(r1);
-  const double r2 = r1 - (double)bf16_bits_to_f32(bmid);
-  const uint32_t blo = f64_to_bf16_bits(r2);
-  uint16_t* ag = a.aug + ((int64_t)h * NC + j) * 4;
-  ag[0] = (uint16_t)bh; ag[1] = (uint16_t)bmid; ag[2] = (uint16_t)blo; ag[3] = 0;
-  a.Bj[h * NC + j] = (float)B;
-  // block max of B over the 256 centroids; group weight sums over 64 channels
+  // the centroid's 8 partial sums, in a fixed order
+  B += __shfl_xor(B, 1, 64);
+  B += __shfl_xor(B, 2, 64);
+  B += __shfl_xor(B, 4, 64);
+  if ((tid & 7) == 0) {
+    const uint32_t bh = f64_to_bf16_bits(B);
+    const double r1 = B - (double)bf16_bits_to_f32(bh);
+    const uint32_t bmid = f64_to_bf16_bits(r1);
+    const double r2 = r1 - (double)bf16_bits_to_f32(bmid);
+    const uint32_t blo = f64_to_bf16_bits(r2);
+    uint16_t* ag = a.aug + ((int64_t)h * NC + j) * 4;
+    ag[0] = (uint16_t)bh; ag[1] = (uint16_t)bmid; ag[2] = (uint16_t)blo; ag[3] = 0;
+    a.Bj[h * NC + j] = (float)B;
+  }
+  // block max of B over its 32 centroids; group weight sums over 64 channels
   // (fp64 sums of fp32 weights, exact for any sane spread of magnitudes)
   const float wmax = wave_max_f((float)B);
-  const int lane = j & 63, wv = j >> 6;
-  double gsum = 0.0;
-  if (wv < 2) gsum = wave_sum_d((double)ws[j]);
+  const int lane = tid & 63, wv = tid >> 6;
   if (lane == 0) bm[wv] = wmax;
+  double gsum = 0.0;
+  if (part == 0 && wv < 2) gsum = wave_sum_d((double)ws[tid]);
   __syncthreads();
-  if (j == 0) a.Bmax[h] = fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3])) * (1.0f + 1.0f / 65536.0f);
-  if (wv < 2 && lane == 0) a.Wg[2 * h + wv] = gsum;
+  if (tid == 0) a.Bmax[h * PREP_PARTS + part] = fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3])) * (1.0f + 1.0f / 65536.0f);
+  if (part == 0 && wv < 2 && lane == 0) a.Wg[2 * h + wv] = gsum;
 }
 
 struct SelectArgs {
@@ -247,7 +263,9 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
     }
   }
   __syncthreads();
-  const float Bmax = a.Bmax[h];
+  float Bmax = a.Bmax[h * PREP_PARTS];
+#pragma unroll
+  for (int p = 1; p < PREP_PARTS; ++p) Bmax = fmaxf(Bmax, a.Bmax[h * PREP_PARTS + p]);
   const double W0 = a.Wg[2 * h], W1 = a.Wg[2 * h + 1];
   const float cb = a.cb;
   const uint16_t* muh = a.mu + (int64_t)h * NC * D;
@@ -682,7 +700,8 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
     {
       const u32x4* mrow = reinterpret_cast<const u32x4*>(a.mu + ((int64_t)h * NC + lane) * D);
       double s[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma nounroll
+      // four channel slices per round trip: 16 table loads in flight
+#pragma unroll 4
       for (int c8 = 0; c8 < D / 8; ++c8) {
         double kk[8], ww[8];
 #pragma unroll
@@ -947,8 +966,21 @@ __global__ __launch_bounds__(256) void lloyd_update_kernel(const void* x, int32_
   for (int64_t t0 = 0; t0 < T; t0 += LU_TILE) {
     const int64_t len = (T - t0 < LU_TILE) ? (T - t0) : LU_TILE;
     __syncthreads();
-    // assignment rows carry no alignment promise: byte loads, coalesced
-    for (int e = tid; e < len; e += 256) tile[e] = ah[t0 + e];
+    // assignment rows carry no alignment promise: byte loads, coalesced, all
+    // of a thread's loads in flight before the first store
+    {
+      uint8_t v[LU_TILE / 256];
+#pragma unroll
+      for (int u = 0; u < LU_TILE / 256; ++u) {
+        const int e = tid + 256 * u;
+        v[u] = e < len ? ah[t0 + e] : (uint8_t)0;
+      }
+#pragma unroll
+      for (int u = 0; u < LU_TILE / 256; ++u) {
+        const int e = tid + 256 * u;
+        if (e < len) tile[e] = v[u];
+      }
+    }
     __syncthreads();
     for (int b = 0; b < len; b += 32) {
       const bool match = (b + q < len) && tile[b + q] == (uint8_t)j;
@@ -1005,7 +1037,7 @@ size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd) {
   b += align256((size_t)H * NC * D * 2);
   b += align256((size_t)H * NC * 4 * 2);
   b += align256((size_t)H * NC * 4);
-  b += align256((size_t)H * 4);
+  b += align256((size_t)H * PREP_PARTS * 4);
   b += align256((size_t)H * 2 * 8);
   b += align256(16);
   b += align256((size_t)H * T * 4);
@@ -1024,7 +1056,7 @@ static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd) {
   w.tbl_lo = reinterpret_cast<uint16_t*>(take((size_t)H * NC * D * 2));
   w.aug = reinterpret_cast<uint16_t*>(take((size_t)H * NC * 4 * 2));
   w.Bj = reinterpret_cast<float*>(take((size_t)H * NC * 4));
-  w.Bmax = reinterpret_cast<float*>(take((size_t)H * 4));
+  w.Bmax = reinterpret_cast<float*>(take((size_t)H * PREP_PARTS * 4));
   w.Wg = reinterpret_cast<double*>(take((size_t)H * 2 * 8));
   w.counter = reinterpret_cast<int32_t*>(take(16));
   w.worklist = reinterpret_cast<int32_t*>(take((size_t)H * T * 4));
@@ -1087,7 +1119,7 @@ static void fill_common(SelectArgs& a, const qwm_tokens* x, const SelWork& w, co
 
 static qwm_status prep(const SelWork& w, const uint16_t* mu, const float* wts, int32_t H, hipStream_t stream) {
   TablePrepArgs p{mu, wts, w.tbl, w.tbl_lo, w.aug, w.Bj, w.Bmax, w.Wg, w.counter};
-  hipLaunchKernelGGL(prep_table_kernel, dim3(H), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(prep_table_kernel, dim3(H, PREP_PARTS), dim3(256), 0, stream, p);
   return check_launch("centroid table preparation");
 }
 
