@@ -139,6 +139,7 @@ struct EigShared {
   double Hm[P][PP];
   double W[P][PP];
   double G[P][PP];
+  double rd[P];           // reciprocals of G's diagonal (solve_rows)
   double cs[P / 2][2];
   double theta[P];
   double red[4][P];
@@ -231,7 +232,10 @@ __device__ void cholesky16(EigShared& sm, int tid, double shift_rel) {
 }
 
 // dst = src R^{-1} (R upper, in G), one row per thread; src == dst allowed.
+// The 16 pivot reciprocals are formed once (sm.rd) and multiplied.
 __device__ __forceinline__ void solve_rows(EigShared& sm, const double (*src)[PP], double (*dst)[PP], int tid) {
+  if (tid < P) sm.rd[tid] = 1.0 / sm.G[tid][tid];
+  __syncthreads();
   if (tid < D) {
     double x[P];
 #pragma unroll
@@ -239,7 +243,7 @@ __device__ __forceinline__ void solve_rows(EigShared& sm, const double (*src)[PP
       double s = src[tid][j];
 #pragma unroll
       for (int p = 0; p < P; ++p) if (p < j) s -= x[p] * sm.G[p][j];
-      x[j] = s / sm.G[j][j];
+      x[j] = s * sm.rd[j];
     }
 #pragma unroll
     for (int j = 0; j < P; ++j) dst[tid][j] = x[j];
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ S, 
   }
   __syncthreads();
   int salt = 0;
-  orthonormalize(sm, sm.Y, sm.X, 3, tid, salt, h);
+  orthonormalize(sm, sm.Y, sm.X, 2, tid, salt, h);
   int it = 0, converged = 0;
   for (it = 1; it <= EIG_ROUNDS; ++it) {
     for (int o = 0; o < ORTH_PER_ROUND; ++o) {
@@ -431,7 +435,9 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ S, 
         matvec(a, src, dst, tid);
         src = dst;
       }
-      orthonormalize(sm, sm.Y, sm.X, 2, tid, salt, h);
+      // between power steps one (shifted) Cholesky-QR pass keeps the block well
+      // conditioned; the last one before Rayleigh-Ritz is a full second pass
+      orthonormalize(sm, sm.Y, sm.X, o + 1 == ORTH_PER_ROUND ? 2 : 1, tid, salt, h);
     }
     matvec(a, sm.X, sm.Y, tid);                   // Y = A X
     // Rayleigh-Ritz: Hm = sym(X^T A X), eigen-decomposed by Jacobi
