@@ -112,6 +112,28 @@ __device__ __forceinline__ float swap32_f(float v) { return __shfl_xor(v, 32, 64
 __device__ __forceinline__ uint32_t swap32_u(uint32_t v) { return __shfl_xor(v, 32, 64); }
 __device__ __forceinline__ double swap32_d(double v) { return __shfl_xor(v, 32, 64); }
 
+// Lanes l and l ^ 32 (v_permlane32_swap, no LDS round trip).  The swap of a
+// value with itself returns s[0] = lane l % 32's value and s[1] = lane
+// (l % 32) + 32's value on both lanes, so the pair reductions below compute the
+// same result, in the same order, on both lanes.
+__device__ __forceinline__ float lanepair_sum(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float lanepair_min(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float lanepair_max(float v) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+// the value held by lane l ^ 32 (hh = l / 32)
+__device__ __forceinline__ float lanepair_other(float v, int hh) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(hh ? s[0] : s[1]);
+}
+
 __device__ __forceinline__ float wave_max_f(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;

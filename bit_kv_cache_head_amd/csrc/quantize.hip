@@ -22,8 +22,6 @@ constexpr int SEL_TOK = 128;     // tokens per block pass (4 waves x 32)
 struct TablePrepArgs {
   const uint16_t* mu;   // [H][256][128] bf16
   const float* w;       // [H][128] or null (w = 1)
-  uint16_t* tbl;        // [H][256][128] bf16  (-2 w mu), rounded
-  uint16_t* tbl_lo;     // [H][256][128] bf16  remainder of -2 w mu (weighted tables only)
   uint16_t* aug;        // [H][256][4]   bf16  (B hi, mid, lo, 0)
   float* Bj;            // [H][256]
   float* Bmax;          // [H][PREP_PARTS] partial maxima of B (times 1 + 2^-16)
@@ -44,14 +42,12 @@ __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
   if (h == 0 && part == 0 && tid == 0) *a.counter = 0;
   __syncthreads();
   const uint16_t* mj = a.mu + ((int64_t)h * NC + j) * D + c0;
-  uint16_t* tj = a.tbl + ((int64_t)h * NC + j) * D + c0;
   double B = 0.0;
   u32x4 v[2];
   v[0] = *reinterpret_cast<const u32x4*>(mj);
   v[1] = *reinterpret_cast<const u32x4*>(mj + 8);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    u32x4 o, ol;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int c = c0 + 8 * half + 2 * e;
@@ -60,14 +56,7 @@ __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
       const float w0 = ws[c], w1 = ws[c + 1];
       B = fma((double)w0 * (double)m0, (double)m0, B);
       B = fma((double)w1 * (double)m1, (double)m1, B);
-      const float p0 = -2.0f * w0 * m0, p1 = -2.0f * w1 * m1;
-      const uint32_t t0 = f32_to_bf16_bits(p0);
-      const uint32_t t1 = f32_to_bf16_bits(p1);
-      o[e] = t0 | (t1 << 16);
-      ol[e] = f32_to_bf16_bits(p0 - bf16_bits_to_f32(t0)) | (f32_to_bf16_bits(p1 - bf16_bits_to_f32(t1)) << 16);
     }
-    *reinterpret_cast<u32x4*>(tj + 8 * half) = o;
-    if (a.w) *reinterpret_cast<u32x4*>(a.tbl_lo + ((int64_t)h * NC + j) * D + c0 + 8 * half) = ol;
   }
   // the centroid's 8 partial sums, in a fixed order
   B += __shfl_xor(B, 1, 64);
@@ -97,7 +86,7 @@ __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
 
 struct SelectArgs {
   const void* x; int64_t T; int64_t st; int64_t sh;
-  const uint16_t* tbl; const uint16_t* tbl_lo; const uint16_t* aug; const float* Bj; const float* Bmax;
+  const uint16_t* aug; const float* Bj; const float* Bmax;
   const double* Wg;
   const uint16_t* mu;   // [H][256][128]
   const float* w;       // [H][128] or null
@@ -111,12 +100,12 @@ struct SelectArgs {
   qwm_diag* diag;
 };
 
-template <bool WT>
 struct SelShared {
-  uint16_t tbl[WT ? 2 : 1][NC * D];   // swizzled: row j, 16-byte chunk c at (c ^ (j & 15)); [1] = remainder
+  uint16_t mu[NC * D];         // centroid rows, swizzled: 16-byte chunk c of row j at chunk (c ^ (j & 15))
   uint16_t aug[NC][4];
   float bj[NC];
   float w[D];
+  float wm2[D];                // -2 w (exact)
   uint16_t ut[R][D];           // U^T (bf16)
   uint8_t codes[4][32][32];
   uint8_t idx[4][32];
@@ -188,76 +177,81 @@ struct ResidStats {
   float d, lo0, hi0, lo1, hi1;
 };
 
-// token value of channel 16 s + 8 hh + e: from the packed bf16 fragment, or the fp32 copy
-template <bool F32>
-__device__ __forceinline__ float kval(const bf16x8 (&kb)[8], const float* kf, int s, int e) {
-  if (F32) return kf[8 * s + e];
-  const uint32_t w = __builtin_bit_cast(u32x4, kb[s])[e >> 1];
-  return (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+// 16-byte chunk c (channels 8c .. 8c+7) of centroid row j in the swizzled LDS table
+__device__ __forceinline__ u32x4 mu_chunk(const uint16_t* tab, int j, int c) {
+  return reinterpret_cast<const u32x4*>(tab)[j * 16 + (c ^ (j & 15))];
 }
 
-template <bool F32, bool WEIGHTED>
-__device__ __forceinline__ ResidStats resid_stats(const bf16x8 (&kb)[8], const float* kf, const uint16_t* mj,
-                                                  int hh, const float* wsm) {
-  // Keep the unpacked token and the weights out of registers across calls:
-  // they are re-derived per candidate (cheap) instead of pinning 128 VGPRs.
+// Residual statistics of the token kf (the lane's channels 16 s + 8 hh + e at
+// kf[8 s + e]) against centroid j of the LDS table.
+template <bool WEIGHTED>
+__device__ __forceinline__ ResidStats resid_stats(const float (&kf)[64], const uint16_t* tab, int j, int hh,
+                                                  const float* wsm) {
+  // the weights are re-read from LDS per candidate instead of pinning 64 VGPRs
   asm volatile("" ::: "memory");
   ResidStats o{0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    u32x4 kw = __builtin_bit_cast(u32x4, kb[s]);
-    asm volatile("" : "+v"(kw));
-    const u32x4 mv = *reinterpret_cast<const u32x4*>(mj + 16 * s + 8 * hh);
+    const u32x4 mv = mu_chunk(tab, j, 2 * s + hh);
     f32x4 w0 = {1.f, 1.f, 1.f, 1.f}, w1 = {1.f, 1.f, 1.f, 1.f};
     if (WEIGHTED) {
       w0 = *reinterpret_cast<const f32x4*>(wsm + 16 * s + 8 * hh);
       w1 = *reinterpret_cast<const f32x4*>(wsm + 16 * s + 8 * hh + 4);
     }
+    float lo = 0.f, hi = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t mw = mv[e >> 1];
       const float m = (e & 1) ? __uint_as_float(mw & 0xFFFF0000u) : __uint_as_float(mw << 16);
-      float x;
-      if (F32) x = kf[8 * s + e];
-      else x = (e & 1) ? __uint_as_float(kw[e >> 1] & 0xFFFF0000u) : __uint_as_float(kw[e >> 1] << 16);
-      const float r = x - m;
+      const float r = kf[8 * s + e] - m;
       if (WEIGHTED) o.d = fmaf((e < 4 ? w0[e] : w1[e - 4]) * r, r, o.d);
       else o.d = fmaf(r, r, o.d);
-      if (s < 4) { o.lo0 = fminf(o.lo0, r); o.hi0 = fmaxf(o.hi0, r); }
-      else { o.lo1 = fminf(o.lo1, r); o.hi1 = fmaxf(o.hi1, r); }
+      lo = fminf(lo, r);
+      hi = fmaxf(hi, r);
     }
+    if (s < 4) { o.lo0 = fminf(o.lo0, lo); o.hi0 = fmaxf(o.hi0, hi); }
+    else { o.lo1 = fminf(o.lo1, lo); o.hi1 = fmaxf(o.hi1, hi); }
   }
-  o.d += swap32_f(o.d);
-  o.lo0 = fminf(o.lo0, swap32_f(o.lo0)); o.hi0 = fmaxf(o.hi0, swap32_f(o.hi0));
-  o.lo1 = fminf(o.lo1, swap32_f(o.lo1)); o.hi1 = fmaxf(o.hi1, swap32_f(o.hi1));
+  o.d = lanepair_sum(o.d);
+  o.lo0 = lanepair_min(o.lo0); o.hi0 = lanepair_max(o.hi0);
+  o.lo1 = lanepair_min(o.lo1); o.hi1 = lanepair_max(o.hi1);
   return o;
 }
 
 constexpr float DREL = 1.0f / 65536.0f;   // relative error bound of the fp32 rescored distance
 
 // QS: QSAC selection (keys with the QSAC flag and M > 1); otherwise nearest.
-// WT: the table carries a bf16 remainder (weighted distances).
+// WT: Query-weighted distances.
+//
+// The GEMM's A operand is the exact bf16 centroid row mu_j, staged once per
+// block in LDS (where the rescoring and the encoder read it too); the B operand
+// is the token side t = -2 w (.) k, exact in bf16 for unweighted bf16 tokens and
+// otherwise carried as a bf16 pair t_hi + t_lo (two MFMAs per k-step).
 template <int MODE, bool F32, bool QS, bool WT>
-__global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
   constexpr int KT = QS ? 8 : 3;   // values tracked per lane (each lane holds half the centroids)
-  __shared__ SelShared<WT> sm;
+  constexpr bool SPLIT = F32 || WT;
+  __shared__ SelShared sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hh = lane >> 5, ln = lane & 31;
   const int h = blockIdx.y;
   const bool use_psac = (MODE == MODE_KEYS) && (a.flags & QWM_PSAC) && a.U != nullptr;
 
-  // ---- stage the per-head table, weights and U^T ----
+  // ---- stage the centroid rows, B_j, weights and U^T ----
   {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.tbl + (int64_t)h * NC * D);
-    const u32x4* srcl = reinterpret_cast<const u32x4*>(a.tbl_lo + (int64_t)h * NC * D);
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.mu + (int64_t)h * NC * D);
+#pragma unroll 4
     for (int e = tid; e < NC * 16; e += 256) {
       const int j = e >> 4, c = e & 15;
-      reinterpret_cast<u32x4*>(sm.tbl[0])[j * 16 + (c ^ (j & 15))] = src[e];
-      if (WT) reinterpret_cast<u32x4*>(sm.tbl[WT ? 1 : 0])[j * 16 + (c ^ (j & 15))] = srcl[e];
+      reinterpret_cast<u32x4*>(sm.mu)[j * 16 + (c ^ (j & 15))] = src[e];
     }
     const uint2* asrc = reinterpret_cast<const uint2*>(a.aug + (int64_t)h * NC * 4);
     reinterpret_cast<uint2*>(sm.aug)[tid] = asrc[tid];
     sm.bj[tid] = a.Bj[h * NC + tid] * (1.0f + 1.0f / 1048576.0f);   // upper bound of B_j
-    if (tid < D) sm.w[tid] = a.w ? a.w[h * D + tid] : 1.0f;
+    if (tid < D) {
+      const float wc = a.w ? a.w[h * D + tid] : 1.0f;
+      sm.w[tid] = wc;
+      sm.wm2[tid] = -2.0f * wc;
+    }
     if (use_psac) {
       for (int e = tid; e < D * R; e += 256) sm.ut[e % R][e / R] = a.U[(int64_t)h * D * R + e];
     }
@@ -268,7 +262,6 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
   for (int p = 1; p < PREP_PARTS; ++p) Bmax = fmaxf(Bmax, a.Bmax[h * PREP_PARTS + p]);
   const double W0 = a.Wg[2 * h], W1 = a.Wg[2 * h + 1];
   const float cb = a.cb;
-  const uint16_t* muh = a.mu + (int64_t)h * NC * D;
 
   const int64_t ntile = (a.T + SEL_TOK - 1) / SEL_TOK;
   for (int64_t tile = blockIdx.x; tile < ntile; tile += a.blocks_per_head) {
@@ -277,16 +270,16 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
     const bool valid = tok < a.T;
     const int64_t rowoff = (int64_t)h * a.sh + (valid ? tok : 0) * a.st;
 
-    // ---- token fragments (B operand) and fp32 copy: channels 16 s + 8 hh + e ----
-    bf16x8 kb[8];
-    bf16x8 kl[8];
-    float kf[F32 ? 64 : 1];
+    // ---- the token in fp32: channels 16 s + 8 hh + e at kf[8 s + e] ----
+    float kf[64];
     if (!F32) {
       const uint16_t* xr = static_cast<const uint16_t*>(a.x) + rowoff;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const u32x4 v = valid ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
-        kb[s] = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          kf[8 * s + e] = (e & 1) ? __uint_as_float(v[e >> 1] & 0xFFFF0000u) : __uint_as_float(v[e >> 1] << 16);
       }
     } else {
       const float* xr = static_cast<const float*>(a.x) + rowoff;
@@ -294,19 +287,35 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
       for (int s = 0; s < 8; ++s) {
         const f32x4 v0 = valid ? *reinterpret_cast<const f32x4*>(xr + 16 * s + 8 * hh) : f32x4{0, 0, 0, 0};
         const f32x4 v1 = valid ? *reinterpret_cast<const f32x4*>(xr + 16 * s + 8 * hh + 4) : f32x4{0, 0, 0, 0};
-        u32x4 hi, lo;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = e < 2 ? v0[2 * e] : v1[2 * e - 4];
-          const float x1 = e < 2 ? v0[2 * e + 1] : v1[2 * e - 3];
-          if (F32) { kf[8 * s + 2 * e] = x0; kf[8 * s + 2 * e + 1] = x1; }
-          const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
-          hi[e] = h0 | (h1 << 16);
-          lo[e] = f32_to_bf16_bits(x0 - bf16_bits_to_f32(h0)) | (f32_to_bf16_bits(x1 - bf16_bits_to_f32(h1)) << 16);
-        }
-        kb[s] = __builtin_bit_cast(bf16x8, hi);
-        kl[s] = __builtin_bit_cast(bf16x8, lo);
+        for (int e = 0; e < 4; ++e) { kf[8 * s + e] = v0[e]; kf[8 * s + 4 + e] = v1[e]; }
       }
+    }
+    // ---- GEMM B operand t = -2 w (.) k: bf16 t_hi (RNE) and, unless exact, the
+    // bf16 t_lo of the remainder t - t_hi (exact in fp32) ----
+    bf16x8 th[8], tl[SPLIT ? 8 : 1];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+      u32x4 hv, lv;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int c = 16 * s + 8 * hh + 2 * e2;
+        const float x0 = kf[8 * s + 2 * e2], x1 = kf[8 * s + 2 * e2 + 1];
+        const float t0 = WT ? sm.wm2[c] * x0 : -2.0f * x0;
+        const float t1 = WT ? sm.wm2[c + 1] * x1 : -2.0f * x1;
+        bf16x2 p;
+        p[0] = (__bf16)t0; p[1] = (__bf16)t1;
+        hv[e2] = __builtin_bit_cast(uint32_t, p);
+        if (SPLIT) {
+          bf16x2 q;
+          q[0] = (__bf16)(t0 - __uint_as_float(hv[e2] << 16));
+          q[1] = (__bf16)(t1 - __uint_as_float(hv[e2] & 0xFFFF0000u));
+          lv[e2] = __builtin_bit_cast(uint32_t, q);
+        }
+      }
+      th[s] = __builtin_bit_cast(bf16x8, hv);
+      if (SPLIT) tl[SPLIT ? s : 0] = __builtin_bit_cast(bf16x8, lv);
     }
     bf16x8 kaug;
     {
@@ -325,15 +334,9 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
       const int j = 32 * ct + ln;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const int c = 2 * s + hh;
-        const bf16x8 af = reinterpret_cast<const bf16x8*>(sm.tbl[0])[j * 16 + (c ^ (j & 15))];
-        acc = mfma_bf16(af, kb[s], acc);
-        if (F32) acc = mfma_bf16(af, kl[s], acc);
-        if (WT) {
-          const bf16x8 al = reinterpret_cast<const bf16x8*>(sm.tbl[WT ? 1 : 0])[j * 16 + (c ^ (j & 15))];
-          acc = mfma_bf16(al, kb[s], acc);
-          if (F32) acc = mfma_bf16(al, kl[s], acc);
-        }
+        const bf16x8 af = __builtin_bit_cast(bf16x8, mu_chunk(sm.mu, j, 2 * s + hh));
+        acc = mfma_bf16(af, th[s], acc);
+        if (SPLIT) acc = mfma_bf16(af, tl[SPLIT ? s : 0], acc);
       }
       {
         u32x4 v = {0, 0, 0, 0};
@@ -347,14 +350,28 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
     float g[2 * KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-      const float o = swap32_f(t[k]);
+      const float o = lanepair_other(t[k], hh);
       g[k] = hh ? o : t[k];
       g[KT + k] = hh ? t[k] : o;
     }
     const float floor_unt = fminf(unpacked(g[KT - 1]), unpacked(g[2 * KT - 1]));   // every untracked value is >= this
+    if (QS) {
+      // one ascending list of the 2 KT tracked values: half 1 reversed makes the
+      // sequence bitonic; four half-cleaner stages sort it
+#pragma unroll
+      for (int k = 0; k < KT / 2; ++k) {
+        const float x = g[KT + k];
+        g[KT + k] = g[2 * KT - 1 - k];
+        g[2 * KT - 1 - k] = x;
+      }
+#pragma unroll
+      for (int d = KT; d >= 1; d >>= 1)
+#pragma unroll
+        for (int i = 0; i < 2 * KT; ++i)
+          if ((i & d) == 0) cswap(g[i], g[i + d]);
+    }
     float gmin = g[0];
-    int kmin = 0;
-    if (g[KT] < gmin) { gmin = g[KT]; kmin = KT; }
+    if (!QS && g[KT] < gmin) gmin = g[KT];
 
     // ---- token norm A = sum_c w_c k_c^2 ----
     float A = 0.f;
@@ -362,10 +379,10 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
     for (int s = 0; s < 8; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = kval<F32>(kb, kf, s, e);
+        const float x = kf[8 * s + e];
         A = fmaf(sm.w[16 * s + 8 * hh + e] * x, x, A);
       }
-    A += swap32_f(A);
+    A = lanepair_sum(A);
     const float A_hi = A * (1.0f + 1.0f / 32768.0f), A_lo = A * (1.0f - 1.0f / 32768.0f);
     // certified bounds on d_Q(j) = A + e_j from the GEMM value f_j:
     //   [lbA + f_j - cb B_j, ubA + f_j + cb B_j]
@@ -374,7 +391,9 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
 #define QWM_LB(pv) (lbA + unpacked(pv) - cb * sm.bj[__float_as_uint(pv) & 0xFFu])
 #define QWM_UB(pv) (ubA + unpacked(pv) + cb * sm.bj[__float_as_uint(pv) & 0xFFu])
 
-    bool fast = valid && __builtin_isfinite(gmin) && __builtin_isfinite(A) && __builtin_isfinite(ubA + cb * Bmax);
+    // |f_j| <= A + 2 B_j: with this bound finite no GEMM value (or partial sum) overflows
+    bool fast = valid && __builtin_isfinite(gmin) && __builtin_isfinite(A) &&
+                __builtin_isfinite(2.0f * (ubA + 2.0f * Bmax));
     int win = (int)(__float_as_uint(gmin) & 0xFFu);
     float wlo0 = 0.f, whi0 = 0.f, wlo1 = 0.f, whi1 = 0.f;   // group ranges of the winner
     bool have_w = false;                                   // ranges known for the winner
@@ -401,7 +420,7 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
         const bool need = fast && !by_bounds && (QWM_LB(cn[e]) <= d1 * (1.0f + DREL));
         if (!__any(need)) continue;
         const int j = (int)(__float_as_uint(cn[e]) & 0xFFu);
-        const ResidStats rs = resid_stats<F32, WT>(kb, kf, muh + (int64_t)j * D, hh, sm.w);
+        const ResidStats rs = resid_stats<WT>(kf, sm.mu, j, hh, sm.w);
         if (need) {
           evm |= 1u << e;
           dn[e] = rs.d;
@@ -427,45 +446,64 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
     } else {
       // QSAC.  Tracked candidate k is certainly outside the M nearest when M other
       // values are certainly smaller; the untracked ones must all be outside too.
-      float Lb[2 * KT], Ub[2 * KT];
-#pragma unroll
-      for (int k = 0; k < 2 * KT; ++k) { Lb[k] = QWM_LB(g[k]); Ub[k] = QWM_UB(g[k]); }
+      // Lb[k] is a lower bound on d_Q of slot k (raised to the rescored value once
+      // the slot is scored); jp packs the slot's centroid index, four per word.
+      float Lb[2 * KT];
+      uint32_t jp[2 * KT / 4];
       int below_floor = 0;
       uint32_t outmask = 0;
+      {
+        float Ub[2 * KT];
 #pragma unroll
-      for (int k = 0; k < 2 * KT; ++k) {
-        below_floor += (Ub[k] < L_unt) ? 1 : 0;
-        int n_before = 0;
+        for (int k = 0; k < 2 * KT; ++k) { Lb[k] = QWM_LB(g[k]); Ub[k] = QWM_UB(g[k]); }
 #pragma unroll
-        for (int m = 0; m < 2 * KT; ++m) n_before += (Ub[m] < Lb[k]) ? 1 : 0;
-        outmask |= (n_before >= a.M ? 1u : 0u) << k;
+        for (int q = 0; q < 2 * KT / 4; ++q) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v |= (__float_as_uint(g[4 * q + e]) & 0xFFu) << (8 * e);
+          jp[q] = v;
+        }
+#pragma unroll
+        for (int k = 0; k < 2 * KT; ++k) {
+          below_floor += (Ub[k] < L_unt) ? 1 : 0;
+          int n_before = 0;
+#pragma unroll
+          for (int m = 0; m < 2 * KT; ++m) n_before += (Ub[m] < Lb[k]) ? 1 : 0;
+          outmask |= (n_before >= a.M ? 1u : 0u) << k;
+        }
       }
       const bool unt_out = below_floor >= a.M;   // untracked centroids are all outside the M nearest
-      // score S for every possible member, smallest values of both halves first,
+      // score S for every possible member in ascending order of the GEMM value,
       // skipping candidates whose distance bound already exceeds the best S (S >= d_Q)
       double Sbest = __builtin_inf();
       float dwin = 0.f;
-      float dv[2 * KT];
-      uint32_t evmask = 0;
-#pragma unroll
-      for (int step = 0; step < 2 * KT; ++step) {
-        const int k = (step & 1) ? KT + (step >> 1) : (step >> 1);
-        dv[k] = 0.f;
-        const bool need = fast && !((outmask >> k) & 1u) &&
-                          ((double)Lb[k] <= Sbest * (1.0 + 1.0 / 1048576.0));
-        if (!__any(need)) continue;
-        const int j = (int)(__float_as_uint(g[k]) & 0xFFu);
-        const ResidStats rs = resid_stats<F32, WT>(kb, kf, muh + (int64_t)j * D, hh, sm.w);
-        if (need) {
-          evmask |= 1u << k;
-          dv[k] = rs.d;
-          const double R0 = (double)rs.hi0 - (double)rs.lo0, R1 = (double)rs.hi1 - (double)rs.lo1;
-          const double S = W0 * R0 * R0 + W1 * R1 * R1;
-          if (!have_w || S < Sbest || (S == Sbest && j < win)) {
-            Sbest = S; win = j; dwin = rs.d;
-            wlo0 = rs.lo0; whi0 = rs.hi0; wlo1 = rs.lo1; whi1 = rs.hi1; have_w = true;
+      // one slot per pass, always from position 0: Lb, jp and outmask rotate by
+      // one slot per pass and are back in place after the 2 KT passes
+#pragma unroll 1
+      for (int it = 0; it < 2 * KT; ++it) {
+        const bool need = fast && !(outmask & 1u) && ((double)Lb[0] <= Sbest * (1.0 + 1.0 / 1048576.0));
+        if (__any(need)) {
+          const int j = (int)(jp[0] & 0xFFu);
+          const ResidStats rs = resid_stats<WT>(kf, sm.mu, j, hh, sm.w);
+          if (need) {
+            Lb[0] = fmaxf(Lb[0], rs.d * (1.0f - DREL));
+            const double R0 = (double)rs.hi0 - (double)rs.lo0, R1 = (double)rs.hi1 - (double)rs.lo1;
+            const double S = W0 * R0 * R0 + W1 * R1 * R1;
+            if (!have_w || S < Sbest || (S == Sbest && j < win)) {
+              Sbest = S; win = j; dwin = rs.d;
+              wlo0 = rs.lo0; whi0 = rs.hi0; wlo1 = rs.lo1; whi1 = rs.hi1; have_w = true;
+            }
           }
         }
+        const float l0 = Lb[0];
+#pragma unroll
+        for (int i = 0; i + 1 < 2 * KT; ++i) Lb[i] = Lb[i + 1];
+        Lb[2 * KT - 1] = l0;
+        const uint32_t j0 = jp[0];
+#pragma unroll
+        for (int q = 0; q + 1 < 2 * KT / 4; ++q) jp[q] = __builtin_amdgcn_alignbit(jp[q + 1], jp[q], 8);
+        jp[2 * KT / 4 - 1] = __builtin_amdgcn_alignbit(j0, jp[2 * KT / 4 - 1], 8);
+        outmask = (outmask >> 1) | ((outmask & 1u) << (2 * KT - 1));
       }
       if (fast) {
         // the winner must be among the M nearest: count every centroid that may precede it
@@ -473,9 +511,8 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
         int before = 0;
 #pragma unroll
         for (int k = 0; k < 2 * KT; ++k) {
-          const int j = (int)(__float_as_uint(g[k]) & 0xFFu);
-          const float lo = ((evmask >> k) & 1u) ? dv[k] * (1.0f - DREL) : Lb[k];
-          before += (j != win && lo <= dwin_hi) ? 1 : 0;
+          const int j = (int)((jp[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+          before += (j != win && Lb[k] <= dwin_hi) ? 1 : 0;
         }
         // untracked centroids either lie outside the M nearest or cannot beat the best S (S >= d_Q)
         const bool unt_ok = unt_out || ((double)L_unt > Sbest * (1.0 + 1.0 / 1048576.0));
@@ -495,9 +532,8 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
       }
     } else {
       // ---- ranges of the winner (when the choice came from bounds alone) ----
-      const uint16_t* mw = muh + (int64_t)win * D;
       if (__any(!have_w)) {
-        const ResidStats rs = resid_stats<F32, WT>(kb, kf, mw, hh, sm.w);
+        const ResidStats rs = resid_stats<WT>(kf, sm.mu, win, hh, sm.w);
         if (!have_w) { wlo0 = rs.lo0; whi0 = rs.hi0; wlo1 = rs.lo1; whi1 = rs.hi1; }
       }
       bool sat0 = false, sat1 = false;
@@ -509,20 +545,20 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const GroupCodec& g = s < 4 ? g0 : g1;
-        const u32x4 mv = *reinterpret_cast<const u32x4*>(mw + 16 * s + 8 * hh);
+        const u32x4 mv = mu_chunk(sm.mu, win, 2 * s + hh);
         uint32_t bits = 0;
         float Ev[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t mwd = mv[e >> 1];
           const float m = (e & 1) ? __uint_as_float(mwd & 0xFFFF0000u) : __uint_as_float(mwd << 16);
-          const float r = kval<F32>(kb, kf, s, e) - m;
+          const float r = kf[8 * s + e] - m;
           const uint32_t q = code_of(r, g);
           bits |= q << (2 * e);
           Ev[e] = r - g.s * ((float)q - (float)g.z);
           if (F32 && use_psac) {
             // add the rounding error of r = fl32(k - mu) (TwoSum) so that E = k - mu - r_hat
-            const float x = kval<F32>(kb, kf, s, e);
+            const float x = kf[8 * s + e];
             const float bv = r - x;
             Ev[e] += (x - (r - bv)) + (-m - bv);
           }
@@ -576,7 +612,7 @@ __global__ __launch_bounds__(256, MODE == MODE_KEYS ? 1 : 2) void select_kernel(
           const f32x16 acc = pacc;
           // lane (token, hh) holds C[4 hh + 0..3] in acc[0..3]
           float m = fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])), fmaxf(fabsf(acc[2]), fabsf(acc[3])));
-          m = fmaxf(m, swap32_f(m));
+          m = lanepair_max(m);
           bool sat = false;
           const uint32_t csb = fp16_up_div((double)m, 127.0f, &sat);
           const float cs = f16_bits_to_f32(csb);
@@ -1025,7 +1061,7 @@ namespace qwm_host {
 using namespace qwm;
 
 struct SelWork {
-  uint16_t* tbl; uint16_t* tbl_lo; uint16_t* aug; float* Bj; float* Bmax; double* Wg; int32_t* counter; int32_t* worklist;
+  uint16_t* aug; float* Bj; float* Bmax; double* Wg; int32_t* counter; int32_t* worklist;
   uint8_t* assign; int32_t* perm;
 };
 
@@ -1033,8 +1069,6 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd) {
   size_t b = 0;
-  b += align256((size_t)H * NC * D * 2);
-  b += align256((size_t)H * NC * D * 2);
   b += align256((size_t)H * NC * 4 * 2);
   b += align256((size_t)H * NC * 4);
   b += align256((size_t)H * PREP_PARTS * 4);
@@ -1052,8 +1086,6 @@ static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd) {
   char* p = static_cast<char*>(ws);
   SelWork w{};
   auto take = [&](size_t n) { char* r = p; p += align256(n); return r; };
-  w.tbl = reinterpret_cast<uint16_t*>(take((size_t)H * NC * D * 2));
-  w.tbl_lo = reinterpret_cast<uint16_t*>(take((size_t)H * NC * D * 2));
   w.aug = reinterpret_cast<uint16_t*>(take((size_t)H * NC * 4 * 2));
   w.Bj = reinterpret_cast<float*>(take((size_t)H * NC * 4));
   w.Bmax = reinterpret_cast<float*>(take((size_t)H * PREP_PARTS * 4));
@@ -1113,25 +1145,29 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
 
 static void fill_common(SelectArgs& a, const qwm_tokens* x, const SelWork& w, const uint16_t* mu) {
   a.x = x->ptr; a.T = x->T; a.st = x->stride_t; a.sh = x->stride_h;
-  a.tbl = w.tbl; a.tbl_lo = w.tbl_lo; a.aug = w.aug; a.Bj = w.Bj; a.Bmax = w.Bmax; a.Wg = w.Wg;
+  a.aug = w.aug; a.Bj = w.Bj; a.Bmax = w.Bmax; a.Wg = w.Wg;
   a.mu = mu; a.counter = w.counter; a.worklist = w.worklist;
 }
 
 static qwm_status prep(const SelWork& w, const uint16_t* mu, const float* wts, int32_t H, hipStream_t stream) {
-  TablePrepArgs p{mu, wts, w.tbl, w.tbl_lo, w.aug, w.Bj, w.Bmax, w.Wg, w.counter};
+  TablePrepArgs p{mu, wts, w.aug, w.Bj, w.Bmax, w.Wg, w.counter};
   hipLaunchKernelGGL(prep_table_kernel, dim3(H, PREP_PARTS), dim3(256), 0, stream, p);
   return check_launch("centroid table preparation");
 }
 
-// Certified bound c on |f_j - e_j| / (||k||_w^2 + B_j) for the GEMM values:
-//   fp32 accumulation of 131 exact products: <= 131 u * 2 (A + B)   ~ 1.6e-5
-//   the 8 index bits packed into each value: <= 2^-15 |f| <= 2^-14 (A + B)
-//   bf16 split of B_j (2^-24 B) and of fp32 tokens (2^-17 (A + B))
-//   weighted tables carry a bf16 remainder (hi + lo, 259 products): the
-//   accumulation term doubles to ~3.1e-5 and the split leaves 2^-18 (A + B)
-// i.e. 8.5e-5 unweighted and 9.6e-5 weighted; the constants below add margin.
-static float error_coeff(bool weighted) {
-  return weighted ? (1.0f / 8192.0f + 1.0f / 32768.0f) : (1.0f / 8192.0f);
+// Certified bound c on |f_j - e_j| / (A + B_j), A = ||k||_w^2, for the GEMM
+// values f_j = B_j + sum_c mu_jc t_c, t = -2 w (.) k (sum_c |mu_jc t_c| <= A + B_j):
+//   fp32 accumulation of 131 exact bf16 products (t exact in bf16: unweighted
+//   bf16 tokens): <= 131 u (2 (A + B)) ~ 1.6e-5; with the t_hi + t_lo pair, 259
+//   products: ~3.1e-5
+//   the pair's remainder |t - t_hi - t_lo| <= 2^-16 |t| (two RNE roundings):
+//   <= 2^-16 (A + B) ~ 1.5e-5; fl32(w k): 2^-24 (A + B)
+//   the 3-part bf16 split of B_j: 2^-24 B
+//   the 8 index bits packed into each value: <= 2^-15 |f| <= 2^-14 (A + 2 B)
+// i.e. ~7.7e-5 with an exact t and ~1.1e-4 with the pair; the constants below
+// add margin.
+static float error_coeff(bool split) {
+  return split ? (1.0f / 8192.0f + 1.0f / 32768.0f) : (1.0f / 8192.0f);
 }
 
 qwm_status launch_keys(const qwm_tokens* k, const uint16_t* centroids, const float* w, const uint16_t* U,
@@ -1145,7 +1181,7 @@ qwm_status launch_keys(const qwm_tokens* k, const uint16_t* centroids, const flo
   SelectArgs a{};
   fill_common(a, k, wk, centroids);
   a.w = wts; a.U = (flags & QWM_PSAC) ? U : nullptr; a.M = M; a.flags = flags;
-  a.cb = error_coeff(wts != nullptr);
+  a.cb = error_coeff(wts != nullptr || k->dtype != QWM_BF16);
   a.idx = out->idx; a.codes = out->codes; a.scale = out->scale; a.zeros = out->zeros;
   a.zstride = zeros_stride(k->T); a.cq = out->c; a.cscale = out->c_scale; a.diag = diag;
   return run_select<MODE_KEYS>(k, a, stream, "key quantization");
@@ -1158,7 +1194,7 @@ qwm_status launch_values(const qwm_tokens* v, const uint16_t* centroids, const q
   if (s != QWM_OK) return s;
   SelectArgs a{};
   fill_common(a, v, wk, centroids);
-  a.w = nullptr; a.U = nullptr; a.M = 1; a.flags = 0; a.cb = error_coeff(false);
+  a.w = nullptr; a.U = nullptr; a.M = 1; a.flags = 0; a.cb = error_coeff(v->dtype != QWM_BF16);
   a.idx = out->idx; a.codes = out->codes; a.scale = out->scale; a.zeros = out->zeros;
   a.zstride = zeros_stride(v->T); a.cq = nullptr; a.cscale = nullptr; a.diag = diag;
   return run_select<MODE_VALUES>(v, a, stream, "value quantization");
@@ -1185,7 +1221,7 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
     if (s != QWM_OK) return s;
     SelectArgs a{};
     fill_common(a, x, wk, cur);
-    a.M = 1; a.flags = 0; a.cb = error_coeff(false);
+    a.M = 1; a.flags = 0; a.cb = error_coeff(x->dtype != QWM_BF16);
     a.idx = wk.assign; a.diag = diag;
     s = run_select<MODE_ASSIGN>(x, a, stream, "Lloyd assignment");
     if (s != QWM_OK) return s;

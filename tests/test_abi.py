@@ -43,7 +43,7 @@ def test_sizes_and_strides():
     assert lib.qwm_zeros_stride(1560) == 780
     assert lib.qwm_workspace_bytes(0, 1560, 12, 0, 0) == 0
     k = lib.qwm_workspace_bytes(2, 1560, 12, 0, 0)
-    assert k >= 12 * 256 * 128 * 2 + 12 * 1560 * 4
+    assert k >= 12 * 256 * 4 * 2 + 12 * 1560 * 4          # B_j split per centroid + fallback worklist
     assert lib.qwm_workspace_bytes(1, 1560, 12, 0, 0) > k       # Lloyd adds assignment + shuffle
     # attention: fp16 centroid tables for every (segment, head), plus split partials
     # one split: fp16 centroid tables and basis fragments only
