@@ -115,6 +115,17 @@ struct SelShared {
   uint16_t cs[4][32];
 };
 
+// Two fp32 values as a bf16 pair (RNE; v_cvt_pk_bf16_f32), and its halves as fp32.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  bf16x2 p;
+  p[0] = (__bf16)a;
+  p[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, p);
+}
+__device__ __forceinline__ float lo_bf16(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
+
 __device__ __forceinline__ float pack_idx(float f, uint32_t j) {
   return __uint_as_float((__float_as_uint(f) & 0xFFFFFF00u) | j);
 }
@@ -156,11 +167,13 @@ __device__ __forceinline__ uint32_t code_of(float r, const GroupCodec& g) {
 }
 
 // Per-lane running list of the K smallest packed values (t[0] <= ... <= t[K-1]).
+// ninf holds -inf in a register the compiler cannot see through, so that the
+// last step stays one v_med3 (a min would first quiet its packed operand).
 template <int K>
-__device__ __forceinline__ void topk_insert(float (&t)[K], float x) {
+__device__ __forceinline__ void topk_insert(float (&t)[K], float x, float ninf) {
 #pragma unroll
   for (int k = K - 1; k >= 1; --k) t[k] = __builtin_amdgcn_fmed3f(t[k - 1], t[k], x);
-  t[0] = fminf(t[0], x);
+  t[0] = __builtin_amdgcn_fmed3f(ninf, t[0], x);
 }
 
 __device__ __forceinline__ void cswap(float& x, float& y) {
@@ -296,7 +309,6 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
     bf16x8 th[8], tl[SPLIT ? 8 : 1];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
       u32x4 hv, lv;
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -304,15 +316,8 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
         const float x0 = kf[8 * s + 2 * e2], x1 = kf[8 * s + 2 * e2 + 1];
         const float t0 = WT ? sm.wm2[c] * x0 : -2.0f * x0;
         const float t1 = WT ? sm.wm2[c + 1] * x1 : -2.0f * x1;
-        bf16x2 p;
-        p[0] = (__bf16)t0; p[1] = (__bf16)t1;
-        hv[e2] = __builtin_bit_cast(uint32_t, p);
-        if (SPLIT) {
-          bf16x2 q;
-          q[0] = (__bf16)(t0 - __uint_as_float(hv[e2] << 16));
-          q[1] = (__bf16)(t1 - __uint_as_float(hv[e2] & 0xFFFF0000u));
-          lv[e2] = __builtin_bit_cast(uint32_t, q);
-        }
+        hv[e2] = pk_bf16(t0, t1);
+        if (SPLIT) lv[e2] = pk_bf16(t0 - lo_bf16(hv[e2]), t1 - hi_bf16(hv[e2]));
       }
       th[s] = __builtin_bit_cast(bf16x8, hv);
       if (SPLIT) tl[SPLIT ? s : 0] = __builtin_bit_cast(bf16x8, lv);
@@ -328,6 +333,8 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
     float t[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) t[k] = __builtin_inff();
+    float ninf;
+    asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(ninf));
 #pragma unroll 1
     for (int ct = 0; ct < 8; ++ct) {
       f32x16 acc = {};
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
         acc = mfma_bf16(__builtin_bit_cast(bf16x8, v), kaug, acc);
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) topk_insert<KT>(t, pack_idx(acc[i], 32 * ct + c_row(i, hh)));
+      for (int i = 0; i < 16; ++i) topk_insert<KT>(t, pack_idx(acc[i], 32 * ct + c_row(i, hh)), ninf);
     }
     // canonical per-token list: g[0..KT) = half 0, g[KT..2KT) = half 1 (identical on both lanes)
     float g[2 * KT];
@@ -450,9 +457,12 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
       // the slot is scored); jp packs the slot's centroid index, four per word.
       float Lb[2 * KT];
       uint32_t jp[2 * KT / 4];
-      int below_floor = 0;
       uint32_t outmask = 0;
+      bool unt_out;
       {
+        // At least M tracked values are certainly below x iff the M-th smallest
+        // upper bound UbM is < x: slot k is out when Lb[k] > UbM, and every
+        // untracked centroid (d_Q >= L_unt) when L_unt > UbM.
         float Ub[2 * KT];
 #pragma unroll
         for (int k = 0; k < 2 * KT; ++k) { Lb[k] = QWM_LB(g[k]); Ub[k] = QWM_UB(g[k]); }
@@ -463,16 +473,25 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
           for (int e = 0; e < 4; ++e) v |= (__float_as_uint(g[4 * q + e]) & 0xFFu) << (8 * e);
           jp[q] = v;
         }
+        // bitonic sort of the 2 KT upper bounds
 #pragma unroll
-        for (int k = 0; k < 2 * KT; ++k) {
-          below_floor += (Ub[k] < L_unt) ? 1 : 0;
-          int n_before = 0;
+        for (int size = 2; size <= 2 * KT; size <<= 1)
 #pragma unroll
-          for (int m = 0; m < 2 * KT; ++m) n_before += (Ub[m] < Lb[k]) ? 1 : 0;
-          outmask |= (n_before >= a.M ? 1u : 0u) << k;
-        }
+          for (int d = size >> 1; d >= 1; d >>= 1)
+#pragma unroll
+            for (int i = 0; i < 2 * KT; ++i)
+              if ((i & d) == 0) {
+                if ((i & size) == 0) cswap(Ub[i], Ub[i + d]);
+                else cswap(Ub[i + d], Ub[i]);
+              }
+        float UbM = __builtin_inff();   // M > 2 KT: no tracked slot can be certified out
+#pragma unroll
+        for (int k = 0; k < 2 * KT; ++k)
+          if (k == a.M - 1) UbM = Ub[k];
+#pragma unroll
+        for (int k = 0; k < 2 * KT; ++k) outmask |= (Lb[k] > UbM ? 1u : 0u) << k;
+        unt_out = L_unt > UbM;   // untracked centroids are all outside the M nearest
       }
-      const bool unt_out = below_floor >= a.M;   // untracked centroids are all outside the M nearest
       // score S for every possible member in ascending order of the GEMM value,
       // skipping candidates whose distance bound already exceeds the best S (S >= d_Q)
       double Sbest = __builtin_inf();
@@ -568,22 +587,16 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
           bf16x8 uf;
           if (ln < R) uf = *reinterpret_cast<const bf16x8*>(&sm.ut[ln][16 * s + 8 * hh]);
           else uf = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+          // E = b0 + b1 + b2 exactly: each part is the RNE bf16 of the remainder
+          // left by the previous ones (the remainders are exact in fp32)
           u32x4 p0, p1, p2;
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
-            uint32_t b[2][3];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              const float ev = Ev[2 * e2 + half];
-              const uint32_t b0 = f32_to_bf16_bits(ev);
-              const float rem1 = ev - bf16_bits_to_f32(b0);
-              const uint32_t b1 = f32_to_bf16_bits(rem1);
-              const float rem2 = rem1 - bf16_bits_to_f32(b1);
-              b[half][0] = b0; b[half][1] = b1; b[half][2] = f32_to_bf16_bits(rem2);
-            }
-            p0[e2] = b[0][0] | (b[1][0] << 16);
-            p1[e2] = b[0][1] | (b[1][1] << 16);
-            p2[e2] = b[0][2] | (b[1][2] << 16);
+            const float ev0 = Ev[2 * e2], ev1 = Ev[2 * e2 + 1];
+            p0[e2] = pk_bf16(ev0, ev1);
+            const float r0 = ev0 - lo_bf16(p0[e2]), r1 = ev1 - hi_bf16(p0[e2]);
+            p1[e2] = pk_bf16(r0, r1);
+            p2[e2] = pk_bf16(r0 - lo_bf16(p1[e2]), r1 - hi_bf16(p1[e2]));
           }
           pacc = mfma_bf16(uf, __builtin_bit_cast(bf16x8, p0), pacc);
           pacc = mfma_bf16(uf, __builtin_bit_cast(bf16x8, p1), pacc);
