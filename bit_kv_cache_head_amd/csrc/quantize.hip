@@ -1146,9 +1146,10 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
   qwm_status s = check_launch(what);
   if (s != QWM_OK) return s;
   // one wave per flagged token; the count is known only on the device, so the
-  // grid covers the worst case and idle blocks exit at once
+  // grid covers the worst case (up to 4,096 tokens in one round, three blocks
+  // per CU) and idle blocks exit at once
   const int64_t worst = ((int64_t)x->H * x->T + 3) / 4;
-  const int fb = (int)(worst < 256 ? worst : 256);
+  const int fb = (int)(worst < 1024 ? worst : 1024);
   if (x->dtype == QWM_BF16)
     hipLaunchKernelGGL((fallback_kernel<MODE, false>), dim3(fb), dim3(256), 0, stream, a);
   else
