@@ -173,7 +173,9 @@ qwm_status qwm_quantize_values(const qwm_tokens* v, const uint16_t* centroids, c
  * (the logit-side PSAC compensation of QuantWM's method section; the logits
  * of Sec. 3.3 with scale = 1/sqrt(d)).
  * segs: DEVICE array of n_segs descriptors (1 <= n_segs <= 4096), each with
- * T >= 1 tokens; keys are numbered in segment order.
+ * 1 <= T < 2^26 tokens (the kernel addresses a segment's packed arrays through
+ * 32-bit buffer ranges; the descriptors live on the device, so this is the
+ * caller's contract, not a checked error); keys are numbered in segment order.
  * out [Tq][H][d] fp32; lse [H][Tq] fp32 (natural log of the softmax
  * denominator, may be NULL); top1 [H][Tq] int32 = argmax of the logits over
  * all keys (may be NULL).  Workspace: QWM_OP_ATTENTION with T = total keys,
@@ -194,8 +196,9 @@ qwm_status qwm_reference_top1(const qwm_tokens* q, const qwm_tokens* k, int32_t*
 
 /* Bytes of workspace an operation needs (256-byte aligned pointer required).
  * QWM_OP_ATTENTION: T = total cached keys, n = number of queries, n_segs =
- * number of segments (fp16 copies of every segment's centroid tables live in
- * the workspace: n_segs * H * 128 KiB, plus the split-key partials); the other
+ * number of segments.  The workspace holds fp16 copies of every segment's
+ * centroid tables (n_segs * H * 128 KiB), every segment's U_r as fp16 MFMA
+ * fragments (n_segs * H * 2 KiB) and the split-key partials.  The other
  * operations ignore n and n_segs. */
 size_t qwm_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t n, int32_t n_segs);
 
