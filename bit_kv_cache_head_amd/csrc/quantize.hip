@@ -948,120 +948,139 @@ __global__ __launch_bounds__(256) void forgy_kernel(const void* x, int32_t dtype
   }
 }
 
-// Block (g, h) owns clusters 8g .. 8g+7 of head h; half-wave k (32 lanes,
-// lane q = channels 4q..4q+3) owns cluster 8g+k.  The assignment bytes are
-// staged in LDS 4,096 at a time; each half-wave scans them in token order and
-// appends its members to a private list, which it drains (loads four token
-// rows in flight) whenever the list could overflow and at the end.  Members
-// are summed in token order, so the fp64 sums are deterministic.
-constexpr int LU_TILE = 4096;
-constexpr int LU_LIST = 256;
+// The mean update runs in two kernels.
+//
+// lloyd_sort_kernel (grid H, 1,024 threads): a stable counting sort of the
+// head's assignment: ids[h][start_j .. start_j + n_j) lists the members of
+// cluster j in token order, start[h][j] = start_j, start[h][256] = T.  Wave w
+// owns the tokens of the w-th of 16 contiguous ranges; after a count and a
+// scan over (cluster, range), it walks its range 64 tokens at a time, and each
+// lane finds the lanes holding the same cluster from eight ballots, so its
+// place is the range's running offset plus the number of such lanes below it.
+//
+// lloyd_sum_kernel (one wave per (head, cluster), 64 lanes x 2 channels): the
+// member rows summed in token order in fp64, 16 rows in flight; the new
+// centroid is bf16(sum / n); an empty cluster keeps its centroid.
+constexpr int LS_WAVES = 16;
 
-__device__ __forceinline__ void lu_accumulate(const void* x, int32_t dtype, int64_t rowbase, int64_t st,
-                                              const int32_t* list, int n, double (&sum)[4]) {
-  int e = 0;
-  if (dtype == QWM_BF16) {
-    const uint16_t* xb = static_cast<const uint16_t*>(x) + rowbase;
-    for (; e + 4 <= n; e += 4) {
-      uint2 v[4];
+__global__ __launch_bounds__(1024) void lloyd_sort_kernel(const uint8_t* assign, int64_t T, int32_t* ids,
+                                                          int32_t* start) {
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ int32_t cnt[LS_WAVES][NC];     // counts, then running offsets
+  __shared__ int32_t tot[NC];
+  for (int e = tid; e < LS_WAVES * NC; e += 1024) (&cnt[0][0])[e] = 0;
+  __syncthreads();
+  const uint8_t* ah = assign + (int64_t)h * T;
+  const int64_t r0 = T * wv / LS_WAVES, r1 = T * (wv + 1) / LS_WAVES;
+  for (int64_t t = r0 + lane; t < r1; t += 64) atomicAdd(&cnt[wv][ah[t]], 1);
+  __syncthreads();
+  if (tid < NC) {
+    int32_t run = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint2*>(xb + (int64_t)list[e + u] * st);
+    for (int w = 0; w < LS_WAVES; ++w) { const int32_t c = cnt[w][tid]; cnt[w][tid] = run; run += c; }
+    tot[tid] = run;
+  }
+  __syncthreads();
+  // exclusive scan of the cluster totals (one wave, 4 clusters per lane)
+  if (wv == 0) {
+    int32_t v[4], sum = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sum[0] += (double)__uint_as_float(v[u].x << 16);
-        sum[1] += (double)__uint_as_float(v[u].x & 0xFFFF0000u);
-        sum[2] += (double)__uint_as_float(v[u].y << 16);
-        sum[3] += (double)__uint_as_float(v[u].y & 0xFFFF0000u);
-      }
-    }
-    for (; e < n; ++e) {
-      const uint2 v = *reinterpret_cast<const uint2*>(xb + (int64_t)list[e] * st);
-      sum[0] += (double)__uint_as_float(v.x << 16);
-      sum[1] += (double)__uint_as_float(v.x & 0xFFFF0000u);
-      sum[2] += (double)__uint_as_float(v.y << 16);
-      sum[3] += (double)__uint_as_float(v.y & 0xFFFF0000u);
-    }
-  } else {
-    const float* xf = static_cast<const float*>(x) + rowbase;
-    for (; e + 4 <= n; e += 4) {
-      f32x4 v[4];
+    for (int i = 0; i < 4; ++i) { v[i] = tot[4 * lane + i]; sum += v[i]; }
+    int32_t inc = sum;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(xf + (int64_t)list[e + u] * st);
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    int32_t run = inc - sum;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sum[0] += (double)v[u][0]; sum[1] += (double)v[u][1]; sum[2] += (double)v[u][2]; sum[3] += (double)v[u][3];
-      }
+    for (int i = 0; i < 4; ++i) { tot[4 * lane + i] = run; run += v[i]; }
+  }
+  __syncthreads();
+  if (tid < NC) {
+    const int32_t base = tot[tid];
+    start[h * (NC + 1) + tid] = base;
+#pragma unroll
+    for (int w = 0; w < LS_WAVES; ++w) cnt[w][tid] += base;
+  }
+  if (tid == 0) start[h * (NC + 1) + NC] = (int32_t)T;
+  __syncthreads();
+  int32_t* idh = ids + (int64_t)h * T;
+  for (int64_t t0 = r0; t0 < r1; t0 += 64) {
+    const int64_t t = t0 + lane;
+    const bool valid = t < r1;
+    const uint32_t key = valid ? ah[t] : 0u;
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool on = (key >> bit) & 1u;
+      const uint64_t bb = __ballot(on);
+      m &= on ? bb : ~bb;
     }
-    for (; e < n; ++e) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(xf + (int64_t)list[e] * st);
-      sum[0] += (double)v[0]; sum[1] += (double)v[1]; sum[2] += (double)v[2]; sum[3] += (double)v[3];
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (valid) {
+      const int32_t base = cnt[wv][key];
+      idh[base + below] = (int32_t)t;
     }
+    // the lowest lane of each cluster advances that cluster's offset (the
+    // reads above come first: one wave's LDS operations complete in order)
+    if (valid && below == 0) cnt[wv][key] += (int32_t)__popcll(m);
   }
 }
 
-__global__ __launch_bounds__(256) void lloyd_update_kernel(const void* x, int32_t dtype, int64_t T, int64_t st,
-                                                           int64_t sh, const uint8_t* assign, const uint16_t* cin,
-                                                           uint16_t* cout) {
-  const int g = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  __shared__ __align__(16) uint8_t tile[LU_TILE];
-  __shared__ int32_t list[8][LU_LIST];
-  const int k = tid >> 5, q = tid & 31, half = (tid >> 5) & 1;
-  const int j = 8 * g + k;
-  const int64_t rowbase = (int64_t)h * sh + 4 * q;
-  double sum[4] = {0.0, 0.0, 0.0, 0.0};
-  int64_t cnt = 0;
-  int n = 0;
-  const uint8_t* ah = assign + (int64_t)h * T;
-  for (int64_t t0 = 0; t0 < T; t0 += LU_TILE) {
-    const int64_t len = (T - t0 < LU_TILE) ? (T - t0) : LU_TILE;
-    __syncthreads();
-    // assignment rows carry no alignment promise: byte loads, coalesced, all
-    // of a thread's loads in flight before the first store
-    {
-      uint8_t v[LU_TILE / 256];
+__global__ __launch_bounds__(256) void lloyd_sum_kernel(const void* x, int32_t dtype, int64_t T, int64_t st,
+                                                        int64_t sh, int32_t H, const int32_t* ids,
+                                                        const int32_t* start, const uint16_t* cin, uint16_t* cout) {
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= (int64_t)H * NC) return;
+  const int h = (int)(unit / NC), j = (int)(unit % NC);
+  const int32_t b = start[h * (NC + 1) + j], n = start[h * (NC + 1) + j + 1] - b;
+  const int32_t* mem = ids + (int64_t)h * T + b;
+  const int64_t rowbase = (int64_t)h * sh + 2 * lane;
+  double s0 = 0.0, s1 = 0.0;
+  constexpr int U = 16;
+  int e = 0;
+  if (dtype == QWM_BF16) {
+    const uint16_t* xb = static_cast<const uint16_t*>(x) + rowbase;
+    for (; e + U <= n; e += U) {
+      uint32_t v[U];
 #pragma unroll
-      for (int u = 0; u < LU_TILE / 256; ++u) {
-        const int e = tid + 256 * u;
-        v[u] = e < len ? ah[t0 + e] : (uint8_t)0;
-      }
+      for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const uint32_t*>(xb + (int64_t)mem[e + u] * st);
 #pragma unroll
-      for (int u = 0; u < LU_TILE / 256; ++u) {
-        const int e = tid + 256 * u;
-        if (e < len) tile[e] = v[u];
+      for (int u = 0; u < U; ++u) {
+        s0 += (double)__uint_as_float(v[u] << 16);
+        s1 += (double)__uint_as_float(v[u] & 0xFFFF0000u);
       }
     }
-    __syncthreads();
-    for (int b = 0; b < len; b += 32) {
-      const bool match = (b + q < len) && tile[b + q] == (uint8_t)j;
-      const uint64_t m = __ballot(match);
-      const uint32_t mh = (uint32_t)(m >> (32 * half));
-      if (match) list[k][n + __popc(mh & ((1u << q) - 1u))] = (int32_t)(t0 + b + q);
-      n += __popc(mh);
-      // drain when the next 32 could overflow (decided per wave, both halves alike)
-      const int nmax = max(n, __shfl_xor(n, 32, 64));
-      if (nmax > LU_LIST - 32) {
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        lu_accumulate(x, dtype, rowbase, st, list[k], n, sum);
-        cnt += n;
-        n = 0;
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      }
+    for (; e < n; ++e) {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(xb + (int64_t)mem[e] * st);
+      s0 += (double)__uint_as_float(v << 16);
+      s1 += (double)__uint_as_float(v & 0xFFFF0000u);
+    }
+  } else {
+    const float* xf = static_cast<const float*>(x) + rowbase;
+    for (; e + U <= n; e += U) {
+      float2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const float2*>(xf + (int64_t)mem[e + u] * st);
+#pragma unroll
+      for (int u = 0; u < U; ++u) { s0 += (double)v[u].x; s1 += (double)v[u].y; }
+    }
+    for (; e < n; ++e) {
+      const float2 v = *reinterpret_cast<const float2*>(xf + (int64_t)mem[e] * st);
+      s0 += (double)v.x;
+      s1 += (double)v.y;
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  lu_accumulate(x, dtype, rowbase, st, list[k], n, sum);
-  cnt += n;
-  const uint16_t* src = cin + ((int64_t)h * NC + j) * D + 4 * q;
-  uint16_t* dst = cout + ((int64_t)h * NC + j) * D + 4 * q;
-  if (cnt > 0) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e] = (uint16_t)f64_to_bf16_bits(sum[e] / (double)cnt);
+  const uint16_t* src = cin + ((int64_t)h * NC + j) * D + 2 * lane;
+  uint16_t* dst = cout + ((int64_t)h * NC + j) * D + 2 * lane;
+  if (n > 0) {
+    dst[0] = (uint16_t)f64_to_bf16_bits(s0 / (double)n);
+    dst[1] = (uint16_t)f64_to_bf16_bits(s1 / (double)n);
   } else if (src != dst) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e] = src[e];
+    dst[0] = src[0];
+    dst[1] = src[1];
   }
 }
 
@@ -1075,7 +1094,7 @@ using namespace qwm;
 
 struct SelWork {
   uint16_t* aug; float* Bj; float* Bmax; double* Wg; int32_t* counter; int32_t* worklist;
-  uint8_t* assign; int32_t* perm;
+  uint8_t* assign; int32_t* perm; int32_t* start;
 };
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1091,6 +1110,7 @@ size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd) {
   if (lloyd) {
     b += align256((size_t)H * T);
     b += align256((size_t)H * T * 4);
+    b += align256((size_t)H * (NC + 1) * 4);
   }
   return b;
 }
@@ -1108,6 +1128,7 @@ static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd) {
   if (lloyd) {
     w.assign = reinterpret_cast<uint8_t*>(take((size_t)H * T));
     w.perm = reinterpret_cast<int32_t*>(take((size_t)H * T * 4));
+    w.start = reinterpret_cast<int32_t*>(take((size_t)H * (NC + 1) * 4));
   }
   return w;
 }
@@ -1239,8 +1260,13 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
     a.idx = wk.assign; a.diag = diag;
     s = run_select<MODE_ASSIGN>(x, a, stream, "Lloyd assignment");
     if (s != QWM_OK) return s;
-    hipLaunchKernelGGL(lloyd_update_kernel, dim3(NC / 8, x->H), dim3(256), 0, stream, x->ptr, x->dtype, x->T,
-                       x->stride_t, x->stride_h, wk.assign, cur, centroids);
+    // the Forgy permutation is dead by now: its buffer holds the sorted members
+    hipLaunchKernelGGL(lloyd_sort_kernel, dim3(x->H), dim3(1024), 0, stream, wk.assign, x->T, wk.perm, wk.start);
+    s = check_launch("Lloyd member sort");
+    if (s != QWM_OK) return s;
+    const int64_t units = (int64_t)x->H * NC;
+    hipLaunchKernelGGL(lloyd_sum_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, x->ptr, x->dtype,
+                       x->T, x->stride_t, x->stride_h, x->H, wk.perm, wk.start, cur, centroids);
     s = check_launch("Lloyd update");
     if (s != QWM_OK) return s;
     cur = centroids;
