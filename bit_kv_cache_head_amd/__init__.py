@@ -13,7 +13,7 @@ import os
 import torch
 
 from ._abi import (lib, LIB_PATH, QWM_OK, QWM_F32, QWM_BF16, QWM_QSAC, QWM_PSAC, QWM_OP_STATS,
-                   QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION, Tokens, QStats,
+                   QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION, QWM_OP_ATTENTION_ACTIVE, Tokens, QStats,
                    Packed, Diag, Segment, check)
 
 D, NC, R, GROUP = 128, 256, 8, 64
@@ -188,18 +188,28 @@ def segments_tensor(segments, device="cuda") -> tuple:
     return host.to(device), total
 
 
-def attention(q: torch.Tensor, segs: torch.Tensor, n_segs: int, total_keys: int, scale: float | None = None,
-              want_lse: bool = False, want_top1: bool = False):
-    """out [Tq, H, 128] fp32 (+ lse [H, Tq], top1 [H, Tq] int32)."""
+def attention(q: torch.Tensor, segs: torch.Tensor | None, n_segs: int, total_keys: int, scale: float | None = None,
+              want_lse: bool = False, want_top1: bool = False, active: tuple | None = None):
+    """out [Tq, H, 128] fp32 (+ lse [H, Tq], top1 [H, Tq] int32).  `active`:
+    (K, V) of the BF16 active chunk, [Ta, H, 128] bf16 each (segs may then be
+    None with n_segs = total_keys = 0)."""
     td = _tokens(q)
     if scale is None:
         scale = 1.0 / (D ** 0.5)
     out = torch.empty(td.T, td.H, D, dtype=torch.float32, device=q.device)
     lse = torch.empty(td.H, td.T, dtype=torch.float32, device=q.device) if want_lse else None
     top1 = torch.empty(td.H, td.T, dtype=torch.int32, device=q.device) if want_top1 else None
-    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_ATTENTION, total_keys, td.H, td.T, n_segs), q.device)
-    check(lib.qwm_attention(C.byref(td), C.c_void_p(segs.data_ptr()), n_segs, total_keys, C.c_float(scale),
-                            _ptr(out), _ptr(lse), _ptr(top1), ws, nb, _stream()))
+    sp = C.c_void_p(segs.data_ptr() if segs is not None else 0)
+    if active is None:
+        ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_ATTENTION, total_keys, td.H, td.T, n_segs), q.device)
+        check(lib.qwm_attention(C.byref(td), sp, n_segs, total_keys, C.c_float(scale),
+                                _ptr(out), _ptr(lse), _ptr(top1), ws, nb, _stream()))
+    else:
+        ka, va = _tokens(active[0]), _tokens(active[1])
+        ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_ATTENTION_ACTIVE, total_keys + ka.T, td.H, td.T, n_segs),
+                         q.device)
+        check(lib.qwm_attention_active(C.byref(td), sp, n_segs, total_keys, C.byref(ka), C.byref(va),
+                                       C.c_float(scale), _ptr(out), _ptr(lse), _ptr(top1), ws, nb, _stream()))
     return out, lse, top1
 
 

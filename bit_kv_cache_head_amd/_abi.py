@@ -10,11 +10,11 @@ LIB_PATH = os.path.join(_PKG, "libquantwm.so")
 QWM_OK, QWM_ERR_ARG, QWM_ERR_UNSUPPORTED, QWM_ERR_WORKSPACE, QWM_ERR_HIP = 0, 1, 2, 3, 4
 QWM_F32, QWM_BF16 = 0, 1
 QWM_QSAC, QWM_PSAC = 1, 2
-QWM_OP_STATS, QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION = 0, 1, 2, 3, 4
+QWM_OP_STATS, QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION, QWM_OP_ATTENTION_ACTIVE = 0, 1, 2, 3, 4, 5
 
 # every symbol include/quantwm.h declares
 EXPORTS = ["qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys", "qwm_quantize_values",
-           "qwm_attention", "qwm_reference_top1", "qwm_workspace_bytes", "qwm_zeros_stride", "qwm_last_error", "qwm_abi_version"]
+           "qwm_attention", "qwm_attention_active", "qwm_reference_top1", "qwm_workspace_bytes", "qwm_zeros_stride", "qwm_last_error", "qwm_abi_version"]
 
 
 class Tokens(C.Structure):
@@ -57,6 +57,7 @@ def _load():
     L.qwm_quantize_keys.argtypes = [P, P, P, P, C.c_int32, C.c_uint32, P, P, P, C.c_size_t, P]
     L.qwm_quantize_values.argtypes = [P, P, P, P, P, C.c_size_t, P]
     L.qwm_attention.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, C.c_size_t, P]
+    L.qwm_attention_active.argtypes = [P, P, C.c_int32, C.c_int64, P, P, C.c_float, P, P, P, P, C.c_size_t, P]
     L.qwm_reference_top1.argtypes = [P, P, P, P]
     L.qwm_workspace_bytes.argtypes = [C.c_int32, C.c_int64, C.c_int32, C.c_int64, C.c_int32]
     L.qwm_workspace_bytes.restype = C.c_size_t
@@ -65,7 +66,7 @@ def _load():
     L.qwm_last_error.restype = C.c_char_p
     L.qwm_abi_version.restype = C.c_int32
     for name in ("qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys",
-                 "qwm_quantize_values", "qwm_attention"):
+                 "qwm_quantize_values", "qwm_attention", "qwm_attention_active"):
         getattr(L, name).restype = C.c_int
     return L
 

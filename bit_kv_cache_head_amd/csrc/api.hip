@@ -1,5 +1,6 @@
 // C ABI of libquantwm: argument validation, workspace sizing, dispatch.
 #include <cstdio>
+#include <algorithm>
 #include <string>
 
 #include "common.hpp"
@@ -31,10 +32,11 @@ qwm_status launch_values(const qwm_tokens* v, const uint16_t* centroids, const q
 qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const uint16_t* init, uint16_t* centroids,
                         qwm_diag* diag, void* ws, hipStream_t stream);
 qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
-                            float scale, float* out, float* lse, int32_t* top1, void* ws, hipStream_t stream);
+                            const qwm_tokens* ka, const qwm_tokens* va, float scale, float* out, float* lse,
+                            int32_t* top1, void* ws, hipStream_t stream);
 qwm_status launch_reference_top1(const qwm_tokens* q, const qwm_tokens* k, int32_t* top1, hipStream_t stream);
 size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd);
-size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs);
+size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs, bool active);
 
 static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -98,7 +100,8 @@ size_t qwm_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t n, int32_t 
     case QWM_OP_CENTROIDS: return select_ws_bytes(T, H, true);
     case QWM_OP_KEYS:
     case QWM_OP_VALUES: return select_ws_bytes(T, H, false);
-    case QWM_OP_ATTENTION: return n_segs >= 1 ? attention_ws_bytes(T, H, n, n_segs) : 0;
+    case QWM_OP_ATTENTION: return n_segs >= 1 ? attention_ws_bytes(T, H, n, n_segs, false) : 0;
+    case QWM_OP_ATTENTION_ACTIVE: return n_segs >= 0 ? attention_ws_bytes(T, H, n, n_segs, true) : 0;
     default: return 0;
   }
 }
@@ -166,21 +169,55 @@ qwm_status qwm_quantize_values(const qwm_tokens* v, const uint16_t* centroids, c
   return launch_values(v, centroids, out, diag, ws, static_cast<hipStream_t>(stream));
 }
 
-qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
-                         float scale, float* out, float* lse, int32_t* top1, void* ws, size_t ws_bytes,
-                         qwm_stream stream) {
+static qwm_status check_attention_common(const qwm_tokens* q, float scale, const float* out, const float* lse,
+                                         const int32_t* top1) {
   qwm_status s = check_tokens(q, "queries", false);
   if (s != QWM_OK) return s;
-  if (!segs || !aligned(segs, 8)) return fail(QWM_ERR_ARG, "segments: null or misaligned device array");
-  if (n_segs < 1 || n_segs > 4096) return fail(QWM_ERR_ARG, "n_segs must be in [1, 4096]");
-  if (total_keys < 1) return fail(QWM_ERR_ARG, "total_keys must be positive");
   if (!(scale > 0.0f) || !__builtin_isfinite(scale)) return fail(QWM_ERR_ARG, "scale must be finite and positive");
   if (!out || !aligned(out, 16)) return fail(QWM_ERR_ARG, "out: null or not 16-byte aligned");
   if (lse && !aligned(lse, 4)) return fail(QWM_ERR_ARG, "lse misaligned");
   if (top1 && !aligned(top1, 4)) return fail(QWM_ERR_ARG, "top1 misaligned");
-  s = check_ws(ws, ws_bytes, attention_ws_bytes(total_keys, q->H, q->T, n_segs));
+  return QWM_OK;
+}
+
+qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
+                         float scale, float* out, float* lse, int32_t* top1, void* ws, size_t ws_bytes,
+                         qwm_stream stream) {
+  qwm_status s = check_attention_common(q, scale, out, lse, top1);
   if (s != QWM_OK) return s;
-  return launch_attention(q, segs, n_segs, total_keys, scale, out, lse, top1, ws, static_cast<hipStream_t>(stream));
+  if (!segs || !aligned(segs, 8)) return fail(QWM_ERR_ARG, "segments: null or misaligned device array");
+  if (n_segs < 1 || n_segs > 4096) return fail(QWM_ERR_ARG, "n_segs must be in [1, 4096]");
+  if (total_keys < 1) return fail(QWM_ERR_ARG, "total_keys must be positive");
+  s = check_ws(ws, ws_bytes, attention_ws_bytes(total_keys, q->H, q->T, n_segs, false));
+  if (s != QWM_OK) return s;
+  return launch_attention(q, segs, n_segs, total_keys, nullptr, nullptr, scale, out, lse, top1, ws,
+                          static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
+                                const qwm_tokens* k_active, const qwm_tokens* v_active, float scale, float* out,
+                                float* lse, int32_t* top1, void* ws, size_t ws_bytes, qwm_stream stream) {
+  qwm_status s = check_attention_common(q, scale, out, lse, top1);
+  if (s != QWM_OK) return s;
+  if (n_segs < 0 || n_segs > 4096) return fail(QWM_ERR_ARG, "n_segs must be in [0, 4096]");
+  if (n_segs > 0 && (!segs || !aligned(segs, 8))) return fail(QWM_ERR_ARG, "segments: null or misaligned device array");
+  if (n_segs > 0 && total_keys < 1) return fail(QWM_ERR_ARG, "total_keys must be positive");
+  if (n_segs == 0 && total_keys != 0) return fail(QWM_ERR_ARG, "total_keys must be 0 without segments");
+  if ((s = check_tokens(k_active, "active keys", false)) != QWM_OK) return s;
+  if ((s = check_tokens(v_active, "active values", false)) != QWM_OK) return s;
+  if (k_active->dtype != QWM_BF16 || v_active->dtype != QWM_BF16)
+    return fail(QWM_ERR_UNSUPPORTED, "the active chunk must be bf16");
+  if (k_active->T != v_active->T || k_active->H != q->H || v_active->H != q->H)
+    return fail(QWM_ERR_ARG, "active chunk: K and V must share T, and H must match the queries");
+  if ((k_active->T > 1 && k_active->stride_t == 0) || (v_active->T > 1 && v_active->stride_t == 0))
+    return fail(QWM_ERR_ARG, "active chunk: zero token stride");
+  if (k_active->T * std::max<int64_t>(k_active->stride_t, qwm::D) >= ((int64_t)1 << 30) ||
+      v_active->T * std::max<int64_t>(v_active->stride_t, qwm::D) >= ((int64_t)1 << 30))
+    return fail(QWM_ERR_UNSUPPORTED, "active chunk: T * stride_t must stay below 2^30 elements");
+  s = check_ws(ws, ws_bytes, attention_ws_bytes(total_keys + k_active->T, q->H, q->T, n_segs, true));
+  if (s != QWM_OK) return s;
+  return launch_attention(q, segs, n_segs, total_keys, k_active, v_active, scale, out, lse, top1, ws,
+                          static_cast<hipStream_t>(stream));
 }
 
 qwm_status qwm_reference_top1(const qwm_tokens* q, const qwm_tokens* k, int32_t* top1, qwm_stream stream) {

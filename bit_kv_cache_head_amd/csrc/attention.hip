@@ -40,14 +40,20 @@ __device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const
 
 struct AttnArgs {
   const void* q; int32_t qdtype; int64_t Tq; int64_t qst; int64_t qsh;
-  const qwm_segment* segs; int32_t n_segs; int32_t nsplit;   // segs: device array
+  const qwm_segment* segs; int32_t n_segs; int32_t nsplit;   // segs: device array; nsplit: splits of its keys
   int32_t nqb; int32_t units;
+  // The active BF16 chunk, attended by the dense units: key t of head h is
+  // ka[t * kast + h * kash] (va alike), global key index kbase_a + t.  Units
+  // [0, units_p) are packed units, [units_p, units) dense ones (nsplit_a splits).
+  const uint16_t* ka; const uint16_t* va; int64_t kast, kash, vast, vash; int64_t Ta; int64_t kbase_a;
+  int32_t units_p; int32_t nsplit_a;
+  int32_t nparts;         // partial sets: nsplit (+ nsplit_a); one set means no partials
   float scale;
   const uint16_t* tabs;   // fp16 centroid tables [seg][H][2][256][128]: K (channel-permuted), V
   const uint16_t* ut;     // fp16 basis fragments [seg][H][R][8][2][8] (zero without PSAC), see attention_tables_kernel
-  // final outputs (nsplit == 1)
+  // final outputs (nparts == 1)
   float* out; float* lse; int32_t* top1; int32_t H;
-  // partial outputs (nsplit > 1): [split][H][Tq][D], [split][H][Tq] x (m, l), top value / index
+  // partial outputs (nparts > 1): [part][H][Tq][D], [part][H][Tq] x (m, l), top value / index
   float* po; float* pm; float* pl; float* ptv; int32_t* pti;
 };
 
@@ -239,8 +245,20 @@ __device__ Pos locate(const AttnArgs& a, int g, int lane) {
   return p;
 }
 
+// Keys of segment s; a dense unit's only segment is the active chunk.
+template <bool DENSE>
+__device__ __forceinline__ int64_t seg_T(const AttnArgs& a, int s) {
+  if constexpr (DENSE) return a.Ta;
+  else return seg_at(a, s).T;
+}
+
 // The next tile (the caller knows one exists); T = keys of p's segment.
+template <bool DENSE>
 __device__ __forceinline__ Pos advance(const AttnArgs& a, Pos p, int64_t T) {
+  if constexpr (DENSE) {
+    p.tile += 1;
+    return p;
+  }
   p.tile += 1;
   while ((int64_t)p.tile * AT_K >= T && p.seg + 1 < a.n_segs) {
     p.kbase += T;
@@ -364,17 +382,34 @@ __device__ __forceinline__ SegDesc seg_desc(const AttnArgs& a, int s, int h) {
   return d;
 }
 
+// A dense unit's descriptor: no packed arrays (every load of them reads 0).
+__device__ __forceinline__ SegDesc dense_desc(const AttnArgs& a) {
+  SegDesc d{};
+  d.T = (int)a.Ta;
+  d.cT = 0;
+  return d;
+}
+template <bool DENSE>
+__device__ __forceinline__ SegDesc desc_for(const AttnArgs& a, int s, int h) {
+  if constexpr (DENSE) return dense_desc(a);
+  else return seg_desc(a, s, h);
+}
+
+template <bool DENSE>
 __device__ __forceinline__ void load_idx(const SegDesc& d, const Pos& P, const Lane& L, TileIdx& x) {
   const int k0 = P.tile * AT_K;
-  const rsrc_t ki = buf(d.ki, d.T), vi = buf(d.vi, d.T);
+  const int pT = DENSE ? 0 : d.T;
+  const rsrc_t ki = buf(d.ki, pT), vi = buf(d.vi, pT);
   x.k = ld8b(ki, L.key, k0);
   x.v0 = ld8b(vi, 2 * L.p, k0);
   x.v1 = ld8b(vi, 2 * L.p + 1, k0);
 }
 
-// The packed bytes of a tile (codes, scales, zero-points, PSAC bytes).
+// The packed bytes of a tile (codes, scales, zero-points, PSAC bytes); for
+// a dense unit all zeros, so its tiles dequantize to the rows themselves.
+template <bool DENSE>
 __device__ __forceinline__ void load_bytes(const SegDesc& d, const Pos& P, const Lane& L, TileRegs& r) {
-  const int k0 = P.tile * AT_K, T = d.T;
+  const int k0 = P.tile * AT_K, T = DENSE ? 0 : d.T;
   {
     const int g = L.blk >> 2;
     r.kcode = ld32(buf(d.kc, T * 32), L.key * 32 + 4 * L.blk, k0 * 32);
@@ -394,9 +429,23 @@ __device__ __forceinline__ void load_bytes(const SegDesc& d, const Pos& P, const
   }
 }
 
-// The fp16 centroid rows of a tile's keys (segment seg), from its indices.
-__device__ __forceinline__ void load_mu(const AttnArgs& a, int seg, int h, const Lane& L, const TileIdx& x,
-                                        TileRegs& r) {
+// The fp16 centroid rows of a tile's keys (segment seg), from its indices;
+// for a dense unit the keys' own bf16 rows (rows_to_f16 converts them once
+// they have arrived).  Rows past the end read as zeros.
+template <bool DENSE>
+__device__ __forceinline__ void load_mu(const AttnArgs& a, int seg, int tile, int h, const Lane& L,
+                                        const TileIdx& x, TileRegs& r) {
+  if constexpr (DENSE) {
+    const int k0 = tile * AT_K, T = (int)a.Ta;
+    const int kst = (int)a.kast * 2, vst = (int)a.vast * 2;   // bytes
+    const rsrc_t kb = buf(a.ka + h * a.kash, T * kst);
+    const rsrc_t vb = buf(a.va + h * a.vash, T * vst);
+    r.kmu[0] = ld128(kb, L.key * kst + 32 * L.blk, k0 * kst);
+    r.kmu[1] = ld128(kb, L.key * kst + 32 * L.blk + 16, k0 * kst);
+    r.vmu[0] = ld128(vb, (2 * L.p) * vst + 16 * L.oct, k0 * vst);
+    r.vmu[1] = ld128(vb, (2 * L.p + 1) * vst + 16 * L.oct, k0 * vst);
+    return;
+  }
   const uint16_t* ktab = a.tabs + ((int64_t)(seg * a.H + h) * 2) * TAB_ELEMS;
   const rsrc_t kt = buf(ktab, TAB_ELEMS * 2);
   const int mo = (int)(x.k * (D * 2)) + 32 * L.blk;
@@ -405,6 +454,25 @@ __device__ __forceinline__ void load_mu(const AttnArgs& a, int seg, int h, const
   const rsrc_t vt = buf(ktab + TAB_ELEMS, TAB_ELEMS * 2);
   r.vmu[0] = ld128(vt, (int)(x.v0 * (D * 2)) + 16 * L.oct);
   r.vmu[1] = ld128(vt, (int)(x.v1 * (D * 2)) + 16 * L.oct);
+}
+
+// Dense rows, as load_mu leaves them, into the fp16 layout of the centroid
+// rows: K channels 16 blk + m and 16 blk + m + 8 in word m (the K tables'
+// permuted order), V channels in order.  bf16 -> fp16 is exact within fp16's
+// range.
+__device__ __forceinline__ void rows_to_f16(TileRegs& r) {
+  const u32x4 a = r.kmu[0], b = r.kmu[1];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const uint32_t lo = (m & 1) ? (a[m >> 1] & 0xFFFF0000u) : (a[m >> 1] << 16);
+    const uint32_t hi = (m & 1) ? (b[m >> 1] & 0xFFFF0000u) : (b[m >> 1] << 16);
+    r.kmu[m >> 2][m & 3] = pack_f16x2(__uint_as_float(lo), __uint_as_float(hi));
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      r.vmu[k][e] = pack_f16x2(__uint_as_float(r.vmu[k][e] << 16), __uint_as_float(r.vmu[k][e] & 0xFFFF0000u));
 }
 
 // Copy the packed-byte fields (the centroid rows are loaded separately).
@@ -546,18 +614,13 @@ __device__ __forceinline__ uint32_t pair_other(uint32_t v, int hh) {
   return hh ? s[0] : s[1];
 }
 
-template <bool TOP1>
-__global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
-  __shared__ AttnBuf sb[2];
+// One unit: 256 Queries (query block qb) x head h x split `split` of nsplit
+// of a key sequence, written to partial set `part`.  DENSE: the key sequence
+// is the active BF16 chunk; otherwise the packed segments.
+template <bool TOP1, bool DENSE>
+__device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf* sb, int qb, int split, int nsplit,
+                                               int part, int h) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hh = lane >> 5, ln = lane & 31;
-  // XCD-aware unit mapping: consecutive units (same head) go to the same XCD
-  const int nb = (int)gridDim.x;
-  const int per = (nb + 7) / 8;
-  const int unit = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-  if (unit >= a.units) return;
-  const int qb = unit % a.nqb;
-  const int split = (unit / a.nqb) % a.nsplit;
-  const int h = unit / (a.nqb * a.nsplit);
   const int64_t qw0 = (int64_t)qb * AT_Q + wv * AT_QW;
   const bool wave_active = qw0 < a.Tq;
   const int64_t qi = qw0 + ln;
@@ -599,12 +662,12 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   for (int c = 0; c < 4; ++c) o_acc[c] = f32x16{};
 
   // this split's share of the tile sequence
-  const int total = count_tiles(a, lane);
-  const int g0 = (int)((int64_t)total * split / a.nsplit);
-  const int count = (int)((int64_t)total * (split + 1) / a.nsplit) - g0;
+  const int total = DENSE ? ntiles(a.Ta) : count_tiles(a, lane);
+  const int g0 = (int)((int64_t)total * split / nsplit);
+  const int count = (int)((int64_t)total * (split + 1) / nsplit) - g0;
   if (count <= 0) {
-    if (qvalid && a.nsplit > 1 && hh == 0) {
-      const int64_t pidx = ((int64_t)split * a.H + h) * a.Tq + qi;
+    if (qvalid && a.nparts > 1 && hh == 0) {
+      const int64_t pidx = ((int64_t)part * a.H + h) * a.Tq + qi;
       a.pm[pidx] = -__builtin_inff(); a.pl[pidx] = 0.f;
       if (TOP1) { a.ptv[pidx] = best_v; a.pti[pidx] = best_i; }
     }
@@ -612,16 +675,18 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   }
   // positions of tiles n, n + 1, n + 2, n + 3 of the split (past the end a
   // position repeats the last tile, so every stage loads memory that exists)
-  Pos P0 = locate(a, g0, lane);
-  Pos P1 = count > 1 ? advance(a, P0, seg_at(a, P0.seg).T) : P0;
-  Pos P2 = count > 2 ? advance(a, P1, seg_at(a, P1.seg).T) : P1;
-  Pos P3 = count > 3 ? advance(a, P2, seg_at(a, P2.seg).T) : P2;
+  Pos P0;
+  if constexpr (DENSE) { P0.seg = 0; P0.tile = g0; P0.kbase = a.kbase_a; }
+  else P0 = locate(a, g0, lane);
+  Pos P1 = count > 1 ? advance<DENSE>(a, P0, seg_T<DENSE>(a, P0.seg)) : P0;
+  Pos P2 = count > 2 ? advance<DENSE>(a, P1, seg_T<DENSE>(a, P1.seg)) : P1;
+  Pos P3 = count > 3 ? advance<DENSE>(a, P2, seg_T<DENSE>(a, P2.seg)) : P2;
   // Load stages of tile t: packed bytes and indices three tiles ahead (HBM
   // latency), centroid rows two tiles ahead (from the indices), dequantization
   // one tile ahead.  Segment fields: T of tiles n .. n + 2, the arrays of
   // tile n + 3's segment.
-  int64_t T0 = seg_at(a, P0.seg).T, T1 = seg_at(a, P1.seg).T, T2 = seg_at(a, P2.seg).T;
-  SegDesc sd = seg_desc(a, P3.seg, h);
+  int64_t T0 = seg_T<DENSE>(a, P0.seg), T1 = seg_T<DENSE>(a, P1.seg), T2 = seg_T<DENSE>(a, P2.seg);
+  SegDesc sd = desc_for<DENSE>(a, P3.seg, h);
 
   // pipeline fill: tile 0 dequantized, tile 1 complete in registers, tile 2's
   // bytes and indices in flight
@@ -629,18 +694,19 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   TileRegs regs, nbytes;
   TileIdx tix;
   {
-    const SegDesc d0 = seg_desc(a, P0.seg, h);
-    load_idx(d0, P0, L, tix);
-    load_bytes(d0, P0, L, regs);
-    load_mu(a, P0.seg, h, L, tix, regs);
+    const SegDesc d0 = desc_for<DENSE>(a, P0.seg, h);
+    load_idx<DENSE>(d0, P0, L, tix);
+    load_bytes<DENSE>(d0, P0, L, regs);
+    load_mu<DENSE>(a, P0.seg, P0.tile, h, L, tix, regs);
+    if constexpr (DENSE) rows_to_f16(regs);
     dequant_tile(regs, L, cm, sb[0]);
-    const SegDesc d1 = seg_desc(a, P1.seg, h);
-    load_idx(d1, P1, L, tix);
-    load_bytes(d1, P1, L, regs);
-    load_mu(a, P1.seg, h, L, tix, regs);
-    const SegDesc d2 = seg_desc(a, P2.seg, h);
-    load_idx(d2, P2, L, tix);
-    load_bytes(d2, P2, L, nbytes);
+    const SegDesc d1 = desc_for<DENSE>(a, P1.seg, h);
+    load_idx<DENSE>(d1, P1, L, tix);
+    load_bytes<DENSE>(d1, P1, L, regs);
+    load_mu<DENSE>(a, P1.seg, P1.tile, h, L, tix, regs);
+    const SegDesc d2 = desc_for<DENSE>(a, P2.seg, h);
+    load_idx<DENSE>(d2, P2, L, tix);
+    load_bytes<DENSE>(d2, P2, L, nbytes);
   }
   __syncthreads();
 
@@ -649,7 +715,7 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   f16x8 qpf = __builtin_bit_cast(f16x8, u32x4{0, 0, 0, 0});
   const h2 ones = as_h2(0x3C003C00u);
   for (int n = 0; n < count; ++n) {
-    if (P0.seg != qp_seg) {
+    if (!DENSE && P0.seg != qp_seg) {
       // Q U for this segment: (U^T) (Q^T) on MFMA with the Query fragments as
       // B; the basis fragments come from the workspace (zeros without PSAC;
       // rows n >= R read as zeros, past the end of their buffer)
@@ -684,13 +750,14 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
     //      Past the end of the split the stages repeat the last tile (into a
     //      buffer nobody reads), so that no load is conditional.
     f32x16 sa = {}, sb2 = {};
+    if constexpr (DENSE) rows_to_f16(regs);
     tile_phase1(&sb[cur], &sb[cur ^ 1], qf, qpf, ln, hh, regs, L, cm, sa, sb2);
     // tile n + 2: its bytes arrived during the previous iteration; fetch its
     // centroid rows.  Tile n + 3: bytes and indices.
     take_bytes(regs, nbytes);
-    load_mu(a, P2.seg, h, L, tix, regs);
-    load_bytes(sd, P3, L, nbytes);
-    load_idx(sd, P3, L, tix);
+    load_mu<DENSE>(a, P2.seg, P2.tile, h, L, tix, regs);
+    load_bytes<DENSE>(sd, P3, L, nbytes);
+    load_idx<DENSE>(sd, P3, L, tix);
 
     if (wave_active) {
       // ---- keys past the segment end (their rows hold centroid 0) ----
@@ -774,8 +841,8 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
     P1 = P2; T1 = T2;
     P2 = P3; T2 = sd.T;
     if (n + 4 < count) {
-      P3 = advance(a, P3, sd.T);
-      if (P3.seg != P2.seg) sd = seg_desc(a, P3.seg, h);
+      P3 = advance<DENSE>(a, P3, sd.T);
+      if (!DENSE && P3.seg != P2.seg) sd = desc_for<DENSE>(a, P3.seg, h);
     }
     cur ^= 1;
   }
@@ -788,7 +855,7 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
     if (ov > best_v || (ov == best_v && oi < best_i)) { best_v = ov; best_i = oi; }
   }
   if (!qvalid) return;
-  if (a.nsplit == 1) {
+  if (a.nparts == 1) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     float* orow = a.out + (qi * a.H + h) * D;
 #pragma unroll
@@ -804,7 +871,7 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
       if (TOP1 && a.top1) a.top1[(int64_t)h * a.Tq + qi] = best_i;
     }
   } else {
-    const int64_t pidx = ((int64_t)split * a.H + h) * a.Tq + qi;
+    const int64_t pidx = ((int64_t)part * a.H + h) * a.Tq + qi;
     float* orow = a.po + pidx * D;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -821,6 +888,24 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   }
 }
 
+template <bool TOP1>
+__global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
+  __shared__ AttnBuf sb[2];
+  // XCD-aware unit mapping: consecutive units (same head) go to the same XCD
+  const int nb = (int)gridDim.x;
+  const int per = (nb + 7) / 8;
+  const int unit = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (unit >= a.units) return;
+  if (unit < a.units_p) {
+    const int qb = unit % a.nqb, split = (unit / a.nqb) % a.nsplit, h = unit / (a.nqb * a.nsplit);
+    attention_body<TOP1, false>(a, sb, qb, split, a.nsplit, split, h);
+  } else {
+    const int u = unit - a.units_p;
+    const int qb = u % a.nqb, split = (u / a.nqb) % a.nsplit_a, h = u / (a.nqb * a.nsplit_a);
+    attention_body<TOP1, true>(a, sb, qb, split, a.nsplit_a, a.nsplit + split, h);
+  }
+}
+
 // Merge split partials.  Grid (ceil(Tq/2), H), 256 threads: two queries per block.
 template <bool TOP1>
 __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
@@ -828,11 +913,11 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
   const int64_t qi = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
   if (qi >= a.Tq) return;
   float mx = -__builtin_inff();
-  for (int p = 0; p < a.nsplit; ++p) mx = fmaxf(mx, a.pm[((int64_t)p * a.H + h) * a.Tq + qi]);
+  for (int p = 0; p < a.nparts; ++p) mx = fmaxf(mx, a.pm[((int64_t)p * a.H + h) * a.Tq + qi]);
   float l = 0.f, o = 0.f;
   float bv = -__builtin_inff();
   int32_t bi = 0x7FFFFFFF;
-  for (int p = 0; p < a.nsplit; ++p) {
+  for (int p = 0; p < a.nparts; ++p) {
     const int64_t pidx = ((int64_t)p * a.H + h) * a.Tq + qi;
     const float pm = a.pm[pidx];
     const float wgt = (pm == -__builtin_inff()) ? 0.f : exp2f(pm - mx);
@@ -875,10 +960,34 @@ static int attention_splits(int64_t Tq, int32_t H, int64_t total_keys) {
 
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs) {
+// Split plan: the key sequence (packed keys, then the active chunk's) gets
+// attention_splits() splits in all, shared between the two in proportion to
+// their keys (each present part at least one); partial sets = splits.
+struct AttnPlan { int nsplit, nsplit_a, nparts; };
+static AttnPlan attention_plan(int64_t Tq, int32_t H, int64_t packed_keys, int64_t active_keys) {
+  const int P = attention_splits(Tq, H, packed_keys + active_keys);
+  AttnPlan p{P, 0, P};
+  if (active_keys > 0) {
+    if (packed_keys == 0) {
+      p.nsplit = 0;
+      p.nsplit_a = P;
+    } else {
+      p.nsplit_a = (int)((P * active_keys + (packed_keys + active_keys) / 2) / (packed_keys + active_keys));
+      if (p.nsplit_a < 1) p.nsplit_a = 1;
+      p.nsplit = P - p.nsplit_a;
+      if (p.nsplit < 1) p.nsplit = 1;
+    }
+    p.nparts = p.nsplit + p.nsplit_a;
+  }
+  return p;
+}
+
+// Workspace for n_segs packed segments and up to (splits + 1) partial sets;
+// total_keys counts every key (packed and active).
+size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs, bool active) {
   size_t bytes = al256((size_t)n_segs * H * 2 * TAB_ELEMS * sizeof(uint16_t)) +
                  al256((size_t)n_segs * H * R * D * sizeof(uint16_t));
-  const int ns = attention_splits(Tq, H, total_keys);
+  const int ns = attention_splits(Tq, H, total_keys) + (active ? 1 : 0);
   if (ns > 1) {
     const size_t n = (size_t)ns * H * Tq;
     bytes += al256(n * D * 4) + 4 * al256(n * 4);
@@ -887,36 +996,48 @@ size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_s
 }
 
 qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
-                            float scale, float* out, float* lse, int32_t* top1, void* ws, hipStream_t stream) {
+                            const qwm_tokens* ka, const qwm_tokens* va, float scale, float* out, float* lse,
+                            int32_t* top1, void* ws, hipStream_t stream) {
   AttnArgs a{};
   a.q = q->ptr; a.qdtype = q->dtype; a.Tq = q->T; a.qst = q->stride_t; a.qsh = q->stride_h;
   a.segs = segs; a.n_segs = n_segs; a.scale = scale; a.out = out; a.lse = lse; a.top1 = top1; a.H = q->H;
-  a.nsplit = attention_splits(q->T, q->H, total_keys);
+  const int64_t Ta = ka ? ka->T : 0;
+  const AttnPlan plan = attention_plan(q->T, q->H, n_segs > 0 ? total_keys : 0, Ta);
+  a.nsplit = plan.nsplit; a.nsplit_a = plan.nsplit_a; a.nparts = plan.nparts;
   a.nqb = (int32_t)((q->T + AT_Q - 1) / AT_Q);
-  a.units = a.nqb * a.nsplit * q->H;
+  a.units_p = a.nqb * a.nsplit * q->H;
+  a.units = a.units_p + a.nqb * a.nsplit_a * q->H;
+  if (ka) {
+    a.ka = static_cast<const uint16_t*>(ka->ptr); a.kast = ka->stride_t; a.kash = ka->stride_h;
+    a.va = static_cast<const uint16_t*>(va->ptr); a.vast = va->stride_t; a.vash = va->stride_h;
+    a.Ta = Ta; a.kbase_a = n_segs > 0 ? total_keys : 0;
+  }
   char* p = static_cast<char*>(ws);
   a.tabs = reinterpret_cast<uint16_t*>(p);
   p += al256((size_t)n_segs * q->H * 2 * TAB_ELEMS * sizeof(uint16_t));
   a.ut = reinterpret_cast<uint16_t*>(p);
   p += al256((size_t)n_segs * q->H * R * D * sizeof(uint16_t));
-  if (a.nsplit > 1) {
-    const size_t n = (size_t)a.nsplit * q->H * q->T;
+  if (a.nparts > 1) {
+    const size_t n = (size_t)a.nparts * q->H * q->T;
     a.po = reinterpret_cast<float*>(p); p += al256(n * D * 4);
     a.pm = reinterpret_cast<float*>(p); p += al256(n * 4);
     a.pl = reinterpret_cast<float*>(p); p += al256(n * 4);
     a.ptv = reinterpret_cast<float*>(p); p += al256(n * 4);
     a.pti = reinterpret_cast<int32_t*>(p);
   }
-  hipLaunchKernelGGL(attention_tables_kernel, dim3((unsigned)(n_segs * q->H), D / 16), dim3(NC), 0, stream, segs, q->H,
-                     const_cast<uint16_t*>(a.tabs), const_cast<uint16_t*>(a.ut));
-  qwm_status s = check_launch("attention tables");
-  if (s != QWM_OK) return s;
+  qwm_status s;
+  if (n_segs > 0) {
+    hipLaunchKernelGGL(attention_tables_kernel, dim3((unsigned)(n_segs * q->H), D / 16), dim3(NC), 0, stream, segs,
+                       q->H, const_cast<uint16_t*>(a.tabs), const_cast<uint16_t*>(a.ut));
+    s = check_launch("attention tables");
+    if (s != QWM_OK) return s;
+  }
   const int per = (a.units + 7) / 8;
   const dim3 grid((unsigned)(per * 8));
   if (top1) hipLaunchKernelGGL(attention_kernel<true>, grid, dim3(AT_T), 0, stream, a);
   else hipLaunchKernelGGL(attention_kernel<false>, grid, dim3(AT_T), 0, stream, a);
   s = check_launch("attention");
-  if (s != QWM_OK || a.nsplit == 1) return s;
+  if (s != QWM_OK || a.nparts == 1) return s;
   const dim3 g2((unsigned)((q->T + 1) / 2), (unsigned)q->H);
   if (top1) hipLaunchKernelGGL(attention_combine_kernel<true>, g2, dim3(256), 0, stream, a);
   else hipLaunchKernelGGL(attention_combine_kernel<false>, g2, dim3(256), 0, stream, a);

@@ -1032,9 +1032,10 @@ __global__ __launch_bounds__(256) void lloyd_sum_kernel(const void* x, int32_t d
                                                         int64_t sh, int32_t H, const int32_t* ids,
                                                         const int32_t* start, const uint16_t* cin, uint16_t* cout) {
   const int lane = threadIdx.x & 63;
-  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (unit >= (int64_t)H * NC) return;
-  const int h = (int)(unit / NC), j = (int)(unit % NC);
+  // wave-uniform unit: the member ids then come in through scalar loads
+  const int unit = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
+  if (unit >= H * NC) return;
+  const int h = unit / NC, j = unit % NC;
   const int32_t b = start[h * (NC + 1) + j], n = start[h * (NC + 1) + j + 1] - b;
   const int32_t* mem = ids + (int64_t)h * T + b;
   const int64_t rowbase = (int64_t)h * sh + 2 * lane;
@@ -1043,10 +1044,20 @@ __global__ __launch_bounds__(256) void lloyd_sum_kernel(const void* x, int32_t d
   int e = 0;
   if (dtype == QWM_BF16) {
     const uint16_t* xb = static_cast<const uint16_t*>(x) + rowbase;
+    int32_t id[U];
+    if (n >= U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) id[u] = mem[u];
+    }
     for (; e + U <= n; e += U) {
       uint32_t v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const uint32_t*>(xb + (int64_t)mem[e + u] * st);
+      for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const uint32_t*>(xb + (int64_t)id[u] * st);
+      // the next batch's ids while these rows are in flight
+      if (e + 2 * U <= n) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) id[u] = mem[e + U + u];
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         s0 += (double)__uint_as_float(v[u] << 16);

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define QWM_ABI_VERSION 2
+#define QWM_ABI_VERSION 3
 #define QWM_HEAD_DIM 128
 #define QWM_GROUP 64
 #define QWM_CENTROIDS 256
@@ -64,7 +64,7 @@ enum { QWM_QSAC = 1u, QWM_PSAC = 2u };
 
 /* Workspace-sizing operation ids for qwm_workspace_bytes(). */
 enum { QWM_OP_STATS = 0, QWM_OP_CENTROIDS = 1, QWM_OP_KEYS = 2, QWM_OP_VALUES = 3,
-       QWM_OP_ATTENTION = 4 };
+       QWM_OP_ATTENTION = 4, QWM_OP_ATTENTION_ACTIVE = 5 };
 
 typedef void* qwm_stream; /* hipStream_t */
 
@@ -185,6 +185,21 @@ qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n
                          int64_t total_keys, float scale, float* out, float* lse, int32_t* top1,
                          void* ws, size_t ws_bytes, qwm_stream stream);
 
+/* qwm_attention over the packed segments plus the active chunk, which stays
+ * BF16 until it completes (QuantWM App. D.1: completed chunks are packed, the
+ * active one is kept as it is).  k_active, v_active: [Ta][H][d] bf16 token
+ * descriptors (Ta >= 1, H equal to the queries', rows 16-byte aligned,
+ * Ta * stride_t < 2^30 elements); row values must lie in fp16's range (the
+ * kernel's tiles are fp16 MFMA operands).  n_segs may be 0 (then segs may be
+ * NULL and total_keys must be 0).  Keys are numbered packed segments first,
+ * then the active chunk (index total_keys + t), for top1.  The active chunk
+ * runs on its own key splits in the same launch; the log-sum-exp merge joins
+ * them.  Workspace: QWM_OP_ATTENTION_ACTIVE with T = total_keys + Ta, n = Tq
+ * and n_segs. */
+qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
+                                const qwm_tokens* k_active, const qwm_tokens* v_active, float scale, float* out,
+                                float* lse, int32_t* top1, void* ws, size_t ws_bytes, qwm_stream stream);
+
 /* Top-1 key of every Query over unquantized keys, the reference side of the
  * token-shift metric (QuantWM v2 Sec. 5.3: how often the key a Query attends
  * to most differs between the quantized cache and BF16).
@@ -198,8 +213,9 @@ qwm_status qwm_reference_top1(const qwm_tokens* q, const qwm_tokens* k, int32_t*
  * QWM_OP_ATTENTION: T = total cached keys, n = number of queries, n_segs =
  * number of segments.  The workspace holds fp16 copies of every segment's
  * centroid tables (n_segs * H * 128 KiB), every segment's U_r as fp16 MFMA
- * fragments (n_segs * H * 2 KiB) and the split-key partials.  The other
- * operations ignore n and n_segs. */
+ * fragments (n_segs * H * 2 KiB) and the split-key partials.
+ * QWM_OP_ATTENTION_ACTIVE: the same with T = all keys (packed + active) and
+ * one more partial set.  The other operations ignore n and n_segs. */
 size_t qwm_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t n, int32_t n_segs);
 
 /* Row stride of the zeros array for a chunk of T tokens. */

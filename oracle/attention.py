@@ -38,7 +38,13 @@ def softmax_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float)
 def segment_kv(seg: dict):
     """Dequantize one cached chunk of one head.  seg holds the per-head arrays:
     k_idx, k_q, k_scale, k_zero, k_Cq, k_cs, k_centroids, U (or None),
-    v_idx, v_q, v_scale, v_zero, v_centroids."""
+    v_idx, v_q, v_scale, v_zero, v_centroids.
+
+    A BF16 chunk (the active chunk, kept unquantized until it completes:
+    QuantWM App. D.1) holds k_bf16 and v_bf16 instead, [T][d] arrays of its
+    bf16 values; attention reads them as they are."""
+    if "k_bf16" in seg:
+        return np.asarray(seg["k_bf16"], np.float64), np.asarray(seg["v_bf16"], np.float64)
     K = dequant_keys(seg["k_idx"], seg["k_q"], seg["k_scale"], seg["k_zero"],
                      seg["k_Cq"], seg["k_cs"], seg["k_centroids"], seg.get("U"))
     V = dequant_values(seg["v_idx"], seg["v_q"], seg["v_scale"], seg["v_zero"],

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert sorted(_abi.EXPORTS) == declared
     for name in declared:
         assert hasattr(_abi.lib, name), name
-    assert _abi.lib.qwm_abi_version() == 2
+    assert _abi.lib.qwm_abi_version() == 3
 
 
 def test_struct_layouts_match_header_sizes():

@@ -338,6 +338,52 @@ def test_attention_on_oracle_cache(qwm, want_top1, sizes):
             _check_top1(top1.cpu().numpy()[h], top, Qv[:, h], segs, h)
 
 
+@pytest.mark.parametrize("sizes,active", [([300, 257], 173), ([64], 1), ([], 130), ([], 1), ([130, 1], 64)])
+def test_attention_with_bf16_active_chunk(qwm, sizes, active):
+    """Packed chunks plus the BF16 active chunk (QuantWM App. D.1): the active
+    chunk's K/V are strided [T, H, 128] views of the token arrays, its length
+    ragged against the 64-key tile; with no packed chunk at all as well."""
+    import torch
+    from gpu_helpers import dev_tokens
+    _log(f"attention with a BF16 active chunk: packed {sizes}, active {active}")
+    w = datagen.make_workload("480p", heads=[0, 1], n_chunks=1, chunk=sum(sizes) + active + 256)
+    segs = _oracle_segments(w, sizes, [0, 1]) if sizes else []
+    dseg, total, keep = _upload_segments(qwm, segs, 2) if sizes else (None, 0, [])
+    pos = sum(sizes)
+    assert total == pos
+    Kall = dev_tokens(w.K, "bf16")
+    Vall = dev_tokens(w.V, "bf16")
+    Kact, Vact = Kall[pos:pos + active], Vall[pos:pos + active]    # views: stride_t = H * 128
+    Qv = w.Q[-200:]
+    out, lse, top1 = qwm.attention(dev_tokens(Qv, "bf16"), dseg, len(sizes), total, want_lse=True, want_top1=True,
+                                   active=(Kact, Vact))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for h in range(2):
+        osegs = [s[h]["oracle"] for s in segs] + [dict(k_bf16=w.K[pos:pos + active, h].astype(np.float64),
+                                                       v_bf16=w.V[pos:pos + active, h].astype(np.float64))]
+        O, L, top = OA.cache_attention(Qv[:, h].astype(np.float64), osegs, 1 / np.sqrt(128))
+        err = np.linalg.norm(out[:, h] - O) / np.linalg.norm(O)
+        Kcat = np.concatenate([OA.segment_kv(sg)[0] for sg in osegs])
+        # LSE is 1-Lipschitz in the max-norm of the logits.  The kernel's logits
+        # use fp16 K0_hat (one RNE rounding, <= 2^-11 relative per element) and
+        # the fp16 PSAC product; its sum uses fp16 probabilities rounded toward
+        # zero (< 2^-10 relative each).  Bound per Query: scale * 2^-10 *
+        # max_j sum_c |q_c k_jc| (the K0_hat term, doubled for the PSAC and fp32
+        # terms) + 2^-9.
+        qa = np.abs(Qv[:, h].astype(np.float64))
+        tol = (1 / np.sqrt(128)) * 2.0 ** -10 * np.max(qa @ np.abs(Kcat).T, axis=1) + 2.0 ** -9
+        lerr = np.abs(lse.cpu().numpy()[h] - L)
+        _log(f"  head {h}: rel L2 {err:.2e}, max |lse error| {lerr.max():.2e} (bound >= {tol.min():.2e})")
+        assert err <= 2e-3
+        assert np.all(lerr <= tol)
+        Lg = Qv[:, h].astype(np.float64) @ Kcat.T
+        gt = top1.cpu().numpy()[h]
+        for i in np.nonzero(gt != top)[0]:
+            a, b = Lg[i, top[i]], Lg[i, gt[i]]
+            assert abs(a - b) <= 1e-3 * abs(a), (i, a, b)
+
+
 def _check_top1(gt, ot, Qh, segs, h):
     """Top-1 agrees except where the oracle's top-2 logit gap is < 1e-3 relative."""
     Ks = [OA.segment_kv(s[h]["oracle"])[0] for s in segs]

@@ -102,3 +102,35 @@ def test_cache_attention_is_attention_on_dequantized_segments():
     # the quantized cache stays close to the bf16 attention
     Oref, _, topref = A.softmax_attention(Q[sl], K, V, 1 / np.sqrt(128))
     assert np.linalg.norm(O - Oref) / np.linalg.norm(Oref) < 0.2
+
+
+def test_bf16_active_chunk_segment():
+    """A BF16 segment (the active chunk, QuantWM App. D.1) is read as its raw
+    values.  Pins: (1) attention over [packed, BF16] is the log-sum-exp merge
+    of the attentions over each part alone (softmax over a union of key sets);
+    (2) a BF16 segment that holds a packed segment's reconstruction attends
+    exactly like the packed segment."""
+    w = datagen.make_workload("480p", heads=[0], n_chunks=2, chunk=300)
+    K, V, Q = (w.K[:, 0].astype(np.float64), w.V[:, 0].astype(np.float64),
+               w.Q[:, 0].astype(np.float64))
+    sl0, sl1 = w.chunk_slice(0), w.chunk_slice(1)
+    Ck = lloyd.lloyd(K[sl0], 256, 2, seed=11)
+    Cv = lloyd.lloyd(V[sl0], 256, 2, seed=12)
+    kq = Qz.quantize_keys(K[sl0], Ck, None, None, M=8)
+    vq = Qz.quantize_values(V[sl0], Cv)
+    packed = dict(k_idx=kq["idx"], k_q=kq["q"], k_scale=kq["scale"], k_zero=kq["zero"], k_Cq=kq["Cq"],
+                  k_cs=kq["c_scale"], k_centroids=Ck, U=None, v_idx=vq["idx"], v_q=vq["q"],
+                  v_scale=vq["scale"], v_zero=vq["zero"], v_centroids=Cv)
+    active = dict(k_bf16=K[sl1], v_bf16=V[sl1])
+    sc = 1 / np.sqrt(128)
+    O, lse, top = A.cache_attention(Q[sl1], [packed, active], sc)
+    Oa, la, ta = A.cache_attention(Q[sl1], [packed], sc)
+    Ob, lb, tb = A.cache_attention(Q[sl1], [active], sc)
+    m = np.maximum(la, lb)
+    wa, wb = np.exp(la - m), np.exp(lb - m)
+    merged = (wa[:, None] * Oa + wb[:, None] * Ob) / (wa + wb)[:, None]
+    assert np.max(np.abs(O - merged)) <= 1e-12 * np.max(np.abs(O))
+    np.testing.assert_allclose(lse, m + np.log(wa + wb), rtol=0, atol=1e-12)
+    Kd, Vd = A.segment_kv(packed)
+    O2, lse2, top2 = A.cache_attention(Q[sl1], [dict(k_bf16=Kd, v_bf16=Vd), active], sc)
+    assert np.array_equal(O, O2) and np.array_equal(top, top2)
