@@ -307,6 +307,44 @@ def keys_bulk(qwm, torch, Kall, table, st):
             "GBps": round(byts / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def decode_ab(qwm, torch, step, fused_ms):
+    """The pages' read path for comparison: decode every packed chunk to BF16
+    (K_hat with PSAC, V_hat), then dense attention over the decoded rows, against
+    the fused dequantizing attention timed in the step."""
+    H, total = step.H, step.total
+    Kd = torch.empty(total, H, D, dtype=torch.bfloat16, device="cuda")
+    Vd = torch.empty_like(Kd)
+    Q = step.Q[step.sl_new]
+
+    def decode_all():
+        pos = 0
+        for (kp, vp, kc, vc, U) in step.segs:
+            qwm.decode_segment(kp, vp, kc, vc, U, Kd[pos:pos + kp.T], Vd[pos:pos + kp.T])
+            pos += kp.T
+
+    def dense():
+        qwm.attention(Q, None, 0, 0, active=(Kd, Vd))
+
+    for f in (decode_all, dense):
+        f()
+    torch.cuda.synchronize()
+    res = {}
+    for name, f in (("decode_ms", decode_all), ("dense_attention_ms", dense)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / 5, 4)
+    res["decode_plus_dense_ms"] = round(res["decode_ms"] + res["dense_attention_ms"], 4)
+    res["fused_ms"] = round(fused_ms, 4)
+    res["decoded_bytes"] = int(2 * total * H * D * 2)
+    res["note"] = ("decoder: every chunk's BF16 K_hat (PSAC included) and V_hat written to HBM, then the same "
+                   "attention kernel reads them as one BF16 chunk; fused: dequantization into LDS inside attention")
+    return res
+
+
 def timed_steps(step, torch, steps, warmup):
     import numpy as np
     for _ in range(warmup):
@@ -385,6 +423,7 @@ def run_stream_or_pass(args, qwm, torch, w):
         res["keys_step"] = {"token_heads": step.chunk * step.H,
                             "ms_incl_stats_wait": round(stage["keys_incl_stats_wait"], 4)}
         res["keys_bulk"] = keys_bulk(qwm, torch, step.K[: (step.nch - 1) * step.chunk], step.prev[0], step.st)
+        res["decode_ab"] = decode_ab(qwm, torch, step, stage["attention"])
     else:
         res["keys_bulk"] = keys_bulk(qwm, torch, step.K, step.Ck, step.st)
     res["wall_s_timed"] = round(wall, 3)

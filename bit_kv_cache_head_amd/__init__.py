@@ -167,6 +167,38 @@ def quantize_values(v: torch.Tensor, centroids: torch.Tensor, out: PackedChunk |
     return out
 
 
+def _segment(kp, vp, kc, vc, U) -> Segment:
+    s = Segment()
+    s.k_codes, s.k_idx, s.k_scale, s.k_zeros = (kp.codes.data_ptr(), kp.idx.data_ptr(),
+                                                kp.scale.data_ptr(), kp.zeros.data_ptr())
+    s.k_c, s.k_c_scale = kp.c.data_ptr(), kp.c_scale.data_ptr()
+    s.v_codes, s.v_idx, s.v_scale, s.v_zeros = (vp.codes.data_ptr(), vp.idx.data_ptr(),
+                                                vp.scale.data_ptr(), vp.zeros.data_ptr())
+    s.k_centroids, s.v_centroids = kc.data_ptr(), vc.data_ptr()
+    s.U = 0 if U is None else U.data_ptr()
+    s.T = kp.T
+    return s
+
+
+def decode_segment(kp, vp, kc, vc, U, k_out: torch.Tensor | None = None, v_out: torch.Tensor | None = None):
+    """BF16 reconstruction of one packed chunk: (K_hat, V_hat) [T, H, 128] bf16
+    (written into k_out / v_out, e.g. views of a larger buffer, when given)."""
+    T, H = kp.T, kp.H
+    if k_out is None:
+        k_out = torch.empty(T, H, D, dtype=torch.bfloat16, device=kp.codes.device)
+    if v_out is None:
+        v_out = torch.empty(T, H, D, dtype=torch.bfloat16, device=kp.codes.device)
+    for o in (k_out, v_out):
+        if o.dtype != torch.bfloat16 or tuple(o.shape) != (T, H, D) or o.stride(2) != 1:
+            raise ValueError("decode outputs must be [T, H, 128] bf16 with contiguous rows")
+    if k_out.stride() != v_out.stride():
+        raise ValueError("decode outputs must share strides")
+    seg = _segment(kp, vp, kc, vc, U)
+    check(lib.qwm_decode_segment(C.byref(seg), H, _ptr(k_out), _ptr(v_out), k_out.stride(0), k_out.stride(1),
+                                 _stream()))
+    return k_out, v_out
+
+
 def segments_tensor(segments, device="cuda") -> tuple:
     """Device array of segment descriptors.  `segments`: list of
     (k: PackedChunk, v: PackedChunk, k_centroids, v_centroids, U or None).

@@ -35,6 +35,8 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
                             const qwm_tokens* ka, const qwm_tokens* va, float scale, float* out, float* lse,
                             int32_t* top1, void* ws, hipStream_t stream);
 qwm_status launch_reference_top1(const qwm_tokens* q, const qwm_tokens* k, int32_t* top1, hipStream_t stream);
+qwm_status launch_decode(const qwm_segment* seg, int32_t H, uint16_t* k_out, uint16_t* v_out, int64_t ost,
+                         int64_t osh, hipStream_t stream);
 size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd);
 size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs, bool active);
 
@@ -192,6 +194,25 @@ qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n
   if (s != QWM_OK) return s;
   return launch_attention(q, segs, n_segs, total_keys, nullptr, nullptr, scale, out, lse, top1, ws,
                           static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_decode_segment(const qwm_segment* seg, int32_t H, uint16_t* k_out, uint16_t* v_out,
+                              int64_t out_stride_t, int64_t out_stride_h, qwm_stream stream) {
+  if (!seg) return fail(QWM_ERR_ARG, "decode: null segment descriptor");
+  if (H < 1 || seg->T < 1) return fail(QWM_ERR_ARG, "decode: H and T must be positive");
+  if ((int64_t)H * seg->T >= ((int64_t)1 << 31)) return fail(QWM_ERR_UNSUPPORTED, "decode: H*T >= 2^31");
+  if (!seg->k_codes || !seg->k_idx || !seg->k_scale || !seg->k_zeros || !seg->v_codes || !seg->v_idx ||
+      !seg->v_scale || !seg->v_zeros || !seg->k_centroids || !seg->v_centroids)
+    return fail(QWM_ERR_ARG, "decode: a packed array or centroid table is null");
+  if (seg->U && (!seg->k_c || !seg->k_c_scale)) return fail(QWM_ERR_ARG, "decode: PSAC basis without coefficients");
+  if (!aligned(seg->k_codes, 16) || !aligned(seg->v_codes, 16) || !aligned(seg->k_centroids, 16) ||
+      !aligned(seg->v_centroids, 16) || !aligned(seg->k_scale, 4) || !aligned(seg->v_scale, 4))
+    return fail(QWM_ERR_ARG, "decode: misaligned packed arrays");
+  if (!k_out || !v_out || !aligned(k_out, 16) || !aligned(v_out, 16))
+    return fail(QWM_ERR_ARG, "decode: outputs null or not 16-byte aligned");
+  if (out_stride_t < qwm::D || out_stride_h < 0 || out_stride_t % 8 || out_stride_h % 8)
+    return fail(QWM_ERR_ARG, "decode: output strides must be multiples of 8 elements, token stride >= d");
+  return launch_decode(seg, H, k_out, v_out, out_stride_t, out_stride_h, static_cast<hipStream_t>(stream));
 }
 
 qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,

@@ -200,6 +200,18 @@ qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, in
                                 const qwm_tokens* k_active, const qwm_tokens* v_active, float scale, float* out,
                                 float* lse, int32_t* top1, void* ws, size_t ws_bytes, qwm_stream stream);
 
+/* Reconstruct one packed chunk in BF16: the decoder of QuantWM App. D.1 /
+ * Fig. 9, which rebuilds temporary BF16 keys and values for a dense
+ * attention (kept here to compare that design with the fused kernel).
+ * K_hat = mu + s (q - z) + (c_s C) U^T (the PSAC term only when seg->U is
+ * not NULL) and V_hat = mu + s (q - z), each element the bf16 RNE of its
+ * exact value.  seg: HOST descriptor of a packed chunk (device pointers),
+ * H heads; k_out, v_out: [T][H][d] bf16 device buffers
+ * with element strides out_stride_t (>= d) and out_stride_h, 16-byte
+ * aligned rows.  No workspace. */
+qwm_status qwm_decode_segment(const qwm_segment* seg, int32_t H, uint16_t* k_out, uint16_t* v_out,
+                              int64_t out_stride_t, int64_t out_stride_h, qwm_stream stream);
+
 /* Top-1 key of every Query over unquantized keys, the reference side of the
  * token-shift metric (QuantWM v2 Sec. 5.3: how often the key a Query attends
  * to most differs between the quantized cache and BF16).

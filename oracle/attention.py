@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .formats import bf16_rne
 from .quantize import dequant_keys, dequant_values
 
 
@@ -50,6 +51,14 @@ def segment_kv(seg: dict):
     V = dequant_values(seg["v_idx"], seg["v_q"], seg["v_scale"], seg["v_zero"],
                        seg["v_centroids"])
     return K, V
+
+
+def decode_segment(seg: dict):
+    """BF16 reconstruction of one packed chunk of one head, the decoder of
+    QuantWM App. D.1 / Fig. 9: every element of K_hat and V_hat (exact in
+    float64) rounded once to bf16, nearest-even."""
+    K, V = segment_kv(seg)
+    return bf16_rne(K), bf16_rne(V)
 
 
 def cache_attention(Q: np.ndarray, segments: list, scale: float):

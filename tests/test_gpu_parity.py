@@ -384,6 +384,46 @@ def test_attention_with_bf16_active_chunk(qwm, sizes, active):
             assert abs(a - b) <= 1e-3 * abs(a), (i, a, b)
 
 
+def test_decode_segment_and_dense_attention(qwm):
+    """The decoder of QuantWM App. D.1 / Fig. 9 (BF16 reconstruction of packed
+    chunks, PSAC included): bit-exact against the oracle's rounded exact
+    values; then attention over the decoded rows as one dense chunk matches
+    the oracle's attention over the same bf16 values."""
+    import torch
+    from gpu_helpers import dev_tokens
+    sizes = [300, 130, 64]
+    _log(f"decode {sizes}")
+    w = datagen.make_workload("480p", heads=[0, 1], n_chunks=1, chunk=sum(sizes) + 256)
+    segs = _oracle_segments(w, sizes, [0, 1])
+    _, _, keep = _upload_segments(qwm, segs, 2)
+    total = sum(sizes)
+    Kd = torch.empty(total, 2, 128, dtype=torch.bfloat16, device="cuda")
+    Vd = torch.empty_like(Kd)
+    pos = 0
+    for (kp, vp, kc, vc, U), T in zip(keep, sizes):
+        qwm.decode_segment(kp, vp, kc, vc, U, Kd[pos:pos + T], Vd[pos:pos + T])
+        pos += T
+    torch.cuda.synchronize()
+    Kg, Vg = Kd.float().cpu().numpy(), Vd.float().cpu().numpy()
+    pos = 0
+    for si, T in enumerate(sizes):
+        for h in range(2):
+            Ko, Vo = OA.decode_segment(segs[si][h]["oracle"])
+            assert np.array_equal(Kg[pos:pos + T, h], Ko), (si, h)
+            assert np.array_equal(Vg[pos:pos + T, h], Vo), (si, h)
+        pos += T
+    Qv = w.Q[-200:]
+    out, lse, _ = qwm.attention(dev_tokens(Qv, "bf16"), None, 0, 0, want_lse=True, active=(Kd, Vd))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for h in range(2):
+        O, L, _ = OA.softmax_attention(Qv[:, h].astype(np.float64), Kg[:, h].astype(np.float64),
+                                       Vg[:, h].astype(np.float64), 1 / np.sqrt(128))
+        err = np.linalg.norm(out[:, h] - O) / np.linalg.norm(O)
+        _log(f"  dense over decoded rows, head {h}: rel L2 {err:.2e}")
+        assert err <= 2e-3
+
+
 def _check_top1(gt, ot, Qh, segs, h):
     """Top-1 agrees except where the oracle's top-2 logit gap is < 1e-3 relative."""
     Ks = [OA.segment_kv(s[h]["oracle"])[0] for s in segs]

@@ -134,3 +134,30 @@ def test_bf16_active_chunk_segment():
     Kd, Vd = A.segment_kv(packed)
     O2, lse2, top2 = A.cache_attention(Q[sl1], [dict(k_bf16=Kd, v_bf16=Vd), active], sc)
     assert np.array_equal(O, O2) and np.array_equal(top, top2)
+
+
+def test_decode_segment_is_the_rounded_reconstruction():
+    """Decode (QuantWM App. D.1 / Fig. 9): bf16 values within half a bf16 ulp of
+    the exact reconstruction; a key whose residual and PSAC terms vanish decodes
+    to its centroid exactly."""
+    from oracle import formats as F
+    w = datagen.make_workload("480p", heads=[0], n_chunks=1, chunk=300)
+    K, V, Q = (w.K[:, 0].astype(np.float64), w.V[:, 0].astype(np.float64), w.Q[:, 0].astype(np.float64))
+    Ck = lloyd.lloyd(K, 256, 2, seed=11)
+    Cv = lloyd.lloyd(V, 256, 2, seed=12)
+    S, n = stats.update(np.zeros((128, 128)), 0, Q)
+    U = stats.principal_basis(S, n)["U_bf16"]
+    kq = Qz.quantize_keys(K, Ck, stats.channel_weights(S, n), U, M=8)
+    vq = Qz.quantize_values(V, Cv)
+    seg = dict(k_idx=kq["idx"], k_q=kq["q"], k_scale=kq["scale"], k_zero=kq["zero"], k_Cq=kq["Cq"],
+               k_cs=kq["c_scale"], k_centroids=Ck, U=U, v_idx=vq["idx"], v_q=vq["q"], v_scale=vq["scale"],
+               v_zero=vq["zero"], v_centroids=Cv)
+    Kx, Vx = A.segment_kv(seg)
+    Kd, Vd = A.decode_segment(seg)
+    for X, Xd in ((Kx, Kd), (Vx, Vd)):
+        assert np.array_equal(F.bf16_rne(Xd), Xd)                  # bf16 values
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(Xd), 1e-30))) - 7)
+        assert np.all(np.abs(Xd - X) <= ulp / 2 + 1e-300)
+    seg0 = dict(seg, k_scale=np.zeros_like(seg["k_scale"]), k_cs=np.zeros_like(seg["k_cs"]))
+    K0, _ = A.decode_segment(seg0)
+    assert np.array_equal(K0, np.asarray(Ck, np.float64)[np.asarray(kq["idx"], np.int64)])
