@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--workload", default="480p", choices=["480p", "720p", "tiny", "depth", "rollout"])
     ap.add_argument("--f-energy", type=float, default=None, help="top-8 Query energy (720p: 0.60 or 0.71)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-ab", action="store_true",
+                    help="skip the decode + dense attention comparison (profiled runs: keeps the attention kernel's "
+                         "dispatches to the fused calls alone)")
     ap.add_argument("--cpu-sample-queries", type=int, default=480)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run device copies of a known size (reference for HBM byte counters)")
@@ -423,7 +426,8 @@ def run_stream_or_pass(args, qwm, torch, w):
         res["keys_step"] = {"token_heads": step.chunk * step.H,
                             "ms_incl_stats_wait": round(stage["keys_incl_stats_wait"], 4)}
         res["keys_bulk"] = keys_bulk(qwm, torch, step.K[: (step.nch - 1) * step.chunk], step.prev[0], step.st)
-        res["decode_ab"] = decode_ab(qwm, torch, step, stage["attention"])
+        if not args.no_decode_ab:
+            res["decode_ab"] = decode_ab(qwm, torch, step, stage["attention"])
     else:
         res["keys_bulk"] = keys_bulk(qwm, torch, step.K, step.Ck, step.st)
     res["wall_s_timed"] = round(wall, 3)
