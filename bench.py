@@ -132,11 +132,15 @@ class Stream:
         self.vdiag = qwm.new_diag()      # the V side counts on its own stream
         # the Query statistics and basis only feed the key quantization, and the V side
         # (table refresh, values) is independent of the K side: each runs on its own
-        # stream, overlapped with the K table refresh
+        # stream.  The statistics a step's keys need come from the previous chunk's
+        # Queries, so each step launches the next step's update as soon as its own
+        # keys have read w and U; it runs beside the step's attention
         self.side = torch.cuda.Stream()
         self.vside = torch.cuda.Stream()
         self.stats_done = torch.cuda.Event()
+        self.keys_done = torch.cuda.Event()
         self.v_done = torch.cuda.Event()
+        self.primed = False
         self.queries = T
         self.new_tokens = T
         self.stage_names = ["launch_side_streams", "lloyd_k", "keys_incl_stats_wait", "values_wait", "attention"]
@@ -165,11 +169,10 @@ class Stream:
         K, V = self.K[self.sl_new], self.V[self.sl_new]
         main = torch.cuda.current_stream()
         rec(0)
-        self.side.wait_stream(main)
+        if not self.primed:          # the first step's statistics (afterwards: the previous step's launch)
+            self._launch_stats(main)
+            self.primed = True
         self.vside.wait_stream(main)
-        with torch.cuda.stream(self.side):
-            qwm.update_query_stats(self.Q[self.sl_prevq], self.st, compute_basis=True)
-            self.stats_done.record(self.side)
         with torch.cuda.stream(self.vside):
             qwm.build_centroids(V, 3, init=self.prev[1], out=self.Cv, diag=self.vdiag)
             qwm.quantize_values(V, self.Cv, out=self.vp, diag=self.vdiag)
@@ -179,12 +182,24 @@ class Stream:
         rec(2)
         main.wait_event(self.stats_done)
         qwm.quantize_keys(K, self.Ck, self.st.w, self.st.U, M=8, flags=3, out=self.kp, diag=self.diag)
+        self.keys_done.record(main)
         rec(3)
+        # the next step's statistics (one update + basis per step, as before)
+        self._launch_stats(main, after=self.keys_done)
         main.wait_event(self.v_done)
         rec(4)
         out, _, _ = qwm.attention(self.Q[self.sl_new], self.dsegs, self.nch, self.total)
         rec(5)
         return out
+
+    def _launch_stats(self, main, after=None):
+        if after is None:
+            self.side.wait_stream(main)
+        else:
+            self.side.wait_event(after)
+        with self.torch.cuda.stream(self.side):
+            self.qwm.update_query_stats(self.Q[self.sl_prevq], self.st, compute_basis=True)
+            self.stats_done.record(self.side)
 
 
 class OnePass:
