@@ -60,8 +60,8 @@ def parse():
     ap.add_argument("--f-energy", type=float, default=None, help="top-8 Query energy (720p: 0.60 or 0.71)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-ab", action="store_true",
-                    help="skip the decode + dense attention comparison (profiled runs: keeps the attention kernel's "
-                         "dispatches to the fused calls alone)")
+                    help="skip the extras after the step (decode + dense attention comparison, M sweep, multi-stage "
+                         "codec); profiled runs use it, so the attention kernel's dispatches are the fused calls alone")
     ap.add_argument("--cpu-sample-queries", type=int, default=480)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run device copies of a known size (reference for HBM byte counters)")
@@ -325,6 +325,49 @@ def keys_bulk(qwm, torch, Kall, table, st):
             "GBps": round(byts / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def keys_m_sweep(qwm, torch, Kall, table, st, Ms=(4, 8, 16, 256)):
+    """The pages' candidate-count ablation (QSAC's M): bulk key quantization
+    (QSAC + PSAC) at each M, same tokens and tables."""
+    H = Kall.shape[1]
+    kb = qwm.PackedChunk(Kall.shape[0], H, True)
+    diag = qwm.new_diag()
+    out = {}
+    for M in Ms:
+        qwm.quantize_keys(Kall, table, st.w, st.U, M=M, flags=3, out=kb)
+        torch.cuda.synchronize()
+        diag.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            qwm.quantize_keys(Kall, table, st.w, st.U, M=M, flags=3, out=kb, diag=diag)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 3
+        out[str(M)] = {"ms": round(ms, 4), "tokens_per_s": round(Kall.shape[0] / (ms * 1e-3), 1),
+                       "exact_fallbacks": int(diag.tolist()[1]) // 3}
+    return out
+
+
+def prq_codec(qwm, torch, X, stages=(1, 2, 3), iters=10):
+    """QVG's progressive residual quantization as a second codec workload: all
+    stages (seeded Lloyd on each stage's residual, nearest assignment, fp32
+    residual) and the last stage's INT2 codes, for 1 to 3 stages."""
+    out = {}
+    for S in stages:
+        qwm.prq_quantize(X, S, iters=iters, seed=1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            qwm.prq_quantize(X, S, iters=iters, seed=1)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 3
+        out[str(S)] = {"ms": round(ms, 4), "token_heads_per_s": round(X.shape[0] * X.shape[1] / (ms * 1e-3), 1)}
+    out["workload"] = f"{X.shape[0]} tokens x {X.shape[1]} heads, {iters} seeded Lloyd iterations per stage"
+    return out
+
+
 def decode_ab(qwm, torch, step, fused_ms):
     """The pages' read path for comparison: decode every packed chunk to BF16
     (K_hat with PSAC, V_hat), then dense attention over the decoded rows, against
@@ -443,6 +486,9 @@ def run_stream_or_pass(args, qwm, torch, w):
         res["keys_bulk"] = keys_bulk(qwm, torch, step.K[: (step.nch - 1) * step.chunk], step.prev[0], step.st)
         if not args.no_decode_ab:
             res["decode_ab"] = decode_ab(qwm, torch, step, stage["attention"])
+            res["keys_m_sweep"] = keys_m_sweep(qwm, torch, step.K[: (step.nch - 1) * step.chunk], step.prev[0],
+                                               step.st)
+            res["prq_codec"] = prq_codec(qwm, torch, step.K[step.sl_new])
     else:
         res["keys_bulk"] = keys_bulk(qwm, torch, step.K, step.Ck, step.st)
     res["wall_s_timed"] = round(wall, 3)

@@ -167,6 +167,39 @@ def quantize_values(v: torch.Tensor, centroids: torch.Tensor, out: PackedChunk |
     return out
 
 
+def centroid_residual(x: torch.Tensor, centroids: torch.Tensor, idx: torch.Tensor,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 [T, H, 128]: every token minus its assigned centroid (idx [H, T] u8)."""
+    td = _tokens(x)
+    if out is None:
+        out = torch.empty(td.T, td.H, D, dtype=torch.float32, device=x.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (td.T, td.H, D) or out.stride(2) != 1:
+        raise ValueError("residual output must be [T, H, 128] fp32 with contiguous rows")
+    check(lib.qwm_centroid_residual(C.byref(td), _ptr(centroids), _ptr(idx), _ptr(out), out.stride(0),
+                                    out.stride(1), _stream()))
+    return out
+
+
+def prq_quantize(x: torch.Tensor, stages: int, iters: int = 10, seed: int = 0):
+    """QVG's progressive residual quantization of the tokens x [T, H, 128]:
+    stages 1 .. S-1 each cluster the current residual (256 centroids, seeded
+    Lloyd, seed + s - 1), take every token's nearest centroid and pass on the
+    fp32 residual; the last stage codes that residual as values are coded.
+    Returns ([(table, idx [H, T] u8)] for the first S - 1 stages, the last
+    stage's table, its PackedChunk)."""
+    if stages < 1:
+        raise ValueError("stages must be >= 1")
+    e = x
+    first = []
+    for s in range(stages - 1):
+        Cs = build_centroids(e, iters, seed=seed + s)
+        pk = quantize_values(e, Cs)              # idx: the nearest centroid of every token
+        first.append((Cs, pk.idx))
+        e = centroid_residual(e, Cs, pk.idx)
+    C_last = build_centroids(e, iters, seed=seed + stages - 1)
+    return first, C_last, quantize_values(e, C_last)
+
+
 def _segment(kp, vp, kc, vc, U) -> Segment:
     s = Segment()
     s.k_codes, s.k_idx, s.k_scale, s.k_zeros = (kp.codes.data_ptr(), kp.idx.data_ptr(),

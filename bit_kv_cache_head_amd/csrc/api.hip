@@ -37,6 +37,8 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
 qwm_status launch_reference_top1(const qwm_tokens* q, const qwm_tokens* k, int32_t* top1, hipStream_t stream);
 qwm_status launch_decode(const qwm_segment* seg, int32_t H, uint16_t* k_out, uint16_t* v_out, int64_t ost,
                          int64_t osh, hipStream_t stream);
+qwm_status launch_centroid_residual(const qwm_tokens* x, const uint16_t* centroids, const uint8_t* idx, float* out,
+                                   int64_t ost, int64_t osh, hipStream_t stream);
 size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd);
 size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs, bool active);
 
@@ -213,6 +215,17 @@ qwm_status qwm_decode_segment(const qwm_segment* seg, int32_t H, uint16_t* k_out
   if (out_stride_t < qwm::D || out_stride_h < 0 || out_stride_t % 8 || out_stride_h % 8)
     return fail(QWM_ERR_ARG, "decode: output strides must be multiples of 8 elements, token stride >= d");
   return launch_decode(seg, H, k_out, v_out, out_stride_t, out_stride_h, static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_centroid_residual(const qwm_tokens* x, const uint16_t* centroids, const uint8_t* idx, float* out,
+                                 int64_t out_stride_t, int64_t out_stride_h, qwm_stream stream) {
+  qwm_status s = check_tokens(x, "tokens", false);
+  if (s != QWM_OK) return s;
+  if (!centroids || !aligned(centroids, 16) || !idx) return fail(QWM_ERR_ARG, "residual: null or misaligned table/idx");
+  if (!out || !aligned(out, 16)) return fail(QWM_ERR_ARG, "residual: output null or not 16-byte aligned");
+  if (out_stride_t < qwm::D || out_stride_h < 0 || out_stride_t % 4 || out_stride_h % 4)
+    return fail(QWM_ERR_ARG, "residual: output strides must be multiples of 4 elements, token stride >= d");
+  return launch_centroid_residual(x, centroids, idx, out, out_stride_t, out_stride_h, static_cast<hipStream_t>(stream));
 }
 
 qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,

@@ -2,7 +2,8 @@
 // and Fig. 9 (residual unpacking, parameter reconstruction, centroid gather
 // and PSAC accumulation into temporary BF16 keys and values that a dense
 // attention then reads).  The fused attention kernel never forms these rows;
-// this path exists to compare the two designs.
+// this path exists to compare the two designs.  The same file holds the
+// centroid residual used by the multi-stage (progressive) codec.
 //
 // Each element is computed exactly in fp64 and rounded once to bf16 (RNE):
 //   K_hat[t][c] = mu_k[idx][c] + s_g (q - z_g) + sum_r (c_s C_r) U[c][r]
@@ -96,6 +97,54 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   *reinterpret_cast<u32x4*>(a.vout + o + 8) = vw[1];
 }
 
+// The residual of every token against its assigned centroid, fp32:
+// out[t][h][c] = fl32(x[t][h][c] - C[h][idx[h][t]][c]) -- the centroid
+// subtraction of QVG's smoothing step (QVG summary Sec. 2A), which its
+// progressive residual quantization repeats stage by stage (Sec. 2B).
+// Grid (ceil(T / 32), H), 256 threads: token tid / 8, channels 16 (tid % 8) .. +16.
+struct ResidArgs {
+  const void* x; int32_t dtype; int64_t T; int64_t st, sh;
+  const uint16_t* C; const uint8_t* idx;
+  float* out; int64_t ost, osh;
+};
+
+__global__ __launch_bounds__(256) void centroid_residual_kernel(ResidArgs a) {
+  const int h = blockIdx.y, tk = threadIdx.x >> 3, cb = threadIdx.x & 7;
+  const int64_t t = (int64_t)blockIdx.x * DEC_TOK + tk;
+  if (t >= a.T) return;
+  const uint16_t* mu = a.C + ((int64_t)h * NC + a.idx[(int64_t)h * a.T + t]) * D + 16 * cb;
+  const u32x4 m0 = *reinterpret_cast<const u32x4*>(mu), m1 = *reinterpret_cast<const u32x4*>(mu + 8);
+  float x[16];
+  const int64_t xo = t * a.st + (int64_t)h * a.sh + 16 * cb;
+  if (a.dtype == QWM_BF16) {
+    const uint16_t* xp = static_cast<const uint16_t*>(a.x) + xo;
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(xp), v1 = *reinterpret_cast<const u32x4*>(xp + 8);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t w = j < 8 ? v0[j >> 1] : v1[(j - 8) >> 1];
+      x[j] = (j & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+    }
+  } else {
+    const float* xp = static_cast<const float*>(a.x) + xo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(xp + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
+    }
+  }
+  f32x4 o[4];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t w = j < 8 ? m0[j >> 1] : m1[(j - 8) >> 1];
+    const float m = (j & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+    o[j >> 2][j & 3] = x[j] - m;
+  }
+  float* op = a.out + t * a.ost + (int64_t)h * a.osh + 16 * cb;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(op + 4 * q) = o[q];
+}
+
 }  // namespace qwm
 
 namespace qwm_host {
@@ -109,6 +158,16 @@ qwm_status launch_decode(const qwm_segment* seg, int32_t H, uint16_t* k_out, uin
   const dim3 grid((unsigned)((seg->T + DEC_TOK - 1) / DEC_TOK), (unsigned)H);
   hipLaunchKernelGGL(decode_kernel, grid, dim3(256), 0, stream, a);
   return check_launch("chunk decode");
+}
+
+qwm_status launch_centroid_residual(const qwm_tokens* x, const uint16_t* centroids, const uint8_t* idx, float* out,
+                                   int64_t ost, int64_t osh, hipStream_t stream) {
+  ResidArgs a{};
+  a.x = x->ptr; a.dtype = x->dtype; a.T = x->T; a.st = x->stride_t; a.sh = x->stride_h;
+  a.C = centroids; a.idx = idx; a.out = out; a.ost = ost; a.osh = osh;
+  const dim3 grid((unsigned)((x->T + DEC_TOK - 1) / DEC_TOK), (unsigned)x->H);
+  hipLaunchKernelGGL(centroid_residual_kernel, grid, dim3(256), 0, stream, a);
+  return check_launch("centroid residual");
 }
 
 }  // namespace qwm_host

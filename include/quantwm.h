@@ -212,6 +212,18 @@ qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, in
 qwm_status qwm_decode_segment(const qwm_segment* seg, int32_t H, uint16_t* k_out, uint16_t* v_out,
                               int64_t out_stride_t, int64_t out_stride_h, qwm_stream stream);
 
+/* The residual of every token against its assigned centroid, in fp32:
+ * out[t][h][c] = fl32(x[t][h][c] - centroids[h][idx[h][t]][c]).  This is the
+ * centroid subtraction of QVG's smoothing step (QVG summary Sec. 2A); its
+ * progressive residual quantization (Sec. 2B) repeats it stage by stage on
+ * the previous stage's residual (bit_kv_cache_head_amd.prq_quantize composes
+ * the stages from this call, qwm_build_centroids and qwm_quantize_values).
+ * x: bf16 or fp32 tokens; centroids [H][256][d] bf16; idx [H][T] u8; out
+ * [T][H][d] fp32 with element strides (multiples of 4, token stride >= d),
+ * 16-byte aligned.  No workspace. */
+qwm_status qwm_centroid_residual(const qwm_tokens* x, const uint16_t* centroids, const uint8_t* idx, float* out,
+                                 int64_t out_stride_t, int64_t out_stride_h, qwm_stream stream);
+
 /* Top-1 key of every Query over unquantized keys, the reference side of the
  * token-shift metric (QuantWM v2 Sec. 5.3: how often the key a Query attends
  * to most differs between the quantized cache and BF16).

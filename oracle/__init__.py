@@ -15,7 +15,8 @@ Modules
   quantize   - QSAC centroid choice, INT2 residual codec, PSAC coefficients,
                value quantization
   attention  - dequantization and softmax attention over the compressed cache,
-               top-1 token selection
+               top-1 token selection, the BF16 decoder
+  prq        - QVG's progressive (multi-stage) residual quantization
   accounting - bits per token-head and compression ratios
 
 Parity pins: every function is pinned by tests under tests/test_oracle_*.py

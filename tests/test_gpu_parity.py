@@ -148,7 +148,7 @@ def _key_inputs(name, T, heads, seed=5):
     return w, K, np.stack(tables), np.stack(ws), np.stack(Us)
 
 
-@pytest.mark.parametrize("flags,M", [(3, 8), (1, 8), (2, 8), (0, 8), (3, 1), (3, 256)])
+@pytest.mark.parametrize("flags,M", [(3, 8), (1, 8), (2, 8), (0, 8), (3, 1), (3, 4), (3, 16), (3, 256)])
 def test_quantize_keys(qwm, flags, M):
     import torch
     from gpu_helpers import dev_tokens, dev_table, dev_basis, packed_host, idx_mismatches_allowed, compare_codec
@@ -422,6 +422,30 @@ def test_decode_segment_and_dense_attention(qwm):
         err = np.linalg.norm(out[:, h] - O) / np.linalg.norm(O)
         _log(f"  dense over decoded rows, head {h}: rel L2 {err:.2e}")
         assert err <= 2e-3
+
+
+@pytest.mark.parametrize("stages", [1, 2, 3])
+def test_prq_quantize(qwm, stages):
+    """QVG's progressive residual quantization (summary Sec. 2B): every stage's
+    table and assignment and the last stage's codes, bit-exact against the
+    oracle (fp32 stage residuals on both sides)."""
+    import torch
+    from gpu_helpers import dev_tokens, packed_host, compare_codec
+    from oracle import prq
+    _log(f"prq {stages} stages")
+    w = datagen.make_workload("480p", heads=[0, 1], n_chunks=1, chunk=600)
+    X = dev_tokens(w.K, "bf16")
+    first, C_last, last = qwm.prq_quantize(X, stages, iters=3, seed=9)
+    torch.cuda.synchronize()
+    for h in range(2):
+        ofirst, oC, olast, _ = prq.prq_quantize(w.K[:, h].astype(np.float64), stages, 3, seed=9, head=h)
+        for (C, idx), (Co, ao) in zip(first, ofirst):
+            assert np.array_equal(C[h].float().cpu().numpy(), Co)
+            assert np.array_equal(idx[h].cpu().numpy(), ao)
+        assert np.array_equal(C_last[h].float().cpu().numpy(), oC)
+        g = packed_host(last)
+        assert np.array_equal(g["idx"][h], olast["idx"])
+        compare_codec(olast, {k: v[h] for k, v in g.items()}, 600, np.ones(600, bool))
 
 
 def _check_top1(gt, ot, Qh, segs, h):
