@@ -325,6 +325,25 @@ def keys_bulk(qwm, torch, Kall, table, st):
             "GBps": round(byts / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def keys_keep_test(qwm, torch, Kall, table, st):
+    """Bulk key quantization with the PSAC keep test (flags QSAC | PSAC | KEEP):
+    time, and the fraction of tokens that keep their coefficients."""
+    H = Kall.shape[1]
+    kb = qwm.PackedChunk(Kall.shape[0], H, True)
+    flags = qwm.QWM_QSAC | qwm.QWM_PSAC | qwm.QWM_PSAC_KEEP
+    qwm.quantize_keys(Kall, table, st.w, st.U, M=8, flags=flags, out=kb)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        qwm.quantize_keys(Kall, table, st.w, st.U, M=8, flags=flags, out=kb)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    kept = float((kb.c_scale != 0).float().mean().item())
+    return {"ms": round(ms, 4), "tokens_per_s": round(Kall.shape[0] / (ms * 1e-3), 1), "kept_fraction": round(kept, 4)}
+
+
 def keys_m_sweep(qwm, torch, Kall, table, st, Ms=(4, 8, 16, 256)):
     """The pages' candidate-count ablation (QSAC's M): bulk key quantization
     (QSAC + PSAC) at each M, same tokens and tables."""
@@ -489,6 +508,8 @@ def run_stream_or_pass(args, qwm, torch, w):
             res["keys_m_sweep"] = keys_m_sweep(qwm, torch, step.K[: (step.nch - 1) * step.chunk], step.prev[0],
                                                step.st)
             res["prq_codec"] = prq_codec(qwm, torch, step.K[step.sl_new])
+            res["keys_keep_test"] = keys_keep_test(qwm, torch, step.K[: (step.nch - 1) * step.chunk], step.prev[0],
+                                                   step.st)
     else:
         res["keys_bulk"] = keys_bulk(qwm, torch, step.K, step.Ck, step.st)
     res["wall_s_timed"] = round(wall, 3)

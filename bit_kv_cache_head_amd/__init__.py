@@ -12,7 +12,7 @@ import os
 
 import torch
 
-from ._abi import (lib, LIB_PATH, QWM_OK, QWM_F32, QWM_BF16, QWM_QSAC, QWM_PSAC, QWM_OP_STATS,
+from ._abi import (lib, LIB_PATH, QWM_OK, QWM_F32, QWM_BF16, QWM_QSAC, QWM_PSAC, QWM_PSAC_KEEP, QWM_OP_STATS,
                    QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION, QWM_OP_ATTENTION_ACTIVE, Tokens, QStats,
                    Packed, Diag, Segment, check)
 
@@ -20,7 +20,7 @@ D, NC, R, GROUP = 128, 256, 8, 64
 
 __all__ = ["QueryStats", "PackedChunk", "Workspace", "update_query_stats", "build_centroids",
            "quantize_keys", "quantize_values", "attention", "segments_tensor", "zeros_stride",
-           "QWM_QSAC", "QWM_PSAC", "LIB_PATH", "new_diag"]
+           "QWM_QSAC", "QWM_PSAC", "QWM_PSAC_KEEP", "LIB_PATH", "new_diag"]
 
 
 def _stream():

@@ -9,7 +9,7 @@ LIB_PATH = os.path.join(_PKG, "libquantwm.so")
 
 QWM_OK, QWM_ERR_ARG, QWM_ERR_UNSUPPORTED, QWM_ERR_WORKSPACE, QWM_ERR_HIP = 0, 1, 2, 3, 4
 QWM_F32, QWM_BF16 = 0, 1
-QWM_QSAC, QWM_PSAC = 1, 2
+QWM_QSAC, QWM_PSAC, QWM_PSAC_KEEP = 1, 2, 4
 QWM_OP_STATS, QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION, QWM_OP_ATTENTION_ACTIVE = 0, 1, 2, 3, 4, 5
 
 # every symbol include/quantwm.h declares

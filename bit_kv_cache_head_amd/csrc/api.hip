@@ -147,7 +147,7 @@ qwm_status qwm_quantize_keys(const qwm_tokens* k, const uint16_t* centroids, con
   qwm_status s = check_tokens(k, "keys", false);
   if (s != QWM_OK) return s;
   if (!centroids || !aligned(centroids, 16)) return fail(QWM_ERR_ARG, "centroids: null or not 16-byte aligned");
-  if (flags & ~(uint32_t)(QWM_QSAC | QWM_PSAC)) return fail(QWM_ERR_ARG, "unknown flag bits");
+  if (flags & ~(uint32_t)(QWM_QSAC | QWM_PSAC | QWM_PSAC_KEEP)) return fail(QWM_ERR_ARG, "unknown flag bits");
   if ((flags & QWM_QSAC) && (M < 1 || M > qwm::NC)) return fail(QWM_ERR_ARG, "M must be in [1, 256]");
   if (w && !aligned(w, 4)) return fail(QWM_ERR_ARG, "w misaligned");
   if (U && !aligned(U, 16)) return fail(QWM_ERR_ARG, "U not 16-byte aligned");

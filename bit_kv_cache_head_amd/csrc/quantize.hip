@@ -627,9 +627,10 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
           float m = fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])), fmaxf(fabsf(acc[2]), fabsf(acc[3])));
           m = lanepair_max(m);
           bool sat = false;
-          const uint32_t csb = fp16_up_div((double)m, 127.0f, &sat);
+          uint32_t csb = fp16_up_div((double)m, 127.0f, &sat);
           const float cs = f16_bits_to_f32(csb);
           uint32_t packed = 0;
+          float chat[4];   // c_s C_q of this lane's four coefficients
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             int qi = 0;
@@ -638,6 +639,53 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
               qi = qi < -127 ? -127 : (qi > 127 ? 127 : qi);
             }
             packed |= ((uint32_t)(uint8_t)(int8_t)qi) << (8 * i);
+            chat[i] = cs * (float)qi;   // exact (11 + 8 significant bits)
+          }
+          if (a.flags & QWM_PSAC_KEEP) {
+            // Keep test (QuantWM method step (4)): the coefficients stay only if the
+            // compensation D = (c_s C_q) U^T lowers the key's Query-weighted error
+            // sum_c w_c e_c^2, i.e. iff sum_c w_c D_c (D_c - 2 E_c) < 0; E is
+            // recomputed from the codes just written, the weights are those of
+            // the centroid choice.
+            float cr[R];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float o = lanepair_other(chat[i], hh);
+              cr[i] = hh ? o : chat[i];
+              cr[4 + i] = hh ? chat[i] : o;
+            }
+            float crit = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+              const GroupCodec& g = s < 4 ? g0 : g1;
+              const u32x4 mv = mu_chunk(sm.mu, win, 2 * s + hh);
+              u32x4 ur[R];
+#pragma unroll
+              for (int r2 = 0; r2 < R; ++r2) ur[r2] = *reinterpret_cast<const u32x4*>(&sm.ut[r2][16 * s + 8 * hh]);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t mwd = mv[e >> 1];
+                const float mu = (e & 1) ? __uint_as_float(mwd & 0xFFFF0000u) : __uint_as_float(mwd << 16);
+                const float x = kf[8 * s + e];
+                const float r = x - mu;
+                const uint32_t q = code_of(r, g);
+                float E = r - g.s * ((float)q - (float)g.z);
+                if (F32) {
+                  const float bv = r - x;
+                  E += (x - (r - bv)) + (-mu - bv);
+                }
+                float Dc = 0.f;
+#pragma unroll
+                for (int r2 = 0; r2 < R; ++r2) {
+                  const uint32_t uw = ur[r2][e >> 1];
+                  const float u = (e & 1) ? __uint_as_float(uw & 0xFFFF0000u) : __uint_as_float(uw << 16);
+                  Dc = fmaf(cr[r2], u, Dc);
+                }
+                crit = fmaf(sm.w[16 * s + 8 * hh + e] * Dc, Dc - 2.0f * E, crit);
+              }
+            }
+            crit = lanepair_sum(crit);
+            if (!(crit < 0.f)) { packed = 0u; csb = 0u; }
           }
           if (valid) {
             *reinterpret_cast<uint32_t*>(&sm.cq[wv][ln][4 * hh]) = packed;

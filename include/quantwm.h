@@ -60,7 +60,12 @@ typedef enum {
 typedef enum { QWM_F32 = 0, QWM_BF16 = 1 } qwm_dtype;
 
 /* Key-quantization flags.  0 = nearest centroid only (the QVG-style baseline). */
-enum { QWM_QSAC = 1u, QWM_PSAC = 2u };
+enum { QWM_QSAC = 1u, QWM_PSAC = 2u,
+       /* the PSAC keep test (QuantWM method step (4)): a key keeps its
+        * coefficients only if they lower its Query-weighted error
+        * sum_c w_c e_c^2 (w under QSAC, else 1); otherwise C = 0, c_scale = 0.
+        * The decision is taken in fp32. */
+       QWM_PSAC_KEEP = 4u };
 
 /* Workspace-sizing operation ids for qwm_workspace_bytes(). */
 enum { QWM_OP_STATS = 0, QWM_OP_CENTROIDS = 1, QWM_OP_KEYS = 2, QWM_OP_VALUES = 3,

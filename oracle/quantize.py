@@ -39,6 +39,7 @@ from .formats import (bf16_rne, fp16_up_div, rne_quotient, pack_codes, pack_zero
 GROUP = 64
 QSAC = 1
 PSAC = 2
+PSAC_KEEP = 4   # the PSAC keep test (QuantWM method step (4))
 
 
 def weighted_dists(K: np.ndarray, C: np.ndarray, w: np.ndarray, block: int = 64) -> np.ndarray:
@@ -110,6 +111,19 @@ def psac_coefficients(E: np.ndarray, U_bf16: np.ndarray):
     return Cq.astype(np.int8), cs, C
 
 
+def psac_keep(E: np.ndarray, Cq: np.ndarray, cs: np.ndarray, U_bf16: np.ndarray, w: np.ndarray):
+    """PSAC keep test (QuantWM method step (4)): a token keeps its coefficients
+    only if the compensation lowers its Query-weighted error
+    sum_c w_c e_c^2, i.e. iff sum_c w_c D_c (D_c - 2 E_c) < 0 with
+    D = (c_s C_q) U^T (the difference of the errors with and without it).
+    Returns (keep [T] bool, that criterion [T], sum_c w_c E_c^2 [T])."""
+    E = np.asarray(E, np.float64)
+    Dm = (np.asarray(cs, np.float64)[:, None] * np.asarray(Cq, np.float64)) @ np.asarray(U_bf16, np.float64).T
+    w = np.asarray(w, np.float64)
+    crit = np.sum(w * Dm * (Dm - 2.0 * E), axis=1)
+    return crit < 0.0, crit, np.sum(w * E * E, axis=1)
+
+
 def select_qsac(K: np.ndarray, C: np.ndarray, w: np.ndarray, M: int):
     """QSAC: top-M candidates by (d_Q, j), then argmin by (S, j).
 
@@ -148,7 +162,9 @@ def quantize_keys(K: np.ndarray, C: np.ndarray, w: np.ndarray | None, U_bf16: np
 
     flags & QSAC: QSAC choice with weights w (w = 1 when None); otherwise the
     nearest centroid (w is then ignored).  flags & PSAC with a basis: PSAC
-    coefficients; otherwise C = 0.
+    coefficients; otherwise C = 0.  flags & PSAC_KEEP: the keep test drops the
+    coefficients (C = 0, c_s = 0) of tokens they do not help, with the channel
+    weights of the centroid choice (w under QSAC, else 1).
     """
     K = np.asarray(K, np.float64)
     T, d = K.shape
@@ -161,15 +177,22 @@ def quantize_keys(K: np.ndarray, C: np.ndarray, w: np.ndarray | None, U_bf16: np
     r = residual(K, np.asarray(C)[idx])
     q, s, z, r_hat, n_sat = encode_residual(r)
     r_rank = 8 if U_bf16 is None else U_bf16.shape[1]
+    keep_info = None
     if (flags & PSAC) and U_bf16 is not None:
         E = K - (np.asarray(C, np.float64)[idx] + r_hat)
         Cq, cs, Craw = psac_coefficients(E, U_bf16)
+        if flags & PSAC_KEEP:
+            wk = np.ones(d) if (w is None or not (flags & QSAC)) else np.asarray(w, np.float32).astype(np.float64)
+            keep, crit, base = psac_keep(E, Cq, cs, U_bf16, wk)
+            Cq = np.where(keep[:, None], Cq, 0).astype(np.int8)
+            cs = np.where(keep, cs, 0.0)
+            keep_info = {"keep": keep, "crit": crit, "base": base}
     else:
         Cq = np.zeros((T, r_rank), np.int8)
         cs = np.zeros(T)
         Craw = None
     return {"idx": idx.astype(np.uint8), "q": q, "scale": s, "zero": z, "r_hat": r_hat,
-            "Cq": Cq, "c_scale": cs, "C_raw": Craw, "info": info, "saturated": n_sat,
+            "Cq": Cq, "c_scale": cs, "C_raw": Craw, "info": info, "saturated": n_sat, "keep": keep_info,
             # packed storage
             "codes": pack_codes(q), "zeros": pack_zeros(z),
             "scale_bits": fp16_bits(s), "c_scale_bits": fp16_bits(cs)}

@@ -148,7 +148,7 @@ def _key_inputs(name, T, heads, seed=5):
     return w, K, np.stack(tables), np.stack(ws), np.stack(Us)
 
 
-@pytest.mark.parametrize("flags,M", [(3, 8), (1, 8), (2, 8), (0, 8), (3, 1), (3, 4), (3, 16), (3, 256)])
+@pytest.mark.parametrize("flags,M", [(3, 8), (1, 8), (2, 8), (0, 8), (3, 1), (3, 4), (3, 16), (3, 256), (7, 8), (6, 8)])
 def test_quantize_keys(qwm, flags, M):
     import torch
     from gpu_helpers import dev_tokens, dev_table, dev_basis, packed_host, idx_mismatches_allowed, compare_codec
@@ -171,6 +171,27 @@ def test_quantize_keys(qwm, flags, M):
         total_mis += nmis
         same = o["idx"] == g["idx"][h]
         compare_codec(o, {k: v[h] for k, v in g.items()}, T, same)
+        if flags & 4:
+            # keep test: decisions agree except near ties.  The kernel decides in
+            # fp32 on coefficients within 1 LSB of the oracle's, so a tie is a
+            # criterion below the effect of one LSB in every coefficient plus
+            # fp32 rounding: 2 c_s sum_c w_c sum_r |U_cr| (|D_c| + |E_c| + c_s |U_cr|)
+            # + 2^-16 sum_c w_c (D_c^2 + E_c^2)
+            full = Qz.quantize_keys(K[:, h].astype(np.float64), Ct[h], wt[h], Ut[h], M=M, flags=flags & ~4)
+            ki = o["keep"]
+            g_keep = (g["c_scale_bits"][h] != 0) | np.any(g["c"][h] != 0, axis=1)
+            mu = np.asarray(Ct[h], np.float64)[np.asarray(o["idx"], np.int64)]
+            E = K[:, h].astype(np.float64) - (mu + o["r_hat"])
+            Ua = np.abs(np.asarray(Ut[h], np.float64))
+            cs = full["c_scale"]
+            D = (cs[:, None] * full["Cq"].astype(np.float64)) @ np.asarray(Ut[h], np.float64).T
+            wk = np.asarray(wt[h], np.float32).astype(np.float64) if flags & 1 else np.ones(128)
+            tol = (2 * cs * np.sum(wk * Ua.sum(axis=1)[None, :] * (np.abs(D) + np.abs(E) + cs[:, None]), axis=1)
+                   + 2.0 ** -16 * np.sum(wk * (D * D + E * E), axis=1))
+            dis = same & (g_keep != ki["keep"])
+            assert np.all(np.abs(ki["crit"][dis]) <= tol[dis]), np.nonzero(dis)[0][:5]
+            same = same & (g_keep == ki["keep"])
+            _log(f"  head {h}: kept {ki['keep'].mean():.3f}, decision near-ties {int(dis.sum())}")
         if flags & 2:
             dc = np.abs(g["c"][h].astype(np.int64) - o["Cq"].astype(np.int64))
             assert dc[same].max() <= 1

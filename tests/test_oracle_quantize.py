@@ -11,6 +11,7 @@ import pytest
 from scipy.spatial.distance import cdist
 
 import datagen
+from oracle import lloyd
 from oracle import quantize as Qz
 from oracle import stats
 from oracle.formats import bf16_rne, unpack_zeros, unpack_codes
@@ -248,3 +249,35 @@ def test_values_are_nearest_plus_codec():
     Vh = Qz.dequant_values(out["idx"], out["q"], out["scale"], out["zero"], C)
     err = np.abs(V - Vh).reshape(64, 2, 64)
     assert np.all(err <= out["scale"][..., None] / 2)
+
+
+def test_psac_keep_test():
+    """The keep test (method step (4)): with it, no token's Query-weighted error
+    sum_c w_c e_c^2 (e = k - K_hat) is above the error without compensation,
+    and the criterion equals the difference of the two errors, computed
+    directly (brute force) for every token."""
+    w = datagen.make_workload("480p", heads=[0], n_chunks=1, chunk=400)
+    K, Q = w.K[:, 0].astype(np.float64), w.Q[:, 0].astype(np.float64)
+    C = lloyd.lloyd(K, 256, 2, seed=3)
+    S, n = stats.update(np.zeros((128, 128)), 0, Q)
+    U = stats.principal_basis(S, n)["U_bf16"]
+    wt = stats.channel_weights(S, n)
+    full = Qz.quantize_keys(K, C, wt, U, M=8, flags=Qz.QSAC | Qz.PSAC)
+    kept = Qz.quantize_keys(K, C, wt, U, M=8, flags=Qz.QSAC | Qz.PSAC | Qz.PSAC_KEEP)
+    assert np.array_equal(full["idx"], kept["idx"]) and np.array_equal(full["q"], kept["q"])
+    info = kept["keep"]
+    w64 = np.asarray(wt, np.float32).astype(np.float64)
+    mu = np.asarray(C, np.float64)[np.asarray(full["idx"], np.int64)]
+    E = K - (mu + full["r_hat"])
+    D = (full["c_scale"][:, None] * full["Cq"].astype(np.float64)) @ np.asarray(U, np.float64).T
+    err_with = np.sum(w64 * (E - D) ** 2, axis=1)
+    err_without = np.sum(w64 * E ** 2, axis=1)
+    np.testing.assert_allclose(info["crit"], err_with - err_without, rtol=1e-9, atol=1e-9 * err_without.max())
+    assert np.array_equal(info["keep"], err_with < err_without)
+    # dropped tokens store zeros; kept ones their coefficients unchanged
+    assert np.all(kept["Cq"][~info["keep"]] == 0) and np.all(kept["c_scale"][~info["keep"]] == 0)
+    assert np.array_equal(kept["Cq"][info["keep"]], full["Cq"][info["keep"]])
+    # the error with the stored coefficients never exceeds the uncompensated one
+    Dk = (kept["c_scale"][:, None] * kept["Cq"].astype(np.float64)) @ np.asarray(U, np.float64).T
+    assert np.all(np.sum(w64 * (E - Dk) ** 2, axis=1) <= err_without * (1 + 1e-12))
+    assert 0 < info["keep"].sum() < len(K) or info["keep"].all()
