@@ -325,7 +325,7 @@ def keys_bulk(qwm, torch, Kall, table, st):
             "GBps": round(byts / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
-def keys_keep_test(qwm, torch, Kall, table, st):
+def keys_keep_test(qwm, torch, Kall, table, st, chunk_tokens):
     """Bulk key quantization with the PSAC keep test (flags QSAC | PSAC | KEEP):
     time, and the fraction of tokens that keep their coefficients."""
     H = Kall.shape[1]
@@ -340,8 +340,23 @@ def keys_keep_test(qwm, torch, Kall, table, st):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / 3
-    kept = float((kb.c_scale != 0).float().mean().item())
-    return {"ms": round(ms, 4), "tokens_per_s": round(Kall.shape[0] / (ms * 1e-3), 1), "kept_fraction": round(kept, 4)}
+    keep = (kb.c_scale != 0)
+    kept = float(keep.float().mean().item())
+    # per (chunk, head) coefficient storage: the smaller of the dense and sparse layouts
+    T = Kall.shape[0]
+    n_ch = T // chunk_tokens
+    counts = keep[:, : n_ch * chunk_tokens].reshape(H, n_ch, chunk_tokens).sum(dim=2).cpu().tolist()
+    dense = sparse_or_dense = 0
+    n_sparse = 0
+    for row in counts:
+        for k in row:
+            lay = qwm.coefficient_layout(chunk_tokens, int(k))
+            dense += lay["dense"]
+            sparse_or_dense += lay["bytes"]
+            n_sparse += lay["layout"] == "sparse"
+    return {"ms": round(ms, 4), "tokens_per_s": round(Kall.shape[0] / (ms * 1e-3), 1), "kept_fraction": round(kept, 4),
+            "coefficient_bytes": {"dense": int(dense), "chosen": int(sparse_or_dense),
+                                  "sparse_chunks": int(n_sparse), "chunks": int(n_ch * H)}}
 
 
 def keys_m_sweep(qwm, torch, Kall, table, st, Ms=(4, 8, 16, 256)):
@@ -509,7 +524,7 @@ def run_stream_or_pass(args, qwm, torch, w):
                                                step.st)
             res["prq_codec"] = prq_codec(qwm, torch, step.K[step.sl_new])
             res["keys_keep_test"] = keys_keep_test(qwm, torch, step.K[: (step.nch - 1) * step.chunk], step.prev[0],
-                                                   step.st)
+                                                   step.st, step.chunk)
     else:
         res["keys_bulk"] = keys_bulk(qwm, torch, step.K, step.Ck, step.st)
     res["wall_s_timed"] = round(wall, 3)

@@ -200,6 +200,17 @@ def prq_quantize(x: torch.Tensor, stages: int, iters: int = 10, seed: int = 0):
     return first, C_last, quantize_values(e, C_last)
 
 
+def coefficient_layout(T: int, kept: int, r: int = R) -> dict:
+    """Bytes of one (chunk, head)'s PSAC coefficients in the dense layout (every
+    token: r INT8 + fp16 scale) and the sparse one (4-byte count, then each kept
+    token's 16-bit index -- 32-bit past 65,536 tokens -- coefficients and
+    scale); the cache keeps the smaller."""
+    dense = T * (r + 2)
+    sparse = 4 + kept * ((2 if T <= 65536 else 4) + r + 2)
+    return {"dense": dense, "sparse": sparse, "layout": "sparse" if sparse < dense else "dense",
+            "bytes": min(dense, sparse)}
+
+
 def _segment(kp, vp, kc, vc, U) -> Segment:
     s = Segment()
     s.k_codes, s.k_idx, s.k_scale, s.k_zeros = (kp.codes.data_ptr(), kp.idx.data_ptr(),
