@@ -40,6 +40,7 @@ GROUP = 64
 QSAC = 1
 PSAC = 2
 PSAC_KEEP = 4   # the PSAC keep test (QuantWM method step (4))
+QSAC_FULL = 8   # QSAC candidates by the full Query second-moment matrix (QuantWM App. C.4 ablation)
 
 
 def weighted_dists(K: np.ndarray, C: np.ndarray, w: np.ndarray, block: int = 64) -> np.ndarray:
@@ -52,6 +53,27 @@ def weighted_dists(K: np.ndarray, C: np.ndarray, w: np.ndarray, block: int = 64)
         diff = K[s:s + block, None, :] - C[None, :, :]
         out[s:s + block] = np.sum(diff * diff * w, axis=2)
     return out
+
+
+def full_dists(K: np.ndarray, C: np.ndarray, Mq: np.ndarray, block: int = 32) -> np.ndarray:
+    """d_full [T][n_c] = (k - mu)^T Mq (k - mu) in float64, direct form: the
+    quadratic form that the full-matrix ablation of QSAC (QuantWM App. C.4)
+    puts in place of the diagonal-weighted distance."""
+    K = np.asarray(K, np.float64)
+    C = np.asarray(C, np.float64)
+    Mq = np.asarray(Mq, np.float64)
+    out = np.empty((K.shape[0], C.shape[0]))
+    for s in range(0, K.shape[0], block):
+        diff = K[s:s + block, None, :] - C[None, :, :]
+        out[s:s + block] = np.sum((diff @ Mq) * diff, axis=2)
+    return out
+
+
+def second_moment(S: np.ndarray, n: int) -> np.ndarray:
+    """M_h = S_h / n_h, the mean of q q^T (identity before any Query, the
+    cold start's w = 1)."""
+    S = np.asarray(S, np.float64)
+    return S / float(n) if n > 0 else np.eye(S.shape[0])
 
 
 def residual(k32: np.ndarray, mu: np.ndarray) -> np.ndarray:
@@ -124,14 +146,19 @@ def psac_keep(E: np.ndarray, Cq: np.ndarray, cs: np.ndarray, U_bf16: np.ndarray,
     return crit < 0.0, crit, np.sum(w * E * E, axis=1)
 
 
-def select_qsac(K: np.ndarray, C: np.ndarray, w: np.ndarray, M: int):
+def select_qsac(K: np.ndarray, C: np.ndarray, w: np.ndarray, M: int, Mq: np.ndarray | None = None):
     """QSAC: top-M candidates by (d_Q, j), then argmin by (S, j).
+
+    With Mq (the full Query second-moment matrix, App. C.4 ablation) the
+    candidates come from the quadratic form (k - mu)^T Mq (k - mu) instead of
+    d_Q; the score S keeps the diagonal weights w (the rest of the pipeline is
+    unchanged in that ablation).
 
     Returns idx [T] and the per-token score table used (for diagnostics):
     dict(dq [T][n_c], cand [T][M], S [T][M]).
     """
     K = np.asarray(K)
-    dq = weighted_dists(K, C, w)
+    dq = weighted_dists(K, C, w) if Mq is None else full_dists(K, C, Mq)
     cand = np.argsort(dq, axis=1, kind="stable")[:, :M]
     W = np.asarray(w, np.float64).reshape(-1, GROUP).sum(axis=1)
     k32 = np.asarray(K, np.float32)
@@ -156,7 +183,7 @@ def select_nearest(X: np.ndarray, C: np.ndarray):
 
 
 def quantize_keys(K: np.ndarray, C: np.ndarray, w: np.ndarray | None, U_bf16: np.ndarray | None,
-                  M: int = 8, flags: int = QSAC | PSAC) -> dict:
+                  M: int = 8, flags: int = QSAC | PSAC, Mq: np.ndarray | None = None) -> dict:
     """One head: K [T][d] (bf16- or fp32-valued), centroid table C [n_c][d]
     (bf16-valued), w [d] float32 or None (w = 1), U_bf16 [d][r] or None (no PSAC).
 
@@ -164,13 +191,19 @@ def quantize_keys(K: np.ndarray, C: np.ndarray, w: np.ndarray | None, U_bf16: np
     nearest centroid (w is then ignored).  flags & PSAC with a basis: PSAC
     coefficients; otherwise C = 0.  flags & PSAC_KEEP: the keep test drops the
     coefficients (C = 0, c_s = 0) of tokens they do not help, with the channel
-    weights of the centroid choice (w under QSAC, else 1).
+    weights of the centroid choice (w under QSAC, else 1).  flags & QSAC_FULL
+    (with QSAC): candidates by the full matrix Mq [d][d] (second_moment()).
     """
     K = np.asarray(K, np.float64)
     T, d = K.shape
     if flags & QSAC:
         ww = np.ones(d, np.float32) if w is None else np.asarray(w, np.float32)
-        idx, info = select_qsac(K, C, ww, M)
+        if flags & QSAC_FULL:
+            if Mq is None:
+                raise ValueError("QSAC_FULL needs the second-moment matrix Mq")
+            idx, info = select_qsac(K, C, ww, M, Mq=Mq)
+        else:
+            idx, info = select_qsac(K, C, ww, M)
     else:
         idx, dq = select_nearest(K, C)
         info = {"dq": dq}

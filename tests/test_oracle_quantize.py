@@ -281,3 +281,80 @@ def test_psac_keep_test():
     Dk = (kept["c_scale"][:, None] * kept["Cq"].astype(np.float64)) @ np.asarray(U, np.float64).T
     assert np.all(np.sum(w64 * (E - Dk) ** 2, axis=1) <= err_without * (1 + 1e-12))
     assert 0 < info["keep"].sum() < len(K) or info["keep"].all()
+
+
+# ---- full-matrix candidate distance (QuantWM App. C.4 ablation) ----
+
+def _spd(rng, d=128, rank=12):
+    A = rng.standard_normal((d, rank))
+    return A @ A.T / rank + 0.05 * np.eye(d)
+
+
+def test_full_distance_is_scipy_mahalanobis():
+    rng = np.random.default_rng(11)
+    K = bf16_rne(rng.standard_normal((15, 128)))
+    C = _table(rng)
+    Mq = _spd(rng)
+    ref = cdist(K, C, "mahalanobis", VI=Mq) ** 2
+    np.testing.assert_allclose(Qz.full_dists(K, C, Mq), ref, rtol=1e-11)
+
+
+def test_full_form_golden_correlation_flips_candidate():
+    # k = 0, mu_0 = e_0 + e_1, mu_1 = e_0 - e_1; Mq = I except Mq[0,1] = Mq[1,0] = 1/2.
+    # Diagonal form (w = diag Mq = 1): both at 2, tie -> index 0.  Full form:
+    # (e_0 + e_1)^T Mq (e_0 + e_1) = 2 + 2(1/2) = 3, (e_0 - e_1)^T Mq (e_0 - e_1) = 2 - 1 = 1 -> index 1.
+    K = np.zeros((1, 128))
+    C = np.zeros((2, 128))
+    C[0, 0], C[0, 1] = 1.0, 1.0
+    C[1, 0], C[1, 1] = 1.0, -1.0
+    Mq = np.eye(128)
+    Mq[0, 1] = Mq[1, 0] = 0.5
+    np.testing.assert_array_equal(Qz.full_dists(K, C, Mq)[0], [3.0, 1.0])
+    w = np.ones(128, np.float32)
+    assert Qz.select_qsac(K, C, w, M=1)[0][0] == 0
+    assert Qz.select_qsac(K, C, w, M=1, Mq=Mq)[0][0] == 1
+    out = Qz.quantize_keys(K, C, w, None, M=1, flags=Qz.QSAC | Qz.QSAC_FULL, Mq=Mq)
+    assert out["idx"][0] == 1
+
+
+def test_full_form_with_diagonal_matrix_is_diagonal_qsac():
+    w8 = datagen.make_workload("480p", heads=[0], n_chunks=2, chunk=400)
+    K = w8.K[400:, 0].astype(np.float64)
+    C = lloyd.lloyd(w8.K[:400, 0].astype(np.float64), 256, 2, seed=3, head=0)
+    S, n = stats.update(np.zeros((128, 128)), 0, w8.Q[:400, 0])
+    wt = stats.channel_weights(S, n)
+    a, ia = Qz.select_qsac(K, C, wt, 8)
+    b, ib = Qz.select_qsac(K, C, wt, 8, Mq=np.diag(wt.astype(np.float64)))
+    np.testing.assert_allclose(ib["dq"], ia["dq"], rtol=1e-13)
+    np.testing.assert_array_equal(np.sort(ib["cand"], axis=1), np.sort(ia["cand"], axis=1))
+    np.testing.assert_array_equal(a, b)
+
+
+def test_full_form_rotation_invariance():
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((10, 128))
+    C = rng.standard_normal((12, 128))
+    Mq = _spd(rng)
+    Qm, _ = np.linalg.qr(rng.standard_normal((128, 128)))
+    d0 = Qz.full_dists(K, C, Mq)
+    d1 = Qz.full_dists(K @ Qm.T, C @ Qm.T, Qm @ Mq @ Qm.T)
+    np.testing.assert_allclose(d1, d0, rtol=1e-9)
+
+
+def test_full_form_all_candidates_is_score_argmin():
+    # with M = n_c every centroid is a candidate: the choice is argmin (S, j)
+    # whatever the distance
+    rng = np.random.default_rng(2)
+    K = bf16_rne(rng.standard_normal((30, 128)))
+    C = _table(rng)
+    wt = rng.uniform(0.2, 3.0, 128).astype(np.float32)
+    a = Qz.select_qsac(K, C, wt, C.shape[0])[0]
+    b = Qz.select_qsac(K, C, wt, C.shape[0], Mq=_spd(rng))[0]
+    np.testing.assert_array_equal(a, b)
+
+
+def test_second_moment_cold_start_and_mean():
+    Q = np.arange(12.0).reshape(3, 4)
+    S = Q.T @ Q
+    np.testing.assert_array_equal(Qz.second_moment(S, 3), S / 3.0)
+    np.testing.assert_array_equal(Qz.second_moment(np.zeros((4, 4)), 0), np.eye(4))
