@@ -156,6 +156,25 @@ def quantize_keys(k: torch.Tensor, centroids: torch.Tensor, w: torch.Tensor | No
     return out
 
 
+def quantize_keys_fullq(k: torch.Tensor, centroids: torch.Tensor, S: torch.Tensor, n: torch.Tensor,
+                        w: torch.Tensor | None, U: torch.Tensor | None, M: int = 8,
+                        flags: int = QWM_QSAC | QWM_PSAC, out: PackedChunk | None = None,
+                        diag: torch.Tensor | None = None) -> PackedChunk:
+    """QSAC with candidates by the full Query second-moment matrix S / n
+    (S [H, 128, 128] fp64, n [H] int64, as QueryStats keeps them)."""
+    td = _tokens(k)
+    if S.dtype != torch.float64 or tuple(S.shape) != (td.H, D, D) or not S.is_contiguous():
+        raise ValueError("S must be a contiguous [H, 128, 128] float64 tensor")
+    if n.dtype != torch.int64 or tuple(n.shape) != (td.H,):
+        raise ValueError("n must be an [H] int64 tensor")
+    if out is None:
+        out = PackedChunk(td.T, td.H, True, k.device)
+    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_KEYS, td.T, td.H, 0, 0), k.device)
+    check(lib.qwm_quantize_keys_fullq(C.byref(td), _ptr(centroids), _ptr(S), _ptr(n), _ptr(w), _ptr(U), M, flags,
+                                      C.byref(out.desc()), _ptr(diag), ws, nb, _stream()))
+    return out
+
+
 def quantize_values(v: torch.Tensor, centroids: torch.Tensor, out: PackedChunk | None = None,
                     diag: torch.Tensor | None = None) -> PackedChunk:
     td = _tokens(v)

@@ -13,8 +13,8 @@ QWM_QSAC, QWM_PSAC, QWM_PSAC_KEEP = 1, 2, 4
 QWM_OP_STATS, QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION, QWM_OP_ATTENTION_ACTIVE = 0, 1, 2, 3, 4, 5
 
 # every symbol include/quantwm.h declares
-EXPORTS = ["qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys", "qwm_quantize_values",
-           "qwm_attention", "qwm_attention_active", "qwm_decode_segment", "qwm_centroid_residual", "qwm_reference_top1", "qwm_workspace_bytes", "qwm_zeros_stride", "qwm_last_error", "qwm_abi_version"]
+EXPORTS = ["qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys", "qwm_quantize_keys_fullq",
+           "qwm_quantize_values", "qwm_attention", "qwm_attention_active", "qwm_decode_segment", "qwm_centroid_residual", "qwm_reference_top1", "qwm_workspace_bytes", "qwm_zeros_stride", "qwm_last_error", "qwm_abi_version"]
 
 
 class Tokens(C.Structure):
@@ -55,6 +55,7 @@ def _load():
     L.qwm_update_query_stats.argtypes = [P, P, C.c_int32, P, C.c_size_t, P]
     L.qwm_build_centroids.argtypes = [P, C.c_int32, C.c_int32, C.c_uint64, P, P, P, P, C.c_size_t, P]
     L.qwm_quantize_keys.argtypes = [P, P, P, P, C.c_int32, C.c_uint32, P, P, P, C.c_size_t, P]
+    L.qwm_quantize_keys_fullq.argtypes = [P, P, P, P, P, P, C.c_int32, C.c_uint32, P, P, P, C.c_size_t, P]
     L.qwm_quantize_values.argtypes = [P, P, P, P, P, C.c_size_t, P]
     L.qwm_attention.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, C.c_size_t, P]
     L.qwm_attention_active.argtypes = [P, P, C.c_int32, C.c_int64, P, P, C.c_float, P, P, P, P, C.c_size_t, P]
@@ -67,7 +68,7 @@ def _load():
     L.qwm_zeros_stride.restype = C.c_int64
     L.qwm_last_error.restype = C.c_char_p
     L.qwm_abi_version.restype = C.c_int32
-    for name in ("qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys",
+    for name in ("qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys", "qwm_quantize_keys_fullq",
                  "qwm_quantize_values", "qwm_attention", "qwm_attention_active", "qwm_decode_segment",
                  "qwm_centroid_residual"):
         getattr(L, name).restype = C.c_int

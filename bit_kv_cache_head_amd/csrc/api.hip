@@ -27,6 +27,9 @@ qwm_status launch_stats(const qwm_tokens* q, const qwm_qstats* st, int32_t compu
 qwm_status launch_keys(const qwm_tokens* k, const uint16_t* centroids, const float* w, const uint16_t* U,
                        int32_t M, uint32_t flags, const qwm_packed* out, qwm_diag* diag, void* ws,
                        hipStream_t stream);
+qwm_status launch_keys_full(const qwm_tokens* k, const uint16_t* centroids, const double* S, const int64_t* n,
+                            const float* w, const uint16_t* U, int32_t M, uint32_t flags, const qwm_packed* out,
+                            qwm_diag* diag, void* ws, hipStream_t stream);
 qwm_status launch_values(const qwm_tokens* v, const uint16_t* centroids, const qwm_packed* out, qwm_diag* diag,
                          void* ws, hipStream_t stream);
 qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const uint16_t* init, uint16_t* centroids,
@@ -158,6 +161,27 @@ qwm_status qwm_quantize_keys(const qwm_tokens* k, const uint16_t* centroids, con
   if (s != QWM_OK) return s;
   return launch_keys(k, centroids, w, U, (flags & QWM_QSAC) ? M : 1, flags, out, diag, ws,
                      static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_quantize_keys_fullq(const qwm_tokens* k, const uint16_t* centroids, const double* S,
+                                   const int64_t* n, const float* w, const uint16_t* U, int32_t M, uint32_t flags,
+                                   const qwm_packed* out, qwm_diag* diag, void* ws, size_t ws_bytes,
+                                   qwm_stream stream) {
+  qwm_status s = check_tokens(k, "keys", false);
+  if (s != QWM_OK) return s;
+  if (!centroids || !aligned(centroids, 16)) return fail(QWM_ERR_ARG, "centroids: null or not 16-byte aligned");
+  if (!S || !n || !aligned(S, 8) || !aligned(n, 8)) return fail(QWM_ERR_ARG, "S / n: null or misaligned");
+  if (flags & ~(uint32_t)(QWM_QSAC | QWM_PSAC | QWM_PSAC_KEEP)) return fail(QWM_ERR_ARG, "unknown flag bits");
+  if (!(flags & QWM_QSAC)) return fail(QWM_ERR_ARG, "the full-matrix distance is a QSAC variant: set QWM_QSAC");
+  if (M < 1 || M > qwm::NC) return fail(QWM_ERR_ARG, "M must be in [1, 256]");
+  if (w && !aligned(w, 4)) return fail(QWM_ERR_ARG, "w misaligned");
+  if (U && !aligned(U, 16)) return fail(QWM_ERR_ARG, "U not 16-byte aligned");
+  if (diag && !aligned(diag, 8)) return fail(QWM_ERR_ARG, "diag misaligned");
+  s = check_packed(out, k, true, (flags & QWM_PSAC) && U);
+  if (s != QWM_OK) return s;
+  s = check_ws(ws, ws_bytes, select_ws_bytes(k->T, k->H, false));
+  if (s != QWM_OK) return s;
+  return launch_keys_full(k, centroids, S, n, w, U, M, flags, out, diag, ws, static_cast<hipStream_t>(stream));
 }
 
 qwm_status qwm_quantize_values(const qwm_tokens* v, const uint16_t* centroids, const qwm_packed* out,

@@ -98,6 +98,8 @@ struct SelectArgs {
   uint8_t* codes; uint16_t* scale; uint8_t* zeros; int64_t zstride; int8_t* cq; uint16_t* cscale;
   int32_t* counter; int32_t* worklist;
   qwm_diag* diag;
+  // full-matrix candidate distance: S [H][128][128] fp64, n [H], mu^T S mu [H][256]
+  const double* qS; const int64_t* qn; const double* qB;
 };
 
 struct SelShared {
@@ -737,19 +739,37 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
 // Exact path for the tokens the fast path did not certify: plain fp64 scoring
 // of all centroids, one wave per token.
 // ---------------------------------------------------------------------------
-template <int MODE, bool F32>
+// FULL: the full-matrix ablation of QSAC (QuantWM App. C.4): every token of
+// head blockIdx.y (no worklist), candidates by the quadratic form
+// (k - mu)^T S (k - mu) with S the head's Query second-moment sum (the
+// positive factor 1 / n does not change the order; S = I before any Query),
+// expanded as k^T S k - 2 (S k) . mu + mu^T S mu with the last term from
+// fullq_bj_kernel; S sits in LDS for the whole block.
+template <int MODE, bool F32, bool FULL = false>
 __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   __shared__ double kx[4][D];
   __shared__ double wx[4][D];
   __shared__ double dq[4][NC];
-  const int count = *a.counter;
-  if (blockIdx.x == 0 && tid == 0 && a.diag && count > 0)
-    atomicAdd((unsigned long long*)&a.diag->exact_fallbacks, (unsigned long long)count);
+  __shared__ double sq[FULL ? D * D : 1];   // S [c][r]
+  __shared__ double tq[FULL ? 4 : 1][D];    // S k
+  int count;
+  if constexpr (FULL) {
+    const int hb = blockIdx.y;
+    const bool cold = a.qn[hb] <= 0;
+    const double* Sh = a.qS + (int64_t)hb * D * D;
+    for (int e = tid; e < D * D; e += 256) sq[e] = cold ? ((e / D == e % D) ? 1.0 : 0.0) : Sh[e];
+    __syncthreads();
+    count = (int)a.T;
+  } else {
+    count = *a.counter;
+    if (blockIdx.x == 0 && tid == 0 && a.diag && count > 0)
+      atomicAdd((unsigned long long*)&a.diag->exact_fallbacks, (unsigned long long)count);
+  }
   const bool use_qsac = (MODE == MODE_KEYS) && (a.flags & QWM_QSAC);
   const bool use_psac = (MODE == MODE_KEYS) && (a.flags & QWM_PSAC) && a.U != nullptr;
   for (int item = blockIdx.x * 4 + wv; item < count; item += gridDim.x * 4) {
-    const int64_t id = a.worklist[item];
+    const int64_t id = FULL ? (int64_t)blockIdx.y * a.T + item : (int64_t)a.worklist[item];
     const int h = (int)(id / a.T);
     const int64_t tok = id % a.T;
     const int64_t rowoff = (int64_t)h * a.sh + tok * a.st;
@@ -791,10 +811,43 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
     wx[wv][2 * lane + 1] = wts ? (double)a.w[h * D + 2 * lane + 1] : 1.0;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if constexpr (FULL) {
+      // t = S k (S symmetric: lane r reads column entries S[c][r], conflict-free)
+      double t0 = 0.0, t1 = 0.0;
+      for (int c = 0; c < D; ++c) {
+        const double kc = kx[wv][c];
+        t0 = fma(sq[c * D + lane], kc, t0);
+        t1 = fma(sq[c * D + lane + 64], kc, t1);
+      }
+      tq[wv][lane] = t0;
+      tq[wv][lane + 64] = t1;
+      const double kSk = wave_sum_d(kx[wv][lane] * t0 + kx[wv][lane + 64] * t1);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const u32x4* mrow = reinterpret_cast<const u32x4*>(a.mu + ((int64_t)h * NC + lane) * D);
+      double s[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+      for (int c8 = 0; c8 < D / 8; ++c8) {
+        double tt[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tt[e] = tq[wv][8 * c8 + e];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 v = mrow[q * 64 * (D / 8) + c8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t wd = v[e >> 1];
+            const double m = (double)((e & 1) ? __uint_as_float(wd & 0xFFFF0000u) : __uint_as_float(wd << 16));
+            s[q] = fma(tt[e], m, s[q]);
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dq[wv][lane + 64 * q] = kSk - 2.0 * s[q] + a.qB[h * NC + lane + 64 * q];
+    } else {
     // d_Q for centroids lane + 64 q, direct form in fp64.  Channels outer (one
     // 8-channel slice of k and w at a time), the four centroids inner, so the
     // token never has to live in registers as a whole.
-    {
       const u32x4* mrow = reinterpret_cast<const u32x4*>(a.mu + ((int64_t)h * NC + lane) * D);
       double s[4] = {0.0, 0.0, 0.0, 0.0};
       // four channel slices per round trip: 16 table loads in flight
@@ -931,13 +984,15 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
         bool s2 = false;
         const uint32_t csb = fp16_up_div(m, 127.0f, &s2);
         const double cs = (double)f16_bits_to_f32(csb);
-        if (lane < R) {
+        // integer coefficients of every lane's view (all lanes need them for
+        // the keep test)
+        int cqi[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
           int qi = 0;
           if (cs > 0.0) {
             // round half to even of C / cs, decided with exact products (n +- 1/2) cs
-            double Ci = C[0];
-#pragma unroll
-            for (int i = 1; i < R; ++i) if (lane == i) Ci = C[i];
+            const double Ci = C[i];
             double n = rint(Ci / cs);
             if (Ci > (n + 0.5) * cs) n += 1.0;
             if (Ci < (n - 0.5) * cs) n -= 1.0;
@@ -946,15 +1001,74 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
             else if (Ci == (n - 0.5) * cs && (ni & 1)) ni -= 1;
             qi = ni < -127 ? -127 : (ni > 127 ? 127 : ni);
           }
-          cq[lane] = (int8_t)qi;
+          cqi[i] = qi;
         }
-        if (lane == 0) a.cscale[base] = (uint16_t)csb;
+        bool keep = true;
+        if (a.flags & QWM_PSAC_KEEP) {
+          // Keep test (QuantWM method step (4)): the coefficients stay only if
+          // the compensation D = (c_s C_q) U^T lowers the Query-weighted error
+          // sum_c w_c e_c^2 (weights of the centroid choice), i.e. iff
+          // sum_c w_c D_c (D_c - 2 e_c) < 0; here in fp64
+          double D0 = 0.0, D1 = 0.0;
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            const double ci = cs * (double)cqi[i];
+            D0 += ci * (double)bf16_bits_to_f32(Uh[(2 * lane) * R + i]);
+            D1 += ci * (double)bf16_bits_to_f32(Uh[(2 * lane + 1) * R + i]);
+          }
+          const double crit = wave_sum_d(wx[wv][2 * lane] * D0 * (D0 - 2.0 * e0) +
+                                         wx[wv][2 * lane + 1] * D1 * (D1 - 2.0 * e1));
+          keep = crit < 0.0;
+        }
+        if (lane < R) {
+          int qi = cqi[0];
+#pragma unroll
+          for (int i = 1; i < R; ++i) if (lane == i) qi = cqi[i];
+          cq[lane] = keep ? (int8_t)qi : (int8_t)0;
+        }
+        if (lane == 0) a.cscale[base] = keep ? (uint16_t)csb : (uint16_t)0;
       } else {
         if (lane < R) cq[lane] = 0;
         if (lane == 0) a.cscale[base] = 0;
       }
     }
   }
+}
+
+// mu_j^T S mu_j in fp64 for the full-matrix candidate distance: grid (H, NC / 4),
+// one wave per centroid; lane r forms (S mu)_r for r = lane, lane + 64 from
+// the column entries S[c][r] (S symmetric; S = I while n = 0).
+__global__ __launch_bounds__(256) void fullq_bj_kernel(const uint16_t* __restrict__ mu, const double* __restrict__ S,
+                                                       const int64_t* __restrict__ n, double* __restrict__ B) {
+  const int h = blockIdx.x, lane = threadIdx.x & 63, j = blockIdx.y * 4 + (threadIdx.x >> 6);
+  __shared__ double m[4][D];
+  const int wv = threadIdx.x >> 6;
+  const uint16_t* row = mu + ((int64_t)h * NC + j) * D;
+  const double m0 = bf16_bits_to_f32(row[lane]), m1 = bf16_bits_to_f32(row[lane + 64]);
+  m[wv][lane] = m0;
+  m[wv][lane + 64] = m1;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  double v;
+  if (n[h] <= 0) {
+    v = m0 * m0 + m1 * m1;
+  } else {
+    const double* Sh = S + (int64_t)h * D * D;
+    double t0 = 0.0, t1 = 0.0;
+    for (int c = 0; c < D; ++c) {
+      const double mc = m[wv][c];
+      t0 = fma(Sh[c * D + lane], mc, t0);
+      t1 = fma(Sh[c * D + lane + 64], mc, t1);
+    }
+    v = m0 * t0 + m1 * t1;
+  }
+  const double b = wave_sum_d(v);
+  if (lane == 0) B[h * NC + j] = b;
+}
+
+// Clears n bytes (the zero-point nibbles that the exact kernel ORs into place).
+__global__ __launch_bounds__(256) void clear_bytes_kernel(uint8_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1152,7 +1266,7 @@ namespace qwm_host {
 using namespace qwm;
 
 struct SelWork {
-  uint16_t* aug; float* Bj; float* Bmax; double* Wg; int32_t* counter; int32_t* worklist;
+  uint16_t* aug; float* Bj; float* Bmax; double* Wg; int32_t* counter; int32_t* worklist; double* qB;
   uint8_t* assign; int32_t* perm; int32_t* start;
 };
 
@@ -1166,6 +1280,7 @@ size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd) {
   b += align256((size_t)H * 2 * 8);
   b += align256(16);
   b += align256((size_t)H * T * 4);
+  b += align256((size_t)H * NC * 8);
   if (lloyd) {
     b += align256((size_t)H * T);
     b += align256((size_t)H * T * 4);
@@ -1184,6 +1299,7 @@ static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd) {
   w.Wg = reinterpret_cast<double*>(take((size_t)H * 2 * 8));
   w.counter = reinterpret_cast<int32_t*>(take(16));
   w.worklist = reinterpret_cast<int32_t*>(take((size_t)H * T * 4));
+  w.qB = reinterpret_cast<double*>(take((size_t)H * NC * 8));
   if (lloyd) {
     w.assign = reinterpret_cast<uint8_t*>(take((size_t)H * T));
     w.perm = reinterpret_cast<int32_t*>(take((size_t)H * T * 4));
@@ -1279,6 +1395,38 @@ qwm_status launch_keys(const qwm_tokens* k, const uint16_t* centroids, const flo
   a.idx = out->idx; a.codes = out->codes; a.scale = out->scale; a.zeros = out->zeros;
   a.zstride = zeros_stride(k->T); a.cq = out->c; a.cscale = out->c_scale; a.diag = diag;
   return run_select<MODE_KEYS>(k, a, stream, "key quantization");
+}
+
+// The full-matrix ablation: S-weighted candidates for every token on the
+// exact fp64 path (one wave per token, 4 per block, one head per grid row).
+qwm_status launch_keys_full(const qwm_tokens* k, const uint16_t* centroids, const double* S, const int64_t* n,
+                            const float* w, const uint16_t* U, int32_t M, uint32_t flags, const qwm_packed* out,
+                            qwm_diag* diag, void* ws, hipStream_t stream) {
+  SelWork wk = carve(ws, k->T, k->H, false);
+  qwm_status s = prep(wk, centroids, w, k->H, stream);
+  if (s != QWM_OK) return s;
+  hipLaunchKernelGGL(fullq_bj_kernel, dim3(k->H, NC / 4), dim3(256), 0, stream, centroids, S, n, wk.qB);
+  s = check_launch("full-matrix centroid terms");
+  if (s != QWM_OK) return s;
+  const int64_t zb = (int64_t)k->H * zeros_stride(k->T);
+  const int64_t zblocks = (zb + 255) / 256;
+  hipLaunchKernelGGL(clear_bytes_kernel, dim3((unsigned)(zblocks < 1024 ? (zblocks > 0 ? zblocks : 1) : 1024)),
+                     dim3(256), 0, stream, out->zeros, zb);
+  s = check_launch("zero-point clear");
+  if (s != QWM_OK) return s;
+  SelectArgs a{};
+  fill_common(a, k, wk, centroids);
+  a.w = w; a.U = (flags & QWM_PSAC) ? U : nullptr; a.M = M; a.flags = flags;
+  a.idx = out->idx; a.codes = out->codes; a.scale = out->scale; a.zeros = out->zeros;
+  a.zstride = zeros_stride(k->T); a.cq = out->c; a.cscale = out->c_scale; a.diag = diag;
+  a.qS = S; a.qn = n; a.qB = wk.qB;
+  const int64_t per = (k->T + 3) / 4;
+  const dim3 grid((unsigned)(per < 64 ? (per > 0 ? per : 1) : 64), (unsigned)k->H);
+  if (k->dtype == QWM_BF16)
+    hipLaunchKernelGGL((fallback_kernel<MODE_KEYS, false, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fallback_kernel<MODE_KEYS, true, true>), grid, dim3(256), 0, stream, a);
+  return check_launch("full-matrix key quantization");
 }
 
 qwm_status launch_values(const qwm_tokens* v, const uint16_t* centroids, const qwm_packed* out, qwm_diag* diag,

@@ -167,6 +167,22 @@ qwm_status qwm_quantize_keys(const qwm_tokens* k, const uint16_t* centroids, con
                              const uint16_t* U, int32_t M, uint32_t flags, const qwm_packed* out,
                              qwm_diag* diag, void* ws, size_t ws_bytes, qwm_stream stream);
 
+/* The full-matrix ablation of QSAC (QuantWM App. C.4): as qwm_quantize_keys
+ * with QWM_QSAC set, except that the M candidates are the M smallest by
+ * ((k - mu)^T M_h (k - mu), index), M_h = S_h / n_h the Query second-moment
+ * matrix (S [H][128][128] fp64 and n [H] int64 as qwm_update_query_stats keeps
+ * them; M_h = I while n_h = 0).  The score S = sum_g W_g R_g^2, the codec, PSAC
+ * and the keep test keep the diagonal weights w, as in that ablation.  Every
+ * token takes the exact fp64 path (expanded form k^T S k - 2 (S k).mu + mu^T S mu),
+ * so the call is much slower than the diagonal one; candidates whose quadratic
+ * forms agree to about 1e-12 relative may order differently from a direct-form
+ * evaluation.  flags: QWM_QSAC required; QWM_PSAC, QWM_PSAC_KEEP as above.
+ * Workspace: QWM_OP_KEYS. */
+qwm_status qwm_quantize_keys_fullq(const qwm_tokens* k, const uint16_t* centroids, const double* S,
+                                   const int64_t* n, const float* w, const uint16_t* U, int32_t M,
+                                   uint32_t flags, const qwm_packed* out, qwm_diag* diag, void* ws,
+                                   size_t ws_bytes, qwm_stream stream);
+
 /* Quantize one chunk of Values: nearest centroid plus the INT2 codec above,
  * no compensation (QuantWM Sec. 2 centroid-residual code; PSAC is Key-only).
  * Workspace: QWM_OP_VALUES. */

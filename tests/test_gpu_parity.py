@@ -148,7 +148,8 @@ def _key_inputs(name, T, heads, seed=5):
     return w, K, np.stack(tables), np.stack(ws), np.stack(Us)
 
 
-@pytest.mark.parametrize("flags,M", [(3, 8), (1, 8), (2, 8), (0, 8), (3, 1), (3, 4), (3, 16), (3, 256), (7, 8), (6, 8)])
+@pytest.mark.parametrize("flags,M", [(3, 8), (1, 8), (2, 8), (0, 8), (3, 1), (3, 4), (3, 16), (3, 256), (7, 8), (6, 8),
+                                     (7, 16), (7, 256)])
 def test_quantize_keys(qwm, flags, M):
     import torch
     from gpu_helpers import dev_tokens, dev_table, dev_basis, packed_host, idx_mismatches_allowed, compare_codec
@@ -203,6 +204,126 @@ def test_quantize_keys(qwm, flags, M):
         else:
             assert np.all(g["c"][h] == 0) and np.all(g["c_scale_bits"][h] == 0)
     _log(f"  idx near-tie mismatches {total_mis}, diag {diag.tolist()}")
+
+
+@pytest.mark.parametrize("flags,M", [(3, 8), (7, 4), (1, 1), (3, 256)])
+def test_quantize_keys_full_matrix(qwm, flags, M):
+    """QSAC candidates by the full Query second-moment matrix (App. C.4
+    ablation) against the oracle's direct quadratic form."""
+    import torch
+    from gpu_helpers import dev_tokens, dev_table, dev_basis, packed_host, idx_mismatches_allowed, compare_codec
+    _log(f"keys full-matrix flags={flags} M={M}")
+    T = 400
+    w, K, Ct, wt, Ut = _key_inputs("480p", T, [0, 1])
+    H = w.H
+    Ss, ns = [], []
+    for h in range(H):
+        S, n = OS.update(np.zeros((128, 128)), 0, w.Q[: min(T, w.Q.shape[0]), h])
+        Ss.append(S)
+        ns.append(n)
+    diag = qwm.new_diag()
+    out = qwm.quantize_keys_fullq(dev_tokens(K, "bf16"), dev_table(Ct), torch.from_numpy(np.stack(Ss)).cuda(),
+                                  torch.tensor(ns, dtype=torch.int64).cuda(), torch.from_numpy(wt).cuda(),
+                                  dev_basis(Ut), M=M, flags=flags, diag=diag)
+    torch.cuda.synchronize()
+    g = packed_host(out)
+    total_mis = 0
+    for h in range(H):
+        Mq = Qz.second_moment(Ss[h], ns[h])
+        o = Qz.quantize_keys(K[:, h].astype(np.float64), Ct[h], wt[h], Ut[h], M=M, flags=flags | Qz.QSAC_FULL, Mq=Mq)
+        nmis, nbad = idx_mismatches_allowed("qsac", o, g["idx"][h], K[:, h], Ct[h], w=wt[h], M=M)
+        assert nbad == 0, f"head {h}: {nbad} centroid choices differ beyond near-ties"
+        total_mis += nmis
+        same = o["idx"] == g["idx"][h]
+        compare_codec(o, {k: v[h] for k, v in g.items()}, T, same)
+        g_keep = (g["c_scale_bits"][h] != 0) | np.any(g["c"][h] != 0, axis=1)
+        if flags & 4:
+            # both sides decide the keep test in fp64 on coefficients within 1 LSB
+            full = Qz.quantize_keys(K[:, h].astype(np.float64), Ct[h], wt[h], Ut[h], M=M,
+                                    flags=(flags & ~4) | Qz.QSAC_FULL, Mq=Mq)
+            ki = o["keep"]
+            mu = np.asarray(Ct[h], np.float64)[np.asarray(o["idx"], np.int64)]
+            E = K[:, h].astype(np.float64) - (mu + o["r_hat"])
+            Ua = np.abs(np.asarray(Ut[h], np.float64))
+            cs = full["c_scale"]
+            D = (cs[:, None] * full["Cq"].astype(np.float64)) @ np.asarray(Ut[h], np.float64).T
+            wk = np.asarray(wt[h], np.float32).astype(np.float64)
+            tol = 2 * cs * np.sum(wk * Ua.sum(axis=1)[None, :] * (np.abs(D) + np.abs(E) + cs[:, None]), axis=1)
+            dis = same & (g_keep != ki["keep"])
+            assert np.all(np.abs(ki["crit"][dis]) <= tol[dis]), np.nonzero(dis)[0][:5]
+            same = same & (g_keep == ki["keep"])
+        if flags & 2:
+            dc = np.abs(g["c"][h].astype(np.int64) - o["Cq"].astype(np.int64))
+            assert dc[same].max() <= 1
+        else:
+            assert np.all(g["c"][h] == 0) and np.all(g["c_scale_bits"][h] == 0)
+        _log(f"  head {h}: idx differs from the diagonal form on "
+             f"{int(np.sum(o['idx'] != Qz.quantize_keys(K[:, h].astype(np.float64), Ct[h], wt[h], None, M=M, flags=1)['idx']))} tokens")
+    _log(f"  idx near-tie mismatches {total_mis}, diag {diag.tolist()}")
+
+
+def test_quantize_keys_full_matrix_cold_start(qwm):
+    """n = 0: M_h = I and w = 1, i.e. the Euclidean QSAC choice."""
+    import torch
+    from gpu_helpers import dev_tokens, dev_table, packed_host, idx_mismatches_allowed, compare_codec
+    T = 300
+    w, K, Ct, wt, Ut = _key_inputs("480p", T, [0, 1])
+    H = w.H
+    out = qwm.quantize_keys_fullq(dev_tokens(K, "bf16"), dev_table(Ct),
+                                  torch.zeros(H, 128, 128, dtype=torch.float64).cuda(),
+                                  torch.zeros(H, dtype=torch.int64).cuda(), None, None, M=8, flags=1)
+    torch.cuda.synchronize()
+    g = packed_host(out)
+    for h in range(H):
+        o = Qz.quantize_keys(K[:, h].astype(np.float64), Ct[h], None, None, M=8, flags=1)
+        nmis, nbad = idx_mismatches_allowed("qsac", o, g["idx"][h], K[:, h], Ct[h], None, 8)
+        assert nbad == 0
+        compare_codec(o, {k: v[h] for k, v in g.items()}, T, o["idx"] == g["idx"][h])
+
+
+@pytest.mark.parametrize("M", [8, 16])
+def test_quantize_keys_keep_rejections(qwm, M):
+    """The keep test where it rejects often: strongly non-uniform weights and a
+    random basis (not the weights' eigenvectors), so the compensation raises the
+    weighted error of about a fifth of the keys.  At M = 16 many tokens take the
+    exact fp64 path, which must apply the test too."""
+    import torch
+    from gpu_helpers import dev_tokens, dev_table, dev_basis, packed_host, idx_mismatches_allowed, compare_codec
+    T = 777
+    w, K, Ct, _, _ = _key_inputs("480p", T, [0, 1])
+    rng = np.random.default_rng(7)
+    wq = np.exp(rng.uniform(-3, 3, (2, 128))).astype(np.float32)
+    Ur = np.stack([F.bf16_rne(np.linalg.qr(rng.standard_normal((128, 8)))[0]) for _ in range(2)])
+    diag = qwm.new_diag()
+    out = qwm.quantize_keys(dev_tokens(K, "bf16"), dev_table(Ct), torch.from_numpy(wq).cuda(), dev_basis(Ur),
+                            M=M, flags=7, diag=diag)
+    torch.cuda.synchronize()
+    g = packed_host(out)
+    for h in range(2):
+        o = Qz.quantize_keys(K[:, h].astype(np.float64), Ct[h], wq[h], Ur[h], M=M, flags=7)
+        nmis, nbad = idx_mismatches_allowed("qsac", o, g["idx"][h], K[:, h], Ct[h], w=wq[h], M=M)
+        assert nbad == 0
+        same = o["idx"] == g["idx"][h]
+        compare_codec(o, {k: v[h] for k, v in g.items()}, T, same)
+        full = Qz.quantize_keys(K[:, h].astype(np.float64), Ct[h], wq[h], Ur[h], M=M, flags=3)
+        ki = o["keep"]
+        assert (~ki["keep"]).sum() > 50
+        g_keep = (g["c_scale_bits"][h] != 0) | np.any(g["c"][h] != 0, axis=1)
+        mu = np.asarray(Ct[h], np.float64)[np.asarray(o["idx"], np.int64)]
+        E = K[:, h].astype(np.float64) - (mu + o["r_hat"])
+        Ua = np.abs(np.asarray(Ur[h], np.float64))
+        cs = full["c_scale"]
+        D = (cs[:, None] * full["Cq"].astype(np.float64)) @ np.asarray(Ur[h], np.float64).T
+        wk = wq[h].astype(np.float64)
+        tol = (2 * cs * np.sum(wk * Ua.sum(axis=1)[None, :] * (np.abs(D) + np.abs(E) + cs[:, None]), axis=1)
+               + 2.0 ** -16 * np.sum(wk * (D * D + E * E), axis=1))
+        dis = same & (g_keep != ki["keep"])
+        assert np.all(np.abs(ki["crit"][dis]) <= tol[dis]), np.nonzero(dis)[0][:5]
+        agree = same & (g_keep == ki["keep"])
+        dc = np.abs(g["c"][h].astype(np.int64) - o["Cq"].astype(np.int64))
+        assert dc[agree].max() <= 1
+        _log(f"  M={M} head {h}: rejected {int((~ki['keep']).sum())}, decision near-ties {int(dis.sum())}, "
+             f"diag {diag.tolist()}")
 
 
 def test_quantize_keys_cold_start_and_fp32(qwm):
