@@ -233,6 +233,30 @@ __device__ __forceinline__ ResidStats resid_stats(const float (&kf)[64], const u
   return o;
 }
 
+// Group ranges alone (the QSAC score S needs no distance): r = fl32(k - mu_j),
+// lo/hi per 64-channel group, with the 0 the coded interval always holds.
+__device__ __forceinline__ ResidStats resid_ranges(const float (&kf)[64], const uint16_t* tab, int j, int hh) {
+  ResidStats o{0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const u32x4 mv = mu_chunk(tab, j, 2 * s + hh);
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t mw = mv[e >> 1];
+      const float r0 = kf[8 * s + e] - __uint_as_float(mw << 16);
+      const float r1 = kf[8 * s + e + 1] - __uint_as_float(mw & 0xFFFF0000u);
+      lo = fminf(fminf(lo, r0), r1);
+      hi = fmaxf(fmaxf(hi, r0), r1);
+    }
+    if (s < 4) { o.lo0 = fminf(o.lo0, lo); o.hi0 = fmaxf(o.hi0, hi); }
+    else { o.lo1 = fminf(o.lo1, lo); o.hi1 = fmaxf(o.hi1, hi); }
+  }
+  o.lo0 = lanepair_min(o.lo0); o.hi0 = lanepair_max(o.hi0);
+  o.lo1 = lanepair_min(o.lo1); o.hi1 = lanepair_max(o.hi1);
+  return o;
+}
+
 constexpr float DREL = 1.0f / 65536.0f;   // relative error bound of the fp32 rescored distance
 
 // QS: QSAC selection (keys with the QSAC flag and M > 1); otherwise nearest.
@@ -495,7 +519,9 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
         unt_out = L_unt > UbM;   // untracked centroids are all outside the M nearest
       }
       // score S for every possible member in ascending order of the GEMM value,
-      // skipping candidates whose distance bound already exceeds the best S (S >= d_Q)
+      // skipping candidates whose distance bound already exceeds the best S (S >= d_Q).
+      // S needs only the group ranges; the winner's exact distance is taken once,
+      // after the scan, for the membership test.
       double Sbest = __builtin_inf();
       float dwin = 0.f;
       // one slot per pass, always from position 0: Lb, jp and outmask rotate by
@@ -505,13 +531,12 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
         const bool need = fast && !(outmask & 1u) && ((double)Lb[0] <= Sbest * (1.0 + 1.0 / 1048576.0));
         if (__any(need)) {
           const int j = (int)(jp[0] & 0xFFu);
-          const ResidStats rs = resid_stats<WT>(kf, sm.mu, j, hh, sm.w);
+          const ResidStats rs = resid_ranges(kf, sm.mu, j, hh);
           if (need) {
-            Lb[0] = fmaxf(Lb[0], rs.d * (1.0f - DREL));
             const double R0 = (double)rs.hi0 - (double)rs.lo0, R1 = (double)rs.hi1 - (double)rs.lo1;
             const double S = W0 * R0 * R0 + W1 * R1 * R1;
             if (!have_w || S < Sbest || (S == Sbest && j < win)) {
-              Sbest = S; win = j; dwin = rs.d;
+              Sbest = S; win = j;
               wlo0 = rs.lo0; whi0 = rs.hi0; wlo1 = rs.lo1; whi1 = rs.hi1; have_w = true;
             }
           }
@@ -525,6 +550,10 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
         for (int q = 0; q + 1 < 2 * KT / 4; ++q) jp[q] = __builtin_amdgcn_alignbit(jp[q + 1], jp[q], 8);
         jp[2 * KT / 4 - 1] = __builtin_amdgcn_alignbit(j0, jp[2 * KT / 4 - 1], 8);
         outmask = (outmask >> 1) | ((outmask & 1u) << (2 * KT - 1));
+      }
+      if (__any(fast)) {
+        const ResidStats rw = resid_stats<WT>(kf, sm.mu, win, hh, sm.w);
+        dwin = rw.d;
       }
       if (fast) {
         // the winner must be among the M nearest: count every centroid that may precede it
