@@ -382,6 +382,32 @@ def keys_m_sweep(qwm, torch, Kall, table, st, Ms=(4, 8, 16, 256)):
     return out
 
 
+def keys_full_matrix(qwm, torch, K, table, st, M=8):
+    """The pages' full-matrix ablation of QSAC (candidates by the Query
+    second-moment matrix instead of its diagonal), QSAC + PSAC on the new chunk,
+    beside the diagonal call on the same tokens; also the share of tokens whose
+    centroid the full form changes."""
+    H = K.shape[1]
+    kd = qwm.PackedChunk(K.shape[0], H, True)
+    kf = qwm.PackedChunk(K.shape[0], H, True)
+    out = {"workload": f"{K.shape[0]} tokens x {H} heads, M={M}"}
+    for name, call in (("diagonal", lambda: qwm.quantize_keys(K, table, st.w, st.U, M=M, flags=3, out=kd)),
+                       ("full", lambda: qwm.quantize_keys_fullq(K, table, st.S, st.n, st.w, st.U, M=M, flags=3,
+                                                                out=kf))):
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 3
+        out[name] = {"ms": round(ms, 4), "token_heads_per_s": round(K.shape[0] * H / (ms * 1e-3), 1)}
+    out["idx_changed_fraction"] = round(float((kd.idx != kf.idx).float().mean().item()), 4)
+    return out
+
+
 def prq_codec(qwm, torch, X, stages=(1, 2, 3), iters=10):
     """QVG's progressive residual quantization as a second codec workload: all
     stages (seeded Lloyd on each stage's residual, nearest assignment, fp32
@@ -523,6 +549,7 @@ def run_stream_or_pass(args, qwm, torch, w):
             res["keys_m_sweep"] = keys_m_sweep(qwm, torch, step.K[: (step.nch - 1) * step.chunk], step.prev[0],
                                                step.st)
             res["prq_codec"] = prq_codec(qwm, torch, step.K[step.sl_new])
+            res["keys_full_matrix"] = keys_full_matrix(qwm, torch, step.K[step.sl_new], step.prev[0], step.st)
             res["keys_keep_test"] = keys_keep_test(qwm, torch, step.K[: (step.nch - 1) * step.chunk], step.prev[0],
                                                    step.st, step.chunk)
     else:
