@@ -102,8 +102,9 @@ struct SelectArgs {
   const double* qS; const int64_t* qn; const double* qB;
 };
 
+constexpr int MU_ROW = D + 8;   // elements per staged centroid row (16 bytes of padding)
 struct SelShared {
-  uint16_t mu[NC * D];         // centroid rows, swizzled: 16-byte chunk c of row j at chunk (c ^ (j & 15))
+  uint16_t mu[NC * MU_ROW];    // centroid rows, padded: 16-byte chunk c of row j at chunk 17 j + c
   uint16_t aug[NC][4];
   float bj[NC];
   float w[D];
@@ -192,9 +193,12 @@ struct ResidStats {
   float d, lo0, hi0, lo1, hi1;
 };
 
-// 16-byte chunk c (channels 8c .. 8c+7) of centroid row j in the swizzled LDS table
+// 16-byte chunk c (channels 8c .. 8c+7) of centroid row j in the LDS table.
+// Rows are 17 chunks apart: the 16 rows a quarter-wave reads at one chunk
+// index fall on distinct bank groups, and a lane's chunk offsets are
+// compile-time constants on top of its row base.
 __device__ __forceinline__ u32x4 mu_chunk(const uint16_t* tab, int j, int c) {
-  return reinterpret_cast<const u32x4*>(tab)[j * 16 + (c ^ (j & 15))];
+  return reinterpret_cast<const u32x4*>(tab)[j * (MU_ROW / 8) + c];
 }
 
 // Residual statistics of the token kf (the lane's channels 16 s + 8 hh + e at
@@ -281,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
 #pragma unroll 4
     for (int e = tid; e < NC * 16; e += 256) {
       const int j = e >> 4, c = e & 15;
-      reinterpret_cast<u32x4*>(sm.mu)[j * 16 + (c ^ (j & 15))] = src[e];
+      reinterpret_cast<u32x4*>(sm.mu)[j * (MU_ROW / 8) + c] = src[e];
     }
     const uint2* asrc = reinterpret_cast<const uint2*>(a.aug + (int64_t)h * NC * 4);
     reinterpret_cast<uint2*>(sm.aug)[tid] = asrc[tid];
