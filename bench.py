@@ -126,24 +126,39 @@ class Stream:
         self.Cv = torch.empty_like(self.Ck)
         self.kp = qwm.PackedChunk(T, H, True)
         self.vp = qwm.PackedChunk(T, H, False)
-        self.segs.append((self.kp, self.vp, self.Ck, self.Cv, self.st.U))
-        self.dsegs, self.total = qwm.segments_tensor(self.segs)
+        # Two sets of statistics outputs (w, U, eigenvalues) over one running sum
+        # (S, n): a step's keys read one set while the update for the next step
+        # writes the other, so the update need not wait for the keys.  The new
+        # chunk's segment names the basis its keys were coded with: one segment
+        # table per set.
+        self.stb = qwm.QueryStats(self.H)
+        self.stb.S, self.stb.n = self.st.S, self.st.n
+        self.stb.w.copy_(self.st.w)
+        self.stb.U.copy_(self.st.U)
+        self.stats = [self.st, self.stb]
+        self.dsegs_pp = []
+        for sx in self.stats:
+            d, self.total = qwm.segments_tensor(self.segs + [(self.kp, self.vp, self.Ck, self.Cv, sx.U)])
+            self.dsegs_pp.append(d)
+        self.parity = 0
+        self.cur_seg = (self.kp, self.vp, self.Ck, self.Cv, self.st.U)   # the new chunk as last coded
         self.diag = qwm.new_diag()
         self.vdiag = qwm.new_diag()      # the V side counts on its own stream
         # the Query statistics and basis only feed the key quantization, and the V side
         # (table refresh, values) is independent of the K side: each runs on its own
         # stream.  The statistics a step's keys need come from the previous chunk's
-        # Queries, so each step launches the next step's update as soon as its own
-        # keys have read w and U; it runs beside the step's attention
+        # Queries, so each step launches the next step's update (into the other
+        # output set) at its start; it runs beside the step's Lloyd iterations and
+        # keys (small, launch-bound kernels), not beside its attention
         self.side = torch.cuda.Stream()
         self.vside = torch.cuda.Stream()
-        self.stats_done = torch.cuda.Event()
-        self.keys_done = torch.cuda.Event()
+        self.stats_done = [torch.cuda.Event(), torch.cuda.Event()]   # one per statistics set
+        self.fork = torch.cuda.Event()
         self.v_done = torch.cuda.Event()
         self.primed = False
         self.queries = T
         self.new_tokens = T
-        self.stage_names = ["launch_side_streams", "lloyd_k", "keys_incl_stats_wait", "values_wait", "attention"]
+        self.stage_names = ["lloyd_k", "side_launch_and_stats_wait", "keys", "values_wait", "attention"]
 
     def _chunk(self, c, sl, prev):
         qwm = self.qwm
@@ -168,38 +183,50 @@ class Stream:
         rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
         K, V = self.K[self.sl_new], self.V[self.sl_new]
         main = torch.cuda.current_stream()
-        rec(0)
+        p = self.parity
+        cur, nxt = self.stats[p], self.stats[p ^ 1]
         if not self.primed:          # the first step's statistics (afterwards: the previous step's launch)
-            self._launch_stats(main)
+            self.side.wait_stream(main)
+            self._launch_stats(cur, p)
             self.primed = True
-        self.vside.wait_stream(main)
+        rec(0)
+        # the side streams start from here: after everything earlier on this stream,
+        # the previous step's attention (which read set p ^ 1's basis) included
+        self.fork.record(main)
+        # the critical path is issued first: the K table refresh
+        qwm.build_centroids(K, 3, init=self.prev[0], out=self.Ck, diag=self.diag)
+        rec(1)
+        self.side.wait_event(self.fork)
+        self._launch_stats(nxt, p ^ 1)   # the next step's statistics (one update + basis per step)
+        self.vside.wait_event(self.fork)
         with torch.cuda.stream(self.vside):
             qwm.build_centroids(V, 3, init=self.prev[1], out=self.Cv, diag=self.vdiag)
             qwm.quantize_values(V, self.Cv, out=self.vp, diag=self.vdiag)
             self.v_done.record(self.vside)
-        rec(1)
-        qwm.build_centroids(K, 3, init=self.prev[0], out=self.Ck, diag=self.diag)
+        main.wait_event(self.stats_done[p])
         rec(2)
-        main.wait_event(self.stats_done)
-        qwm.quantize_keys(K, self.Ck, self.st.w, self.st.U, M=8, flags=3, out=self.kp, diag=self.diag)
-        self.keys_done.record(main)
+        qwm.quantize_keys(K, self.Ck, cur.w, cur.U, M=8, flags=3, out=self.kp, diag=self.diag)
+        self.cur_seg = (self.kp, self.vp, self.Ck, self.Cv, cur.U)
         rec(3)
-        # the next step's statistics (one update + basis per step, as before)
-        self._launch_stats(main, after=self.keys_done)
         main.wait_event(self.v_done)
         rec(4)
-        out, _, _ = qwm.attention(self.Q[self.sl_new], self.dsegs, self.nch, self.total)
+        out, _, _ = qwm.attention(self.Q[self.sl_new], self.dsegs_pp[self.parity], self.nch, self.total)
         rec(5)
+        self.parity ^= 1
         return out
 
-    def _launch_stats(self, main, after=None):
-        if after is None:
-            self.side.wait_stream(main)
-        else:
-            self.side.wait_event(after)
+    def all_segs(self):
+        """Every segment of the cache: the prefilled chunks and the new one."""
+        return self.segs + [self.cur_seg]
+
+    def join(self):
+        """Make the current stream wait for the statistics the last step launched."""
+        self.torch.cuda.current_stream().wait_event(self.stats_done[self.parity])
+
+    def _launch_stats(self, st, i):
         with self.torch.cuda.stream(self.side):
-            self.qwm.update_query_stats(self.Q[self.sl_prevq], self.st, compute_basis=True)
-            self.stats_done.record(self.side)
+            self.qwm.update_query_stats(self.Q[self.sl_prevq], st, compute_basis=True)
+            self.stats_done[i].record(self.side)
 
 
 class OnePass:
@@ -439,7 +466,7 @@ def decode_ab(qwm, torch, step, fused_ms):
 
     def decode_all():
         pos = 0
-        for (kp, vp, kc, vc, U) in step.segs:
+        for (kp, vp, kc, vc, U) in step.all_segs():
             qwm.decode_segment(kp, vp, kc, vc, U, Kd[pos:pos + kp.T], Vd[pos:pos + kp.T])
             pos += kp.T
 
@@ -484,6 +511,8 @@ def timed_steps(step, torch, steps, warmup):
     t_start.record()
     for i in range(steps):
         step.run(evs[i])
+    if hasattr(step, "join"):
+        step.join()      # work the timed steps launched on side streams
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -541,8 +570,17 @@ def run_stream_or_pass(args, qwm, torch, w):
         res["roofline"]["traffic"] = attention_traffic()
     res["stages_ms"] = {k: round(v, 4) for k, v in stage.items()}
     if isinstance(step, Stream):
+        # the overlapped step against the same calls made one after another on one
+        # stream: the attention output must be bit-identical
+        out = step.run()
+        step.join()
+        torch.cuda.synchronize()
+        dsegs, total = qwm.segments_tensor(step.all_segs())
+        ref, _, _ = qwm.attention(step.Q[step.sl_new], dsegs, step.nch, total)
+        torch.cuda.synchronize()
+        res["step_check_max_abs_diff"] = float((out - ref).abs().max().item())
         res["keys_step"] = {"token_heads": step.chunk * step.H,
-                            "ms_incl_stats_wait": round(stage["keys_incl_stats_wait"], 4)}
+                            "ms": round(stage["keys"], 4)}
         res["keys_bulk"] = keys_bulk(qwm, torch, step.K[: (step.nch - 1) * step.chunk], step.prev[0], step.st)
         if not args.no_decode_ab:
             res["decode_ab"] = decode_ab(qwm, torch, step, stage["attention"])

@@ -784,6 +784,7 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
   __shared__ double kx[4][D];
   __shared__ double wx[4][D];
   __shared__ double dq[4][NC];
+  __shared__ uint8_t cand[4][NC];          // the M candidates in (d, j) order
   __shared__ double sq[FULL ? D * D : 1];   // S [c][r]
   __shared__ double tq[FULL ? 4 : 1][D];    // S k
   int count;
@@ -924,7 +925,8 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
       const double Wa = a.Wg[2 * h], Wb = a.Wg[2 * h + 1];
       double bestS = __builtin_inf();
       int bestj = 0;
-      // M rounds of (d_Q, j) selection
+      // M rounds of (d_Q, j) selection (LDS and shuffles only) ...
+      int nc = 0;
       for (int m = 0; m < a.M; ++m) {
         double bv = __builtin_inf();
         int bj = NC;
@@ -939,27 +941,39 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
           if (ov < bv || (ov == bv && oj < bj)) { bv = ov; bj = oj; }
         }
         if (bj >= NC) break;
-        // remove it from the pool
+        // remove it from the pool, record it
         if (lane == (bj & 63)) dq[wv][bj] = __builtin_inf();
+        if (lane == 0) cand[wv][nc] = (uint8_t)bj;
+        ++nc;
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        // S for candidate bj: lanes 0..31 group 0, 32..63 group 1
-        const uint16_t* mj = a.mu + ((int64_t)h * NC + bj) * D;
-        float rlo = 0.f, rhi = 0.f;
-        {
-          const float m0 = bf16_bits_to_f32(mj[2 * lane]), m1 = bf16_bits_to_f32(mj[2 * lane + 1]);
-          const float r0 = (float)x0 - m0, r1 = (float)x1 - m1;
-          rlo = fminf(fminf(r0, r1), 0.f);
-          rhi = fmaxf(fmaxf(r0, r1), 0.f);
+      }
+      // ... then S for the candidates, eight at a time with their centroid rows
+      // loaded together (the choice by (S, j) does not depend on the order);
+      // lanes 0..31 group 0, 32..63 group 1
+      for (int m0 = 0; m0 < nc; m0 += 8) {
+        uint32_t mw[8];
+        int jj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          jj[u] = cand[wv][m0 + u < nc ? m0 + u : m0];
+          mw[u] = *reinterpret_cast<const uint32_t*>(a.mu + ((int64_t)h * NC + jj[u]) * D + 2 * lane);
         }
-        for (int o = 16; o > 0; o >>= 1) {
-          rlo = fminf(rlo, __shfl_xor(rlo, o, 64));
-          rhi = fmaxf(rhi, __shfl_xor(rhi, o, 64));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (m0 + u >= nc) break;
+          const float r0 = (float)x0 - __uint_as_float(mw[u] << 16);
+          const float r1 = (float)x1 - __uint_as_float(mw[u] & 0xFFFF0000u);
+          float rlo = fminf(fminf(r0, r1), 0.f), rhi = fmaxf(fmaxf(r0, r1), 0.f);
+          for (int o = 16; o > 0; o >>= 1) {
+            rlo = fminf(rlo, __shfl_xor(rlo, o, 64));
+            rhi = fmaxf(rhi, __shfl_xor(rhi, o, 64));
+          }
+          const double Rg = (double)rhi - (double)rlo;
+          const double Ra = __shfl(Rg, 0, 64), Rb = __shfl(Rg, 32, 64);
+          const double S = Wa * Ra * Ra + Wb * Rb * Rb;
+          if (S < bestS || (S == bestS && jj[u] < bestj)) { bestS = S; bestj = jj[u]; }
         }
-        const double Rg = (double)rhi - (double)rlo;
-        const double Ra = __shfl(Rg, 0, 64), Rb = __shfl(Rg, 32, 64);
-        const double S = Wa * Ra * Ra + Wb * Rb * Rb;
-        if (S < bestS || (S == bestS && bj < bestj)) { bestS = S; bestj = bj; }
       }
       win = bestj;
     }
