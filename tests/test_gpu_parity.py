@@ -281,6 +281,36 @@ def test_quantize_keys_full_matrix_cold_start(qwm):
         compare_codec(o, {k: v[h] for k, v in g.items()}, T, o["idx"] == g["idx"][h])
 
 
+@pytest.mark.parametrize("T,dtype", [(1, "bf16"), (129, "f32"), (257, "bf16")])
+def test_quantize_keys_full_matrix_shapes(qwm, T, dtype):
+    """Full-matrix QSAC at a single token, a ragged fp32 chunk and a ragged bf16
+    chunk (the kernel's grid covers four tokens per block)."""
+    import torch
+    from gpu_helpers import dev_tokens, dev_table, dev_basis, packed_host, idx_mismatches_allowed, compare_codec
+    w, K, Ct, wt, Ut = _key_inputs("480p", 300, [0, 1])   # tables from 300 tokens (Forgy needs >= 256)
+    K = np.ascontiguousarray(K[:T])
+    H = w.H
+    Ss, ns = [], []
+    for h in range(H):
+        S, n = OS.update(np.zeros((128, 128)), 0, w.Q[:300, h])
+        Ss.append(S)
+        ns.append(n)
+    out = qwm.quantize_keys_fullq(dev_tokens(K, dtype), dev_table(Ct), torch.from_numpy(np.stack(Ss)).cuda(),
+                                  torch.tensor(ns, dtype=torch.int64).cuda(), torch.from_numpy(wt).cuda(),
+                                  dev_basis(Ut), M=8, flags=3)
+    torch.cuda.synchronize()
+    g = packed_host(out)
+    for h in range(H):
+        o = Qz.quantize_keys(K[:, h].astype(np.float64), Ct[h], wt[h], Ut[h], M=8, flags=3 | Qz.QSAC_FULL,
+                             Mq=Qz.second_moment(Ss[h], ns[h]))
+        nmis, nbad = idx_mismatches_allowed("qsac", o, g["idx"][h], K[:, h], Ct[h], w=wt[h], M=8)
+        assert nbad == 0
+        same = o["idx"] == g["idx"][h]
+        compare_codec(o, {k: v[h] for k, v in g.items()}, T, same)
+        dc = np.abs(g["c"][h].astype(np.int64) - o["Cq"].astype(np.int64))
+        assert dc[same].max() <= 1
+
+
 @pytest.mark.parametrize("M", [8, 16])
 def test_quantize_keys_keep_rejections(qwm, M):
     """The keep test where it rejects often: strongly non-uniform weights and a
