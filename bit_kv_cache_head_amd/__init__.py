@@ -308,6 +308,25 @@ def attention(q: torch.Tensor, segs: torch.Tensor | None, n_segs: int, total_key
     return out, lse, top1
 
 
+def attention_merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor, lse_b: torch.Tensor,
+                    out: torch.Tensor | None = None, want_lse: bool = False):
+    """Log-sum-exp merge of two attention results over disjoint key sets:
+    out [Tq, H, 128] fp32 (+ lse [H, Tq])."""
+    Tq, H = out_a.shape[0], out_a.shape[1]
+    for t in (out_a, out_b):
+        if t.dtype != torch.float32 or tuple(t.shape) != (Tq, H, D) or not t.is_contiguous():
+            raise ValueError("outputs must be contiguous [Tq, H, 128] float32")
+    for t in (lse_a, lse_b):
+        if t.dtype != torch.float32 or tuple(t.shape) != (H, Tq) or not t.is_contiguous():
+            raise ValueError("lse must be contiguous [H, Tq] float32")
+    if out is None:
+        out = torch.empty_like(out_a)
+    lse = torch.empty(H, Tq, dtype=torch.float32, device=out_a.device) if want_lse else None
+    check(lib.qwm_attention_merge(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), Tq, H, _ptr(out), _ptr(lse),
+                                  _stream()))
+    return out, lse
+
+
 def reference_top1(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
     """top1 [H, Tq] int32: argmax over all keys k [Tk, H, 128] (bf16) of q . k."""
     tq, tk = _tokens(q), _tokens(k)

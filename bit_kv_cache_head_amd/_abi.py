@@ -14,7 +14,7 @@ QWM_OP_STATS, QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION, QW
 
 # every symbol include/quantwm.h declares
 EXPORTS = ["qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys", "qwm_quantize_keys_fullq",
-           "qwm_quantize_values", "qwm_attention", "qwm_attention_active", "qwm_decode_segment", "qwm_centroid_residual", "qwm_reference_top1", "qwm_workspace_bytes", "qwm_zeros_stride", "qwm_last_error", "qwm_abi_version"]
+           "qwm_quantize_values", "qwm_attention", "qwm_attention_merge", "qwm_attention_active", "qwm_decode_segment", "qwm_centroid_residual", "qwm_reference_top1", "qwm_workspace_bytes", "qwm_zeros_stride", "qwm_last_error", "qwm_abi_version"]
 
 
 class Tokens(C.Structure):
@@ -58,6 +58,7 @@ def _load():
     L.qwm_quantize_keys_fullq.argtypes = [P, P, P, P, P, P, C.c_int32, C.c_uint32, P, P, P, C.c_size_t, P]
     L.qwm_quantize_values.argtypes = [P, P, P, P, P, C.c_size_t, P]
     L.qwm_attention.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, C.c_size_t, P]
+    L.qwm_attention_merge.argtypes = [P, P, P, P, C.c_int64, C.c_int32, P, P, P]
     L.qwm_attention_active.argtypes = [P, P, C.c_int32, C.c_int64, P, P, C.c_float, P, P, P, P, C.c_size_t, P]
     L.qwm_decode_segment.argtypes = [P, C.c_int32, P, P, C.c_int64, C.c_int64, P]
     L.qwm_centroid_residual.argtypes = [P, P, P, P, C.c_int64, C.c_int64, P]
@@ -69,8 +70,8 @@ def _load():
     L.qwm_last_error.restype = C.c_char_p
     L.qwm_abi_version.restype = C.c_int32
     for name in ("qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys", "qwm_quantize_keys_fullq",
-                 "qwm_quantize_values", "qwm_attention", "qwm_attention_active", "qwm_decode_segment",
-                 "qwm_centroid_residual"):
+                 "qwm_quantize_values", "qwm_attention", "qwm_attention_merge", "qwm_attention_active",
+                 "qwm_decode_segment", "qwm_centroid_residual"):
         getattr(L, name).restype = C.c_int
     return L
 

@@ -27,6 +27,8 @@ qwm_status launch_stats(const qwm_tokens* q, const qwm_qstats* st, int32_t compu
 qwm_status launch_keys(const qwm_tokens* k, const uint16_t* centroids, const float* w, const uint16_t* U,
                        int32_t M, uint32_t flags, const qwm_packed* out, qwm_diag* diag, void* ws,
                        hipStream_t stream);
+qwm_status launch_attention_merge(const float* oa, const float* la, const float* ob, const float* lb, int64_t Tq,
+                                  int32_t H, float* out, float* lse, hipStream_t stream);
 qwm_status launch_keys_full(const qwm_tokens* k, const uint16_t* centroids, const double* S, const int64_t* n,
                             const float* w, const uint16_t* U, int32_t M, uint32_t flags, const qwm_packed* out,
                             qwm_diag* diag, void* ws, hipStream_t stream);
@@ -250,6 +252,17 @@ qwm_status qwm_centroid_residual(const qwm_tokens* x, const uint16_t* centroids,
   if (out_stride_t < qwm::D || out_stride_h < 0 || out_stride_t % 4 || out_stride_h % 4)
     return fail(QWM_ERR_ARG, "residual: output strides must be multiples of 4 elements, token stride >= d");
   return launch_centroid_residual(x, centroids, idx, out, out_stride_t, out_stride_h, static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_attention_merge(const float* out_a, const float* lse_a, const float* out_b, const float* lse_b,
+                               int64_t Tq, int32_t H, float* out, float* lse, qwm_stream stream) {
+  if (Tq < 1 || H < 1 || Tq * H >= ((int64_t)1 << 31)) return fail(QWM_ERR_ARG, "merge: Tq, H out of range");
+  if (!out_a || !lse_a || !out_b || !lse_b || !out) return fail(QWM_ERR_ARG, "merge: null buffer");
+  if (!aligned(out_a, 4) || !aligned(lse_a, 4) || !aligned(out_b, 4) || !aligned(lse_b, 4) || !aligned(out, 4) ||
+      (lse && !aligned(lse, 4)))
+    return fail(QWM_ERR_ARG, "merge: misaligned buffer");
+  if (lse && (lse == lse_a || lse == lse_b)) return fail(QWM_ERR_ARG, "merge: lse must not alias lse_a or lse_b");
+  return launch_attention_merge(out_a, lse_a, out_b, lse_b, Tq, H, out, lse, static_cast<hipStream_t>(stream));
 }
 
 qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,

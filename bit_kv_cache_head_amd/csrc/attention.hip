@@ -936,6 +936,35 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
   }
 }
 
+// Log-sum-exp merge of two attention results of the same Queries over disjoint
+// key sets: with m = max(la, lb), O = (e^(la - m) Oa + e^(lb - m) Ob) / (e^(la - m) +
+// e^(lb - m)) and lse = m + log of that denominator; a part with lse = -inf has
+// no keys.  Grid ceil(Tq H / 2), 256 threads: 128 channels of two (query, head)
+// rows per block.  out may be oa or ob (each thread reads its elements before
+// writing them); lse must not alias la or lb.
+__global__ __launch_bounds__(256) void attention_merge_kernel(const float* oa, const float* __restrict__ la,
+                                                              const float* ob, const float* __restrict__ lb,
+                                                              int64_t Tq, int32_t H, float* out, float* lse) {
+  const int64_t r = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+  if (r >= Tq * H) return;
+  const int c = threadIdx.x & 127;
+  const int64_t q = r / H;
+  const int h = (int)(r % H);
+  const float a = la[(int64_t)h * Tq + q], b = lb[(int64_t)h * Tq + q];
+  const float m = fmaxf(a, b);
+  const int64_t e = r * D + c;
+  if (m == -__builtin_inff()) {
+    out[e] = 0.f;
+    if (lse && c == 0) lse[(int64_t)h * Tq + q] = -__builtin_inff();
+    return;
+  }
+  const float wa = (a == -__builtin_inff()) ? 0.f : expf(a - m);
+  const float wb = (b == -__builtin_inff()) ? 0.f : expf(b - m);
+  const float den = wa + wb;
+  out[e] = (wa * oa[e] + wb * ob[e]) / den;
+  if (lse && c == 0) lse[(int64_t)h * Tq + q] = m + logf(den);
+}
+
 }  // namespace qwm
 
 namespace qwm_host {
@@ -1042,6 +1071,14 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
   if (top1) hipLaunchKernelGGL(attention_combine_kernel<true>, g2, dim3(256), 0, stream, a);
   else hipLaunchKernelGGL(attention_combine_kernel<false>, g2, dim3(256), 0, stream, a);
   return check_launch("attention merge");
+}
+
+qwm_status launch_attention_merge(const float* oa, const float* la, const float* ob, const float* lb, int64_t Tq,
+                                  int32_t H, float* out, float* lse, hipStream_t stream) {
+  const int64_t rows = Tq * H;
+  hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, stream, oa, la, ob, lb, Tq,
+                     H, out, lse);
+  return check_launch("attention merge of two parts");
 }
 
 }  // namespace qwm_host

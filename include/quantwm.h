@@ -206,6 +206,20 @@ qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n
                          int64_t total_keys, float scale, float* out, float* lse, int32_t* top1,
                          void* ws, size_t ws_bytes, qwm_stream stream);
 
+/* Log-sum-exp merge of two attention results of the same Queries over
+ * disjoint key sets, e.g. the cached chunks and the newest one, computed by two
+ * qwm_attention calls with lse.  The softmax of the method section's logits
+ * over the union is the two parts' outputs weighted by e^lse: with
+ * m = max(lse_a, lse_b), out = (e^(lse_a - m) out_a + e^(lse_b - m) out_b) /
+ * (e^(lse_a - m) + e^(lse_b - m)) and lse = m + log of that denominator.
+ * out_a, out_b, out [Tq][H][d] fp32; lse_a, lse_b, lse [H][Tq] fp32 (natural
+ * log; -inf marks a part without keys; a row with no keys in either part gets
+ * out = 0, lse = -inf).  lse may be NULL.  out may be out_a or out_b; lse must
+ * not alias lse_a or lse_b (QWM_ERR_ARG).  Device buffers owned by the caller;
+ * no workspace. */
+qwm_status qwm_attention_merge(const float* out_a, const float* lse_a, const float* out_b, const float* lse_b,
+                               int64_t Tq, int32_t H, float* out, float* lse, qwm_stream stream);
+
 /* qwm_attention over the packed segments plus the active chunk, which stays
  * BF16 until it completes (QuantWM App. D.1: completed chunks are packed, the
  * active one is kept as it is).  k_active, v_active: [Ta][H][d] bf16 token

@@ -117,3 +117,15 @@ def test_reference_top1_validation():
     assert lib.qwm_reference_top1(C.byref(q), C.byref(_tok(ptr=0x2000, H=3)), C.c_void_p(0x3000), None) == 1
     assert lib.qwm_reference_top1(C.byref(q), C.byref(k), None, None) == 1
     assert b"top1" in lib.qwm_last_error()
+
+
+def test_attention_merge_validation():
+    from bit_kv_cache_head_amd._abi import lib
+    p = [C.c_void_p(a) for a in (0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000)]
+    # null part, bad sizes, lse aliasing a part's lse, misaligned buffer: rejected before any device access
+    assert lib.qwm_attention_merge(None, p[1], p[2], p[3], 10, 2, p[4], p[5], None) == 1
+    assert lib.qwm_attention_merge(p[0], p[1], p[2], p[3], 0, 2, p[4], p[5], None) == 1
+    assert lib.qwm_attention_merge(p[0], p[1], p[2], p[3], 10, 0, p[4], p[5], None) == 1
+    assert lib.qwm_attention_merge(p[0], p[1], p[2], p[3], 10, 2, p[4], p[1], None) == 1
+    assert b"alias" in lib.qwm_last_error()
+    assert lib.qwm_attention_merge(p[0], p[1], p[2], p[3], 10, 2, C.c_void_p(0x4002), p[5], None) == 1

@@ -510,6 +510,38 @@ def test_attention_on_oracle_cache(qwm, want_top1, sizes):
             _check_top1(top1.cpu().numpy()[h], top, Qv[:, h], segs, h)
 
 
+@pytest.mark.parametrize("split", [1, 2, 4])
+def test_attention_merge_of_two_parts(qwm, split):
+    """Attention over the first `split` segments and over the rest, joined by
+    qwm_attention_merge, against the oracle over all of them; out written over
+    the first part's buffer (allowed aliasing)."""
+    import torch
+    from gpu_helpers import dev_tokens
+    sizes = [300, 257, 64, 1, 130]
+    w = datagen.make_workload("480p", heads=[0, 1], n_chunks=1, chunk=sum(sizes) + 256)
+    segs = _oracle_segments(w, sizes, [0, 1])
+    da, ta, ka = _upload_segments(qwm, segs[:split], 2)
+    db, tb, kb = _upload_segments(qwm, segs[split:], 2)
+    Qv = w.Q[-200:]
+    Qd = dev_tokens(Qv, "bf16")
+    oa, la, _ = qwm.attention(Qd, da, split, ta, want_lse=True)
+    ob, lb, _ = qwm.attention(Qd, db, len(sizes) - split, tb, want_lse=True)
+    out, lse = qwm.attention_merge(oa, la, ob, lb, out=oa, want_lse=True)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for h in range(2):
+        O, L, _ = OA.cache_attention(Qv[:, h].astype(np.float64), [s[h]["oracle"] for s in segs], 1 / np.sqrt(128))
+        err = np.linalg.norm(out[:, h] - O) / np.linalg.norm(O)
+        _log(f"  split {split} head {h}: rel L2 {err:.2e}")
+        assert err <= 2e-3
+        np.testing.assert_allclose(lse.cpu().numpy()[h], L, rtol=1e-4, atol=1e-4)
+    # a part without keys (lse = -inf) leaves the other unchanged
+    empty_l = torch.full_like(lb, -float("inf"))
+    o2, l2 = qwm.attention_merge(ob, lb, torch.zeros_like(ob), empty_l, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, ob) and torch.equal(l2, lb)
+
+
 @pytest.mark.parametrize("sizes,active", [([300, 257], 173), ([64], 1), ([], 130), ([], 1), ([130, 1], 64)])
 def test_attention_with_bf16_active_chunk(qwm, sizes, active):
     """Packed chunks plus the BF16 active chunk (QuantWM App. D.1): the active
