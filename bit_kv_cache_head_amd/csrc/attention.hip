@@ -906,15 +906,17 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   }
 }
 
-// Merge split partials.  Grid (ceil(Tq/2), H), 256 threads: two queries per block.
+// Merge split partials.  Grid (ceil(Tq/8), H), 256 threads: eight queries per
+// block, 32 threads per query, four channels per thread (16-byte accesses).
 template <bool TOP1>
 __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
-  const int h = blockIdx.y, c = threadIdx.x & 127;
-  const int64_t qi = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+  const int h = blockIdx.y, c = 4 * (threadIdx.x & 31);
+  const int64_t qi = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   if (qi >= a.Tq) return;
   float mx = -__builtin_inff();
   for (int p = 0; p < a.nparts; ++p) mx = fmaxf(mx, a.pm[((int64_t)p * a.H + h) * a.Tq + qi]);
-  float l = 0.f, o = 0.f;
+  float l = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
   float bv = -__builtin_inff();
   int32_t bi = 0x7FFFFFFF;
   for (int p = 0; p < a.nparts; ++p) {
@@ -922,14 +924,16 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
     const float pm = a.pm[pidx];
     const float wgt = (pm == -__builtin_inff()) ? 0.f : exp2f(pm - mx);
     l += a.pl[pidx] * wgt;
-    o += a.po[pidx * D + c] * wgt;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(a.po + pidx * D + c);
+    o += v * wgt;
     if (TOP1) {
-      const float v = a.ptv[pidx];
-      const int32_t i = a.pti[pidx];
-      if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+      const float tv = a.ptv[pidx];
+      const int32_t ti = a.pti[pidx];
+      if (tv > bv || (tv == bv && ti < bi)) { bv = tv; bi = ti; }
     }
   }
-  a.out[(qi * a.H + h) * D + c] = l > 0.f ? o / l : 0.f;
+  *reinterpret_cast<f32x4*>(a.out + (qi * a.H + h) * D + c) =
+      l > 0.f ? f32x4{o[0] / l, o[1] / l, o[2] / l, o[3] / l} : f32x4{0.f, 0.f, 0.f, 0.f};
   if (c == 0) {
     if (a.lse) a.lse[(int64_t)h * a.Tq + qi] = (mx + log2f(l)) / LOG2E;
     if (TOP1 && a.top1) a.top1[(int64_t)h * a.Tq + qi] = bi;
@@ -1067,7 +1071,7 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
   else hipLaunchKernelGGL(attention_kernel<false>, grid, dim3(AT_T), 0, stream, a);
   s = check_launch("attention");
   if (s != QWM_OK || a.nparts == 1) return s;
-  const dim3 g2((unsigned)((q->T + 1) / 2), (unsigned)q->H);
+  const dim3 g2((unsigned)((q->T + 7) / 8), (unsigned)q->H);
   if (top1) hipLaunchKernelGGL(attention_combine_kernel<true>, g2, dim3(256), 0, stream, a);
   else hipLaunchKernelGGL(attention_combine_kernel<false>, g2, dim3(256), 0, stream, a);
   return check_launch("attention merge");
