@@ -925,9 +925,17 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
       const double Wa = a.Wg[2 * h], Wb = a.Wg[2 * h + 1];
       double bestS = __builtin_inf();
       int bestj = 0;
-      // M rounds of (d_Q, j) selection (LDS and shuffles only) ...
+      // M rounds of (d_Q, j) selection (LDS and shuffles only); with M >= n_c
+      // every centroid is a candidate and there is nothing to select ...
       int nc = 0;
-      for (int m = 0; m < a.M; ++m) {
+      if (a.M >= NC) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cand[wv][lane + 64 * q] = (uint8_t)(lane + 64 * q);
+        nc = NC;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
+      for (int m = 0; m < (a.M >= NC ? 0 : a.M); ++m) {
         double bv = __builtin_inf();
         int bj = NC;
         for (int q = 0; q < 4; ++q) {
