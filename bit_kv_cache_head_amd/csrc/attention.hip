@@ -3,11 +3,11 @@
 // on-demand reconstruction of keys and values, here fused into the kernel).
 //
 // Work unit: one head, 256 queries (8 waves x 32), one share of every
-// segment's 64-key tiles.  Tiles flow through a two-stage pipeline: the packed
-// bytes and centroid rows of tile t+2 are fetched into registers, tile t+1 is
-// dequantized from registers into the second LDS buffer (fp16: K0_hat rows,
-// the PSAC coefficients c_scale * c as 8 extra contraction channels, V_hat
-// transposed), while tile t runs
+// segment's 64-key tiles.  Tiles flow through a register pipeline: the index
+// bytes and packed bytes of tile t+3 and the centroid rows of tile t+2 are in
+// flight, tile t+1 is dequantized from registers into the second LDS buffer
+// (fp16: K0_hat rows, the PSAC coefficients c_scale * c as 8 extra
+// contraction channels, V_hat transposed), while tile t runs
 //   S^T = [K0_hat | C_hat] [Q | Q U]^T     (MFMA 32x32x16 f16, contraction 128 + 16)
 //   online softmax in fp32 (exp2 domain, lazy rescaling)
 //   O^T += V_hat^T P                       (MFMA 32x32x16 f16)
