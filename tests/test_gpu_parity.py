@@ -510,6 +510,63 @@ def test_attention_on_oracle_cache(qwm, want_top1, sizes):
             _check_top1(top1.cpu().numpy()[h], top, Qv[:, h], segs, h)
 
 
+def _slice_quantized(o: dict, sl: slice, keys: bool) -> dict:
+    """Token range sl of one head's oracle quantization, repacked as a chunk of its own."""
+    r = {"idx": o["idx"][sl], "q": o["q"][sl], "scale": o["scale"][sl], "zero": o["zero"][sl],
+         "scale_bits": o["scale_bits"][sl], "codes": F.pack_codes(o["q"][sl]), "zeros": F.pack_zeros(o["zero"][sl])}
+    if keys:
+        r.update(Cq=o["Cq"][sl], c_scale=o["c_scale"][sl], c_scale_bits=o["c_scale_bits"][sl])
+    return r
+
+
+def test_attention_over_many_small_segments(qwm):
+    """150 segments of 1..40 keys (more than the 64 descriptors a wave scans at
+    once when it locates its share, one-key segments, a ragged tile in almost
+    every segment), all with PSAC, against the oracle over the same segments."""
+    import torch
+    from gpu_helpers import dev_tokens
+    rng = np.random.default_rng(12)
+    sizes = [int(x) for x in rng.integers(1, 41, 150)]
+    sizes[3] = sizes[70] = 1
+    T = sum(sizes)
+    w = datagen.make_workload("480p", heads=[0, 1], n_chunks=1, chunk=T + 600)
+    per_head = []
+    for h in range(2):
+        Ck = OL.lloyd(w.K[-512:, h].astype(np.float64), 256, 2, seed=31, head=h)
+        Cv = OL.lloyd(w.V[-512:, h].astype(np.float64), 256, 2, seed=32, head=h)
+        S, n = OS.update(np.zeros((128, 128)), 0, w.Q[-300:, h])
+        U = OS.principal_basis(S, n)["U_bf16"]
+        kq = Qz.quantize_keys(w.K[:T, h].astype(np.float64), Ck, OS.channel_weights(S, n), U, M=8)
+        vq = Qz.quantize_values(w.V[:T, h].astype(np.float64), Cv)
+        per_head.append((Ck, Cv, U, kq, vq))
+    segs, pos = [], 0
+    for Tn in sizes:
+        sl = slice(pos, pos + Tn)
+        per = []
+        for h in range(2):
+            Ck, Cv, U, kq, vq = per_head[h]
+            k, v = _slice_quantized(kq, sl, True), _slice_quantized(vq, sl, False)
+            per.append(dict(k=k, v=v, Ck=Ck, Cv=Cv, U=U,
+                            oracle=dict(k_idx=k["idx"], k_q=k["q"], k_scale=k["scale"], k_zero=k["zero"],
+                                        k_Cq=k["Cq"], k_cs=k["c_scale"], k_centroids=Ck, U=U,
+                                        v_idx=v["idx"], v_q=v["q"], v_scale=v["scale"], v_zero=v["zero"],
+                                        v_centroids=Cv)))
+        segs.append(per)
+        pos += Tn
+    dseg, total, keep = _upload_segments(qwm, segs, 2)
+    assert total == T
+    Qv = w.Q[-130:]
+    out, lse, _ = qwm.attention(dev_tokens(Qv, "bf16"), dseg, len(sizes), total, want_lse=True)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for h in range(2):
+        O, L, _ = OA.cache_attention(Qv[:, h].astype(np.float64), [s[h]["oracle"] for s in segs], 1 / np.sqrt(128))
+        err = np.linalg.norm(out[:, h] - O) / np.linalg.norm(O)
+        _log(f"  150 segments, head {h}: rel L2 {err:.2e}")
+        assert err <= 2e-3
+        np.testing.assert_allclose(lse.cpu().numpy()[h], L, rtol=1e-4, atol=1e-4)
+
+
 @pytest.mark.parametrize("split", [1, 2, 4])
 def test_attention_merge_of_two_parts(qwm, split):
     """Attention over the first `split` segments and over the rest, joined by
