@@ -510,6 +510,28 @@ def test_attention_on_oracle_cache(qwm, want_top1, sizes):
             _check_top1(top1.cpu().numpy()[h], top, Qv[:, h], segs, h)
 
 
+@pytest.mark.parametrize("tq", [1, 33, 257, 513])
+def test_attention_query_counts(qwm, tq):
+    """One Query, a ragged wave, and query blocks of 256 whose last block holds
+    a single Query (its other waves idle), against the oracle."""
+    import torch
+    from gpu_helpers import dev_tokens
+    sizes = [300, 130]
+    w = datagen.make_workload("480p", heads=[0, 1], n_chunks=1, chunk=sum(sizes) + 600)
+    segs = _oracle_segments(w, sizes, [0, 1])
+    dseg, total, keep = _upload_segments(qwm, segs, 2)
+    Qv = w.Q[-tq:]
+    out, lse, top1 = qwm.attention(dev_tokens(Qv, "bf16"), dseg, len(sizes), total, want_lse=True, want_top1=True)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for h in range(2):
+        O, L, top = OA.cache_attention(Qv[:, h].astype(np.float64), [s[h]["oracle"] for s in segs], 1 / np.sqrt(128))
+        err = np.linalg.norm(out[:, h] - O) / np.linalg.norm(O)
+        assert err <= 2e-3, (tq, h, err)
+        np.testing.assert_allclose(lse.cpu().numpy()[h], L, rtol=1e-4, atol=1e-4)
+        _check_top1(top1.cpu().numpy()[h], top, Qv[:, h], segs, h)
+
+
 def _slice_quantized(o: dict, sl: slice, keys: bool) -> dict:
     """Token range sl of one head's oracle quantization, repacked as a chunk of its own."""
     r = {"idx": o["idx"][sl], "q": o["q"][sl], "scale": o["scale"][sl], "zero": o["zero"][sl],
