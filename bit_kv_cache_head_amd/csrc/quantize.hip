@@ -1176,7 +1176,7 @@ __global__ __launch_bounds__(256) void forgy_kernel(const void* x, int32_t dtype
 // place is the range's running offset plus the number of such lanes below it.
 //
 // lloyd_sum_kernel (one wave per (head, cluster), 64 lanes x 2 channels): the
-// member rows summed in token order in fp64, 16 rows in flight; the new
+// member rows summed in token order in fp64, 32 rows in flight; the new
 // centroid is bf16(sum / n); an empty cluster keeps its centroid.
 constexpr int LS_WAVES = 16;
 
@@ -1257,7 +1257,7 @@ __global__ __launch_bounds__(256) void lloyd_sum_kernel(const void* x, int32_t d
   const int32_t* mem = ids + (int64_t)h * T + b;
   const int64_t rowbase = (int64_t)h * sh + 2 * lane;
   double s0 = 0.0, s1 = 0.0;
-  constexpr int U = 16;
+  constexpr int U = 32;
   int e = 0;
   if (dtype == QWM_BF16) {
     const uint16_t* xb = static_cast<const uint16_t*>(x) + rowbase;
