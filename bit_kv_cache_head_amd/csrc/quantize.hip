@@ -307,6 +307,20 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
   const float cb = a.cb;
 
   const int64_t ntile = (a.T + SEL_TOK - 1) / SEL_TOK;
+  // Nearest-centroid modes (Lloyd assignment, values) have registers to spare:
+  // each tile issues the next tile's bf16 token rows before its own work, so
+  // their HBM latency passes under it.
+  constexpr bool PF = !F32 && MODE != MODE_KEYS;
+  u32x4 nrow[PF ? 8 : 1];
+  auto fetch_rows = [&](int64_t t) __attribute__((always_inline)) {
+    const int64_t tk = t * SEL_TOK + wv * 32 + ln;
+    const bool ok = t < ntile && tk < a.T;
+    const uint16_t* xr = static_cast<const uint16_t*>(a.x) + (int64_t)h * a.sh + (ok ? tk : 0) * a.st;
+#pragma unroll
+    for (int s = 0; s < (PF ? 8 : 1); ++s)
+      nrow[s] = ok ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+  };
+  if constexpr (PF) fetch_rows(blockIdx.x);
   for (int64_t tile = blockIdx.x; tile < ntile; tile += a.blocks_per_head) {
     const int64_t tok0 = tile * SEL_TOK + wv * 32;
     const int64_t tok = tok0 + ln;
@@ -317,9 +331,17 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
     float kf[64];
     if (!F32) {
       const uint16_t* xr = static_cast<const uint16_t*>(a.x) + rowoff;
+      u32x4 crow[PF ? 8 : 1];
+      if constexpr (PF) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) crow[s] = nrow[s];
+        fetch_rows(tile + a.blocks_per_head);
+      }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const u32x4 v = valid ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
+        u32x4 v;
+        if constexpr (PF) v = crow[s];
+        else v = valid ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           kf[8 * s + e] = (e & 1) ? __uint_as_float(v[e >> 1] & 0xFFFF0000u) : __uint_as_float(v[e >> 1] << 16);
