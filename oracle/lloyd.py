@@ -12,6 +12,12 @@ Fisher-Yates shuffle driven by SplitMix64 (Steele, Lea & Flood, OOPSLA 2014),
 seeded with seed + (head << 32); Euclidean assignment with ties to the lowest
 centroid index; new centroid = bf16(mean of its members), computed in float64;
 an empty cluster keeps its centroid.
+
+Tokens with a NaN or infinite channel take no part in the table: the
+quantizers store them as index 0 with zero codes (a degenerate case the
+pages leave open), so they are never Forgy picks (the shuffle goes on past
+them; slots left without a finite token hold zeros) and never members of a
+cluster.
 """
 from __future__ import annotations
 
@@ -38,17 +44,30 @@ class SplitMix64:
         return z ^ (z >> 31)
 
 
-def forgy_indices(N: int, n_c: int, seed: int, head: int) -> np.ndarray:
+def forgy_indices(N: int, n_c: int, seed: int, head: int, finite=None) -> np.ndarray:
     """First n_c picks of a Fisher-Yates shuffle of range(N): pick i swaps slot i
-    with slot i + (next() mod (N - i))."""
+    with slot i + (next() mod (N - i)).  With a boolean mask `finite`, picks of
+    rows outside it are dropped and the shuffle goes on until n_c finite rows
+    are picked or the range is exhausted; missing picks are -1."""
     if N < n_c:
         raise ValueError("fewer tokens than centroids")
     rng = SplitMix64(seed + (head << 32))
     perm = list(range(N))
-    for i in range(n_c):
+    picks = []
+    i = 0
+    while len(picks) < n_c and i < N:
         j = i + rng.next() % (N - i)
         perm[i], perm[j] = perm[j], perm[i]
-    return np.array(perm[:n_c], dtype=np.int64)
+        if finite is None or finite[perm[i]]:
+            picks.append(perm[i])
+        i += 1
+    picks += [-1] * (n_c - len(picks))
+    return np.array(picks, dtype=np.int64)
+
+
+def finite_rows(X: np.ndarray) -> np.ndarray:
+    """Rows whose every channel is finite."""
+    return np.all(np.isfinite(np.asarray(X, np.float64)), axis=1)
 
 
 def sq_dists(X: np.ndarray, C: np.ndarray, block: int = 256) -> np.ndarray:
@@ -84,16 +103,20 @@ def lloyd(X: np.ndarray, n_c: int = 256, iters: int = 10, seed: int = 0, head: i
     init=None: Forgy seeding; otherwise warm start from the given table.
     """
     X = np.asarray(X, np.float64)
+    fin = finite_rows(X)
     if init is None:
-        C = bf16_rne(X[forgy_indices(X.shape[0], n_c, seed, head)])
+        idx = forgy_indices(X.shape[0], n_c, seed, head, finite=None if fin.all() else fin)
+        C = np.zeros((n_c, X.shape[1]))
+        C[idx >= 0] = bf16_rne(X[idx[idx >= 0]])
     else:
         C = np.array(init, dtype=np.float64, copy=True)
+    Xf = X[fin]
     hist = []
     for _ in range(iters):
-        a = assign(X, C)
+        a = assign(Xf, C)
         if return_history:
             hist.append((C.copy(), a.copy()))
-        C = update_means(X, a, C)
+        C = update_means(Xf, a, C)
     if return_history:
         return C, hist
     return C

@@ -41,6 +41,55 @@ def test_forgy_first_pick_by_hand():
     assert lloyd.forgy_indices(N, 256, seed=5, head=2)[0] == first
 
 
+def test_forgy_picks_by_hand():
+    """Picks 0-3 of the seeded shuffle for N = 10, worked by hand from the
+    published SplitMix64 outputs (tests/golden/forgy_tiny.json): a dropped
+    '+ i', a modulus of N instead of N - i, or a missed swap each change them."""
+    g = json.load(open(os.path.join(GOLD, "forgy_tiny.json")))
+    sm = json.load(open(os.path.join(GOLD, "splitmix64.json")))["cases"][0]
+    assert g["seed"] == sm["seed"]
+    assert [s["output"] for s in g["steps"]] == sm["outputs"][:4]
+    got = lloyd.forgy_indices(g["N"], g["n_c"], seed=g["seed"], head=g["head"])
+    assert got.tolist() == g["picks"]
+
+
+def test_forgy_skips_nonfinite_rows_by_hand():
+    """A pick that lands on a row with a non-finite channel is dropped and the
+    shuffle takes one more step (tests/golden/forgy_tiny.json, worked by hand)."""
+    g = json.load(open(os.path.join(GOLD, "forgy_tiny.json")))
+    fin = np.ones(g["N"], bool)
+    fin[g["nonfinite_case"]["nonfinite_rows"]] = False
+    got = lloyd.forgy_indices(g["N"], g["n_c"], seed=g["seed"], head=g["head"], finite=fin)
+    assert got.tolist() == g["nonfinite_case"]["picks"]
+    # fewer finite rows than centroids: the missing picks are marked
+    fin[:] = False
+    fin[[3, 5]] = True
+    got = lloyd.forgy_indices(g["N"], g["n_c"], seed=g["seed"], head=g["head"], finite=fin)
+    assert sorted(got[:2].tolist()) == [3, 5] and got[2:].tolist() == [-1, -1]
+
+
+def test_lloyd_ignores_nonfinite_rows():
+    """Rows with a NaN or infinite channel change nothing: the table built
+    with them equals the one built on the finite rows alone (warm start), and
+    a Forgy start takes only finite rows."""
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((300, 16))
+    init = bf16_rne(X[:32] + 0.01)
+    Xb = X.copy()
+    bad = [3, 50, 51, 299]
+    Xb[3, 0] = np.nan
+    Xb[50, 5] = np.inf
+    Xb[51, :] = -np.inf
+    Xb[299, 15] = np.nan
+    keep = np.setdiff1d(np.arange(300), bad)
+    np.testing.assert_array_equal(lloyd.lloyd(Xb, 32, 4, init=init), lloyd.lloyd(X[keep], 32, 4, init=init))
+    C0 = lloyd.lloyd(Xb, 32, 0, seed=2, head=1)
+    assert np.all(np.isfinite(C0))
+    picks = lloyd.forgy_indices(300, 32, 2, 1, finite=lloyd.finite_rows(Xb))
+    assert not set(picks.tolist()) & set(bad)
+    np.testing.assert_array_equal(C0, bf16_rne(Xb[picks]))
+
+
 def test_lloyd_matches_sklearn():
     """Data whose cluster means are exact in bf16: every Lloyd step agrees with
     scikit-learn's Lloyd k-means from the same initial table."""
