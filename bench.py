@@ -138,7 +138,8 @@ class Stream:
         self.stats = [self.st, self.stb]
         self.dsegs_pp = []
         for sx in self.stats:
-            d, self.total = qwm.segments_tensor(self.segs + [(self.kp, self.vp, self.Ck, self.Cv, sx.U)])
+            d = qwm.segment_array(self.segs + [(self.kp, self.vp, self.Ck, self.Cv, sx.U)])
+            self.total = d.total
             self.dsegs_pp.append(d)
         self.parity = 0
         self.cur_seg = (self.kp, self.vp, self.Ck, self.Cv, self.st.U)   # the new chunk as last coded
@@ -210,7 +211,7 @@ class Stream:
         rec(3)
         main.wait_event(self.v_done)
         rec(4)
-        out, _, _ = qwm.attention(self.Q[self.sl_new], self.dsegs_pp[self.parity], self.nch, self.total)
+        out, _, _ = qwm.attention(self.Q[self.sl_new], self.dsegs_pp[self.parity])
         rec(5)
         self.parity ^= 1
         return out
@@ -246,7 +247,8 @@ class OnePass:
         self.Cv = torch.empty_like(self.Ck)
         self.kp = qwm.PackedChunk(T, H, True)
         self.vp = qwm.PackedChunk(T, H, False)
-        self.dsegs, self.total = qwm.segments_tensor([(self.kp, self.vp, self.Ck, self.Cv, self.st.U)])
+        self.dsegs = qwm.segment_array([(self.kp, self.vp, self.Ck, self.Cv, self.st.U)])
+        self.total = self.dsegs.total
         self.diag = qwm.new_diag()
         self.nch = 1
         self.queries = int(w.Q.shape[0])
@@ -267,7 +269,7 @@ class OnePass:
         rec(3)
         qwm.quantize_values(self.V, self.Cv, out=self.vp, diag=self.diag)
         rec(4)
-        out, _, _ = qwm.attention(self.Q, self.dsegs, 1, self.total)
+        out, _, _ = qwm.attention(self.Q, self.dsegs)
         rec(5)
         return out
 
@@ -471,7 +473,7 @@ def decode_ab(qwm, torch, step, fused_ms):
             pos += kp.T
 
     def dense():
-        qwm.attention(Q, None, 0, 0, active=(Kd, Vd))
+        qwm.attention(Q, None, active=(Kd, Vd))
 
     for f in (decode_all, dense):
         f()
@@ -575,8 +577,9 @@ def run_stream_or_pass(args, qwm, torch, w):
         out = step.run()
         step.join()
         torch.cuda.synchronize()
-        dsegs, total = qwm.segments_tensor(step.all_segs())
-        ref, _, _ = qwm.attention(step.Q[step.sl_new], dsegs, step.nch, total)
+        dsegs = qwm.segment_array(step.all_segs())
+        total = dsegs.total
+        ref, _, _ = qwm.attention(step.Q[step.sl_new], dsegs)
         torch.cuda.synchronize()
         res["step_check_max_abs_diff"] = float((out - ref).abs().max().item())
         res["keys_step"] = {"token_heads": step.chunk * step.H,
@@ -646,8 +649,9 @@ def run_rollout(args, qwm, torch, w):
                     kp = qwm.quantize_keys(K, Ck, st.w if flags & 1 else None, U, M=8, flags=flags)
                 vp = qwm.quantize_values(V, Cv)
                 segs.append((kp, vp, Ck, Cv, U))
-                dsegs, total = qwm.segments_tensor(segs)
-                _, _, top1 = qwm.attention(Qd[sl], dsegs, len(segs), total, want_top1=True)
+                dsegs = qwm.segment_array(segs)
+                total = dsegs.total
+                _, _, top1 = qwm.attention(Qd[sl], dsegs, want_top1=True)
                 tops.append(top1)
                 qwm.update_query_stats(Qd[sl], st, compute_basis=True)   # causal: feeds the next chunks
                 prev = (Ck, Cv)

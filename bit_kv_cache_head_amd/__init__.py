@@ -19,7 +19,7 @@ from ._abi import (lib, LIB_PATH, QWM_OK, QWM_F32, QWM_BF16, QWM_QSAC, QWM_PSAC,
 D, NC, R, GROUP = 128, 256, 8, 64
 
 __all__ = ["QueryStats", "PackedChunk", "Workspace", "update_query_stats", "build_centroids",
-           "quantize_keys", "quantize_values", "attention", "segments_tensor", "zeros_stride",
+           "quantize_keys", "quantize_values", "attention", "segment_array", "SegmentArray", "zeros_stride",
            "QWM_QSAC", "QWM_PSAC", "QWM_PSAC_KEEP", "LIB_PATH", "new_diag"]
 
 
@@ -262,48 +262,51 @@ def decode_segment(kp, vp, kc, vc, U, k_out: torch.Tensor | None = None, v_out: 
     return k_out, v_out
 
 
-def segments_tensor(segments, device="cuda") -> tuple:
-    """Device array of segment descriptors.  `segments`: list of
-    (k: PackedChunk, v: PackedChunk, k_centroids, v_centroids, U or None).
-    Returns (device uint8 tensor, total keys).  Keep the tensor alive while in use."""
-    arr = (Segment * len(segments))()
-    total = 0
-    for i, (kp, vp, kc, vc, U) in enumerate(segments):
-        s = arr[i]
-        s.k_codes, s.k_idx, s.k_scale, s.k_zeros = (kp.codes.data_ptr(), kp.idx.data_ptr(),
-                                                    kp.scale.data_ptr(), kp.zeros.data_ptr())
-        s.k_c, s.k_c_scale = kp.c.data_ptr(), kp.c_scale.data_ptr()
-        s.v_codes, s.v_idx, s.v_scale, s.v_zeros = (vp.codes.data_ptr(), vp.idx.data_ptr(),
-                                                    vp.scale.data_ptr(), vp.zeros.data_ptr())
-        s.k_centroids, s.v_centroids = kc.data_ptr(), vc.data_ptr()
-        s.U = 0 if U is None else U.data_ptr()
-        s.T = kp.T
-        total += kp.T
-    host = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
-    return host.to(device), total
+class SegmentArray:
+    """Host array of segment descriptors for attention (the library validates
+    them, sums their keys and copies them to the device itself).  `segments`:
+    list of (k: PackedChunk, v: PackedChunk, k_centroids, v_centroids, U or None).
+    Keep the chunks alive while the array is in use."""
+
+    def __init__(self, segments):
+        self.n = len(segments)
+        self.arr = (Segment * max(self.n, 1))()
+        self.total = 0
+        for i, (kp, vp, kc, vc, U) in enumerate(segments):
+            self.arr[i] = _segment(kp, vp, kc, vc, U)
+            self.total += kp.T
+
+    def ptr(self):
+        return C.cast(self.arr, C.c_void_p) if self.n else C.c_void_p(0)
 
 
-def attention(q: torch.Tensor, segs: torch.Tensor | None, n_segs: int, total_keys: int, scale: float | None = None,
+def segment_array(segments) -> SegmentArray:
+    return SegmentArray(segments)
+
+
+def attention(q: torch.Tensor, segs: SegmentArray | None, scale: float | None = None,
               want_lse: bool = False, want_top1: bool = False, active: tuple | None = None):
     """out [Tq, H, 128] fp32 (+ lse [H, Tq], top1 [H, Tq] int32).  `active`:
     (K, V) of the BF16 active chunk, [Ta, H, 128] bf16 each (segs may then be
-    None with n_segs = total_keys = 0)."""
+    None)."""
     td = _tokens(q)
     if scale is None:
         scale = 1.0 / (D ** 0.5)
+    n_segs = 0 if segs is None else segs.n
+    total = 0 if segs is None else segs.total
+    sp = C.c_void_p(0) if segs is None else segs.ptr()
     out = torch.empty(td.T, td.H, D, dtype=torch.float32, device=q.device)
     lse = torch.empty(td.H, td.T, dtype=torch.float32, device=q.device) if want_lse else None
     top1 = torch.empty(td.H, td.T, dtype=torch.int32, device=q.device) if want_top1 else None
-    sp = C.c_void_p(segs.data_ptr() if segs is not None else 0)
     if active is None:
-        ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_ATTENTION, total_keys, td.H, td.T, n_segs), q.device)
-        check(lib.qwm_attention(C.byref(td), sp, n_segs, total_keys, C.c_float(scale),
+        ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_ATTENTION, total, td.H, td.T, n_segs), q.device)
+        check(lib.qwm_attention(C.byref(td), sp, n_segs, C.c_float(scale),
                                 _ptr(out), _ptr(lse), _ptr(top1), ws, nb, _stream()))
     else:
         ka, va = _tokens(active[0]), _tokens(active[1])
-        ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_ATTENTION_ACTIVE, total_keys + ka.T, td.H, td.T, n_segs),
+        ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_ATTENTION_ACTIVE, total + ka.T, td.H, td.T, n_segs),
                          q.device)
-        check(lib.qwm_attention_active(C.byref(td), sp, n_segs, total_keys, C.byref(ka), C.byref(va),
+        check(lib.qwm_attention_active(C.byref(td), sp, n_segs, C.byref(ka), C.byref(va),
                                        C.c_float(scale), _ptr(out), _ptr(lse), _ptr(top1), ws, nb, _stream()))
     return out, lse, top1
 

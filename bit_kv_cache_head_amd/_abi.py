@@ -57,9 +57,9 @@ def _load():
     L.qwm_quantize_keys.argtypes = [P, P, P, P, C.c_int32, C.c_uint32, P, P, P, C.c_size_t, P]
     L.qwm_quantize_keys_fullq.argtypes = [P, P, P, P, P, P, C.c_int32, C.c_uint32, P, P, P, C.c_size_t, P]
     L.qwm_quantize_values.argtypes = [P, P, P, P, P, C.c_size_t, P]
-    L.qwm_attention.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, C.c_size_t, P]
+    L.qwm_attention.argtypes = [P, P, C.c_int32, C.c_float, P, P, P, P, C.c_size_t, P]
     L.qwm_attention_merge.argtypes = [P, P, P, P, C.c_int64, C.c_int32, P, P, P]
-    L.qwm_attention_active.argtypes = [P, P, C.c_int32, C.c_int64, P, P, C.c_float, P, P, P, P, C.c_size_t, P]
+    L.qwm_attention_active.argtypes = [P, P, C.c_int32, P, P, C.c_float, P, P, P, P, C.c_size_t, P]
     L.qwm_decode_segment.argtypes = [P, C.c_int32, P, P, C.c_int64, C.c_int64, P]
     L.qwm_centroid_residual.argtypes = [P, P, P, P, C.c_int64, C.c_int64, P]
     L.qwm_reference_top1.argtypes = [P, P, P, P]

@@ -146,9 +146,8 @@ qwm_status qwm_build_centroids(const qwm_tokens* x, int32_t n_centroids, int32_t
   return launch_lloyd(x, iters, seed, init, centroids, diag, ws, static_cast<hipStream_t>(stream));
 }
 
-qwm_status qwm_quantize_keys(const qwm_tokens* k, const uint16_t* centroids, const float* w, const uint16_t* U,
-                             int32_t M, uint32_t flags, const qwm_packed* out, qwm_diag* diag, void* ws,
-                             size_t ws_bytes, qwm_stream stream) {
+static qwm_status check_keys_args(const qwm_tokens* k, const uint16_t* centroids, const float* w, const uint16_t* U,
+                                  int32_t M, uint32_t flags, const qwm_packed* out, qwm_diag* diag) {
   qwm_status s = check_tokens(k, "keys", false);
   if (s != QWM_OK) return s;
   if (!centroids || !aligned(centroids, 16)) return fail(QWM_ERR_ARG, "centroids: null or not 16-byte aligned");
@@ -157,7 +156,13 @@ qwm_status qwm_quantize_keys(const qwm_tokens* k, const uint16_t* centroids, con
   if (w && !aligned(w, 4)) return fail(QWM_ERR_ARG, "w misaligned");
   if (U && !aligned(U, 16)) return fail(QWM_ERR_ARG, "U not 16-byte aligned");
   if (diag && !aligned(diag, 8)) return fail(QWM_ERR_ARG, "diag misaligned");
-  s = check_packed(out, k, true, (flags & QWM_PSAC) && U);
+  return check_packed(out, k, true, (flags & QWM_PSAC) && U);
+}
+
+qwm_status qwm_quantize_keys(const qwm_tokens* k, const uint16_t* centroids, const float* w, const uint16_t* U,
+                             int32_t M, uint32_t flags, const qwm_packed* out, qwm_diag* diag, void* ws,
+                             size_t ws_bytes, qwm_stream stream) {
+  qwm_status s = check_keys_args(k, centroids, w, U, M, flags, out, diag);
   if (s != QWM_OK) return s;
   s = check_ws(ws, ws_bytes, select_ws_bytes(k->T, k->H, false));
   if (s != QWM_OK) return s;
@@ -199,6 +204,30 @@ qwm_status qwm_quantize_values(const qwm_tokens* v, const uint16_t* centroids, c
   return launch_values(v, centroids, out, diag, ws, static_cast<hipStream_t>(stream));
 }
 
+// Every descriptor of a host segment array, before any HIP call: T in
+// [1, 2^26) (the kernel reaches a segment-head's rows through 32-bit buffer
+// ranges), every array the attention reads present and aligned, the total
+// key count (returned in *total) below 2^31 (top-1 indices are int32).
+static qwm_status check_segments(const qwm_segment* segs, int32_t n_segs, int64_t* total) {
+  *total = 0;
+  for (int32_t i = 0; i < n_segs; ++i) {
+    const qwm_segment& g = segs[i];
+    const std::string at = "segment " + std::to_string(i) + ": ";
+    if (g.T < 1 || g.T >= ((int64_t)1 << 26)) return fail(QWM_ERR_ARG, at + "T must be in [1, 2^26)");
+    if (!g.k_codes || !g.k_idx || !g.k_scale || !g.k_zeros || !g.v_codes || !g.v_idx || !g.v_scale ||
+        !g.v_zeros || !g.k_centroids || !g.v_centroids)
+      return fail(QWM_ERR_ARG, at + "a packed array or centroid table is null");
+    if (g.U && (!g.k_c || !g.k_c_scale)) return fail(QWM_ERR_ARG, at + "a basis without PSAC coefficients");
+    if (!aligned(g.k_codes, 16) || !aligned(g.v_codes, 16) || !aligned(g.k_scale, 4) || !aligned(g.v_scale, 4) ||
+        !aligned(g.k_zeros, 4) || !aligned(g.v_zeros, 4) || !aligned(g.k_centroids, 16) ||
+        !aligned(g.v_centroids, 16) || (g.U && (!aligned(g.U, 16) || !aligned(g.k_c, 8) || !aligned(g.k_c_scale, 2))))
+      return fail(QWM_ERR_ARG, at + "misaligned array (codes and tables 16 B, scales and zeros 4 B, c 8 B, U 16 B)");
+    *total += g.T;
+    if (*total >= ((int64_t)1 << 31)) return fail(QWM_ERR_UNSUPPORTED, "more than 2^31 - 1 keys in all");
+  }
+  return QWM_OK;
+}
+
 static qwm_status check_attention_common(const qwm_tokens* q, float scale, const float* out, const float* lse,
                                          const int32_t* top1) {
   qwm_status s = check_tokens(q, "queries", false);
@@ -210,14 +239,14 @@ static qwm_status check_attention_common(const qwm_tokens* q, float scale, const
   return QWM_OK;
 }
 
-qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
-                         float scale, float* out, float* lse, int32_t* top1, void* ws, size_t ws_bytes,
-                         qwm_stream stream) {
+qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, float scale, float* out,
+                         float* lse, int32_t* top1, void* ws, size_t ws_bytes, qwm_stream stream) {
   qwm_status s = check_attention_common(q, scale, out, lse, top1);
   if (s != QWM_OK) return s;
-  if (!segs || !aligned(segs, 8)) return fail(QWM_ERR_ARG, "segments: null or misaligned device array");
   if (n_segs < 1 || n_segs > 4096) return fail(QWM_ERR_ARG, "n_segs must be in [1, 4096]");
-  if (total_keys < 1) return fail(QWM_ERR_ARG, "total_keys must be positive");
+  if (!segs) return fail(QWM_ERR_ARG, "segments: null host array");
+  int64_t total_keys = 0;
+  if ((s = check_segments(segs, n_segs, &total_keys)) != QWM_OK) return s;
   s = check_ws(ws, ws_bytes, attention_ws_bytes(total_keys, q->H, q->T, n_segs, false));
   if (s != QWM_OK) return s;
   return launch_attention(q, segs, n_segs, total_keys, nullptr, nullptr, scale, out, lse, top1, ws,
@@ -265,15 +294,15 @@ qwm_status qwm_attention_merge(const float* out_a, const float* lse_a, const flo
   return launch_attention_merge(out_a, lse_a, out_b, lse_b, Tq, H, out, lse, static_cast<hipStream_t>(stream));
 }
 
-qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
+qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs,
                                 const qwm_tokens* k_active, const qwm_tokens* v_active, float scale, float* out,
                                 float* lse, int32_t* top1, void* ws, size_t ws_bytes, qwm_stream stream) {
   qwm_status s = check_attention_common(q, scale, out, lse, top1);
   if (s != QWM_OK) return s;
   if (n_segs < 0 || n_segs > 4096) return fail(QWM_ERR_ARG, "n_segs must be in [0, 4096]");
-  if (n_segs > 0 && (!segs || !aligned(segs, 8))) return fail(QWM_ERR_ARG, "segments: null or misaligned device array");
-  if (n_segs > 0 && total_keys < 1) return fail(QWM_ERR_ARG, "total_keys must be positive");
-  if (n_segs == 0 && total_keys != 0) return fail(QWM_ERR_ARG, "total_keys must be 0 without segments");
+  if (n_segs > 0 && !segs) return fail(QWM_ERR_ARG, "segments: null host array");
+  int64_t total_keys = 0;
+  if ((s = check_segments(segs, n_segs, &total_keys)) != QWM_OK) return s;
   if ((s = check_tokens(k_active, "active keys", false)) != QWM_OK) return s;
   if ((s = check_tokens(v_active, "active values", false)) != QWM_OK) return s;
   if (k_active->dtype != QWM_BF16 || v_active->dtype != QWM_BF16)
@@ -285,6 +314,7 @@ qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, in
   if (k_active->T * std::max<int64_t>(k_active->stride_t, qwm::D) >= ((int64_t)1 << 30) ||
       v_active->T * std::max<int64_t>(v_active->stride_t, qwm::D) >= ((int64_t)1 << 30))
     return fail(QWM_ERR_UNSUPPORTED, "active chunk: T * stride_t must stay below 2^30 elements");
+  if (total_keys + k_active->T >= ((int64_t)1 << 31)) return fail(QWM_ERR_UNSUPPORTED, "more than 2^31 - 1 keys in all");
   s = check_ws(ws, ws_bytes, attention_ws_bytes(total_keys + k_active->T, q->H, q->T, n_segs, true));
   if (s != QWM_OK) return s;
   return launch_attention(q, segs, n_segs, total_keys, k_active, v_active, scale, out, lse, top1, ws,

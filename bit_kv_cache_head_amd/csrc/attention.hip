@@ -13,6 +13,8 @@
 //   O^T += V_hat^T P                       (MFMA 32x32x16 f16)
 // Split-key partial results are merged by a second kernel.  Work units are
 // mapped to blocks so that one head's units share an XCD (and its L2).
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace qwm {
@@ -40,7 +42,7 @@ __device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const
 
 struct AttnArgs {
   const void* q; int32_t qdtype; int64_t Tq; int64_t qst; int64_t qsh;
-  const qwm_segment* segs; int32_t n_segs; int32_t nsplit;   // segs: device array; nsplit: splits of its keys
+  const qwm_segment* segs; int32_t n_segs; int32_t nsplit;   // segs: the workspace copy of the descriptors; nsplit: splits of its keys
   int32_t nqb; int32_t units;
   // The active BF16 chunk, attended by the dense units: key t of head h is
   // ka[t * kast + h * kash] (va alike), global key index kbase_a + t.  Units
@@ -115,20 +117,33 @@ __device__ __forceinline__ h2 code_pair(uint32_t w, int sh, const CodeMasks& m) 
 }
 
 // ---------------------------------------------------------------------------
-// fp16 copies of every segment's centroid tables (exact for bf16 values in
-// fp16's normal range), and of its basis as the A operand of (U^T)(Q^T): for
+// Per-call set-up of the segments, from a batch of host descriptors passed by
+// value (kernel arguments, so the caller's array may die when the call
+// returns): the descriptors go to the device array the attention kernel reads;
+// every segment's centroid tables become fp16 copies (exact for bf16 values in
+// fp16's normal range), and its basis becomes the A operand of (U^T)(Q^T): for
 // basis vector n, k-step s and lane half hh, the 8 values U[c][n] at the
 // channels c = 16 s + 4 hh + j / 2 + 8 (j % 2) (j = 0..7) that the Query
 // fragments hold in that position.  Zeros for a segment without a basis.
-// Grid (n_segs * H, 8): block (sh, y) converts centroids 32 y .. +32, thread
-// (centroid 32 y + tid / 8, channels 16 (tid % 8) .. +16), so a wave reads 8
-// whole rows; blocks y = 0 also write the basis fragments.
+// Grid (count * H, 8): block (sh, y) converts centroids 32 y .. +32 of local
+// segment sh / H, head sh % H, thread (centroid 32 y + tid / 8, channels
+// 16 (tid % 8) .. +16), so a wave reads 8 whole rows; blocks y = 0 also write
+// the basis fragments, and block (local segment, head 0, y = 0) its descriptor.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attention_tables_kernel(const qwm_segment* __restrict__ segs, int32_t H,
+constexpr int SEG_BATCH = 24;   // descriptors per launch (2.6 KiB of kernel arguments)
+struct SegBatch {
+  qwm_segment s[SEG_BATCH];
+  int32_t first, count;
+};
+
+__global__ __launch_bounds__(256) void attention_tables_kernel(SegBatch b, int32_t H, qwm_segment* __restrict__ dsegs,
                                                                uint16_t* __restrict__ tabs, uint16_t* __restrict__ ut) {
-  const int sh = blockIdx.x, seg = sh / H, h = sh % H, tid = threadIdx.x;
+  const int local = (int)blockIdx.x / H, h = (int)blockIdx.x % H, tid = threadIdx.x;
+  const int seg = b.first + local, sh = seg * H + h;
   const int j = 32 * (int)blockIdx.y + (tid >> 3), blk = tid & 7;
-  const qwm_segment& sg = segs[seg];
+  const qwm_segment& sg = b.s[local];
+  if (blockIdx.y == 0 && h == 0 && tid < (int)(sizeof(qwm_segment) / 8))
+    reinterpret_cast<uint64_t*>(dsegs + seg)[tid] = reinterpret_cast<const uint64_t*>(&sg)[tid];
   if (blockIdx.y == 0) {
     // four consecutive fragment values (same n, s, hh; j' = 4 (tid % 2) .. +4)
     const int i = 4 * tid, n = i >> 7, s = (i >> 4) & 7, hf = (i >> 3) & 1;
@@ -1018,7 +1033,8 @@ static AttnPlan attention_plan(int64_t Tq, int32_t H, int64_t packed_keys, int64
 // Workspace for n_segs packed segments and up to (splits + 1) partial sets;
 // total_keys counts every key (packed and active).
 size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs, bool active) {
-  size_t bytes = al256((size_t)n_segs * H * 2 * TAB_ELEMS * sizeof(uint16_t)) +
+  size_t bytes = al256((size_t)n_segs * sizeof(qwm_segment)) +
+                 al256((size_t)n_segs * H * 2 * TAB_ELEMS * sizeof(uint16_t)) +
                  al256((size_t)n_segs * H * R * D * sizeof(uint16_t));
   const int ns = attention_splits(Tq, H, total_keys) + (active ? 1 : 0);
   if (ns > 1) {
@@ -1033,7 +1049,7 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
                             int32_t* top1, void* ws, hipStream_t stream) {
   AttnArgs a{};
   a.q = q->ptr; a.qdtype = q->dtype; a.Tq = q->T; a.qst = q->stride_t; a.qsh = q->stride_h;
-  a.segs = segs; a.n_segs = n_segs; a.scale = scale; a.out = out; a.lse = lse; a.top1 = top1; a.H = q->H;
+  a.n_segs = n_segs; a.scale = scale; a.out = out; a.lse = lse; a.top1 = top1; a.H = q->H;
   const int64_t Ta = ka ? ka->T : 0;
   const AttnPlan plan = attention_plan(q->T, q->H, n_segs > 0 ? total_keys : 0, Ta);
   a.nsplit = plan.nsplit; a.nsplit_a = plan.nsplit_a; a.nparts = plan.nparts;
@@ -1046,6 +1062,9 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
     a.Ta = Ta; a.kbase_a = n_segs > 0 ? total_keys : 0;
   }
   char* p = static_cast<char*>(ws);
+  qwm_segment* dsegs = reinterpret_cast<qwm_segment*>(p);
+  p += al256((size_t)n_segs * sizeof(qwm_segment));
+  a.segs = dsegs;
   a.tabs = reinterpret_cast<uint16_t*>(p);
   p += al256((size_t)n_segs * q->H * 2 * TAB_ELEMS * sizeof(uint16_t));
   a.ut = reinterpret_cast<uint16_t*>(p);
@@ -1059,9 +1078,14 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
     a.pti = reinterpret_cast<int32_t*>(p);
   }
   qwm_status s;
-  if (n_segs > 0) {
-    hipLaunchKernelGGL(attention_tables_kernel, dim3((unsigned)(n_segs * q->H), D / 16), dim3(NC), 0, stream, segs,
-                       q->H, const_cast<uint16_t*>(a.tabs), const_cast<uint16_t*>(a.ut));
+  // the host descriptors travel in kernel arguments, SEG_BATCH per launch
+  for (int first = 0; first < n_segs; first += SEG_BATCH) {
+    SegBatch b{};
+    b.first = first;
+    b.count = std::min(SEG_BATCH, n_segs - first);
+    for (int i = 0; i < b.count; ++i) b.s[i] = segs[first + i];
+    hipLaunchKernelGGL(attention_tables_kernel, dim3((unsigned)(b.count * q->H), D / 16), dim3(NC), 0, stream, b,
+                       q->H, dsegs, const_cast<uint16_t*>(a.tabs), const_cast<uint16_t*>(a.ut));
     s = check_launch("attention tables");
     if (s != QWM_OK) return s;
   }

@@ -100,6 +100,9 @@ struct SelectArgs {
   qwm_diag* diag;
   // full-matrix candidate distance: S [H][128][128] fp64, n [H], mu^T S mu [H][256]
   const double* qS; const int64_t* qn; const double* qB;
+  // Lloyd: one bit per token, set for rows with a non-finite channel (they
+  // take no part in the mean update); [H][excl_words] u32
+  uint32_t* excl; int64_t excl_words;
 };
 
 constexpr int MU_ROW = D + 8;   // elements per staged centroid row (16 bytes of padding)
@@ -854,6 +857,7 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
         }
       } else if (lane == 0) {
         a.idx[base] = 0;
+        if (a.excl) atomicOr(a.excl + (int64_t)h * a.excl_words + (tok >> 5), 1u << (tok & 31));
         if (a.diag) atomicAdd((unsigned long long*)&a.diag->nonfinite_rows, 1ull);
       }
       continue;
@@ -1159,7 +1163,35 @@ __device__ __forceinline__ uint64_t splitmix_next(uint64_t& state) {
   return z ^ (z >> 31);
 }
 
-// perm [H][T] int32 workspace.  Grid H, 256 threads.
+// Whether row `row` of head h has only finite channels.
+__device__ __forceinline__ bool row_finite(const void* x, int32_t dtype, int64_t st, int64_t sh, int h, int64_t row) {
+  const int64_t off = (int64_t)h * sh + row * st;
+  uint32_t bad = 0u;
+  if (dtype == QWM_BF16) {
+    const uint4* r = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
+    for (int c = 0; c < D / 8; ++c) {
+      const uint4 v = r[c];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {   // bf16 exponent all ones: Inf or NaN
+        bad |= ((w4[k] & 0x7F80u) == 0x7F80u) | ((w4[k] & 0x7F800000u) == 0x7F800000u);
+      }
+    }
+  } else {
+    const float4* r = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+    for (int c = 0; c < D / 4; ++c) {
+      const float4 v = r[c];
+      bad |= !(__builtin_isfinite(v.x) && __builtin_isfinite(v.y) && __builtin_isfinite(v.z) && __builtin_isfinite(v.w));
+    }
+  }
+  return bad == 0u;
+}
+
+// perm [H][T] int32 workspace.  Grid H, 256 threads.  The first 256 picks of
+// the shuffle are checked in parallel; only when one of them lands on a row
+// with a non-finite channel does thread 0 drop those picks and go on with the
+// shuffle (checking each further pick), leaving zero rows for slots that no
+// finite token fills.
 __global__ __launch_bounds__(256) void forgy_kernel(const void* x, int32_t dtype, int64_t T, int64_t st, int64_t sh,
                                                     uint64_t seed, int32_t* perm, uint16_t* out) {
   const int h = blockIdx.x, tid = threadIdx.x;
@@ -1167,8 +1199,9 @@ __global__ __launch_bounds__(256) void forgy_kernel(const void* x, int32_t dtype
   for (int64_t i = tid; i < T; i += 256) p[i] = (int32_t)i;
   __syncthreads();
   __shared__ int32_t pick[NC];
+  __shared__ uint8_t ok[NC];
+  uint64_t state = seed + ((uint64_t)h << 32);   // thread 0's generator
   if (tid == 0) {
-    uint64_t state = seed + ((uint64_t)h << 32);
     for (int i = 0; i < NC; ++i) {
       const uint64_t r = splitmix_next(state);
       const int64_t j = i + (int64_t)(r % (uint64_t)(T - i));
@@ -1177,12 +1210,28 @@ __global__ __launch_bounds__(256) void forgy_kernel(const void* x, int32_t dtype
     }
   }
   __syncthreads();
+  ok[tid] = row_finite(x, dtype, st, sh, h, pick[tid]) ? 1 : 0;
+  if (__syncthreads_count(ok[tid] == 0) > 0 && tid == 0) {
+    int slot = 0;
+    for (int i = 0; i < NC; ++i)
+      if (ok[i]) pick[slot++] = pick[i];
+    for (int64_t i = NC; slot < NC && i < T; ++i) {
+      const uint64_t r = splitmix_next(state);
+      const int64_t j = i + (int64_t)(r % (uint64_t)(T - i));
+      const int32_t t = p[i]; p[i] = p[j]; p[j] = t;
+      if (row_finite(x, dtype, st, sh, h, p[i])) pick[slot++] = p[i];
+    }
+    for (; slot < NC; ++slot) pick[slot] = -1;
+  }
+  __syncthreads();
   for (int e = tid; e < NC * D; e += 256) {
     const int i = e / D, c = e % D;
-    const int64_t off = (int64_t)h * sh + (int64_t)pick[i] * st + c;
-    uint32_t b;
-    if (dtype == QWM_BF16) b = static_cast<const uint16_t*>(x)[off];
-    else b = f32_to_bf16_bits(static_cast<const float*>(x)[off]);
+    uint32_t b = 0u;
+    if (pick[i] >= 0) {
+      const int64_t off = (int64_t)h * sh + (int64_t)pick[i] * st + c;
+      if (dtype == QWM_BF16) b = static_cast<const uint16_t*>(x)[off];
+      else b = f32_to_bf16_bits(static_cast<const float*>(x)[off]);
+    }
     out[((int64_t)h * NC + i) * D + c] = (uint16_t)b;
   }
 }
@@ -1202,7 +1251,8 @@ __global__ __launch_bounds__(256) void forgy_kernel(const void* x, int32_t dtype
 // centroid is bf16(sum / n); an empty cluster keeps its centroid.
 constexpr int LS_WAVES = 16;
 
-__global__ __launch_bounds__(1024) void lloyd_sort_kernel(const uint8_t* assign, int64_t T, int32_t* ids,
+__global__ __launch_bounds__(1024) void lloyd_sort_kernel(const uint8_t* assign, const uint32_t* excl,
+                                                          int64_t excl_words, int64_t T, int32_t* ids,
                                                           int32_t* start) {
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   __shared__ int32_t cnt[LS_WAVES][NC];     // counts, then running offsets
@@ -1210,8 +1260,10 @@ __global__ __launch_bounds__(1024) void lloyd_sort_kernel(const uint8_t* assign,
   for (int e = tid; e < LS_WAVES * NC; e += 1024) (&cnt[0][0])[e] = 0;
   __syncthreads();
   const uint8_t* ah = assign + (int64_t)h * T;
+  const uint32_t* eh = excl + (int64_t)h * excl_words;
   const int64_t r0 = T * wv / LS_WAVES, r1 = T * (wv + 1) / LS_WAVES;
-  for (int64_t t = r0 + lane; t < r1; t += 64) atomicAdd(&cnt[wv][ah[t]], 1);
+  for (int64_t t = r0 + lane; t < r1; t += 64)
+    if (!((eh[t >> 5] >> (t & 31)) & 1u)) atomicAdd(&cnt[wv][ah[t]], 1);
   __syncthreads();
   if (tid < NC) {
     int32_t run = 0;
@@ -1234,6 +1286,8 @@ __global__ __launch_bounds__(1024) void lloyd_sort_kernel(const uint8_t* assign,
     int32_t run = inc - sum;
 #pragma unroll
     for (int i = 0; i < 4; ++i) { tot[4 * lane + i] = run; run += v[i]; }
+    // members in all: the end of the last cluster (excluded rows are not members)
+    if (lane == 63) start[h * (NC + 1) + NC] = run;
   }
   __syncthreads();
   if (tid < NC) {
@@ -1242,12 +1296,11 @@ __global__ __launch_bounds__(1024) void lloyd_sort_kernel(const uint8_t* assign,
 #pragma unroll
     for (int w = 0; w < LS_WAVES; ++w) cnt[w][tid] += base;
   }
-  if (tid == 0) start[h * (NC + 1) + NC] = (int32_t)T;
   __syncthreads();
   int32_t* idh = ids + (int64_t)h * T;
   for (int64_t t0 = r0; t0 < r1; t0 += 64) {
     const int64_t t = t0 + lane;
-    const bool valid = t < r1;
+    const bool valid = t < r1 && !((eh[t >> 5] >> (t & 31)) & 1u);
     const uint32_t key = valid ? ah[t] : 0u;
     uint64_t m = __ballot(valid);
 #pragma unroll
@@ -1344,12 +1397,14 @@ using namespace qwm;
 
 struct SelWork {
   uint16_t* aug; float* Bj; float* Bmax; double* Wg; int32_t* counter; int32_t* worklist; double* qB;
-  uint8_t* assign; int32_t* perm; int32_t* start;
+  uint8_t* assign; int32_t* perm; int32_t* start; uint32_t* excl;
 };
 
-static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd) {
+static constexpr int64_t excl_words(int64_t T) { return (T + 31) / 32; }
+
+constexpr size_t select_ws_bytes_c(int64_t T, int32_t H, bool lloyd) {
   size_t b = 0;
   b += align256((size_t)H * NC * 4 * 2);
   b += align256((size_t)H * NC * 4);
@@ -1362,9 +1417,12 @@ size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd) {
     b += align256((size_t)H * T);
     b += align256((size_t)H * T * 4);
     b += align256((size_t)H * (NC + 1) * 4);
+    b += align256((size_t)H * excl_words(T) * 4);
   }
   return b;
 }
+
+size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd) { return select_ws_bytes_c(T, H, lloyd); }
 
 static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd) {
   char* p = static_cast<char*>(ws);
@@ -1381,6 +1439,7 @@ static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd) {
     w.assign = reinterpret_cast<uint8_t*>(take((size_t)H * T));
     w.perm = reinterpret_cast<int32_t*>(take((size_t)H * T * 4));
     w.start = reinterpret_cast<int32_t*>(take((size_t)H * (NC + 1) * 4));
+    w.excl = reinterpret_cast<uint32_t*>(take((size_t)H * excl_words(T) * 4));
   }
   return w;
 }
@@ -1535,17 +1594,26 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
       return check_launch("centroid copy");
     return QWM_OK;
   }
+  if (iters > 0) {   // no row excluded yet: the exact path marks non-finite rows
+    const int64_t eb = (int64_t)x->H * excl_words(x->T) * 4;
+    const int64_t eblocks = (eb + 255) / 256;
+    hipLaunchKernelGGL(clear_bytes_kernel, dim3((unsigned)(eblocks < 1024 ? eblocks : 1024)), dim3(256), 0, stream,
+                       reinterpret_cast<uint8_t*>(wk.excl), eb);
+    qwm_status s = check_launch("Lloyd exclusion clear");
+    if (s != QWM_OK) return s;
+  }
   for (int it = 0; it < iters; ++it) {
     qwm_status s = prep(wk, cur, nullptr, x->H, stream);
     if (s != QWM_OK) return s;
     SelectArgs a{};
     fill_common(a, x, wk, cur);
     a.M = 1; a.flags = 0; a.cb = error_coeff(x->dtype != QWM_BF16);
-    a.idx = wk.assign; a.diag = diag;
+    a.idx = wk.assign; a.diag = diag; a.excl = wk.excl; a.excl_words = excl_words(x->T);
     s = run_select<MODE_ASSIGN>(x, a, stream, "Lloyd assignment");
     if (s != QWM_OK) return s;
     // the Forgy permutation is dead by now: its buffer holds the sorted members
-    hipLaunchKernelGGL(lloyd_sort_kernel, dim3(x->H), dim3(1024), 0, stream, wk.assign, x->T, wk.perm, wk.start);
+    hipLaunchKernelGGL(lloyd_sort_kernel, dim3(x->H), dim3(1024), 0, stream, wk.assign, wk.excl, excl_words(x->T),
+                       x->T, wk.perm, wk.start);
     s = check_launch("Lloyd member sort");
     if (s != QWM_OK) return s;
     const int64_t units = (int64_t)x->H * NC;

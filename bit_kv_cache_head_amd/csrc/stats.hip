@@ -267,7 +267,7 @@ __device__ void orthonormalize(EigShared& sm, double (*src)[PP], double (*dst)[P
     if (ps == 1) {
       uint32_t weak = 0;
 #pragma unroll
-      for (int j = 0; j < P; ++j) weak |= (sm.G[j][j] < 0.1 ? 1u : 0u) << j;
+      for (int j = 0; j < P; ++j) weak |= (!(sm.G[j][j] >= 0.1) ? 1u : 0u) << j;   // NaN counts as weak
       if (weak) {                       // uniform: every thread read the same diagonal
         ++salt;
         for (int e = tid; e < D * P; e += 256) {
@@ -404,11 +404,15 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ S, 
     tr = wave_sum_d(tr);
     if (l == 0) sm.trace = tr;
   }
-  // start: previous basis (if any) in columns 0..7, hashed vectors elsewhere
+  // start: previous basis (if any) in columns 0..7, hashed vectors elsewhere.
+  // A stored basis with a non-finite entry (e.g. never initialised) is ignored.
   {
-    int mine = 0;
-    for (int e = tid; e < D * R; e += 256) mine |= (Uh[e] != 0);
-    const bool have_prev = __syncthreads_or(mine) != 0;
+    int mine = 0, bad = 0;
+    for (int e = tid; e < D * R; e += 256) {
+      mine |= (Uh[e] != 0);
+      bad |= !is_finite_f(bf16_bits_to_f32(Uh[e]));
+    }
+    const bool have_prev = __syncthreads_or(mine) != 0 && __syncthreads_or(bad) == 0;
     for (int e = tid; e < D * P; e += 256) {
       const int i = e / P, j = e % P;
       double v;

@@ -5,7 +5,9 @@
  * Video Generation", arXiv 2609.26425 v2), for AMD MI355X (gfx950).
  *
  * Conventions shared by every call
- *  - Every buffer argument is DEVICE memory owned by the caller.  The library
+ *  - Every buffer argument is DEVICE memory owned by the caller, except the
+ *    descriptor arrays (qwm_tokens, qwm_qstats, qwm_packed, qwm_segment),
+ *    which live on the host and are read during the call only.  The library
  *    never allocates, frees or keeps a pointer after a call returns.
  *  - Every call validates its arguments on the host first (no HIP call is made
  *    when validation fails), then only enqueues kernels on `stream` (a
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define QWM_ABI_VERSION 3
+#define QWM_ABI_VERSION 4
 #define QWM_HEAD_DIM 128
 #define QWM_GROUP 64
 #define QWM_CENTROIDS 256
@@ -90,7 +92,9 @@ typedef struct {
   double* S;        /* [H][d][d] running sum of q q^T (in/out) */
   int64_t* n;       /* [H] Queries seen so far (in/out) */
   float* w;         /* [H][d] channel sensitivity diag(S)/n, 1 while n == 0 (out) */
-  uint16_t* U;      /* [H][d][r] bf16 top-r eigenvectors of S/n (out; zero while n == 0) */
+  uint16_t* U;      /* [H][d][r] bf16 top-r eigenvectors of S/n (in/out: a finite nonzero U warm-starts
+                       the eigen-solver; zero it, or leave the previous output, before a call;
+                       a U with a non-finite entry is ignored; zero while n == 0) */
   float* lambda;    /* [H][r] their eigenvalues, descending (out) */
   float* energy;    /* [H] sum of the top-r eigenvalues / trace (out) */
   int32_t* iters;   /* [H] eigen-iterations used, negative if not converged; may be NULL */
@@ -193,18 +197,24 @@ qwm_status qwm_quantize_values(const qwm_tokens* v, const uint16_t* centroids, c
  * out = softmax(scale * (Q K0_hat^T + (Q U) (c_scale c)^T)) V_hat
  * (the logit-side PSAC compensation of QuantWM's method section; the logits
  * of Sec. 3.3 with scale = 1/sqrt(d)).
- * segs: DEVICE array of n_segs descriptors (1 <= n_segs <= 4096), each with
- * 1 <= T < 2^26 tokens (the kernel addresses a segment's packed arrays through
- * 32-bit buffer ranges; the descriptors live on the device, so this is the
- * caller's contract, not a checked error); keys are numbered in segment order.
+ * segs: HOST array of n_segs descriptors (1 <= n_segs <= 4096) whose pointers
+ * address device memory.  The library validates every descriptor before any
+ * HIP call (QWM_ERR_ARG: T outside [1, 2^26) -- the kernel reaches a
+ * segment's rows through 32-bit buffer ranges --, a null packed array or
+ * table, a basis without coefficients, codes / tables / U not 16-byte, scales
+ * / zeros not 4-byte, c not 8-byte aligned; QWM_ERR_UNSUPPORTED: 2^31 keys or
+ * more in all), sums the keys itself and copies the descriptors into the
+ * workspace through kernel arguments, so the host array may be freed as soon
+ * as the call returns.  Keys are numbered in segment order.
+ * q: bf16 or fp32 [Tq][H][d]; its values must lie in fp16's range
+ * (|q| <= 65504), as must every centroid value and every reconstruction
+ * mu + s (q - z): the dequantized tiles and Q are fp16 MFMA operands.
  * out [Tq][H][d] fp32; lse [H][Tq] fp32 (natural log of the softmax
  * denominator, may be NULL); top1 [H][Tq] int32 = argmax of the logits over
  * all keys (may be NULL).  Workspace: QWM_OP_ATTENTION with T = total keys,
- * n = Tq (query count) and n_segs.  Centroid values must lie in fp16's range
- * (|x| <= 65504): the dequantized tiles are fp16 MFMA operands. */
-qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs,
-                         int64_t total_keys, float scale, float* out, float* lse, int32_t* top1,
-                         void* ws, size_t ws_bytes, qwm_stream stream);
+ * n = Tq (query count) and n_segs. */
+qwm_status qwm_attention(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, float scale, float* out,
+                         float* lse, int32_t* top1, void* ws, size_t ws_bytes, qwm_stream stream);
 
 /* Log-sum-exp merge of two attention results of the same Queries over
  * disjoint key sets, e.g. the cached chunks and the newest one, computed by two
@@ -222,16 +232,17 @@ qwm_status qwm_attention_merge(const float* out_a, const float* lse_a, const flo
 
 /* qwm_attention over the packed segments plus the active chunk, which stays
  * BF16 until it completes (QuantWM App. D.1: completed chunks are packed, the
- * active one is kept as it is).  k_active, v_active: [Ta][H][d] bf16 token
- * descriptors (Ta >= 1, H equal to the queries', rows 16-byte aligned,
- * Ta * stride_t < 2^30 elements); row values must lie in fp16's range (the
- * kernel's tiles are fp16 MFMA operands).  n_segs may be 0 (then segs may be
- * NULL and total_keys must be 0).  Keys are numbered packed segments first,
- * then the active chunk (index total_keys + t), for top1.  The active chunk
- * runs on its own key splits in the same launch; the log-sum-exp merge joins
- * them.  Workspace: QWM_OP_ATTENTION_ACTIVE with T = total_keys + Ta, n = Tq
- * and n_segs. */
-qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs, int64_t total_keys,
+ * active one is kept as it is).  segs: host array as for qwm_attention, same
+ * checks; n_segs may be 0 (then segs may be NULL).  k_active, v_active:
+ * [Ta][H][d] bf16 token descriptors (Ta >= 1, H equal to the queries', rows
+ * 16-byte aligned, Ta * stride_t < 2^30 elements); row values must lie in
+ * fp16's range (the kernel's tiles are fp16 MFMA operands).  Keys are
+ * numbered packed segments first, then the active chunk (index
+ * sum of the segments' T + t), for top1.  The active chunk runs on its own
+ * key splits in the same launch; the log-sum-exp merge joins them.
+ * Workspace: QWM_OP_ATTENTION_ACTIVE with T = all keys (packed + active),
+ * n = Tq and n_segs. */
+qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, int32_t n_segs,
                                 const qwm_tokens* k_active, const qwm_tokens* v_active, float scale, float* out,
                                 float* lse, int32_t* top1, void* ws, size_t ws_bytes, qwm_stream stream);
 
@@ -270,9 +281,10 @@ qwm_status qwm_reference_top1(const qwm_tokens* q, const qwm_tokens* k, int32_t*
 
 /* Bytes of workspace an operation needs (256-byte aligned pointer required).
  * QWM_OP_ATTENTION: T = total cached keys, n = number of queries, n_segs =
- * number of segments.  The workspace holds fp16 copies of every segment's
- * centroid tables (n_segs * H * 128 KiB), every segment's U_r as fp16 MFMA
- * fragments (n_segs * H * 2 KiB) and the split-key partials.
+ * number of segments.  The workspace holds the segment descriptors, fp16
+ * copies of every segment's centroid tables (n_segs * H * 128 KiB), every
+ * segment's U_r as fp16 MFMA fragments (n_segs * H * 2 KiB) and the split-key
+ * partials.
  * QWM_OP_ATTENTION_ACTIVE: the same with T = all keys (packed + active) and
  * one more partial set.  The other operations ignore n and n_segs. */
 size_t qwm_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t n, int32_t n_segs);

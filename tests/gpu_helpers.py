@@ -104,3 +104,18 @@ def compare_codec(orc: dict, gpu: dict, T: int, mask: np.ndarray):
     np.testing.assert_array_equal(gpu["scale_bits"][mask], orc["scale_bits"][mask])
     gz = F.unpack_zeros(gpu["zeros"][: (T + 1) // 2], T)
     np.testing.assert_array_equal(gz[mask], orc["zero"][mask])
+
+
+def check_top1_near_tie(gt, ot, Qh, oracle_segs):
+    """Top-1 must agree except where the oracle's top-2 logit gap is below
+    1e-3 relative: every mismatch must be such a near-tie.  gt, ot: GPU and
+    oracle top-1 of the Queries Qh [n, d]; oracle_segs: the oracle's segment
+    dicts of the head.  Returns the number of (allowed) mismatches."""
+    from oracle import attention as OA
+    Kall = np.concatenate([OA.segment_kv(s)[0] for s in oracle_segs])
+    L = np.asarray(Qh, np.float64) @ Kall.T
+    bad = np.nonzero(np.asarray(gt) != np.asarray(ot))[0]
+    for i in bad:
+        a, b = L[i, ot[i]], L[i, gt[i]]
+        assert abs(a - b) <= 1e-3 * abs(a), (int(i), a, b)
+    return len(bad)

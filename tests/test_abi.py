@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert sorted(_abi.EXPORTS) == declared
     for name in declared:
         assert hasattr(_abi.lib, name), name
-    assert _abi.lib.qwm_abi_version() == 3
+    assert _abi.lib.qwm_abi_version() == 4
 
 
 def test_struct_layouts_match_header_sizes():
@@ -45,9 +45,9 @@ def test_sizes_and_strides():
     k = lib.qwm_workspace_bytes(2, 1560, 12, 0, 0)
     assert k >= 12 * 256 * 4 * 2 + 12 * 1560 * 4          # B_j split per centroid + fallback worklist
     assert lib.qwm_workspace_bytes(1, 1560, 12, 0, 0) > k       # Lloyd adds assignment + shuffle
-    # attention: fp16 centroid tables for every (segment, head), plus split partials
-    # one split: fp16 centroid tables and basis fragments only
-    assert lib.qwm_workspace_bytes(4, 64, 1, 16, 1) == 2 * 256 * 128 * 2 + 8 * 128 * 2
+    # attention: the segment descriptors, fp16 centroid tables for every (segment, head),
+    # plus split partials; one split: descriptors, tables and basis fragments only
+    assert lib.qwm_workspace_bytes(4, 64, 1, 16, 1) == 256 + 2 * 256 * 128 * 2 + 8 * 128 * 2
     big = lib.qwm_workspace_bytes(4, 39000, 12, 1560, 25)
     assert big >= 25 * 12 * 2 * 256 * 128 * 2
     assert lib.qwm_workspace_bytes(4, 39000, 12, 1560, 0) == 0
@@ -101,12 +101,59 @@ def test_other_validation_paths():
     qs.r, qs.H = 8, 3
     assert lib.qwm_update_query_stats(C.byref(t), C.byref(qs), 1, None, 0, None) == 1
     # attention: segments, scale
-    assert lib.qwm_attention(C.byref(t), None, 1, 10, C.c_float(0.1), C.c_void_p(0x1000), None, None,
+    segs = _segs(3)
+    assert lib.qwm_attention(C.byref(t), None, 1, C.c_float(0.1), C.c_void_p(0x1000), None, None,
                              None, 0, None) == 1
-    assert lib.qwm_attention(C.byref(t), C.c_void_p(0x1000), 0, 10, C.c_float(0.1), C.c_void_p(0x1000),
+    assert lib.qwm_attention(C.byref(t), segs, 0, C.c_float(0.1), C.c_void_p(0x1000),
                              None, None, None, 0, None) == 1
-    assert lib.qwm_attention(C.byref(t), C.c_void_p(0x1000), 1, 10, C.c_float(-1.0), C.c_void_p(0x1000),
+    assert lib.qwm_attention(C.byref(t), segs, 3, C.c_float(-1.0), C.c_void_p(0x1000),
                              None, None, None, 0, None) == 1
+    # valid descriptors but no workspace: the workspace check comes last
+    assert lib.qwm_attention(C.byref(t), segs, 3, C.c_float(0.1), C.c_void_p(0x1000),
+                             None, None, None, 0, None) == 3
+
+
+def _segs(n, T=100):
+    """Host descriptors with aligned (never dereferenced) device addresses."""
+    from bit_kv_cache_head_amd._abi import Segment
+    arr = (Segment * n)()
+    for i in range(n):
+        s = arr[i]
+        base = 0x100000 * (i + 1)
+        for k, name in enumerate(["k_codes", "k_idx", "k_scale", "k_zeros", "k_c", "k_c_scale", "v_codes",
+                                  "v_idx", "v_scale", "v_zeros", "k_centroids", "v_centroids", "U"]):
+            setattr(s, name, base + 0x1000 * k)
+        s.T = T
+    return arr
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("T", 0, 1), ("T", 1 << 26, 1), ("T", -5, 1), ("k_codes", 0, 1), ("v_centroids", 0, 1),
+    ("k_codes", 0x100004, 1), ("k_scale", 0x100002, 1), ("U", 0x100008, 1), ("k_c", 0x100004, 1),
+])
+def test_attention_segment_validation(field, value, code):
+    """Every host descriptor is checked before any HIP call: a bad segment T,
+    a null array or a misaligned pointer in segment 1 of 3 is QWM_ERR_ARG."""
+    from bit_kv_cache_head_amd._abi import lib
+    t = _tok()
+    segs = _segs(3)
+    setattr(segs[1], field, value)
+    ws = C.c_void_p(0x10000000)
+    args = (C.c_float(0.1), C.c_void_p(0x1000), None, None, ws, 1 << 40, None)
+    assert lib.qwm_attention(C.byref(t), segs, 3, *args) == code
+    assert b"segment 1" in lib.qwm_last_error()
+    ka = _tok(ptr=0x2000, T=8)
+    assert lib.qwm_attention_active(C.byref(t), segs, 3, C.byref(ka), C.byref(ka), *args) == code
+
+
+def test_attention_total_keys_limit():
+    """Keys are summed on the host: 2^31 or more in all is refused."""
+    from bit_kv_cache_head_amd._abi import lib
+    t = _tok()
+    segs = _segs(40, T=(1 << 26) - 1)
+    assert lib.qwm_attention(C.byref(t), segs, 40, C.c_float(0.1), C.c_void_p(0x1000), None, None,
+                             C.c_void_p(0x10000000), 1 << 40, None) == 2
+    assert b"2^31" in lib.qwm_last_error()
 
 
 def test_reference_top1_validation():

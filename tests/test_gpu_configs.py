@@ -188,7 +188,8 @@ def _random_cache(qwm, H, sizes, seed):
         keep.append((kp, vp, kc, vc, U))
         lst.append((kp, vp, kc, vc, U))
         torch.cuda.synchronize()
-    dseg, total = qwm.segments_tensor(lst)
+    dseg = qwm.segment_array(lst)
+    total = dseg.total
     return dseg, total, keep, (lambda h: [head(s, h) for s in range(len(sizes))])
 
 
@@ -200,12 +201,12 @@ ATTN = [("720p", [3600] * 25, 3600, 40), ("depth", [28000], 1560, 40), ("rollout
 @pytest.mark.parametrize("name,sizes,tq,H", ATTN)
 def test_attention_full_shapes(qwm, name, sizes, tq, H):
     import torch
-    from gpu_helpers import dev_tokens
+    from gpu_helpers import dev_tokens, check_top1_near_tie
     _log(f"attention full shape {name}: H={H}, {len(sizes)} segments, {sum(sizes)} keys, {tq} queries")
     dseg, total, keep, oseg = _random_cache(qwm, H, sizes, seed={"720p": 71, "depth": 72, "rollout": 73, "tiny": 74}[name])
     dtype = "f32" if name == "tiny" else "bf16"
     Qv = datagen.make_workload(name, heads=list(range(H)), n_chunks=1, chunk=tq, n_queries=tq).Q
-    out, lse, top1 = qwm.attention(dev_tokens(Qv, dtype), dseg, len(sizes), total, want_lse=True, want_top1=True)
+    out, lse, top1 = qwm.attention(dev_tokens(Qv, dtype), dseg, want_lse=True, want_top1=True)
     torch.cuda.synchronize()
     out, lse, top1 = out.cpu().numpy(), lse.cpu().numpy(), top1.cpu().numpy()
     sample = np.unique(np.array([0, 1, 31, 32, 255, 256, tq // 2, tq - 2, tq - 1]))
@@ -218,7 +219,8 @@ def test_attention_full_shapes(qwm, name, sizes, tq, H):
         _log(f"  head {h}: rel L2 {err:.2e}")
         assert err <= 2e-3
         np.testing.assert_allclose(lse[h, sample], L, rtol=1e-4, atol=1e-4)
-        assert np.mean(top1[h, sample] == top) >= 0.8   # top-1 of sampled rows (near-ties aside)
+        nt = check_top1_near_tie(top1[h, sample], top, Qh, oseg(h))
+        _log(f"  head {h}: top-1 ok ({nt} counted near-ties)")
 
 
 def test_tiny_config_end_to_end(qwm):
@@ -236,8 +238,9 @@ def test_tiny_config_end_to_end(qwm):
     Cv = qwm.build_centroids(dev_tokens(V, "f32"), 10, seed=102)
     kp = qwm.quantize_keys(dev_tokens(K, "f32"), Ck, st.w, st.U, M=8, flags=3)
     vp = qwm.quantize_values(dev_tokens(V, "f32"), Cv)
-    segs, total = qwm.segments_tensor([(kp, vp, Ck, Cv, st.U)])
-    out, lse, top1 = qwm.attention(dev_tokens(Q, "f32"), segs, 1, total, want_lse=True, want_top1=True)
+    segs = qwm.segment_array([(kp, vp, Ck, Cv, st.U)])
+    total = segs.total
+    out, lse, top1 = qwm.attention(dev_tokens(Q, "f32"), segs, want_lse=True, want_top1=True)
     torch.cuda.synchronize()
     # oracle pipeline
     S, n = OS.update(np.zeros((128, 128)), 0, Q[:, 0])
