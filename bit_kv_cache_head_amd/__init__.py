@@ -156,6 +156,20 @@ def quantize_keys(k: torch.Tensor, centroids: torch.Tensor, w: torch.Tensor | No
     return out
 
 
+def quantize_keys_noalloc(k: torch.Tensor, centroids: torch.Tensor, w: torch.Tensor | None, U: torch.Tensor | None,
+                          M: int = 8, flags: int = QWM_QSAC | QWM_PSAC, out: PackedChunk | None = None,
+                          diag: torch.Tensor | None = None) -> PackedChunk:
+    """quantize_keys without a workspace: the library's static device scratch
+    (at most 64 heads and 2^21 token-heads per call; calls that overlap on one
+    device race)."""
+    td = _tokens(k)
+    if out is None:
+        out = PackedChunk(td.T, td.H, True, k.device)
+    check(lib.qwm_quantize_keys_noalloc(C.byref(td), _ptr(centroids), _ptr(w), _ptr(U), M, flags,
+                                        C.byref(out.desc()), _ptr(diag), _stream()))
+    return out
+
+
 def quantize_keys_fullq(k: torch.Tensor, centroids: torch.Tensor, S: torch.Tensor, n: torch.Tensor,
                         w: torch.Tensor | None, U: torch.Tensor | None, M: int = 8,
                         flags: int = QWM_QSAC | QWM_PSAC, out: PackedChunk | None = None,

@@ -11,9 +11,11 @@ QWM_OK, QWM_ERR_ARG, QWM_ERR_UNSUPPORTED, QWM_ERR_WORKSPACE, QWM_ERR_HIP = 0, 1,
 QWM_F32, QWM_BF16 = 0, 1
 QWM_QSAC, QWM_PSAC, QWM_PSAC_KEEP = 1, 2, 4
 QWM_OP_STATS, QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION, QWM_OP_ATTENTION_ACTIVE = 0, 1, 2, 3, 4, 5
+QWM_NOALLOC_MAX_HEADS, QWM_NOALLOC_MAX_TOKEN_HEADS = 64, 1 << 21
 
 # every symbol include/quantwm.h declares
-EXPORTS = ["qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys", "qwm_quantize_keys_fullq",
+EXPORTS = ["qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys", "qwm_quantize_keys_noalloc",
+           "qwm_quantize_keys_fullq",
            "qwm_quantize_values", "qwm_attention", "qwm_attention_merge", "qwm_attention_active", "qwm_decode_segment", "qwm_centroid_residual", "qwm_reference_top1", "qwm_workspace_bytes", "qwm_zeros_stride", "qwm_last_error", "qwm_abi_version"]
 
 
@@ -55,6 +57,7 @@ def _load():
     L.qwm_update_query_stats.argtypes = [P, P, C.c_int32, P, C.c_size_t, P]
     L.qwm_build_centroids.argtypes = [P, C.c_int32, C.c_int32, C.c_uint64, P, P, P, P, C.c_size_t, P]
     L.qwm_quantize_keys.argtypes = [P, P, P, P, C.c_int32, C.c_uint32, P, P, P, C.c_size_t, P]
+    L.qwm_quantize_keys_noalloc.argtypes = [P, P, P, P, C.c_int32, C.c_uint32, P, P, P]
     L.qwm_quantize_keys_fullq.argtypes = [P, P, P, P, P, P, C.c_int32, C.c_uint32, P, P, P, C.c_size_t, P]
     L.qwm_quantize_values.argtypes = [P, P, P, P, P, C.c_size_t, P]
     L.qwm_attention.argtypes = [P, P, C.c_int32, C.c_float, P, P, P, P, C.c_size_t, P]
@@ -69,7 +72,8 @@ def _load():
     L.qwm_zeros_stride.restype = C.c_int64
     L.qwm_last_error.restype = C.c_char_p
     L.qwm_abi_version.restype = C.c_int32
-    for name in ("qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys", "qwm_quantize_keys_fullq",
+    for name in ("qwm_update_query_stats", "qwm_build_centroids", "qwm_quantize_keys", "qwm_quantize_keys_noalloc",
+                 "qwm_quantize_keys_fullq",
                  "qwm_quantize_values", "qwm_attention", "qwm_attention_merge", "qwm_attention_active",
                  "qwm_decode_segment", "qwm_centroid_residual"):
         getattr(L, name).restype = C.c_int

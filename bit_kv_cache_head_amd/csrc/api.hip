@@ -45,6 +45,7 @@ qwm_status launch_decode(const qwm_segment* seg, int32_t H, uint16_t* k_out, uin
 qwm_status launch_centroid_residual(const qwm_tokens* x, const uint16_t* centroids, const uint8_t* idx, float* out,
                                    int64_t ost, int64_t osh, hipStream_t stream);
 size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd);
+qwm_status noalloc_keys_scratch(void** ptr);
 size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs, bool active);
 
 static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -166,6 +167,21 @@ qwm_status qwm_quantize_keys(const qwm_tokens* k, const uint16_t* centroids, con
   if (s != QWM_OK) return s;
   s = check_ws(ws, ws_bytes, select_ws_bytes(k->T, k->H, false));
   if (s != QWM_OK) return s;
+  return launch_keys(k, centroids, w, U, (flags & QWM_QSAC) ? M : 1, flags, out, diag, ws,
+                     static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_quantize_keys_noalloc(const qwm_tokens* k, const uint16_t* centroids, const float* w,
+                                     const uint16_t* U, int32_t M, uint32_t flags, const qwm_packed* out,
+                                     qwm_diag* diag, qwm_stream stream) {
+  qwm_status s = check_keys_args(k, centroids, w, U, M, flags, out, diag);
+  if (s != QWM_OK) return s;
+  if (k->H > QWM_NOALLOC_MAX_HEADS || (int64_t)k->H * k->T > (int64_t)QWM_NOALLOC_MAX_TOKEN_HEADS)
+    return fail(QWM_ERR_UNSUPPORTED, "no-allocation keys: at most " + std::to_string(QWM_NOALLOC_MAX_HEADS) +
+                                         " heads and " + std::to_string(QWM_NOALLOC_MAX_TOKEN_HEADS) +
+                                         " token-heads (H * T) per call");
+  void* ws = nullptr;
+  if ((s = noalloc_keys_scratch(&ws)) != QWM_OK) return s;
   return launch_keys(k, centroids, w, U, (flags & QWM_QSAC) ? M : 1, flags, out, diag, ws,
                      static_cast<hipStream_t>(stream));
 }

@@ -9,6 +9,8 @@
 // with a certified error |f_j - e_j| <= c (||k||_w^2 + B_j).  A token whose
 // choice the bound cannot certify (close runners-up, non-finite values) is
 // sent to an exact fp64 path; no result depends on the approximation.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace qwm {
@@ -1423,6 +1425,41 @@ constexpr size_t select_ws_bytes_c(int64_t T, int32_t H, bool lloyd) {
 }
 
 size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd) { return select_ws_bytes_c(T, H, lloyd); }
+
+// ---------------------------------------------------------------------------
+// Scratch of qwm_quantize_keys_noalloc, for callers that cannot allocate: the
+// workspace of one key call of at most NOALLOC_MAX_H heads and
+// NOALLOC_MAX_TH token-heads, in a static device array (one per device, held
+// until the process ends).  Host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device.
+// ---------------------------------------------------------------------------
+constexpr int32_t NOALLOC_MAX_H = QWM_NOALLOC_MAX_HEADS;
+constexpr int64_t NOALLOC_MAX_TH = QWM_NOALLOC_MAX_TOKEN_HEADS;
+constexpr size_t NOALLOC_BYTES = select_ws_bytes_c(NOALLOC_MAX_TH / NOALLOC_MAX_H, NOALLOC_MAX_H, false);
+}  // namespace qwm_host
+
+static __device__ __align__(256) uint8_t scratch[qwm_host::NOALLOC_BYTES];
+
+namespace qwm_host {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static void* g_scratch_ptr[NOALLOC_MAX_DEVICES];
+static hipError_t g_scratch_err[NOALLOC_MAX_DEVICES];
+static std::once_flag g_scratch_once[NOALLOC_MAX_DEVICES];
+
+// Device address of the current device's scratch (looked up once per device).
+qwm_status noalloc_keys_scratch(void** ptr) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QWM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return fail(QWM_ERR_UNSUPPORTED, "device ordinal beyond 63");
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess)
+    return fail(QWM_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(g_scratch_err[dev]));
+  *ptr = g_scratch_ptr[dev];
+  return QWM_OK;
+}
 
 static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd) {
   char* p = static_cast<char*>(ws);

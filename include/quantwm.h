@@ -171,6 +171,25 @@ qwm_status qwm_quantize_keys(const qwm_tokens* k, const uint16_t* centroids, con
                              const uint16_t* U, int32_t M, uint32_t flags, const qwm_packed* out,
                              qwm_diag* diag, void* ws, size_t ws_bytes, qwm_stream stream);
 
+/* qwm_quantize_keys for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and results, with no workspace argument.  The scratch they need
+ * lives in a static device array of the library, one per device (about
+ * 8.6 MB, held until the process ends), sized for at most
+ * QWM_NOALLOC_MAX_HEADS heads and QWM_NOALLOC_MAX_TOKEN_HEADS token-heads
+ * (H * T) per call; larger calls return QWM_ERR_UNSUPPORTED before any HIP
+ * call.  Every call on one device shares that array: calls that may overlap
+ * on one device (different streams, or threads without ordering) race and
+ * must be ordered by the caller.  Each call re-initialises what it reads
+ * (the work counter is cleared by its own first kernel, no memset), so no
+ * state carries over from the previous call.  The call allocates and frees
+ * nothing; its first call on a device looks up the array's address. */
+#define QWM_NOALLOC_MAX_HEADS 64
+#define QWM_NOALLOC_MAX_TOKEN_HEADS (1 << 21)
+qwm_status qwm_quantize_keys_noalloc(const qwm_tokens* k, const uint16_t* centroids, const float* w,
+                                     const uint16_t* U, int32_t M, uint32_t flags, const qwm_packed* out,
+                                     qwm_diag* diag, qwm_stream stream);
+
 /* The full-matrix ablation of QSAC (QuantWM App. C.4): as qwm_quantize_keys
  * with QWM_QSAC set, except that the M candidates are the M smallest by
  * ((k - mu)^T M_h (k - mu), index), M_h = S_h / n_h the Query second-moment
