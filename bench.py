@@ -1,25 +1,30 @@
 """Benchmark of the QuantWM 2-bit KV-cache hot path on one MI355X.
 
-Default workload (480p): one step = one streaming chunk of the 480p-shaped
-single-layer cache (H = 12 heads, d = 128; 24 cached latent frames of
-30x52 = 1,560 tokens plus the new frame): update the Query statistics with the
-previous chunk's Queries and re-derive the principal basis, refresh the K and V
-centroid tables with 3 warm-started Lloyd iterations, quantize the new Keys
-(QSAC + PSAC, M = 8) and Values, then attend with the new chunk's 1,560 Queries
-over all 39,000 cached keys in 25 compressed segments.  Inputs are seeded
-synthetic caches resident in HBM.
+Default workload (depth): the full-depth memory case.  40 layers x 40 heads x
+d = 128, 28,000 cached tokens per layer (about 21.4 GiB of bf16 K + V), all
+resident in HBM, drawn on the device from the seeded recipe.  One step is the
+whole hot path over every layer: update the Query statistics from the layer's
+1,560 Queries and derive the principal basis, build the K and V centroid tables
+(10 seeded Lloyd iterations each), quantize the Keys (QSAC + PSAC, M = 8) and
+the Values, then attend with the 1,560 Queries over the layer's 2-bit cache.
 
-Other workloads (--workload):
-  720p    the same streaming step with H = 40 and 3,600-token chunks
+`value` is the metric's first half: Key tokens quantized per second by
+qwm_quantize_keys (QSAC + PSAC), token positions across all heads, from HIP
+events around every key call of the timed steps.  `roofline` is the
+compressed-cache attention's MFMA fraction (the metric's second half), from
+HIP events around every attention call.  Per-stage rooflines, resident bytes
+and compression ratio, device counters, the rollout ablations (token-shift
+rates) and the CPU oracle baseline with a parity sample ride along.
+
+Other workloads (--workload), parity-test shapes reported for context:
+  480p    streaming step of the 480p-shaped layer (H = 12, 25 x 1,560-token chunks)
+  720p    the same with H = 40 and 3,600-token chunks
   tiny    one pass: 4,096 fp32 keys/values, 512 Queries, 10 seeded Lloyd iterations
-  depth   one layer of the full-depth cache (H = 40, 28,000 tokens, 1,560 Queries,
-          10 seeded Lloyd iterations); resident bytes of all 40 layers reported
   rollout causal rollout of 40 chunks (H = 24) for each ablation (nearest
           centroid, QSAC, PSAC, QSAC + PSAC); per-ablation throughput and the
           top-1 shift rate against attention over the bf16 keys
 
-Prints one JSON line.  `value` = new tokens per second through the whole step;
-the attention kernel's roofline and (480p) the CPU oracle baseline ride along.
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -44,6 +49,9 @@ PACKED_BYTES_PER_KEY_HEAD = 85.0                       # K 47.5 + V 37.5 bytes r
 SEG_TABLE_BYTES_PER_HEAD = 2 * 256 * 128 * 2 + 128 * 8 * 2        # K, V centroids + U = 133,120
 BITS_PER_TOKEN_HEAD = 680                              # K 380 + V 300 bits resident
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_480p_step_traffic.md")
+DEPTH_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_depth_traffic.md")
+VALUE_BYTES_PER_TOKEN_HEAD = 256 + 37.5                # read bf16 value, write packed value
+LLOYD_FLOP_PER_TOKEN_HEAD = 2 * 256 * 128              # one assignment GEMM per iteration
 ATTN_SOURCE = os.path.join(ROOT, "bit_kv_cache_head_amd", "csrc", "attention.hip")
 
 
@@ -56,7 +64,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="480p", choices=["480p", "720p", "tiny", "depth", "rollout"])
+    ap.add_argument("--workload", default="depth", choices=["depth", "480p", "720p", "tiny", "rollout"])
+    ap.add_argument("--layers", type=int, default=40, help="depth: layers of the cache (40 = full depth)")
+    ap.add_argument("--no-rollout", action="store_true", help="depth: skip the rollout ablations extra")
     ap.add_argument("--f-energy", type=float, default=None, help="top-8 Query energy (720p: 0.60 or 0.71)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-ab", action="store_true",
@@ -85,11 +95,11 @@ def copy_calibration(torch):
     del x, y
 
 
-def attention_traffic():
+def attention_traffic(path=TRAFFIC_FILE):
     """HBM bytes per attention launch from the committed counter summary, when
     it was taken on the attention source as it is now; else None."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None
     sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()[:16]
@@ -231,7 +241,7 @@ class Stream:
 
 
 class OnePass:
-    """One pass over a single chunk (tiny, and one layer of depth): statistics
+    """One pass over a single chunk (tiny): statistics
     and basis from the Queries, 10 seeded Lloyd iterations for K and V, keys,
     values, attention of the Queries over the chunk."""
 
@@ -272,6 +282,440 @@ class OnePass:
         out, _, _ = qwm.attention(self.Q, self.dsegs)
         rec(5)
         return out
+
+
+class FullDepth:
+    """The full-depth memory case: every layer's cache resident in HBM; one
+    step runs the whole hot path over all layers.
+
+    Per layer, three streams: the statistics and basis on one side stream
+    (they feed only the keys), the V table and the values on another (they
+    feed only the attention), the K table, the keys and the attention on the
+    main stream.  HIP events on the main stream bracket every key call and
+    every attention call."""
+
+    LLOYD_ITERS = 10
+
+    def __init__(self, qwm, torch, datagen, layers, f_energy=None):
+        self.qwm, self.torch = qwm, torch
+        self.L = layers
+        self.layers = []
+        for l in range(layers):
+            K, V, Q = datagen.device_layer("depth", l, f_energy=f_energy)
+            self.layers.append((K, V, Q))
+        K0, _, Q0 = self.layers[0]
+        self.T, self.H = K0.shape[0], K0.shape[1]
+        self.queries = Q0.shape[0]
+        H, T = self.H, self.T
+        self.st, self.Ck, self.Cv, self.kp, self.vp, self.segs = [], [], [], [], [], []
+        for l in range(layers):
+            st = qwm.QueryStats(H)
+            Ck = torch.empty(H, 256, D, dtype=torch.bfloat16, device="cuda")
+            Cv = torch.empty_like(Ck)
+            kp = qwm.PackedChunk(T, H, True)
+            vp = qwm.PackedChunk(T, H, False)
+            self.st.append(st); self.Ck.append(Ck); self.Cv.append(Cv); self.kp.append(kp); self.vp.append(vp)
+            self.segs.append(qwm.segment_array([(kp, vp, Ck, Cv, st.U)]))
+        self.diag = qwm.new_diag()
+        self.vdiag = qwm.new_diag()
+        self.side = torch.cuda.Stream()
+        self.vside = torch.cuda.Stream()
+        self.fork = [torch.cuda.Event() for _ in range(layers)]
+        self.stats_done = [torch.cuda.Event() for _ in range(layers)]
+        self.v_done = [torch.cuda.Event() for _ in range(layers)]
+        self.total = T
+        self.nch = 1
+        self.new_tokens = T * layers
+        self.out = None
+
+    def run(self, events=None):
+        """events: None, or a list that receives one (keys start, keys end,
+        attention start, attention end) tuple of timing events per layer."""
+        qwm, torch = self.qwm, self.torch
+        main = torch.cuda.current_stream()
+        for l in range(self.L):
+            K, V, Q = self.layers[l]
+            st = self.st[l]
+            self.fork[l].record(main)
+            self.side.wait_event(self.fork[l])
+            with torch.cuda.stream(self.side):
+                st.reset()
+                qwm.update_query_stats(Q, st, compute_basis=True)
+                self.stats_done[l].record(self.side)
+            self.vside.wait_event(self.fork[l])
+            with torch.cuda.stream(self.vside):
+                qwm.build_centroids(V, self.LLOYD_ITERS, seed=2, out=self.Cv[l], diag=self.vdiag)
+                qwm.quantize_values(V, self.Cv[l], out=self.vp[l], diag=self.vdiag)
+                self.v_done[l].record(self.vside)
+            qwm.build_centroids(K, self.LLOYD_ITERS, seed=1, out=self.Ck[l], diag=self.diag)
+            main.wait_event(self.stats_done[l])
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if events is not None else None
+            if ev: ev[0].record(main)
+            qwm.quantize_keys(K, self.Ck[l], st.w, st.U, M=8, flags=3, out=self.kp[l], diag=self.diag)
+            if ev: ev[1].record(main)
+            main.wait_event(self.v_done[l])
+            if ev: ev[2].record(main)
+            self.out, _, _ = qwm.attention(Q, self.segs[l])
+            if ev: ev[3].record(main)
+            if ev: events.append(ev)
+        return self.out
+
+    def resident_bytes(self):
+        """Bytes the compressed cache holds: packed chunks plus per-(layer, head)
+        tables (K and V centroids, the basis)."""
+        packed = sum(kp.nbytes() + vp.nbytes() for kp, vp in zip(self.kp, self.vp))
+        tables = self.L * self.H * SEG_TABLE_BYTES_PER_HEAD
+        return packed, tables
+
+
+def depth_timed(step, torch, steps, warmup):
+    """Warm-up, then `steps` timed steps bracketed by synchronisation; per-call
+    key and attention times from the events of every layer of every step."""
+    import numpy as np
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    for d in (step.diag, step.vdiag):
+        d.zero_()
+    step.run()
+    torch.cuda.synchronize()
+    diag_step = (step.diag + step.vdiag).tolist()
+    evs = []
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for _ in range(steps):
+        step.run(evs)
+    torch.cuda.current_stream().wait_stream(step.side)
+    torch.cuda.current_stream().wait_stream(step.vside)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t_start.elapsed_time(t_end) / steps
+    keys_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    attn_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    return ms, keys_ms, attn_ms, wall, diag_step
+
+
+def stage_rooflines(torch, qwm, step, keys_ms, attn_ms):
+    """Kernel-level rates of the depth layer's stages, each against the roofline
+    that bounds it (algorithmic work per unit as the design notes state it),
+    timed one call at a time after the step (layer 0's inputs)."""
+    H, T, Tq = step.H, step.T, step.queries
+    K, V, Q = step.layers[0]
+    st, Ck, Cv, kp, vp = step.st[0], step.Ck[0], step.Cv[0], step.kp[0], step.vp[0]
+
+    def timed(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    st2 = qwm.QueryStats(H)
+    lloyd1 = timed(lambda: qwm.build_centroids(K, 1, init=Ck, out=torch.empty_like(Ck)))
+    vals = timed(lambda: qwm.quantize_values(V, Cv, out=vp))
+    stats = timed(lambda: (st2.reset(), qwm.update_query_stats(Q, st2, compute_basis=True)))
+    kms = float(keys_ms.mean())
+    ams = float(attn_ms.mean())
+    th = T * H
+    kbytes = KEY_BYTES_PER_TOKEN_HEAD * th + KEY_TABLE_BYTES_PER_HEAD * H
+    vbytes = VALUE_BYTES_PER_TOKEN_HEAD * th + 256 * 128 * 2 * H
+    aflop = ATTN_FLOP_PER_QKH * Tq * T * H
+    abytes = PACKED_BYTES_PER_KEY_HEAD * T * H + SEG_TABLE_BYTES_PER_HEAD * H + Tq * H * (256 + 512)
+    lflop = LLOYD_FLOP_PER_TOKEN_HEAD * th
+    return {
+        "keys": {"bound": "hbm", "ms": round(kms, 4), "GBps": round(kbytes / kms / 1e6, 1),
+                 "frac": round(kbytes / kms / 1e6 / HBM_PEAK_GBPS, 4), "bytes_per_call": int(kbytes),
+                 "token_heads_per_s": round(th / (kms * 1e-3), 1)},
+        "values": {"bound": "hbm", "ms": round(vals, 4), "GBps": round(vbytes / vals / 1e6, 1),
+                   "frac": round(vbytes / vals / 1e6 / HBM_PEAK_GBPS, 4), "bytes_per_call": int(vbytes)},
+        "lloyd_iteration": {"bound": "mfma", "ms": round(lloyd1, 4),
+                            "TFLOPs": round(lflop / lloyd1 / 1e9, 1),
+                            "frac": round(lflop / lloyd1 / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+                            "note": "one warm-started iteration: assignment, member sort, member sums"},
+        "attention": {"bound": "mfma", "ms": round(ams, 4), "TFLOPs": round(aflop / ams / 1e9, 1),
+                      "frac": round(aflop / ams / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+                      "compressed_GBps": round(abytes / ams / 1e6, 1)},
+        "stats_and_basis": {"bound": "latency", "ms": round(stats, 4)},
+    }
+
+
+def _pool_worker_init():
+    """Worker set-up: the oracle's BLAS on one thread per worker."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _oracle_keys_unit(args):
+    """One (layer, head) unit of the CPU baseline: the oracle's statistics and
+    Jacobi basis from the layer's Queries, its Forgy table over the head's
+    tokens, then its QSAC + PSAC key quantization of `rows` tokens, timed."""
+    import numpy as np
+    from oracle import lloyd as OL, quantize as Qz, stats as OS
+    K, Q, rows, seed, head = args
+    S, n = OS.update(np.zeros((D, D)), 0, Q.astype(np.float64))
+    basis = OS.principal_basis(S, n)
+    wts = OS.channel_weights(S, n)
+    C0 = OL.lloyd(K.astype(np.float64), 256, 0, seed=seed, head=head)
+    t0 = time.perf_counter()
+    o = Qz.quantize_keys(K[:rows].astype(np.float64), C0, wts, basis["U_bf16"], M=8, flags=3)
+    dt = time.perf_counter() - t0
+    return {"head": head, "seconds": dt, "rows": rows, "table": C0, "w": wts, "U": basis["U_bf16"],
+            "idx": o["idx"], "q": o["q"], "scale_bits": o["scale_bits"], "zero": o["zero"], "Cq": o["Cq"],
+            "c_scale_bits": o["c_scale_bits"], "dq": o["info"]["dq"]}
+
+
+def start_cpu_pool():
+    """The oracle's worker pool, started before anything touches the GPU (its
+    workers come from a fork server that never initialises the device)."""
+    import multiprocessing as mp
+    n = max(1, min(len(os.sched_getaffinity(0)), 16))
+    ctx = mp.get_context("forkserver")
+    return ctx.Pool(n, initializer=_pool_worker_init), n
+
+
+def _near_tie(k, C, w, o_j, g_j, dq, M, rel=1e-6):
+    """Whether a GPU centroid choice g_j that differs from the oracle's o_j is a
+    near-tie of the oracle's own scores: QSAC scores S within `rel`, or, when
+    the GPU's choice lies outside the oracle's M nearest by d_Q, the d_Q values
+    at that boundary within `rel`."""
+    import numpy as np
+    from oracle import quantize as Qz
+    Wg = np.asarray(w, np.float64).reshape(-1, 64).sum(axis=1)
+
+    def S_of(j):
+        _, _, R = Qz.group_ranges(Qz.residual(np.asarray(k, np.float64)[None], np.asarray(C)[j][None]))
+        return float(Qz.qsac_score(R, Wg)[0])
+    so, sg = S_of(o_j), S_of(g_j)
+    if abs(sg - so) <= rel * max(so, 1e-300):
+        return True
+    order = np.argsort(dq, kind="stable")
+    if g_j not in order[:M]:
+        dm = dq[order[M - 1]]
+        return abs(dq[g_j] - dm) <= rel * max(dm, 1e-300)
+    return False
+
+
+def cpu_baseline_depth(pool, workers, qwm, torch, step, rows=4096):
+    """The oracle, untuned, on a bounded sample of the depth workload's key
+    quantization: `workers` (layer 0, head) units in parallel, each the first
+    `rows` tokens of one head.  Also a parity sample: the GPU's key call on the
+    same heads with the oracle's tables, weights and basis, compared with the
+    oracle's outputs (indices, codes, scales, zero-points, C)."""
+    import numpy as np
+    from oracle import formats as F
+    K, _, Q = step.layers[0]
+    heads = list(range(min(workers, step.H)))
+    Kh = K[:, heads].float().cpu().numpy()
+    Qh = Q[:, heads].float().cpu().numpy()
+    units = [(np.ascontiguousarray(Kh[:, i]), np.ascontiguousarray(Qh[:, i]), rows, 1, h) for i, h in enumerate(heads)]
+    t0 = time.perf_counter()
+    res = pool.map(_oracle_keys_unit, units)
+    wall = time.perf_counter() - t0
+    cpu_s = sum(r["seconds"] for r in res)
+    token_heads = rows * len(heads)
+    keys_wall = max(r["seconds"] for r in res)
+    value = token_heads / keys_wall / step.H          # token positions across all heads
+    # parity sample: the GPU key call on the sampled heads with the oracle's inputs
+    Kd = K[:rows, heads].contiguous()
+    tab = torch.from_numpy(np.stack([r["table"] for r in res]).astype(np.float32)).to(torch.bfloat16).cuda()
+    wt = torch.from_numpy(np.stack([r["w"] for r in res]).astype(np.float32)).cuda()
+    Ub = torch.from_numpy(np.stack([r["U"] for r in res]).astype(np.float32)).to(torch.bfloat16).cuda()
+    kp = qwm.quantize_keys(Kd, tab, wt, Ub, M=8, flags=3)
+    torch.cuda.synchronize()
+    gidx = kp.idx.cpu().numpy()
+    gcodes = kp.codes.cpu().numpy()
+    gscale = kp.scale.cpu().numpy().view(np.uint16)
+    gz = kp.zeros.cpu().numpy()
+    gc = kp.c.cpu().numpy()
+    mism = near = code_bad = c_lsb2 = 0
+    c_lsb1 = 0
+    for i, r in enumerate(res):
+        o_idx = r["idx"].astype(np.int64)
+        g_idx = gidx[i].astype(np.int64)
+        bad = np.nonzero(o_idx != g_idx)[0]
+        mism += len(bad)
+        for t in bad:
+            near += int(_near_tie(Kh[t, i], r["table"], r["w"], int(o_idx[t]), int(g_idx[t]), r["dq"][t], 8))
+        same = o_idx == g_idx
+        q = F.unpack_codes(gcodes[i], 128)
+        zz = F.unpack_zeros(gz[i][: (rows + 1) // 2], rows)
+        code_bad += int(np.sum(np.any(q[same] != r["q"][same], axis=1) | np.any(gscale[i][same] != r["scale_bits"][same], axis=1)
+                               | np.any(zz[same] != r["zero"][same], axis=1)))
+        dc = np.abs(gc[i].astype(np.int64) - r["Cq"].astype(np.int64))[same]
+        c_lsb1 += int(np.sum(dc == 1))
+        c_lsb2 += int(np.sum(dc > 1))
+    return {
+        "cpu_baseline": {"value": round(value, 2), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+                         "sample": f"key quantization (QSAC + PSAC, M = 8) of the first {rows:,} tokens of heads "
+                                   f"0-{len(heads) - 1} of layer 0 of the depth cache, one (layer, head) unit per "
+                                   f"worker process ({workers} workers, BLAS 1 thread each); tokens/s = token-heads/s "
+                                   f"/ {step.H} heads, from the slowest unit's time",
+                         "token_heads_per_s": round(token_heads / keys_wall, 1), "cpu_seconds": round(cpu_s, 2),
+                         "wall_s_with_setup": round(wall, 2)},
+        "parity_sample": {"token_heads": token_heads, "idx_mismatches": mism, "near_ties": near,
+                          "mismatches_beyond_near_ties": mism - near, "codec_mismatches_on_equal_idx": code_bad,
+                          "c_off_by_1_lsb": c_lsb1, "c_off_by_more": c_lsb2,
+                          "note": "GPU qwm_quantize_keys on the sampled heads with the oracle's own Forgy table, "
+                                  "weights and basis, against the oracle's outputs"},
+    }
+
+
+def rollout_ablations(qwm, torch, datagen, chunks=40):
+    """The causal rollout (H = 24, 40 chunks of 1,560 tokens, drawn on the
+    device) under each ablation: per-ablation tokens/s and the top-1 shift
+    rate against attention over the bf16 keys."""
+    import numpy as np
+    Kd, Vd, Qd = datagen.device_layer("rollout", 0)
+    H, T = Kd.shape[1], 1560
+    refs = []
+    for t in range(chunks):
+        sl = slice(t * T, (t + 1) * T)
+        refs.append(qwm.reference_top1(Qd[sl], Kd[: sl.stop]))
+    names = {0: "nearest", 1: "qsac", 2: "psac", 3: "qsac+psac"}
+    out = {}
+    for flags in (0, 1, 2, 3):
+        for _ in range(2):
+            st = qwm.QueryStats(H)
+            segs, prev, tops = [], None, []
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for t in range(chunks):
+                sl = slice(t * T, (t + 1) * T)
+                K, V = Kd[sl], Vd[sl]
+                if prev is None:
+                    Ck = qwm.build_centroids(K, 10, seed=1)
+                    Cv = qwm.build_centroids(V, 10, seed=2)
+                    U = None
+                    kp = qwm.quantize_keys(K, Ck, None, None, M=8, flags=flags)
+                else:
+                    Ck = qwm.build_centroids(K, 3, init=prev[0])
+                    Cv = qwm.build_centroids(V, 3, init=prev[1])
+                    U = st.U.clone() if flags & 2 else None
+                    kp = qwm.quantize_keys(K, Ck, st.w if flags & 1 else None, U, M=8, flags=flags)
+                vp = qwm.quantize_values(V, Cv)
+                segs.append((kp, vp, Ck, Cv, U))
+                _, _, top1 = qwm.attention(Qd[sl], qwm.segment_array(segs), want_top1=True)
+                tops.append(top1)
+                qwm.update_query_stats(Qd[sl], st, compute_basis=True)
+                prev = (Ck, Cv)
+            torch.cuda.synchronize()
+            secs = time.perf_counter() - t0
+        rates = [float((tops[t] != refs[t]).float().mean().item()) for t in range(chunks)]
+        out[names[flags]] = {"tokens_per_s": round(chunks * T / secs, 1), "seconds": round(secs, 4),
+                             "shift_rate": round(float(np.mean(rates[1:])), 5),
+                             "shift_rate_cold_start": round(rates[0], 5)}
+    out["workload"] = (f"rollout: H={H}, d=128, {chunks} chunks x {T:,} tokens drawn on the device, causal "
+                       f"statistics, 10 seeded + 3 warm Lloyd iterations per chunk, attention of each chunk's "
+                       f"Queries over the cache so far; shift = top-1 key differs from the top-1 over the bf16 keys")
+    return out
+
+
+def rank_sweep(qwm, torch, step, ranks=(8, 16, 32)):
+    """The pages' PSAC rank ablation on layer 0 of the depth cache: basis,
+    QSAC + PSAC keys and attention at each rank, with the stored bits per
+    token-head (K + V, dense coefficients) and the extra bits per cached
+    element over rank 8 (the pages report +0.1341 and +0.2569 bit going from
+    8 to 16 on two models)."""
+    K, V, Q = step.layers[0]
+    H, T = step.H, step.T
+    Ck, Cv, vp = step.Ck[0], step.Cv[0], step.vp[0]
+    out = {}
+
+    def timed(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for r in ranks:
+        st = qwm.QueryStats(H, r=r)
+        t_stats = timed(lambda: (st.reset(), qwm.update_query_stats(Q, st, compute_basis=True)))
+        kp = qwm.PackedChunk(T, H, True, r=r)
+        t_keys = timed(lambda: qwm.quantize_keys(K, Ck, st.w, st.U, M=8, flags=3, out=kp))
+        segs = qwm.segment_array([(kp, vp, Ck, Cv, st.U)])
+        t_attn = timed(lambda: qwm.attention(Q, segs))
+        bits = (kp.nbytes() + vp.nbytes()) * 8 / (H * T)
+        out[str(r)] = {"stats_and_basis_ms": round(t_stats, 4), "keys_ms": round(t_keys, 4),
+                       "attention_ms": round(t_attn, 4), "bits_per_token_head": round(bits, 2),
+                       "extra_bits_per_element_vs_r8": round((bits - 680.0) / 256.0, 4),
+                       "eig_iterations_max": int(st.iters.abs().max().item())}
+    out["note"] = ("rank 8: subspace-iteration basis and coefficients fused into the selection kernel; ranks 16 "
+                   "and 32: one-sided Jacobi basis and an exact fp64 coefficient pass; the attention kernel takes "
+                   "one PSAC k-step for ranks up to 16 and two for 32")
+    return out
+
+
+def run_depth(args, qwm, torch, datagen, pool):
+    import numpy as np
+    log(f"drawing {args.layers} depth layers on the device")
+    step = FullDepth(qwm, torch, datagen, args.layers, f_energy=args.f_energy)
+    torch.cuda.synchronize()
+    log("timing")
+    ms, keys_ms, attn_ms, wall, diag_step = depth_timed(step, torch, args.steps, args.warmup)
+    L, H, T, Tq = step.L, step.H, step.T, step.queries
+    keys_total_s = float(keys_ms.sum()) * 1e-3
+    value = L * T * args.steps / keys_total_s
+    config = {"workload": f"full-depth memory case: {L} layers x H={H} heads x d=128, {T:,} cached tokens per "
+                          f"layer (bf16 K+V {L * H * T * 2 * D * 2 / 2 ** 30:.2f} GiB resident), {Tq:,} Queries per "
+                          f"layer; per layer: statistics + basis, 10 seeded Lloyd iterations for K and for V, "
+                          f"QSAC+PSAC keys (M=8, r=8, 256 centroids), values, attention over the layer's 2-bit cache",
+              "layers": L, "heads": H, "tokens_per_layer": T, "queries_per_layer": Tq}
+    if args.f_energy is not None:
+        config["f_energy"] = args.f_energy
+    res = base_result(args, value, ms, "bf16", config)
+    res["value_definition"] = ("token positions (all heads) quantized per second by qwm_quantize_keys "
+                               "(QSAC+PSAC), summed over the HIP-event times of every key call of the timed steps")
+    res["step_tokens_per_s"] = round(L * T / (ms * 1e-3), 1)
+    flops = ATTN_FLOP_PER_QKH * Tq * T * H
+    am = float(attn_ms.mean())
+    ach = flops / (am * 1e-3) / 1e12
+    abytes = PACKED_BYTES_PER_KEY_HEAD * T * H + SEG_TABLE_BYTES_PER_HEAD * H + Tq * H * (256 + 512)
+    res["roofline"] = {"kernel": "qwm_attention (fused dequant + PSAC + online softmax; the call's kernels: "
+                                 "attention_tables_kernel, attention_kernel, attention_combine_kernel)",
+                       "bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": attention_traffic(DEPTH_TRAFFIC_FILE),
+                       "flop_per_launch": int(flops), "avg_launch_ms": round(am, 4), "launches": int(len(attn_ms)),
+                       "algorithmic_bytes_per_launch": int(abytes),
+                       "compressed_GBps": round(abytes / (am * 1e-3) / 1e9, 1)}
+    kb = KEY_BYTES_PER_TOKEN_HEAD * T * H + KEY_TABLE_BYTES_PER_HEAD * H
+    km = float(keys_ms.mean())
+    res["keys"] = {"avg_call_ms": round(km, 4), "calls": int(len(keys_ms)), "token_heads_per_call": T * H,
+                   "GBps": round(kb / (km * 1e-3) / 1e9, 1), "hbm_frac": round(kb / (km * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                   "algorithmic_bytes_per_call": int(kb)}
+    res["stage_rooflines"] = stage_rooflines(torch, qwm, step, keys_ms, attn_ms)
+    packed, tables = step.resident_bytes()
+    bf16 = L * H * T * 2 * D * 2
+    res["resident"] = {"packed_bytes": int(packed), "table_bytes": int(tables),
+                       "GiB": round((packed + tables) / 2 ** 30, 3), "bf16_GiB": round(bf16 / 2 ** 30, 3),
+                       "ratio": round(bf16 / (packed + tables), 3), "ratio_without_tables": round(bf16 / packed, 3),
+                       "bits_per_token_head": round(packed * 8 / (L * H * T), 2)}
+    res["device_counters_per_step"] = {"nonfinite_rows": int(diag_step[0]), "exact_fallbacks": int(diag_step[1]),
+                                       "scale_saturations": int(diag_step[2])}
+    res["wall_s_timed"] = round(wall, 3)
+    log("rank sweep")
+    res["rank_sweep"] = rank_sweep(qwm, torch, step)
+    if not args.no_rollout:
+        log("rollout ablations")
+        res["rollout_ablations"] = rollout_ablations(qwm, torch, datagen)
+    if pool is not None:
+        log("timing the CPU oracle sample")
+        res.update(cpu_baseline_depth(pool[0], pool[1], qwm, torch, step))
+    return res
 
 
 def cpu_baseline(w, nq, heads=6):
@@ -599,14 +1043,6 @@ def run_stream_or_pass(args, qwm, torch, w):
     res["exact_fallbacks_per_step"] = int(diag_step[1])
     res["nonfinite_rows_per_step"] = int(diag_step[0])
     res["eig_iterations"] = step.st.iters.tolist()
-    if args.workload == "depth":
-        layers = 40
-        resident = layers * w.H * (w.T * BITS_PER_TOKEN_HEAD // 8 + SEG_TABLE_BYTES_PER_HEAD)
-        bf16 = layers * w.H * w.T * 2 * D * 2
-        res["resident"] = {"layers": layers, "bytes": int(resident), "GiB": round(resident / 2 ** 30, 3),
-                           "bf16_GiB": round(bf16 / 2 ** 30, 3), "ratio": round(bf16 / resident, 3),
-                           "per_layer_ms": round(ms, 3), "all_layers_s": round(layers * ms * 1e-3, 3),
-                           "note": "one synthetic layer timed; the 40 layers do identical work"}
     if args.workload == "480p" and not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_queries)
@@ -678,6 +1114,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is not "
               f"part of this build", file=sys.stderr)
         sys.exit(2)
+    pool = None
+    if args.workload == "depth" and not args.no_cpu_baseline:
+        pool = start_cpu_pool()          # before anything touches the GPU
     import torch
     import bit_kv_cache_head_amd as qwm
     import datagen
@@ -685,12 +1124,18 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration(torch)
-    log(f"generating the {args.workload} workload")
-    w = datagen.make_workload(args.workload, f_energy=args.f_energy)
-    if args.workload == "rollout":
-        res = run_rollout(args, qwm, torch, w)
+    if args.workload == "depth":
+        res = run_depth(args, qwm, torch, datagen, pool)
     else:
-        res = run_stream_or_pass(args, qwm, torch, w)
+        log(f"generating the {args.workload} workload")
+        w = datagen.make_workload(args.workload, f_energy=args.f_energy)
+        if args.workload == "rollout":
+            res = run_rollout(args, qwm, torch, w)
+        else:
+            res = run_stream_or_pass(args, qwm, torch, w)
+    if pool is not None:
+        pool[0].close()
+        pool[0].join()
     print(json.dumps(res), flush=True)
 
 

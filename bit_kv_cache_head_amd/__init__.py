@@ -78,15 +78,16 @@ def new_diag(device="cuda") -> torch.Tensor:
 
 
 class QueryStats:
-    """Per-head running Query statistics and principal basis (device tensors)."""
+    """Per-head running Query statistics and principal basis (device tensors);
+    r = PSAC rank (8, or 16 / 32 for the rank ablation)."""
 
-    def __init__(self, H: int, device="cuda"):
-        self.H = H
+    def __init__(self, H: int, device="cuda", r: int = R):
+        self.H, self.r = H, r
         self.S = torch.zeros(H, D, D, dtype=torch.float64, device=device)
         self.n = torch.zeros(H, dtype=torch.int64, device=device)
         self.w = torch.ones(H, D, dtype=torch.float32, device=device)
-        self.U = torch.zeros(H, D, R, dtype=torch.bfloat16, device=device)
-        self.lam = torch.zeros(H, R, dtype=torch.float32, device=device)
+        self.U = torch.zeros(H, D, r, dtype=torch.bfloat16, device=device)
+        self.lam = torch.zeros(H, r, dtype=torch.float32, device=device)
         self.energy = torch.zeros(H, dtype=torch.float32, device=device)
         self.iters = torch.zeros(H, dtype=torch.int32, device=device)
 
@@ -99,25 +100,25 @@ class QueryStats:
 
     def desc(self) -> QStats:
         return QStats(_ptr(self.S), _ptr(self.n), _ptr(self.w), _ptr(self.U), _ptr(self.lam),
-                      _ptr(self.energy), _ptr(self.iters), self.H, D, R, 0)
+                      _ptr(self.energy), _ptr(self.iters), self.H, D, self.r, 0)
 
 
 class PackedChunk:
     """One packed chunk: codes [H,T,32] u8, idx [H,T] u8, scale [H,T,2] fp16 bits,
     zeros [H, zstride] u8, c [H,T,8] i8 and c_scale [H,T] fp16 bits (keys)."""
 
-    def __init__(self, T: int, H: int, keys: bool, device="cuda"):
-        self.T, self.H, self.keys = T, H, keys
+    def __init__(self, T: int, H: int, keys: bool, device="cuda", r: int = R):
+        self.T, self.H, self.keys, self.r = T, H, keys, r
         self.codes = torch.empty(H, T, D // 4, dtype=torch.uint8, device=device)
         self.idx = torch.empty(H, T, dtype=torch.uint8, device=device)
         self.scale = torch.empty(H, T, 2, dtype=torch.int16, device=device)
         self.zeros = torch.zeros(H, zeros_stride(T), dtype=torch.uint8, device=device)
-        self.c = torch.empty(H, T, R, dtype=torch.int8, device=device) if keys else None
+        self.c = torch.empty(H, T, r, dtype=torch.int8, device=device) if keys else None
         self.c_scale = torch.empty(H, T, dtype=torch.int16, device=device) if keys else None
 
     def desc(self) -> Packed:
         return Packed(_ptr(self.codes), _ptr(self.idx), _ptr(self.scale), _ptr(self.zeros),
-                      _ptr(self.c), _ptr(self.c_scale), self.T, self.H, R)
+                      _ptr(self.c), _ptr(self.c_scale), self.T, self.H, self.r)
 
     def nbytes(self) -> int:
         tot = self.codes.numel() + self.idx.numel() + 2 * self.scale.numel() + self.zeros.numel()
@@ -149,7 +150,7 @@ def quantize_keys(k: torch.Tensor, centroids: torch.Tensor, w: torch.Tensor | No
                   diag: torch.Tensor | None = None) -> PackedChunk:
     td = _tokens(k)
     if out is None:
-        out = PackedChunk(td.T, td.H, True, k.device)
+        out = PackedChunk(td.T, td.H, True, k.device, r=R if U is None else U.shape[2])
     ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_KEYS, td.T, td.H, 0, 0), k.device)
     check(lib.qwm_quantize_keys(C.byref(td), _ptr(centroids), _ptr(w), _ptr(U), M, flags,
                                 C.byref(out.desc()), _ptr(diag), ws, nb, _stream()))
@@ -164,7 +165,7 @@ def quantize_keys_noalloc(k: torch.Tensor, centroids: torch.Tensor, w: torch.Ten
     device race)."""
     td = _tokens(k)
     if out is None:
-        out = PackedChunk(td.T, td.H, True, k.device)
+        out = PackedChunk(td.T, td.H, True, k.device, r=R if U is None else U.shape[2])
     check(lib.qwm_quantize_keys_noalloc(C.byref(td), _ptr(centroids), _ptr(w), _ptr(U), M, flags,
                                         C.byref(out.desc()), _ptr(diag), _stream()))
     return out
@@ -182,7 +183,7 @@ def quantize_keys_fullq(k: torch.Tensor, centroids: torch.Tensor, S: torch.Tenso
     if n.dtype != torch.int64 or tuple(n.shape) != (td.H,):
         raise ValueError("n must be an [H] int64 tensor")
     if out is None:
-        out = PackedChunk(td.T, td.H, True, k.device)
+        out = PackedChunk(td.T, td.H, True, k.device, r=R if U is None else U.shape[2])
     ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_KEYS, td.T, td.H, 0, 0), k.device)
     check(lib.qwm_quantize_keys_fullq(C.byref(td), _ptr(centroids), _ptr(S), _ptr(n), _ptr(w), _ptr(U), M, flags,
                                       C.byref(out.desc()), _ptr(diag), ws, nb, _stream()))
@@ -254,6 +255,7 @@ def _segment(kp, vp, kc, vc, U) -> Segment:
     s.k_centroids, s.v_centroids = kc.data_ptr(), vc.data_ptr()
     s.U = 0 if U is None else U.data_ptr()
     s.T = kp.T
+    s.r = kp.r
     return s
 
 

@@ -46,7 +46,7 @@ class Segment(C.Structure):
                 ("k_zeros", C.c_void_p), ("k_c", C.c_void_p), ("k_c_scale", C.c_void_p),
                 ("v_codes", C.c_void_p), ("v_idx", C.c_void_p), ("v_scale", C.c_void_p),
                 ("v_zeros", C.c_void_p), ("k_centroids", C.c_void_p), ("v_centroids", C.c_void_p),
-                ("U", C.c_void_p), ("T", C.c_int64)]
+                ("U", C.c_void_p), ("T", C.c_int64), ("r", C.c_int32), ("reserved", C.c_int32)]
 
 
 def _load():

@@ -84,7 +84,7 @@ static qwm_status check_packed(const qwm_packed* p, const qwm_tokens* x, bool ke
     return fail(QWM_ERR_ARG, "packed: codes must be 16-byte, scale and zeros 4-byte aligned");
   if (keys) {
     if (!p->c || !p->c_scale) return fail(QWM_ERR_ARG, "packed keys: null c / c_scale");
-    if (p->r != qwm::R) return fail(QWM_ERR_UNSUPPORTED, "packed keys: rank must be 8");
+    if (p->r != 8 && p->r != 16 && p->r != 32) return fail(QWM_ERR_UNSUPPORTED, "packed keys: rank must be 8, 16 or 32");
     if (!aligned(p->c, 8) || !aligned(p->c_scale, 2)) return fail(QWM_ERR_ARG, "packed keys: c misaligned");
   }
   (void)psac;
@@ -123,7 +123,7 @@ qwm_status qwm_update_query_stats(const qwm_tokens* q, const qwm_qstats* st, int
   if (s != QWM_OK) return s;
   if (!st) return fail(QWM_ERR_ARG, "stats: null descriptor");
   if (st->H != q->H || st->d != qwm::D) return fail(QWM_ERR_ARG, "stats: H / d differ from the queries");
-  if (st->r != qwm::R) return fail(QWM_ERR_UNSUPPORTED, "stats: rank must be 8");
+  if (st->r != 8 && st->r != 16 && st->r != 32) return fail(QWM_ERR_UNSUPPORTED, "stats: rank must be 8, 16 or 32");
   if (!st->S || !st->n || !st->w) return fail(QWM_ERR_ARG, "stats: null S / n / w");
   if (!aligned(st->S, 8) || !aligned(st->n, 8) || !aligned(st->w, 4)) return fail(QWM_ERR_ARG, "stats: misaligned");
   if (compute_basis && (!st->U || !st->lambda || !st->energy))
@@ -230,6 +230,7 @@ static qwm_status check_segments(const qwm_segment* segs, int32_t n_segs, int64_
     const qwm_segment& g = segs[i];
     const std::string at = "segment " + std::to_string(i) + ": ";
     if (g.T < 1 || g.T >= ((int64_t)1 << 26)) return fail(QWM_ERR_ARG, at + "T must be in [1, 2^26)");
+    if (g.r != 8 && g.r != 16 && g.r != 32) return fail(QWM_ERR_UNSUPPORTED, at + "rank must be 8, 16 or 32");
     if (!g.k_codes || !g.k_idx || !g.k_scale || !g.k_zeros || !g.v_codes || !g.v_idx || !g.v_scale ||
         !g.v_zeros || !g.k_centroids || !g.v_centroids)
       return fail(QWM_ERR_ARG, at + "a packed array or centroid table is null");
@@ -278,6 +279,7 @@ qwm_status qwm_decode_segment(const qwm_segment* seg, int32_t H, uint16_t* k_out
       !seg->v_scale || !seg->v_zeros || !seg->k_centroids || !seg->v_centroids)
     return fail(QWM_ERR_ARG, "decode: a packed array or centroid table is null");
   if (seg->U && (!seg->k_c || !seg->k_c_scale)) return fail(QWM_ERR_ARG, "decode: PSAC basis without coefficients");
+  if (seg->r != 8 && seg->r != 16 && seg->r != 32) return fail(QWM_ERR_UNSUPPORTED, "decode: rank must be 8, 16 or 32");
   if (!aligned(seg->k_codes, 16) || !aligned(seg->v_codes, 16) || !aligned(seg->k_centroids, 16) ||
       !aligned(seg->v_centroids, 16) || !aligned(seg->k_scale, 4) || !aligned(seg->v_scale, 4))
     return fail(QWM_ERR_ARG, "decode: misaligned packed arrays");

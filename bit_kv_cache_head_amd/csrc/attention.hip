@@ -52,7 +52,7 @@ struct AttnArgs {
   int32_t nparts;         // partial sets: nsplit (+ nsplit_a); one set means no partials
   float scale;
   const uint16_t* tabs;   // fp16 centroid tables [seg][H][2][256][128]: K (channel-permuted), V
-  const uint16_t* ut;     // fp16 basis fragments [seg][H][R][8][2][8] (zero without PSAC), see attention_tables_kernel
+  const uint16_t* ut;     // fp16 basis fragments [seg][H][UT_ROWS][8][2][8] (rows < the rank written), see attention_tables_kernel
   // final outputs (nparts == 1)
   float* out; float* lse; int32_t* top1; int32_t H;
   // partial outputs (nparts > 1): [part][H][Tq][D], [part][H][Tq] x (m, l), top value / index
@@ -69,12 +69,14 @@ struct AttnArgs {
 // per-thread base plus a compile-time offset.
 constexpr int KSTR = 2 * D + 16;      // bytes per K0_hat row
 constexpr int VSTR = 2 * AT_K + 16;   // bytes per V_hat^T row
+// NPK: PSAC k-steps of 16 coefficients (1: ranks 8 and 16; 2: rank 32)
+template <int NPK>
 struct AttnBuf {
-  uint8_t khat[AT_K * KSTR];   // [key][128 permuted channels] fp16
-  uint8_t vt[D * VSTR];        // [channel][64 keys in vslot order] fp16
-  uint8_t chat[AT_K * 16];     // [key][8] fp16: c_scale * c
+  uint8_t khat[AT_K * KSTR];       // [key][128 permuted channels] fp16
+  uint8_t vt[D * VSTR];            // [channel][64 keys in vslot order] fp16
+  uint8_t chat[AT_K * 32 * NPK];   // [key][16 NPK] fp16: c_scale * c (zeros past the rank)
 };
-constexpr int BUF_BYTES = (int)sizeof(AttnBuf);
+constexpr int UT_ROWS = QWM_MAX_RANK;   // basis rows per (segment, head) in the fragment buffer
 
 // slot of a key in the transposed V tile: bits 2 and 3 swapped (matches the
 // register order of the probabilities produced by the S^T MFMA)
@@ -130,7 +132,7 @@ __device__ __forceinline__ h2 code_pair(uint32_t w, int sh, const CodeMasks& m) 
 // 16 (tid % 8) .. +16), so a wave reads 8 whole rows; blocks y = 0 also write
 // the basis fragments, and block (local segment, head 0, y = 0) its descriptor.
 // ---------------------------------------------------------------------------
-constexpr int SEG_BATCH = 24;   // descriptors per launch (2.6 KiB of kernel arguments)
+constexpr int SEG_BATCH = 24;   // descriptors per launch (2.8 KiB of kernel arguments)
 struct SegBatch {
   qwm_segment s[SEG_BATCH];
   int32_t first, count;
@@ -145,20 +147,24 @@ __global__ __launch_bounds__(256) void attention_tables_kernel(SegBatch b, int32
   if (blockIdx.y == 0 && h == 0 && tid < (int)(sizeof(qwm_segment) / 8))
     reinterpret_cast<uint64_t*>(dsegs + seg)[tid] = reinterpret_cast<const uint64_t*>(&sg)[tid];
   if (blockIdx.y == 0) {
-    // four consecutive fragment values (same n, s, hh; j' = 4 (tid % 2) .. +4)
-    const int i = 4 * tid, n = i >> 7, s = (i >> 4) & 7, hf = (i >> 3) & 1;
-    uint32_t w[2] = {0u, 0u};
-    if (sg.U != nullptr) {
-      const uint16_t* Uh = sg.U + (int64_t)h * D * R;
+    // basis rows n < r: four consecutive fragment values per thread and pass
+    // (same n, s, hh; j' = 4 (i % 2) .. +4); rows past the rank are never read
+    const int rk = sg.r;
+    for (int i = 4 * tid; i < rk * D; i += 4 * 256) {
+      const int n = i >> 7, s = (i >> 4) & 7, hf = (i >> 3) & 1;
+      uint32_t w[2] = {0u, 0u};
+      if (sg.U != nullptr) {
+        const uint16_t* Uh = sg.U + (int64_t)h * D * rk;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jj = (i & 7) + e;
-        const int c = 16 * s + 4 * hf + (jj >> 1) + 8 * (jj & 1);
-        const uint16_t v = __builtin_bit_cast(uint16_t, (_Float16)__uint_as_float((uint32_t)Uh[c * R + n] << 16));
-        w[e >> 1] |= (uint32_t)v << (16 * (e & 1));
+        for (int e = 0; e < 4; ++e) {
+          const int jj = (i & 7) + e;
+          const int c = 16 * s + 4 * hf + (jj >> 1) + 8 * (jj & 1);
+          const uint16_t v = __builtin_bit_cast(uint16_t, (_Float16)__uint_as_float((uint32_t)Uh[c * rk + n] << 16));
+          w[e >> 1] |= (uint32_t)v << (16 * (e & 1));
+        }
       }
+      *reinterpret_cast<uint2*>(ut + (int64_t)sh * UT_ROWS * D + i) = make_uint2(w[0], w[1]);
     }
-    *reinterpret_cast<uint2*>(ut + (int64_t)sh * R * D + i) = make_uint2(w[0], w[1]);
   }
   const u32x4* kr = reinterpret_cast<const u32x4*>(sg.k_centroids + ((int64_t)h * NC + j) * D);
   const u32x4* vr = reinterpret_cast<const u32x4*>(sg.v_centroids + ((int64_t)h * NC + j) * D);
@@ -325,8 +331,9 @@ __device__ __forceinline__ u32x4 ld128(rsrc_t r, int off, int so = 0) {
 struct Lane {
   int key, blk, p, oct;
   uint32_t zsh_k, zsh_v;   // bit offset of this thread's zero-point in its byte
-  int c_off;               // byte offset of this thread's PSAC pair in a tile buffer
+  int c_off;               // byte offset of this thread's PSAC coefficients in a tile buffer
 };
+template <int NPK>
 __device__ __forceinline__ Lane lane_share(int tid) {
   Lane L;
   L.key = tid >> 3;
@@ -335,11 +342,8 @@ __device__ __forceinline__ Lane lane_share(int tid) {
   L.oct = tid & 15;
   L.zsh_k = 4u * (uint32_t)(L.key & 1) + 2u * (uint32_t)(L.blk >> 2);
   L.zsh_v = 2u * (uint32_t)(L.oct >> 3);
-  // threads blk < 4 own coefficient pairs 2 blk, 2 blk + 1 of their key; the
-  // others compute the same pair and store it into the unused padding of their
-  // K0_hat row, so that the store needs no branch
-  L.c_off = L.blk < 4 ? (int)offsetof(AttnBuf, chat) + L.key * 16 + 4 * L.blk
-                      : L.key * KSTR + 2 * D + 4 * (L.blk & 3);
+  // thread blk owns coefficients 2 NPK blk .. +2 NPK of its key
+  L.c_off = (int)offsetof(AttnBuf<NPK>, chat) + L.key * 32 * NPK + 4 * NPK * L.blk;
   return L;
 }
 
@@ -372,6 +376,7 @@ struct SegDesc {
   const uint8_t *kc, *ks, *kz, *c, *cs, *vc, *vs, *vz, *ki, *vi;
   int T;
   int cT;     // rows of PSAC coefficients: T, or 0 without PSAC (empty descriptors)
+  int r;      // PSAC rank (bytes per coefficient row)
 };
 __device__ __forceinline__ SegDesc seg_desc(const AttnArgs& a, int s, int h) {
   cseg& g = seg_at(a, s);
@@ -384,7 +389,8 @@ __device__ __forceinline__ SegDesc seg_desc(const AttnArgs& a, int s, int h) {
   d.ks = reinterpret_cast<const uint8_t*>(g.k_scale + hb * 2);
   d.kz = g.k_zeros + zb;
   // without PSAC the descriptors are empty: the loads return zeros and touch no memory
-  d.c = psac ? reinterpret_cast<const uint8_t*>(g.k_c + hb * R) : g.k_codes;
+  d.r = __builtin_amdgcn_readfirstlane(g.r);
+  d.c = psac ? reinterpret_cast<const uint8_t*>(g.k_c + hb * d.r) : g.k_codes;
   d.cs = psac ? reinterpret_cast<const uint8_t*>(g.k_c_scale + hb) : g.k_codes;
   d.vc = g.v_codes + hb * 32;
   d.vs = reinterpret_cast<const uint8_t*>(g.v_scale + hb * 2);
@@ -402,6 +408,7 @@ __device__ __forceinline__ SegDesc dense_desc(const AttnArgs& a) {
   SegDesc d{};
   d.T = (int)a.Ta;
   d.cT = 0;
+  d.r = 8;
   return d;
 }
 template <bool DENSE>
@@ -422,7 +429,7 @@ __device__ __forceinline__ void load_idx(const SegDesc& d, const Pos& P, const L
 
 // The packed bytes of a tile (codes, scales, zero-points, PSAC bytes); for
 // a dense unit all zeros, so its tiles dequantize to the rows themselves.
-template <bool DENSE>
+template <bool DENSE, int NPK>
 __device__ __forceinline__ void load_bytes(const SegDesc& d, const Pos& P, const Lane& L, TileRegs& r) {
   const int k0 = P.tile * AT_K, T = DENSE ? 0 : d.T;
   {
@@ -430,7 +437,10 @@ __device__ __forceinline__ void load_bytes(const SegDesc& d, const Pos& P, const
     r.kcode = ld32(buf(d.kc, T * 32), L.key * 32 + 4 * L.blk, k0 * 32);
     r.kscale = ld16(buf(d.ks, T * 4), L.key * 4 + 2 * g, k0 * 4);
     r.kzb = ld8(buf(d.kz, (T + 1) >> 1), L.key >> 1, k0 >> 1);
-    r.c2 = ld16(buf(d.c, d.cT * R), L.key * R + 2 * (L.blk & 3), k0 * R);
+    const rsrc_t cr = buf(d.c, d.cT * d.r);
+    const uint32_t cv = NPK == 1 ? ld16(cr, L.key * d.r + 2 * L.blk, k0 * d.r)
+                                 : ld32(cr, L.key * d.r + 4 * L.blk, k0 * d.r);
+    r.c2 = (2 * NPK * L.blk < d.r) ? cv : 0u;
     r.cs = ld16(buf(d.cs, d.cT * 2), L.key * 2, k0 * 2);
   }
   {
@@ -496,10 +506,29 @@ __device__ __forceinline__ void take_bytes(TileRegs& d, const TileRegs& s) {
   d.vcode0 = s.vcode0; d.vcode1 = s.vcode1; d.vscale0 = s.vscale0; d.vscale1 = s.vscale1; d.vzb = s.vzb;
 }
 
+// PSAC coefficients c_scale * c of the thread's share of its key: each int8
+// pair becomes the exact fp16 pair (1024 + c + 128) - 1152, then one rounded
+// fp16 product.
+template <int NPK>
+__device__ __forceinline__ void store_coeffs(const TileRegs& r, const Lane& L, uint8_t* buf_base) {
+  const _Float16 cs = __builtin_bit_cast(_Float16, (uint16_t)r.cs);
+  const h2 bias = h2{(_Float16)1152.0f, (_Float16)1152.0f};
+  const uint32_t sp0 = __builtin_amdgcn_perm(0u, r.c2, 0x0C010C00u) ^ 0x64806480u;
+  const uint32_t v0 = as_u32((as_h2(sp0) - bias) * h2{cs, cs});
+  if constexpr (NPK == 1) {
+    *reinterpret_cast<uint32_t*>(buf_base + L.c_off) = v0;
+  } else {
+    const uint32_t sp1 = __builtin_amdgcn_perm(0u, r.c2, 0x0C030C02u) ^ 0x64806480u;
+    const uint32_t v1 = as_u32((as_h2(sp1) - bias) * h2{cs, cs});
+    *reinterpret_cast<uint2*>(buf_base + L.c_off) = make_uint2(v0, v1);
+  }
+}
+
 // fp16 pair (-1024 - z0, -1024 - z1) from two 2-bit zero-points: 0xE400 + z
 __device__ __forceinline__ h2 neg_zero_pair(uint32_t z01) { return as_h2(z01 | 0xE400E400u); }
 
-__device__ __forceinline__ void dequant_tile(const TileRegs& r, const Lane& L, const CodeMasks& cm, AttnBuf& b) {
+template <int NPK>
+__device__ __forceinline__ void dequant_tile(const TileRegs& r, const Lane& L, const CodeMasks& cm, AttnBuf<NPK>& b) {
   {
     // K0_hat: s (c - z) + mu in packed fp16 (c - z is exact; one rounding in the fma)
     const uint32_t z = __builtin_amdgcn_ubfe(r.kzb, L.zsh_k, 2);
@@ -515,15 +544,7 @@ __device__ __forceinline__ void dequant_tile(const TileRegs& r, const Lane& L, c
     u32x4* kr = reinterpret_cast<u32x4*>(b.khat + L.key * KSTR + 32 * L.blk);
     kr[0] = o[0];
     kr[1] = o[1];
-    {
-      // PSAC coefficients c_scale * c of this key, two of the eight: the int8
-      // pair becomes the exact fp16 pair (1024 + c + 128) - 1152, then one
-      // rounded fp16 product
-      const uint32_t sp = __builtin_amdgcn_perm(0u, r.c2, 0x0C010C00u) ^ 0x64806480u;
-      const h2 c = as_h2(sp) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
-      const _Float16 cs = __builtin_bit_cast(_Float16, (uint16_t)r.cs);
-      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(&b) + L.c_off) = as_u32(c * h2{cs, cs});
-    }
+    store_coeffs<NPK>(r, L, reinterpret_cast<uint8_t*>(&b));
   }
   {
     // V_hat, keys 2p (low half) and 2p + 1 (high half) of channel 8 oct + c
@@ -547,8 +568,9 @@ __device__ __forceinline__ void dequant_tile(const TileRegs& r, const Lane& L, c
 // woven between them one code word at a time: a wave's VALU work issued
 // between its own MFMAs runs while they execute.  The order is fixed by
 // scheduling barriers; operand reads run two steps ahead.
-__device__ __forceinline__ void tile_phase1(const AttnBuf* __restrict__ B, AttnBuf* __restrict__ W,
-                                            const f16x8 (&qf)[8], const f16x8& qpf, int ln, int hh,
+template <int NPK>
+__device__ __forceinline__ void tile_phase1(const AttnBuf<NPK>* __restrict__ B, AttnBuf<NPK>* __restrict__ W,
+                                            const f16x8 (&qf)[8], const f16x8 (&qpf)[NPK], int ln, int hh,
                                             const TileRegs& r, const Lane& L, const CodeMasks& cm,
                                             f32x16& sa, f32x16& sb2) {
   const uint8_t* krow = B->khat + ln * KSTR + 16 * hh;
@@ -570,7 +592,7 @@ __device__ __forceinline__ void tile_phase1(const AttnBuf* __restrict__ B, AttnB
   fb[0] = *reinterpret_cast<const f16x8*>(krow + 32 * KSTR);
   fa[1] = *reinterpret_cast<const f16x8*>(krow + 32);
   fb[1] = *reinterpret_cast<const f16x8*>(krow + 32 * KSTR + 32);
-  f16x8 ca, cb;
+  f16x8 ca[NPK], cb[NPK];
   u32x4 ko[2];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -579,11 +601,14 @@ __device__ __forceinline__ void tile_phase1(const AttnBuf* __restrict__ B, AttnB
       fa[s + 2] = *reinterpret_cast<const f16x8*>(krow + 32 * (s + 2));
       fb[s + 2] = *reinterpret_cast<const f16x8*>(krow + 32 * KSTR + 32 * (s + 2));
     } else if (s == 6) {
-      // PSAC step operands: k = 0..7 (hh = 0) are the coefficients; the hh = 1
-      // half reads the same finite values against zeros in qpf (all of qpf is
-      // zero for a segment without PSAC, whose coefficients are stored as zeros)
-      ca = *reinterpret_cast<const f16x8*>(B->chat + ln * 16);
-      cb = *reinterpret_cast<const f16x8*>(B->chat + (32 + ln) * 16);
+      // PSAC step operands: coefficients 16 k + 8 hh .. +8 of key ln (and
+      // 32 + ln); zeros past the segment's rank, and in qpf for a segment
+      // without PSAC
+#pragma unroll
+      for (int k = 0; k < NPK; ++k) {
+        ca[k] = *reinterpret_cast<const f16x8*>(B->chat + ln * 32 * NPK + 32 * k + 16 * hh);
+        cb[k] = *reinterpret_cast<const f16x8*>(B->chat + (32 + ln) * 32 * NPK + 32 * k + 16 * hh);
+      }
     }
     sa = mfma_f16(fa[s], qf[s], sa);
     {
@@ -600,18 +625,14 @@ __device__ __forceinline__ void tile_phase1(const AttnBuf* __restrict__ B, AttnB
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  sa = mfma_f16(ca, qpf, sa);
-  {
-    // PSAC coefficients c_scale * c of this thread's key, two of the eight: the
-    // int8 pair becomes the exact fp16 pair (1024 + c + 128) - 1152, then one
-    // rounded fp16 product
-    const uint32_t sp = __builtin_amdgcn_perm(0u, r.c2, 0x0C010C00u) ^ 0x64806480u;
-    const h2 c = as_h2(sp) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
-    const _Float16 cs = __builtin_bit_cast(_Float16, (uint16_t)r.cs);
-    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(W) + L.c_off) = as_u32(c * h2{cs, cs});
-  }
+  sa = mfma_f16(ca[0], qpf[0], sa);
+  store_coeffs<NPK>(r, L, reinterpret_cast<uint8_t*>(W));
   __builtin_amdgcn_sched_barrier(0);
-  sb2 = mfma_f16(cb, qpf, sb2);
+  sb2 = mfma_f16(cb[0], qpf[0], sb2);
+  if constexpr (NPK == 2) {
+    sa = mfma_f16(ca[1], qpf[1], sa);
+    sb2 = mfma_f16(cb[1], qpf[1], sb2);
+  }
 }
 
 // Lanes l and l ^ 32 hold the two halves of one query column.
@@ -632,8 +653,8 @@ __device__ __forceinline__ uint32_t pair_other(uint32_t v, int hh) {
 // One unit: 256 Queries (query block qb) x head h x split `split` of nsplit
 // of a key sequence, written to partial set `part`.  DENSE: the key sequence
 // is the active BF16 chunk; otherwise the packed segments.
-template <bool TOP1, bool DENSE>
-__device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf* sb, int qb, int split, int nsplit,
+template <bool TOP1, bool DENSE, int NPK>
+__device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf<NPK>* sb, int qb, int split, int nsplit,
                                                int part, int h) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hh = lane >> 5, ln = lane & 31;
   const int64_t qw0 = (int64_t)qb * AT_Q + wv * AT_QW;
@@ -641,7 +662,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf* sb, i
   const int64_t qi = qw0 + ln;
   const bool qvalid = qi < a.Tq;
   const int64_t qoff = (int64_t)h * a.qsh + (qvalid ? qi : 0) * a.qst;
-  const Lane L = lane_share(tid);
+  const Lane L = lane_share<NPK>(tid);
 
   // Q fragments (B operand of S^T), fp16, in the permuted channel order of the
   // K0_hat rows: k-step s, half hh holds channels 16 s + 4 hh + e and
@@ -711,49 +732,64 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf* sb, i
   {
     const SegDesc d0 = desc_for<DENSE>(a, P0.seg, h);
     load_idx<DENSE>(d0, P0, L, tix);
-    load_bytes<DENSE>(d0, P0, L, regs);
+    load_bytes<DENSE, NPK>(d0, P0, L, regs);
     load_mu<DENSE>(a, P0.seg, P0.tile, h, L, tix, regs);
     if constexpr (DENSE) rows_to_f16(regs);
-    dequant_tile(regs, L, cm, sb[0]);
+    dequant_tile<NPK>(regs, L, cm, sb[0]);
     const SegDesc d1 = desc_for<DENSE>(a, P1.seg, h);
     load_idx<DENSE>(d1, P1, L, tix);
-    load_bytes<DENSE>(d1, P1, L, regs);
+    load_bytes<DENSE, NPK>(d1, P1, L, regs);
     load_mu<DENSE>(a, P1.seg, P1.tile, h, L, tix, regs);
     const SegDesc d2 = desc_for<DENSE>(a, P2.seg, h);
     load_idx<DENSE>(d2, P2, L, tix);
-    load_bytes<DENSE>(d2, P2, L, nbytes);
+    load_bytes<DENSE, NPK>(d2, P2, L, nbytes);
   }
   __syncthreads();
 
   int cur = 0;
   int qp_seg = -1;
-  f16x8 qpf = __builtin_bit_cast(f16x8, u32x4{0, 0, 0, 0});
+  f16x8 qpf[NPK];
+#pragma unroll
+  for (int k = 0; k < NPK; ++k) qpf[k] = __builtin_bit_cast(f16x8, u32x4{0, 0, 0, 0});
   const h2 ones = as_h2(0x3C003C00u);
   for (int n = 0; n < count; ++n) {
     if (!DENSE && P0.seg != qp_seg) {
       // Q U for this segment: (U^T) (Q^T) on MFMA with the Query fragments as
       // B; the basis fragments come from the workspace (zeros without PSAC;
-      // rows n >= R read as zeros, past the end of their buffer)
+      // rows n >= the rank read as zeros, past the end of their buffer)
       qp_seg = P0.seg;
-      const rsrc_t ur = buf(a.ut + (int64_t)(P0.seg * a.H + h) * (R * D), R * D * 2);
+      const int rk = __builtin_amdgcn_readfirstlane(seg_at(a, P0.seg).r);
+      const rsrc_t ur = buf(a.ut + (int64_t)(P0.seg * a.H + h) * (UT_ROWS * D), rk * D * 2);
       f32x16 acc = {};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const u32x4 v = ld128(ur, ((ln * 8 + s) * 2 + hh) * 16);
         acc = mfma_f16(__builtin_bit_cast(f16x8, v), qf[s], acc);
       }
-      // lane (query, hh) holds (QU)[4 hh + 0..3]; hh = 0 needs all 8
-      const float o0 = swap32_f(acc[0]), o1 = swap32_f(acc[1]), o2 = swap32_f(acc[2]), o3 = swap32_f(acc[3]);
-      u32x4 pv = {0, 0, 0, 0};
-      if (hh == 0) {
-        pv[0] = pack_f16x2(acc[0], acc[1]);
-        pv[1] = pack_f16x2(acc[2], acc[3]);
-        pv[2] = pack_f16x2(o0, o1);
-        pv[3] = pack_f16x2(o2, o3);
+      // lane (query, hh) holds (QU)[n] for n = 8 (i / 4) + 4 hh + i % 4 in acc[i];
+      // the PSAC k-step k needs n = 16 k + 8 hh .. +8 of its query: four of its
+      // own values and four of the partner lane's
+#pragma unroll
+      for (int k = 0; k < NPK; ++k) {
+        float recv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) recv[e] = swap32_f(hh ? acc[8 * k + e] : acc[8 * k + 4 + e]);
+        u32x4 pv;
+        if (hh == 0) {
+          pv[0] = pack_f16x2(acc[8 * k], acc[8 * k + 1]);
+          pv[1] = pack_f16x2(acc[8 * k + 2], acc[8 * k + 3]);
+          pv[2] = pack_f16x2(recv[0], recv[1]);
+          pv[3] = pack_f16x2(recv[2], recv[3]);
+        } else {
+          pv[0] = pack_f16x2(recv[0], recv[1]);
+          pv[1] = pack_f16x2(recv[2], recv[3]);
+          pv[2] = pack_f16x2(acc[8 * k + 4], acc[8 * k + 5]);
+          pv[3] = pack_f16x2(acc[8 * k + 6], acc[8 * k + 7]);
+        }
+        qpf[k] = __builtin_bit_cast(f16x8, pv);
       }
-      qpf = __builtin_bit_cast(f16x8, pv);
     }
-    const AttnBuf& B = sb[cur];
+    const AttnBuf<NPK>& B = sb[cur];
     const int64_t k0 = (int64_t)P0.tile * AT_K;
     const int nvalid = (int)((T0 - k0) < AT_K ? (T0 - k0) : AT_K);
 
@@ -766,12 +802,12 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf* sb, i
     //      buffer nobody reads), so that no load is conditional.
     f32x16 sa = {}, sb2 = {};
     if constexpr (DENSE) rows_to_f16(regs);
-    tile_phase1(&sb[cur], &sb[cur ^ 1], qf, qpf, ln, hh, regs, L, cm, sa, sb2);
+    tile_phase1<NPK>(&sb[cur], &sb[cur ^ 1], qf, qpf, ln, hh, regs, L, cm, sa, sb2);
     // tile n + 2: its bytes arrived during the previous iteration; fetch its
     // centroid rows.  Tile n + 3: bytes and indices.
     take_bytes(regs, nbytes);
     load_mu<DENSE>(a, P2.seg, P2.tile, h, L, tix, regs);
-    load_bytes<DENSE>(sd, P3, L, nbytes);
+    load_bytes<DENSE, NPK>(sd, P3, L, nbytes);
     load_idx<DENSE>(sd, P3, L, tix);
 
     if (wave_active) {
@@ -903,9 +939,9 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf* sb, i
   }
 }
 
-template <bool TOP1>
+template <bool TOP1, int NPK>
 __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
-  __shared__ AttnBuf sb[2];
+  __shared__ AttnBuf<NPK> sb[2];
   // XCD-aware unit mapping: consecutive units (same head) go to the same XCD
   const int nb = (int)gridDim.x;
   const int per = (nb + 7) / 8;
@@ -913,11 +949,11 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   if (unit >= a.units) return;
   if (unit < a.units_p) {
     const int qb = unit % a.nqb, split = (unit / a.nqb) % a.nsplit, h = unit / (a.nqb * a.nsplit);
-    attention_body<TOP1, false>(a, sb, qb, split, a.nsplit, split, h);
+    attention_body<TOP1, false, NPK>(a, sb, qb, split, a.nsplit, split, h);
   } else {
     const int u = unit - a.units_p;
     const int qb = u % a.nqb, split = (u / a.nqb) % a.nsplit_a, h = u / (a.nqb * a.nsplit_a);
-    attention_body<TOP1, true>(a, sb, qb, split, a.nsplit_a, a.nsplit + split, h);
+    attention_body<TOP1, true, NPK>(a, sb, qb, split, a.nsplit_a, a.nsplit + split, h);
   }
 }
 
@@ -1035,7 +1071,7 @@ static AttnPlan attention_plan(int64_t Tq, int32_t H, int64_t packed_keys, int64
 size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs, bool active) {
   size_t bytes = al256((size_t)n_segs * sizeof(qwm_segment)) +
                  al256((size_t)n_segs * H * 2 * TAB_ELEMS * sizeof(uint16_t)) +
-                 al256((size_t)n_segs * H * R * D * sizeof(uint16_t));
+                 al256((size_t)n_segs * H * UT_ROWS * D * sizeof(uint16_t));
   const int ns = attention_splits(Tq, H, total_keys) + (active ? 1 : 0);
   if (ns > 1) {
     const size_t n = (size_t)ns * H * Tq;
@@ -1068,7 +1104,7 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
   a.tabs = reinterpret_cast<uint16_t*>(p);
   p += al256((size_t)n_segs * q->H * 2 * TAB_ELEMS * sizeof(uint16_t));
   a.ut = reinterpret_cast<uint16_t*>(p);
-  p += al256((size_t)n_segs * q->H * R * D * sizeof(uint16_t));
+  p += al256((size_t)n_segs * q->H * UT_ROWS * D * sizeof(uint16_t));
   if (a.nparts > 1) {
     const size_t n = (size_t)a.nparts * q->H * q->T;
     a.po = reinterpret_cast<float*>(p); p += al256(n * D * 4);
@@ -1091,8 +1127,17 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
   }
   const int per = (a.units + 7) / 8;
   const dim3 grid((unsigned)(per * 8));
-  if (top1) hipLaunchKernelGGL(attention_kernel<true>, grid, dim3(AT_T), 0, stream, a);
-  else hipLaunchKernelGGL(attention_kernel<false>, grid, dim3(AT_T), 0, stream, a);
+  // one PSAC k-step covers ranks 8 and 16; a rank-32 segment needs two
+  int max_r = 8;
+  for (int i = 0; i < n_segs; ++i)
+    if (segs[i].U != nullptr && segs[i].r > max_r) max_r = segs[i].r;
+  if (max_r > 16) {
+    if (top1) hipLaunchKernelGGL((attention_kernel<true, 2>), grid, dim3(AT_T), 0, stream, a);
+    else hipLaunchKernelGGL((attention_kernel<false, 2>), grid, dim3(AT_T), 0, stream, a);
+  } else {
+    if (top1) hipLaunchKernelGGL((attention_kernel<true, 1>), grid, dim3(AT_T), 0, stream, a);
+    else hipLaunchKernelGGL((attention_kernel<false, 1>), grid, dim3(AT_T), 0, stream, a);
+  }
   s = check_launch("attention");
   if (s != QWM_OK || a.nparts == 1) return s;
   const dim3 g2((unsigned)((q->T + 7) / 8), (unsigned)q->H);

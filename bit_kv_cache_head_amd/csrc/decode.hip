@@ -29,14 +29,15 @@ constexpr int DEC_TOK = 32;   // tokens per block: 8 threads per token, 16 chann
 // Grid (ceil(T / 32), H), 256 threads.  Thread (token tid / 8, channels
 // 16 (tid % 8) .. +16): the 16 channels' codes are one 32-bit word of the
 // token's code row (channel 16 b + j at bits 2 j).
+template <int RK>   // PSAC rank of the chunk: 8, 16 or 32
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int h = blockIdx.y, tid = threadIdx.x, tk = tid >> 3, cb = tid & 7;
   const qwm_segment& g = a.seg;
   const int64_t T = g.T;
-  __shared__ double U[D][R];
+  __shared__ double U[D][RK];
   const bool psac = g.U != nullptr;
   if (psac)
-    for (int e = tid; e < D * R; e += 256) U[e / R][e % R] = (double)bf16_bits_to_f32(g.U[(int64_t)h * D * R + e]);
+    for (int e = tid; e < D * RK; e += 256) U[e / RK][e % RK] = (double)bf16_bits_to_f32(g.U[(int64_t)h * D * RK + e]);
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * DEC_TOK + tk;
   if (t >= T) return;
@@ -51,11 +52,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int z = (g.k_zeros[zrow] >> zsh) & 3;
     const uint16_t* mu = g.k_centroids + ((int64_t)h * NC + g.k_idx[ht]) * D + 16 * cb;
     const u32x4 m0 = *reinterpret_cast<const u32x4*>(mu), m1 = *reinterpret_cast<const u32x4*>(mu + 8);
-    double cc[R];
+    double cc[RK];
     if (psac) {
       const double cs = (double)f16_bits_to_f32(g.k_c_scale[ht]);
 #pragma unroll
-      for (int r = 0; r < R; ++r) cc[r] = cs * (double)g.k_c[ht * R + r];
+      for (int r = 0; r < RK; ++r) cc[r] = cs * (double)g.k_c[ht * RK + r];
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       double v = m + s * (double)(q - z);
       if (psac) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) v += cc[r] * U[16 * cb + j][r];
+        for (int r = 0; r < RK; ++r) v += cc[r] * U[16 * cb + j][r];
       }
       ko[j] = (uint16_t)f64_to_bf16_bits(v);
     }
@@ -156,7 +157,9 @@ qwm_status launch_decode(const qwm_segment* seg, int32_t H, uint16_t* k_out, uin
   a.seg = *seg;
   a.H = H; a.kout = k_out; a.vout = v_out; a.ost = ost; a.osh = osh;
   const dim3 grid((unsigned)((seg->T + DEC_TOK - 1) / DEC_TOK), (unsigned)H);
-  hipLaunchKernelGGL(decode_kernel, grid, dim3(256), 0, stream, a);
+  if (seg->r == 32) hipLaunchKernelGGL(decode_kernel<32>, grid, dim3(256), 0, stream, a);
+  else if (seg->r == 16) hipLaunchKernelGGL(decode_kernel<16>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(decode_kernel<8>, grid, dim3(256), 0, stream, a);
   return check_launch("chunk decode");
 }
 

@@ -690,6 +690,8 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
           m = lanepair_max(m);
           bool sat = false;
           uint32_t csb = fp16_up_div((double)m, 127.0f, &sat);
+          if (sat && fast && valid && hh == 0 && a.diag)
+            atomicAdd((unsigned long long*)&a.diag->scale_saturations, 1ull);
           const float cs = f16_bits_to_f32(csb);
           uint32_t packed = 0;
           float chat[4];   // c_s C_q of this lane's four coefficients
@@ -782,7 +784,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
             const uint8_t hi = (2 * lane + 1 < nv) ? sm.nib[wv][2 * lane + 1] : 0;
             a.zeros[(int64_t)h * a.zstride + (tok0 >> 1) + lane] = (uint8_t)(lo | (hi << 4));
           }
-          if (MODE == MODE_KEYS) {
+          if (MODE == MODE_KEYS && a.cq != nullptr) {   // null: a later pass writes the coefficients
             if (lane < nv) {
               *reinterpret_cast<uint2*>(a.cq + (base + lane) * R) = *reinterpret_cast<const uint2*>(&sm.cq[wv][lane][0]);
               a.cscale[base + lane] = sm.cs[wv][lane];
@@ -851,7 +853,7 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
         if (lane == 0) {
           a.idx[base] = 0;
           a.scale[base * 2] = 0; a.scale[base * 2 + 1] = 0;
-          if (MODE == MODE_KEYS) {
+          if (MODE == MODE_KEYS && a.cq != nullptr) {
             *reinterpret_cast<uint2*>(a.cq + base * R) = make_uint2(0u, 0u);
             a.cscale[base] = 0;
           }
@@ -1047,7 +1049,7 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
       atomicOr(word, nib << sh);
       if (nsat && a.diag) atomicAdd((unsigned long long*)&a.diag->scale_saturations, (unsigned long long)nsat);
     }
-    if (MODE == MODE_KEYS) {
+    if (MODE == MODE_KEYS && a.cq != nullptr) {
       int8_t* cq = a.cq + base * R;
       if (use_psac) {
         // E = k - mu - r_hat in fp64 (exact), C = E U in fp64
@@ -1066,6 +1068,7 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
         for (int i = 0; i < R; ++i) m = fmax(m, fabs(C[i]));
         bool s2 = false;
         const uint32_t csb = fp16_up_div(m, 127.0f, &s2);
+        if (s2 && lane == 0 && a.diag) atomicAdd((unsigned long long*)&a.diag->scale_saturations, 1ull);
         const double cs = (double)f16_bits_to_f32(csb);
         // integer coefficients of every lane's view (all lanes need them for
         // the keep test)
@@ -1116,6 +1119,111 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
       }
     }
   }
+}
+
+// PSAC coefficients for the rank ablation (r = 16, 32), exact in fp64, after
+// the centroid choice and codes are stored (QuantWM Sec. 4.2, method step (4);
+// App. C.2 rank study): E = k - (mu_idx + s (q - z)), C = E U, c_s = smallest
+// fp16 with 127 c_s >= max|C|, C_q = clamp(rne(C / c_s), -127, 127); the keep
+// test as in the exact path.  One wave per token (4 per block), lane l holds
+// channels 2 l, 2 l + 1.  Rows with a non-finite channel store zeros.
+struct PsacArgs {
+  const void* x; int32_t dtype; int64_t T; int64_t st, sh; int32_t H;
+  const uint16_t* mu; const float* w; const uint16_t* U; uint32_t flags;
+  const uint8_t* idx; const uint8_t* codes; const uint16_t* scale; const uint8_t* zeros; int64_t zstride;
+  int8_t* cq; uint16_t* cscale; qwm_diag* diag;
+};
+
+template <int RR>
+__global__ __launch_bounds__(256) void psac_kernel(PsacArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (id >= (int64_t)a.H * a.T) return;
+  const int h = (int)(id / a.T);
+  const int64_t tok = id % a.T, base = id;
+  int8_t* cq = a.cq + base * RR;
+  const bool psac = (a.flags & QWM_PSAC) && a.U != nullptr;
+  const int64_t rowoff = (int64_t)h * a.sh + tok * a.st + 2 * lane;
+  double x0, x1;
+  if (a.dtype == QWM_F32) {
+    const float* xr = static_cast<const float*>(a.x) + rowoff;
+    x0 = xr[0]; x1 = xr[1];
+  } else {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.x) + rowoff);
+    x0 = bf16_bits_to_f32(v & 0xFFFFu); x1 = bf16_bits_to_f32(v >> 16);
+  }
+  const bool bad = __any(!(__builtin_isfinite(x0) && __builtin_isfinite(x1)));
+  if (!psac || bad) {
+    if (lane < RR) cq[lane] = 0;
+    if (lane == 0) a.cscale[base] = 0;
+    return;
+  }
+  const int g = lane >> 5;
+  const uint32_t mw = *reinterpret_cast<const uint32_t*>(a.mu + ((int64_t)h * NC + a.idx[base]) * D + 2 * lane);
+  const double m0 = bf16_bits_to_f32(mw & 0xFFFFu), m1 = bf16_bits_to_f32(mw >> 16);
+  const uint32_t cb = a.codes[base * 32 + (lane >> 1)] >> (4 * (lane & 1));
+  const int q0 = (int)(cb & 3u), q1 = (int)((cb >> 2) & 3u);
+  const double sg = (double)f16_bits_to_f32(a.scale[base * 2 + g]);
+  const int z = (a.zeros[(int64_t)h * a.zstride + (tok >> 1)] >> (4 * (int)(tok & 1) + 2 * g)) & 3;
+  const double e0 = x0 - (m0 + sg * (double)(q0 - z));
+  const double e1 = x1 - (m1 + sg * (double)(q1 - z));
+  const uint16_t* Uh = a.U + (int64_t)h * D * RR;
+  double u0[RR], u1[RR];
+#pragma unroll
+  for (int i = 0; i < RR; ++i) {
+    u0[i] = (double)bf16_bits_to_f32(Uh[(2 * lane) * RR + i]);
+    u1[i] = (double)bf16_bits_to_f32(Uh[(2 * lane + 1) * RR + i]);
+  }
+  double C[RR];
+#pragma unroll
+  for (int i = 0; i < RR; ++i) C[i] = wave_sum_d(e0 * u0[i] + e1 * u1[i]);
+  double m = 0.0;
+#pragma unroll
+  for (int i = 0; i < RR; ++i) m = fmax(m, fabs(C[i]));
+  bool sat = false;
+  const uint32_t csb = fp16_up_div(m, 127.0f, &sat);
+  if (sat && lane == 0 && a.diag) atomicAdd((unsigned long long*)&a.diag->scale_saturations, 1ull);
+  const double cs = (double)f16_bits_to_f32(csb);
+  int cqi[RR];
+#pragma unroll
+  for (int i = 0; i < RR; ++i) {
+    int qi = 0;
+    if (cs > 0.0) {
+      // round half to even of C / cs, decided with exact products (n +- 1/2) cs
+      const double Ci = C[i];
+      double nq = rint(Ci / cs);
+      if (Ci > (nq + 0.5) * cs) nq += 1.0;
+      if (Ci < (nq - 0.5) * cs) nq -= 1.0;
+      int ni = (int)nq;
+      if (Ci == (nq + 0.5) * cs && (ni & 1)) ni += 1;
+      else if (Ci == (nq - 0.5) * cs && (ni & 1)) ni -= 1;
+      qi = ni < -127 ? -127 : (ni > 127 ? 127 : ni);
+    }
+    cqi[i] = qi;
+  }
+  bool keep = true;
+  if (a.flags & QWM_PSAC_KEEP) {
+    // the compensation D = (c_s C_q) U^T must lower sum_c w_c e_c^2 (weights of
+    // the centroid choice: w under QSAC, else 1)
+    double D0 = 0.0, D1 = 0.0;
+#pragma unroll
+    for (int i = 0; i < RR; ++i) {
+      const double ci = cs * (double)cqi[i];
+      D0 += ci * u0[i];
+      D1 += ci * u1[i];
+    }
+    const bool wts = (a.flags & QWM_QSAC) && a.w != nullptr;
+    const double w0 = wts ? (double)a.w[h * D + 2 * lane] : 1.0, w1 = wts ? (double)a.w[h * D + 2 * lane + 1] : 1.0;
+    const double crit = wave_sum_d(w0 * D0 * (D0 - 2.0 * e0) + w1 * D1 * (D1 - 2.0 * e1));
+    keep = crit < 0.0;
+  }
+  if (lane < RR) {
+    int qi = cqi[0];
+#pragma unroll
+    for (int i = 1; i < RR; ++i) if (lane == i) qi = cqi[i];
+    cq[lane] = keep ? (int8_t)qi : (int8_t)0;
+  }
+  if (lane == 0) a.cscale[base] = keep ? (uint16_t)csb : (uint16_t)0;
 }
 
 // mu_j^T S mu_j in fp64 for the full-matrix candidate distance: grid (H, NC / 4),
@@ -1553,21 +1661,39 @@ static float error_coeff(bool split) {
   return split ? (1.0f / 8192.0f + 1.0f / 32768.0f) : (1.0f / 8192.0f);
 }
 
+// The rank ablation's coefficients: one exact pass after the codes are stored.
+static qwm_status launch_psac(const qwm_tokens* k, const uint16_t* centroids, const float* w, const uint16_t* U,
+                              uint32_t flags, const qwm_packed* out, qwm_diag* diag, hipStream_t stream) {
+  PsacArgs p{};
+  p.x = k->ptr; p.dtype = k->dtype; p.T = k->T; p.st = k->stride_t; p.sh = k->stride_h; p.H = k->H;
+  p.mu = centroids; p.w = w; p.U = U; p.flags = flags;
+  p.idx = out->idx; p.codes = out->codes; p.scale = out->scale; p.zeros = out->zeros; p.zstride = zeros_stride(k->T);
+  p.cq = out->c; p.cscale = out->c_scale; p.diag = diag;
+  const int64_t blocks = ((int64_t)k->H * k->T + 3) / 4;
+  if (out->r == 16) hipLaunchKernelGGL(psac_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(psac_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return check_launch("PSAC coefficients");
+}
+
 qwm_status launch_keys(const qwm_tokens* k, const uint16_t* centroids, const float* w, const uint16_t* U,
                        int32_t M, uint32_t flags, const qwm_packed* out, qwm_diag* diag, void* ws,
                        hipStream_t stream) {
   SelWork wk = carve(ws, k->T, k->H, false);
   const bool qsac = flags & QWM_QSAC;
   const float* wts = qsac ? w : nullptr;
+  const bool fused_psac = out->r == R;   // rank 8: coefficients inside the selection kernels
   qwm_status s = prep(wk, centroids, wts, k->H, stream);
   if (s != QWM_OK) return s;
   SelectArgs a{};
   fill_common(a, k, wk, centroids);
-  a.w = wts; a.U = (flags & QWM_PSAC) ? U : nullptr; a.M = M; a.flags = flags;
+  a.w = wts; a.U = (fused_psac && (flags & QWM_PSAC)) ? U : nullptr; a.M = M; a.flags = flags;
   a.cb = error_coeff(wts != nullptr || k->dtype != QWM_BF16);
   a.idx = out->idx; a.codes = out->codes; a.scale = out->scale; a.zeros = out->zeros;
-  a.zstride = zeros_stride(k->T); a.cq = out->c; a.cscale = out->c_scale; a.diag = diag;
-  return run_select<MODE_KEYS>(k, a, stream, "key quantization");
+  a.zstride = zeros_stride(k->T); a.diag = diag;
+  a.cq = fused_psac ? out->c : nullptr; a.cscale = fused_psac ? out->c_scale : nullptr;
+  s = run_select<MODE_KEYS>(k, a, stream, "key quantization");
+  if (s != QWM_OK || fused_psac) return s;
+  return launch_psac(k, centroids, wts, U, flags, out, diag, stream);
 }
 
 // The full-matrix ablation: S-weighted candidates for every token on the
@@ -1587,11 +1713,13 @@ qwm_status launch_keys_full(const qwm_tokens* k, const uint16_t* centroids, cons
                      dim3(256), 0, stream, out->zeros, zb);
   s = check_launch("zero-point clear");
   if (s != QWM_OK) return s;
+  const bool fused_psac = out->r == R;
   SelectArgs a{};
   fill_common(a, k, wk, centroids);
-  a.w = w; a.U = (flags & QWM_PSAC) ? U : nullptr; a.M = M; a.flags = flags;
+  a.w = w; a.U = (fused_psac && (flags & QWM_PSAC)) ? U : nullptr; a.M = M; a.flags = flags;
   a.idx = out->idx; a.codes = out->codes; a.scale = out->scale; a.zeros = out->zeros;
-  a.zstride = zeros_stride(k->T); a.cq = out->c; a.cscale = out->c_scale; a.diag = diag;
+  a.zstride = zeros_stride(k->T); a.diag = diag;
+  a.cq = fused_psac ? out->c : nullptr; a.cscale = fused_psac ? out->c_scale : nullptr;
   a.qS = S; a.qn = n; a.qB = wk.qB;
   const int64_t per = (k->T + 3) / 4;
   const dim3 grid((unsigned)(per < 64 ? (per > 0 ? per : 1) : 64), (unsigned)k->H);
@@ -1599,7 +1727,9 @@ qwm_status launch_keys_full(const qwm_tokens* k, const uint16_t* centroids, cons
     hipLaunchKernelGGL((fallback_kernel<MODE_KEYS, false, true>), grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((fallback_kernel<MODE_KEYS, true, true>), grid, dim3(256), 0, stream, a);
-  return check_launch("full-matrix key quantization");
+  s = check_launch("full-matrix key quantization");
+  if (s != QWM_OK || fused_psac) return s;
+  return launch_psac(k, centroids, w, U, flags, out, diag, stream);
 }
 
 qwm_status launch_values(const qwm_tokens* v, const uint16_t* centroids, const qwm_packed* out, qwm_diag* diag,

@@ -517,6 +517,135 @@ __global__ __launch_bounds__(256) void eig_kernel(const double* __restrict__ S, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Principal basis for the rank ablation (r = 16, 32): one-sided (Hestenes)
+// Jacobi in fp64 on W = S / n + tau I, tau = trace / d > 0, one block per head.
+// Column pairs are rotated until every pair is orthogonal; then the columns
+// are (lambda_i + tau) v_i, so their norms order the eigenvalues and their
+// directions are the eigenvectors (the shift keeps every column away from
+// zero, so a rank-deficient M still yields an orthonormal basis).  Rounds
+// follow the circle method: 127 rounds of 64 disjoint pairs cover every pair
+// once per sweep.  Thread (pair tid / 4, rows 32 (tid % 4) .. +32).  W lives in
+// LDS column-major with a 2-double pad per column, so the 16 columns a wave
+// touches at one row offset fall on distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int JW = D + 2;             // doubles per stored column
+constexpr int JACOBI_SWEEPS = 30;
+constexpr double JACOBI_TOL = 1e-11;  // |w_p . w_q| <= tol ||w_p|| ||w_q|| for every pair
+
+__device__ __forceinline__ int circle_player(int m, int round) {
+  return m == 0 ? 0 : 1 + (m - 1 + round) % (D - 1);
+}
+
+__global__ __launch_bounds__(256) void jacobi_eig_kernel(const double* __restrict__ S, const int64_t* __restrict__ n,
+                                                         uint16_t* __restrict__ U, float* __restrict__ lambda,
+                                                         float* __restrict__ energy, int32_t* __restrict__ iters,
+                                                         int32_t r) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  __shared__ double W[D * JW];
+  __shared__ double nrm[D];
+  __shared__ int order[D];
+  __shared__ double trace_s;
+  __shared__ int rotated;
+  const int64_t nn = n[h];
+  uint16_t* Uh = U + (int64_t)h * D * r;
+  if (nn <= 0) {
+    for (int e = tid; e < D * r; e += 256) Uh[e] = 0;
+    if (tid < r) lambda[h * r + tid] = 0.f;
+    if (tid == 0) { energy[h] = 0.f; if (iters) iters[h] = 0; }
+    return;
+  }
+  const double* Sh = S + (int64_t)h * D * D;
+  if (tid < 64) {
+    double tr = 0.0;
+    for (int c = tid; c < D; c += 64) tr += Sh[c * D + c] / (double)nn;
+    tr = wave_sum_d(tr);
+    if (tid == 0) trace_s = tr;
+  }
+  __syncthreads();
+  const double tau = trace_s > 0.0 ? trace_s / D : 1.0;
+  for (int e = tid; e < D * D; e += 256) {
+    const int c = e / D, i = e % D;   // column c, row i (symmetric: read the upper triangle)
+    const double v = (i <= c) ? Sh[i * D + c] : Sh[c * D + i];
+    W[c * JW + i] = v / (double)nn + (i == c ? tau : 0.0);
+  }
+  __syncthreads();
+  const int pr = tid >> 2, part = tid & 3, r0 = 32 * part;
+  if (tid == 0) rotated = 0;
+  __syncthreads();
+  int sweep = 0;
+  for (sweep = 1; sweep <= JACOBI_SWEEPS; ++sweep) {
+    for (int round = 0; round < D - 1; ++round) {
+      const int p = circle_player(pr, round), q = circle_player(D - 1 - pr, round);
+      double* wp = W + p * JW + r0;
+      double* wq = W + q * JW + r0;
+      double al = 0.0, be = 0.0, ga = 0.0;
+#pragma unroll 8
+      for (int i = 0; i < 32; ++i) {
+        const double x = wp[i], y = wq[i];
+        al = fma(x, x, al);
+        be = fma(y, y, be);
+        ga = fma(x, y, ga);
+      }
+      // the pair's four threads are consecutive lanes of one wave
+      al += __shfl_xor(al, 1, 64); be += __shfl_xor(be, 1, 64); ga += __shfl_xor(ga, 1, 64);
+      al += __shfl_xor(al, 2, 64); be += __shfl_xor(be, 2, 64); ga += __shfl_xor(ga, 2, 64);
+      if (fabs(ga) > JACOBI_TOL * sqrt(al * be)) {
+        // rotation that makes the pair orthogonal (smaller of the two angles)
+        const double zeta = (be - al) / (2.0 * ga);
+        const double t = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
+        const double c = 1.0 / sqrt(1.0 + t * t), sn = c * t;
+#pragma unroll 8
+        for (int i = 0; i < 32; ++i) {
+          const double x = wp[i], y = wq[i];
+          wp[i] = c * x - sn * y;
+          wq[i] = sn * x + c * y;
+        }
+        if (part == 0) rotated = 1;   // benign race: every writer stores 1
+      }
+      __syncthreads();
+    }
+    const int any = rotated;   // every thread reads the flag after the last round's barrier ...
+    __syncthreads();
+    if (tid == 0) rotated = 0;   // ... before it is cleared for the next sweep
+    __syncthreads();
+    if (!any) break;
+  }
+  // column norms = lambda + tau; order descending (lower column first on ties)
+  if (tid < D) {
+    double s2 = 0.0;
+    for (int i = 0; i < D; ++i) s2 = fma(W[tid * JW + i], W[tid * JW + i], s2);
+    nrm[tid] = sqrt(s2);
+  }
+  __syncthreads();
+  if (tid < D) {
+    const double v = nrm[tid];
+    int rank = 0;
+    for (int c = 0; c < D; ++c) rank += (nrm[c] > v || (nrm[c] == v && c < tid)) ? 1 : 0;
+    order[rank] = tid;
+  }
+  __syncthreads();
+  // outputs: the top r columns, normalised, largest-magnitude entry positive
+  if (tid < r) {
+    const int c = order[tid];
+    int imax = 0;
+    double vmax = -1.0;
+    for (int i = 0; i < D; ++i) {
+      const double v = fabs(W[c * JW + i]);
+      if (v > vmax) { vmax = v; imax = i; }
+    }
+    const double sg = (W[c * JW + imax] < 0.0 ? -1.0 : 1.0) / nrm[c];
+    for (int i = 0; i < D; ++i) Uh[i * r + tid] = (uint16_t)f64_to_bf16_bits(sg * W[c * JW + i]);
+    lambda[h * r + tid] = (float)(nrm[c] - tau);
+  }
+  if (tid == 0) {
+    double top = 0.0;
+    for (int j = 0; j < r; ++j) top += nrm[order[j]] - tau;
+    energy[h] = (float)(top / trace_s);
+    if (iters) iters[h] = sweep <= JACOBI_SWEEPS ? sweep : -JACOBI_SWEEPS;
+  }
+}
+
 }  // namespace qwm
 
 // ---------------------------------------------------------------------------
@@ -541,8 +670,12 @@ qwm_status launch_stats(const qwm_tokens* q, const qwm_qstats* st, int32_t compu
   qwm_status s = check_launch("query stats finalize");
   if (s != QWM_OK) return s;
   if (compute_basis) {
-    hipLaunchKernelGGL(eig_kernel, dim3(st->H), dim3(256), 0, stream, st->S, st->n, st->U, st->lambda,
-                       st->energy, st->iters);
+    if (st->r == R)
+      hipLaunchKernelGGL(eig_kernel, dim3(st->H), dim3(256), 0, stream, st->S, st->n, st->U, st->lambda,
+                         st->energy, st->iters);
+    else
+      hipLaunchKernelGGL(jacobi_eig_kernel, dim3(st->H), dim3(256), 0, stream, st->S, st->n, st->U, st->lambda,
+                         st->energy, st->iters, st->r);
     s = check_launch("principal basis");
   }
   return s;

@@ -180,3 +180,75 @@ def make_workload(name: str, *, seed: int = 0, layer: int = 0, heads=None, n_chu
         K, V, Q = round_to_bf16(K), round_to_bf16(V), round_to_bf16(Q)
     return Workload(name=name, dtype=dtype, chunk=tpc, n_chunks=nch, heads=heads, layer=layer,
                     f_energy=f, K=K, V=V, Q=Q)
+
+
+# ---------------------------------------------------------------------------
+# The same recipe drawn on the GPU.  The full-depth cache (40 layers x 40 heads
+# x 28,000 tokens, about 21 GiB of bf16 K and V) is too large to draw with the
+# numpy streams above in a benchmark's time, so its layers are drawn on the
+# device by torch's Philox generator: same distributions (cluster means,
+# per-frame drift, uniform cluster choice, noise; Haar basis and geometric
+# Query spectrum), different random numbers from the numpy streams.  One
+# generator per (config, layer, stream) draws all heads of the layer at once.
+# ---------------------------------------------------------------------------
+def _torch_seed(seed: int, cfg: int, layer: int, stream: int) -> int:
+    s = np.random.SeedSequence([seed, cfg, layer, 1000 + stream]).generate_state(2, dtype=np.uint32)
+    return int(s[0]) | (int(s[1] & 0x7FFFFFFF) << 32)
+
+
+def _device_clusters(g, H: int, n_tokens: int, frame_tokens: int, device, drift: float = 0.05,
+                     noise: float = 0.1):
+    """[n_tokens, H, d] bf16 tokens from drifting Gaussian clusters (all heads)."""
+    import torch
+    f32 = torch.float32
+    sigma = torch.exp(torch.empty(H, 1, D_HEAD, dtype=f32, device=device)
+                      .uniform_(math.log(0.25), math.log(4.0), generator=g))
+    means = sigma * torch.randn(H, N_CLUSTERS, D_HEAD, dtype=f32, device=device, generator=g)
+    out = torch.empty(n_tokens, H, D_HEAD, dtype=torch.bfloat16, device=device)
+    t = 0
+    frame = 0
+    while t < n_tokens:
+        if frame > 0:
+            means = means + drift * torch.randn(H, N_CLUSTERS, D_HEAD, dtype=f32, device=device, generator=g)
+        m = min(frame_tokens, n_tokens - t)
+        assign = torch.randint(0, N_CLUSTERS, (H, m), device=device, generator=g)
+        x = torch.gather(means, 1, assign[:, :, None].expand(H, m, D_HEAD))
+        x = x + noise * torch.randn(H, m, D_HEAD, dtype=f32, device=device, generator=g)
+        out[t:t + m] = x.transpose(0, 1).to(torch.bfloat16)
+        t += m
+        frame += 1
+    return out
+
+
+def device_layer(name: str, layer: int, *, seed: int = 0, f_energy=None, device="cuda", heads=None,
+                 n_tokens=None, n_queries=None):
+    """(K, V [T, H, d], Q [nq, H, d]) bf16 device tensors of one layer of a
+    workload, drawn on the device (see above).  heads / n_tokens / n_queries
+    shrink the draw (a smaller draw is not a slice of the full one)."""
+    import torch
+    cfg_id, H, dtype, tpc, nch, nq, f = CONFIGS[name]
+    if dtype != "bf16":
+        raise ValueError("device_layer draws the bf16 workloads")
+    f = f if f_energy is None else f_energy
+    T = tpc * nch if n_tokens is None else n_tokens
+    H = H if heads is None else heads
+    nq = (T if nq is None else nq) if n_queries is None else n_queries
+    frame = {"depth": FRAME_480P}.get(name, tpc)
+    gens = {}
+    for stream in (_STREAM_K, _STREAM_V, _STREAM_Q):
+        g = torch.Generator(device=device)
+        g.manual_seed(_torch_seed(seed, cfg_id, layer, stream))
+        gens[stream] = g
+    K = _device_clusters(gens[_STREAM_K], H, T, frame, device)
+    V = _device_clusters(gens[_STREAM_V], H, T, frame, device)
+    # Haar bases (QR of a Gaussian with the sign of R's diagonal fixed), fp64 on the host
+    gq = torch.Generator()
+    gq.manual_seed(_torch_seed(seed, cfg_id, layer, _STREAM_Q + 10))
+    G = torch.randn(H, D_HEAD, D_HEAD, dtype=torch.float64, generator=gq)
+    qm, rm = torch.linalg.qr(G)
+    U = (qm * torch.sign(torch.diagonal(rm, dim1=1, dim2=2))[:, None, :]).to(torch.float32).to(device)
+    lam = torch.from_numpy(query_spectrum(f)).to(torch.float32).to(device)
+    z = torch.randn(H, nq, D_HEAD, dtype=torch.float32, device=device, generator=gens[_STREAM_Q])
+    q = torch.matmul(z * torch.sqrt(lam)[None, None, :], U.transpose(1, 2).contiguous())   # [H, nq, d]
+    Q = q.transpose(0, 1).contiguous().to(torch.bfloat16)
+    return K, V, Q

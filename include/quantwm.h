@@ -18,8 +18,9 @@
  *    ABI.  Calls are reentrant; calls that share output or state buffers must
  *    be ordered by the caller (same stream).
  *  - Shapes: head dim d = 128, residual groups of 64 channels (G = 2),
- *    n_c = 256 centroids, PSAC rank r = 8 (the configuration of the paper's
- *    implementation details, Sec. 5.1 / App. D.1).
+ *    n_c = 256 centroids (the configuration of the paper's implementation
+ *    details, Sec. 5.1 / App. D.1), PSAC rank r = 8 by default and 16 or 32
+ *    for the paper's rank ablation (App. C.2, Table 9).
  *  - bf16 and fp16 values travel as uint16_t bit patterns.
  *  - Token tensors are [T][H][d] with element strides (channel stride 1).
  *
@@ -45,11 +46,12 @@
 extern "C" {
 #endif
 
-#define QWM_ABI_VERSION 4
+#define QWM_ABI_VERSION 5
 #define QWM_HEAD_DIM 128
 #define QWM_GROUP 64
 #define QWM_CENTROIDS 256
-#define QWM_RANK 8
+#define QWM_RANK 8        /* default PSAC rank */
+#define QWM_MAX_RANK 32   /* supported ranks: 8, 16, 32 */
 
 typedef enum {
   QWM_OK = 0,
@@ -98,10 +100,11 @@ typedef struct {
   float* lambda;    /* [H][r] their eigenvalues, descending (out) */
   float* energy;    /* [H] sum of the top-r eigenvalues / trace (out) */
   int32_t* iters;   /* [H] eigen-iterations used, negative if not converged; may be NULL */
-  int32_t H, d, r, reserved;
+  int32_t H, d, r, reserved;   /* r: 8, 16 or 32 (U [H][d][r], lambda [H][r]) */
 } qwm_qstats;
 
-/* One packed chunk (layout above).  c and c_scale are NULL for Values. */
+/* One packed chunk (layout above).  c and c_scale are NULL for Values; for
+ * keys c is [H][T][r] with r = 8, 16 or 32. */
 typedef struct {
   uint8_t* codes;
   uint8_t* idx;
@@ -123,13 +126,15 @@ typedef struct {
 
 /* One cached chunk as read by qwm_attention.  Pointers address the whole
  * chunk ([H][...] arrays); centroid tables are [H][256][d] bf16; U is
- * [H][d][r] bf16 or NULL (no PSAC term: cold-start chunk or PSAC off). */
+ * [H][d][r] bf16 or NULL (no PSAC term: cold-start chunk or PSAC off); r is
+ * the chunk's PSAC rank (8, 16 or 32: k_c is [H][T][r]). */
 typedef struct {
   const uint8_t* k_codes; const uint8_t* k_idx; const uint16_t* k_scale; const uint8_t* k_zeros;
   const int8_t* k_c; const uint16_t* k_c_scale;
   const uint8_t* v_codes; const uint8_t* v_idx; const uint16_t* v_scale; const uint8_t* v_zeros;
   const uint16_t* k_centroids; const uint16_t* v_centroids; const uint16_t* U;
   int64_t T;
+  int32_t r, reserved;
 } qwm_segment;
 
 /* Update the per-head Query statistics with the Queries q (T may be 0) and
@@ -138,6 +143,9 @@ typedef struct {
  * w = diag(M_h), U_r = top-8 eigenvectors of M_h stored in BF16).
  * S accumulates in fp64; q may be QWM_BF16 or QWM_F32.
  * Eigenvector order: eigenvalue descending; sign: largest-|entry| positive.
+ * r = 8: block subspace iteration warm-started from U; r = 16 or 32 (the
+ * rank ablation): one-sided Jacobi on the whole 128 x 128 matrix, which
+ * neither reads U nor reports iterations in a comparable way (iters = sweeps).
  * Workspace: qwm_workspace_bytes(QWM_OP_STATS, ...) bytes (0 today). */
 qwm_status qwm_update_query_stats(const qwm_tokens* q, const qwm_qstats* st, int32_t compute_basis,
                                   void* ws, size_t ws_bytes, qwm_stream stream);
@@ -163,7 +171,9 @@ qwm_status qwm_build_centroids(const qwm_tokens* x, int32_t n_centroids, int32_t
  * Without QWM_QSAC: nearest centroid.  Codec: s_g = smallest fp16 with 3 s_g >= R_g,
  * z_g = clamp(rne(-lo_g / s_g), 0, 3), q_c = clamp(rne(r_c / s_g) + z_g, 0, 3)
  * (rne = round half to even of the exact quotient; s_g = 0 -> z = q = 0).
- * flags & QWM_PSAC with U != NULL: E = k - k0_hat, C = E U ([d][r] bf16),
+ * flags & QWM_PSAC with U != NULL: E = k - k0_hat, C = E U (U [H][d][r] bf16,
+ * r = out->r: 8, or 16 / 32 for the rank ablation, whose coefficients come from
+ * a second, exact fp64 pass),
  * c_scale = smallest fp16 with 127 c_scale >= max|C|, c = clamp(rne(C / c_scale),
  * -127, 127); otherwise c = 0 and c_scale = 0.
  * out->T must equal k->T and out->H k->H.  Workspace: QWM_OP_KEYS. */

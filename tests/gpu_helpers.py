@@ -45,8 +45,10 @@ def packed_host(p) -> dict:
 
 
 def upload_packed(PackedChunk, H: int, T: int, keys: bool, heads_out: list) -> object:
-    """Device PackedChunk holding the oracle's packed arrays (one dict per head)."""
-    pc = PackedChunk(T, H, keys)
+    """Device PackedChunk holding the oracle's packed arrays (one dict per head);
+    the PSAC rank is the width of the oracle's coefficients."""
+    r = heads_out[0]["Cq"].shape[1] if keys else 8
+    pc = PackedChunk(T, H, keys, r=r)
     zs = pc.zeros.shape[1]
     codes = np.stack([o["codes"] for o in heads_out])
     idx = np.stack([o["idx"] for o in heads_out])

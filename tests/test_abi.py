@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert sorted(_abi.EXPORTS) == declared
     for name in declared:
         assert hasattr(_abi.lib, name), name
-    assert _abi.lib.qwm_abi_version() == 4
+    assert _abi.lib.qwm_abi_version() == 5
 
 
 def test_struct_layouts_match_header_sizes():
@@ -31,7 +31,7 @@ def test_struct_layouts_match_header_sizes():
     assert C.sizeof(_abi.Tokens) == 48
     assert C.sizeof(_abi.QStats) == 72
     assert C.sizeof(_abi.Packed) == 64
-    assert C.sizeof(_abi.Segment) == 112
+    assert C.sizeof(_abi.Segment) == 120
     assert C.sizeof(_abi.Diag) == 32
 
 
@@ -47,7 +47,7 @@ def test_sizes_and_strides():
     assert lib.qwm_workspace_bytes(1, 1560, 12, 0, 0) > k       # Lloyd adds assignment + shuffle
     # attention: the segment descriptors, fp16 centroid tables for every (segment, head),
     # plus split partials; one split: descriptors, tables and basis fragments only
-    assert lib.qwm_workspace_bytes(4, 64, 1, 16, 1) == 256 + 2 * 256 * 128 * 2 + 8 * 128 * 2
+    assert lib.qwm_workspace_bytes(4, 64, 1, 16, 1) == 256 + 2 * 256 * 128 * 2 + 32 * 128 * 2   # basis rows up to rank 32
     big = lib.qwm_workspace_bytes(4, 39000, 12, 1560, 25)
     assert big >= 25 * 12 * 2 * 256 * 128 * 2
     assert lib.qwm_workspace_bytes(4, 39000, 12, 1560, 0) == 0
@@ -124,12 +124,14 @@ def _segs(n, T=100):
                                   "v_idx", "v_scale", "v_zeros", "k_centroids", "v_centroids", "U"]):
             setattr(s, name, base + 0x1000 * k)
         s.T = T
+        s.r = 8
     return arr
 
 
 @pytest.mark.parametrize("field,value,code", [
     ("T", 0, 1), ("T", 1 << 26, 1), ("T", -5, 1), ("k_codes", 0, 1), ("v_centroids", 0, 1),
     ("k_codes", 0x100004, 1), ("k_scale", 0x100002, 1), ("U", 0x100008, 1), ("k_c", 0x100004, 1),
+    ("r", 12, 2), ("r", 0, 2),
 ])
 def test_attention_segment_validation(field, value, code):
     """Every host descriptor is checked before any HIP call: a bad segment T,

@@ -45,3 +45,24 @@ def test_frame_drift_and_cluster_noise():
     assert f0.shape[0] <= 256 and f1.shape[0] <= 256
     sig = np.exp(datagen.rng_for(0, 9, 0, 0, 1).uniform(np.log(0.25), np.log(4.0), 128))
     assert 0.25 <= sig.min() and sig.max() <= 4.0
+
+
+def test_device_layer_recipe():
+    """The on-device draw of a layer (CPU device here): shapes, bf16, reproducible
+    per (layer, seed), layers differ, and the Query spectrum's top-8 share is the
+    requested one (within sampling error)."""
+    import torch
+    K, V, Q = datagen.device_layer("depth", 3, device="cpu", heads=4, n_tokens=3000, n_queries=4000)
+    assert K.shape == (3000, 4, 128) and V.shape == K.shape and Q.shape == (4000, 4, 128)
+    assert K.dtype == torch.bfloat16 and Q.dtype == torch.bfloat16
+    K2, _, _ = datagen.device_layer("depth", 3, device="cpu", heads=4, n_tokens=3000, n_queries=4000)
+    assert torch.equal(K, K2)
+    K3, _, _ = datagen.device_layer("depth", 4, device="cpu", heads=4, n_tokens=3000, n_queries=4000)
+    assert not torch.equal(K, K3)
+    for h in range(4):
+        q = Q[:, h].double().numpy()
+        ev = np.linalg.eigvalsh(q.T @ q / len(q))[::-1]
+        assert abs(ev[:8].sum() / ev.sum() - 0.65) < 0.03
+        # 256 well-separated clusters: noise 0.1 around each token's mean
+        x = K[:, h].float().numpy()
+        assert 0.2 < np.median(x.std(axis=0)) < 4.0

@@ -307,3 +307,32 @@ def test_reference_top1_and_shift_rate(qwm):
         assert np.mean(g == ref) >= 0.95
     # shift rate between a cache attention top-1 and the reference: identical inputs give 0
     assert OA.shift_rate(top[0], top[0]) == 0.0
+
+
+def _oracle_lloyd_unit(args):
+    X, iters, seed, head = args
+    from oracle import lloyd as L
+    return L.lloyd(X, 256, iters, seed=seed, head=head)
+
+
+def test_depth_layer_lloyd_ten_iterations(qwm):
+    """The depth workload's table build as the bench runs it: 10 seeded Lloyd
+    iterations over a full 28,000-token layer, all 40 heads in one call (the
+    layer drawn on the device); heads 0 and 39 against the oracle's Lloyd, bit
+    for bit, the oracle's two heads in parallel processes."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import torch
+    from gpu_helpers import host
+    _log("depth layer: 10 seeded Lloyd iterations, 28,000 tokens x 40 heads")
+    K, _, _ = datagen.device_layer("depth", 0)
+    C = qwm.build_centroids(K, 10, seed=1)
+    torch.cuda.synchronize()
+    heads = [0, 39]
+    units = [(K[:, h].double().cpu().numpy(), 10, 1, h) for h in heads]
+    with cf.ProcessPoolExecutor(max_workers=2, mp_context=mp.get_context("spawn")) as ex:
+        tables = list(ex.map(_oracle_lloyd_unit, units))
+    Cg = host(C)
+    for h, Co in zip(heads, tables):
+        np.testing.assert_array_equal(Cg[h], Co)
+        _log(f"  head {h}: table bit-exact")

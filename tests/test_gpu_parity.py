@@ -462,6 +462,55 @@ def test_nonfinite_and_degenerate_tokens(qwm):
     np.testing.assert_array_equal(g["idx"][0, keep], o["idx"])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scale_saturation(qwm, dtype):
+    """Residual ranges past 3 x 65504 and PSAC coefficients past 127 x 65504:
+    the fp16 scales saturate at 65504 and are counted (the degenerate-input
+    reading); codes, scales, zero-points and c_scale bit for bit against the
+    oracle, C within 1 LSB, the counter equal to the oracle's saturations."""
+    import torch
+    from gpu_helpers import dev_tokens, dev_table, dev_basis, packed_host, idx_mismatches_allowed, compare_codec
+    w = datagen.make_workload("480p", heads=[0, 1], n_chunks=1, chunk=400)
+    K = w.K.copy()
+    Ct = np.stack([OL.lloyd(K[:, h].astype(np.float64), 256, 2, seed=5, head=h) for h in range(2)])
+    rng = np.random.default_rng(21)
+    Ub = np.stack([F.bf16_rne(datagen.haar_orthogonal(rng, 128)[:, :8]) for _ in range(2)])
+    wt = rng.uniform(0.2, 3.0, (2, 128)).astype(np.float32)
+    # group 0 of token 3: range 4e5 (scale 4e5 / 3 > 65504); token 7: group 1 at +-1e7
+    # (both scales saturate, and the uncoded error drives |C| past 127 x 65504);
+    # token 11: -3e5 in one channel; token 12: one channel at 2e5, just past the limit
+    for h in range(2):
+        K[3, h, 10] = 4.0e5
+        K[7, h, 64:] = np.where(np.arange(64) % 2 == 0, 1.0e7, -1.0e7)
+        K[11, h, 100] = -3.0e5
+        K[12, h, 5] = 2.0e5
+    if dtype == "bf16":
+        K = F.bf16_rne(K.astype(np.float64)).astype(np.float32)
+    diag = qwm.new_diag()
+    kp = qwm.quantize_keys(dev_tokens(K, dtype), dev_table(Ct), torch.from_numpy(wt).cuda(), dev_basis(Ub), M=8,
+                           flags=3, diag=diag)
+    torch.cuda.synchronize()
+    g = packed_host(kp)
+    want_sat = 0
+    for h in range(2):
+        o = Qz.quantize_keys(K[:, h].astype(np.float64), Ct[h], wt[h], Ub[h], M=8, flags=3)
+        nmis, nbad = idx_mismatches_allowed("qsac", o, g["idx"][h], K[:, h], Ct[h], w=wt[h], M=8)
+        assert nbad == 0
+        same = o["idx"] == g["idx"][h]
+        assert same[[3, 7, 11, 12]].all()
+        compare_codec(o, {k: v[h] for k, v in g.items()}, 400, same)
+        assert np.array_equal(g["c_scale_bits"][h][same], o["c_scale_bits"][same])
+        assert np.abs(g["c"][h].astype(np.int64) - o["Cq"].astype(np.int64))[same].max() <= 1
+        sat_c = int(np.sum(np.max(np.abs(o["C_raw"]), axis=1) > 127.0 * 65504.0))
+        assert o["saturated"] >= 4 and sat_c >= 1
+        for t in (3, 7, 11, 12):
+            assert 0x7BFF in g["scale_bits"][h][t]
+        assert g["c_scale_bits"][h][7] == 0x7BFF
+        want_sat += o["saturated"] + sat_c
+    _log(f"  saturations: {int(diag[2])} (oracle {want_sat})")
+    assert int(diag[2]) == want_sat
+
+
 # ---------------------------------------------------------------------------
 # Attention over the compressed cache
 # ---------------------------------------------------------------------------
