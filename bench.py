@@ -660,6 +660,57 @@ def rank_sweep(qwm, torch, step, ranks=(8, 16, 32)):
     return out
 
 
+def storage_refinements(qwm, torch, step):
+    """The storage refinements on layer 0 of the depth cache: the keep test
+    (diagonal in the key kernel, and the full e^T M e form as a pass), the
+    per-head dense / sparse coefficient layout, and two-level INT8 + FP16
+    group scales; resident bits per token-head and the attention time over
+    each stored form."""
+    K, V, Q = step.layers[0]
+    H, T = step.H, step.T
+    st, Ck, Cv = step.st[0], step.Ck[0], step.Cv[0]
+
+    def timed(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    out = {}
+    vp = qwm.quantize_values(V, Cv)
+    for name, flags, full in (("plain", 3, False), ("keep_diagonal", 7, False), ("keep_full", 3, True)):
+        kp = qwm.quantize_keys(K, Ck, st.w, st.U, M=8, flags=flags)
+        ms_keep = timed(lambda: qwm.psac_keep_full(K, Ck, st, st.U, kp)) if full else None
+        kept = float((kp.c_scale != 0).float().mean().item())
+        dense_bytes = kp.nbytes()
+        ms_compact = timed(lambda: qwm.compact_coefficients(kp))
+        lay = kp.layouts()
+        seg = qwm.segment_array([(kp, vp, Ck, Cv, st.U)])
+        ms_attn = timed(lambda: qwm.attention(Q, seg))
+        out[name] = {"kept_fraction": round(kept, 5), "sparse_heads": sum(1 for l in lay if l[0] == 1),
+                     "key_bytes_dense": int(dense_bytes), "key_bytes_stored": int(kp.nbytes()),
+                     "compact_ms": round(ms_compact, 4), "attention_ms": round(ms_attn, 4)}
+        if full:
+            out[name]["keep_full_pass_ms"] = round(ms_keep, 4)
+    # two-level scales on keys and values
+    kp = qwm.quantize_keys(K, Ck, st.w, st.U, M=8, flags=3)
+    vp2 = qwm.quantize_values(V, Cv)
+    ms_two = timed(lambda: (qwm.two_level_scales(K, Ck, kp, st.w, st.U, flags=3),
+                            qwm.two_level_scales(V, Cv, vp2)), n=1)
+    seg = qwm.segment_array([(kp, vp2, Ck, Cv, st.U)])
+    ms_attn = timed(lambda: qwm.attention(Q, seg))
+    bits = (kp.nbytes() + vp2.nbytes()) * 8 / (H * T)
+    out["two_level"] = {"bits_per_token_head": round(bits, 2), "convert_ms": round(ms_two, 4),
+                        "attention_ms": round(ms_attn, 4),
+                        "ratio_per_token_vs_bf16": round(4096 / bits, 3)}
+    return out
+
+
 def run_depth(args, qwm, torch, datagen, pool):
     import numpy as np
     log(f"drawing {args.layers} depth layers on the device")
@@ -709,6 +760,8 @@ def run_depth(args, qwm, torch, datagen, pool):
     res["wall_s_timed"] = round(wall, 3)
     log("rank sweep")
     res["rank_sweep"] = rank_sweep(qwm, torch, step)
+    log("storage refinements")
+    res["storage_refinements"] = storage_refinements(qwm, torch, step)
     if not args.no_rollout:
         log("rollout ablations")
         res["rollout_ablations"] = rollout_ablations(qwm, torch, datagen)
@@ -798,7 +851,7 @@ def keys_bulk(qwm, torch, Kall, table, st):
             "GBps": round(byts / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
-def keys_keep_test(qwm, torch, Kall, table, st, chunk_tokens):
+def keys_keep_test(qwm, torch, Kall, table, st):
     """Bulk key quantization with the PSAC keep test (flags QSAC | PSAC | KEEP):
     time, and the fraction of tokens that keep their coefficients."""
     H = Kall.shape[1]
@@ -813,23 +866,8 @@ def keys_keep_test(qwm, torch, Kall, table, st, chunk_tokens):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / 3
-    keep = (kb.c_scale != 0)
-    kept = float(keep.float().mean().item())
-    # per (chunk, head) coefficient storage: the smaller of the dense and sparse layouts
-    T = Kall.shape[0]
-    n_ch = T // chunk_tokens
-    counts = keep[:, : n_ch * chunk_tokens].reshape(H, n_ch, chunk_tokens).sum(dim=2).cpu().tolist()
-    dense = sparse_or_dense = 0
-    n_sparse = 0
-    for row in counts:
-        for k in row:
-            lay = qwm.coefficient_layout(chunk_tokens, int(k))
-            dense += lay["dense"]
-            sparse_or_dense += lay["bytes"]
-            n_sparse += lay["layout"] == "sparse"
-    return {"ms": round(ms, 4), "tokens_per_s": round(Kall.shape[0] / (ms * 1e-3), 1), "kept_fraction": round(kept, 4),
-            "coefficient_bytes": {"dense": int(dense), "chosen": int(sparse_or_dense),
-                                  "sparse_chunks": int(n_sparse), "chunks": int(n_ch * H)}}
+    kept = float((kb.c_scale != 0).float().mean().item())
+    return {"ms": round(ms, 4), "tokens_per_s": round(Kall.shape[0] / (ms * 1e-3), 1), "kept_fraction": round(kept, 4)}
 
 
 def keys_m_sweep(qwm, torch, Kall, table, st, Ms=(4, 8, 16, 256)):
@@ -1036,7 +1074,7 @@ def run_stream_or_pass(args, qwm, torch, w):
             res["prq_codec"] = prq_codec(qwm, torch, step.K[step.sl_new])
             res["keys_full_matrix"] = keys_full_matrix(qwm, torch, step.K[step.sl_new], step.prev[0], step.st)
             res["keys_keep_test"] = keys_keep_test(qwm, torch, step.K[: (step.nch - 1) * step.chunk], step.prev[0],
-                                                   step.st, step.chunk)
+                                                   step.st)
     else:
         res["keys_bulk"] = keys_bulk(qwm, torch, step.K, step.Ck, step.st)
     res["wall_s_timed"] = round(wall, 3)

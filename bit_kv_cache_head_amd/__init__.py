@@ -10,11 +10,13 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+import numpy as np
 import torch
 
 from ._abi import (lib, LIB_PATH, QWM_OK, QWM_F32, QWM_BF16, QWM_QSAC, QWM_PSAC, QWM_PSAC_KEEP, QWM_OP_STATS,
-                   QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION, QWM_OP_ATTENTION_ACTIVE, Tokens, QStats,
-                   Packed, Diag, Segment, check)
+                   QWM_OP_CENTROIDS, QWM_OP_KEYS, QWM_OP_VALUES, QWM_OP_ATTENTION, QWM_OP_ATTENTION_ACTIVE,
+                   QWM_OP_KEEP_FULL, QWM_LAYOUT_DENSE, QWM_LAYOUT_SPARSE, Tokens, QStats, Packed, Diag, Segment, CDir,
+                   check)
 
 D, NC, R, GROUP = 128, 256, 8, 64
 
@@ -73,7 +75,7 @@ _WS = Workspace()
 
 
 def new_diag(device="cuda") -> torch.Tensor:
-    """Device counters: [nonfinite_rows, exact_fallbacks, scale_saturations, reserved] int64."""
+    """Device counters: [nonfinite_rows, exact_fallbacks, scale_saturations, layout_overflows] int64."""
     return torch.zeros(4, dtype=torch.int64, device=device)
 
 
@@ -109,6 +111,8 @@ class PackedChunk:
 
     def __init__(self, T: int, H: int, keys: bool, device="cuda", r: int = R):
         self.T, self.H, self.keys, self.r = T, H, keys, r
+        self.scale_q = self.scale2 = None      # two-level scales (two_level_scales)
+        self.cdir = self.carena = None         # compacted coefficients (compact_coefficients)
         self.codes = torch.empty(H, T, D // 4, dtype=torch.uint8, device=device)
         self.idx = torch.empty(H, T, dtype=torch.uint8, device=device)
         self.scale = torch.empty(H, T, 2, dtype=torch.int16, device=device)
@@ -121,10 +125,36 @@ class PackedChunk:
                       _ptr(self.c), _ptr(self.c_scale), self.T, self.H, self.r)
 
     def nbytes(self) -> int:
-        tot = self.codes.numel() + self.idx.numel() + 2 * self.scale.numel() + self.zeros.numel()
+        """Bytes the chunk keeps: codes, indices, zero-points, its scales
+        (fp16, or INT8 codes plus the second level) and its coefficients
+        (dense, or as compacted)."""
+        tot = self.codes.numel() + self.idx.numel() + self.zeros.numel()
+        tot += 2 * self.scale.numel() if self.scale2 is None else self.scale_q.numel() + 2 * self.scale2.numel()
         if self.keys:
-            tot += self.c.numel() + 2 * self.c_scale.numel()
+            if self.cdir is None:
+                tot += self.c.numel() + 2 * self.c_scale.numel()
+            else:
+                tot += sum(self.coefficient_bytes())
         return tot
+
+    def coefficient_bytes(self) -> list:
+        """Per head: bytes of the compacted coefficients (host read of the directory)."""
+        d = self.cdir.cpu().numpy().view(np.int64).reshape(self.H, 2)
+        out = []
+        for h in range(self.H):
+            layout, count = int(d[h, 0] & 0xFFFFFFFF), int(d[h, 0] >> 32)
+            layout = layout - (1 << 32) if layout >= 1 << 31 else layout
+            out.append(int(lib.qwm_coefficient_bytes(layout, self.T, count, self.r)) if layout >= 0 else 0)
+        return out
+
+    def layouts(self) -> list:
+        """Per head: (layout, kept count, arena offset) of the compacted coefficients."""
+        d = self.cdir.cpu().numpy().view(np.int64).reshape(self.H, 2)
+        res = []
+        for h in range(self.H):
+            lo = int(d[h, 0] & 0xFFFFFFFF)
+            res.append((lo - (1 << 32) if lo >= 1 << 31 else lo, int(d[h, 0] >> 32), int(d[h, 1])))
+        return res
 
 
 def update_query_stats(q: torch.Tensor, st: QueryStats, compute_basis: bool = True):
@@ -234,15 +264,49 @@ def prq_quantize(x: torch.Tensor, stages: int, iters: int = 10, seed: int = 0):
     return first, C_last, quantize_values(e, C_last)
 
 
-def coefficient_layout(T: int, kept: int, r: int = R) -> dict:
-    """Bytes of one (chunk, head)'s PSAC coefficients in the dense layout (every
-    token: r INT8 + fp16 scale) and the sparse one (4-byte count, then each kept
-    token's 16-bit index -- 32-bit past 65,536 tokens -- coefficients and
-    scale); the cache keeps the smaller."""
-    dense = T * (r + 2)
-    sparse = 4 + kept * ((2 if T <= 65536 else 4) + r + 2)
-    return {"dense": dense, "sparse": sparse, "layout": "sparse" if sparse < dense else "dense",
-            "bytes": min(dense, sparse)}
+def two_level_scales(x: torch.Tensor, centroids: torch.Tensor, chunk: PackedChunk, w: torch.Tensor | None = None,
+                     U: torch.Tensor | None = None, flags: int = QWM_QSAC | QWM_PSAC,
+                     diag: torch.Tensor | None = None) -> PackedChunk:
+    """Convert a quantized chunk (the x and table it was quantized with; for
+    keys also its w, U and flags) to two-level group scales: INT8 step codes
+    chunk.scale_q [H, T, 2] under fp16 second-level scales chunk.scale2 [H, 2];
+    codes, zero-points (and C) re-encoded in place."""
+    td = _tokens(x)
+    chunk.scale_q = torch.empty(chunk.H, chunk.T, 2, dtype=torch.uint8, device=x.device)
+    chunk.scale2 = torch.empty(chunk.H, 2, dtype=torch.int16, device=x.device)
+    check(lib.qwm_two_level_scales(C.byref(td), _ptr(centroids), _ptr(w), _ptr(U), flags, int(chunk.keys),
+                                   C.byref(chunk.desc()), _ptr(chunk.scale_q), _ptr(chunk.scale2), _ptr(diag),
+                                   _stream()))
+    return chunk
+
+
+def psac_keep_full(k: torch.Tensor, centroids: torch.Tensor, st: "QueryStats", U: torch.Tensor,
+                   chunk: PackedChunk) -> PackedChunk:
+    """The keep test with the full second moment S / n of st on a key chunk
+    quantized without QWM_PSAC_KEEP (coefficients dropped in place)."""
+    td = _tokens(k)
+    ws, nb = _WS.get(lib.qwm_workspace_bytes(QWM_OP_KEEP_FULL, td.T, td.H, chunk.r, 0), k.device)
+    check(lib.qwm_psac_keep_full(C.byref(td), _ptr(centroids), _ptr(st.S), _ptr(st.n), _ptr(U), C.byref(chunk.desc()),
+                                 _ptr(chunk.scale_q), _ptr(chunk.scale2), ws, nb, _stream()))
+    return chunk
+
+
+def compact_coefficients(chunk: PackedChunk, arena: torch.Tensor | None = None, used: torch.Tensor | None = None,
+                         diag: torch.Tensor | None = None) -> PackedChunk:
+    """Store the chunk's coefficients per head in the smaller of the dense and
+    sparse layouts (chunk.cdir [H] directory, chunk.carena the arena).  Without
+    an arena, one sized for the dense layout of every head is allocated."""
+    H, T, r = chunk.H, chunk.T, chunk.r
+    if arena is None:
+        arena = torch.empty(H * int(lib.qwm_coefficient_bytes(QWM_LAYOUT_DENSE, T, T, r)), dtype=torch.uint8,
+                            device=chunk.c.device)
+    if used is None:
+        used = torch.zeros(1, dtype=torch.int64, device=chunk.c.device)
+    chunk.cdir = torch.empty(H * 16, dtype=torch.uint8, device=chunk.c.device)
+    chunk.carena = arena
+    check(lib.qwm_compact_coefficients(C.byref(chunk.desc()), _ptr(chunk.cdir), _ptr(arena), arena.numel(),
+                                       _ptr(used), _ptr(diag), _stream()))
+    return chunk
 
 
 def _segment(kp, vp, kc, vc, U) -> Segment:
@@ -256,6 +320,12 @@ def _segment(kp, vp, kc, vc, U) -> Segment:
     s.U = 0 if U is None else U.data_ptr()
     s.T = kp.T
     s.r = kp.r
+    if kp.cdir is not None:
+        s.k_cdir, s.k_carena = kp.cdir.data_ptr(), kp.carena.data_ptr()
+    if kp.scale2 is not None:
+        s.k_scale, s.k_scale2 = kp.scale_q.data_ptr(), kp.scale2.data_ptr()
+    if vp.scale2 is not None:
+        s.v_scale, s.v_scale2 = vp.scale_q.data_ptr(), vp.scale2.data_ptr()
     return s
 
 

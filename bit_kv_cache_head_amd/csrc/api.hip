@@ -46,6 +46,16 @@ qwm_status launch_centroid_residual(const qwm_tokens* x, const uint16_t* centroi
                                    int64_t ost, int64_t osh, hipStream_t stream);
 size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd);
 qwm_status noalloc_keys_scratch(void** ptr);
+size_t keepfull_ws_bytes(int32_t H, int32_t r);
+int64_t coefficient_layout_bytes(int32_t layout, int64_t T, int64_t count, int32_t r);
+qwm_status launch_two_level(const qwm_tokens* x, const uint16_t* centroids, const float* w, const uint16_t* U,
+                            uint32_t flags, const qwm_packed* io, bool keys, uint8_t* scale_q, uint16_t* scale2,
+                            qwm_diag* diag, hipStream_t stream);
+qwm_status launch_keep_full(const qwm_tokens* k, const uint16_t* centroids, const double* S, const int64_t* n,
+                            const uint16_t* U, const qwm_packed* io, const uint8_t* scale_q, const uint16_t* scale2,
+                            void* ws, hipStream_t stream);
+qwm_status launch_compact(const qwm_packed* keys, qwm_cdir* dir, uint8_t* arena, int64_t arena_bytes,
+                          int64_t* arena_used, qwm_diag* diag, hipStream_t stream);
 size_t attention_ws_bytes(int64_t total_keys, int32_t H, int64_t Tq, int32_t n_segs, bool active);
 
 static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -112,6 +122,7 @@ size_t qwm_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t n, int32_t 
     case QWM_OP_VALUES: return select_ws_bytes(T, H, false);
     case QWM_OP_ATTENTION: return n_segs >= 1 ? attention_ws_bytes(T, H, n, n_segs, false) : 0;
     case QWM_OP_ATTENTION_ACTIVE: return n_segs >= 0 ? attention_ws_bytes(T, H, n, n_segs, true) : 0;
+    case QWM_OP_KEEP_FULL: return (n == 8 || n == 16 || n == 32) ? keepfull_ws_bytes(H, (int32_t)n) : 0;
     default: return 0;
   }
 }
@@ -239,6 +250,10 @@ static qwm_status check_segments(const qwm_segment* segs, int32_t n_segs, int64_
         !aligned(g.k_zeros, 4) || !aligned(g.v_zeros, 4) || !aligned(g.k_centroids, 16) ||
         !aligned(g.v_centroids, 16) || (g.U && (!aligned(g.U, 16) || !aligned(g.k_c, 8) || !aligned(g.k_c_scale, 2))))
       return fail(QWM_ERR_ARG, at + "misaligned array (codes and tables 16 B, scales and zeros 4 B, c 8 B, U 16 B)");
+    if (g.k_cdir && (!g.k_carena || !aligned(g.k_cdir, 8) || !aligned(g.k_carena, 16)))
+      return fail(QWM_ERR_ARG, at + "a coefficient directory needs its arena (directory 8-byte, arena 16-byte aligned)");
+    if ((g.k_scale2 && !aligned(g.k_scale2, 4)) || (g.v_scale2 && !aligned(g.v_scale2, 4)))
+      return fail(QWM_ERR_ARG, at + "second-level scales misaligned");
     *total += g.T;
     if (*total >= ((int64_t)1 << 31)) return fail(QWM_ERR_UNSUPPORTED, "more than 2^31 - 1 keys in all");
   }
@@ -280,6 +295,7 @@ qwm_status qwm_decode_segment(const qwm_segment* seg, int32_t H, uint16_t* k_out
     return fail(QWM_ERR_ARG, "decode: a packed array or centroid table is null");
   if (seg->U && (!seg->k_c || !seg->k_c_scale)) return fail(QWM_ERR_ARG, "decode: PSAC basis without coefficients");
   if (seg->r != 8 && seg->r != 16 && seg->r != 32) return fail(QWM_ERR_UNSUPPORTED, "decode: rank must be 8, 16 or 32");
+  if (seg->k_cdir && !seg->k_carena) return fail(QWM_ERR_ARG, "decode: a coefficient directory needs its arena");
   if (!aligned(seg->k_codes, 16) || !aligned(seg->v_codes, 16) || !aligned(seg->k_centroids, 16) ||
       !aligned(seg->v_centroids, 16) || !aligned(seg->k_scale, 4) || !aligned(seg->v_scale, 4))
     return fail(QWM_ERR_ARG, "decode: misaligned packed arrays");
@@ -337,6 +353,58 @@ qwm_status qwm_attention_active(const qwm_tokens* q, const qwm_segment* segs, in
   if (s != QWM_OK) return s;
   return launch_attention(q, segs, n_segs, total_keys, k_active, v_active, scale, out, lse, top1, ws,
                           static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_two_level_scales(const qwm_tokens* x, const uint16_t* centroids, const float* w, const uint16_t* U,
+                                uint32_t flags, int32_t keys, const qwm_packed* inout, uint8_t* scale_q,
+                                uint16_t* scale2, qwm_diag* diag, qwm_stream stream) {
+  qwm_status s = check_tokens(x, "tokens", false);
+  if (s != QWM_OK) return s;
+  if (!centroids || !aligned(centroids, 16)) return fail(QWM_ERR_ARG, "centroids: null or not 16-byte aligned");
+  if (flags & ~(uint32_t)(QWM_QSAC | QWM_PSAC | QWM_PSAC_KEEP)) return fail(QWM_ERR_ARG, "unknown flag bits");
+  if (w && !aligned(w, 4)) return fail(QWM_ERR_ARG, "w misaligned");
+  if (U && !aligned(U, 16)) return fail(QWM_ERR_ARG, "U not 16-byte aligned");
+  if (diag && !aligned(diag, 8)) return fail(QWM_ERR_ARG, "diag misaligned");
+  if ((s = check_packed(inout, x, keys != 0, false)) != QWM_OK) return s;
+  if (!scale_q || !scale2 || !aligned(scale_q, 2) || !aligned(scale2, 4))
+    return fail(QWM_ERR_ARG, "scale_q / scale2: null or misaligned");
+  return launch_two_level(x, centroids, w, keys ? U : nullptr, keys ? flags : 0u, inout, keys != 0, scale_q, scale2,
+                          diag, static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_psac_keep_full(const qwm_tokens* k, const uint16_t* centroids, const double* S, const int64_t* n,
+                              const uint16_t* U, const qwm_packed* inout, const uint8_t* scale_q,
+                              const uint16_t* scale2, void* ws, size_t ws_bytes, qwm_stream stream) {
+  qwm_status s = check_tokens(k, "keys", false);
+  if (s != QWM_OK) return s;
+  if (!centroids || !aligned(centroids, 16)) return fail(QWM_ERR_ARG, "centroids: null or not 16-byte aligned");
+  if (!S || !n || !aligned(S, 8) || !aligned(n, 8)) return fail(QWM_ERR_ARG, "S / n: null or misaligned");
+  if (!U || !aligned(U, 16)) return fail(QWM_ERR_ARG, "U: null or not 16-byte aligned");
+  if ((s = check_packed(inout, k, true, true)) != QWM_OK) return s;
+  if (scale2 && (!scale_q || !aligned(scale2, 4))) return fail(QWM_ERR_ARG, "two-level scales: scale_q missing");
+  s = check_ws(ws, ws_bytes, keepfull_ws_bytes(k->H, inout->r));
+  if (s != QWM_OK) return s;
+  return launch_keep_full(k, centroids, S, n, U, inout, scale_q, scale2, ws, static_cast<hipStream_t>(stream));
+}
+
+qwm_status qwm_compact_coefficients(const qwm_packed* keys, qwm_cdir* dir, uint8_t* arena, int64_t arena_bytes,
+                                    int64_t* arena_used, qwm_diag* diag, qwm_stream stream) {
+  if (!keys) return fail(QWM_ERR_ARG, "keys: null descriptor");
+  if (keys->T < 1 || keys->H < 1 || keys->T >= ((int64_t)1 << 26)) return fail(QWM_ERR_ARG, "keys: T in [1, 2^26), H >= 1");
+  if (!keys->c || !keys->c_scale || !aligned(keys->c, 8) || !aligned(keys->c_scale, 2))
+    return fail(QWM_ERR_ARG, "keys: c / c_scale null or misaligned");
+  if (keys->r != 8 && keys->r != 16 && keys->r != 32) return fail(QWM_ERR_UNSUPPORTED, "rank must be 8, 16 or 32");
+  if (!dir || !aligned(dir, 8)) return fail(QWM_ERR_ARG, "dir: null or misaligned");
+  if (!arena || !aligned(arena, 256) || arena_bytes < 0) return fail(QWM_ERR_ARG, "arena: null or not 256-byte aligned");
+  if (!arena_used || !aligned(arena_used, 8)) return fail(QWM_ERR_ARG, "arena_used: null or misaligned");
+  if (diag && !aligned(diag, 8)) return fail(QWM_ERR_ARG, "diag misaligned");
+  return launch_compact(keys, dir, arena, arena_bytes, arena_used, diag, static_cast<hipStream_t>(stream));
+}
+
+int64_t qwm_coefficient_bytes(int32_t layout, int64_t T, int64_t count, int32_t r) {
+  if (T < 0 || count < 0 || count > T || (r != 8 && r != 16 && r != 32)) return -1;
+  if (layout != QWM_LAYOUT_DENSE && layout != QWM_LAYOUT_SPARSE) return -1;
+  return coefficient_layout_bytes(layout, T, count, r);
 }
 
 qwm_status qwm_reference_top1(const qwm_tokens* q, const qwm_tokens* k, int32_t* top1, qwm_stream stream) {

@@ -132,7 +132,7 @@ __device__ __forceinline__ h2 code_pair(uint32_t w, int sh, const CodeMasks& m) 
 // 16 (tid % 8) .. +16), so a wave reads 8 whole rows; blocks y = 0 also write
 // the basis fragments, and block (local segment, head 0, y = 0) its descriptor.
 // ---------------------------------------------------------------------------
-constexpr int SEG_BATCH = 24;   // descriptors per launch (2.8 KiB of kernel arguments)
+constexpr int SEG_BATCH = 20;   // descriptors per launch (3 KiB of kernel arguments)
 struct SegBatch {
   qwm_segment s[SEG_BATCH];
   int32_t first, count;
@@ -360,6 +360,7 @@ struct TileIdx {
 };
 struct TileRegs {
   uint32_t kcode, kscale, kzb, c2, cs;
+  uint32_t bmhi;   // sparse coefficients: the tile's bitmap word is (bmhi, c2), its prefix count cs
   uint32_t vcode0, vcode1, vscale0, vscale1, vzb;
   u32x4 kmu[2];   // 16 permuted fp16 centroid channels
   u32x4 vmu[2];   // 8 fp16 centroid channels of each of the two keys
@@ -375,9 +376,19 @@ struct TileRegs {
 struct SegDesc {
   const uint8_t *kc, *ks, *kz, *c, *cs, *vc, *vs, *vz, *ki, *vi;
   int T;
-  int cT;     // rows of PSAC coefficients: T, or 0 without PSAC (empty descriptors)
+  int cT;     // rows of PSAC coefficients: T (dense), the kept count (sparse), or 0 without PSAC
   int r;      // PSAC rank (bytes per coefficient row)
+  // compacted coefficients in the sparse layout: bitmap words and prefix counts
+  const uint8_t *cbm, *cpre;
+  int csparse, nw;
+  // two-level group scales: INT8 step codes under fp16 second-level scales
+  // (group 0 in the low half, group 1 in the high half)
+  int ktwo, vtwo;
+  uint32_t ks2, vs2;
 };
+__device__ __forceinline__ int64_t al16(int64_t n) { return (n + 15) & ~(int64_t)15; }
+
+template <bool EXT>
 __device__ __forceinline__ SegDesc seg_desc(const AttnArgs& a, int s, int h) {
   cseg& g = seg_at(a, s);
   const int64_t T = g.T;
@@ -400,6 +411,40 @@ __device__ __forceinline__ SegDesc seg_desc(const AttnArgs& a, int s, int h) {
   d.T = (int)T;
   // wave-uniform by construction; saying so keeps the descriptors scalar
   d.cT = __builtin_amdgcn_readfirstlane(psac ? (int)T : 0);
+  d.cbm = d.cpre = nullptr;
+  d.csparse = 0; d.nw = 0; d.ktwo = 0; d.vtwo = 0; d.ks2 = 0u; d.vs2 = 0u;
+  if constexpr (EXT) {
+    if (psac && g.k_cdir != nullptr) {
+      const __attribute__((address_space(4))) qwm_cdir* dir = (const __attribute__((address_space(4))) qwm_cdir*)g.k_cdir;
+      const int layout = dir[h].layout, count = dir[h].count;
+      const uint8_t* base = g.k_carena + dir[h].offset;
+      if (layout == QWM_LAYOUT_DENSE) {
+        d.c = base;
+        d.cs = base + al16(T * d.r);
+      } else if (layout == QWM_LAYOUT_SPARSE) {
+        const int64_t nw = (T + 63) / 64;
+        d.cbm = base;
+        d.cpre = base + al16(nw * 8);
+        d.c = d.cpre + al16(nw * 4);
+        d.cs = d.c + al16((int64_t)count * d.r);
+        d.csparse = 1;
+        d.nw = (int)nw;
+        d.cT = __builtin_amdgcn_readfirstlane(count);
+      } else {
+        d.cT = 0;   // the arena could not hold this head: no compensation
+      }
+    }
+    if (g.k_scale2 != nullptr) {
+      d.ktwo = 1;
+      d.ks = reinterpret_cast<const uint8_t*>(g.k_scale) + hb * 2;   // INT8 step codes: [H][T][G] bytes
+      d.ks2 = __builtin_amdgcn_readfirstlane(*(const __attribute__((address_space(4))) uint32_t*)(g.k_scale2 + 2 * h));
+    }
+    if (g.v_scale2 != nullptr) {
+      d.vtwo = 1;
+      d.vs = reinterpret_cast<const uint8_t*>(g.v_scale) + hb * 2;
+      d.vs2 = __builtin_amdgcn_readfirstlane(*(const __attribute__((address_space(4))) uint32_t*)(g.v_scale2 + 2 * h));
+    }
+  }
   return d;
 }
 
@@ -411,10 +456,10 @@ __device__ __forceinline__ SegDesc dense_desc(const AttnArgs& a) {
   d.r = 8;
   return d;
 }
-template <bool DENSE>
+template <bool DENSE, bool EXT>
 __device__ __forceinline__ SegDesc desc_for(const AttnArgs& a, int s, int h) {
   if constexpr (DENSE) return dense_desc(a);
-  else return seg_desc(a, s, h);
+  else return seg_desc<EXT>(a, s, h);
 }
 
 template <bool DENSE>
@@ -429,28 +474,76 @@ __device__ __forceinline__ void load_idx(const SegDesc& d, const Pos& P, const L
 
 // The packed bytes of a tile (codes, scales, zero-points, PSAC bytes); for
 // a dense unit all zeros, so its tiles dequantize to the rows themselves.
-template <bool DENSE, int NPK>
+template <bool DENSE, int NPK, bool EXT>
 __device__ __forceinline__ void load_bytes(const SegDesc& d, const Pos& P, const Lane& L, TileRegs& r) {
   const int k0 = P.tile * AT_K, T = DENSE ? 0 : d.T;
   {
     const int g = L.blk >> 2;
     r.kcode = ld32(buf(d.kc, T * 32), L.key * 32 + 4 * L.blk, k0 * 32);
-    r.kscale = ld16(buf(d.ks, T * 4), L.key * 4 + 2 * g, k0 * 4);
+    if (EXT && d.ktwo) r.kscale = ld8(buf(d.ks, T * 2), L.key * 2 + g, k0 * 2);   // step code, scaled in load_mu
+    else r.kscale = ld16(buf(d.ks, T * 4), L.key * 4 + 2 * g, k0 * 4);
     r.kzb = ld8(buf(d.kz, (T + 1) >> 1), L.key >> 1, k0 >> 1);
-    const rsrc_t cr = buf(d.c, d.cT * d.r);
-    const uint32_t cv = NPK == 1 ? ld16(cr, L.key * d.r + 2 * L.blk, k0 * d.r)
-                                 : ld32(cr, L.key * d.r + 4 * L.blk, k0 * d.r);
-    r.c2 = (2 * NPK * L.blk < d.r) ? cv : 0u;
-    r.cs = ld16(buf(d.cs, d.cT * 2), L.key * 2, k0 * 2);
+    if (EXT && d.csparse) {
+      // the tile's bitmap word and prefix count; load_mu gathers the kept rows
+      const rsrc_t bm = buf(d.cbm, d.nw * 8);
+      r.c2 = ld32(bm, 0, P.tile * 8);
+      r.bmhi = ld32(bm, 4, P.tile * 8);
+      r.cs = ld32(buf(d.cpre, d.nw * 4), 0, P.tile * 4);
+    } else {
+      const rsrc_t cr = buf(d.c, d.cT * d.r);
+      const uint32_t cv = NPK == 1 ? ld16(cr, L.key * d.r + 2 * L.blk, k0 * d.r)
+                                   : ld32(cr, L.key * d.r + 4 * L.blk, k0 * d.r);
+      r.c2 = (2 * NPK * L.blk < d.r) ? cv : 0u;
+      r.cs = ld16(buf(d.cs, d.cT * 2), L.key * 2, k0 * 2);
+    }
   }
   {
     const int g = L.oct >> 3;
-    const rsrc_t vc = buf(d.vc, T * 32), vs = buf(d.vs, T * 4);
+    const rsrc_t vc = buf(d.vc, T * 32);
     r.vcode0 = ld16(vc, (2 * L.p) * 32 + 2 * L.oct, k0 * 32);
     r.vcode1 = ld16(vc, (2 * L.p + 1) * 32 + 2 * L.oct, k0 * 32);
-    r.vscale0 = ld16(vs, (2 * L.p) * 4 + 2 * g, k0 * 4);
-    r.vscale1 = ld16(vs, (2 * L.p + 1) * 4 + 2 * g, k0 * 4);
+    if (EXT && d.vtwo) {
+      const rsrc_t vs = buf(d.vs, T * 2);
+      r.vscale0 = ld8(vs, (2 * L.p) * 2 + g, k0 * 2);
+      r.vscale1 = ld8(vs, (2 * L.p + 1) * 2 + g, k0 * 2);
+    } else {
+      const rsrc_t vs = buf(d.vs, T * 4);
+      r.vscale0 = ld16(vs, (2 * L.p) * 4 + 2 * g, k0 * 4);
+      r.vscale1 = ld16(vs, (2 * L.p + 1) * 4 + 2 * g, k0 * 4);
+    }
     r.vzb = ld8(buf(d.vz, (T + 1) >> 1), L.p, k0 >> 1);
+  }
+}
+
+// The stored-format conversions of a tile whose bytes have arrived (segment
+// descriptor d): a sparse head's kept rows are gathered by the tile's bitmap
+// word and prefix count; two-level step codes become fp16 steps (code times
+// the power-of-two second-level scale: exact).
+template <int NPK>
+__device__ __forceinline__ void ext_convert(const SegDesc& d, const Lane& L, TileRegs& r) {
+  if (d.csparse) {
+    const uint32_t lo = r.c2, hi = r.bmhi, pre = r.cs;
+    const int key = L.key;
+    const uint32_t word = key < 32 ? lo : hi;
+    const bool kept = (word >> (key & 31)) & 1u;
+    const uint32_t below = key < 32 ? __popc(lo & ((1u << key) - 1u))
+                                    : __popc(lo) + __popc(hi & ((1u << (key - 32)) - 1u));
+    const int e = (int)(pre + below);
+    const rsrc_t cr = buf(d.c, d.cT * d.r);
+    const uint32_t cv = NPK == 1 ? ld16(cr, e * d.r + 2 * L.blk) : ld32(cr, e * d.r + 4 * L.blk);
+    const uint32_t sv = ld16(buf(d.cs, d.cT * 2), e * 2);
+    r.c2 = (kept && 2 * NPK * L.blk < d.r) ? cv : 0u;
+    r.cs = kept ? sv : 0u;
+  }
+  if (d.ktwo) {
+    const uint32_t s2 = (L.blk >> 2) ? (d.ks2 >> 16) : (d.ks2 & 0xFFFFu);
+    const _Float16 st = (_Float16)(float)r.kscale * __builtin_bit_cast(_Float16, (uint16_t)s2);
+    r.kscale = (uint32_t)__builtin_bit_cast(uint16_t, st);
+  }
+  if (d.vtwo) {
+    const _Float16 s2 = __builtin_bit_cast(_Float16, (uint16_t)((L.oct >> 3) ? (d.vs2 >> 16) : (d.vs2 & 0xFFFFu)));
+    r.vscale0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)((_Float16)(float)r.vscale0 * s2));
+    r.vscale1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)((_Float16)(float)r.vscale1 * s2));
   }
 }
 
@@ -502,7 +595,7 @@ __device__ __forceinline__ void rows_to_f16(TileRegs& r) {
 
 // Copy the packed-byte fields (the centroid rows are loaded separately).
 __device__ __forceinline__ void take_bytes(TileRegs& d, const TileRegs& s) {
-  d.kcode = s.kcode; d.kscale = s.kscale; d.kzb = s.kzb; d.c2 = s.c2; d.cs = s.cs;
+  d.kcode = s.kcode; d.kscale = s.kscale; d.kzb = s.kzb; d.c2 = s.c2; d.cs = s.cs; d.bmhi = s.bmhi;
   d.vcode0 = s.vcode0; d.vcode1 = s.vcode1; d.vscale0 = s.vscale0; d.vscale1 = s.vscale1; d.vzb = s.vzb;
 }
 
@@ -653,7 +746,7 @@ __device__ __forceinline__ uint32_t pair_other(uint32_t v, int hh) {
 // One unit: 256 Queries (query block qb) x head h x split `split` of nsplit
 // of a key sequence, written to partial set `part`.  DENSE: the key sequence
 // is the active BF16 chunk; otherwise the packed segments.
-template <bool TOP1, bool DENSE, int NPK>
+template <bool TOP1, bool DENSE, int NPK, bool EXT>
 __device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf<NPK>* sb, int qb, int split, int nsplit,
                                                int part, int h) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hh = lane >> 5, ln = lane & 31;
@@ -722,7 +815,10 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf<NPK>* 
   // one tile ahead.  Segment fields: T of tiles n .. n + 2, the arrays of
   // tile n + 3's segment.
   int64_t T0 = seg_T<DENSE>(a, P0.seg), T1 = seg_T<DENSE>(a, P1.seg), T2 = seg_T<DENSE>(a, P2.seg);
-  SegDesc sd = desc_for<DENSE>(a, P3.seg, h);
+  SegDesc sd = desc_for<DENSE, EXT>(a, P3.seg, h);
+  // the descriptor of tile n + 2's segment, whose bytes get their stored-format
+  // conversions once they have arrived
+  SegDesc sdm = desc_for<DENSE, EXT>(a, P2.seg, h);
 
   // pipeline fill: tile 0 dequantized, tile 1 complete in registers, tile 2's
   // bytes and indices in flight
@@ -730,19 +826,21 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf<NPK>* 
   TileRegs regs, nbytes;
   TileIdx tix;
   {
-    const SegDesc d0 = desc_for<DENSE>(a, P0.seg, h);
+    const SegDesc d0 = desc_for<DENSE, EXT>(a, P0.seg, h);
     load_idx<DENSE>(d0, P0, L, tix);
-    load_bytes<DENSE, NPK>(d0, P0, L, regs);
+    load_bytes<DENSE, NPK, EXT>(d0, P0, L, regs);
+    if constexpr (EXT) ext_convert<NPK>(d0, L, regs);
     load_mu<DENSE>(a, P0.seg, P0.tile, h, L, tix, regs);
     if constexpr (DENSE) rows_to_f16(regs);
     dequant_tile<NPK>(regs, L, cm, sb[0]);
-    const SegDesc d1 = desc_for<DENSE>(a, P1.seg, h);
+    const SegDesc d1 = desc_for<DENSE, EXT>(a, P1.seg, h);
     load_idx<DENSE>(d1, P1, L, tix);
-    load_bytes<DENSE, NPK>(d1, P1, L, regs);
+    load_bytes<DENSE, NPK, EXT>(d1, P1, L, regs);
+    if constexpr (EXT) ext_convert<NPK>(d1, L, regs);
     load_mu<DENSE>(a, P1.seg, P1.tile, h, L, tix, regs);
-    const SegDesc d2 = desc_for<DENSE>(a, P2.seg, h);
+    const SegDesc d2 = desc_for<DENSE, EXT>(a, P2.seg, h);
     load_idx<DENSE>(d2, P2, L, tix);
-    load_bytes<DENSE, NPK>(d2, P2, L, nbytes);
+    load_bytes<DENSE, NPK, EXT>(d2, P2, L, nbytes);
   }
   __syncthreads();
 
@@ -806,8 +904,9 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf<NPK>* 
     // tile n + 2: its bytes arrived during the previous iteration; fetch its
     // centroid rows.  Tile n + 3: bytes and indices.
     take_bytes(regs, nbytes);
+    if constexpr (EXT) ext_convert<NPK>(sdm, L, regs);
     load_mu<DENSE>(a, P2.seg, P2.tile, h, L, tix, regs);
-    load_bytes<DENSE, NPK>(sd, P3, L, nbytes);
+    load_bytes<DENSE, NPK, EXT>(sd, P3, L, nbytes);
     load_idx<DENSE>(sd, P3, L, tix);
 
     if (wave_active) {
@@ -891,9 +990,10 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf<NPK>* 
     P0 = P1; T0 = T1;
     P1 = P2; T1 = T2;
     P2 = P3; T2 = sd.T;
+    if constexpr (EXT) sdm = sd;
     if (n + 4 < count) {
       P3 = advance<DENSE>(a, P3, sd.T);
-      if (!DENSE && P3.seg != P2.seg) sd = desc_for<DENSE>(a, P3.seg, h);
+      if (!DENSE && P3.seg != P2.seg) sd = desc_for<DENSE, EXT>(a, P3.seg, h);
     }
     cur ^= 1;
   }
@@ -939,7 +1039,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, AttnBuf<NPK>* 
   }
 }
 
-template <bool TOP1, int NPK>
+template <bool TOP1, int NPK, bool EXT>
 __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   __shared__ AttnBuf<NPK> sb[2];
   // XCD-aware unit mapping: consecutive units (same head) go to the same XCD
@@ -949,11 +1049,11 @@ __global__ __launch_bounds__(AT_T, 1) void attention_kernel(AttnArgs a) {
   if (unit >= a.units) return;
   if (unit < a.units_p) {
     const int qb = unit % a.nqb, split = (unit / a.nqb) % a.nsplit, h = unit / (a.nqb * a.nsplit);
-    attention_body<TOP1, false, NPK>(a, sb, qb, split, a.nsplit, split, h);
+    attention_body<TOP1, false, NPK, EXT>(a, sb, qb, split, a.nsplit, split, h);
   } else {
     const int u = unit - a.units_p;
     const int qb = u % a.nqb, split = (u / a.nqb) % a.nsplit_a, h = u / (a.nqb * a.nsplit_a);
-    attention_body<TOP1, true, NPK>(a, sb, qb, split, a.nsplit_a, a.nsplit + split, h);
+    attention_body<TOP1, true, NPK, false>(a, sb, qb, split, a.nsplit_a, a.nsplit + split, h);
   }
 }
 
@@ -1127,16 +1227,25 @@ qwm_status launch_attention(const qwm_tokens* q, const qwm_segment* segs, int32_
   }
   const int per = (a.units + 7) / 8;
   const dim3 grid((unsigned)(per * 8));
-  // one PSAC k-step covers ranks 8 and 16; a rank-32 segment needs two
+  // one PSAC k-step covers ranks 8 and 16; a rank-32 segment needs two.  The
+  // stored-format conversions (compacted coefficients, two-level scales) are
+  // compiled in only when a segment uses them.
   int max_r = 8;
-  for (int i = 0; i < n_segs; ++i)
+  bool ext = false;
+  for (int i = 0; i < n_segs; ++i) {
     if (segs[i].U != nullptr && segs[i].r > max_r) max_r = segs[i].r;
-  if (max_r > 16) {
-    if (top1) hipLaunchKernelGGL((attention_kernel<true, 2>), grid, dim3(AT_T), 0, stream, a);
-    else hipLaunchKernelGGL((attention_kernel<false, 2>), grid, dim3(AT_T), 0, stream, a);
-  } else {
-    if (top1) hipLaunchKernelGGL((attention_kernel<true, 1>), grid, dim3(AT_T), 0, stream, a);
-    else hipLaunchKernelGGL((attention_kernel<false, 1>), grid, dim3(AT_T), 0, stream, a);
+    ext = ext || segs[i].k_cdir != nullptr || segs[i].k_scale2 != nullptr || segs[i].v_scale2 != nullptr;
+  }
+  const int variant = (top1 ? 4 : 0) + (max_r > 16 ? 2 : 0) + (ext ? 1 : 0);
+  switch (variant) {
+    case 0: hipLaunchKernelGGL((attention_kernel<false, 1, false>), grid, dim3(AT_T), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((attention_kernel<false, 1, true>), grid, dim3(AT_T), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((attention_kernel<false, 2, false>), grid, dim3(AT_T), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((attention_kernel<false, 2, true>), grid, dim3(AT_T), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((attention_kernel<true, 1, false>), grid, dim3(AT_T), 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((attention_kernel<true, 1, true>), grid, dim3(AT_T), 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((attention_kernel<true, 2, false>), grid, dim3(AT_T), 0, stream, a); break;
+    default: hipLaunchKernelGGL((attention_kernel<true, 2, true>), grid, dim3(AT_T), 0, stream, a); break;
   }
   s = check_launch("attention");
   if (s != QWM_OK || a.nparts == 1) return s;

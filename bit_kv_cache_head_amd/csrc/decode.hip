@@ -48,15 +48,42 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   uint16_t ko[16], vo[16];
   {
     const uint32_t code = *reinterpret_cast<const uint32_t*>(g.k_codes + ht * 32 + 4 * cb);
-    const double s = (double)f16_bits_to_f32(g.k_scale[ht * 2 + grp]);
+    // group step: fp16, or a two-level step code times its power-of-two second level
+    const double s = g.k_scale2 ? (double)reinterpret_cast<const uint8_t*>(g.k_scale)[ht * 2 + grp] *
+                                      (double)f16_bits_to_f32(g.k_scale2[h * 2 + grp])
+                                : (double)f16_bits_to_f32(g.k_scale[ht * 2 + grp]);
     const int z = (g.k_zeros[zrow] >> zsh) & 3;
     const uint16_t* mu = g.k_centroids + ((int64_t)h * NC + g.k_idx[ht]) * D + 16 * cb;
     const u32x4 m0 = *reinterpret_cast<const u32x4*>(mu), m1 = *reinterpret_cast<const u32x4*>(mu + 8);
     double cc[RK];
     if (psac) {
-      const double cs = (double)f16_bits_to_f32(g.k_c_scale[ht]);
+      // the key's coefficients: dense rows, or from the compacted layout
+      const int8_t* crow = g.k_c + ht * RK;
+      const uint16_t* csp = g.k_c_scale + ht;
+      bool have = true;
+      if (g.k_cdir) {
+        const qwm_cdir e = g.k_cdir[h];
+        const uint8_t* base = g.k_carena + e.offset;
+        if (e.layout == QWM_LAYOUT_DENSE) {
+          crow = reinterpret_cast<const int8_t*>(base) + t * RK;
+          csp = reinterpret_cast<const uint16_t*>(base + ((T * RK + 15) & ~(int64_t)15)) + t;
+        } else if (e.layout == QWM_LAYOUT_SPARSE) {
+          const int64_t nw = (T + 63) / 64;
+          const uint64_t word = reinterpret_cast<const uint64_t*>(base)[t >> 6];
+          const uint32_t pre = reinterpret_cast<const uint32_t*>(base + ((nw * 8 + 15) & ~(int64_t)15))[t >> 6];
+          const int b = (int)(t & 63);
+          have = (word >> b) & 1ull;
+          const int64_t ent = (int64_t)pre + __popcll(word & ((1ull << b) - 1ull));
+          const uint8_t* cbase = base + ((nw * 8 + 15) & ~(int64_t)15) + ((nw * 4 + 15) & ~(int64_t)15);
+          crow = reinterpret_cast<const int8_t*>(cbase) + ent * RK;
+          csp = reinterpret_cast<const uint16_t*>(cbase + (((int64_t)e.count * RK + 15) & ~(int64_t)15)) + ent;
+        } else {
+          have = false;
+        }
+      }
+      const double cs = have ? (double)f16_bits_to_f32(*csp) : 0.0;
 #pragma unroll
-      for (int r = 0; r < RK; ++r) cc[r] = cs * (double)g.k_c[ht * RK + r];
+      for (int r = 0; r < RK; ++r) cc[r] = have ? cs * (double)crow[r] : 0.0;
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -73,7 +100,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
   {
     const uint32_t code = *reinterpret_cast<const uint32_t*>(g.v_codes + ht * 32 + 4 * cb);
-    const double s = (double)f16_bits_to_f32(g.v_scale[ht * 2 + grp]);
+    const double s = g.v_scale2 ? (double)reinterpret_cast<const uint8_t*>(g.v_scale)[ht * 2 + grp] *
+                                      (double)f16_bits_to_f32(g.v_scale2[h * 2 + grp])
+                                : (double)f16_bits_to_f32(g.v_scale[ht * 2 + grp]);
     const int z = (g.v_zeros[zrow] >> zsh) & 3;
     const uint16_t* mu = g.v_centroids + ((int64_t)h * NC + g.v_idx[ht]) * D + 16 * cb;
     const u32x4 m0 = *reinterpret_cast<const u32x4*>(mu), m1 = *reinterpret_cast<const u32x4*>(mu + 8);

@@ -12,6 +12,7 @@
 #include <mutex>
 
 #include "common.hpp"
+#include "psac.hpp"
 
 namespace qwm {
 
@@ -1167,63 +1168,10 @@ __global__ __launch_bounds__(256) void psac_kernel(PsacArgs a) {
   const int z = (a.zeros[(int64_t)h * a.zstride + (tok >> 1)] >> (4 * (int)(tok & 1) + 2 * g)) & 3;
   const double e0 = x0 - (m0 + sg * (double)(q0 - z));
   const double e1 = x1 - (m1 + sg * (double)(q1 - z));
-  const uint16_t* Uh = a.U + (int64_t)h * D * RR;
-  double u0[RR], u1[RR];
-#pragma unroll
-  for (int i = 0; i < RR; ++i) {
-    u0[i] = (double)bf16_bits_to_f32(Uh[(2 * lane) * RR + i]);
-    u1[i] = (double)bf16_bits_to_f32(Uh[(2 * lane + 1) * RR + i]);
-  }
-  double C[RR];
-#pragma unroll
-  for (int i = 0; i < RR; ++i) C[i] = wave_sum_d(e0 * u0[i] + e1 * u1[i]);
-  double m = 0.0;
-#pragma unroll
-  for (int i = 0; i < RR; ++i) m = fmax(m, fabs(C[i]));
-  bool sat = false;
-  const uint32_t csb = fp16_up_div(m, 127.0f, &sat);
-  if (sat && lane == 0 && a.diag) atomicAdd((unsigned long long*)&a.diag->scale_saturations, 1ull);
-  const double cs = (double)f16_bits_to_f32(csb);
-  int cqi[RR];
-#pragma unroll
-  for (int i = 0; i < RR; ++i) {
-    int qi = 0;
-    if (cs > 0.0) {
-      // round half to even of C / cs, decided with exact products (n +- 1/2) cs
-      const double Ci = C[i];
-      double nq = rint(Ci / cs);
-      if (Ci > (nq + 0.5) * cs) nq += 1.0;
-      if (Ci < (nq - 0.5) * cs) nq -= 1.0;
-      int ni = (int)nq;
-      if (Ci == (nq + 0.5) * cs && (ni & 1)) ni += 1;
-      else if (Ci == (nq - 0.5) * cs && (ni & 1)) ni -= 1;
-      qi = ni < -127 ? -127 : (ni > 127 ? 127 : ni);
-    }
-    cqi[i] = qi;
-  }
-  bool keep = true;
-  if (a.flags & QWM_PSAC_KEEP) {
-    // the compensation D = (c_s C_q) U^T must lower sum_c w_c e_c^2 (weights of
-    // the centroid choice: w under QSAC, else 1)
-    double D0 = 0.0, D1 = 0.0;
-#pragma unroll
-    for (int i = 0; i < RR; ++i) {
-      const double ci = cs * (double)cqi[i];
-      D0 += ci * u0[i];
-      D1 += ci * u1[i];
-    }
-    const bool wts = (a.flags & QWM_QSAC) && a.w != nullptr;
-    const double w0 = wts ? (double)a.w[h * D + 2 * lane] : 1.0, w1 = wts ? (double)a.w[h * D + 2 * lane + 1] : 1.0;
-    const double crit = wave_sum_d(w0 * D0 * (D0 - 2.0 * e0) + w1 * D1 * (D1 - 2.0 * e1));
-    keep = crit < 0.0;
-  }
-  if (lane < RR) {
-    int qi = cqi[0];
-#pragma unroll
-    for (int i = 1; i < RR; ++i) if (lane == i) qi = cqi[i];
-    cq[lane] = keep ? (int8_t)qi : (int8_t)0;
-  }
-  if (lane == 0) a.cscale[base] = keep ? (uint16_t)csb : (uint16_t)0;
+  const bool wts = (a.flags & QWM_QSAC) && a.w != nullptr;
+  psac_token<RR>(e0, e1, lane, a.U + (int64_t)h * D * RR, (a.flags & QWM_PSAC_KEEP) != 0,
+                 wts ? (double)a.w[h * D + 2 * lane] : 1.0, wts ? (double)a.w[h * D + 2 * lane + 1] : 1.0,
+                 cq, a.cscale + base, a.diag);
 }
 
 // mu_j^T S mu_j in fp64 for the full-matrix candidate distance: grid (H, NC / 4),

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define QWM_ABI_VERSION 5
+#define QWM_ABI_VERSION 6
 #define QWM_HEAD_DIM 128
 #define QWM_GROUP 64
 #define QWM_CENTROIDS 256
@@ -73,7 +73,7 @@ enum { QWM_QSAC = 1u, QWM_PSAC = 2u,
 
 /* Workspace-sizing operation ids for qwm_workspace_bytes(). */
 enum { QWM_OP_STATS = 0, QWM_OP_CENTROIDS = 1, QWM_OP_KEYS = 2, QWM_OP_VALUES = 3,
-       QWM_OP_ATTENTION = 4, QWM_OP_ATTENTION_ACTIVE = 5 };
+       QWM_OP_ATTENTION = 4, QWM_OP_ATTENTION_ACTIVE = 5, QWM_OP_KEEP_FULL = 6 };
 
 typedef void* qwm_stream; /* hipStream_t */
 
@@ -120,14 +120,38 @@ typedef struct {
 typedef struct {
   int64_t nonfinite_rows;     /* tokens with a NaN/Inf channel: stored as idx 0, codes 0 */
   int64_t exact_fallbacks;    /* tokens whose centroid choice needed the exact (slow) path */
-  int64_t scale_saturations;  /* group ranges beyond 3 * 65504 (scale saturates) */
-  int64_t reserved;
+  int64_t scale_saturations;  /* group ranges beyond 3 * 65504, or PSAC coefficients beyond
+                                 127 * 65504 (the fp16 scale saturates) */
+  int64_t layout_overflows;   /* qwm_compact_coefficients: heads the arena could not hold */
 } qwm_diag;
+
+/* Where one head's PSAC coefficients of a chunk live after
+ * qwm_compact_coefficients (QuantWM App. D.1: each chunk keeps the smaller of
+ * a dense and a sparse layout, sparse indices included).  At arena + offset:
+ *   dense  (layout 0): c [T][r] i8, then c_scale [T] fp16;
+ *   sparse (layout 1): bitmap [ceil(T/64)] u64 (key 64 w + b kept iff bit b of
+ *          word w), the kept count before each word [ceil(T/64)] u32, then the
+ *          kept keys' c [count][r] i8 and c_scale [count] fp16 in key order.
+ * Every section starts on a 16-byte boundary.  A key keeps coefficients iff its
+ * c_scale is nonzero.  layout -1: the arena was too small (nothing stored). */
+#define QWM_LAYOUT_DENSE 0
+#define QWM_LAYOUT_SPARSE 1
+#define QWM_LAYOUT_OVERFLOW (-1)
+typedef struct {
+  int32_t layout;
+  int32_t count;    /* keys that keep coefficients */
+  int64_t offset;   /* byte offset in the arena */
+} qwm_cdir;
 
 /* One cached chunk as read by qwm_attention.  Pointers address the whole
  * chunk ([H][...] arrays); centroid tables are [H][256][d] bf16; U is
  * [H][d][r] bf16 or NULL (no PSAC term: cold-start chunk or PSAC off); r is
- * the chunk's PSAC rank (8, 16 or 32: k_c is [H][T][r]). */
+ * the chunk's PSAC rank (8, 16 or 32: k_c is [H][T][r]).
+ * k_cdir / k_carena: NULL, or the chunk's compacted coefficients
+ * ([H] directory entries and their arena; k_c and k_c_scale are then unused).
+ * k_scale2 / v_scale2: NULL for fp16 group steps in k_scale / v_scale, or the
+ * [H][G] fp16 second-level scales of a two-level chunk, whose k_scale / v_scale
+ * then hold [H][T][G] INT8 step codes (see qwm_two_level_scales). */
 typedef struct {
   const uint8_t* k_codes; const uint8_t* k_idx; const uint16_t* k_scale; const uint8_t* k_zeros;
   const int8_t* k_c; const uint16_t* k_c_scale;
@@ -135,6 +159,8 @@ typedef struct {
   const uint16_t* k_centroids; const uint16_t* v_centroids; const uint16_t* U;
   int64_t T;
   int32_t r, reserved;
+  const qwm_cdir* k_cdir; const uint8_t* k_carena;
+  const uint16_t* k_scale2; const uint16_t* v_scale2;
 } qwm_segment;
 
 /* Update the per-head Query statistics with the Queries q (T may be 0) and
@@ -199,6 +225,56 @@ qwm_status qwm_quantize_keys(const qwm_tokens* k, const uint16_t* centroids, con
 qwm_status qwm_quantize_keys_noalloc(const qwm_tokens* k, const uint16_t* centroids, const float* w,
                                      const uint16_t* U, int32_t M, uint32_t flags, const qwm_packed* out,
                                      qwm_diag* diag, qwm_stream stream);
+
+/* Two-level group scales (rainbus digest, method step (3): group scales in
+ * INT8 under an FP16 second level) for a chunk already quantized by
+ * qwm_quantize_keys (keys != 0) or qwm_quantize_values (keys == 0): per (head,
+ * group g) the second-level scale s2_g is the smallest power of two p >= 2^-24
+ * with 255 p >= the largest fp16 step of the group; each token's step code is
+ * q = min(ceil(s / p), floor(65504 / p)) and its effective step q p (an exact
+ * fp16 value, never below s, so the codes still cover the range).  The codes
+ * and zero-points are re-encoded with the effective steps; for keys the PSAC
+ * coefficients are recomputed in fp64 from the new error (same flags, w and U
+ * as the quantizing call; QWM_PSAC_KEEP applies the diagonal keep test).
+ * x, centroids: the inputs of the quantizing call.  inout: the chunk (reads
+ * idx and the fp16 scale array; rewrites codes, zeros and, for keys, c and
+ * c_scale).  scale_q [H][T][G] u8, scale2 [H][G] fp16: outputs.  Afterwards
+ * attention and the decoder read the chunk with k_scale = scale_q and
+ * k_scale2 = scale2 (or the V fields).  No workspace. */
+qwm_status qwm_two_level_scales(const qwm_tokens* x, const uint16_t* centroids, const float* w, const uint16_t* U,
+                                uint32_t flags, int32_t keys, const qwm_packed* inout, uint8_t* scale_q,
+                                uint16_t* scale2, qwm_diag* diag, qwm_stream stream);
+
+/* The keep test with the full Query second moment (method step (4): the
+ * coefficients stay only where they lower the Query-weighted error, here
+ * e^T M_h e with M_h = S_h / n_h, the objective of the method section), as a
+ * pass over keys quantized without QWM_PSAC_KEEP: a key keeps its
+ * coefficients iff D^T S (D - 2 e) < 0, D = (c_scale c) U^T, e = k - k0_hat
+ * recomputed from its stored codes and step (fp16 scales, or the two-level
+ * scale_q and scale2 when scale2 is not NULL); otherwise c = 0, c_scale = 0.
+ * Heads with n_h = 0 are left as they are.  S [H][128][128] fp64 and n [H] as
+ * qwm_update_query_stats keeps them; U [H][d][r] the basis the keys were coded
+ * with.  Decided in fp64 through U^T S and U^T S U.  Workspace:
+ * QWM_OP_KEEP_FULL (T ignored, n = r). */
+qwm_status qwm_psac_keep_full(const qwm_tokens* k, const uint16_t* centroids, const double* S, const int64_t* n,
+                              const uint16_t* U, const qwm_packed* inout, const uint8_t* scale_q,
+                              const uint16_t* scale2, void* ws, size_t ws_bytes, qwm_stream stream);
+
+/* Store a chunk's PSAC coefficients in the smaller of the dense and the sparse
+ * layout, per head (QuantWM App. D.1; the layouts are described at qwm_cdir).
+ * keys: the chunk (reads c, c_scale, T, H, r).  Each head takes its bytes
+ * from the arena with one device-side atomic add on *arena_used (int64,
+ * device; the caller sets it, e.g. to 0) and records layout, count and offset
+ * in dir[h] (device).  A head that does not fit gets layout -1 and is counted
+ * in diag->layout_overflows.  arena: device, 256-byte aligned, arena_bytes
+ * long; qwm_coefficient_bytes gives a head's size under either layout (the
+ * dense one is the most a head can need). */
+qwm_status qwm_compact_coefficients(const qwm_packed* keys, qwm_cdir* dir, uint8_t* arena, int64_t arena_bytes,
+                                    int64_t* arena_used, qwm_diag* diag, qwm_stream stream);
+
+/* Bytes of one head's coefficients under a layout (QWM_LAYOUT_DENSE or
+ * QWM_LAYOUT_SPARSE) with T keys of which `count` keep coefficients, rank r. */
+int64_t qwm_coefficient_bytes(int32_t layout, int64_t T, int64_t count, int32_t r);
 
 /* The full-matrix ablation of QSAC (QuantWM App. C.4): as qwm_quantize_keys
  * with QWM_QSAC set, except that the M candidates are the M smallest by

@@ -47,16 +47,3 @@ def resident_ratio(tokens_per_chunk: int, n_chunks: int, d: int = 128, n_c: int 
     T = tokens_per_chunk * n_chunks
     comp = T * bits_per_token_head(d, 64, r) / 8 + n_chunks * table_bytes(d, n_c, r)
     return T * bf16_bits_per_token_head(d) / 8 / comp
-
-
-def coefficient_layout_bytes(T: int, kept: int, r: int = 8):
-    """PSAC coefficient storage of one (chunk, head) under the two layouts the
-    pages choose between per chunk (QuantWM App. D.1: the smaller of a dense
-    and a sparse layout, sparse indices included).  Dense: every token's r
-    INT8 coefficients and fp16 scale.  Sparse (reading): a 4-byte count, then
-    the kept tokens' indices (2 bytes each while T <= 65,536, else 4) and their
-    coefficients and scales.  Returns (dense, sparse, chosen) in bytes."""
-    dense = T * (r + 2)
-    index_bytes = 2 if T <= 65536 else 4
-    sparse = 4 + kept * (index_bytes + r + 2)
-    return dense, sparse, min(dense, sparse)

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert sorted(_abi.EXPORTS) == declared
     for name in declared:
         assert hasattr(_abi.lib, name), name
-    assert _abi.lib.qwm_abi_version() == 5
+    assert _abi.lib.qwm_abi_version() == 6
 
 
 def test_struct_layouts_match_header_sizes():
@@ -31,7 +31,8 @@ def test_struct_layouts_match_header_sizes():
     assert C.sizeof(_abi.Tokens) == 48
     assert C.sizeof(_abi.QStats) == 72
     assert C.sizeof(_abi.Packed) == 64
-    assert C.sizeof(_abi.Segment) == 120
+    assert C.sizeof(_abi.Segment) == 152
+    assert C.sizeof(_abi.CDir) == 16
     assert C.sizeof(_abi.Diag) == 32
 
 

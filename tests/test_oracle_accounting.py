@@ -45,21 +45,15 @@ def test_tables_and_resident_ratios():
     assert abs(Ac.resident_ratio(28000, 1) - 5.70) < 0.01
 
 
-def test_coefficient_layout_choice():
-    """Dense vs sparse PSAC coefficient storage (QuantWM App. D.1): closed forms
-    at the extremes and at the crossover; the package's host-side choice agrees."""
-    from oracle import accounting as Acc
-    import bit_kv_cache_head_amd as qwm
-    assert Acc.coefficient_layout_bytes(1560, 0) == (15600, 4, 4)
-    assert Acc.coefficient_layout_bytes(1560, 1560) == (15600, 4 + 1560 * 12, 15600)
-    # sparse wins iff 4 + 12 kept < 10 T
-    T = 1560
-    kmax = (10 * T - 4 - 1) // 12
-    assert Acc.coefficient_layout_bytes(T, kmax)[1] < T * 10 <= Acc.coefficient_layout_bytes(T, kmax + 1)[1]
-    assert Acc.coefficient_layout_bytes(70000, 10)[1] == 4 + 10 * 14      # 32-bit indices past 65,536
-    for T in (1, 64, 1560, 28000, 70000):
-        for kept in (0, 1, T // 3, T // 2, T):
-            d, s, c = Acc.coefficient_layout_bytes(T, kept)
-            got = qwm.coefficient_layout(T, kept)
-            assert (got["dense"], got["sparse"], got["bytes"]) == (d, s, c)
-            assert got["layout"] == ("sparse" if s < d else "dense")
+def test_coefficient_layout_bytes_of_the_library():
+    """The library's host-side layout sizes (qwm_coefficient_bytes) equal the
+    oracle's dense and sparse layout sizes (oracle.storage, QuantWM App. D.1)."""
+    from oracle import storage as St
+    from bit_kv_cache_head_amd._abi import lib, QWM_LAYOUT_DENSE, QWM_LAYOUT_SPARSE
+    for r in (8, 16, 32):
+        for T in (1, 63, 64, 65, 1560, 28000, 70000):
+            for kept in sorted({0, 1, T // 3, T // 2, T - 1, T} - {-1}):
+                assert lib.qwm_coefficient_bytes(QWM_LAYOUT_DENSE, T, kept, r) == St.dense_bytes(T, r)
+                assert lib.qwm_coefficient_bytes(QWM_LAYOUT_SPARSE, T, kept, r) == St.sparse_bytes(T, kept, r)
+    assert lib.qwm_coefficient_bytes(QWM_LAYOUT_SPARSE, 10, 11, 8) == -1
+    assert lib.qwm_coefficient_bytes(7, 10, 1, 8) == -1
