@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--workload", default="depth", choices=["depth", "480p", "720p", "tiny", "rollout"])
     ap.add_argument("--layers", type=int, default=40, help="depth: layers of the cache (40 = full depth)")
     ap.add_argument("--no-rollout", action="store_true", help="depth: skip the rollout ablations extra")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="depth: skip the rank sweep, stored-format and rollout extras")
     ap.add_argument("--f-energy", type=float, default=None, help="top-8 Query energy (720p: 0.60 or 0.71)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-ab", action="store_true",
@@ -758,11 +760,12 @@ def run_depth(args, qwm, torch, datagen, pool):
     res["device_counters_per_step"] = {"nonfinite_rows": int(diag_step[0]), "exact_fallbacks": int(diag_step[1]),
                                        "scale_saturations": int(diag_step[2])}
     res["wall_s_timed"] = round(wall, 3)
-    log("rank sweep")
-    res["rank_sweep"] = rank_sweep(qwm, torch, step)
-    log("storage refinements")
-    res["storage_refinements"] = storage_refinements(qwm, torch, step)
-    if not args.no_rollout:
+    if not args.no_extras:
+        log("rank sweep")
+        res["rank_sweep"] = rank_sweep(qwm, torch, step)
+        log("storage refinements")
+        res["storage_refinements"] = storage_refinements(qwm, torch, step)
+    if not (args.no_rollout or args.no_extras):
         log("rollout ablations")
         res["rollout_ablations"] = rollout_ablations(qwm, torch, datagen)
     if pool is not None:

@@ -9,6 +9,7 @@
 // with a certified error |f_j - e_j| <= c (||k||_w^2 + B_j).  A token whose
 // choice the bound cannot certify (close runners-up, non-finite values) is
 // sent to an exact fp64 path; no result depends on the approximation.
+#include <atomic>
 #include <mutex>
 
 #include "common.hpp"
@@ -95,7 +96,6 @@ struct SelectArgs {
   const float* w;       // [H][128] or null
   const uint16_t* U;    // [H][128][8] or null
   int32_t M; uint32_t flags; float cb;  // cb: certified relative error coefficient
-  int32_t blocks_per_head;
   // outputs
   uint8_t* idx;         // [H][T] (assignment for MODE_ASSIGN)
   uint8_t* codes; uint16_t* scale; uint8_t* zeros; int64_t zstride; int8_t* cq; uint16_t* cscale;
@@ -312,7 +312,11 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
   const double W0 = a.Wg[2 * h], W1 = a.Wg[2 * h + 1];
   const float cb = a.cb;
 
+  // This block's tiles of head h: a contiguous share [t_begin, t_end), equal
+  // to within one tile across the head's gridDim.x blocks.
   const int64_t ntile = (a.T + SEL_TOK - 1) / SEL_TOK;
+  const int64_t t_begin = (int64_t)blockIdx.x * ntile / gridDim.x;
+  const int64_t t_end = (int64_t)(blockIdx.x + 1) * ntile / gridDim.x;
   // Nearest-centroid modes (Lloyd assignment, values) have registers to spare:
   // each tile issues the next tile's bf16 token rows before its own work, so
   // their HBM latency passes under it.
@@ -320,14 +324,14 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
   u32x4 nrow[PF ? 8 : 1];
   auto fetch_rows = [&](int64_t t) __attribute__((always_inline)) {
     const int64_t tk = t * SEL_TOK + wv * 32 + ln;
-    const bool ok = t < ntile && tk < a.T;
+    const bool ok = t < t_end && tk < a.T;
     const uint16_t* xr = static_cast<const uint16_t*>(a.x) + (int64_t)h * a.sh + (ok ? tk : 0) * a.st;
 #pragma unroll
     for (int s = 0; s < (PF ? 8 : 1); ++s)
       nrow[s] = ok ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
   };
-  if constexpr (PF) fetch_rows(blockIdx.x);
-  for (int64_t tile = blockIdx.x; tile < ntile; tile += a.blocks_per_head) {
+  if constexpr (PF) fetch_rows(t_begin);
+  for (int64_t tile = t_begin; tile < t_end; ++tile) {
     const int64_t tok0 = tile * SEL_TOK + wv * 32;
     const int64_t tok = tok0 + ln;
     const bool valid = tok < a.T;
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
       if constexpr (PF) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) crow[s] = nrow[s];
-        fetch_rows(tile + a.blocks_per_head);
+        fetch_rows(tile + 1);
       }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -1537,9 +1541,25 @@ static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd) {
   return w;
 }
 
+// Compute units of the current device, looked up once per device.
+static int device_cus() {
+  static std::atomic<int> cache[NOALLOC_MAX_DEVICES];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Selection blocks per head: the grid fits in one wave of resident blocks (two
+// per CU: 80 KiB of LDS each), and each block takes an equal contiguous share
+// of its head's tiles, so no block is left running alone at the end.
 static int blocks_per_head(int64_t T, int32_t H) {
   const int64_t ntile = (T + SEL_TOK - 1) / SEL_TOK;
-  int64_t want = (2 * 256 * 2 + H - 1) / H;   // about four blocks per CU overall
+  int64_t want = 2 * (int64_t)device_cus() / H;
   if (want < 1) want = 1;
   return (int)(ntile < want ? ntile : want);
 }
@@ -1547,7 +1567,6 @@ static int blocks_per_head(int64_t T, int32_t H) {
 template <int MODE>
 static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t stream, const char* what) {
   const int bph = blocks_per_head(x->T, x->H);
-  a.blocks_per_head = bph;
   const bool qs = (MODE == MODE_KEYS) && (a.flags & QWM_QSAC) && a.M > 1;
   const bool wt = (MODE == MODE_KEYS) && a.w != nullptr;
   const dim3 grid(bph, x->H), block(256);
