@@ -368,7 +368,10 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
     }
     // ---- GEMM B operand t = -2 w (.) k: bf16 t_hi (RNE) and, unless exact, the
     // bf16 t_lo of the remainder t - t_hi (exact in fp32) ----
+    // The token norm A = sum_c w_c k_c^2 is gathered on the way as
+    // -(1/2) sum_c t_c k_c (t_c = fl32(-2 w_c k_c), one fma per channel).
     bf16x8 th[8], tl[SPLIT ? 8 : 1];
+    float An = 0.f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       u32x4 hv, lv;
@@ -378,6 +381,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
         const float x0 = kf[8 * s + 2 * e2], x1 = kf[8 * s + 2 * e2 + 1];
         const float t0 = WT ? sm.wm2[c] * x0 : -2.0f * x0;
         const float t1 = WT ? sm.wm2[c + 1] * x1 : -2.0f * x1;
+        An = fmaf(t1, x1, fmaf(t0, x0, An));
         hv[e2] = pk_bf16(t0, t1);
         if (SPLIT) lv[e2] = pk_bf16(t0 - lo_bf16(hv[e2]), t1 - hi_bf16(hv[e2]));
       }
@@ -443,15 +447,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
     if (!QS && g[KT] < gmin) gmin = g[KT];
 
     // ---- token norm A = sum_c w_c k_c^2 ----
-    float A = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = kf[8 * s + e];
-        A = fmaf(sm.w[16 * s + 8 * hh + e] * x, x, A);
-      }
-    A = lanepair_sum(A);
+    const float A = lanepair_sum(-0.5f * An);
     const float A_hi = A * (1.0f + 1.0f / 32768.0f), A_lo = A * (1.0f - 1.0f / 32768.0f);
     // certified bounds on d_Q(j) = A + e_j from the GEMM value f_j:
     //   [lbA + f_j - cb B_j, ubA + f_j + cb B_j]
@@ -517,17 +513,25 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
       // values are certainly smaller; the untracked ones must all be outside too.
       // Lb[k] is a lower bound on d_Q of slot k (raised to the rescored value once
       // the slot is scored); jp packs the slot's centroid index, four per word.
-      float Lb[2 * KT];
-      uint32_t jp[2 * KT / 4];
+      // vectors, so that the scan below reads slot `it` by register indexing
+      typedef float lbvec __attribute__((ext_vector_type(2 * KT)));
+      typedef uint32_t jpvec __attribute__((ext_vector_type(2 * KT / 4)));
+      lbvec Lb;
+      jpvec jp;
       uint32_t outmask = 0;
       bool unt_out;
       {
-        // At least M tracked values are certainly below x iff the M-th smallest
-        // upper bound UbM is < x: slot k is out when Lb[k] > UbM, and every
-        // untracked centroid (d_Q >= L_unt) when L_unt > UbM.
-        float Ub[2 * KT];
+        // UbM = the largest upper bound among the first M slots: M tracked
+        // centroids certainly lie at or below it, so slot k is out when
+        // Lb[k] > UbM, and every untracked centroid (d_Q >= L_unt) when
+        // L_unt > UbM.  (The slots are in GEMM-value order, so UbM is the M-th
+        // smallest upper bound up to the c B_j terms.)
+        float UbM = a.M > 2 * KT ? __builtin_inff() : -__builtin_inff();   // M > 2 KT: no slot is out
 #pragma unroll
-        for (int k = 0; k < 2 * KT; ++k) { Lb[k] = QWM_LB(g[k]); Ub[k] = QWM_UB(g[k]); }
+        for (int k = 0; k < 2 * KT; ++k) {
+          Lb[k] = QWM_LB(g[k]);
+          if (k < a.M) UbM = fmaxf(UbM, QWM_UB(g[k]));
+        }
 #pragma unroll
         for (int q = 0; q < 2 * KT / 4; ++q) {
           uint32_t v = 0;
@@ -535,21 +539,6 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
           for (int e = 0; e < 4; ++e) v |= (__float_as_uint(g[4 * q + e]) & 0xFFu) << (8 * e);
           jp[q] = v;
         }
-        // bitonic sort of the 2 KT upper bounds
-#pragma unroll
-        for (int size = 2; size <= 2 * KT; size <<= 1)
-#pragma unroll
-          for (int d = size >> 1; d >= 1; d >>= 1)
-#pragma unroll
-            for (int i = 0; i < 2 * KT; ++i)
-              if ((i & d) == 0) {
-                if ((i & size) == 0) cswap(Ub[i], Ub[i + d]);
-                else cswap(Ub[i + d], Ub[i]);
-              }
-        float UbM = __builtin_inff();   // M > 2 KT: no tracked slot can be certified out
-#pragma unroll
-        for (int k = 0; k < 2 * KT; ++k)
-          if (k == a.M - 1) UbM = Ub[k];
 #pragma unroll
         for (int k = 0; k < 2 * KT; ++k) outmask |= (Lb[k] > UbM ? 1u : 0u) << k;
         unt_out = L_unt > UbM;   // untracked centroids are all outside the M nearest
@@ -560,13 +549,12 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
       // after the scan, for the membership test.
       double Sbest = __builtin_inf();
       float dwin = 0.f;
-      // one slot per pass, always from position 0: Lb, jp and outmask rotate by
-      // one slot per pass and are back in place after the 2 KT passes
+      // one slot per pass (`it` is wave-uniform: slot it is read by register indexing)
 #pragma unroll 1
       for (int it = 0; it < 2 * KT; ++it) {
-        const bool need = fast && !(outmask & 1u) && ((double)Lb[0] <= Sbest * (1.0 + 1.0 / 1048576.0));
+        const bool need = fast && !((outmask >> it) & 1u) && ((double)Lb[it] <= Sbest * (1.0 + 1.0 / 1048576.0));
         if (__any(need)) {
-          const int j = (int)(jp[0] & 0xFFu);
+          const int j = (int)((jp[it >> 2] >> (8 * (it & 3))) & 0xFFu);
           const ResidStats rs = resid_ranges(kf, sm.mu, j, hh);
           if (need) {
             const double R0 = (double)rs.hi0 - (double)rs.lo0, R1 = (double)rs.hi1 - (double)rs.lo1;
@@ -577,15 +565,6 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
             }
           }
         }
-        const float l0 = Lb[0];
-#pragma unroll
-        for (int i = 0; i + 1 < 2 * KT; ++i) Lb[i] = Lb[i + 1];
-        Lb[2 * KT - 1] = l0;
-        const uint32_t j0 = jp[0];
-#pragma unroll
-        for (int q = 0; q + 1 < 2 * KT / 4; ++q) jp[q] = __builtin_amdgcn_alignbit(jp[q + 1], jp[q], 8);
-        jp[2 * KT / 4 - 1] = __builtin_amdgcn_alignbit(j0, jp[2 * KT / 4 - 1], 8);
-        outmask = (outmask >> 1) | ((outmask & 1u) << (2 * KT - 1));
       }
       if (__any(fast)) {
         const ResidStats rw = resid_stats<WT>(kf, sm.mu, win, hh, sm.w);
