@@ -293,8 +293,10 @@ class FullDepth:
     Per layer, three streams: the statistics and basis on one side stream
     (they feed only the keys), the V table and the values on another (they
     feed only the attention), the K table, the keys and the attention on the
-    main stream.  HIP events on the main stream bracket every key call and
-    every attention call."""
+    main stream.  The two tables' Lloyd iterations share the GPU; the key call
+    starts once the V side is done, so it has the GPU to itself, as does the
+    attention after it.  HIP events on the main stream bracket every key call
+    and every attention call."""
 
     LLOYD_ITERS = 10
 
@@ -351,11 +353,11 @@ class FullDepth:
                 self.v_done[l].record(self.vside)
             qwm.build_centroids(K, self.LLOYD_ITERS, seed=1, out=self.Ck[l], diag=self.diag)
             main.wait_event(self.stats_done[l])
+            main.wait_event(self.v_done[l])
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if events is not None else None
             if ev: ev[0].record(main)
             qwm.quantize_keys(K, self.Ck[l], st.w, st.U, M=8, flags=3, out=self.kp[l], diag=self.diag)
             if ev: ev[1].record(main)
-            main.wait_event(self.v_done[l])
             if ev: ev[2].record(main)
             self.out, _, _ = qwm.attention(Q, self.segs[l])
             if ev: ev[3].record(main)

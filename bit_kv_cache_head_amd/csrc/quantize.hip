@@ -271,14 +271,16 @@ constexpr float DREL = 1.0f / 65536.0f;   // relative error bound of the fp32 re
 
 // QS: QSAC selection (keys with the QSAC flag and M > 1); otherwise nearest.
 // WT: Query-weighted distances.
+// KQ: GEMM values tracked per lane in QSAC selection (8 for M <= 8, 16 for
+//     M <= 16: each lane holds half the centroids, so 2 KQ >= M candidates).
 //
 // The GEMM's A operand is the exact bf16 centroid row mu_j, staged once per
 // block in LDS (where the rescoring and the encoder read it too); the B operand
 // is the token side t = -2 w (.) k, exact in bf16 for unweighted bf16 tokens and
 // otherwise carried as a bf16 pair t_hi + t_lo (two MFMAs per k-step).
-template <int MODE, bool F32, bool QS, bool WT>
-__global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
-  constexpr int KT = QS ? 8 : 3;   // values tracked per lane (each lane holds half the centroids)
+template <int MODE, bool F32, bool QS, bool WT, int KQ = 8>
+__global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArgs a) {
+  constexpr int KT = QS ? KQ : 3;   // values tracked per lane (each lane holds half the centroids)
   constexpr bool SPLIT = F32 || WT;
   __shared__ SelShared sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hh = lane >> 5, ln = lane & 31;
@@ -1550,14 +1552,21 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
   const bool wt = (MODE == MODE_KEYS) && a.w != nullptr;
   const dim3 grid(bph, x->H), block(256);
   const bool f32 = x->dtype != QWM_BF16;
+  // M in 9 .. 16: sixteen values tracked per lane, so that the shortlist can
+  // still be certified without the exact path
+  const bool kq16 = qs && a.M > 8 && a.M <= 16;
   if constexpr (MODE == MODE_KEYS) {
     if (f32) {
-      if (qs && wt) hipLaunchKernelGGL((select_kernel<MODE, true, true, true>), grid, block, 0, stream, a);
+      if (kq16 && wt) hipLaunchKernelGGL((select_kernel<MODE, true, true, true, 16>), grid, block, 0, stream, a);
+      else if (kq16) hipLaunchKernelGGL((select_kernel<MODE, true, true, false, 16>), grid, block, 0, stream, a);
+      else if (qs && wt) hipLaunchKernelGGL((select_kernel<MODE, true, true, true>), grid, block, 0, stream, a);
       else if (qs) hipLaunchKernelGGL((select_kernel<MODE, true, true, false>), grid, block, 0, stream, a);
       else if (wt) hipLaunchKernelGGL((select_kernel<MODE, true, false, true>), grid, block, 0, stream, a);
       else hipLaunchKernelGGL((select_kernel<MODE, true, false, false>), grid, block, 0, stream, a);
     } else {
-      if (qs && wt) hipLaunchKernelGGL((select_kernel<MODE, false, true, true>), grid, block, 0, stream, a);
+      if (kq16 && wt) hipLaunchKernelGGL((select_kernel<MODE, false, true, true, 16>), grid, block, 0, stream, a);
+      else if (kq16) hipLaunchKernelGGL((select_kernel<MODE, false, true, false, 16>), grid, block, 0, stream, a);
+      else if (qs && wt) hipLaunchKernelGGL((select_kernel<MODE, false, true, true>), grid, block, 0, stream, a);
       else if (qs) hipLaunchKernelGGL((select_kernel<MODE, false, true, false>), grid, block, 0, stream, a);
       else if (wt) hipLaunchKernelGGL((select_kernel<MODE, false, false, true>), grid, block, 0, stream, a);
       else hipLaunchKernelGGL((select_kernel<MODE, false, false, false>), grid, block, 0, stream, a);

@@ -336,3 +336,60 @@ def test_depth_layer_lloyd_ten_iterations(qwm):
     for h, Co in zip(heads, tables):
         np.testing.assert_array_equal(Cg[h], Co)
         _log(f"  head {h}: table bit-exact")
+
+
+def test_attention_over_quantized_depth_layer(qwm):
+    """Attention over a quantized depth layer as the bench builds it: all 40
+    heads of a full 28,000-token layer quantized on the GPU (QSAC + PSAC keys,
+    M = 8, and values) with the oracle's Forgy tables and statistics, then
+    attended by the layer's 1,560 Queries.  For heads 0 and 39 the oracle
+    quantizes the same tokens with the same tables and attends to its own
+    cache; sampled Queries agree to the attention tolerance.  Centroid choices
+    may differ only at counted near-ties, and so may a top-1 key."""
+    import torch
+    from gpu_helpers import dev_tokens, dev_table, dev_basis, packed_host
+    _log("attention over a quantized depth layer: 28,000 keys x 40 heads, 1,560 Queries")
+    w = datagen.make_workload("depth", n_chunks=1)
+    H, T = w.H, w.chunk
+    K, V, Q = w.K[:T], w.V[:T], w.Q
+    heads = [0, H - 1]
+    ob = {}
+    for h in heads:
+        S, n = OS.update(np.zeros((128, 128)), 0, Q[:, h])
+        b = OS.principal_basis(S, n)
+        ob[h] = (OS.channel_weights(S, n), b["U_bf16"])
+    wt = np.stack([ob[heads[0]][0]] * H)
+    Ub = np.stack([ob[heads[0]][1]] * H)
+    wt[heads[1]], Ub[heads[1]] = ob[heads[1]][0], ob[heads[1]][1]
+    CK, CV = _forgy_tables(K, 41), _forgy_tables(V, 42)
+    dCK, dCV, dU = dev_table(CK), dev_table(CV), dev_basis(Ub)
+    kp = qwm.quantize_keys(dev_tokens(K, "bf16"), dCK, torch.from_numpy(wt.astype(np.float32)).cuda(), dU,
+                           M=8, flags=3)
+    vp = qwm.quantize_values(dev_tokens(V, "bf16"), dCV)
+    seg = qwm.segment_array([(kp, vp, dCK, dCV, dU)])
+    out, lse, top1 = qwm.attention(dev_tokens(Q, "bf16"), seg, want_lse=True, want_top1=True)
+    torch.cuda.synchronize()
+    out, lse, top1 = out.cpu().numpy(), lse.cpu().numpy(), top1.cpu().numpy()
+    gk, gv = packed_host(kp), packed_host(vp)
+    tq = Q.shape[0]
+    sample = np.unique(np.array([0, 1, 31, 32, 255, 256, tq // 2, tq - 2, tq - 1]))
+    for h in heads:
+        ok = Qz.quantize_keys(K[:, h].astype(np.float64), CK[h], wt[h], Ub[h], M=8, flags=3)
+        ov = Qz.quantize_values(V[:, h].astype(np.float64), CV[h])
+        nk = _check_keys("qsac", ok, gk, h, K[:, h], CK[h], wt[h], 8, 3)
+        nv = _check_keys("nearest", ov, gv, h, V[:, h], CV[h], None, 1, 0)
+        differ = (ok["idx"] != gk["idx"][h]) | (ov["idx"] != gv["idx"][h])
+        oseg = [dict(k_idx=ok["idx"], k_q=ok["q"], k_scale=ok["scale"], k_zero=ok["zero"], k_Cq=ok["Cq"],
+                     k_cs=ok["c_scale"], k_centroids=CK[h], U=Ub[h], v_idx=ov["idx"], v_q=ov["q"],
+                     v_scale=ov["scale"], v_zero=ov["zero"], v_centroids=CV[h])]
+        Qh = F.bf16_rne(Q[sample, h].astype(np.float64))
+        O, L, top = OA.cache_attention(Qh, oseg, 1 / np.sqrt(128))
+        err = np.linalg.norm(out[sample, h] - O) / np.linalg.norm(O)
+        _log(f"  head {h}: {nk} + {nv} near-tie centroid choices, rel L2 {err:.2e}")
+        assert err <= 2e-3
+        np.testing.assert_allclose(lse[h, sample], L, rtol=1e-4, atol=1e-4)
+        gt = top1[h, sample]
+        keep = ~(differ[gt] | differ[top])      # a top-1 key whose own coding differs is a counted near-tie
+        from gpu_helpers import check_top1_near_tie
+        nt = check_top1_near_tie(gt[keep], top[keep], Qh[keep], oseg)
+        _log(f"  head {h}: top-1 ok ({nt} near-tie logits, {int((~keep).sum())} on near-tie keys)")
