@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libquantwm.so")
-SOURCES = ["api.hip", "stats.hip", "quantize.hip", "attention.hip", "decode.hip", "reference.hip", "storage.hip"]
+SOURCES = ["api.hip", "stats.hip", "quantize.hip", "lloyd.hip", "attention.hip", "decode.hip", "reference.hip", "storage.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -10,9 +10,11 @@
 // choice the bound cannot certify (close runners-up, non-finite values) is
 // sent to an exact fp64 path; no result depends on the approximation.
 #include <atomic>
+#include <climits>
 #include <mutex>
 
 #include "common.hpp"
+#include "lloyd.hpp"
 #include "psac.hpp"
 
 namespace qwm {
@@ -31,6 +33,7 @@ struct TablePrepArgs {
   float* Bmax;          // [H][PREP_PARTS] partial maxima of B (times 1 + 2^-16)
   double* Wg;           // [H][2]
   int32_t* counter;     // fallback work counter (zeroed here)
+  int32_t* zero; int32_t nzero;   // more counters zeroed here (Lloyd lists), or null
 };
 
 // Block (h, part): centroids 32 part .. +32 of head h; thread (centroid
@@ -44,6 +47,8 @@ __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
   __shared__ float bm[4];
   if (tid < D) ws[tid] = a.w ? a.w[h * D + tid] : 1.0f;
   if (h == 0 && part == 0 && tid == 0) *a.counter = 0;
+  if (h == 0 && part == 0 && a.zero)
+    for (int i = tid; i < a.nzero; i += 256) a.zero[i] = 0;
   __syncthreads();
   const uint16_t* mj = a.mu + ((int64_t)h * NC + j) * D + c0;
   double B = 0.0;
@@ -106,6 +111,14 @@ struct SelectArgs {
   // Lloyd: one bit per token, set for rows with a non-finite channel (they
   // take no part in the mean update); [H][excl_words] u32
   uint32_t* excl; int64_t excl_words;
+  // Lloyd with distance bounds (MODE_ASSIGN): per token-head an upper bound on
+  // the distance to the chosen centroid and a lower bound on the distance to
+  // every other ([H][T], or null); after the first iteration only the tokens
+  // of the per-head lists wl [H][T] (counts wl_cnt [H]) are assigned, and every
+  // changed assignment is recorded as (h T + t, old | new << 8) in chg
+  float* ub; float* lb;
+  const int32_t* wl; const int32_t* wl_cnt;
+  uint2* chg; int32_t* chg_cnt;
 };
 
 constexpr int MU_ROW = D + 8;   // elements per staged centroid row (16 bytes of padding)
@@ -116,12 +129,22 @@ struct SelShared {
   float w[D];
   float wm2[D];                // -2 w (exact)
   uint16_t ut[R][D];           // U^T (bf16)
-  uint8_t codes[4][32][32];
   uint8_t idx[4][32];
-  uint16_t scale[4][32][2];
-  uint8_t nib[4][32];
-  int8_t cq[4][32][R];
-  uint16_t cs[4][32];
+  union {
+    struct {                   // keys and values: the wave's 32 tokens, staged for coalesced stores
+      uint8_t codes[4][32][32];
+      uint16_t scale[4][32][2];
+      uint8_t nib[4][32];
+      int8_t cq[4][32][R];
+      uint16_t cs[4][32];
+    } k;
+    struct {                   // Lloyd assignment: the wave's tokens, their bounds, certified or not
+      int32_t tok[4][32];
+      float ub[4][32];
+      float lb[4][32];
+      uint8_t fast[4][32];
+    } l;
+  };
 };
 
 // Two fp32 values as a bf16 pair (RNE; v_cvt_pk_bf16_f32), and its halves as fp32.
@@ -286,6 +309,16 @@ __global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArg
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hh = lane >> 5, ln = lane & 31;
   const int h = blockIdx.y;
   const bool use_psac = (MODE == MODE_KEYS) && (a.flags & QWM_PSAC) && a.U != nullptr;
+  // Lloyd after the first iteration: only the tokens of head h's list
+  const bool wlm = (MODE == MODE_ASSIGN) && a.wl != nullptr;
+  const int64_t nlist = wlm ? (int64_t)a.wl_cnt[h] : a.T;   // tokens (list entries) of head h
+
+  // This block's tiles of head h: a contiguous share [t_begin, t_end), equal
+  // to within one tile across the head's gridDim.x blocks.
+  const int64_t ntile = (nlist + SEL_TOK - 1) / SEL_TOK;
+  const int64_t t_begin = (int64_t)blockIdx.x * ntile / gridDim.x;
+  const int64_t t_end = (int64_t)(blockIdx.x + 1) * ntile / gridDim.x;
+  if (t_begin >= t_end) return;   // block-uniform
 
   // ---- stage the centroid rows, B_j, weights and U^T ----
   {
@@ -314,30 +347,33 @@ __global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArg
   const double W0 = a.Wg[2 * h], W1 = a.Wg[2 * h + 1];
   const float cb = a.cb;
 
-  // This block's tiles of head h: a contiguous share [t_begin, t_end), equal
-  // to within one tile across the head's gridDim.x blocks.
-  const int64_t ntile = (a.T + SEL_TOK - 1) / SEL_TOK;
-  const int64_t t_begin = (int64_t)blockIdx.x * ntile / gridDim.x;
-  const int64_t t_end = (int64_t)(blockIdx.x + 1) * ntile / gridDim.x;
+  // The token of this lane in tile t (list entry t SEL_TOK + 32 wv + ln);
+  // ok = false past the block's tiles or the head's tokens.
+  auto lane_token = [&](int64_t t, bool& ok) __attribute__((always_inline)) -> int64_t {
+    const int64_t e = t * SEL_TOK + wv * 32 + ln;
+    ok = t < t_end && e < nlist;
+    if (!wlm) return ok ? e : 0;
+    return ok ? (int64_t)a.wl[(int64_t)h * a.T + e] : 0;
+  };
   // Nearest-centroid modes (Lloyd assignment, values) have registers to spare:
   // each tile issues the next tile's bf16 token rows before its own work, so
   // their HBM latency passes under it.
   constexpr bool PF = !F32 && MODE != MODE_KEYS;
   u32x4 nrow[PF ? 8 : 1];
   auto fetch_rows = [&](int64_t t) __attribute__((always_inline)) {
-    const int64_t tk = t * SEL_TOK + wv * 32 + ln;
-    const bool ok = t < t_end && tk < a.T;
-    const uint16_t* xr = static_cast<const uint16_t*>(a.x) + (int64_t)h * a.sh + (ok ? tk : 0) * a.st;
+    bool ok;
+    const int64_t tk = lane_token(t, ok);
+    const uint16_t* xr = static_cast<const uint16_t*>(a.x) + (int64_t)h * a.sh + tk * a.st;
 #pragma unroll
     for (int s = 0; s < (PF ? 8 : 1); ++s)
       nrow[s] = ok ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
   };
   if constexpr (PF) fetch_rows(t_begin);
   for (int64_t tile = t_begin; tile < t_end; ++tile) {
-    const int64_t tok0 = tile * SEL_TOK + wv * 32;
-    const int64_t tok = tok0 + ln;
-    const bool valid = tok < a.T;
-    const int64_t rowoff = (int64_t)h * a.sh + (valid ? tok : 0) * a.st;
+    const int64_t tok0 = tile * SEL_TOK + wv * 32;   // first list entry of the wave
+    bool valid;
+    const int64_t tok = lane_token(tile, valid);
+    const int64_t rowoff = (int64_t)h * a.sh + tok * a.st;
 
     // ---- the token in fp32: channels 16 s + 8 hh + e at kf[8 s + e] ----
     float kf[64];
@@ -464,6 +500,7 @@ __global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArg
     int win = (int)(__float_as_uint(gmin) & 0xFFu);
     float wlo0 = 0.f, whi0 = 0.f, wlo1 = 0.f, whi1 = 0.f;   // group ranges of the winner
     bool have_w = false;                                   // ranges known for the winner
+    float bu2 = 0.f, bl2 = 0.f;   // Lloyd: squared distance bounds, the winner's (upper) and every other's (lower)
 
     if (!QS) {
       // nearest centroid (weighted when QSAC runs with M == 1)
@@ -509,6 +546,17 @@ __global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArg
           ok = ok && (j == win || lo > hi1);
         }
         fast = ok;
+      }
+      if (MODE == MODE_ASSIGN) {
+        float l2 = L_unt;
+#pragma unroll
+        for (int e = 0; e < 6; ++e) {
+          const int j = (int)(__float_as_uint(cn[e]) & 0xFFu);
+          const float lo = ((evm >> e) & 1u) ? dn[e] * (1.0f - DREL) : QWM_LB(cn[e]);
+          if (j != win) l2 = fminf(l2, lo);
+        }
+        bu2 = by_bounds ? ub0 : d1 * (1.0f + DREL);
+        bl2 = l2;
       }
     } else {
       // QSAC.  Tracked candidate k is certainly outside the M nearest when M other
@@ -589,8 +637,13 @@ __global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArg
 
     if (MODE == MODE_ASSIGN) {
       if (valid && hh == 0) {
+        sm.l.tok[wv][ln] = (int32_t)tok;
+        sm.l.fast[wv][ln] = fast ? 1 : 0;
         if (fast) {
           sm.idx[wv][ln] = (uint8_t)win;
+          // Euclidean distance bounds, rounded outward
+          sm.l.ub[wv][ln] = sqrtf(bu2) * (1.0f + 1.0f / 1048576.0f);
+          sm.l.lb[wv][ln] = sqrtf(fmaxf(bl2, 0.f)) * (1.0f - 1.0f / 1048576.0f);
         } else {
           const int slot = atomicAdd(a.counter, 1);
           a.worklist[slot] = (int32_t)((int64_t)h * a.T + tok);
@@ -630,7 +683,7 @@ __global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArg
             Ev[e] += (x - (r - bv)) + (-m - bv);
           }
         }
-        if (valid) *reinterpret_cast<uint16_t*>(&sm.codes[wv][ln][4 * s + 2 * hh]) = (uint16_t)bits;
+        if (valid) *reinterpret_cast<uint16_t*>(&sm.k.codes[wv][ln][4 * s + 2 * hh]) = (uint16_t)bits;
         if (use_psac) {
           bf16x8 uf;
           if (ln < R) uf = *reinterpret_cast<const bf16x8*>(&sm.ut[ln][16 * s + 8 * hh]);
@@ -654,18 +707,18 @@ __global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArg
       if (valid && hh == 0) {
         if (fast) {
           sm.idx[wv][ln] = (uint8_t)win;
-          sm.scale[wv][ln][0] = (uint16_t)g0.sbits;
-          sm.scale[wv][ln][1] = (uint16_t)g1.sbits;
-          sm.nib[wv][ln] = (uint8_t)(g0.z | (g1.z << 2));
+          sm.k.scale[wv][ln][0] = (uint16_t)g0.sbits;
+          sm.k.scale[wv][ln][1] = (uint16_t)g1.sbits;
+          sm.k.nib[wv][ln] = (uint8_t)(g0.z | (g1.z << 2));
           if ((sat0 || sat1) && a.diag) atomicAdd((unsigned long long*)&a.diag->scale_saturations,
                                                   (unsigned long long)((int)sat0 + (int)sat1));
         } else {
           const int slot = atomicAdd(a.counter, 1);
           a.worklist[slot] = (int32_t)((int64_t)h * a.T + tok);
           sm.idx[wv][ln] = 0;
-          sm.nib[wv][ln] = 0;
-          sm.scale[wv][ln][0] = 0;
-          sm.scale[wv][ln][1] = 0;
+          sm.k.nib[wv][ln] = 0;
+          sm.k.scale[wv][ln][0] = 0;
+          sm.k.scale[wv][ln][1] = 0;
         }
       }
       if (MODE == MODE_KEYS) {
@@ -738,42 +791,68 @@ __global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArg
             if (!(crit < 0.f)) { packed = 0u; csb = 0u; }
           }
           if (valid) {
-            *reinterpret_cast<uint32_t*>(&sm.cq[wv][ln][4 * hh]) = packed;
-            if (hh == 0) sm.cs[wv][ln] = (uint16_t)csb;
+            *reinterpret_cast<uint32_t*>(&sm.k.cq[wv][ln][4 * hh]) = packed;
+            if (hh == 0) sm.k.cs[wv][ln] = (uint16_t)csb;
           }
         } else if (valid) {
-          *reinterpret_cast<uint32_t*>(&sm.cq[wv][ln][4 * hh]) = 0u;
-          if (hh == 0) sm.cs[wv][ln] = 0;
+          *reinterpret_cast<uint32_t*>(&sm.k.cq[wv][ln][4 * hh]) = 0u;
+          if (hh == 0) sm.k.cs[wv][ln] = 0;
         }
       }
     }
     __syncthreads();
 
     // ---- coalesced write-out of the wave's 32 tokens ----
-    {
+    if (MODE == MODE_ASSIGN) {
+      const int64_t left = nlist - tok0;
+      const int nv = (int)(left < 32 ? (left > 0 ? left : 0) : 32);   // list entries of this wave
+      const bool live = lane < nv;
+      const int64_t o = (int64_t)h * a.T + (live ? (wlm ? (int64_t)sm.l.tok[wv][lane] : tok0 + lane) : 0);
+      const bool certified = live && sm.l.fast[wv][lane];
+      const uint32_t nw = live ? sm.idx[wv][lane] : 0u;
+      const uint32_t old = (wlm && certified) ? a.idx[o] : nw;
+      // changed assignments: one atomic per wave reserves their records
+      const uint64_t cm = __ballot(old != nw);
+      if (cm) {
+        const int leader = __ffsll((long long)cm) - 1;
+        int base = 0;
+        if (lane == leader) base = atomicAdd(a.chg_cnt, __popcll(cm));
+        base = __shfl(base, leader, 64);
+        if (old != nw) a.chg[base + __popcll(cm & ((1ull << lane) - 1ull))] = make_uint2((uint32_t)o, old | (nw << 8));
+      }
+      if (certified) {
+        a.idx[o] = (uint8_t)nw;
+        if (a.ub) {
+          a.ub[o] = sm.l.ub[wv][lane];
+          a.lb[o] = sm.l.lb[wv][lane];
+        }
+      } else if (live && !wlm) {
+        a.idx[o] = 0;   // the exact path fills it in
+      }
+    } else {
       const int64_t base = (int64_t)h * a.T + tok0;
       const int nv = (int)((a.T - tok0) < 32 ? (a.T - tok0) : 32);   // tokens of this wave
       if (nv > 0) {
         if (lane < nv) a.idx[base + lane] = sm.idx[wv][lane];
-        if (MODE != MODE_ASSIGN) {
+        {
           {
             const int t = lane >> 1, part = lane & 1;
             if (t < nv)
               *reinterpret_cast<u32x4*>(a.codes + (base + t) * 32 + 16 * part) =
-                  *reinterpret_cast<const u32x4*>(&sm.codes[wv][t][16 * part]);
+                  *reinterpret_cast<const u32x4*>(&sm.k.codes[wv][t][16 * part]);
           }
           if (lane < nv)
             *reinterpret_cast<uint32_t*>(a.scale + (base + lane) * 2) =
-                *reinterpret_cast<const uint32_t*>(&sm.scale[wv][lane][0]);
+                *reinterpret_cast<const uint32_t*>(&sm.k.scale[wv][lane][0]);
           if (2 * lane < nv) {
-            const uint8_t lo = sm.nib[wv][2 * lane];
-            const uint8_t hi = (2 * lane + 1 < nv) ? sm.nib[wv][2 * lane + 1] : 0;
+            const uint8_t lo = sm.k.nib[wv][2 * lane];
+            const uint8_t hi = (2 * lane + 1 < nv) ? sm.k.nib[wv][2 * lane + 1] : 0;
             a.zeros[(int64_t)h * a.zstride + (tok0 >> 1) + lane] = (uint8_t)(lo | (hi << 4));
           }
           if (MODE == MODE_KEYS && a.cq != nullptr) {   // null: a later pass writes the coefficients
             if (lane < nv) {
-              *reinterpret_cast<uint2*>(a.cq + (base + lane) * R) = *reinterpret_cast<const uint2*>(&sm.cq[wv][lane][0]);
-              a.cscale[base + lane] = sm.cs[wv][lane];
+              *reinterpret_cast<uint2*>(a.cq + (base + lane) * R) = *reinterpret_cast<const uint2*>(&sm.k.cq[wv][lane][0]);
+              a.cscale[base + lane] = sm.k.cs[wv][lane];
             }
           }
         }
@@ -847,8 +926,10 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
         }
       } else if (lane == 0) {
         a.idx[base] = 0;
-        if (a.excl) atomicOr(a.excl + (int64_t)h * a.excl_words + (tok >> 5), 1u << (tok & 31));
-        if (a.diag) atomicAdd((unsigned long long*)&a.diag->nonfinite_rows, 1ull);
+        // counted once per build: when its exclusion bit is first set
+        const uint32_t bit = 1u << (tok & 31);
+        const uint32_t was = a.excl ? atomicOr(a.excl + (int64_t)h * a.excl_words + (tok >> 5), bit) : 0u;
+        if (a.diag && !(was & bit)) atomicAdd((unsigned long long*)&a.diag->nonfinite_rows, 1ull);
       }
       continue;
     }
@@ -924,6 +1005,7 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     int win = 0;
+    double dwin = 0.0;   // the winner's exact squared distance (nearest-centroid choice)
     if (!use_qsac) {
       double bv = dq[wv][lane];
       int bj = lane;
@@ -937,6 +1019,7 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
         if (ov < bv || (ov == bv && oj < bj)) { bv = ov; bj = oj; }
       }
       win = bj;
+      dwin = bv;
     } else {
       const double Wa = a.Wg[2 * h], Wb = a.Wg[2 * h + 1];
       double bestS = __builtin_inf();
@@ -1002,7 +1085,30 @@ __global__ __launch_bounds__(256) void fallback_kernel(SelectArgs a) {
       win = bestj;
     }
     if (MODE == MODE_ASSIGN) {
-      if (lane == 0) a.idx[base] = (uint8_t)win;
+      if (a.ub != nullptr) {
+        // bounds for the later iterations: the winner's distance and the
+        // second smallest (exact fp64 distances), rounded outward
+        if (lane == (win & 63)) dq[wv][win] = __builtin_inf();
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        double b2 = dq[wv][lane];
+        for (int q = 1; q < 4; ++q) b2 = fmin(b2, dq[wv][lane + 64 * q]);
+        for (int o = 32; o > 0; o >>= 1) b2 = fmin(b2, __shfl_xor(b2, o, 64));
+        if (lane == 0) {
+          a.ub[base] = (float)sqrt(dwin) * (1.0f + 1.0f / 1048576.0f);
+          a.lb[base] = (float)sqrt(b2) * (1.0f - 1.0f / 1048576.0f);
+        }
+      }
+      if (lane == 0) {
+        if (a.wl != nullptr) {
+          const uint32_t old = a.idx[base];
+          if (old != (uint32_t)win) {
+            const int slot = atomicAdd(a.chg_cnt, 1);
+            a.chg[slot] = make_uint2((uint32_t)base, old | ((uint32_t)win << 8));
+          }
+        }
+        a.idx[base] = (uint8_t)win;
+      }
       continue;
     }
     // codec for the winner
@@ -1212,6 +1318,7 @@ __device__ __forceinline__ bool row_finite(const void* x, int32_t dtype, int64_t
   uint32_t bad = 0u;
   if (dtype == QWM_BF16) {
     const uint4* r = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
+#pragma unroll
     for (int c = 0; c < D / 8; ++c) {
       const uint4 v = r[c];
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
@@ -1222,6 +1329,7 @@ __device__ __forceinline__ bool row_finite(const void* x, int32_t dtype, int64_t
     }
   } else {
     const float4* r = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+#pragma unroll
     for (int c = 0; c < D / 4; ++c) {
       const float4 v = r[c];
       bad |= !(__builtin_isfinite(v.x) && __builtin_isfinite(v.y) && __builtin_isfinite(v.z) && __builtin_isfinite(v.w));
@@ -1230,41 +1338,64 @@ __device__ __forceinline__ bool row_finite(const void* x, int32_t dtype, int64_t
   return bad == 0u;
 }
 
-// perm [H][T] int32 workspace.  Grid H, 256 threads.  The first 256 picks of
-// the shuffle are checked in parallel; only when one of them lands on a row
-// with a non-finite channel does thread 0 drop those picks and go on with the
-// shuffle (checking each further pick), leaving zero rows for slots that no
-// finite token fills.
+// Grid H, 256 threads.  The 256 picks of the partial Fisher-Yates shuffle
+// (pick i swaps slot i with slot j_i = i + r_i mod (T - i), r_i the i-th
+// SplitMix64 output) are found in parallel: thread i draws r_i directly (the
+// generator's state after i + 1 steps is seed + (i + 1) * gamma), and the token
+// in slot p just before swap i is p itself unless some earlier swap k < i had
+// j_k = p, in which case it is the token slot k held just before swap k (the
+// last such k; resolved by walking back).  Only when a pick lands on a row with
+// a non-finite channel does thread 0 replay the shuffle sequentially in perm
+// ([H][T] int32 workspace) and go on past slot 255 (checking each further
+// pick), leaving zero rows for slots that no finite token fills.
+__device__ __forceinline__ uint64_t splitmix_at(uint64_t seed, uint64_t k) {
+  uint64_t state = seed + k * 0x9E3779B97F4A7C15ull;   // state after k steps
+  state -= 0x9E3779B97F4A7C15ull;                      // splitmix_next adds it back
+  return splitmix_next(state);
+}
+
 __global__ __launch_bounds__(256) void forgy_kernel(const void* x, int32_t dtype, int64_t T, int64_t st, int64_t sh,
                                                     uint64_t seed, int32_t* perm, uint16_t* out) {
   const int h = blockIdx.x, tid = threadIdx.x;
-  int32_t* p = perm + (int64_t)h * T;
-  for (int64_t i = tid; i < T; i += 256) p[i] = (int32_t)i;
-  __syncthreads();
   __shared__ int32_t pick[NC];
+  __shared__ int64_t js[NC];
   __shared__ uint8_t ok[NC];
-  uint64_t state = seed + ((uint64_t)h << 32);   // thread 0's generator
-  if (tid == 0) {
-    for (int i = 0; i < NC; ++i) {
-      const uint64_t r = splitmix_next(state);
-      const int64_t j = i + (int64_t)(r % (uint64_t)(T - i));
-      const int32_t t = p[i]; p[i] = p[j]; p[j] = t;
-      pick[i] = p[i];
+  const uint64_t s0 = seed + ((uint64_t)h << 32);
+  {
+    const uint64_t r = splitmix_at(s0, (uint64_t)tid + 1);
+    js[tid] = tid + (int64_t)(r % (uint64_t)(T - tid));
+  }
+  __syncthreads();
+  {
+    int64_t p = js[tid];
+    int lim = tid;
+    for (;;) {
+      int k = -1;
+      for (int q = lim - 1; q >= 0; --q)
+        if (js[q] == p) { k = q; break; }
+      if (k < 0) break;
+      p = k;
+      lim = k;
     }
+    pick[tid] = (int32_t)p;
   }
   __syncthreads();
   ok[tid] = row_finite(x, dtype, st, sh, h, pick[tid]) ? 1 : 0;
-  if (__syncthreads_count(ok[tid] == 0) > 0 && tid == 0) {
-    int slot = 0;
-    for (int i = 0; i < NC; ++i)
-      if (ok[i]) pick[slot++] = pick[i];
-    for (int64_t i = NC; slot < NC && i < T; ++i) {
-      const uint64_t r = splitmix_next(state);
-      const int64_t j = i + (int64_t)(r % (uint64_t)(T - i));
-      const int32_t t = p[i]; p[i] = p[j]; p[j] = t;
-      if (row_finite(x, dtype, st, sh, h, p[i])) pick[slot++] = p[i];
+  if (__syncthreads_count(ok[tid] == 0) > 0) {
+    int32_t* p = perm + (int64_t)h * T;
+    for (int64_t i = tid; i < T; i += 256) p[i] = (int32_t)i;
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t state = s0;
+      int slot = 0;
+      for (int64_t i = 0; slot < NC && i < T; ++i) {
+        const uint64_t r = splitmix_next(state);
+        const int64_t j = i + (int64_t)(r % (uint64_t)(T - i));
+        const int32_t t = p[i]; p[i] = p[j]; p[j] = t;
+        if (i < NC ? ok[i] != 0 : row_finite(x, dtype, st, sh, h, p[i])) pick[slot++] = p[i];
+      }
+      for (; slot < NC; ++slot) pick[slot] = -1;
     }
-    for (; slot < NC; ++slot) pick[slot] = -1;
   }
   __syncthreads();
   for (int e = tid; e < NC * D; e += 256) {
@@ -1291,13 +1422,16 @@ __global__ __launch_bounds__(256) void forgy_kernel(const void* x, int32_t dtype
 //
 // lloyd_sum_kernel (one wave per (head, cluster), 64 lanes x 2 channels): the
 // member rows summed in token order in fp64, 32 rows in flight; the new
-// centroid is bf16(sum / n); an empty cluster keeps its centroid.
+// centroid is bf16(sum / n); an empty cluster keeps its centroid.  Heads that
+// hold their sums in fixed point (not flagged, isums given) store the exact
+// integer sums and counts instead, for the mean update of lloyd.hip.
 constexpr int LS_WAVES = 16;
 
-__global__ __launch_bounds__(1024) void lloyd_sort_kernel(const uint8_t* assign, const uint32_t* excl,
+__global__ __launch_bounds__(1024) void lloyd_sort_kernel(const int32_t* hflag, const uint8_t* assign, const uint32_t* excl,
                                                           int64_t excl_words, int64_t T, int32_t* ids,
                                                           int32_t* start) {
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (hflag != nullptr && hflag[h] == 0) return;   // the integer path handles this head
   __shared__ int32_t cnt[LS_WAVES][NC];     // counts, then running offsets
   __shared__ int32_t tot[NC];
   for (int e = tid; e < LS_WAVES * NC; e += 1024) (&cnt[0][0])[e] = 0;
@@ -1365,17 +1499,71 @@ __global__ __launch_bounds__(1024) void lloyd_sort_kernel(const uint8_t* assign,
 
 __global__ __launch_bounds__(256) void lloyd_sum_kernel(const void* x, int32_t dtype, int64_t T, int64_t st,
                                                         int64_t sh, int32_t H, const int32_t* ids,
-                                                        const int32_t* start, const uint16_t* cin, uint16_t* cout) {
+                                                        const int32_t* start, const uint16_t* cin, uint16_t* cout,
+                                                        const int32_t* hflag, const int32_t* emax,
+                                                        int64_t* isums, int32_t* icnt, int32_t P) {
   const int lane = threadIdx.x & 63;
   // wave-uniform unit: the member ids then come in through scalar loads
   const int unit = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
   if (unit >= H * NC) return;
   const int h = unit / NC, j = unit % NC;
+  const bool fixed = hflag != nullptr && hflag[h] == 0;
+  if (fixed && isums == nullptr) return;   // lloyd.hip keeps this head's sums by changes
   const int32_t b = start[h * (NC + 1) + j], n = start[h * (NC + 1) + j + 1] - b;
   const int32_t* mem = ids + (int64_t)h * T + b;
   const int64_t rowbase = (int64_t)h * sh + 2 * lane;
-  double s0 = 0.0, s1 = 0.0;
   constexpr int U = 32;
+  if (fixed) {
+    // exact integer sums in units 2^(emax_c - P), any order
+    const int32_t e0 = emax[h * D + 2 * lane], e1 = emax[h * D + 2 * lane + 1];
+    const int sc0 = e0 == INT_MIN ? 0 : P - e0, sc1 = e1 == INT_MIN ? 0 : P - e1;
+    int64_t s0 = 0, s1 = 0;
+    int e = 0;
+    if (dtype == QWM_BF16) {
+      const uint16_t* xb = static_cast<const uint16_t*>(x) + rowbase;
+      int32_t id[U];
+      if (n >= U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) id[u] = mem[u];
+      }
+      for (; e + U <= n; e += U) {
+        uint32_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const uint32_t*>(xb + (int64_t)id[u] * st);
+        // the next batch's ids while these rows are in flight
+        if (e + 2 * U <= n) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) id[u] = mem[e + U + u];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) { s0 += to_fixed<8>(v[u] & 0xFFFFu, sc0); s1 += to_fixed<8>(v[u] >> 16, sc1); }
+      }
+      for (; e < n; ++e) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(xb + (int64_t)mem[e] * st);
+        s0 += to_fixed<8>(v & 0xFFFFu, sc0);
+        s1 += to_fixed<8>(v >> 16, sc1);
+      }
+    } else {
+      const float* xf = static_cast<const float*>(x) + rowbase;
+      for (; e + U <= n; e += U) {
+        uint2 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const uint2*>(xf + (int64_t)mem[e + u] * st);
+#pragma unroll
+        for (int u = 0; u < U; ++u) { s0 += to_fixed<24>(v[u].x, sc0); s1 += to_fixed<24>(v[u].y, sc1); }
+      }
+      for (; e < n; ++e) {
+        const uint2 v = *reinterpret_cast<const uint2*>(xf + (int64_t)mem[e] * st);
+        s0 += to_fixed<24>(v.x, sc0);
+        s1 += to_fixed<24>(v.y, sc1);
+      }
+    }
+    isums[(int64_t)unit * D + 2 * lane] = s0;
+    isums[(int64_t)unit * D + 2 * lane + 1] = s1;
+    if (lane == 0) icnt[unit] = n;
+    return;
+  }
+  double s0 = 0.0, s1 = 0.0;
   int e = 0;
   if (dtype == QWM_BF16) {
     const uint16_t* xb = static_cast<const uint16_t*>(x) + rowbase;
@@ -1441,6 +1629,7 @@ using namespace qwm;
 struct SelWork {
   uint16_t* aug; float* Bj; float* Bmax; double* Wg; int32_t* counter; int32_t* worklist; double* qB;
   uint8_t* assign; int32_t* perm; int32_t* start; uint32_t* excl;
+  LloydState ll;
 };
 
 static constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1465,7 +1654,9 @@ constexpr size_t select_ws_bytes_c(int64_t T, int32_t H, bool lloyd) {
   return b;
 }
 
-size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd) { return select_ws_bytes_c(T, H, lloyd); }
+size_t select_ws_bytes(int64_t T, int32_t H, bool lloyd) {
+  return select_ws_bytes_c(T, H, lloyd) + (lloyd ? lloyd_state_bytes(T, H) : 0);
+}
 
 // ---------------------------------------------------------------------------
 // Scratch of qwm_quantize_keys_noalloc, for callers that cannot allocate: the
@@ -1502,7 +1693,7 @@ qwm_status noalloc_keys_scratch(void** ptr) {
   return QWM_OK;
 }
 
-static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd) {
+static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd, int32_t dtype = QWM_BF16) {
   char* p = static_cast<char*>(ws);
   SelWork w{};
   auto take = [&](size_t n) { char* r = p; p += align256(n); return r; };
@@ -1518,6 +1709,7 @@ static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd) {
     w.perm = reinterpret_cast<int32_t*>(take((size_t)H * T * 4));
     w.start = reinterpret_cast<int32_t*>(take((size_t)H * (NC + 1) * 4));
     w.excl = reinterpret_cast<uint32_t*>(take((size_t)H * excl_words(T) * 4));
+    w.ll = lloyd_state_carve(p, T, H, dtype);
   }
   return w;
 }
@@ -1580,8 +1772,10 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
   // one wave per flagged token; the count is known only on the device, so the
   // grid covers the worst case (up to 4,096 tokens in one round, three blocks
   // per CU) and idle blocks exit at once
+  // (a bounded Lloyd iteration sends few tokens: a quarter of the grid)
   const int64_t worst = ((int64_t)x->H * x->T + 3) / 4;
-  const int fb = (int)(worst < 1024 ? worst : 1024);
+  const int64_t cap = a.wl != nullptr ? 256 : 1024;
+  const int fb = (int)(worst < cap ? worst : cap);
   if (x->dtype == QWM_BF16)
     hipLaunchKernelGGL((fallback_kernel<MODE, false>), dim3(fb), dim3(256), 0, stream, a);
   else
@@ -1595,8 +1789,9 @@ static void fill_common(SelectArgs& a, const qwm_tokens* x, const SelWork& w, co
   a.mu = mu; a.counter = w.counter; a.worklist = w.worklist;
 }
 
-static qwm_status prep(const SelWork& w, const uint16_t* mu, const float* wts, int32_t H, hipStream_t stream) {
-  TablePrepArgs p{mu, wts, w.aug, w.Bj, w.Bmax, w.Wg, w.counter};
+static qwm_status prep(const SelWork& w, const uint16_t* mu, const float* wts, int32_t H, hipStream_t stream,
+                       int32_t* zero = nullptr, int32_t nzero = 0) {
+  TablePrepArgs p{mu, wts, w.aug, w.Bj, w.Bmax, w.Wg, w.counter, zero, nzero};
   hipLaunchKernelGGL(prep_table_kernel, dim3(H, PREP_PARTS), dim3(256), 0, stream, p);
   return check_launch("centroid table preparation");
 }
@@ -1702,7 +1897,8 @@ qwm_status launch_values(const qwm_tokens* v, const uint16_t* centroids, const q
 
 qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const uint16_t* init, uint16_t* centroids,
                         qwm_diag* diag, void* ws, hipStream_t stream) {
-  SelWork wk = carve(ws, x->T, x->H, true);
+  SelWork wk = carve(ws, x->T, x->H, true, x->dtype);
+  const LloydState& ll = wk.ll;
   const uint16_t* cur = init;
   if (init == nullptr) {
     hipLaunchKernelGGL(forgy_kernel, dim3(x->H), dim3(256), 0, stream, x->ptr, x->dtype, x->T, x->stride_t,
@@ -1723,25 +1919,50 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
                        reinterpret_cast<uint8_t*>(wk.excl), eb);
     qwm_status s = check_launch("Lloyd exclusion clear");
     if (s != QWM_OK) return s;
+    // the fixed-point units of the member sums; heads with values finer than
+    // their unit are flagged and take the fp64 member sums every iteration
+    s = lloyd_scan(x, ll, stream);
+    if (s != QWM_OK) return s;
   }
   for (int it = 0; it < iters; ++it) {
-    qwm_status s = prep(wk, cur, nullptr, x->H, stream);
+    // every iteration: the table terms of the GEMM, cleared list counters
+    qwm_status s = prep(wk, cur, nullptr, x->H, stream, ll.wl_cnt, x->H + 1);
     if (s != QWM_OK) return s;
     SelectArgs a{};
     fill_common(a, x, wk, cur);
     a.M = 1; a.flags = 0; a.cb = error_coeff(x->dtype != QWM_BF16);
     a.idx = wk.assign; a.diag = diag; a.excl = wk.excl; a.excl_words = excl_words(x->T);
+    a.ub = ll.ub; a.lb = ll.lb;
+    // The first two iterations assign every token (the means still move far)
+    // and sum the members from scratch; later ones assign again only the
+    // tokens whose bounds no longer settle their centroid (every token of a
+    // flagged head) and apply the recorded changes to the integer sums.
+    const bool bounded = it >= 2;
+    if (bounded) {
+      s = lloyd_bounds(x, wk.assign, wk.excl, excl_words(x->T), ll, stream);
+      if (s != QWM_OK) return s;
+      a.wl = ll.wl; a.wl_cnt = ll.wl_cnt; a.chg = ll.chg; a.chg_cnt = ll.chg_cnt;
+    }
     s = run_select<MODE_ASSIGN>(x, a, stream, "Lloyd assignment");
     if (s != QWM_OK) return s;
-    // the Forgy permutation is dead by now: its buffer holds the sorted members
-    hipLaunchKernelGGL(lloyd_sort_kernel, dim3(x->H), dim3(1024), 0, stream, wk.assign, wk.excl, excl_words(x->T),
-                       x->T, wk.perm, wk.start);
+    // members sorted by centroid (the Forgy permutation is dead by now: its
+    // buffer holds them), summed in fp64 for flagged heads, in fixed point for
+    // the others while they are summed from scratch
+    hipLaunchKernelGGL(lloyd_sort_kernel, dim3(x->H), dim3(1024), 0, stream, bounded ? ll.hflag : nullptr, wk.assign,
+                       wk.excl, excl_words(x->T), x->T, wk.perm, wk.start);
     s = check_launch("Lloyd member sort");
     if (s != QWM_OK) return s;
     const int64_t units = (int64_t)x->H * NC;
     hipLaunchKernelGGL(lloyd_sum_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, x->ptr, x->dtype,
-                       x->T, x->stride_t, x->stride_h, x->H, wk.perm, wk.start, cur, centroids);
+                       x->T, x->stride_t, x->stride_h, x->H, wk.perm, wk.start, cur, centroids, ll.hflag, ll.emax,
+                       bounded ? nullptr : ll.sums, ll.cnt, ll.P);
     s = check_launch("Lloyd update");
+    if (s != QWM_OK) return s;
+    if (bounded) {
+      s = lloyd_apply_changes(x, ll, stream);
+      if (s != QWM_OK) return s;
+    }
+    s = lloyd_finalize(x, ll, cur, centroids, stream);
     if (s != QWM_OK) return s;
     cur = centroids;
   }

@@ -182,7 +182,14 @@ qwm_status qwm_update_query_stats(const qwm_tokens* q, const qwm_qstats* st, int
  * tokens drawn by a SplitMix64-driven partial Fisher-Yates shuffle seeded with
  * seed + (head << 32); otherwise warm start from init ([H][256][d] bf16, may
  * equal centroids).  Assignment: nearest centroid (ties -> lowest index),
- * exact; update: bf16(mean) computed in fp64; empty clusters keep their value.
+ * exact; update: bf16(mean of the members); empty clusters keep their value.
+ * The mean is bf16(fl64(sum) / n) with the member sum exact: in 64-bit fixed
+ * point per (head, channel), or, for a head holding a value finer than that
+ * fixed-point unit, in fp64 in token order.  After the first iteration a token
+ * is re-assigned only when distance bounds (upper to its centroid, lower to
+ * the others, moved by how far the means moved) no longer settle its centroid.
+ * Rows with a NaN or Inf channel take no part; diag->nonfinite_rows counts
+ * them once per call.
  * Output centroids [H][256][d] bf16.  Requires T >= 256 when init == NULL.
  * Workspace: qwm_workspace_bytes(QWM_OP_CENTROIDS, T, H, ...). */
 qwm_status qwm_build_centroids(const qwm_tokens* x, int32_t n_centroids, int32_t iters, uint64_t seed,
