@@ -15,7 +15,7 @@
 //
 //  * Integer member sums.  Channel c of a head is summed in fixed point, in
 //    units of 2^(emax_c - P) (emax_c: the largest binary exponent of the
-//    channel's values, P = 62 - bit length of T).  Every value of the channel
+//    channel's values, P = min(62 - bit length of T, 48)).  Every value of the channel
 //    is then a whole number of units, unless it is finer than the unit (the
 //    head is then flagged and takes the fp64 member-sum path of quantize.hip),
 //    and no sum of T values leaves 64 bits.  Integer sums do not depend on the
@@ -326,7 +326,7 @@ LloydState lloyd_state_carve(char*& p, int64_t T, int32_t H, int32_t dtype) {
   s.chg = reinterpret_cast<uint2*>(take(8 * h * t));
   int bl = 0;
   for (int64_t v = T; v > 0; v >>= 1) ++bl;
-  s.P = 62 - bl;
+  s.P = 62 - bl < 48 ? 62 - bl : 48;
   s.MB = dtype == QWM_BF16 ? 8 : 24;
   return s;
 }

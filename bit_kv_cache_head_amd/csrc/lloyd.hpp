@@ -52,7 +52,8 @@ struct LloydState {
   // changed assignments of an iteration: (h T + t, old | new << 8)
   uint2* chg;       // [H T]
   int32_t* chg_cnt; // [1]
-  int32_t P;        // fixed-point unit 2^(emax - P) with P = 62 - bit length of T
+  int32_t P;        // fixed-point unit 2^(emax - P), P = min(62 - bit length of T, 48): no sum of
+                    // T values leaves 63 bits, and a sum of 32 is exact in fp64
   int32_t MB;       // significant bits of a token value (8 bf16, 24 fp32)
 };
 

@@ -1514,10 +1514,17 @@ __global__ __launch_bounds__(256) void lloyd_sum_kernel(const void* x, int32_t d
   const int64_t rowbase = (int64_t)h * sh + 2 * lane;
   constexpr int U = 32;
   if (fixed) {
-    // exact integer sums in units 2^(emax_c - P), any order
+    // exact integer sums in units 2^(emax_c - P).  Every value of an unflagged
+    // head is a whole number of units below 2^P (P <= 48), so the fp64 sum of
+    // a batch of at most 32 rows is exact (below 2^53 units); each batch sum
+    // is then scaled to units and added as an integer.
     const int32_t e0 = emax[h * D + 2 * lane], e1 = emax[h * D + 2 * lane + 1];
     const int sc0 = e0 == INT_MIN ? 0 : P - e0, sc1 = e1 == INT_MIN ? 0 : P - e1;
     int64_t s0 = 0, s1 = 0;
+    auto flush = [&](double d0, double d1) __attribute__((always_inline)) {
+      s0 += (int64_t)ldexp(d0, sc0);
+      s1 += (int64_t)ldexp(d1, sc1);
+    };
     int e = 0;
     if (dtype == QWM_BF16) {
       const uint16_t* xb = static_cast<const uint16_t*>(x) + rowbase;
@@ -1535,28 +1542,39 @@ __global__ __launch_bounds__(256) void lloyd_sum_kernel(const void* x, int32_t d
 #pragma unroll
           for (int u = 0; u < U; ++u) id[u] = mem[e + U + u];
         }
+        double d0 = 0.0, d1 = 0.0;
 #pragma unroll
-        for (int u = 0; u < U; ++u) { s0 += to_fixed<8>(v[u] & 0xFFFFu, sc0); s1 += to_fixed<8>(v[u] >> 16, sc1); }
+        for (int u = 0; u < U; ++u) {
+          d0 += (double)__uint_as_float(v[u] << 16);
+          d1 += (double)__uint_as_float(v[u] & 0xFFFF0000u);
+        }
+        flush(d0, d1);
       }
+      double d0 = 0.0, d1 = 0.0;
       for (; e < n; ++e) {
         const uint32_t v = *reinterpret_cast<const uint32_t*>(xb + (int64_t)mem[e] * st);
-        s0 += to_fixed<8>(v & 0xFFFFu, sc0);
-        s1 += to_fixed<8>(v >> 16, sc1);
+        d0 += (double)__uint_as_float(v << 16);
+        d1 += (double)__uint_as_float(v & 0xFFFF0000u);
       }
+      flush(d0, d1);
     } else {
       const float* xf = static_cast<const float*>(x) + rowbase;
       for (; e + U <= n; e += U) {
-        uint2 v[U];
+        float2 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const uint2*>(xf + (int64_t)mem[e + u] * st);
+        for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const float2*>(xf + (int64_t)mem[e + u] * st);
+        double d0 = 0.0, d1 = 0.0;
 #pragma unroll
-        for (int u = 0; u < U; ++u) { s0 += to_fixed<24>(v[u].x, sc0); s1 += to_fixed<24>(v[u].y, sc1); }
+        for (int u = 0; u < U; ++u) { d0 += (double)v[u].x; d1 += (double)v[u].y; }
+        flush(d0, d1);
       }
+      double d0 = 0.0, d1 = 0.0;
       for (; e < n; ++e) {
-        const uint2 v = *reinterpret_cast<const uint2*>(xf + (int64_t)mem[e] * st);
-        s0 += to_fixed<24>(v.x, sc0);
-        s1 += to_fixed<24>(v.y, sc1);
+        const float2 v = *reinterpret_cast<const float2*>(xf + (int64_t)mem[e] * st);
+        d0 += (double)v.x;
+        d1 += (double)v.y;
       }
+      flush(d0, d1);
     }
     isums[(int64_t)unit * D + 2 * lane] = s0;
     isums[(int64_t)unit * D + 2 * lane + 1] = s1;
