@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
 }
 
 struct SelectArgs {
-  const void* x; int64_t T; int64_t st; int64_t sh;
+  const void* x; int64_t T; int64_t st; int64_t sh; int32_t H;
   const uint16_t* aug; const float* Bj; const float* Bmax;
   const double* Wg;
   const uint16_t* mu;   // [H][256][128]
@@ -301,24 +301,18 @@ constexpr float DREL = 1.0f / 65536.0f;   // relative error bound of the fp32 re
 // block in LDS (where the rescoring and the encoder read it too); the B operand
 // is the token side t = -2 w (.) k, exact in bf16 for unweighted bf16 tokens and
 // otherwise carried as a bf16 pair t_hi + t_lo (two MFMAs per k-step).
-template <int MODE, bool F32, bool QS, bool WT, int KQ = 8>
-__global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArgs a) {
+// select_range: tiles [t_begin, t_end) of head h (tokens, or entries of the
+// head's list for Lloyd's bounded iterations; nlist of them), with the head's
+// tables staged first.  Every tile ends with a block barrier, so a block may
+// call it again for another head.
+template <int MODE, bool F32, bool QS, bool WT, int KQ>
+__device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, const int h, const int64_t nlist,
+                                             const int64_t t_begin, const int64_t t_end) {
   constexpr int KT = QS ? KQ : 3;   // values tracked per lane (each lane holds half the centroids)
   constexpr bool SPLIT = F32 || WT;
-  __shared__ SelShared sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hh = lane >> 5, ln = lane & 31;
-  const int h = blockIdx.y;
   const bool use_psac = (MODE == MODE_KEYS) && (a.flags & QWM_PSAC) && a.U != nullptr;
-  // Lloyd after the first iteration: only the tokens of head h's list
   const bool wlm = (MODE == MODE_ASSIGN) && a.wl != nullptr;
-  const int64_t nlist = wlm ? (int64_t)a.wl_cnt[h] : a.T;   // tokens (list entries) of head h
-
-  // This block's tiles of head h: a contiguous share [t_begin, t_end), equal
-  // to within one tile across the head's gridDim.x blocks.
-  const int64_t ntile = (nlist + SEL_TOK - 1) / SEL_TOK;
-  const int64_t t_begin = (int64_t)blockIdx.x * ntile / gridDim.x;
-  const int64_t t_end = (int64_t)(blockIdx.x + 1) * ntile / gridDim.x;
-  if (t_begin >= t_end) return;   // block-uniform
 
   // ---- stage the centroid rows, B_j, weights and U^T ----
   {
@@ -859,6 +853,39 @@ __global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArg
       }
     }
     __syncthreads();
+  }
+}
+
+// Block (x, h) takes a contiguous share of head h's tiles (tokens, or list
+// entries in Lloyd's bounded iterations), equal to within one tile across the
+// head's gridDim.x blocks.  FLAT (Lloyd's bounded iterations): the grid is
+// one-dimensional; all heads' lists, taken one after the other, form NT tiles,
+// and block b takes tiles [b NT / G, (b + 1) NT / G) of them (G blocks), head by
+// head, so that a short or uneven list still spreads over the whole grid.
+template <int MODE, bool F32, bool QS, bool WT, int KQ = 8, bool FLAT = false>
+__global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArgs a) {
+  __shared__ SelShared sm;
+  if constexpr (FLAT) {
+    int64_t nt = 0;
+    for (int g = 0; g < a.H; ++g) nt += ((int64_t)a.wl_cnt[g] + SEL_TOK - 1) / SEL_TOK;
+    const int64_t r0 = (int64_t)blockIdx.x * nt / gridDim.x;
+    const int64_t r1 = (int64_t)(blockIdx.x + 1) * nt / gridDim.x;
+    int64_t lo = 0;   // first tile of head g
+    for (int g = 0; g < a.H && lo < r1; ++g) {
+      const int64_t n = a.wl_cnt[g];
+      const int64_t hi = lo + (n + SEL_TOK - 1) / SEL_TOK;
+      if (hi > r0 && hi > lo)
+        select_range<MODE, F32, QS, WT, KQ>(a, sm, g, n, (lo > r0 ? lo : r0) - lo, (hi < r1 ? hi : r1) - lo);
+      lo = hi;
+    }
+  } else {
+    const int h = blockIdx.y;
+    const int64_t nlist = (MODE == MODE_ASSIGN && a.wl != nullptr) ? (int64_t)a.wl_cnt[h] : a.T;
+    const int64_t ntile = (nlist + SEL_TOK - 1) / SEL_TOK;
+    const int64_t t_begin = (int64_t)blockIdx.x * ntile / gridDim.x;
+    const int64_t t_end = (int64_t)(blockIdx.x + 1) * ntile / gridDim.x;
+    if (t_begin >= t_end) return;   // block-uniform
+    select_range<MODE, F32, QS, WT, KQ>(a, sm, h, nlist, t_begin, t_end);
   }
 }
 
@@ -1781,6 +1808,18 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
       else if (wt) hipLaunchKernelGGL((select_kernel<MODE, false, false, true>), grid, block, 0, stream, a);
       else hipLaunchKernelGGL((select_kernel<MODE, false, false, false>), grid, block, 0, stream, a);
     }
+  } else if constexpr (MODE == MODE_ASSIGN) {
+    if (a.wl != nullptr) {
+      // one resident wave of blocks over all heads' listed tiles
+      const int64_t tiles = (int64_t)x->H * ((x->T + SEL_TOK - 1) / SEL_TOK);
+      const int64_t g = 2 * (int64_t)device_cus();
+      const dim3 fgrid((unsigned)(tiles < g ? tiles : g));
+      if (f32) hipLaunchKernelGGL((select_kernel<MODE, true, false, false, 8, true>), fgrid, block, 0, stream, a);
+      else hipLaunchKernelGGL((select_kernel<MODE, false, false, false, 8, true>), fgrid, block, 0, stream, a);
+    } else {
+      if (f32) hipLaunchKernelGGL((select_kernel<MODE, true, false, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((select_kernel<MODE, false, false, false>), grid, block, 0, stream, a);
+    }
   } else {
     if (f32) hipLaunchKernelGGL((select_kernel<MODE, true, false, false>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((select_kernel<MODE, false, false, false>), grid, block, 0, stream, a);
@@ -1802,7 +1841,7 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
 }
 
 static void fill_common(SelectArgs& a, const qwm_tokens* x, const SelWork& w, const uint16_t* mu) {
-  a.x = x->ptr; a.T = x->T; a.st = x->stride_t; a.sh = x->stride_h;
+  a.x = x->ptr; a.T = x->T; a.st = x->stride_t; a.sh = x->stride_h; a.H = x->H;
   a.aug = w.aug; a.Bj = w.Bj; a.Bmax = w.Bmax; a.Wg = w.Wg;
   a.mu = mu; a.counter = w.counter; a.worklist = w.worklist;
 }
