@@ -70,11 +70,16 @@ struct AttnArgs {
 constexpr int KSTR = 2 * D + 16;      // bytes per K0_hat row
 constexpr int VSTR = 2 * AT_K + 16;   // bytes per V_hat^T row
 // NPK: PSAC k-steps of 16 coefficients (1: ranks 8 and 16; 2: rank 32)
+// PSAC coefficients sit in 2 NPK planes of 8 per key (16 bytes), planes
+// padded by 128 bytes: the 16 lanes of an operand read cover 256 contiguous
+// bytes, and the coefficient stores of a wave (8 keys x 8 threads) fall in 64
+// different banks.
+constexpr int CPL = AT_K * 16 + 128;   // bytes per coefficient plane
 template <int NPK>
 struct AttnBuf {
   uint8_t khat[AT_K * KSTR];       // [key][128 permuted channels] fp16
   uint8_t vt[D * VSTR];            // [channel][64 keys in vslot order] fp16
-  uint8_t chat[AT_K * 32 * NPK];   // [key][16 NPK] fp16: c_scale * c (zeros past the rank)
+  uint8_t chat[2 * NPK * CPL];     // [plane q][key][8] fp16: c_scale * c for coefficients 8 q .. 8 q + 7 (zeros past the rank)
 };
 constexpr int UT_ROWS = QWM_MAX_RANK;   // basis rows per (segment, head) in the fragment buffer
 
@@ -338,12 +343,17 @@ __device__ __forceinline__ Lane lane_share(int tid) {
   Lane L;
   L.key = tid >> 3;
   L.blk = tid & 7;
-  L.p = tid >> 4;
+  // key pair p (keys 2p, 2p + 1) of the V_hat tile: a wave's four pairs fill
+  // all four 32-bit words of their 16-byte chunks of a V_hat^T row, so that
+  // the wave's 64 stores per channel hit 64 different banks
+  const int w = tid >> 6, j = (tid >> 4) & 3;
+  L.p = 8 * (w >> 1) + 2 * (w & 1) + (j & 1) + 4 * (j >> 1);
   L.oct = tid & 15;
   L.zsh_k = 4u * (uint32_t)(L.key & 1) + 2u * (uint32_t)(L.blk >> 2);
   L.zsh_v = 2u * (uint32_t)(L.oct >> 3);
   // thread blk owns coefficients 2 NPK blk .. +2 NPK of its key
-  L.c_off = (int)offsetof(AttnBuf<NPK>, chat) + L.key * 32 * NPK + 4 * NPK * L.blk;
+  const int c0 = 2 * NPK * L.blk;
+  L.c_off = (int)offsetof(AttnBuf<NPK>, chat) + (c0 >> 3) * CPL + L.key * 16 + 2 * (c0 & 7);
   return L;
 }
 
@@ -699,8 +709,8 @@ __device__ __forceinline__ void tile_phase1(const AttnBuf<NPK>* __restrict__ B, 
       // without PSAC
 #pragma unroll
       for (int k = 0; k < NPK; ++k) {
-        ca[k] = *reinterpret_cast<const f16x8*>(B->chat + ln * 32 * NPK + 32 * k + 16 * hh);
-        cb[k] = *reinterpret_cast<const f16x8*>(B->chat + (32 + ln) * 32 * NPK + 32 * k + 16 * hh);
+        ca[k] = *reinterpret_cast<const f16x8*>(B->chat + (2 * k + hh) * CPL + ln * 16);
+        cb[k] = *reinterpret_cast<const f16x8*>(B->chat + (2 * k + hh) * CPL + (32 + ln) * 16);
       }
     }
     sa = mfma_f16(fa[s], qf[s], sa);
