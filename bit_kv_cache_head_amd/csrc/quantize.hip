@@ -295,7 +295,9 @@ constexpr float DREL = 1.0f / 65536.0f;   // relative error bound of the fp32 re
 // QS: QSAC selection (keys with the QSAC flag and M > 1); otherwise nearest.
 // WT: Query-weighted distances.
 // KQ: GEMM values tracked per lane in QSAC selection (8 for M <= 8, 16 for
-//     M <= 16: each lane holds half the centroids, so 2 KQ >= M candidates).
+//     M <= 16: each lane holds half the centroids, so 2 KQ >= M candidates);
+//     256 for M >= 256, where every centroid is a candidate and S is scored
+//     for all of them.
 //
 // The GEMM's A operand is the exact bf16 centroid row mu_j, staged once per
 // block in LDS (where the rescoring and the encoder read it too); the B operand
@@ -308,7 +310,9 @@ constexpr float DREL = 1.0f / 65536.0f;   // relative error bound of the fp32 re
 template <int MODE, bool F32, bool QS, bool WT, int KQ>
 __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, const int h, const int64_t nlist,
                                              const int64_t t_begin, const int64_t t_end) {
-  constexpr int KT = QS ? KQ : 3;   // values tracked per lane (each lane holds half the centroids)
+  // KQ = 256: QSAC with M >= 256 (every centroid a candidate), scored exhaustively
+  constexpr bool EXH = QS && KQ == NC;
+  constexpr int KT = (QS && !EXH) ? KQ : 3;   // values tracked per lane (each lane holds half the centroids)
   constexpr bool SPLIT = F32 || WT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hh = lane >> 5, ln = lane & 31;
   const bool use_psac = (MODE == MODE_KEYS) && (a.flags & QWM_PSAC) && a.U != nullptr;
@@ -460,7 +464,7 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
       g[KT + k] = hh ? t[k] : o;
     }
     const float floor_unt = fminf(unpacked(g[KT - 1]), unpacked(g[2 * KT - 1]));   // every untracked value is >= this
-    if (QS) {
+    if (QS && !EXH) {
       // one ascending list of the 2 KT tracked values: half 1 reversed makes the
       // sequence bitonic; four half-cleaner stages sort it
 #pragma unroll
@@ -476,7 +480,7 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
           if ((i & d) == 0) cswap(g[i], g[i + d]);
     }
     float gmin = g[0];
-    if (!QS && g[KT] < gmin) gmin = g[KT];
+    if ((!QS || EXH) && g[KT] < gmin) gmin = g[KT];
 
     // ---- token norm A = sum_c w_c k_c^2 ----
     const float A = lanepair_sum(-0.5f * An);
@@ -552,6 +556,21 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
         bu2 = by_bounds ? ub0 : d1 * (1.0f + DREL);
         bl2 = l2;
       }
+    } else if constexpr (EXH) {
+      // QSAC with every centroid a candidate (M >= 256): the choice is the smallest (S, j)
+      // over all of them, S from exact fp32 group ranges (nothing to certify)
+      double Sbest = __builtin_inf();
+#pragma unroll 1
+      for (int j = 0; j < NC; ++j) {
+        const ResidStats rs = resid_ranges(kf, sm.mu, j, hh);
+        const double R0 = (double)rs.hi0 - (double)rs.lo0, R1 = (double)rs.hi1 - (double)rs.lo1;
+        const double S = W0 * R0 * R0 + W1 * R1 * R1;
+        if (!have_w || S < Sbest || (S == Sbest && j < win)) {
+          Sbest = S; win = j;
+          wlo0 = rs.lo0; whi0 = rs.hi0; wlo1 = rs.lo1; whi1 = rs.hi1; have_w = true;
+        }
+      }
+      fast = fast && __builtin_isfinite(Sbest);
     } else {
       // QSAC.  Tracked candidate k is certainly outside the M nearest when M other
       // values are certainly smaller; the untracked ones must all be outside too.
@@ -1790,10 +1809,16 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
   const dim3 grid(bph, x->H), block(256);
   const bool f32 = x->dtype != QWM_BF16;
   // M in 9 .. 16: sixteen values tracked per lane, so that the shortlist can
-  // still be certified without the exact path
+  // still be certified without the exact path; M >= 256: every centroid
   const bool kq16 = qs && a.M > 8 && a.M <= 16;
+  const bool exh = qs && a.M >= NC;
   if constexpr (MODE == MODE_KEYS) {
-    if (f32) {
+    if (exh) {
+      if (f32 && wt) hipLaunchKernelGGL((select_kernel<MODE, true, true, true, NC>), grid, block, 0, stream, a);
+      else if (f32) hipLaunchKernelGGL((select_kernel<MODE, true, true, false, NC>), grid, block, 0, stream, a);
+      else if (wt) hipLaunchKernelGGL((select_kernel<MODE, false, true, true, NC>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((select_kernel<MODE, false, true, false, NC>), grid, block, 0, stream, a);
+    } else if (f32) {
       if (kq16 && wt) hipLaunchKernelGGL((select_kernel<MODE, true, true, true, 16>), grid, block, 0, stream, a);
       else if (kq16) hipLaunchKernelGGL((select_kernel<MODE, true, true, false, 16>), grid, block, 0, stream, a);
       else if (qs && wt) hipLaunchKernelGGL((select_kernel<MODE, true, true, true>), grid, block, 0, stream, a);
