@@ -307,7 +307,7 @@ constexpr float DREL = 1.0f / 65536.0f;   // relative error bound of the fp32 re
 // head's list for Lloyd's bounded iterations; nlist of them), with the head's
 // tables staged first.  Every tile ends with a block barrier, so a block may
 // call it again for another head.
-template <int MODE, bool F32, bool QS, bool WT, int KQ>
+template <int MODE, bool F32, bool QS, bool WT, int KQ, bool BND>
 __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, const int h, const int64_t nlist,
                                              const int64_t t_begin, const int64_t t_end) {
   // KQ = 256: QSAC with M >= 256 (every centroid a candidate), scored exhaustively
@@ -545,7 +545,7 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
         }
         fast = ok;
       }
-      if (MODE == MODE_ASSIGN) {
+      if (MODE == MODE_ASSIGN && BND) {
         float l2 = L_unt;
 #pragma unroll
         for (int e = 0; e < 6; ++e) {
@@ -654,9 +654,10 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
         sm.l.fast[wv][ln] = fast ? 1 : 0;
         if (fast) {
           sm.idx[wv][ln] = (uint8_t)win;
-          // Euclidean distance bounds, rounded outward
-          sm.l.ub[wv][ln] = sqrtf(bu2) * (1.0f + 1.0f / 1048576.0f);
-          sm.l.lb[wv][ln] = sqrtf(fmaxf(bl2, 0.f)) * (1.0f - 1.0f / 1048576.0f);
+          if (BND) {   // Euclidean distance bounds, rounded outward
+            sm.l.ub[wv][ln] = sqrtf(bu2) * (1.0f + 1.0f / 1048576.0f);
+            sm.l.lb[wv][ln] = sqrtf(fmaxf(bl2, 0.f)) * (1.0f - 1.0f / 1048576.0f);
+          }
         } else {
           const int slot = atomicAdd(a.counter, 1);
           a.worklist[slot] = (int32_t)((int64_t)h * a.T + tok);
@@ -835,7 +836,7 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
       }
       if (certified) {
         a.idx[o] = (uint8_t)nw;
-        if (a.ub) {
+        if (BND) {
           a.ub[o] = sm.l.ub[wv][lane];
           a.lb[o] = sm.l.lb[wv][lane];
         }
@@ -881,7 +882,8 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
 // one-dimensional; all heads' lists, taken one after the other, form NT tiles,
 // and block b takes tiles [b NT / G, (b + 1) NT / G) of them (G blocks), head by
 // head, so that a short or uneven list still spreads over the whole grid.
-template <int MODE, bool F32, bool QS, bool WT, int KQ = 8, bool FLAT = false>
+// BND (Lloyd assignment): the distance bounds are written (a.ub, a.lb).
+template <int MODE, bool F32, bool QS, bool WT, int KQ = 8, bool FLAT = false, bool BND = false>
 __global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArgs a) {
   __shared__ SelShared sm;
   if constexpr (FLAT) {
@@ -894,7 +896,7 @@ __global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArg
       const int64_t n = a.wl_cnt[g];
       const int64_t hi = lo + (n + SEL_TOK - 1) / SEL_TOK;
       if (hi > r0 && hi > lo)
-        select_range<MODE, F32, QS, WT, KQ>(a, sm, g, n, (lo > r0 ? lo : r0) - lo, (hi < r1 ? hi : r1) - lo);
+        select_range<MODE, F32, QS, WT, KQ, BND>(a, sm, g, n, (lo > r0 ? lo : r0) - lo, (hi < r1 ? hi : r1) - lo);
       lo = hi;
     }
   } else {
@@ -904,7 +906,7 @@ __global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArg
     const int64_t t_begin = (int64_t)blockIdx.x * ntile / gridDim.x;
     const int64_t t_end = (int64_t)(blockIdx.x + 1) * ntile / gridDim.x;
     if (t_begin >= t_end) return;   // block-uniform
-    select_range<MODE, F32, QS, WT, KQ>(a, sm, h, nlist, t_begin, t_end);
+    select_range<MODE, F32, QS, WT, KQ, BND>(a, sm, h, nlist, t_begin, t_end);
   }
 }
 
@@ -1839,8 +1841,11 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
       const int64_t tiles = (int64_t)x->H * ((x->T + SEL_TOK - 1) / SEL_TOK);
       const int64_t g = 2 * (int64_t)device_cus();
       const dim3 fgrid((unsigned)(tiles < g ? tiles : g));
-      if (f32) hipLaunchKernelGGL((select_kernel<MODE, true, false, false, 8, true>), fgrid, block, 0, stream, a);
-      else hipLaunchKernelGGL((select_kernel<MODE, false, false, false, 8, true>), fgrid, block, 0, stream, a);
+      if (f32) hipLaunchKernelGGL((select_kernel<MODE, true, false, false, 8, true, true>), fgrid, block, 0, stream, a);
+      else hipLaunchKernelGGL((select_kernel<MODE, false, false, false, 8, true, true>), fgrid, block, 0, stream, a);
+    } else if (a.ub != nullptr) {
+      if (f32) hipLaunchKernelGGL((select_kernel<MODE, true, false, false, 8, false, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((select_kernel<MODE, false, false, false, 8, false, true>), grid, block, 0, stream, a);
     } else {
       if (f32) hipLaunchKernelGGL((select_kernel<MODE, true, false, false>), grid, block, 0, stream, a);
       else hipLaunchKernelGGL((select_kernel<MODE, false, false, false>), grid, block, 0, stream, a);
@@ -1994,6 +1999,11 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
       return check_launch("centroid copy");
     return QWM_OK;
   }
+  // Builds of at most three iterations (at most one could skip tokens, and the
+  // scan and bound kernels would cost more than it saves) take the plain form:
+  // every iteration assigns every token and every head's members are summed
+  // in fp64 in token order (no flags: no scan).
+  const bool with_bounds = iters >= 4;
   if (iters > 0) {   // no row excluded yet: the exact path marks non-finite rows
     const int64_t eb = (int64_t)x->H * excl_words(x->T) * 4;
     const int64_t eblocks = (eb + 255) / 256;
@@ -2003,8 +2013,10 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
     if (s != QWM_OK) return s;
     // the fixed-point units of the member sums; heads with values finer than
     // their unit are flagged and take the fp64 member sums every iteration
-    s = lloyd_scan(x, ll, stream);
-    if (s != QWM_OK) return s;
+    if (with_bounds) {
+      s = lloyd_scan(x, ll, stream);
+      if (s != QWM_OK) return s;
+    }
   }
   for (int it = 0; it < iters; ++it) {
     // every iteration: the table terms of the GEMM, cleared list counters
@@ -2014,12 +2026,12 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
     fill_common(a, x, wk, cur);
     a.M = 1; a.flags = 0; a.cb = error_coeff(x->dtype != QWM_BF16);
     a.idx = wk.assign; a.diag = diag; a.excl = wk.excl; a.excl_words = excl_words(x->T);
-    a.ub = ll.ub; a.lb = ll.lb;
+    if (with_bounds) { a.ub = ll.ub; a.lb = ll.lb; }
     // The first two iterations assign every token (the means still move far)
     // and sum the members from scratch; later ones assign again only the
     // tokens whose bounds no longer settle their centroid (every token of a
     // flagged head) and apply the recorded changes to the integer sums.
-    const bool bounded = it >= 2;
+    const bool bounded = with_bounds && it >= 2;
     if (bounded) {
       s = lloyd_bounds(x, wk.assign, wk.excl, excl_words(x->T), ll, stream);
       if (s != QWM_OK) return s;
@@ -2036,7 +2048,8 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
     if (s != QWM_OK) return s;
     const int64_t units = (int64_t)x->H * NC;
     hipLaunchKernelGGL(lloyd_sum_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, x->ptr, x->dtype,
-                       x->T, x->stride_t, x->stride_h, x->H, wk.perm, wk.start, cur, centroids, ll.hflag, ll.emax,
+                       x->T, x->stride_t, x->stride_h, x->H, wk.perm, wk.start, cur, centroids,
+                       with_bounds ? ll.hflag : nullptr, ll.emax,
                        bounded ? nullptr : ll.sums, ll.cnt, ll.P);
     s = check_launch("Lloyd update");
     if (s != QWM_OK) return s;
@@ -2044,8 +2057,10 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
       s = lloyd_apply_changes(x, ll, stream);
       if (s != QWM_OK) return s;
     }
-    s = lloyd_finalize(x, ll, cur, centroids, stream);
-    if (s != QWM_OK) return s;
+    if (with_bounds) {   // (without flags every mean comes from the fp64 member sums)
+      s = lloyd_finalize(x, ll, cur, centroids, stream);
+      if (s != QWM_OK) return s;
+    }
     cur = centroids;
   }
   return QWM_OK;
