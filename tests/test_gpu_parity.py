@@ -414,28 +414,31 @@ def test_quantize_keys_keep_rejections(qwm, M):
              f"diag {diag.tolist()}")
 
 
-def test_quantize_keys_cold_start_and_fp32(qwm):
-    """Chunk 0: w = 1 and no basis (PSAC inactive); fp32 tokens."""
+@pytest.mark.parametrize("M", [8, 256])
+def test_quantize_keys_cold_start_and_fp32(qwm, M):
+    """Chunk 0: w = 1 and no basis (PSAC inactive); fp32 tokens.  M = 256: every
+    centroid a candidate (the exhaustive variant of the selection kernel)."""
     import torch
     from gpu_helpers import dev_tokens, dev_table, packed_host, idx_mismatches_allowed, compare_codec
+    _log(f"fp32 keys M={M}")
     T = 600
     w, K, Ct, wt, Ut = _key_inputs("tiny", T, None)
-    out = qwm.quantize_keys(dev_tokens(K, "f32"), dev_table(Ct), None, None, M=8, flags=3)
+    out = qwm.quantize_keys(dev_tokens(K, "f32"), dev_table(Ct), None, None, M=M, flags=3)
     torch.cuda.synchronize()
     g = packed_host(out)
-    o = Qz.quantize_keys(K[:, 0].astype(np.float64), Ct[0], None, None, M=8, flags=3)
-    nmis, nbad = idx_mismatches_allowed("qsac", o, g["idx"][0], K[:, 0], Ct[0], None, 8)
+    o = Qz.quantize_keys(K[:, 0].astype(np.float64), Ct[0], None, None, M=M, flags=3)
+    nmis, nbad = idx_mismatches_allowed("qsac", o, g["idx"][0], K[:, 0], Ct[0], None, M)
     assert nbad == 0
     compare_codec(o, {k: v[0] for k, v in g.items()}, T, o["idx"] == g["idx"][0])
     assert np.all(g["c"] == 0)
     # fp32 with weights and PSAC
     wdev = torch.from_numpy(wt).cuda()
     from gpu_helpers import dev_basis
-    out = qwm.quantize_keys(dev_tokens(K, "f32"), dev_table(Ct), wdev, dev_basis(Ut), M=8, flags=3)
+    out = qwm.quantize_keys(dev_tokens(K, "f32"), dev_table(Ct), wdev, dev_basis(Ut), M=M, flags=3)
     torch.cuda.synchronize()
     g = packed_host(out)
-    o = Qz.quantize_keys(K[:, 0].astype(np.float64), Ct[0], wt[0], Ut[0], M=8, flags=3)
-    nmis, nbad = idx_mismatches_allowed("qsac", o, g["idx"][0], K[:, 0], Ct[0], wt[0], 8)
+    o = Qz.quantize_keys(K[:, 0].astype(np.float64), Ct[0], wt[0], Ut[0], M=M, flags=3)
+    nmis, nbad = idx_mismatches_allowed("qsac", o, g["idx"][0], K[:, 0], Ct[0], wt[0], M)
     assert nbad == 0
     same = o["idx"] == g["idx"][0]
     compare_codec(o, {k: v[0] for k, v in g.items()}, T, same)
