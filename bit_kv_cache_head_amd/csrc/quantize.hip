@@ -1460,13 +1460,16 @@ __global__ __launch_bounds__(256) void forgy_kernel(const void* x, int32_t dtype
 
 // The mean update runs in two kernels.
 //
-// lloyd_sort_kernel (grid H, 1,024 threads): a stable counting sort of the
-// head's assignment: ids[h][start_j .. start_j + n_j) lists the members of
-// cluster j in token order, start[h][j] = start_j, start[h][256] = T.  Wave w
-// owns the tokens of the w-th of 16 contiguous ranges; after a count and a
-// scan over (cluster, range), it walks its range 64 tokens at a time, and each
-// lane finds the lanes holding the same cluster from eight ballots, so its
-// place is the range's running offset plus the number of such lanes below it.
+// lloyd_sort_kernel (grid (H, nb), 1,024 threads): a stable counting sort of
+// the head's assignment: ids[h][start_j .. start_j + n_j) lists the members of
+// cluster j in token order, start[h][j] = start_j, start[h][256] = members in
+// all.  Block (h, b) places the b-th of nb contiguous chunks; each block counts
+// the whole head (one byte per token) for the cluster totals and the members
+// of the chunks before its own.  Wave w owns the tokens of the w-th of 16
+// ranges of the chunk; after a count and a scan over (cluster, range), it walks
+// its range 64 tokens at a time, and each lane finds the lanes holding the same
+// cluster from eight ballots, so its place is the range's running offset plus
+// the number of such lanes below it.
 //
 // lloyd_sum_kernel (one wave per (head, cluster), 64 lanes x 2 channels): the
 // member rows summed in token order in fp64, 32 rows in flight; the new
@@ -1482,19 +1485,29 @@ __global__ __launch_bounds__(1024) void lloyd_sort_kernel(const int32_t* hflag, 
   if (hflag != nullptr && hflag[h] == 0) return;   // the integer path handles this head
   __shared__ int32_t cnt[LS_WAVES][NC];     // counts, then running offsets
   __shared__ int32_t tot[NC];
+  __shared__ int32_t pre[NC];               // members in the chunks before this block's
   for (int e = tid; e < LS_WAVES * NC; e += 1024) (&cnt[0][0])[e] = 0;
+  if (tid < NC) { tot[tid] = 0; pre[tid] = 0; }
   __syncthreads();
   const uint8_t* ah = assign + (int64_t)h * T;
   const uint32_t* eh = excl + (int64_t)h * excl_words;
-  const int64_t r0 = T * wv / LS_WAVES, r1 = T * (wv + 1) / LS_WAVES;
+  // block (h, b) places chunk b of gridDim.y; wave w the w-th of 16 parts of it
+  const int nb = gridDim.y, b = blockIdx.y;
+  const int64_t c0 = T * b / nb, c1 = T * (b + 1) / nb;
+  const int64_t r0 = c0 + (c1 - c0) * wv / LS_WAVES, r1 = c0 + (c1 - c0) * (wv + 1) / LS_WAVES;
   for (int64_t t = r0 + lane; t < r1; t += 64)
     if (!((eh[t >> 5] >> (t & 31)) & 1u)) atomicAdd(&cnt[wv][ah[t]], 1);
+  // the other chunks: the members before this one, and the cluster totals
+  for (int64_t t = tid; t < c0; t += 1024)
+    if (!((eh[t >> 5] >> (t & 31)) & 1u)) atomicAdd(&pre[ah[t]], 1);
+  for (int64_t t = c1 + tid; t < T; t += 1024)
+    if (!((eh[t >> 5] >> (t & 31)) & 1u)) atomicAdd(&tot[ah[t]], 1);
   __syncthreads();
   if (tid < NC) {
     int32_t run = 0;
 #pragma unroll
     for (int w = 0; w < LS_WAVES; ++w) { const int32_t c = cnt[w][tid]; cnt[w][tid] = run; run += c; }
-    tot[tid] = run;
+    tot[tid] += run + pre[tid];
   }
   __syncthreads();
   // exclusive scan of the cluster totals (one wave, 4 clusters per lane)
@@ -1512,12 +1525,12 @@ __global__ __launch_bounds__(1024) void lloyd_sort_kernel(const int32_t* hflag, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) { tot[4 * lane + i] = run; run += v[i]; }
     // members in all: the end of the last cluster (excluded rows are not members)
-    if (lane == 63) start[h * (NC + 1) + NC] = run;
+    if (lane == 63 && b == 0) start[h * (NC + 1) + NC] = run;
   }
   __syncthreads();
   if (tid < NC) {
-    const int32_t base = tot[tid];
-    start[h * (NC + 1) + tid] = base;
+    if (b == 0) start[h * (NC + 1) + tid] = tot[tid];
+    const int32_t base = tot[tid] + pre[tid];
 #pragma unroll
     for (int w = 0; w < LS_WAVES; ++w) cnt[w][tid] += base;
   }
@@ -2042,7 +2055,12 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
     // members sorted by centroid (the Forgy permutation is dead by now: its
     // buffer holds them), summed in fp64 for flagged heads, in fixed point for
     // the others while they are summed from scratch
-    hipLaunchKernelGGL(lloyd_sort_kernel, dim3(x->H), dim3(1024), 0, stream, bounded ? ll.hflag : nullptr, wk.assign,
+    // (every head when all are sorted: chunks over the resident grid, two
+    // 1,024-thread blocks per CU; bounded: only flagged heads, one block each)
+    int nb = bounded ? 1 : 2 * device_cus() / x->H;
+    nb = nb < 1 ? 1 : (nb > 8 ? 8 : nb);
+    if ((int64_t)nb * 64 > x->T) nb = 1;
+    hipLaunchKernelGGL(lloyd_sort_kernel, dim3(x->H, nb), dim3(1024), 0, stream, bounded ? ll.hflag : nullptr, wk.assign,
                        wk.excl, excl_words(x->T), x->T, wk.perm, wk.start);
     s = check_launch("Lloyd member sort");
     if (s != QWM_OK) return s;
