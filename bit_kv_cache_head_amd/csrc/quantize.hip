@@ -2039,7 +2039,8 @@ qwm_status launch_lloyd(const qwm_tokens* x, int32_t iters, uint64_t seed, const
     fill_common(a, x, wk, cur);
     a.M = 1; a.flags = 0; a.cb = error_coeff(x->dtype != QWM_BF16);
     a.idx = wk.assign; a.diag = diag; a.excl = wk.excl; a.excl_words = excl_words(x->T);
-    if (with_bounds) { a.ub = ll.ub; a.lb = ll.lb; }
+    // (the bounds that the third iteration starts from are the second's)
+    if (with_bounds && it >= 1) { a.ub = ll.ub; a.lb = ll.lb; }
     // The first two iterations assign every token (the means still move far)
     // and sum the members from scratch; later ones assign again only the
     // tokens whose bounds no longer settle their centroid (every token of a
