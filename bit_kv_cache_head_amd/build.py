@@ -31,8 +31,10 @@ CFLAGS = [
 
 # Per-source additions.  attention.hip sees no NaN in its logits (scores of
 # finite fp16 tiles; keys past a segment end are masked with -inf), so its
-# max reductions need no NaN quieting.
-EXTRA = {"attention.hip": ["-fno-honor-nans"]}
+# max reductions need no NaN quieting; its scheduler favours instruction-level
+# parallelism (about 1.5 % faster on the full-depth attention call, no new
+# spills in the kernels the steps run).
+EXTRA = {"attention.hip": ["-fno-honor-nans", "-mllvm", "--amdgpu-sched-strategy=max-ilp"]}
 
 
 def _compile(src: str) -> str:
