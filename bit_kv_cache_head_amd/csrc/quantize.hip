@@ -158,8 +158,10 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 __device__ __forceinline__ float lo_bf16(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
 
-__device__ __forceinline__ float pack_idx(float f, uint32_t j) {
-  return __uint_as_float((__float_as_uint(f) & 0xFFFFFF00u) | j);
+// f with its low byte replaced by byte b of jb (v_perm_b32, selector
+// 0x07060500 + b: bytes 3..1 of f, then byte b of jb).
+__device__ __forceinline__ float pack_idx(float f, uint32_t jb, int b) {
+  return __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(f), jb, 0x07060500u + (uint32_t)b));
 }
 
 // Thresholds of the INT2 code: q = #{k : r > tau'_k}, k = 1..3.
@@ -437,6 +439,9 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
     for (int k = 0; k < KT; ++k) t[k] = __builtin_inff();
     float ninf;
     asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(ninf));
+    // centroid indices of the lane's 16 values, four to a word: byte b of
+    // jb0 + 8 q 0x01010101 is 32 ct + c_row(4 q + b, hh)
+    uint32_t jb0 = (uint32_t)(4 * hh) * 0x01010101u + 0x03020100u;
 #pragma unroll 1
     for (int ct = 0; ct < 8; ++ct) {
       f32x16 acc = {};
@@ -453,7 +458,8 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
         acc = mfma_bf16(__builtin_bit_cast(bf16x8, v), kaug, acc);
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) topk_insert<KT>(t, pack_idx(acc[i], 32 * ct + c_row(i, hh)), ninf);
+      for (int i = 0; i < 16; ++i) topk_insert<KT>(t, pack_idx(acc[i], jb0 + (uint32_t)(8 * (i >> 2)) * 0x01010101u, i & 3), ninf);
+      jb0 += 32u * 0x01010101u;
     }
     // canonical per-token list: g[0..KT) = half 0, g[KT..2KT) = half 1 (identical on both lanes)
     float g[2 * KT];
