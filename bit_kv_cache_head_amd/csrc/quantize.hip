@@ -889,8 +889,11 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
 // and block b takes tiles [b NT / G, (b + 1) NT / G) of them (G blocks), head by
 // head, so that a short or uneven list still spreads over the whole grid.
 // BND (Lloyd assignment): the distance bounds are written (a.ub, a.lb).
+// Every variant runs two blocks per CU (the LDS allows two), KQ = 16 too: it
+// would need about 320 registers per lane and spills instead, which still
+// beats one wave per SIMD.
 template <int MODE, bool F32, bool QS, bool WT, int KQ = 8, bool FLAT = false, bool BND = false>
-__global__ __launch_bounds__(256, KQ == 16 ? 1 : 2) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
   __shared__ SelShared sm;
   if constexpr (FLAT) {
     int64_t nt = 0;
