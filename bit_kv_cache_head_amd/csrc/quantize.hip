@@ -121,6 +121,15 @@ struct SelectArgs {
   uint2* chg; int32_t* chg_cnt;
 };
 
+// Orders one wave's LDS writes before its later reads (and reads before later
+// writes) of the same locations: the compiler keeps them in program order and
+// one wave's LDS operations complete in order.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 constexpr int MU_ROW = D + 8;   // elements per staged centroid row (16 bytes of padding)
 struct SelShared {
   uint16_t mu[NC * MU_ROW];    // centroid rows, padded: 16-byte chunk c of row j at chunk 17 j + c
@@ -307,7 +316,9 @@ constexpr float DREL = 1.0f / 65536.0f;   // relative error bound of the fp32 re
 // otherwise carried as a bf16 pair t_hi + t_lo (two MFMAs per k-step).
 // select_range: tiles [t_begin, t_end) of head h (tokens, or entries of the
 // head's list for Lloyd's bounded iterations; nlist of them), with the head's
-// tables staged first.  Every tile ends with a block barrier, so a block may
+// tables staged first.  Within the range the waves share only the staged
+// tables, which they read, and each stages its own tokens' output, so the
+// tiles need no block barrier; the range ends with one, so that a block may
 // call it again for another head.
 template <int MODE, bool F32, bool QS, bool WT, int KQ, bool BND>
 __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, const int h, const int64_t nlist,
@@ -820,7 +831,8 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
         }
       }
     }
-    __syncthreads();
+    // the staging rows are the wave's own: a wave-level barrier orders them
+    wave_lds_sync();
 
     // ---- coalesced write-out of the wave's 32 tokens ----
     if (MODE == MODE_ASSIGN) {
@@ -878,8 +890,9 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
         }
       }
     }
-    __syncthreads();
+    wave_lds_sync();   // before the next tile's staging writes
   }
+  __syncthreads();     // the block may stage another head's tables next
 }
 
 // Block (x, h) takes a contiguous share of head h's tiles (tokens, or list
