@@ -351,6 +351,9 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
       for (int e = tid; e < D * R; e += 256) sm.ut[e % R][e / R] = a.U[(int64_t)h * D * R + e];
     }
   }
+  // block counter of the wave tiles handed out (in the padding of centroid row 0)
+  int32_t* next_wt = reinterpret_cast<int32_t*>(sm.mu + D);
+  if (tid == 0) *next_wt = 0;
   __syncthreads();
   float Bmax = a.Bmax[h * PREP_PARTS];
 #pragma unroll
@@ -358,11 +361,18 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
   const double W0 = a.Wg[2 * h], W1 = a.Wg[2 * h + 1];
   const float cb = a.cb;
 
-  // The token of this lane in tile t (list entry t SEL_TOK + 32 wv + ln);
-  // ok = false past the block's tiles or the head's tokens.
-  auto lane_token = [&](int64_t t, bool& ok) __attribute__((always_inline)) -> int64_t {
-    const int64_t e = t * SEL_TOK + wv * 32 + ln;
-    ok = t < t_end && e < nlist;
+  // The block's range is cut into wave tiles of 32 list entries: wave tile u
+  // (relative to the range) holds entries 32 (4 t_begin + u) + 0..31.  Wave w
+  // starts with u = w; whenever a wave starts a tile it takes the next one from
+  // the block counter (plus 4), so waves that finish early take more tiles.
+  // nwt: wave tiles that hold at least one entry.
+  const int64_t wt0 = 4 * t_begin;
+  const int64_t nwt_r = 4 * (t_end - t_begin), nwt_l = (nlist + 31) / 32 - wt0;
+  const int64_t nwt = nwt_r < nwt_l ? nwt_r : nwt_l;
+  // The token of this lane in wave tile u; ok = false past the range or the list.
+  auto lane_token = [&](int64_t u, bool& ok) __attribute__((always_inline)) -> int64_t {
+    const int64_t e = (wt0 + u) * 32 + ln;
+    ok = u < nwt && e < nlist;
     if (!wlm) return ok ? e : 0;
     return ok ? (int64_t)a.wl[(int64_t)h * a.T + e] : 0;
   };
@@ -379,11 +389,15 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
     for (int s = 0; s < (PF ? 8 : 1); ++s)
       nrow[s] = ok ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
   };
-  if constexpr (PF) fetch_rows(t_begin);
-  for (int64_t tile = t_begin; tile < t_end; ++tile) {
-    const int64_t tok0 = tile * SEL_TOK + wv * 32;   // first list entry of the wave
+  int64_t u = __builtin_amdgcn_readfirstlane(wv);
+  if constexpr (PF) fetch_rows(u);
+  while (u < nwt) {
+    int32_t taken = 0;
+    if (lane == 0) taken = atomicAdd(next_wt, 1);
+    const int64_t un = 4 + (int64_t)__builtin_amdgcn_readfirstlane(taken);   // the wave's next tile
+    const int64_t tok0 = (wt0 + u) * 32;   // first list entry of the wave tile
     bool valid;
-    const int64_t tok = lane_token(tile, valid);
+    const int64_t tok = lane_token(u, valid);
     const int64_t rowoff = (int64_t)h * a.sh + tok * a.st;
 
     // ---- the token in fp32: channels 16 s + 8 hh + e at kf[8 s + e] ----
@@ -394,7 +408,7 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
       if constexpr (PF) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) crow[s] = nrow[s];
-        fetch_rows(tile + 1);
+        fetch_rows(un);
       }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -891,6 +905,7 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
       }
     }
     wave_lds_sync();   // before the next tile's staging writes
+    u = un;
   }
   __syncthreads();     // the block may stage another head's tables next
 }
