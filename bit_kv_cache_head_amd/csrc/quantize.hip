@@ -32,8 +32,9 @@ struct TablePrepArgs {
   float* Bj;            // [H][256]
   float* Bmax;          // [H][PREP_PARTS] partial maxima of B (times 1 + 2^-16)
   double* Wg;           // [H][2]
-  int32_t* counter;     // fallback work counter (zeroed here)
+  int32_t* counter;     // fallback work counter, then at counter + 4 the H wave-tile counters (all zeroed here)
   int32_t* zero; int32_t nzero;   // more counters zeroed here (Lloyd lists), or null
+  int32_t H;
 };
 
 // Block (h, part): centroids 32 part .. +32 of head h; thread (centroid
@@ -46,7 +47,10 @@ __global__ __launch_bounds__(256) void prep_table_kernel(TablePrepArgs a) {
   __shared__ float ws[D];
   __shared__ float bm[4];
   if (tid < D) ws[tid] = a.w ? a.w[h * D + tid] : 1.0f;
-  if (h == 0 && part == 0 && tid == 0) *a.counter = 0;
+  if (h == 0 && part == 0) {
+    if (tid == 0) *a.counter = 0;
+    for (int i = tid; i < a.H; i += 256) a.counter[4 + i] = 0;
+  }
   if (h == 0 && part == 0 && a.zero)
     for (int i = tid; i < a.nzero; i += 256) a.zero[i] = 0;
   __syncthreads();
@@ -105,6 +109,8 @@ struct SelectArgs {
   uint8_t* idx;         // [H][T] (assignment for MODE_ASSIGN)
   uint8_t* codes; uint16_t* scale; uint8_t* zeros; int64_t zstride; int8_t* cq; uint16_t* cscale;
   int32_t* counter; int32_t* worklist;
+  // per head: key wave tiles handed out so far
+  int32_t* tcnt;
   qwm_diag* diag;
   // full-matrix candidate distance: S [H][128][128] fp64, n [H], mu^T S mu [H][256]
   const double* qS; const int64_t* qn; const double* qB;
@@ -320,7 +326,7 @@ constexpr float DREL = 1.0f / 65536.0f;   // relative error bound of the fp32 re
 // tables, which they read, and each stages its own tokens' output, so the
 // tiles need no block barrier; the range ends with one, so that a block may
 // call it again for another head.
-template <int MODE, bool F32, bool QS, bool WT, int KQ, bool BND>
+template <int MODE, bool F32, bool QS, bool WT, int KQ, bool BND, bool GDYN>
 __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, const int h, const int64_t nlist,
                                              const int64_t t_begin, const int64_t t_end) {
   // KQ = 256: QSAC with M >= 256 (every centroid a candidate), scored exhaustively
@@ -354,6 +360,8 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
   // block counter of the wave tiles handed out (in the padding of centroid row 0)
   int32_t* next_wt = reinterpret_cast<int32_t*>(sm.mu + D);
   if (tid == 0) *next_wt = 0;
+  // GDYN: every block of the head draws from the head's counter a.tcnt[h] instead
+  int32_t* const gcnt = GDYN ? a.tcnt + h : nullptr;
   __syncthreads();
   float Bmax = a.Bmax[h * PREP_PARTS];
 #pragma unroll
@@ -365,6 +373,9 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
   // (relative to the range) holds entries 32 (4 t_begin + u) + 0..31.  Wave w
   // starts with u = w; whenever a wave starts a tile it takes the next one from
   // the block counter (plus 4), so waves that finish early take more tiles.
+  // GDYN: the range is the whole head, and every wave
+  // of every block on the head takes each of its tiles from it, so that blocks
+  // that get more of their CU take more tiles.
   // nwt: wave tiles that hold at least one entry.
   const int64_t wt0 = 4 * t_begin;
   const int64_t nwt_r = 4 * (t_end - t_begin), nwt_l = (nlist + 31) / 32 - wt0;
@@ -389,12 +400,15 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
     for (int s = 0; s < (PF ? 8 : 1); ++s)
       nrow[s] = ok ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
   };
-  int64_t u = __builtin_amdgcn_readfirstlane(wv);
+  auto take_tile = [&]() __attribute__((always_inline)) -> int64_t {
+    int32_t taken = 0;
+    if (lane == 0) taken = GDYN ? atomicAdd(gcnt, 1) : atomicAdd(next_wt, 1);
+    return (GDYN ? 0 : 4) + (int64_t)__builtin_amdgcn_readfirstlane(taken);
+  };
+  int64_t u = GDYN ? take_tile() : (int64_t)__builtin_amdgcn_readfirstlane(wv);
   if constexpr (PF) fetch_rows(u);
   while (u < nwt) {
-    int32_t taken = 0;
-    if (lane == 0) taken = atomicAdd(next_wt, 1);
-    const int64_t un = 4 + (int64_t)__builtin_amdgcn_readfirstlane(taken);   // the wave's next tile
+    const int64_t un = take_tile();   // the wave's next tile
     const int64_t tok0 = (wt0 + u) * 32;   // first list entry of the wave tile
     bool valid;
     const int64_t tok = lane_token(u, valid);
@@ -910,10 +924,14 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
   __syncthreads();     // the block may stage another head's tables next
 }
 
-// Block (x, h) takes a contiguous share of head h's tiles (tokens, or list
-// entries in Lloyd's bounded iterations), equal to within one tile across the
-// head's gridDim.x blocks.  FLAT (Lloyd's bounded iterations): the grid is
-// one-dimensional; all heads' lists, taken one after the other, form NT tiles,
+// Keys: the grid is one-dimensional.  Block b serves head b mod H; a head's
+// blocks take its 32-token wave tiles from the head's counter a.tcnt[h] one by
+// one, so that blocks that get more of their CU (a CU runs the block that
+// arrived first ahead of its later partner) take more tiles.  Values and the
+// full Lloyd assignment: block (x, h) takes a fixed share of head h's tiles
+// (their tiles are cheap, and the counter's atomics cost more than the balance
+// gains).  FLAT (Lloyd's bounded
+// iterations): all heads' lists, taken one after the other, form NT tiles,
 // and block b takes tiles [b NT / G, (b + 1) NT / G) of them (G blocks), head by
 // head, so that a short or uneven list still spreads over the whole grid.
 // BND (Lloyd assignment): the distance bounds are written (a.ub, a.lb).
@@ -933,17 +951,26 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
       const int64_t n = a.wl_cnt[g];
       const int64_t hi = lo + (n + SEL_TOK - 1) / SEL_TOK;
       if (hi > r0 && hi > lo)
-        select_range<MODE, F32, QS, WT, KQ, BND>(a, sm, g, n, (lo > r0 ? lo : r0) - lo, (hi < r1 ? hi : r1) - lo);
+        select_range<MODE, F32, QS, WT, KQ, BND, false>(a, sm, g, n, (lo > r0 ? lo : r0) - lo, (hi < r1 ? hi : r1) - lo);
       lo = hi;
     }
+  } else if constexpr (MODE == MODE_KEYS) {
+    // one-dimensional grid, heads interleaved (block b serves head b mod H), so
+    // that each head has blocks of every dispatch round; the blocks of a head
+    // take its wave tiles from the head's counter
+    const int h = (int)(blockIdx.x % (unsigned)a.H);
+    const int64_t ntile = (a.T + SEL_TOK - 1) / SEL_TOK;
+    if (ntile <= 0) return;   // block-uniform
+    select_range<MODE, F32, QS, WT, KQ, BND, true>(a, sm, h, a.T, 0, ntile);
   } else {
+    // block (x, h): a contiguous share of head h's tiles, equal to within one
+    // tile across the head's gridDim.x blocks
     const int h = blockIdx.y;
-    const int64_t nlist = (MODE == MODE_ASSIGN && a.wl != nullptr) ? (int64_t)a.wl_cnt[h] : a.T;
-    const int64_t ntile = (nlist + SEL_TOK - 1) / SEL_TOK;
+    const int64_t ntile = (a.T + SEL_TOK - 1) / SEL_TOK;
     const int64_t t_begin = (int64_t)blockIdx.x * ntile / gridDim.x;
     const int64_t t_end = (int64_t)(blockIdx.x + 1) * ntile / gridDim.x;
     if (t_begin >= t_end) return;   // block-uniform
-    select_range<MODE, F32, QS, WT, KQ, BND>(a, sm, h, nlist, t_begin, t_end);
+    select_range<MODE, F32, QS, WT, KQ, BND, false>(a, sm, h, a.T, t_begin, t_end);
   }
 }
 
@@ -1758,7 +1785,7 @@ constexpr size_t select_ws_bytes_c(int64_t T, int32_t H, bool lloyd) {
   b += align256((size_t)H * NC * 4);
   b += align256((size_t)H * PREP_PARTS * 4);
   b += align256((size_t)H * 2 * 8);
-  b += align256(16);
+  b += align256(16 + (size_t)H * 4);
   b += align256((size_t)H * T * 4);
   b += align256((size_t)H * NC * 8);
   if (lloyd) {
@@ -1817,7 +1844,7 @@ static SelWork carve(void* ws, int64_t T, int32_t H, bool lloyd, int32_t dtype =
   w.Bj = reinterpret_cast<float*>(take((size_t)H * NC * 4));
   w.Bmax = reinterpret_cast<float*>(take((size_t)H * PREP_PARTS * 4));
   w.Wg = reinterpret_cast<double*>(take((size_t)H * 2 * 8));
-  w.counter = reinterpret_cast<int32_t*>(take(16));
+  w.counter = reinterpret_cast<int32_t*>(take(16 + (size_t)H * 4));
   w.worklist = reinterpret_cast<int32_t*>(take((size_t)H * T * 4));
   w.qB = reinterpret_cast<double*>(take((size_t)H * NC * 8));
   if (lloyd) {
@@ -1858,7 +1885,10 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
   const int bph = blocks_per_head(x->T, x->H);
   const bool qs = (MODE == MODE_KEYS) && (a.flags & QWM_QSAC) && a.M > 1;
   const bool wt = (MODE == MODE_KEYS) && a.w != nullptr;
-  const dim3 grid(bph, x->H), block(256);
+  // keys: one-dimensional, heads interleaved, tiles from the per-head counters
+  // (a.tcnt); values and Lloyd: (blocks per head, H)
+  const dim3 grid(MODE == MODE_KEYS ? (unsigned)(bph * x->H) : (unsigned)bph, MODE == MODE_KEYS ? 1u : (unsigned)x->H),
+      block(256);
   const bool f32 = x->dtype != QWM_BF16;
   // M in 9 .. 16: sixteen values tracked per lane, so that the shortlist can
   // still be certified without the exact path; M >= 256: every centroid
@@ -1924,11 +1954,12 @@ static void fill_common(SelectArgs& a, const qwm_tokens* x, const SelWork& w, co
   a.x = x->ptr; a.T = x->T; a.st = x->stride_t; a.sh = x->stride_h; a.H = x->H;
   a.aug = w.aug; a.Bj = w.Bj; a.Bmax = w.Bmax; a.Wg = w.Wg;
   a.mu = mu; a.counter = w.counter; a.worklist = w.worklist;
+  a.tcnt = w.counter + 4;
 }
 
 static qwm_status prep(const SelWork& w, const uint16_t* mu, const float* wts, int32_t H, hipStream_t stream,
                        int32_t* zero = nullptr, int32_t nzero = 0) {
-  TablePrepArgs p{mu, wts, w.aug, w.Bj, w.Bmax, w.Wg, w.counter, zero, nzero};
+  TablePrepArgs p{mu, wts, w.aug, w.Bj, w.Bmax, w.Wg, w.counter, zero, nzero, H};
   hipLaunchKernelGGL(prep_table_kernel, dim3(H, PREP_PARTS), dim3(256), 0, stream, p);
   return check_launch("centroid table preparation");
 }
