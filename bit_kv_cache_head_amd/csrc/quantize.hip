@@ -24,6 +24,9 @@ enum { MODE_ASSIGN = 0, MODE_VALUES = 1, MODE_KEYS = 2 };
 constexpr int PREP_PARTS = NC / 32;   // table-preparation blocks per head
 
 constexpr int SEL_TOK = 128;     // tokens per block pass (4 waves x 32)
+// Internal selection flag (above the public QWM_* bits): the key blocks of a
+// head take its wave tiles from the per-head counters at counter + 4.
+constexpr uint32_t SEL_HEAD_COUNTERS = 0x80000000u;
 
 struct TablePrepArgs {
   const uint16_t* mu;   // [H][256][128] bf16
@@ -109,8 +112,6 @@ struct SelectArgs {
   uint8_t* idx;         // [H][T] (assignment for MODE_ASSIGN)
   uint8_t* codes; uint16_t* scale; uint8_t* zeros; int64_t zstride; int8_t* cq; uint16_t* cscale;
   int32_t* counter; int32_t* worklist;
-  // per head: key wave tiles handed out so far
-  int32_t* tcnt;
   qwm_diag* diag;
   // full-matrix candidate distance: S [H][128][128] fp64, n [H], mu^T S mu [H][256]
   const double* qS; const int64_t* qn; const double* qB;
@@ -360,8 +361,10 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
   // block counter of the wave tiles handed out (in the padding of centroid row 0)
   int32_t* next_wt = reinterpret_cast<int32_t*>(sm.mu + D);
   if (tid == 0) *next_wt = 0;
-  // GDYN: every block of the head draws from the head's counter a.tcnt[h] instead
-  int32_t* const gcnt = GDYN ? a.tcnt + h : nullptr;
+  // GDYN with SEL_HEAD_COUNTERS: every block of the head draws from the head's
+  // counter a.counter[4 + h] instead (a large call; a small one keeps fixed
+  // block shares)
+  int32_t* const gcnt = (GDYN && (a.flags & SEL_HEAD_COUNTERS)) ? a.counter + 4 + h : nullptr;
   __syncthreads();
   float Bmax = a.Bmax[h * PREP_PARTS];
 #pragma unroll
@@ -400,15 +403,26 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
     for (int s = 0; s < (PF ? 8 : 1); ++s)
       nrow[s] = ok ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
   };
-  auto take_tile = [&]() __attribute__((always_inline)) -> int64_t {
-    int32_t taken = 0;
-    if (lane == 0) taken = GDYN ? atomicAdd(gcnt, 1) : atomicAdd(next_wt, 1);
-    return (GDYN ? 0 : 4) + (int64_t)__builtin_amdgcn_readfirstlane(taken);
-  };
-  int64_t u = GDYN ? take_tile() : (int64_t)__builtin_amdgcn_readfirstlane(wv);
+  const bool glob = GDYN && gcnt != nullptr;   // block-uniform
+  int64_t u = __builtin_amdgcn_readfirstlane(wv);
+  if constexpr (GDYN) {
+    if (glob) {
+      int32_t taken = 0;
+      if (lane == 0) taken = atomicAdd(gcnt, 1);
+      u = __builtin_amdgcn_readfirstlane(taken);
+    }
+  }
   if constexpr (PF) fetch_rows(u);
   while (u < nwt) {
-    const int64_t un = take_tile();   // the wave's next tile
+    int32_t taken = 0;
+    int64_t un;   // the wave's next tile
+    if constexpr (GDYN) {
+      if (lane == 0) taken = glob ? atomicAdd(gcnt, 1) : atomicAdd(next_wt, 1);
+      un = (glob ? 0 : 4) + (int64_t)__builtin_amdgcn_readfirstlane(taken);
+    } else {
+      if (lane == 0) taken = atomicAdd(next_wt, 1);
+      un = 4 + (int64_t)__builtin_amdgcn_readfirstlane(taken);
+    }
     const int64_t tok0 = (wt0 + u) * 32;   // first list entry of the wave tile
     bool valid;
     const int64_t tok = lane_token(u, valid);
@@ -925,7 +939,7 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
 }
 
 // Keys: the grid is one-dimensional.  Block b serves head b mod H; a head's
-// blocks take its 32-token wave tiles from the head's counter a.tcnt[h] one by
+// blocks take its 32-token wave tiles from the head's counter a.counter[4 + h] one by
 // one, so that blocks that get more of their CU (a CU runs the block that
 // arrived first ahead of its later partner) take more tiles.  Values and the
 // full Lloyd assignment: block (x, h) takes a fixed share of head h's tiles
@@ -954,17 +968,25 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
         select_range<MODE, F32, QS, WT, KQ, BND, false>(a, sm, g, n, (lo > r0 ? lo : r0) - lo, (hi < r1 ? hi : r1) - lo);
       lo = hi;
     }
-  } else if constexpr (MODE == MODE_KEYS) {
+  } else if constexpr (MODE == MODE_KEYS && KQ != 16) {
     // one-dimensional grid, heads interleaved (block b serves head b mod H), so
-    // that each head has blocks of every dispatch round; the blocks of a head
-    // take its wave tiles from the head's counter
+    // that each head has blocks of every dispatch round; with SEL_HEAD_COUNTERS the blocks
+    // of a head take its wave tiles from the head's counter, otherwise block
+    // b / H of the head a fixed share of its tiles
     const int h = (int)(blockIdx.x % (unsigned)a.H);
     const int64_t ntile = (a.T + SEL_TOK - 1) / SEL_TOK;
-    if (ntile <= 0) return;   // block-uniform
-    select_range<MODE, F32, QS, WT, KQ, BND, true>(a, sm, h, a.T, 0, ntile);
+    int64_t t_begin = 0, t_end = ntile;
+    if (!(a.flags & SEL_HEAD_COUNTERS)) {
+      const int64_t bph = gridDim.x / (unsigned)a.H, j = blockIdx.x / (unsigned)a.H;
+      t_begin = j * ntile / bph;
+      t_end = (j + 1) * ntile / bph;
+    }
+    if (t_begin >= t_end) return;   // block-uniform
+    select_range<MODE, F32, QS, WT, KQ, BND, true>(a, sm, h, a.T, t_begin, t_end);
   } else {
     // block (x, h): a contiguous share of head h's tiles, equal to within one
-    // tile across the head's gridDim.x blocks
+    // tile across the head's gridDim.x blocks (values, the full Lloyd
+    // assignment, and the sixteen-value key variant, which spills less so)
     const int h = blockIdx.y;
     const int64_t ntile = (a.T + SEL_TOK - 1) / SEL_TOK;
     const int64_t t_begin = (int64_t)blockIdx.x * ntile / gridDim.x;
@@ -1886,13 +1908,16 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
   const bool qs = (MODE == MODE_KEYS) && (a.flags & QWM_QSAC) && a.M > 1;
   const bool wt = (MODE == MODE_KEYS) && a.w != nullptr;
   // keys: one-dimensional, heads interleaved, tiles from the per-head counters
-  // (a.tcnt); values and Lloyd: (blocks per head, H)
-  const dim3 grid(MODE == MODE_KEYS ? (unsigned)(bph * x->H) : (unsigned)bph, MODE == MODE_KEYS ? 1u : (unsigned)x->H),
-      block(256);
-  const bool f32 = x->dtype != QWM_BF16;
+  // (SEL_HEAD_COUNTERS) when every wave has at least 16 tiles to draw (fewer, and the
+  // counters' atomics cost more than the balance gains); values and Lloyd:
+  // (blocks per head, H)
+  if (MODE == MODE_KEYS && (x->T + 31) / 32 >= 64 * (int64_t)bph) a.flags |= SEL_HEAD_COUNTERS;
   // M in 9 .. 16: sixteen values tracked per lane, so that the shortlist can
   // still be certified without the exact path; M >= 256: every centroid
   const bool kq16 = qs && a.M > 8 && a.M <= 16;
+  const bool flat_keys = MODE == MODE_KEYS && !kq16;
+  const dim3 grid(flat_keys ? (unsigned)(bph * x->H) : (unsigned)bph, flat_keys ? 1u : (unsigned)x->H), block(256);
+  const bool f32 = x->dtype != QWM_BF16;
   const bool exh = qs && a.M >= NC;
   if constexpr (MODE == MODE_KEYS) {
     if (exh) {
@@ -1954,7 +1979,6 @@ static void fill_common(SelectArgs& a, const qwm_tokens* x, const SelWork& w, co
   a.x = x->ptr; a.T = x->T; a.st = x->stride_t; a.sh = x->stride_h; a.H = x->H;
   a.aug = w.aug; a.Bj = w.Bj; a.Bmax = w.Bmax; a.Wg = w.Wg;
   a.mu = mu; a.counter = w.counter; a.worklist = w.worklist;
-  a.tcnt = w.counter + 4;
 }
 
 static qwm_status prep(const SelWork& w, const uint16_t* mu, const float* wts, int32_t H, hipStream_t stream,
