@@ -968,7 +968,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
         select_range<MODE, F32, QS, WT, KQ, BND, false>(a, sm, g, n, (lo > r0 ? lo : r0) - lo, (hi < r1 ? hi : r1) - lo);
       lo = hi;
     }
-  } else if constexpr (MODE == MODE_KEYS && KQ != 16) {
+  } else if constexpr (MODE == MODE_KEYS) {
     // one-dimensional grid, heads interleaved (block b serves head b mod H), so
     // that each head has blocks of every dispatch round; with SEL_HEAD_COUNTERS the blocks
     // of a head take its wave tiles from the head's counter, otherwise block
@@ -986,7 +986,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
   } else {
     // block (x, h): a contiguous share of head h's tiles, equal to within one
     // tile across the head's gridDim.x blocks (values, the full Lloyd
-    // assignment, and the sixteen-value key variant, which spills less so)
+    // assignment)
     const int h = blockIdx.y;
     const int64_t ntile = (a.T + SEL_TOK - 1) / SEL_TOK;
     const int64_t t_begin = (int64_t)blockIdx.x * ntile / gridDim.x;
@@ -1915,7 +1915,7 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
   // M in 9 .. 16: sixteen values tracked per lane, so that the shortlist can
   // still be certified without the exact path; M >= 256: every centroid
   const bool kq16 = qs && a.M > 8 && a.M <= 16;
-  const bool flat_keys = MODE == MODE_KEYS && !kq16;
+  const bool flat_keys = MODE == MODE_KEYS;
   const dim3 grid(flat_keys ? (unsigned)(bph * x->H) : (unsigned)bph, flat_keys ? 1u : (unsigned)x->H), block(256);
   const bool f32 = x->dtype != QWM_BF16;
   const bool exh = qs && a.M >= NC;
