@@ -111,6 +111,9 @@ struct SelectArgs {
   // outputs
   uint8_t* idx;         // [H][T] (assignment for MODE_ASSIGN)
   uint8_t* codes; uint16_t* scale; uint8_t* zeros; int64_t zstride; int8_t* cq; uint16_t* cscale;
+  // counter: the exact path's work counter; counter + 4 .. + 4 + H: the heads'
+  // key wave-tile counters (SEL_HEAD_COUNTERS); both zeroed by the table
+  // preparation
   int32_t* counter; int32_t* worklist;
   qwm_diag* diag;
   // full-matrix candidate distance: S [H][128][128] fp64, n [H], mu^T S mu [H][256]
@@ -376,9 +379,9 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
   // (relative to the range) holds entries 32 (4 t_begin + u) + 0..31.  Wave w
   // starts with u = w; whenever a wave starts a tile it takes the next one from
   // the block counter (plus 4), so waves that finish early take more tiles.
-  // GDYN: the range is the whole head, and every wave
-  // of every block on the head takes each of its tiles from it, so that blocks
-  // that get more of their CU take more tiles.
+  // With the head's counter (gcnt) the range is the whole head, and every wave
+  // of every block on the head takes each of its tiles, the first included,
+  // from that counter, so that blocks that get more of their CU take more.
   // nwt: wave tiles that hold at least one entry.
   const int64_t wt0 = 4 * t_begin;
   const int64_t nwt_r = 4 * (t_end - t_begin), nwt_l = (nlist + 31) / 32 - wt0;
