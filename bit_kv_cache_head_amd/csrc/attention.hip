@@ -1145,8 +1145,10 @@ static int attention_splits(int64_t Tq, int32_t H, int64_t total_keys) {
     if (s > 1 && tiles / s < 8) break;                 // keep splits meaningfully long
     const int64_t n = units * s;
     const int64_t rounds = (n + 255) / 256;
-    // CU occupancy over whole rounds, minus a small cost per extra split (merge work)
-    const double score = (double)n / (double)(rounds * 256) - 0.02 * s;
+    // CU occupancy over whole rounds, minus a cost per split (partial outputs,
+    // merge work, pipeline fill per unit); 0.04 measured best on the full-depth
+    // layer (4 splits: 1.29-1.31 ms, against 1.31-1.35 ms with 6 at 0.02)
+    const double score = (double)n / (double)(rounds * 256) - 0.04 * s;
     if (score > best_score + 1e-9) { best_score = score; best = s; }
   }
   return best;
