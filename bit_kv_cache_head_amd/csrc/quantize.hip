@@ -24,7 +24,7 @@ enum { MODE_ASSIGN = 0, MODE_VALUES = 1, MODE_KEYS = 2 };
 constexpr int PREP_PARTS = NC / 32;   // table-preparation blocks per head
 
 constexpr int SEL_TOK = 128;     // tokens per block pass (4 waves x 32)
-// Internal selection flag (above the public QWM_* bits): the key blocks of a
+// Internal selection flag (above the public QWM_* bits): the key or value blocks of a
 // head take its wave tiles from the per-head counters at counter + 4.
 constexpr uint32_t SEL_HEAD_COUNTERS = 0x80000000u;
 
@@ -112,8 +112,8 @@ struct SelectArgs {
   uint8_t* idx;         // [H][T] (assignment for MODE_ASSIGN)
   uint8_t* codes; uint16_t* scale; uint8_t* zeros; int64_t zstride; int8_t* cq; uint16_t* cscale;
   // counter: the exact path's work counter; counter + 4 .. + 4 + H: the heads'
-  // key wave-tile counters (SEL_HEAD_COUNTERS); both zeroed by the table
-  // preparation
+  // key or value wave-tile counters (SEL_HEAD_COUNTERS); both zeroed by the
+  // table preparation
   int32_t* counter; int32_t* worklist;
   qwm_diag* diag;
   // full-matrix candidate distance: S [H][128][128] fp64, n [H], mu^T S mu [H][256]
@@ -407,12 +407,15 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
       nrow[s] = ok ? *reinterpret_cast<const u32x4*>(xr + 16 * s + 8 * hh) : u32x4{0, 0, 0, 0};
   };
   const bool glob = GDYN && gcnt != nullptr;   // block-uniform
+  constexpr int GCH = MODE == MODE_KEYS ? 1 : 2;   // wave tiles per draw from the head's counter
   int64_t u = __builtin_amdgcn_readfirstlane(wv);
+  int64_t cend = 0;
   if constexpr (GDYN) {
     if (glob) {
       int32_t taken = 0;
       if (lane == 0) taken = atomicAdd(gcnt, 1);
-      u = __builtin_amdgcn_readfirstlane(taken);
+      u = (int64_t)__builtin_amdgcn_readfirstlane(taken) * GCH;
+      cend = u + GCH;
     }
   }
   if constexpr (PF) fetch_rows(u);
@@ -420,8 +423,13 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
     int32_t taken = 0;
     int64_t un;   // the wave's next tile
     if constexpr (GDYN) {
-      if (lane == 0) taken = glob ? atomicAdd(gcnt, 1) : atomicAdd(next_wt, 1);
-      un = (glob ? 0 : 4) + (int64_t)__builtin_amdgcn_readfirstlane(taken);
+      if (GCH > 1 && glob && u + 1 < cend) {
+        un = u + 1;
+      } else {
+        if (lane == 0) taken = glob ? atomicAdd(gcnt, 1) : atomicAdd(next_wt, 1);
+        un = glob ? (int64_t)__builtin_amdgcn_readfirstlane(taken) * GCH : 4 + (int64_t)__builtin_amdgcn_readfirstlane(taken);
+        cend = un + GCH;
+      }
     } else {
       if (lane == 0) taken = atomicAdd(next_wt, 1);
       un = 4 + (int64_t)__builtin_amdgcn_readfirstlane(taken);
@@ -941,13 +949,13 @@ __device__ __forceinline__ void select_range(const SelectArgs a, SelShared& sm, 
   __syncthreads();     // the block may stage another head's tables next
 }
 
-// Keys: the grid is one-dimensional.  Block b serves head b mod H; a head's
-// blocks take its 32-token wave tiles from the head's counter a.counter[4 + h] one by
-// one, so that blocks that get more of their CU (a CU runs the block that
-// arrived first ahead of its later partner) take more tiles.  Values and the
-// full Lloyd assignment: block (x, h) takes a fixed share of head h's tiles
-// (their tiles are cheap, and the counter's atomics cost more than the balance
-// gains).  FLAT (Lloyd's bounded
+// Keys and values: the grid is one-dimensional.  Block b serves head b mod H;
+// a head's blocks take its 32-token wave tiles from the head's counter
+// a.counter[4 + h] (one tile per draw for keys, two for values), so that
+// blocks that get more of their CU (a CU runs the block that arrived first
+// ahead of its later partner) take more tiles.  The full Lloyd assignment:
+// block (x, h) takes a fixed share of head h's tiles (its tiles are cheap, and
+// the counter's atomics cost more than the balance gains).  FLAT (Lloyd's bounded
 // iterations): all heads' lists, taken one after the other, form NT tiles,
 // and block b takes tiles [b NT / G, (b + 1) NT / G) of them (G blocks), head by
 // head, so that a short or uneven list still spreads over the whole grid.
@@ -971,7 +979,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
         select_range<MODE, F32, QS, WT, KQ, BND, false>(a, sm, g, n, (lo > r0 ? lo : r0) - lo, (hi < r1 ? hi : r1) - lo);
       lo = hi;
     }
-  } else if constexpr (MODE == MODE_KEYS) {
+  } else if constexpr (MODE == MODE_KEYS || MODE == MODE_VALUES) {
     // one-dimensional grid, heads interleaved (block b serves head b mod H), so
     // that each head has blocks of every dispatch round; with SEL_HEAD_COUNTERS the blocks
     // of a head take its wave tiles from the head's counter, otherwise block
@@ -988,8 +996,7 @@ __global__ __launch_bounds__(256, 2) void select_kernel(SelectArgs a) {
     select_range<MODE, F32, QS, WT, KQ, BND, true>(a, sm, h, a.T, t_begin, t_end);
   } else {
     // block (x, h): a contiguous share of head h's tiles, equal to within one
-    // tile across the head's gridDim.x blocks (values, the full Lloyd
-    // assignment)
+    // tile across the head's gridDim.x blocks (the full Lloyd assignment)
     const int h = blockIdx.y;
     const int64_t ntile = (a.T + SEL_TOK - 1) / SEL_TOK;
     const int64_t t_begin = (int64_t)blockIdx.x * ntile / gridDim.x;
@@ -1910,15 +1917,15 @@ static qwm_status run_select(const qwm_tokens* x, SelectArgs& a, hipStream_t str
   const int bph = blocks_per_head(x->T, x->H);
   const bool qs = (MODE == MODE_KEYS) && (a.flags & QWM_QSAC) && a.M > 1;
   const bool wt = (MODE == MODE_KEYS) && a.w != nullptr;
-  // keys: one-dimensional, heads interleaved, tiles from the per-head counters
-  // (SEL_HEAD_COUNTERS) when every wave has at least 16 tiles to draw (fewer, and the
-  // counters' atomics cost more than the balance gains); values and Lloyd:
-  // (blocks per head, H)
-  if (MODE == MODE_KEYS && (x->T + 31) / 32 >= 64 * (int64_t)bph) a.flags |= SEL_HEAD_COUNTERS;
+  // keys and values: one-dimensional, heads interleaved, tiles from the
+  // per-head counters (SEL_HEAD_COUNTERS) when every wave has at least 16
+  // tiles to draw (fewer, and the counters' atomics cost more than the
+  // balance gains); the Lloyd assignment: (blocks per head, H)
+  if ((MODE == MODE_KEYS || MODE == MODE_VALUES) && (x->T + 31) / 32 >= 64 * (int64_t)bph) a.flags |= SEL_HEAD_COUNTERS;
   // M in 9 .. 16: sixteen values tracked per lane, so that the shortlist can
   // still be certified without the exact path; M >= 256: every centroid
   const bool kq16 = qs && a.M > 8 && a.M <= 16;
-  const bool flat_keys = MODE == MODE_KEYS;
+  const bool flat_keys = MODE == MODE_KEYS || MODE == MODE_VALUES;
   const dim3 grid(flat_keys ? (unsigned)(bph * x->H) : (unsigned)bph, flat_keys ? 1u : (unsigned)x->H), block(256);
   const bool f32 = x->dtype != QWM_BF16;
   const bool exh = qs && a.M >= NC;
